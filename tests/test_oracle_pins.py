@@ -1,0 +1,318 @@
+"""Pins for the float64 oracle: facts fixed by the pages and by the mathematics.
+
+Every check here compares the oracle with something other than itself:
+a worked example derived by hand, closed forms, textbook special cases
+(the plain delta rule, gated DeltaNet, gated linear attention), brute-force
+dense unrolling with explicit transition matrices, and invariants (content
+boundary, chunk-length independence without a content projection, state
+chaining). The pages print no numeric example of their own.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import carve_forward, sigmoid
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def rand_inputs(rng, B, T, H, dk, dv, rank=0, ub_std=0.3):
+    q = rng.standard_normal((B, T, H, dk))
+    k = rng.standard_normal((B, T, H, dk))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, T, H, dv))
+    x = rng.standard_normal((B, T, H, dk))
+    g = -(np.maximum(x, 0) + np.log1p(np.exp(-np.abs(x))))
+    bx = rng.standard_normal((B, T, H, dk))
+    w = 1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H))))
+    Ud = Uu = None
+    if rank:
+        Ud = ub_std * rng.standard_normal((H, rank, dv))
+        Uu = ub_std * rng.standard_normal((H, dk, rank))
+    return q, k, v, g, bx, w, Ud, Uu
+
+
+# ---------------------------------------------------------------- worked example
+
+def test_hand_worked_example():
+    """Gist.science summary §2.1-2.3: a 4-token pass worked by hand (tests/golden)."""
+    fx = json.load(open(os.path.join(HERE, "golden", "hand_worked_content_gate.json")))
+    tb = lambda key: np.transpose(np.array(fx[key], dtype=np.float64), (1, 0, 2, 3))
+    q, k, v = tb("q"), tb("k"), tb("v")
+    g = np.log(tb("g_exp"))
+    p = tb("bx_sigmoid")
+    bx = np.log(p / (1 - p))
+    w = np.transpose(np.array(fx["w"]), (1, 0, 2))
+    Ud = np.array(fx["U_down"])
+    Uu = np.log(np.array(fx["U_up_exp"]))
+    o, S, m = carve_forward(q, k, v, g, bx, w, fx["L"], Ud, Uu,
+                            state_in=np.array(fx["state_in"]))
+    np.testing.assert_allclose(o, tb("expected_o"), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(S, np.array(fx["expected_state_out"]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(m, np.array(fx["expected_mean_out"]), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- closed forms
+
+def test_single_token_closed_form():
+    """T=1: o_1 = S_in q_1 and S_1 = S_in D (I - (b k) k^T) + w v k^T with b from mean_in."""
+    rng = np.random.default_rng(1)
+    B, H, dk, dv, r = 2, 3, 5, 4, 2
+    q, k, v, g, bx, w, Ud, Uu = rand_inputs(rng, B, 1, H, dk, dv, rank=r)
+    S_in = rng.standard_normal((B, H, dv, dk))
+    m_in = rng.standard_normal((B, H, dv))
+    o, S, m = carve_forward(q, k, v, g, bx, w, 1, Ud, Uu, state_in=S_in, mean_in=m_in)
+    for b_ in range(B):
+        for h in range(H):
+            z = Uu[h] @ (Ud[h] @ m_in[b_, h])
+            bb = 1 / (1 + np.exp(-(bx[b_, 0, h] + z)))
+            kk = k[b_, 0, h]
+            D = np.diag(np.exp(g[b_, 0, h]))
+            S1 = S_in[b_, h] @ D @ (np.eye(dk) - np.outer(bb * kk, kk)) + w[b_, 0, h] * np.outer(v[b_, 0, h], kk)
+            np.testing.assert_allclose(o[b_, 0, h], S_in[b_, h] @ q[b_, 0, h], atol=1e-13)
+            np.testing.assert_allclose(S[b_, h], S1, atol=1e-13)
+            np.testing.assert_allclose(m[b_, h], S_in[b_, h] @ q[b_, 0, h], atol=1e-13)
+
+
+def test_zero_state_first_token():
+    """With S_in = 0 the first readout is 0 and S_1 = w v k^T."""
+    rng = np.random.default_rng(2)
+    q, k, v, g, bx, w, _, _ = rand_inputs(rng, 1, 1, 2, 6, 3)
+    o, S, _ = carve_forward(q, k, v, g, bx, w, 1)
+    assert np.all(o == 0)
+    np.testing.assert_allclose(S[0], w[0, 0, :, None, None] * v[0, 0][:, :, None] * k[0, 0][:, None, :], atol=1e-15)
+
+
+def test_plain_delta_rule_exact_retrieval():
+    """b=1, g=0, w=1 is the delta rule: with unit keys S_t k_t = v_t exactly,
+    so a query equal to the last key reads back the last value."""
+    rng = np.random.default_rng(3)
+    B, T, H, dk, dv = 1, 12, 2, 8, 5
+    q, k, v, _, _, _, _, _ = rand_inputs(rng, B, T, H, dk, dv)
+    q[:, 1:] = k[:, :-1]                   # query t+1 = key t
+    g = np.zeros_like(k)
+    bx = np.full_like(k, 40.0)             # sigmoid(40) == 1.0 exactly in float64
+    assert sigmoid(40.0) == 1.0
+    w = np.ones((B, T, H))
+    o, S, _ = carve_forward(q, k, v, g, bx, w, 4)
+    np.testing.assert_allclose(o[:, 1:], v[:, :-1], atol=1e-12)
+    np.testing.assert_allclose(np.einsum("bhed,bhd->bhe", S, k[:, -1]), v[:, -1], atol=1e-12)
+
+
+def test_plain_delta_rule_orthonormal_keys():
+    """Delta rule with orthonormal keys and T <= d_k: S_T = sum_t v_t k_t^T."""
+    rng = np.random.default_rng(4)
+    dk, dv, T = 8, 3, 6
+    Q, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    k = Q[:, :T].T[None, :, None, :]
+    v = rng.standard_normal((1, T, 1, dv))
+    q = rng.standard_normal((1, T, 1, dk))
+    o, S, _ = carve_forward(q, k, v, np.zeros_like(k), np.full_like(k, 40.0), np.ones((1, T, 1)), T)
+    np.testing.assert_allclose(S[0, 0], sum(np.outer(v[0, t, 0], k[0, t, 0]) for t in range(T)), atol=1e-12)
+
+
+def test_gated_deltanet_special_case():
+    """Theorem 1 (subsumption): scalar decay alpha and scalar erase=write beta give
+    gated DeltaNet, S_t = alpha_t S_{t-1} (I - beta_t k k^T) + beta_t v k^T."""
+    rng = np.random.default_rng(5)
+    B, T, H, dk, dv = 2, 10, 2, 6, 4
+    q, k, v, _, _, _, _, _ = rand_inputs(rng, B, T, H, dk, dv)
+    alpha = rng.uniform(0.3, 1.0, (B, T, H))
+    beta = rng.uniform(0.05, 0.95, (B, T, H))
+    g = np.repeat(np.log(alpha)[..., None], dk, axis=-1)
+    bx = np.repeat(np.log(beta / (1 - beta))[..., None], dk, axis=-1)
+    o, S, _ = carve_forward(q, k, v, g, bx, beta, 5)
+    for b_ in range(B):
+        for h in range(H):
+            St = np.zeros((dv, dk))
+            for t in range(T):
+                np.testing.assert_allclose(o[b_, t, h], St @ q[b_, t, h], atol=1e-12)
+                kk = k[b_, t, h]
+                St = alpha[b_, t, h] * St @ (np.eye(dk) - beta[b_, t, h] * np.outer(kk, kk)) \
+                    + beta[b_, t, h] * np.outer(v[b_, t, h], kk)
+            np.testing.assert_allclose(S[b_, h], St, atol=1e-12)
+
+
+def test_no_erase_is_gated_linear_attention():
+    """b = 0 leaves decay and write only: o_t = S_in (e^{G_{t-1}} q_t)
+    + sum_{j<t} w_j v_j <k_j e^{G_{t-1} - G_j}, q_t> (G inclusive, G_{-1} = 0).
+    Pins the key-axis decay direction and the exclusive readout index."""
+    rng = np.random.default_rng(6)
+    B, T, H, dk, dv = 1, 9, 2, 5, 3
+    q, k, v, g, _, w, _, _ = rand_inputs(rng, B, T, H, dk, dv)
+    bx = np.full_like(k, -800.0)           # sigmoid(-800) underflows to 0.0
+    assert sigmoid(-800.0) == 0.0
+    S_in = rng.standard_normal((B, H, dv, dk))
+    o, _, _ = carve_forward(q, k, v, g, bx, w, 3, state_in=S_in)
+    G = np.cumsum(g, axis=1)
+    for h in range(H):
+        for t in range(T):
+            Gp = G[0, t - 1, h] if t > 0 else np.zeros(dk)
+            ref = S_in[0, h] @ (np.exp(Gp) * q[0, t, h])
+            for j in range(t):
+                ref = ref + w[0, j, h] * v[0, j, h] * np.dot(k[0, j, h] * np.exp(Gp - G[0, j, h]), q[0, t, h])
+            np.testing.assert_allclose(o[0, t, h], ref, atol=1e-12)
+
+
+def test_hard_decay_is_memoryless():
+    """alpha = 0 (g = -1e4): every step wipes the state, so o_{t+1} = w_t v_t <k_t, q_{t+1}>."""
+    rng = np.random.default_rng(7)
+    B, T, H, dk, dv = 1, 8, 2, 6, 4
+    q, k, v, _, bx, w, _, _ = rand_inputs(rng, B, T, H, dk, dv)
+    g = np.full_like(k, -1e4)
+    S_in = rng.standard_normal((B, H, dv, dk))
+    o, S, _ = carve_forward(q, k, v, g, bx, w, 4, state_in=S_in)
+    ref = w[:, :-1, :, None] * v[:, :-1] * np.sum(k[:, :-1] * q[:, 1:], axis=-1, keepdims=True)
+    np.testing.assert_allclose(o[:, 1:], ref, atol=1e-13)
+    np.testing.assert_allclose(o[0, 0], np.einsum("hed,hd->he", S_in[0], q[0, 0]), atol=1e-13)
+    np.testing.assert_allclose(S[0], w[0, -1, :, None, None] * v[0, -1][:, :, None] * k[0, -1][:, None, :], atol=1e-13)
+
+
+# ---------------------------------------------------------------- brute force
+
+def brute_force(q, k, v, g, bx, w, L, Ud, Uu, S_in):
+    """Dense unrolling with explicit d_k x d_k transitions M_t = D_t (I - (b_t k_t) k_t^T):
+    S_t = S_in prod_{s<=t} M_s + sum_{j<=t} w_j v_j k_j^T prod_{j<s<=t} M_s,
+    each S_t rebuilt from scratch; the content gate is recomputed from the
+    previous chunk's outputs."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, T, H, dv))
+    S_T = np.zeros((B, H, dv, dk))
+    for b_ in range(B):
+        for h in range(H):
+            M, W = [], []
+            prev_mean = np.zeros(dv)
+            for t in range(T):
+                c = t // L
+                if t % L == 0 and c > 0:
+                    prev_mean = o[b_, (c - 1) * L:c * L, h].mean(axis=0)
+                z = Uu[h] @ (Ud[h] @ prev_mean) if Ud is not None else 0.0
+                bb = 1 / (1 + np.exp(-(bx[b_, t, h] + z)))
+                kk = k[b_, t, h]
+                M.append(np.diag(np.exp(g[b_, t, h])) @ (np.eye(dk) - np.outer(bb * kk, kk)))
+                W.append(w[b_, t, h] * np.outer(v[b_, t, h], kk))
+
+                def state_after(n):          # state after n tokens, from scratch
+                    P = np.eye(dk)
+                    for s in range(n):
+                        P = P @ M[s]
+                    acc = S_in[b_, h] @ P
+                    for j in range(n):
+                        P = np.eye(dk)
+                        for s in range(j + 1, n):
+                            P = P @ M[s]
+                        acc = acc + W[j] @ P
+                    return acc
+                o[b_, t, h] = state_after(t) @ q[b_, t, h]
+            S_T[b_, h] = state_after(T)
+    return o, S_T
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 4])
+def test_brute_force_unrolling(L):
+    rng = np.random.default_rng(10 + L)
+    B, T, H, dk, dv = 1, 12, 2, 5, 3
+    q, k, v, g, bx, w, Ud, Uu = rand_inputs(rng, B, T, H, dk, dv, rank=2, ub_std=1.5)
+    S_in = rng.standard_normal((B, H, dv, dk))
+    o, S, _ = carve_forward(q, k, v, g, bx, w, L, Ud, Uu, state_in=S_in)
+    o_ref, S_ref = brute_force(q, k, v, g, bx, w, L, Ud, Uu, S_in)
+    np.testing.assert_allclose(o, o_ref, atol=1e-12)
+    np.testing.assert_allclose(S, S_ref, atol=1e-12)
+
+
+# ---------------------------------------------------------------- content path
+
+def test_content_gate_closed_form():
+    """Gist.science summary §2.1: chunk 1 is gated by the mean of chunk 0's outputs.
+    With k = 0 and g = 0 in chunk 0, S stays S_in, so m_0 = S_in mean(q_0..q_{L-1})
+    and the second token of chunk 1 reads S_in D (I - (b k) k^T) + w v k^T with
+    b = sigmoid(bx + U_up U_down m_0)."""
+    rng = np.random.default_rng(20)
+    B, L, H, dk, dv, r = 1, 4, 2, 5, 3, 2
+    T = 2 * L
+    q, k, v, g, bx, w, Ud, Uu = rand_inputs(rng, B, T, H, dk, dv, rank=r, ub_std=2.0)
+    k[:, :L] = 0.0
+    g[:, :L] = 0.0
+    S_in = rng.standard_normal((B, H, dv, dk))
+    o, _, _ = carve_forward(q, k, v, g, bx, w, L, Ud, Uu, state_in=S_in)
+    for h in range(H):
+        m0 = S_in[0, h] @ q[0, :L, h].mean(axis=0)
+        b = 1 / (1 + np.exp(-(bx[0, L, h] + Uu[h] @ (Ud[h] @ m0))))
+        kk = k[0, L, h]
+        S1 = S_in[0, h] @ np.diag(np.exp(g[0, L, h])) @ (np.eye(dk) - np.outer(b * kk, kk)) \
+            + w[0, L, h] * np.outer(v[0, L, h], kk)
+        np.testing.assert_allclose(o[0, :L + 1, h], q[0, :L + 1, h] @ S_in[0, h].T, atol=1e-13)
+        np.testing.assert_allclose(o[0, L + 1, h], S1 @ q[0, L + 1, h], atol=1e-13)
+
+
+def test_short_sequence_gets_no_content_signal():
+    """Limitations paragraph: a sequence no longer than one chunk gets no content
+    signal, so with mean_in = 0 the output does not depend on U_b at all."""
+    rng = np.random.default_rng(21)
+    q, k, v, g, bx, w, Ud, Uu = rand_inputs(rng, 2, 8, 2, 6, 4, rank=3, ub_std=3.0)
+    o0, S0, _ = carve_forward(q, k, v, g, bx, w, 8)
+    o1, S1, _ = carve_forward(q, k, v, g, bx, w, 8, Ud, Uu)
+    assert np.array_equal(o0, o1) and np.array_equal(S0, S1)
+    o2, _, _ = carve_forward(q, k, v, g, bx, w, 4, Ud, Uu)     # two chunks: the signal exists
+    assert np.abs(o2 - o0).max() > 1e-3
+
+
+def test_zero_projection_is_memory_blind_key_axis_rule():
+    """U_b = 0 gives the memory-blind key-axis gated delta rule: b = sigmoid(bx),
+    S_t = S_{t-1} D_t (I - (b_t k_t) k_t^T) + w_t v_t k_t^T, written here with
+    explicit matrices. A zero-filled projection equals an absent one bitwise,
+    and the output does not depend on L."""
+    rng = np.random.default_rng(22)
+    B, T, H, dk, dv, r = 1, 16, 2, 6, 4, 3
+    q, k, v, g, bx, w, Ud, Uu = rand_inputs(rng, B, T, H, dk, dv, rank=r)
+    S_in = rng.standard_normal((B, H, dv, dk))
+    o, S, _ = carve_forward(q, k, v, g, bx, w, 4, state_in=S_in)
+    oz, Sz, _ = carve_forward(q, k, v, g, bx, w, 4, np.zeros_like(Ud), np.zeros_like(Uu), state_in=S_in)
+    assert np.array_equal(o, oz) and np.array_equal(S, Sz)
+    for L in (1, 2, 8, 16):
+        oL, SL, _ = carve_forward(q, k, v, g, bx, w, L, state_in=S_in)
+        assert np.array_equal(oL, o) and np.array_equal(SL, S)
+    for h in range(H):
+        St = S_in[0, h].copy()
+        for t in range(T):
+            np.testing.assert_allclose(o[0, t, h], St @ q[0, t, h], atol=1e-12)
+            bb = 1 / (1 + np.exp(-bx[0, t, h]))
+            kk = k[0, t, h]
+            St = St @ np.diag(np.exp(g[0, t, h])) @ (np.eye(dk) - np.outer(bb * kk, kk)) \
+                + w[0, t, h] * np.outer(v[0, t, h], kk)
+        np.testing.assert_allclose(S[0, h], St, atol=1e-12)
+
+
+def test_state_and_mean_chaining():
+    """Running [0, T) equals [0, T/2) then [T/2, T) with S and m carried over."""
+    rng = np.random.default_rng(23)
+    B, T, H, dk, dv, L = 2, 24, 2, 5, 4, 4
+    q, k, v, g, bx, w, Ud, Uu = rand_inputs(rng, B, T, H, dk, dv, rank=2, ub_std=2.0)
+    o, S, m = carve_forward(q, k, v, g, bx, w, L, Ud, Uu)
+    h = T // 2
+    oa, Sa, ma = carve_forward(q[:, :h], k[:, :h], v[:, :h], g[:, :h], bx[:, :h], w[:, :h], L, Ud, Uu)
+    ob, Sb, mb = carve_forward(q[:, h:], k[:, h:], v[:, h:], g[:, h:], bx[:, h:], w[:, h:], L, Ud, Uu,
+                               state_in=Sa, mean_in=ma)
+    np.testing.assert_allclose(np.concatenate([oa, ob], axis=1), o, atol=1e-13)
+    np.testing.assert_allclose(Sb, S, atol=1e-13)
+    np.testing.assert_allclose(mb, m, atol=1e-13)
+
+
+def test_state_stays_bounded():
+    """Theorem 4 (Lyapunov): with decay and erase the state norm stays bounded."""
+    rng = np.random.default_rng(24)
+    q, k, v, g, bx, w, Ud, Uu = rand_inputs(rng, 1, 2048, 2, 16, 16, rank=4, ub_std=0.05)
+    o, S, m = carve_forward(q, k, v, g, bx, w, 64, Ud, Uu)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
+    assert np.abs(S).max() < 10.0
+
+
+def test_rejects_ragged_length():
+    rng = np.random.default_rng(25)
+    q, k, v, g, bx, w, _, _ = rand_inputs(rng, 1, 10, 1, 4, 4)
+    with pytest.raises(ValueError):
+        carve_forward(q, k, v, g, bx, w, 4)
