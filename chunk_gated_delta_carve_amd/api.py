@@ -1,0 +1,90 @@
+"""PyTorch-facing binding of the CARVE C ABI.
+
+Argument marshalling only: tensors are checked, outputs and workspace are
+allocated with torch on the GPU, and the C entry point is called on torch's
+current HIP stream. Every step of the forward pass runs in the HIP library;
+there is no CPU or PyTorch fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.float32: _lib.CARVE_F32, torch.bfloat16: _lib.CARVE_BF16}
+
+
+def make_config(B, H, T, dk, dv, L, rank, dtype) -> _lib.CarveConfig:
+    return _lib.CarveConfig(B, H, T, dk, dv, L, rank, _DTYPES[dtype] if isinstance(dtype, torch.dtype) else dtype)
+
+
+def recurrent_ref_shapes(B, H, T, dk, dv, L, rank=0, dtype=torch.bfloat16) -> _lib.CarveShapes:
+    return _lib.ref_shapes(make_config(B, H, T, dk, dv, L, rank, dtype))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def chunk_fwd(q, k, v, g, bx, w, L=64, ub_down=None, ub_up=None, state_in=None, mean_in=None,
+              return_state=False, out=None, workspace=None, stream=None):
+    """CARVE forward pass. Shapes: q, k, g, bx [B,T,H,dk]; v [B,T,H,dv]; w [B,T,H];
+    ub_down [H,r,dv]; ub_up [H,dk,r]; state_in [B,H,dv,dk] fp32; mean_in [B,H,dv] fp32.
+    Returns o [B,T,H,dv] (and (state_out, mean_out) when return_state)."""
+    if q.device.type != "cuda":
+        raise ValueError("chunk_fwd runs on the GPU only; move the inputs to a cuda device")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt, dev = q.dtype, q.device
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    rank = 0 if ub_down is None else int(ub_down.shape[1])
+    if (ub_down is None) != (ub_up is None):
+        raise ValueError("ub_down and ub_up come together")
+    for name, t, shp in (("q", q, (B, T, H, dk)), ("k", k, (B, T, H, dk)), ("v", v, (B, T, H, dv)),
+                         ("g", g, (B, T, H, dk)), ("bx", bx, (B, T, H, dk)), ("w", w, (B, T, H))):
+        _need(t, name, shp, dt, dev)
+    if rank:
+        _need(ub_down, "ub_down", (H, rank, dv), dt, dev)
+        _need(ub_up, "ub_up", (H, dk, rank), dt, dev)
+    _need(state_in, "state_in", (B, H, dv, dk), torch.float32, dev)
+    _need(mean_in, "mean_in", (B, H, dv), torch.float32, dev)
+
+    cfg = make_config(B, H, T, dk, dv, L, rank, dt)
+    sh = _lib.ref_shapes(cfg)
+    o = out if out is not None else torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    _need(o, "out", (B, T, H, dv), dt, dev)
+    state_out = mean_out = None
+    if return_state:
+        state_out = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+        mean_out = torch.empty((B, H, dv), dtype=torch.float32, device=dev)
+    ws_bytes = int(sh.workspace_bytes)
+    if ws_bytes and (workspace is None or workspace.numel() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    code = _lib.lib().carve_chunk_fwd(
+        ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(bx), _ptr(w),
+        _ptr(ub_down), _ptr(ub_up), _ptr(state_in), _ptr(mean_in),
+        _ptr(o), _ptr(state_out), _ptr(mean_out),
+        _ptr(workspace) if ws_bytes else None, ctypes.c_size_t(ws_bytes if ws_bytes else 0),
+        ctypes.c_void_p(stream))
+    _lib.check(code)
+    if return_state:
+        return o, state_out, mean_out
+    return o

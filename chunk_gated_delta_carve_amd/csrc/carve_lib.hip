@@ -1,0 +1,149 @@
+// Host side of the CARVE C ABI: validation, shape contract, dispatch.
+// Every check runs before the first HIP call so argument errors are reported
+// (and unit-testable) on a machine without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+
+#include "carve.h"
+#include "kernels/chunk_serial.h"
+
+namespace {
+
+thread_local char g_hip_msg[256] = "no HIP error recorded";
+
+bool valid_width(int d) { return d == 64 || d == 128; }
+bool valid_chunk(int L) { return L == 16 || L == 32 || L == 64 || L == 128; }
+
+int check_config(const carve_config* c) {
+  if (!c) return CARVE_EINVAL;
+  if (c->B < 0 || c->H < 0 || c->T < 0 || c->rank < 0) return CARVE_EINVAL;
+  if (c->dtype != CARVE_F32 && c->dtype != CARVE_BF16) return CARVE_EINVAL;
+  if (!valid_width(c->dk) || !valid_width(c->dv) || c->dk != c->dv) return CARVE_EUNSUPPORTED;
+  if (!valid_chunk(c->L)) return CARVE_EUNSUPPORTED;
+  if (c->rank > 64) return CARVE_EUNSUPPORTED;
+  // offsets are computed in 64-bit, the grid in 32-bit
+  if ((int64_t)c->B * c->H > 0x7fffffffLL) return CARVE_EUNSUPPORTED;
+  return CARVE_OK;
+}
+
+size_t elem_bytes(int dtype) { return dtype == CARVE_F32 ? 4 : 2; }
+
+bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u); }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// block length used by the chunk-serial kernel: divides L, fits LDS
+int serial_block(const carve_config* c) {
+  int bl = c->L < 64 ? c->L : 64;
+  if (c->dtype == CARVE_F32 && c->dk == 128 && bl > 32) bl = 32;
+  return bl;
+}
+
+template <typename E, int D, int BL>
+hipError_t launch_serial(const carve::FwdArgs& a, hipStream_t s) {
+  using LY = carve::SerialLayout<E, D, D, BL>;
+  auto kern = carve::carve_chunk_serial_kernel<E, D, D, BL>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, LY::bytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(a.B * a.H), dim3(LY::NT), LY::bytes, s, a);
+  return hipGetLastError();
+}
+
+template <typename E, int D>
+hipError_t dispatch_block(const carve::FwdArgs& a, int bl, hipStream_t s) {
+  switch (bl) {
+    case 16: return launch_serial<E, D, 16>(a, s);
+    case 32: return launch_serial<E, D, 32>(a, s);
+    default:
+      if constexpr (sizeof(E) == 4 && D == 128) return hipErrorInvalidValue;
+      else return launch_serial<E, D, 64>(a, s);
+  }
+}
+
+}  // namespace
+
+extern "C" int carve_recurrent_ref_shapes(const carve_config* cfg, carve_shapes* out) {
+  const int st = check_config(cfg);
+  if (st != CARVE_OK) return st;
+  if (!out) return CARVE_EINVAL;
+  const int64_t B = cfg->B, H = cfg->H, T = cfg->T, dk = cfg->dk, dv = cfg->dv, r = cfg->rank;
+  out->q = out->k = out->g = out->bx = B * T * H * dk;
+  out->v = out->o = B * T * H * dv;
+  out->w = B * T * H;
+  out->ub_down = H * r * dv;
+  out->ub_up = H * dk * r;
+  out->state = B * H * dv * dk;
+  out->mean = B * H * dv;
+  out->workspace_bytes = 0;
+  return CARVE_OK;
+}
+
+extern "C" int carve_chunk_fwd(const carve_config* cfg,
+                               const void* q, const void* k, const void* v,
+                               const void* g, const void* bx, const void* w,
+                               const void* ub_down, const void* ub_up,
+                               const float* state_in, const float* mean_in,
+                               void* o, float* state_out, float* mean_out,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  carve_shapes sh;
+  int st = carve_recurrent_ref_shapes(cfg, &sh);
+  if (st != CARVE_OK) return st;
+  const bool tokens = sh.q > 0;
+  if (tokens && (!q || !k || !v || !g || !bx || !w || !o)) return CARVE_EINVAL;
+  const bool content = cfg->rank > 0;
+  if (content && (int64_t)cfg->B * cfg->H > 0 && (!ub_down || !ub_up)) return CARVE_EINVAL;
+  const void* ptrs[] = {q, k, v, g, bx, w, content ? ub_down : nullptr, content ? ub_up : nullptr,
+                        state_in, mean_in, o, state_out, mean_out, workspace};
+  for (const void* p : ptrs)
+    if (misaligned(p)) return CARVE_EALIGN;
+  if (workspace_bytes < (size_t)sh.workspace_bytes) return CARVE_EWORKSPACE;
+  const size_t es = elem_bytes(cfg->dtype);
+  const size_t ob = (size_t)sh.o * es;
+  const struct { const void* p; size_t n; } ins[] = {
+      {q, (size_t)sh.q * es}, {k, (size_t)sh.k * es}, {v, (size_t)sh.v * es},
+      {g, (size_t)sh.g * es}, {bx, (size_t)sh.bx * es}, {w, (size_t)sh.w * es},
+      {state_in, (size_t)sh.state * 4}, {mean_in, (size_t)sh.mean * 4}};
+  for (const auto& in : ins)
+    if (overlaps(o, ob, in.p, in.n)) return CARVE_EINVAL;
+  if ((int64_t)cfg->B * cfg->H == 0) return CARVE_OK;
+  if (!tokens && !state_out && !mean_out) return CARVE_OK;
+
+  carve::FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.bx = bx; a.w = w;
+  a.ub_down = ub_down; a.ub_up = ub_up;
+  a.state_in = state_in; a.mean_in = mean_in;
+  a.o = o; a.state_out = state_out; a.mean_out = mean_out;
+  a.B = cfg->B; a.H = cfg->H; a.T = cfg->T; a.L = cfg->L; a.rank = cfg->rank;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int bl = serial_block(cfg);
+  hipError_t e;
+  if (cfg->dtype == CARVE_BF16)
+    e = cfg->dk == 64 ? dispatch_block<carve::bf16, 64>(a, bl, s) : dispatch_block<carve::bf16, 128>(a, bl, s);
+  else
+    e = cfg->dk == 64 ? dispatch_block<float, 64>(a, bl, s) : dispatch_block<float, 128>(a, bl, s);
+  if (e != hipSuccess) {
+    std::snprintf(g_hip_msg, sizeof(g_hip_msg), "%s", hipGetErrorString(e));
+    return CARVE_EHIP;
+  }
+  return CARVE_OK;
+}
+
+extern "C" const char* carve_error_string(int code) {
+  switch (code) {
+    case CARVE_OK: return "ok";
+    case CARVE_EINVAL: return "invalid argument (NULL required pointer, negative size, bad rank or overlapping output)";
+    case CARVE_EUNSUPPORTED: return "unsupported configuration (dk/dv in {64,128} with dk == dv, L in {16,32,64,128}, rank <= 64)";
+    case CARVE_EALIGN: return "a tensor pointer is not 16-byte aligned";
+    case CARVE_EWORKSPACE: return "workspace smaller than carve_recurrent_ref_shapes() requires";
+    case CARVE_EHIP: return g_hip_msg;
+    default: return "unknown status code";
+  }
+}

@@ -1,0 +1,139 @@
+// Shared device helpers for the CARVE kernels on gfx950 (CDNA4).
+//
+// MFMA conventions used everywhere (16x16 output tiles, 64-wide wavefronts):
+//   lane l, group g = l / 16, column c = l % 16
+//   C tile (f32x4):   lane holds C[4g + i][c], i = 0..3
+//   A fragment:       lane holds A[c][k-slots of group g]
+//   B fragment:       lane holds B[k-slots of group g][c]
+// A and B use the same map from (g, slot) to the reduction index k, so any
+// permutation of k inside one instruction is allowed as long as both operands
+// agree. Two maps are used:
+//   natural: slot i of group g is k = K * g + i  (K = slots per lane)
+//   c-pair : for bf16 16x16x32, slots 0..3 are k = 4g + i and slots 4..7 are
+//            k = 16 + 4g + (i - 4); for f32 16x16x4, step p of a 16-row block
+//            uses k = 16 (p / 4) + 4g + (p % 4).
+// The c-pair map lets a C tile (rows 4g..4g+3 of a lane) feed the next
+// instruction's B operand straight from registers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace carve {
+
+typedef __bf16 bf16;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+template <typename M> __device__ __forceinline__ M from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+constexpr float kLog2e = 1.4426950408889634f;
+
+// logistic(x) = 1 / (1 + e^{-x}); saturates cleanly at both ends
+__device__ __forceinline__ float sigmoid_f(float x) {
+  return fast_rcp(1.0f + fast_exp2(-x * kLog2e));
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// ---------------------------------------------------------------------------
+// MFMA policy per operand type.
+template <typename M> struct Mma;
+
+template <> struct Mma<bf16> {
+  static constexpr int KS = 32;  // reduction length of one instruction
+  typedef bf16x8 frag;
+  __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  // natural map from a row-major tile: row `row`, k = k0 + 8g + i
+  __device__ __forceinline__ static frag ld_nat(const bf16* base, int ld, int row, int k0) {
+    const int g = lane_id() >> 4;
+    return *reinterpret_cast<const bf16x8*>(base + row * ld + k0 + 8 * g);
+  }
+  __device__ __forceinline__ static frag ld_nat(const float* base, int ld, int row, int k0) {
+    const int g = lane_id() >> 4;
+    const f32x4* p = reinterpret_cast<const f32x4*>(base + row * ld + k0 + 8 * g);
+    f32x4 a = p[0], b = p[1];
+    return frag{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3],
+                (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
+  }
+  // c-pair map, reduction step p: k = 32p + 4g + i (i < 4), 32p + 16 + 4g + i - 4
+  __device__ __forceinline__ static frag ld_cp(const bf16* base, int ld, int row, int p) {
+    const int g = lane_id() >> 4;
+    const bf16* r = base + row * ld + 32 * p + 4 * g;
+    bf16x4 lo = *reinterpret_cast<const bf16x4*>(r);
+    bf16x4 hi = *reinterpret_cast<const bf16x4*>(r + 16);
+    return frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  // B operand for reduction step p built from C tiles t[2p], t[2p+1]
+  __device__ __forceinline__ static frag from_c(const f32x4* t, int p) {
+    f32x4 a = t[2 * p], b = t[2 * p + 1];
+    return frag{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3],
+                (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
+  }
+  // number of reduction steps covering `n` rows of C tiles (n multiple of 16)
+  __device__ __forceinline__ static constexpr int steps(int n) { return (n + 31) / 32; }
+};
+
+template <> struct Mma<float> {
+  static constexpr int KS = 4;
+  typedef float frag;
+  __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static frag ld_nat(const float* base, int ld, int row, int k0) {
+    return base[row * ld + k0 + (lane_id() >> 4)];
+  }
+  __device__ __forceinline__ static frag ld_cp(const float* base, int ld, int row, int p) {
+    const int g = lane_id() >> 4;
+    return base[row * ld + 16 * (p >> 2) + 4 * g + (p & 3)];
+  }
+  __device__ __forceinline__ static frag from_c(const f32x4* t, int p) { return t[p >> 2][p & 3]; }
+  __device__ __forceinline__ static constexpr int steps(int n) { return n / 4; }
+};
+
+// 16x16x16 product whose B operand is one C tile (bf16: one instruction with
+// the natural 4-slot map, which coincides with the C layout; f32: four
+// 16x16x4 instructions). A is read from a row-major fp32 tile.
+template <typename M> struct Mma16;
+template <> struct Mma16<bf16> {
+  __device__ __forceinline__ static f32x4 mma_rowA_cB(const float* A, int lda, int row, int k0,
+                                                      f32x4 b, f32x4 c, float sign) {
+    const int g = lane_id() >> 4;
+    f32x4 a = *reinterpret_cast<const f32x4*>(A + row * lda + k0 + 4 * g);
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    bf16x4 av{(bf16)(sign * a[0]), (bf16)(sign * a[1]), (bf16)(sign * a[2]), (bf16)(sign * a[3])};
+    bf16x4 bv{(bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, av),
+                                                      __builtin_bit_cast(s4, bv), c, 0, 0, 0);
+  }
+};
+template <> struct Mma16<float> {
+  __device__ __forceinline__ static f32x4 mma_rowA_cB(const float* A, int lda, int row, int k0,
+                                                      f32x4 b, f32x4 c, float sign) {
+    const int g = lane_id() >> 4;
+    const float* a = A + row * lda + k0 + 4 * g;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(sign * a[p], b[p], c, 0, 0, 0);
+    return c;
+  }
+};
+
+// Sum over the four row groups of a C tile column: lanes c, c+16, c+32, c+48.
+__device__ __forceinline__ float sum_groups(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+}  // namespace carve

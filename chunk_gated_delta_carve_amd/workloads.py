@@ -133,3 +133,12 @@ def make_inputs(wl: Workload) -> dict:
         out["U_down"] = _cast(wl.ub_std * draw((H, wl.rank, dv)), wl.dtype)
         out["U_up"] = _cast(wl.ub_std * draw((H, dk, wl.rank)), wl.dtype)
     return out
+
+
+def to_torch(stored: np.ndarray, dtype: str, device="cuda"):
+    """Move a storage array from make_inputs to a torch tensor (bf16 bits become torch.bfloat16)."""
+    import torch
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(stored)).to(device)
+    t = torch.from_numpy(np.ascontiguousarray(stored).view(np.int16))
+    return t.view(torch.bfloat16).to(device)

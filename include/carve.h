@@ -1,0 +1,117 @@
+/*
+ * carve.h: C ABI of the CARVE chunk-parallel forward pass on MI355X (gfx950).
+ *
+ * The operation is the forward pass of the CARVE recurrent layer (arXiv
+ * 2606.27229, "CARVE: Content-Aware Recurrent with Value Efficiency for
+ * Chunk-Parallel Linear Attention"), as described in the gist.science
+ * technical summaries:
+ *   section 1 (problem statement)   per head a state S of shape d_v x d_k;
+ *   section 2 (method)              every gate acts on the key axis only;
+ *   section 2.1 (output reuse)      o_t = S_{t-1} q_t, chunk mean
+ *                                   m_c = (1/L) sum o_t, erase gate
+ *                                   b = sigmoid(b_x + U_b m), one chunk stale;
+ *   section 2.2 (scalar write)      one write gate w per head and token,
+ *                                   broadcast over the value channels;
+ *   section 2.3 (key-axis decay)    exponential decay exp(g) on the key axis.
+ * Per token (readings: b scales the retrieval key; decay precedes erase):
+ *   o_t = S q_t;  S <- S diag(exp(g_t)) (I - (b_t * k_t) k_t^T) + w_t v_t k_t^T
+ * with b_t = sigmoid(bx_t + U_up (U_down m_{c-1})) for every token of chunk c,
+ * m_{-1} = mean_in (zero when absent), and m_c the mean of chunk c's outputs
+ * over the tokens it holds (a last chunk may be partial).
+ * The library computes this with the WY-form chunk solver (Theorem 11 in
+ * section 3 of the same summaries: key-axis-only erase leaves one triangular
+ * system per chunk).
+ *
+ * Conventions for every entry point:
+ *   - No HIP types cross this header; `stream` is a hipStream_t passed as
+ *     void* (NULL = the null stream).
+ *   - All tensor pointers are device pointers owned by the caller. The library
+ *     never allocates, frees or synchronises; work is queued on `stream` and
+ *     the call returns before it finishes.
+ *   - Tensors are dense, row-major, 16-byte aligned, no strides.
+ *   - Every argument check runs before the first HIP call, so invalid
+ *     arguments are reported (and testable) without a GPU.
+ *   - The library keeps no state; concurrent calls need distinct outputs.
+ *   - Errors are returned as a carve_status code; nothing is thrown.
+ */
+#ifndef CARVE_H
+#define CARVE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CARVE_OK = 0,
+  CARVE_EINVAL = 1,        /* NULL required pointer, negative size, bad rank */
+  CARVE_EUNSUPPORTED = 2,  /* d_k/d_v not in {64,128}, L not in {16,32,64,128}, d_k != d_v */
+  CARVE_EALIGN = 3,        /* a pointer is not 16-byte aligned */
+  CARVE_EWORKSPACE = 4,    /* workspace smaller than carve_recurrent_ref_shapes() asks */
+  CARVE_EHIP = 5           /* a HIP launch failed; carve_error_string(CARVE_EHIP) has the text */
+} carve_status;
+
+typedef enum { CARVE_F32 = 0, CARVE_BF16 = 1 } carve_dtype;
+
+/* Problem description. B batch, H heads, T tokens, dk key width, dv value
+ * width, L chunk length of the content signal, rank of U_b (0 = no content
+ * projection), dtype of every activation tensor and of U_down/U_up. */
+typedef struct {
+  int32_t B, H, T, dk, dv, L, rank;
+  int32_t dtype; /* carve_dtype */
+} carve_config;
+
+/* Element counts of every tensor (not bytes), and the workspace size in bytes. */
+typedef struct {
+  int64_t q, k, v, g, bx, w;   /* inputs */
+  int64_t ub_down, ub_up;      /* content projection factors (0 when rank == 0) */
+  int64_t o;                   /* output */
+  int64_t state, mean;         /* optional fp32 state_in/out and mean_in/out */
+  int64_t workspace_bytes;     /* device scratch the caller must provide */
+} carve_shapes;
+
+/* Validates `cfg` and fills `out` with the shape contract of the recurrence:
+ *   q, k, g, bx : [B, T, H, dk]      v, o : [B, T, H, dv]      w : [B, T, H]
+ *   ub_down     : [H, rank, dv]      ub_up : [H, dk, rank]
+ *   state       : [B, H, dv, dk] fp32   mean : [B, H, dv] fp32
+ * Returns CARVE_OK, CARVE_EINVAL or CARVE_EUNSUPPORTED. Makes no HIP call. */
+int carve_recurrent_ref_shapes(const carve_config* cfg, carve_shapes* out);
+
+/* Forward pass of the CARVE layer (see the header comment for the math).
+ *   q, k       [B,T,H,dk] dtype   query and key (used as given: no scaling)
+ *   v          [B,T,H,dv] dtype   value
+ *   g          [B,T,H,dk] dtype   log-decay, expected <= 0
+ *   bx         [B,T,H,dk] dtype   erase logit
+ *   w          [B,T,H]    dtype   scalar write gate
+ *   ub_down    [H,rank,dv] dtype, ub_up [H,dk,rank] dtype: U_b = ub_up @ ub_down
+ *              per head. Ignored when rank == 0; required when rank > 0.
+ *   state_in   [B,H,dv,dk] fp32 or NULL (zeros)
+ *   mean_in    [B,H,dv] fp32 or NULL (zeros): the mean that gates chunk 0
+ *   o          [B,T,H,dv] dtype   output; must not overlap any input
+ *   state_out  [B,H,dv,dk] fp32 or NULL (not written); may equal state_in
+ *   mean_out   [B,H,dv] fp32 or NULL (not written); may equal mean_in. It
+ *              receives the mean of the last (possibly partial) chunk, or
+ *              mean_in when T == 0.
+ *   workspace  device scratch of at least shapes.workspace_bytes (may be NULL
+ *              when that is 0)
+ *   stream     hipStream_t as void*
+ * B, H or T may be 0 (nothing to compute; with T == 0 the state and mean pass
+ * through). T need not be a multiple of L. */
+int carve_chunk_fwd(const carve_config* cfg,
+                    const void* q, const void* k, const void* v,
+                    const void* g, const void* bx, const void* w,
+                    const void* ub_down, const void* ub_up,
+                    const float* state_in, const float* mean_in,
+                    void* o, float* state_out, float* mean_out,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. For CARVE_EHIP it returns the HIP error text
+ * of the most recent failure on the calling thread. */
+const char* carve_error_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CARVE_H */

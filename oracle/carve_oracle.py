@@ -36,7 +36,9 @@ Readings where the pages leave a step open (each listed in the design notes):
   R2  Decay is applied first, then erase acts on the decayed state.
   R3  The gate of chunk c uses m_{c-1}; m_{-1} is mean_in (default zero).
   R4  U_b = U_up @ U_down per head, U_down [r, d_v], U_up [d_k, r].
-  R5  No 1/sqrt(d_k) scale on q; T must be a multiple of L.
+  R5  No 1/sqrt(d_k) scale on q.
+  R6  T need not be a multiple of L: the last chunk may be partial, and its
+      mean is taken over the tokens it holds (it can only reach mean_out).
 """
 from __future__ import annotations
 
@@ -73,7 +75,7 @@ def carve_forward(q, k, v, g, bx, w, L, U_down=None, U_up=None,
       q, k, g, bx : [B, T, H, d_k]   query, key, log-decay (<= 0), erase logit
       v           : [B, T, H, d_v]   value
       w           : [B, T, H]        scalar write gate
-      L           : chunk length of the content signal
+      L           : chunk length of the content signal (T need not be a multiple)
       U_down      : [H, r, d_v] or None;  U_up: [H, d_k, r] or None
       state_in    : [B, H, d_v, d_k] or None (zeros)
       mean_in     : [B, H, d_v] or None (zeros): the mean that feeds chunk 0
@@ -90,8 +92,8 @@ def carve_forward(q, k, v, g, bx, w, L, U_down=None, U_up=None,
     q, k, v, g, bx, w = map(f, (q, k, v, g, bx, w))
     B, T, H, dk = q.shape
     dv = v.shape[-1]
-    if T % L != 0:
-        raise ValueError("T must be a multiple of L (reading R5)")
+    if L < 1:
+        raise ValueError("L must be positive")
     Ud = None if U_down is None else f(U_down)
     Uu = None if U_up is None else f(U_up)
 
@@ -99,10 +101,11 @@ def carve_forward(q, k, v, g, bx, w, L, U_down=None, U_up=None,
     m = np.zeros((B, H, dv)) if mean_in is None else f(mean_in).copy()
     o = np.empty((B, T, H, dv))
 
-    for c in range(T // L):
+    for c in range((T + L - 1) // L):
         z = content_gate_bias(m, Ud, Uu)
         acc = np.zeros((B, H, dv))
-        for t in range(c * L, (c + 1) * L):
+        t_end = min(T, (c + 1) * L)                              # reading R6
+        for t in range(c * L, t_end):
             logit = bx[:, t] if z is None else bx[:, t] + z
             b = sigmoid(logit)                                   # [B, H, dk]
             ot = np.einsum("bhed,bhd->bhe", S, q[:, t])          # o_t = S_{t-1} q_t
@@ -112,5 +115,5 @@ def carve_forward(q, k, v, g, bx, w, L, U_down=None, U_up=None,
             r = np.einsum("bhed,bhd->bhe", S, b * k[:, t])        # erase-weighted retrieval
             delta = w[:, t, :, None] * v[:, t] - r               # [B, H, dv]
             S = S + delta[:, :, :, None] * k[:, t][:, :, None, :]
-        m = acc / L
+        m = acc / (t_end - c * L)
     return o, S, m

@@ -1,0 +1,115 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/carve.h, reports the shape contract, and rejects invalid
+arguments before making any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from chunk_gated_delta_carve_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        from chunk_gated_delta_carve_amd.build import build_library
+        build_library(verbose=False)
+    return _lib.lib()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "carve.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(carve_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(L, n)
+
+
+def cfg(**kw):
+    base = dict(B=2, H=3, T=100, dk=64, dv=64, L=64, rank=4, dtype=_lib.CARVE_BF16)
+    base.update(kw)
+    return _lib.CarveConfig(*(base[n] for n in ("B", "H", "T", "dk", "dv", "L", "rank", "dtype")))
+
+
+def test_shape_contract(L):
+    sh = _lib.ref_shapes(cfg())
+    assert sh.q == sh.k == sh.g == sh.bx == 2 * 100 * 3 * 64
+    assert sh.v == sh.o == 2 * 100 * 3 * 64
+    assert sh.w == 2 * 100 * 3
+    assert sh.ub_down == 3 * 4 * 64 and sh.ub_up == 3 * 64 * 4
+    assert sh.state == 2 * 3 * 64 * 64 and sh.mean == 2 * 3 * 64
+    assert sh.workspace_bytes >= 0
+    sh = _lib.ref_shapes(cfg(rank=0, dk=128, dv=128, L=128, dtype=_lib.CARVE_F32))
+    assert sh.ub_down == 0 and sh.ub_up == 0 and sh.state == 2 * 3 * 128 * 128
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dk=32, dv=32), _lib.CARVE_EUNSUPPORTED),
+    (dict(dk=64, dv=128), _lib.CARVE_EUNSUPPORTED),
+    (dict(dk=96, dv=96), _lib.CARVE_EUNSUPPORTED),
+    (dict(L=48), _lib.CARVE_EUNSUPPORTED),
+    (dict(L=256), _lib.CARVE_EUNSUPPORTED),
+    (dict(rank=65), _lib.CARVE_EUNSUPPORTED),
+    (dict(T=-1), _lib.CARVE_EINVAL),
+    (dict(B=-2), _lib.CARVE_EINVAL),
+    (dict(rank=-1), _lib.CARVE_EINVAL),
+    (dict(dtype=7), _lib.CARVE_EINVAL),
+])
+def test_config_rejected(L, kw, code):
+    out = _lib.CarveShapes()
+    assert L.carve_recurrent_ref_shapes(ctypes.byref(cfg(**kw)), ctypes.byref(out)) == code
+
+
+def test_null_config_and_output(L):
+    out = _lib.CarveShapes()
+    assert L.carve_recurrent_ref_shapes(None, ctypes.byref(out)) == _lib.CARVE_EINVAL
+    assert L.carve_recurrent_ref_shapes(ctypes.byref(cfg()), None) == _lib.CARVE_EINVAL
+
+
+FAKE = 0x10000000   # never dereferenced: validation fails before any use
+
+
+def call_fwd(L, c, **ptrs):
+    names = ["q", "k", "v", "g", "bx", "w", "ub_down", "ub_up", "state_in", "mean_in",
+             "o", "state_out", "mean_out", "workspace"]
+    base = {n: None for n in names}
+    step = 1 << 24
+    for i, n in enumerate(["q", "k", "v", "g", "bx", "w", "ub_down", "ub_up", "o"]):
+        base[n] = FAKE + i * step
+    base.update(ptrs)
+    args = [ctypes.c_void_p(base[n]) if base[n] is not None else None for n in names]
+    return L.carve_chunk_fwd(ctypes.byref(c) if c is not None else None, *args,
+                             ctypes.c_size_t(ptrs.get("ws_bytes", 0) if False else 0), None)
+
+
+def test_fwd_argument_errors(L):
+    c = cfg()
+    assert call_fwd(L, None) == _lib.CARVE_EINVAL
+    assert call_fwd(L, c, q=None) == _lib.CARVE_EINVAL
+    assert call_fwd(L, c, o=None) == _lib.CARVE_EINVAL
+    assert call_fwd(L, c, ub_down=None) == _lib.CARVE_EINVAL          # rank > 0 needs U_b
+    assert call_fwd(L, c, k=FAKE + 0x1000 + 4) == _lib.CARVE_EALIGN
+    assert call_fwd(L, c, state_in=FAKE - 8) == _lib.CARVE_EALIGN
+    assert call_fwd(L, c, o=FAKE + 64) == _lib.CARVE_EINVAL           # o overlaps q
+    assert call_fwd(L, cfg(dk=96, dv=96)) == _lib.CARVE_EUNSUPPORTED
+    # nothing to do: no HIP call is made and the call succeeds
+    assert call_fwd(L, cfg(B=0)) == _lib.CARVE_OK
+    assert call_fwd(L, cfg(T=0)) == _lib.CARVE_OK
+
+
+def test_error_strings(L):
+    for code in range(6):
+        assert len(_lib.error_string(code)) > 0
+    assert "unknown" in _lib.error_string(99)

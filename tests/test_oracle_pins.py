@@ -212,10 +212,10 @@ def brute_force(q, k, v, g, bx, w, L, Ud, Uu, S_in):
     return o, S_T
 
 
-@pytest.mark.parametrize("L", [1, 2, 3, 4])
-def test_brute_force_unrolling(L):
-    rng = np.random.default_rng(10 + L)
-    B, T, H, dk, dv = 1, 12, 2, 5, 3
+@pytest.mark.parametrize("L,T", [(1, 12), (2, 12), (3, 12), (4, 12), (4, 11), (5, 12)])
+def test_brute_force_unrolling(L, T):
+    rng = np.random.default_rng(10 + L + T)
+    B, H, dk, dv = 1, 2, 5, 3
     q, k, v, g, bx, w, Ud, Uu = rand_inputs(rng, B, T, H, dk, dv, rank=2, ub_std=1.5)
     S_in = rng.standard_normal((B, H, dv, dk))
     o, S, _ = carve_forward(q, k, v, g, bx, w, L, Ud, Uu, state_in=S_in)
@@ -311,8 +311,24 @@ def test_state_stays_bounded():
     assert np.abs(S).max() < 10.0
 
 
-def test_rejects_ragged_length():
+def test_ragged_length_is_causal_prefix():
+    """A partial last chunk (reading R6): outputs are causal, so a ragged run is
+    the prefix of a longer run, and mean_out is the mean of its partial chunk."""
     rng = np.random.default_rng(25)
-    q, k, v, g, bx, w, _, _ = rand_inputs(rng, 1, 10, 1, 4, 4)
-    with pytest.raises(ValueError):
-        carve_forward(q, k, v, g, bx, w, 4)
+    q, k, v, g, bx, w, Ud, Uu = rand_inputs(rng, 2, 16, 2, 5, 4, rank=2, ub_std=2.0)
+    o16, _, _ = carve_forward(q, k, v, g, bx, w, 4, Ud, Uu)
+    sl = slice(0, 11)
+    o11, S11, m11 = carve_forward(q[:, sl], k[:, sl], v[:, sl], g[:, sl], bx[:, sl], w[:, sl], 4, Ud, Uu)
+    np.testing.assert_array_equal(o11, o16[:, :11])
+    np.testing.assert_allclose(m11, o11[:, 8:11].mean(axis=1), atol=1e-14)
+
+
+def test_empty_sequence_passes_state_through():
+    rng = np.random.default_rng(26)
+    q, k, v, g, bx, w, Ud, Uu = rand_inputs(rng, 1, 0, 2, 4, 3, rank=2)
+    S_in = rng.standard_normal((1, 2, 3, 4))
+    m_in = rng.standard_normal((1, 2, 3))
+    o, S, m = carve_forward(q, k, v, g, bx, w, 4, Ud, Uu, state_in=S_in, mean_in=m_in)
+    assert o.shape == (1, 0, 2, 3)
+    np.testing.assert_array_equal(S, S_in)
+    np.testing.assert_array_equal(m, m_in)
