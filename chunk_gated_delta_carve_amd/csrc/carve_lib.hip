@@ -7,7 +7,7 @@
 #include <cstring>
 
 #include "carve.h"
-#include "kernels/chunk_serial.h"
+#include "kernels/kernels.h"
 
 namespace {
 
@@ -45,14 +45,51 @@ int serial_block(const carve_config* c) {
   return bl;
 }
 
+// Without a content projection the gates do not depend on earlier outputs and
+// the chunk-parallel schedule (intra + state kernels, block length 64) is used.
+bool chunk_parallel(const carve_config* c) { return c->rank == 0 && c->dtype == CARVE_BF16; }
+constexpr int kParallelBlock = 64;
+
+int64_t parallel_workspace_bytes(const carve_config* c) {
+  const int64_t nblk = (c->T + kParallelBlock - 1) / kParallelBlock;
+  const int64_t img = c->dk == 64 ? carve::BlockLayout<carve::bf16, 64, 64, kParallelBlock>::wBytes
+                                  : carve::BlockLayout<carve::bf16, 128, 128, kParallelBlock>::wBytes;
+  return (int64_t)c->B * c->H * nblk * img;
+}
+
+template <typename K>
+hipError_t set_lds(K kern, int bytes) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
 template <typename E, int D, int BL>
 hipError_t launch_serial(const carve::FwdArgs& a, hipStream_t s) {
-  using LY = carve::SerialLayout<E, D, D, BL>;
+  using LY = carve::BlockLayout<E, D, D, BL>;
   auto kern = carve::carve_chunk_serial_kernel<E, D, D, BL>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, LY::bytes);
+  hipError_t e = set_lds(kern, LY::serial_bytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(a.B * a.H), dim3(LY::NT), LY::bytes, s, a);
+  hipLaunchKernelGGL(kern, dim3(a.B * a.H), dim3(LY::NT), LY::serial_bytes, s, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_parallel(const carve::FwdArgs& a, hipStream_t s) {
+  using E = carve::bf16;
+  constexpr int BL = kParallelBlock;
+  using LY = carve::BlockLayout<E, D, D, BL>;
+  const int nblk = (a.T + BL - 1) / BL;
+  auto intra = carve::carve_intra_kernel<E, D, D, BL>;
+  auto state = carve::carve_state_kernel<E, D, D, BL>;
+  hipError_t e = set_lds(intra, LY::intra_bytes);
+  if (e == hipSuccess) e = set_lds(state, 2 * LY::sBytes);
+  if (e != hipSuccess) return e;
+  if (nblk > 0) {
+    hipLaunchKernelGGL(intra, dim3(a.B * a.H * nblk), dim3(LY::NT), LY::intra_bytes, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(state, dim3(a.B * a.H), dim3(LY::NT), 2 * LY::sBytes, s, a);
   return hipGetLastError();
 }
 
@@ -81,7 +118,7 @@ extern "C" int carve_recurrent_ref_shapes(const carve_config* cfg, carve_shapes*
   out->ub_up = H * dk * r;
   out->state = B * H * dv * dk;
   out->mean = B * H * dv;
-  out->workspace_bytes = 0;
+  out->workspace_bytes = chunk_parallel(cfg) ? parallel_workspace_bytes(cfg) : 0;
   return CARVE_OK;
 }
 
@@ -120,12 +157,15 @@ extern "C" int carve_chunk_fwd(const carve_config* cfg,
   a.ub_down = ub_down; a.ub_up = ub_up;
   a.state_in = state_in; a.mean_in = mean_in;
   a.o = o; a.state_out = state_out; a.mean_out = mean_out;
+  a.ws = workspace;
   a.B = cfg->B; a.H = cfg->H; a.T = cfg->T; a.L = cfg->L; a.rank = cfg->rank;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int bl = serial_block(cfg);
   hipError_t e;
-  if (cfg->dtype == CARVE_BF16)
+  if (chunk_parallel(cfg))
+    e = cfg->dk == 64 ? launch_parallel<64>(a, s) : launch_parallel<128>(a, s);
+  else if (cfg->dtype == CARVE_BF16)
     e = cfg->dk == 64 ? dispatch_block<carve::bf16, 64>(a, bl, s) : dispatch_block<carve::bf16, 128>(a, bl, s);
   else
     e = cfg->dk == 64 ? dispatch_block<float, 64>(a, bl, s) : dispatch_block<float, 128>(a, bl, s);

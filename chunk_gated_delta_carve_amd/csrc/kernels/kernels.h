@@ -1,0 +1,240 @@
+// CARVE forward kernels for gfx950, all built from the per-block operations
+// in block.h.
+//
+//   carve_chunk_serial_kernel  one workgroup per (batch, head) walks the
+//       sequence block by block. Needed whenever the content projection U_b
+//       is present: the erase gate of chunk c depends on the mean output of
+//       chunk c-1, so every stage of a block waits for the previous block.
+//   carve_intra_kernel + carve_state_kernel  used when U_b is absent: the
+//       gates no longer depend on earlier outputs, so gate prep, the Grams,
+//       the triangular inverse and W/U run for all blocks at once (one
+//       workgroup per block); each block's state-pass operands go to a
+//       workspace, and a per-(batch, head) kernel then runs only the serial
+//       state update and the output.
+// Both schedules call the same device functions in the same order, and the
+// workspace holds the same rounded values the serial kernel keeps in LDS, so
+// they produce bitwise-identical results for equal inputs.
+#pragma once
+#include "block.h"
+
+namespace carve {
+
+template <typename E, int DK, int DV, int BL>
+__global__ void __launch_bounds__((BlockLayout<E, DK, DV, BL>::NT))
+carve_chunk_serial_kernel(FwdArgs a) {
+  using B = Block<E, DK, DV, BL>;
+  using LY = typename B::LY;
+  constexpr int NT = LY::NT, NB = LY::NB;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const auto s = B::carve(smem);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int gq = lane >> 4, cc = lane & 15;
+  const int bh = blockIdx.x;
+  Rows<E> src{static_cast<const E*>(a.q), static_cast<const E*>(a.k), static_cast<const E*>(a.v),
+              static_cast<const E*>(a.g), static_cast<const E*>(a.bx), static_cast<const E*>(a.w),
+              a.T, a.H, bh / a.H, bh % a.H};
+  const int h = src.h;
+  const int T = a.T, L = a.L, rank = a.rank;
+  E* __restrict__ O = static_cast<E*>(a.o);
+  const E* Ud = static_cast<const E*>(a.ub_down);
+  const E* Uu = static_cast<const E*>(a.ub_up);
+  const int e0 = 16 * wave;
+
+  B::zero_lds(smem, LY::serial_bytes);
+  const Sink<E> sink = B::lds_sink(s);
+  f32x4 St[DK / 16];
+  B::load_state(a.state_in, bh, St);
+  __syncthreads();
+  for (int e = tid; e < DV; e += NT) s.M[e] = a.mean_in ? a.mean_in[(size_t)bh * DV + e] : 0.f;
+  __syncthreads();
+
+  // z = U_up (U_down m) into s.Z (all threads call; ends with a barrier)
+  auto content_bias = [&]() {
+    if (rank > 0) {
+      for (int r = tid; r < rank; r += NT) {
+        float y = 0.f;
+        for (int e = 0; e < DV; ++e) y += ldg(Ud, ((size_t)h * rank + r) * DV + e) * s.M[e];
+        s.Y[r] = y;
+      }
+      __syncthreads();
+      for (int d = tid; d < DK; d += NT) {
+        float z = 0.f;
+        for (int r = 0; r < rank; ++r) z += ldg(Uu, ((size_t)h * DK + d) * rank + r) * s.Y[r];
+        s.Z[d] = z;
+      }
+    }
+    __syncthreads();
+  };
+  content_bias();
+
+  float m_part = 0.f;                   // running column sum of O for this lane's channel
+  const int nblk = (T + BL - 1) / BL;
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int t0 = blk * BL;
+    const int nvalid = min(BL, T - t0);
+    const bool fallback = B::gate_pass(s, src, t0, nvalid, sink);
+    B::grams(s, src, t0, nvalid, fallback, sink);
+    B::inverse(s);
+    B::build_w(s, sink);
+    f32x4 U[NB], Ot[NB];
+    B::build_u(s, U);
+    B::state_step(s.W, s.Qd, s.P, s.KdT, s.Egl, U, St, Ot);
+#pragma unroll
+    for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * gq + i;
+        m_part += Ot[rt][i];                       // rows past nvalid are exactly 0
+        if (r < nvalid) O[src.row(t0 + r) * DV + e0 + cc] = from_f32<E>(Ot[rt][i]);
+      }
+    __syncthreads();
+    const bool chunk_end = ((t0 + BL) % L == 0) || (t0 + BL >= T);
+    if (chunk_end) {
+      const int chunk = t0 / L;
+      const int count = min(L, T - chunk * L);
+      const float tot = sum_groups(m_part);
+      if (gq == 0) s.M[e0 + cc] = tot / (float)count;
+      m_part = 0.f;
+      __syncthreads();
+      if (t0 + BL < T) content_bias();
+    }
+  }
+  if (a.state_out) B::store_state(a.state_out, bh, St);
+  if (a.mean_out)
+    for (int e = tid; e < DV; e += NT) a.mean_out[(size_t)bh * DV + e] = s.M[e];
+}
+
+// One workgroup per (block, batch, head): everything that does not depend on
+// the state. Writes the block's state-pass operand image to the workspace.
+template <typename E, int DK, int DV, int BL>
+__global__ void __launch_bounds__((BlockLayout<E, DK, DV, BL>::NT))
+carve_intra_kernel(FwdArgs a) {
+  using B = Block<E, DK, DV, BL>;
+  using LY = typename B::LY;
+  constexpr int NT = LY::NT, NB = LY::NB;
+  static_assert(BL >= 32, "the image has no padding columns to clear");
+  extern __shared__ __align__(16) unsigned char smem[];
+  const auto s = B::carve(smem);
+
+  const int nblk = (a.T + BL - 1) / BL;
+  const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk;
+  Rows<E> src{static_cast<const E*>(a.q), static_cast<const E*>(a.k), static_cast<const E*>(a.v),
+              static_cast<const E*>(a.g), static_cast<const E*>(a.bx), static_cast<const E*>(a.w),
+              a.T, a.H, bh / a.H, bh % a.H};
+  const int t0 = blk * BL;
+  const int nvalid = min(BL, a.T - t0);
+  unsigned char* img = static_cast<unsigned char*>(a.ws) + ((size_t)bh * nblk + blk) * LY::wBytes;
+  const Sink<E> sink = B::image_sink(img);
+
+  B::zero_lds(smem, LY::intra_bytes);   // z = 0: no content projection
+  __syncthreads();
+  const bool fallback = B::gate_pass(s, src, t0, nvalid, sink);
+  B::grams(s, src, t0, nvalid, fallback, sink);
+  B::inverse(s);
+  B::build_w(s, sink);
+  f32x4 U[NB];
+  B::build_u(s, U);
+
+  for (int i = threadIdx.x; i < DK; i += NT) reinterpret_cast<float*>(img + LY::wEgl)[i] = s.Egl[i];
+  E* Ui = reinterpret_cast<E*>(img + LY::wU);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int gq = lane >> 4, cc = lane & 15;
+#pragma unroll
+  for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Ui[(16 * rt + 4 * gq + i) * DV + 16 * wave + cc] = from_f32<E>(U[rt][i]);
+}
+
+// One workgroup per (batch, head): the serial state pass and the output.
+// Block images stream through two LDS buffers; the next one is fetched into
+// registers while the current one is used.
+template <typename E, int DK, int DV, int BL>
+__global__ void __launch_bounds__((BlockLayout<E, DK, DV, BL>::NT))
+carve_state_kernel(FwdArgs a) {
+  using B = Block<E, DK, DV, BL>;
+  using LY = typename B::LY;
+  constexpr int NT = LY::NT, NB = LY::NB;
+  constexpr int CH = LY::wBytes / 16;                 // 16-byte chunks per image
+  constexpr int PER = (CH + NT - 1) / NT;             // chunks per thread
+  static_assert(2 * LY::sBytes <= 160 * 1024, "two staging buffers fit");
+  extern __shared__ __align__(16) unsigned char smem[];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int gq = lane >> 4, cc = lane & 15;
+  const int bh = blockIdx.x;
+  const int T = a.T, H = a.H, L = a.L;
+  const int bidx = bh / H, h = bh % H;
+  const int nblk = (T + BL - 1) / BL;
+  const int e0 = 16 * wave;
+  E* __restrict__ O = static_cast<E*>(a.o);
+  const unsigned char* imgs = static_cast<const unsigned char*>(a.ws) + (size_t)bh * nblk * LY::wBytes;
+
+  f32x4 St[DK / 16];
+  B::load_state(a.state_in, bh, St);
+  const int mstart = T > 0 ? ((T - 1) / L) * L : 0;   // first token of the last chunk
+  float m_part = 0.f;
+
+  f32x4 pre[PER];
+  auto fetch = [&](int blk) {
+    const f32x4* g = reinterpret_cast<const f32x4*>(imgs + (size_t)blk * LY::wBytes);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int c = tid + j * NT;
+      if (c < CH) pre[j] = g[c];
+    }
+  };
+  auto deposit = [&](int buf) {
+    unsigned char* d = smem + buf * LY::sBytes;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int c = tid + j * NT;
+      if (c < CH) *reinterpret_cast<f32x4*>(d + LY::stage_offset(c)) = pre[j];
+    }
+  };
+  if (nblk > 0) {
+    fetch(0);
+    deposit(0);
+  }
+  __syncthreads();
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int cur = blk & 1;
+    if (blk + 1 < nblk) fetch(blk + 1);
+    const unsigned char* buf = smem + cur * LY::sBytes;
+    const E* Wm = reinterpret_cast<const E*>(buf + LY::sW);
+    const E* Qd = reinterpret_cast<const E*>(buf + LY::sQd);
+    const E* Pm = reinterpret_cast<const E*>(buf + LY::sP);
+    const E* KdT = reinterpret_cast<const E*>(buf + LY::sKdT);
+    const E* Ui = reinterpret_cast<const E*>(buf + LY::sU);
+    const float* Egl = reinterpret_cast<const float*>(buf + LY::sEgl);
+    f32x4 U[NB], Ot[NB];
+#pragma unroll
+    for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) U[rt][i] = to_f32(Ui[(16 * rt + 4 * gq + i) * DV + e0 + cc]);
+    B::state_step(Wm, Qd, Pm, KdT, Egl, U, St, Ot);
+    const int t0 = blk * BL;
+    const int nvalid = min(BL, T - t0);
+#pragma unroll
+    for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * gq + i;
+        if (t0 + r >= mstart) m_part += Ot[rt][i];   // rows past nvalid are exactly 0
+        if (r < nvalid) O[((size_t)(bidx * T + t0 + r) * H + h) * DV + e0 + cc] = from_f32<E>(Ot[rt][i]);
+      }
+    if (blk + 1 < nblk) deposit(cur ^ 1);
+    __syncthreads();
+  }
+  if (a.state_out) B::store_state(a.state_out, bh, St);
+  if (a.mean_out) {
+    const float tot = sum_groups(m_part);
+    if (T == 0) {
+      for (int e = tid; e < DV; e += NT) a.mean_out[(size_t)bh * DV + e] = a.mean_in ? a.mean_in[(size_t)bh * DV + e] : 0.f;
+    } else if (gq == 0) {
+      a.mean_out[(size_t)bh * DV + e0 + cc] = tot / (float)(T - mstart);
+    }
+  }
+}
+
+}  // namespace carve

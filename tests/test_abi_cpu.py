@@ -109,6 +109,18 @@ def test_fwd_argument_errors(L):
     assert call_fwd(L, cfg(T=0)) == _lib.CARVE_OK
 
 
+def test_workspace_contract(L):
+    """Without a content projection (bf16) the chunk-parallel schedule needs a
+    workspace; a smaller one is rejected before any HIP call."""
+    c = cfg(rank=0)
+    sh = _lib.ref_shapes(c)
+    assert sh.workspace_bytes > 0
+    assert _lib.ref_shapes(cfg(rank=4)).workspace_bytes == 0
+    assert _lib.ref_shapes(cfg(rank=0, dtype=_lib.CARVE_F32)).workspace_bytes == 0
+    assert call_fwd(L, c, ub_down=None, ub_up=None) == _lib.CARVE_EWORKSPACE
+    assert call_fwd(L, cfg(rank=0, B=0)) == _lib.CARVE_OK
+
+
 def test_error_strings(L):
     for code in range(6):
         assert len(_lib.error_string(code)) > 0

@@ -163,6 +163,12 @@ EDGE = [
     ("bf16-d64-L32", "bf16", 2, 2, 320, 64, 32, 8),
     ("bf16-d128-L16", "bf16", 1, 2, 160, 128, 16, 8),
     ("no-ub-L16", "f32", 1, 2, 192, 64, 16, 0),
+    # no content projection in bf16: the chunk-parallel schedule
+    ("par-T1", "bf16", 1, 2, 1, 64, 32, 0),
+    ("par-T64", "bf16", 1, 1, 64, 64, 64, 0),
+    ("par-ragged-100-L16", "bf16", 1, 3, 100, 64, 16, 0),
+    ("par-d128-ragged-200-L128", "bf16", 2, 2, 200, 128, 128, 0),
+    ("par-d128-L64", "bf16", 1, 3, 512, 128, 64, 0),
 ]
 
 
