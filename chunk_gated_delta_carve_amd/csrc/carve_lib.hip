@@ -82,14 +82,15 @@ hipError_t launch_parallel(const carve::FwdArgs& a, hipStream_t s) {
   auto intra = carve::carve_intra_kernel<E, D, D, BL>;
   auto state = carve::carve_state_kernel<E, D, D, BL>;
   hipError_t e = set_lds(intra, LY::intra_bytes);
-  if (e == hipSuccess) e = set_lds(state, 2 * LY::sBytes);
+  constexpr int state_lds = 2 * LY::sBytes;
+  if (e == hipSuccess) e = set_lds(state, state_lds);
   if (e != hipSuccess) return e;
   if (nblk > 0) {
     hipLaunchKernelGGL(intra, dim3(a.B * a.H * nblk), dim3(LY::NT), LY::intra_bytes, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(state, dim3(a.B * a.H), dim3(LY::NT), 2 * LY::sBytes, s, a);
+  hipLaunchKernelGGL(state, dim3(a.B * a.H), dim3(LY::NT), state_lds, s, a);
   return hipGetLastError();
 }
 

@@ -43,7 +43,7 @@ constexpr float kSpanLimit2 = 96.0f;   // max decay (log2 units) inside a 16-row
 
 template <typename E, int DK, int DV, int BL>
 struct BlockLayout {
-  static_assert(DK % 32 == 0 && DV % 16 == 0, "head widths");
+  static_assert(DK % 32 == 0 && DV % 16 == 0 && DK == DV, "head widths");
   static_assert(BL == 16 || BL == 32 || BL == 64, "block length");
   static constexpr int NW = DV / 16;                 // one wave per 16 value channels
   static constexpr int NT = NW * 64;
@@ -55,34 +55,39 @@ struct BlockLayout {
   static constexpr int LD = DK + PE;                 // pitch of [.][DK] tiles
   static constexpr int LK = KP + PE;                 // pitch of [.][KP] tiles
   static constexpr int LV = DV + PE;                 // pitch of the value tile
-  static constexpr int LT = KP + 4;                  // pitch of T (fp32)
   static constexpr int LA = BL + 4;                  // pitch of A (fp32)
+  static constexpr int LTD = 16 + 4;                 // pitch of the diagonal inverses (fp32)
+  static constexpr int NFAR = NB > 2 ? (NB - 1) * (NB - 2) / 2 : 1;   // sub-block pairs J < I-1
 
   // LDS byte offsets. Small arrays first, then tiles; the chunk-parallel
-  // kernel stops after A, the chunk-serial kernel also keeps Qd, KdT, P.
+  // kernel stops at intra_bytes, the chunk-serial kernel also keeps the
+  // state-pass operands Qd, KdT, P, W.
   static constexpr int oGb = 0;                              // [NB+1][DK] f32 (log2 units)
   static constexpr int oSeg = oGb + (NB + 1) * DK * 4;       // [NB][DK] f32
-  static constexpr int oEgl = oSeg + NB * DK * 4;            // [DK] f32
-  static constexpr int oWg = oEgl + DK * 4;                  // [KP] f32 write gate (zero padded)
+  static constexpr int oEgl = oSeg + NB * DK * 4;            // [DK] f32 e^{G_BL}
+  static constexpr int oEGs = oEgl + DK * 4;                 // [NB][DK] f32 e^{Gs_I}
+  static constexpr int oWg = oEGs + NB * DK * 4;             // [KP] f32 write gate (zero padded)
   static constexpr int oZ = oWg + KP * 4;                    // [DK] f32
   static constexpr int oM = oZ + DK * 4;                     // [DV] f32
   static constexpr int oY = oM + DV * 4;                     // [64] f32
   static constexpr int oFlag = oY + 64 * 4;                  // int
-  static constexpr int oKx = oFlag + 16;                     // [BL][LD] E   (serial: later W)
-  static constexpr int oQx = oKx + BL * LD * ES;             // [BL][LD] E   (later T, fp32)
+  static constexpr int oFd = oFlag + 16;                     // [NB][DK] f32 e^{Gs_J - Ge_J}
+  static constexpr int oFf = oFd + NB * DK * 4;              // [NFAR][DK] f32 e^{Gs_I - Ge_J}
+  static constexpr int oOnes = oFf + NFAR * DK * 4;          // [DK] f32 all ones
+  static constexpr int oKx = oOnes + DK * 4;                 // [BL][LD] E
+  static constexpr int oQx = oKx + BL * LD * ES;             // [BL][LD] E   (then A, fp32)
   static constexpr int oKy = oQx + BL * LD * ES;             // [BL][LD] E
-  static constexpr int oKbT = oKy + BL * LD * ES;            // [DK][LK] E
-  static constexpr int oV = oKbT + DK * LK * ES;             // [KP][LV] E (rows >= BL stay 0)
-  static constexpr int oA = oV + KP * LV * ES;               // [BL][LA] f32
-  static constexpr int intra_bytes = oA + BL * LA * 4;
+  static constexpr int oV = oKy + BL * LD * ES;              // [KP][LV] E   (then U; rows >= BL stay 0)
+  static constexpr int oTd = oV + KP * LV * ES;              // [NB][16][LTD] f32
+  static constexpr int intra_bytes = oTd + NB * 16 * LTD * 4;
   static constexpr int oQd = intra_bytes;                    // [BL][LD] E
   static constexpr int oKdT = oQd + BL * LD * ES;            // [DK][LK] E
   static constexpr int oP = oKdT + DK * LK * ES;             // [BL][LK] E
-  static constexpr int serial_bytes = oP + BL * LK * ES;
-  static_assert(2 * BL * LD * ES >= BL * LT * 4, "T fits in the Qx/Ky region");
-  static_assert(BL * LD * ES >= NB * 256 * 2 * 4, "fallback accumulators fit in Kx");
+  static constexpr int oW = oP + BL * LK * ES;               // [BL][LD] E
+  static constexpr int serial_bytes = oW + BL * LD * ES;
+  static_assert(2 * BL * LD * ES >= BL * LA * 4, "A fits in the Qx/Ky region");
   static_assert(serial_bytes <= 160 * 1024, "LDS budget");
-  static_assert(oKx % 16 == 0, "tile alignment");
+  static_assert(oKx % 16 == 0 && oV % 16 == 0 && oTd % 16 == 0, "tile alignment");
 
   // dense image of one block's state-pass operands (workspace)
   static constexpr int wW = 0;                               // [BL][DK] E
@@ -116,6 +121,25 @@ struct BlockLayout {
 template <typename E>
 __device__ __forceinline__ float ldg(const E* p, size_t i) { return to_f32(p[i]); }
 
+// multiply fragment slot values by per-k factors (natural map)
+template <typename M> struct FragScale;
+template <> struct FragScale<bf16> {
+  __device__ __forceinline__ static bf16x8 apply(bf16x8 a, const float* fac, int k0) {
+    const int g = lane_id() >> 4;
+    const f32x4* f = reinterpret_cast<const f32x4*>(fac + k0 + 8 * g);
+    const f32x4 f0 = f[0], f1 = f[1];
+    return bf16x8{(bf16)((float)a[0] * f0[0]), (bf16)((float)a[1] * f0[1]),
+                  (bf16)((float)a[2] * f0[2]), (bf16)((float)a[3] * f0[3]),
+                  (bf16)((float)a[4] * f1[0]), (bf16)((float)a[5] * f1[1]),
+                  (bf16)((float)a[6] * f1[2]), (bf16)((float)a[7] * f1[3])};
+  }
+};
+template <> struct FragScale<float> {
+  __device__ __forceinline__ static float apply(float a, const float* fac, int k0) {
+    return a * fac[k0 + (lane_id() >> 4)];
+  }
+};
+
 // Token rows of one (batch, head) in the [B, T, H, d] layout.
 template <typename E>
 struct Rows {
@@ -140,12 +164,12 @@ struct Block {
   using MM = Mma<E>;
   using Frag = typename MM::frag;
   static constexpr int NW = LY::NW, NT = LY::NT, NB = LY::NB, KP = LY::KP, KS = MM::KS;
-  static constexpr int LD = LY::LD, LK = LY::LK, LV = LY::LV, LT = LY::LT, LA = LY::LA;
+  static constexpr int LD = LY::LD, LK = LY::LK, LV = LY::LV, LA = LY::LA, LTD = LY::LTD;
 
   struct Smem {
     unsigned char* base;
-    E *Kx, *Qx, *Ky, *KbT, *V, *Qd, *KdT, *P, *W;
-    float *T, *A, *Gb, *Seg, *Egl, *Wg, *Z, *M, *Y;
+    E *Kx, *Qx, *Ky, *V, *Qd, *KdT, *P, *W;
+    float *A, *Td, *Gb, *Seg, *Egl, *EGs, *Wg, *Z, *M, *Y, *Fd, *Ff, *Ones;
     int* Flag;
   };
 
@@ -153,24 +177,27 @@ struct Block {
     Smem s;
     s.base = smem;
     s.Kx = reinterpret_cast<E*>(smem + LY::oKx);
-    s.W = s.Kx;                                        // chunk-serial: W reuses Kx
     s.Qx = reinterpret_cast<E*>(smem + LY::oQx);
-    s.T = reinterpret_cast<float*>(smem + LY::oQx);    // T reuses Qx/Ky after the Grams
+    s.A = reinterpret_cast<float*>(smem + LY::oQx);    // A reuses Qx/Ky after the Grams
     s.Ky = reinterpret_cast<E*>(smem + LY::oKy);
-    s.KbT = reinterpret_cast<E*>(smem + LY::oKbT);
     s.V = reinterpret_cast<E*>(smem + LY::oV);
-    s.A = reinterpret_cast<float*>(smem + LY::oA);
+    s.Td = reinterpret_cast<float*>(smem + LY::oTd);
     s.Qd = reinterpret_cast<E*>(smem + LY::oQd);
     s.KdT = reinterpret_cast<E*>(smem + LY::oKdT);
     s.P = reinterpret_cast<E*>(smem + LY::oP);
+    s.W = reinterpret_cast<E*>(smem + LY::oW);
     s.Gb = reinterpret_cast<float*>(smem + LY::oGb);
     s.Seg = reinterpret_cast<float*>(smem + LY::oSeg);
     s.Egl = reinterpret_cast<float*>(smem + LY::oEgl);
+    s.EGs = reinterpret_cast<float*>(smem + LY::oEGs);
     s.Wg = reinterpret_cast<float*>(smem + LY::oWg);
     s.Z = reinterpret_cast<float*>(smem + LY::oZ);
     s.M = reinterpret_cast<float*>(smem + LY::oM);
     s.Y = reinterpret_cast<float*>(smem + LY::oY);
     s.Flag = reinterpret_cast<int*>(smem + LY::oFlag);
+    s.Fd = reinterpret_cast<float*>(smem + LY::oFd);
+    s.Ff = reinterpret_cast<float*>(smem + LY::oFf);
+    s.Ones = reinterpret_cast<float*>(smem + LY::oOnes);
     return s;
   }
 
@@ -192,8 +219,9 @@ struct Block {
   // factorised diagonal Grams. Ends with a barrier.
   __device__ static bool gate_pass(const Smem& s, const Rows<E>& src, int t0, int nvalid, const Sink<E>& out) {
     const int tid = threadIdx.x;
-    const int gs = tid / DK, gd = tid % DK;
+    const int gs = wave_id() * 64 / DK, gd = tid % DK;
     if (tid == 0) s.Flag[0] = 0;
+    for (int d = tid; d < DK; d += NT) s.Ones[d] = 1.f;
     float gv[16], kv[16], qv[16], bv[16];
     if (gs < NB) {
 #pragma unroll
@@ -212,10 +240,11 @@ struct Block {
     {
       constexpr int CPR = DV * LY::ES / 16;          // chunks per row
       constexpr int NCH = BL * CPR;
-      f32x4 vc[(NCH + NT - 1) / NT];
+      constexpr int PER = (NCH + NT - 1) / NT;
+      f32x4 vc[PER];
 #pragma unroll
-      for (int j = 0; j < (NCH + NT - 1) / NT; ++j) {
-        const int c = threadIdx.x + j * NT;
+      for (int j = 0; j < PER; ++j) {
+        const int c = tid + j * NT;
         if (c < NCH) {
           const int r = c / CPR, cc = c % CPR;
           const int rc = min(r, nvalid - 1);
@@ -224,8 +253,8 @@ struct Block {
         }
       }
 #pragma unroll
-      for (int j = 0; j < (NCH + NT - 1) / NT; ++j) {
-        const int c = threadIdx.x + j * NT;
+      for (int j = 0; j < PER; ++j) {
+        const int c = tid + j * NT;
         if (c < NCH) {
           const int r = c / CPR, cc = c % CPR;
           *reinterpret_cast<f32x4*>(s.V + r * LV + cc * (16 / LY::ES)) = vc[j];
@@ -257,17 +286,31 @@ struct Block {
       }
       const float Gs = base;                         // G before this sub-block
       const float Ge = base + run;                   // G at its last row
+      const float eGs = fast_exp2(Gs);
       s.Gb[gs * DK + gd] = Gs;
+      s.EGs[gs * DK + gd] = eGs;
       if (gs == NB - 1) {
         s.Gb[NB * DK + gd] = total;
         s.Egl[gd] = fast_exp2(total);
       }
       if (Gs - Ge > kSpanLimit2) atomicOr(s.Flag, 1);
-      const float eGs = fast_exp2(Gs);
+      // Gram scaling factors of this column: diagonal sub-block gs, and the
+      // pairs (I, gs) with I > gs + 1
+      s.Fd[gs * DK + gd] = fast_exp2(Gs - Ge);
+#pragma unroll
+      for (int I = 0; I < NB; ++I) {
+        if (I > gs + 1) {
+          float gsI = 0.f;                           // G before sub-block I
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+            if (j < I) gsI += s.Seg[j * DK + gd];
+          s.Ff[((I - 2) * (I - 1) / 2 + gs) * DK + gd] = fast_exp2(gsI - Ge);
+        }
+      }
       const float eTail = fast_exp2(total - Ge);
       const float z = s.Z[gd];
       float eprev = 1.f;                             // e^{G_{r-1} - Gs}
-      E kb[16], kd[16];
+      E kd[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int r = 16 * gs + i;
@@ -275,254 +318,247 @@ struct Block {
         const float bb = sigmoid_f(bv[i] + z);
         const float e1 = fast_exp2(Gr - Gs);         // <= 1
         const float en = fast_exp2(Ge - Gr);         // <= 1
-        const float bk = bb * kv[i];
-        s.Kx[r * LD + gd] = from_f32<E>(bk * e1);
+        s.Kx[r * LD + gd] = from_f32<E>(bb * kv[i] * e1);
         s.Qx[r * LD + gd] = from_f32<E>(qv[i] * eprev);
         s.Ky[r * LD + gd] = from_f32<E>(kv[i] * en);
         out.Qd[r * out.ldQd + gd] = from_f32<E>(qv[i] * eprev * eGs);
-        kb[i] = from_f32<E>(bk * e1 * eGs);
         kd[i] = from_f32<E>(kv[i] * en * eTail);
         eprev = e1;
       }
-      // transposed tiles: this thread's 16 rows are 16 consecutive elements
-      E* kbt = s.KbT + gd * LK + 16 * gs;
+      // Kdec transposed: this thread's 16 rows are 16 consecutive elements
       E* kdt = out.KdT + gd * out.ldKdT + 16 * gs;
 #pragma unroll
-      for (int c = 0; c < 16 * LY::ES / 16; ++c) {
-        *reinterpret_cast<f32x4*>(kbt + c * (16 / LY::ES)) = *reinterpret_cast<const f32x4*>(kb + c * (16 / LY::ES));
+      for (int c = 0; c < 16 * LY::ES / 16; ++c)
         *reinterpret_cast<f32x4*>(kdt + c * (16 / LY::ES)) = *reinterpret_cast<const f32x4*>(kd + c * (16 / LY::ES));
-      }
     }
     __syncthreads();
     return s.Flag[0] != 0;
   }
 
   // -------------------------------------------------------------- Grams A, P
+  // A (fp32) lands over the Qx/Ky region once every wave is done with them.
+  // Ends with a barrier.
   __device__ static void grams(const Smem& s, const Rows<E>& src, int t0, int nvalid, bool fallback,
                                const Sink<E>& out) {
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     const int gq = lane >> 4, cc = lane & 15;
-    constexpr int NPAIR = NB * (NB + 1) / 2;
-    for (int pr = wave; pr < NPAIR; pr += NW) {
-      int I = 0, J = pr;
-      while (J > I) { J -= I + 1; ++I; }
-      const bool diag = (I == J);
-      f32x4 accA = zero4(), accP = zero4();
+    constexpr int TPW = (NB * NB + NW - 1) / NW;     // tiles per wave
+    f32x4 accA[TPW];
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      accA[k] = zero4();
+      const int tile = wave + k * NW;
+      if (tile >= NB * NB) continue;
+      const int I = tile / NB, J = tile % NB;
+      if (J > I) {                                   // above the diagonal: P is zero
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out.P[(16 * I + 4 * gq + i) * out.ldP + 16 * J + cc] = from_f32<E>(0.f);
+        continue;
+      }
+      const bool diag = (I == J), far = (J < I - 1);
+      // left factor e^{Gs_I - Ge_J} for far pairs, right factor e^{Gs_J - Ge_J}
+      // on the diagonal; other tiles multiply by ones (no branches)
+      const float* fl = far ? s.Ff + ((I - 2) * (I - 1) / 2 + J) * DK : s.Ones;
+      const float* fr = diag ? s.Fd + J * DK : s.Ones;
+      f32x4 acP = zero4();
+      Frag ka[DK / KS], qa[DK / KS], kb[DK / KS];
 #pragma unroll
       for (int p = 0; p < DK / KS; ++p) {
-        Frag ka = MM::ld_nat(s.Kx, LD, 16 * I + cc, p * KS);
-        Frag qa = MM::ld_nat(s.Qx, LD, 16 * I + cc, p * KS);
-        Frag kb = MM::ld_nat(s.Ky, LD, 16 * J + cc, p * KS);
-        if constexpr (KS == 32) {
+        ka[p] = MM::ld_nat(s.Kx, LD, 16 * I + cc, p * KS);
+        qa[p] = MM::ld_nat(s.Qx, LD, 16 * I + cc, p * KS);
+        kb[p] = MM::ld_nat(s.Ky, LD, 16 * J + cc, p * KS);
+      }
 #pragma unroll
-          for (int sl = 0; sl < 8; ++sl) {
-            const int kk = p * KS + 8 * gq + sl;
-            if (J < I - 1) {                          // left factor e^{Gs_I - Ge_J}
-              const float f = fast_exp2(s.Gb[I * DK + kk] - s.Gb[(J + 1) * DK + kk]);
-              ka[sl] = (bf16)((float)ka[sl] * f);
-              qa[sl] = (bf16)((float)qa[sl] * f);
-            }
-            if (diag)                                 // right factor e^{Gs_J - Ge_J}
-              kb[sl] = (bf16)((float)kb[sl] * fast_exp2(s.Gb[J * DK + kk] - s.Gb[(J + 1) * DK + kk]));
-          }
-        } else {
-          const int kk = p * KS + gq;
-          if (J < I - 1) {
-            const float f = fast_exp2(s.Gb[I * DK + kk] - s.Gb[(J + 1) * DK + kk]);
-            ka = ka * f;
-            qa = qa * f;
-          }
-          if (diag) kb = kb * fast_exp2(s.Gb[J * DK + kk] - s.Gb[(J + 1) * DK + kk]);
-        }
-        accA = MM::mma(ka, kb, accA);
-        accP = MM::mma(qa, kb, accP);
+      for (int p = 0; p < DK / KS; ++p) {
+        const Frag a = FragScale<E>::apply(ka[p], fl, p * KS);
+        const Frag aq = FragScale<E>::apply(qa[p], fl, p * KS);
+        const Frag b = FragScale<E>::apply(kb[p], fr, p * KS);
+        accA[k] = MM::mma(a, b, accA[k]);
+        acP = MM::mma(aq, b, acP);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * I + 4 * gq + i, j = 16 * J + cc;
         const bool keep = !diag || (j < r);
-        s.A[r * LA + j] = keep ? accA[i] : 0.f;
-        out.P[r * out.ldP + j] = from_f32<E>(keep ? accP[i] : 0.f);
+        accA[k][i] = keep ? accA[k][i] : 0.f;
+        out.P[r * out.ldP + j] = from_f32<E>(keep ? acP[i] : 0.f);
       }
     }
-    // P blocks above the diagonal and the padding columns are zero
-    for (int idx = tid; idx < BL * KP; idx += NT) {
-      const int r = idx / KP, j = idx % KP;
-      if (j >= 16 * (r / 16 + 1)) out.P[r * out.ldP + j] = from_f32<E>(0.f);
+    // padding columns of P (only when BL < KP)
+    if constexpr (BL < KP)
+      for (int idx = tid; idx < BL * (KP - BL); idx += NT)
+        out.P[(idx / (KP - BL)) * out.ldP + BL + idx % (KP - BL)] = from_f32<E>(0.f);
+    __syncthreads();                                 // Qx/Ky are free now
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      const int tile = wave + k * NW;
+      if (tile >= NB * NB) continue;
+      const int I = tile / NB, J = tile % NB;
+      if (J > I) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s.A[(16 * I + 4 * gq + i) * LA + 16 * J + cc] = accA[k][i];
     }
     __syncthreads();
-    if (fallback) grams_pairwise(s, src, t0, nvalid, out);
+    if (fallback) {
+      grams_pairwise(s, src, t0, nvalid, out);
+      __syncthreads();
+    }
   }
 
-  // Diagonal sub-blocks rebuilt pairwise from the raw gates: only for decays
-  // too steep for the factorised form; slow but exact.
+  // Diagonal sub-blocks rebuilt pairwise, straight from the raw gates in
+  // global memory: used only for decays too steep for the factorised form.
+  // Slow but exact; needs no LDS scratch.
   __device__ static void grams_pairwise(const Smem& s, const Rows<E>& src, int t0, int nvalid,
                                         const Sink<E>& out) {
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int gs = tid / DK, gd = tid % DK;
-    float* accA = reinterpret_cast<float*>(s.base + LY::oKx);       // [NB][16][16]
-    float* accP = accA + NB * 256;
-    for (int i = tid; i < NB * 512; i += NT) accA[i] = 0.f;
-    __syncthreads();
-    if (gs < NB) {
-      const float z = s.Z[gd];
-      auto off_of = [&](int r) { return src.row(t0 + r) * DK + gd; };
-      float* Gloc = reinterpret_cast<float*>(s.base + LY::oQx) + gd;  // dead Qx region
-      float run = 0.f;
-      for (int i = 0; i < 16; ++i) {
-        const int r = 16 * gs + i;
-        run += (r < nvalid) ? ldg(src.G, off_of(r)) * kLog2e : 0.f;
-        Gloc[(16 * gs + i) * DK] = run;
-      }
-      for (int ri = 1; ri < 16; ++ri) {
-        const int r = 16 * gs + ri;
-        float kr = 0.f, qr = 0.f, br = 0.f;
-        if (r < nvalid) {
-          kr = ldg(src.K, off_of(r));
-          qr = ldg(src.Q, off_of(r));
-          br = sigmoid_f(ldg(src.BX, off_of(r)) + z);
-        }
-        for (int ji = 0; ji < ri; ++ji) {
-          const int j = 16 * gs + ji;
-          const float kj = (j < nvalid) ? ldg(src.K, off_of(j)) : 0.f;
-          const float Gr = Gloc[(16 * gs + ri) * DK], Gj = Gloc[(16 * gs + ji) * DK];
-          const float Gp = Gloc[(16 * gs + ri - 1) * DK];
-          float ca = br * kr * kj * fast_exp2(Gr - Gj);
-          float cp = qr * kj * fast_exp2(Gp - Gj);
-          for (int off = 32; off >= 1; off >>= 1) {
-            ca += __shfl_xor(ca, off);
-            cp += __shfl_xor(cp, off);
-          }
-          if (lane == 0) {
-            atomicAdd(&accA[gs * 256 + ri * 16 + ji], ca);
-            atomicAdd(&accP[gs * 256 + ri * 16 + ji], cp);
-          }
+    for (int item = threadIdx.x; item < NB * 120; item += NT) {
+      const int I = item / 120;
+      int p = item % 120, ri = 1;
+      while (p >= ri) { p -= ri; ++ri; }
+      const int ji = p;
+      const int r = 16 * I + ri, j = 16 * I + ji;
+      float sa = 0.f, sp = 0.f;
+      if (r < nvalid) {
+        const size_t rowr = src.row(t0 + r) * DK, rowj = src.row(t0 + j) * DK;
+        for (int d = 0; d < DK; ++d) {
+          float dg = 0.f;                          // G_{r-1} - G_j, log2 units
+          for (int t = j + 1; t < r; ++t) dg += ldg(src.G, src.row(t0 + t) * DK + d) * kLog2e;
+          const float gr = ldg(src.G, rowr + d) * kLog2e;
+          const float kj = ldg(src.K, rowj + d);
+          const float br = sigmoid_f(ldg(src.BX, rowr + d) + s.Z[d]);
+          sa += br * ldg(src.K, rowr + d) * kj * fast_exp2(dg + gr);
+          sp += ldg(src.Q, rowr + d) * kj * fast_exp2(dg);
         }
       }
+      s.A[r * LA + j] = sa;
+      out.P[r * out.ldP + j] = from_f32<E>(sp);
     }
-    __syncthreads();
-    for (int i = tid; i < NB * 256; i += NT) {
-      const int sb = i / 256, ri = (i / 16) % 16, ji = i % 16;
-      const int r = 16 * sb + ri, j = 16 * sb + ji;
-      s.A[r * LA + j] = (ji < ri) ? accA[i] : 0.f;
-      out.P[r * out.ldP + j] = from_f32<E>((ji < ri) ? accP[i] : 0.f);
+  }
+
+  // -------------------------------------------------------------- (I + A_II)^{-1}
+  // Diagonal 16x16 blocks by forward substitution in fp32. Wave 0, lane
+  // (block ib = gq, column c = cc) keeps its whole column in registers.
+  // Ends with a barrier.
+  __device__ static void inverse_diag(const Smem& s) {
+    const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
+    const int ib = lane >> 4, c = lane & 15;
+    if (wave == 0 && ib < NB) {
+      const float* Ablk = s.A + (16 * ib) * LA + 16 * ib;
+      float t[16];
+      float cur[16], nxt[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) *reinterpret_cast<f32x4*>(cur + 4 * q4) = *reinterpret_cast<const f32x4*>(Ablk + LA + 4 * q4);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (r >= 1 && r + 1 < 16) {                    // fetch row r+1 while row r is reduced
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            if (4 * q4 < r + 1) *reinterpret_cast<f32x4*>(nxt + 4 * q4) = *reinterpret_cast<const f32x4*>(Ablk + (r + 1) * LA + 4 * q4);
+        }
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < r; ++j) acc += cur[j] * t[j];
+        t[r] = (r == c) ? 1.f : ((r > c) ? -acc : 0.f);
+        if (r >= 1 && r + 1 < 16) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) cur[j] = nxt[j];
+        }
+      }
+      float* Tb = s.Td + ib * 16 * LTD;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Tb[r * LTD + c] = t[r];
     }
     __syncthreads();
   }
 
-  // -------------------------------------------------------------- T = (I + A)^{-1}
-  __device__ static void inverse(const Smem& s) {
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // -------------------------------------------------------------- [W | U] = (I + A)^{-1} [Kb | w V]
+  // Blocked forward substitution over 16-row sub-blocks:
+  //   X_I = T_II (R_I - sum_{J<I} A_IJ X_J),  R = [b k e^{G} | w v],
+  // with T_II the diagonal inverses. Wave w solves the two 16-column tiles
+  // 2w, 2w+1 of [W | U] (DK + DV = 32 NW columns) independently, keeping its
+  // X_J tiles in registers. W goes to the sink, U (rounded to E) overwrites
+  // the value tile in place. Ends with a barrier.
+  __device__ static void solve(const Smem& s, const Sink<E>& out) {
+    const int wave = wave_id(), lane = threadIdx.x & 63;
     const int gq = lane >> 4, cc = lane & 15;
-    // diagonal 16x16 blocks by forward substitution (fp32): wave 0, lane
-    // (block ib = gq, column c = cc) keeps its whole column in registers
-    if (wave == 0) {
-      const int ib = gq, c = cc;
-      if (ib < NB) {
-        const float* Ablk = s.A + (16 * ib) * LA + 16 * ib;
-        float t[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float acc = 0.f;
-#pragma unroll
-          for (int j = 0; j < r; ++j) acc += Ablk[r * LA + j] * t[j];
-          t[r] = (r == c) ? 1.f : ((r > c) ? -acc : 0.f);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s.T[(16 * ib + r) * LT + 16 * ib + c] = t[r];
-      }
-    }
-    // zero every row block right of its diagonal block (upper blocks, padding)
-    for (int idx = tid; idx < BL * KP; idx += NT) {
-      const int r = idx / KP, j = idx % KP;
-      if (j >= 16 * (r / 16 + 1)) s.T[r * LT + j] = 0.f;
-    }
-    __syncthreads();
-    // off-diagonal blocks: wave J walks its block column downwards,
-    // T_IJ = -T_II sum_{J<=K<I} A_IK T_KJ, keeping T_KJ as C tiles
-    if (NB > 1 && wave < NB - 1) {
-      const int J = wave;
-      f32x4 Tc[NB];
-#pragma unroll
-      for (int I = 0; I < NB; ++I) Tc[I] = zero4();
+    // operands that do not depend on the recursion, loaded up front:
+    // right-hand sides R (C layout), A_IJ rows and T_II rows (fp32)
+    // both column tiles of a wave lie on the same side of [W | U]
+    const bool isW = 2 * wave < DK / 16;
+    const int col0 = 32 * wave - (isW ? 0 : DK) + cc;
+    f32x4 R[NB][2];
+    if (isW) {
 #pragma unroll
       for (int I = 0; I < NB; ++I)
-        if (I == J)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) Tc[I][i] = s.T[(16 * J + 4 * gq + i) * LT + 16 * J + cc];
-#pragma unroll
-      for (int I = 1; I < NB; ++I) {
-        if (I <= J) continue;
-        f32x4 X = zero4();
-#pragma unroll
-        for (int Kb = 0; Kb < NB; ++Kb)
-          if (Kb >= J && Kb < I) X = Mma16<E>::mma_rowA_cB(s.A, LA, 16 * I + cc, 16 * Kb, Tc[Kb], X, 1.f);
-        Tc[I] = Mma16<E>::mma_rowA_cB(s.T, LT, 16 * I + cc, 16 * I, X, zero4(), -1.f);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s.T[(16 * I + 4 * gq + i) * LT + 16 * J + cc] = Tc[I][i];
-      }
-    }
-    __syncthreads();
-  }
-
-  // -------------------------------------------------------------- W = T (b k e^{G})
-  // Ends with a barrier.
-  __device__ static void build_w(const Smem& s, const Sink<E>& out) {
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int gq = lane >> 4, cc = lane & 15;
-    constexpr int NTILE = NB * (DK / 16);
-    for (int tt = wave; tt < NTILE; tt += NW) {
-      const int I = tt / (DK / 16), dt = tt % (DK / 16);
-      f32x4 acc = zero4();
-      const int nst = MM::steps(16 * (I + 1));
-      for (int p = 0; p < nst; ++p)
-        acc = MM::mma(MM::ld_nat(s.T, LT, 16 * I + cc, p * KS), MM::ld_nat(s.KbT, LK, 16 * dt + cc, p * KS), acc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) out.W[(16 * I + 4 * gq + i) * out.ldW + 16 * dt + cc] = from_f32<E>(acc[i]);
-    }
-    __syncthreads();
-  }
-
-  // -------------------------------------------------------------- U = T diag(w) V
-  // Per wave, channels [16 wave, 16 wave + 16); values rounded to E so every
-  // schedule feeds the state pass identical operands. The value operand is
-  // gathered from the row-major V tile with the c-pair map.
-  __device__ static void build_u(const Smem& s, f32x4 (&U)[NB]) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int gq = lane >> 4, cc = lane & 15;
-    const int e0 = 16 * wave;
-#pragma unroll
-    for (int rt = 0; rt < NB; ++rt) {
-      f32x4 u = zero4();
-#pragma unroll
-      for (int p = 0; p < MM::steps(BL); ++p) {
-        if (p >= MM::steps(16 * (rt + 1))) break;
-        Frag ta, vb;
-        if constexpr (KS == 32) {
-          const float* tr = s.T + (16 * rt + cc) * LT + 32 * p + 4 * gq;
-          const f32x4 t0 = *reinterpret_cast<const f32x4*>(tr);
-          const f32x4 t1 = *reinterpret_cast<const f32x4*>(tr + 16);
-          const float* wg = s.Wg + 32 * p + 4 * gq;
-          const f32x4 w0 = *reinterpret_cast<const f32x4*>(wg);
-          const f32x4 w1 = *reinterpret_cast<const f32x4*>(wg + 16);
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            ta[i] = (bf16)(t0[i] * w0[i]);
-            ta[4 + i] = (bf16)(t1[i] * w1[i]);
-            vb[i] = s.V[(32 * p + 4 * gq + i) * LV + e0 + cc];
-            vb[4 + i] = s.V[(32 * p + 16 + 4 * gq + i) * LV + e0 + cc];
+            const int r = 16 * I + 4 * gq + i, c = col0 + 16 * t;
+            R[I][t][i] = to_f32(s.Kx[r * LD + c]) * s.EGs[I * DK + c];   // b k e^{G_r}
           }
-        } else {
-          const int k = 16 * (p >> 2) + 4 * gq + (p & 3);
-          ta = s.T[(16 * rt + cc) * LT + k] * s.Wg[k];
-          vb = s.V[k * LV + e0 + cc];
-        }
-        u = MM::mma(ta, vb, u);
-      }
+    } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) u[i] = to_f32(from_f32<E>(u[i]));
-      U[rt] = u;
+      for (int I = 0; I < NB; ++I)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 16 * I + 4 * gq + i, c = col0 + 16 * t;
+            R[I][t][i] = s.Wg[r] * to_f32(s.V[r * LV + c]);              // w v
+          }
     }
+    f32x4 Arow[NB > 1 ? NB * (NB - 1) / 2 : 1], Trow[NB];
+#pragma unroll
+    for (int I = 0; I < NB; ++I) {
+      Trow[I] = *reinterpret_cast<const f32x4*>(s.Td + I * 16 * LTD + cc * LTD + 4 * gq);
+#pragma unroll
+      for (int J = 0; J < I; ++J)
+        Arow[I * (I - 1) / 2 + J] = *reinterpret_cast<const f32x4*>(s.A + (16 * I + cc) * LA + 16 * J + 4 * gq);
+    }
+    f32x4 X[NB][2];
+#pragma unroll
+    for (int I = 0; I < NB; ++I) {
+      f32x4 acc[2] = {R[I][0], R[I][1]};
+#pragma unroll
+      for (int J = 0; J < I; ++J)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) acc[t] = Mma16<E>::mma_a_cB(Arow[I * (I - 1) / 2 + J], X[J][t], acc[t], -1.f);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        f32x4 x = Mma16<E>::mma_a_cB(Trow[I], acc[t], zero4(), 1.f);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = to_f32(from_f32<E>(x[i]));
+        X[I][t] = x;
+      }
+    }
+    if (isW) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int I = 0; I < NB; ++I)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            out.W[(16 * I + 4 * gq + i) * out.ldW + col0 + 16 * t] = from_f32<E>(X[I][t][i]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int I = 0; I < NB; ++I)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            s.V[(16 * I + 4 * gq + i) * LV + col0 + 16 * t] = from_f32<E>(X[I][t][i]);
+    }
+    __syncthreads();
+  }
+
+  // U tiles of this wave's 16 value channels, from the value tile after solve()
+  __device__ static void load_u(const Smem& s, f32x4 (&U)[NB]) {
+    const int wave = wave_id(), lane = threadIdx.x & 63;
+    const int gq = lane >> 4, cc = lane & 15;
+#pragma unroll
+    for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) U[rt][i] = to_f32(s.V[(16 * rt + 4 * gq + i) * LV + 16 * wave + cc]);
   }
 
   // -------------------------------------------------------------- state and output
@@ -567,7 +603,7 @@ struct Block {
 
   // load/store S^T C tiles of this wave from/to a [B,H,DV,DK] fp32 tensor
   __device__ static void load_state(const float* S, int bh, f32x4 (&St)[DK / 16]) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = wave_id(), lane = threadIdx.x & 63;
     const int gq = lane >> 4, cc = lane & 15;
 #pragma unroll
     for (int dt = 0; dt < DK / 16; ++dt) {
@@ -576,7 +612,7 @@ struct Block {
     }
   }
   __device__ static void store_state(float* S, int bh, const f32x4 (&St)[DK / 16]) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = wave_id(), lane = threadIdx.x & 63;
     const int gq = lane >> 4, cc = lane & 15;
 #pragma unroll
     for (int dt = 0; dt < DK / 16; ++dt)

@@ -26,6 +26,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+// wave index as a scalar: lets the compiler treat per-wave decisions as
+// uniform branches instead of exec-masked divergent code
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
@@ -103,13 +106,12 @@ template <> struct Mma<float> {
 
 // 16x16x16 product whose B operand is one C tile (bf16: one instruction with
 // the natural 4-slot map, which coincides with the C layout; f32: four
-// 16x16x4 instructions). A is read from a row-major fp32 tile.
+// 16x16x4 instructions). The A operand is a lane's 4 fp32 values of row c,
+// k = 4g + i.
 template <typename M> struct Mma16;
 template <> struct Mma16<bf16> {
-  __device__ __forceinline__ static f32x4 mma_rowA_cB(const float* A, int lda, int row, int k0,
-                                                      f32x4 b, f32x4 c, float sign) {
-    const int g = lane_id() >> 4;
-    f32x4 a = *reinterpret_cast<const f32x4*>(A + row * lda + k0 + 4 * g);
+  // A operand given as 4 fp32 values (row c, k = 4g + i), B from a C tile
+  __device__ __forceinline__ static f32x4 mma_a_cB(f32x4 a, f32x4 b, f32x4 c, float sign) {
     typedef short s4 __attribute__((ext_vector_type(4)));
     bf16x4 av{(bf16)(sign * a[0]), (bf16)(sign * a[1]), (bf16)(sign * a[2]), (bf16)(sign * a[3])};
     bf16x4 bv{(bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
@@ -118,10 +120,7 @@ template <> struct Mma16<bf16> {
   }
 };
 template <> struct Mma16<float> {
-  __device__ __forceinline__ static f32x4 mma_rowA_cB(const float* A, int lda, int row, int k0,
-                                                      f32x4 b, f32x4 c, float sign) {
-    const int g = lane_id() >> 4;
-    const float* a = A + row * lda + k0 + 4 * g;
+  __device__ __forceinline__ static f32x4 mma_a_cB(f32x4 a, f32x4 b, f32x4 c, float sign) {
 #pragma unroll
     for (int p = 0; p < 4; ++p)
       c = __builtin_amdgcn_mfma_f32_16x16x4f32(sign * a[p], b[p], c, 0, 0, 0);

@@ -28,7 +28,7 @@ carve_chunk_serial_kernel(FwdArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const auto s = B::carve(smem);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int gq = lane >> 4, cc = lane & 15;
   const int bh = blockIdx.x;
   Rows<E> src{static_cast<const E*>(a.q), static_cast<const E*>(a.k), static_cast<const E*>(a.v),
@@ -75,10 +75,10 @@ carve_chunk_serial_kernel(FwdArgs a) {
     const int nvalid = min(BL, T - t0);
     const bool fallback = B::gate_pass(s, src, t0, nvalid, sink);
     B::grams(s, src, t0, nvalid, fallback, sink);
-    B::inverse(s);
-    B::build_w(s, sink);
+    B::inverse_diag(s);
+    B::solve(s, sink);
     f32x4 U[NB], Ot[NB];
-    B::build_u(s, U);
+    B::load_u(s, U);
     B::state_step(s.W, s.Qd, s.P, s.KdT, s.Egl, U, St, Ot);
 #pragma unroll
     for (int rt = 0; rt < NB; ++rt)
@@ -127,40 +127,41 @@ carve_intra_kernel(FwdArgs a) {
   unsigned char* img = static_cast<unsigned char*>(a.ws) + ((size_t)bh * nblk + blk) * LY::wBytes;
   const Sink<E> sink = B::image_sink(img);
 
-  B::zero_lds(smem, LY::intra_bytes);   // z = 0: no content projection
+  for (int d = threadIdx.x; d < DK; d += NT) s.Z[d] = 0.f;   // no content projection
   __syncthreads();
   const bool fallback = B::gate_pass(s, src, t0, nvalid, sink);
   B::grams(s, src, t0, nvalid, fallback, sink);
-  B::inverse(s);
-  B::build_w(s, sink);
-  f32x4 U[NB];
-  B::build_u(s, U);
+  B::inverse_diag(s);
+  B::solve(s, sink);
 
+  // U (in the value tile) and e^{G_BL} to the image, 16-byte chunks
   for (int i = threadIdx.x; i < DK; i += NT) reinterpret_cast<float*>(img + LY::wEgl)[i] = s.Egl[i];
-  E* Ui = reinterpret_cast<E*>(img + LY::wU);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int gq = lane >> 4, cc = lane & 15;
-#pragma unroll
-  for (int rt = 0; rt < NB; ++rt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) Ui[(16 * rt + 4 * gq + i) * DV + 16 * wave + cc] = from_f32<E>(U[rt][i]);
+  constexpr int CPR = DV * LY::ES / 16;
+  for (int c = threadIdx.x; c < BL * CPR; c += NT) {
+    const int r = c / CPR, k = c % CPR;
+    *reinterpret_cast<f32x4*>(img + LY::wU + (r * DV) * LY::ES + 16 * k) =
+        *reinterpret_cast<const f32x4*>(s.V + r * LY::LV + k * (16 / LY::ES));
+  }
 }
 
 // One workgroup per (batch, head): the serial state pass and the output.
-// Block images stream through two LDS buffers; the next one is fetched into
-// registers while the current one is used.
+// Block images stream through two LDS buffers (the next one is fetched into
+// registers while the current one is used). Outputs are staged in the U
+// region of the current buffer (U is in registers by then) and written as
+// 16-byte row chunks.
 template <typename E, int DK, int DV, int BL>
 __global__ void __launch_bounds__((BlockLayout<E, DK, DV, BL>::NT))
 carve_state_kernel(FwdArgs a) {
   using B = Block<E, DK, DV, BL>;
   using LY = typename B::LY;
-  constexpr int NT = LY::NT, NB = LY::NB;
+  constexpr int NT = LY::NT, NB = LY::NB, ES = LY::ES;
   constexpr int CH = LY::wBytes / 16;                 // 16-byte chunks per image
   constexpr int PER = (CH + NT - 1) / NT;             // chunks per thread
-  static_assert(2 * LY::sBytes <= 160 * 1024, "two staging buffers fit");
+  constexpr int OCPR = DV * ES / 16;                  // output chunks per row
+  static_assert(2 * LY::sBytes <= 160 * 1024, "staging buffers fit");
   extern __shared__ __align__(16) unsigned char smem[];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int gq = lane >> 4, cc = lane & 15;
   const int bh = blockIdx.x;
   const int T = a.T, H = a.H, L = a.L;
@@ -215,14 +216,22 @@ carve_state_kernel(FwdArgs a) {
     B::state_step(Wm, Qd, Pm, KdT, Egl, U, St, Ot);
     const int t0 = blk * BL;
     const int nvalid = min(BL, T - t0);
+    E* so = const_cast<E*>(Ui);                      // [BL][DV], U already in registers
+    __syncthreads();                                 // every wave has read its U
 #pragma unroll
     for (int rt = 0; rt < NB; ++rt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rt + 4 * gq + i;
         if (t0 + r >= mstart) m_part += Ot[rt][i];   // rows past nvalid are exactly 0
-        if (r < nvalid) O[((size_t)(bidx * T + t0 + r) * H + h) * DV + e0 + cc] = from_f32<E>(Ot[rt][i]);
+        so[r * DV + e0 + cc] = from_f32<E>(Ot[rt][i]);
       }
+    __syncthreads();
+    for (int c = tid; c < nvalid * OCPR; c += NT) {
+      const int r = c / OCPR, k = c % OCPR;
+      *reinterpret_cast<f32x4*>(O + ((size_t)(bidx * T + t0 + r) * H + h) * DV + k * (16 / ES)) =
+          *reinterpret_cast<const f32x4*>(so + r * DV + k * (16 / ES));
+    }
     if (blk + 1 < nblk) deposit(cur ^ 1);
     __syncthreads();
   }
