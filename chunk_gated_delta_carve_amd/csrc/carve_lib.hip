@@ -41,7 +41,7 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 // block length used by the chunk-serial kernel: divides L, fits LDS
 int serial_block(const carve_config* c) {
   int bl = c->L < 64 ? c->L : 64;
-  if (c->dtype == CARVE_F32 && c->dk == 128 && bl > 32) bl = 32;
+  if (c->dtype == CARVE_F32 && c->dk == 128) bl = 16;
   return bl;
 }
 
@@ -98,7 +98,9 @@ template <typename E, int D>
 hipError_t dispatch_block(const carve::FwdArgs& a, int bl, hipStream_t s) {
   switch (bl) {
     case 16: return launch_serial<E, D, 16>(a, s);
-    case 32: return launch_serial<E, D, 32>(a, s);
+    case 32:
+      if constexpr (sizeof(E) == 4 && D == 128) return hipErrorInvalidValue;
+      else return launch_serial<E, D, 32>(a, s);
     default:
       if constexpr (sizeof(E) == 4 && D == 128) return hipErrorInvalidValue;
       else return launch_serial<E, D, 64>(a, s);

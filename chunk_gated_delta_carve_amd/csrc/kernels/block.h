@@ -7,14 +7,19 @@
 // Reuse"; §2.2 scalar write gate; §2.3 key-axis decay):
 //   A_rj  = sum_d b_r k_r k_j e^{G_r - G_j}          (j < r)
 //   P_rj  = sum_d q_r k_j e^{G_{r-1} - G_j}          (j < r)
-//   T     = (I + A)^{-1}
-//   W     = T (b k e^{G_r}),   U = T (w v)
+//   [W | U] = (I + A)^{-1} [b k e^{G_r} | w v]       (WY form)
 //   Delta = U - W S^T
 //   O     = (q e^{G_{r-1}}) S^T + P Delta           (o_t = S_{t-1} q_t)
-//   S    <- S diag(e^{G_BL}) + Delta^T (k e^{G_BL - G_j})
+//   S    <- S diag(e^{G_BL}) + Delta^T Kdec,  Kdec_j = k_j e^{G_BL - G_j}
 // This is exact algebra for the token recurrence S <- S D (I - (b k) k^T) +
 // w v k^T; one triangular system per block exists because every gate acts on
 // the key axis (Theorem 11, §3 of the same summary).
+//
+// The state pass only needs the block's affine map S <- S M + C and the
+// output map O = Qe S^T + Ol, with
+//   M  = diag(e^{G_BL}) - W^T Kdec    C  = U^T Kdec
+//   Qe = Qd - P W                     Ol = P U          (Qd_r = q_r e^{G_{r-1}})
+// so each block hands M^T, C^T, Qe and Ol to the state pass.
 //
 // Exponent safety: the Grams use 16-row sub-blocks. For sub-blocks I > J the
 // factor e^{G_r - G_j} is split as e^{G_r - Gs_I} e^{Gs_I - Ge_J} e^{Ge_J - G_j}
@@ -41,6 +46,8 @@ struct FwdArgs {
 
 constexpr float kSpanLimit2 = 96.0f;   // max decay (log2 units) inside a 16-row sub-block
 
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
 template <typename E, int DK, int DV, int BL>
 struct BlockLayout {
   static_assert(DK % 32 == 0 && DV % 16 == 0 && DK == DV, "head widths");
@@ -54,67 +61,78 @@ struct BlockLayout {
   static constexpr int PE = 16 / ES;                 // 16-byte row padding, in elements
   static constexpr int LD = DK + PE;                 // pitch of [.][DK] tiles
   static constexpr int LK = KP + PE;                 // pitch of [.][KP] tiles
-  static constexpr int LV = DV + PE;                 // pitch of the value tile
+  static constexpr int LV = DV + PE;                 // pitch of [.][DV] tiles
   static constexpr int LA = BL + 4;                  // pitch of A (fp32)
-  static constexpr int LTD = 16 + 4;                 // pitch of the diagonal inverses (fp32)
+  static constexpr int LTD = 16 + PE;                // pitch of the diagonal inverses (E)
   static constexpr int NFAR = NB > 2 ? (NB - 1) * (NB - 2) / 2 : 1;   // sub-block pairs J < I-1
 
-  // LDS byte offsets. Small arrays first, then tiles; the chunk-parallel
-  // kernel stops at intra_bytes, the chunk-serial kernel also keeps the
-  // state-pass operands Qd, KdT, P, W.
-  static constexpr int oGb = 0;                              // [NB+1][DK] f32 (log2 units)
-  static constexpr int oSeg = oGb + (NB + 1) * DK * 4;       // [NB][DK] f32
-  static constexpr int oEgl = oSeg + NB * DK * 4;            // [DK] f32 e^{G_BL}
+  // ---- LDS. Persistent small arrays, then regions whose contents change
+  // once their first occupant is dead:
+  //   RB: Gb, Seg, Fd, Ff (gate pass -> Grams), then Td (inverse -> solve)
+  //   R1: Kx (gate -> solve), then Wt = W^T (solve -> affine)
+  //   R2: Qx, Ky (gate -> Grams), then A (Grams -> solve), then Qd, P (-> affine)
+  //   R3: V (gate -> solve), then Ut = U^T (solve -> affine)
+  //   R4: KdT = Kdec^T (gate -> affine)
+  // The chunk-serial kernel also keeps Mt and Qe (C^T and Ol stay in the
+  // registers of the wave that owns their value channels).
+  static constexpr int oEgl = 0;                             // [DK] f32 e^{G_BL}
   static constexpr int oEGs = oEgl + DK * 4;                 // [NB][DK] f32 e^{Gs_I}
   static constexpr int oWg = oEGs + NB * DK * 4;             // [KP] f32 write gate (zero padded)
   static constexpr int oZ = oWg + KP * 4;                    // [DK] f32
   static constexpr int oM = oZ + DK * 4;                     // [DV] f32
   static constexpr int oY = oM + DV * 4;                     // [64] f32
-  static constexpr int oFlag = oY + 64 * 4;                  // int
-  static constexpr int oFd = oFlag + 16;                     // [NB][DK] f32 e^{Gs_J - Ge_J}
+  static constexpr int oOnes = oY + 64 * 4;                  // [DK] f32 all ones
+  static constexpr int oFlag = oOnes + DK * 4;               // int
+  static constexpr int oRB = oFlag + 16;
+  static constexpr int oGb = oRB;                            // [NB+1][DK] f32 (log2 units)
+  static constexpr int oSeg = oGb + (NB + 1) * DK * 4;       // [NB][DK] f32
+  static constexpr int oFd = oSeg + NB * DK * 4;             // [NB][DK] f32 e^{Gs_J - Ge_J}
   static constexpr int oFf = oFd + NB * DK * 4;              // [NFAR][DK] f32 e^{Gs_I - Ge_J}
-  static constexpr int oOnes = oFf + NFAR * DK * 4;          // [DK] f32 all ones
-  static constexpr int oKx = oOnes + DK * 4;                 // [BL][LD] E
-  static constexpr int oQx = oKx + BL * LD * ES;             // [BL][LD] E   (then A, fp32)
-  static constexpr int oKy = oQx + BL * LD * ES;             // [BL][LD] E
-  static constexpr int oV = oKy + BL * LD * ES;              // [KP][LV] E   (then U; rows >= BL stay 0)
-  static constexpr int oTd = oV + KP * LV * ES;              // [NB][16][LTD] f32
-  static constexpr int intra_bytes = oTd + NB * 16 * LTD * 4;
-  static constexpr int oQd = intra_bytes;                    // [BL][LD] E
-  static constexpr int oKdT = oQd + BL * LD * ES;            // [DK][LK] E
-  static constexpr int oP = oKdT + DK * LK * ES;             // [BL][LK] E
-  static constexpr int oW = oP + BL * LK * ES;               // [BL][LD] E
-  static constexpr int serial_bytes = oW + BL * LD * ES;
-  static_assert(2 * BL * LD * ES >= BL * LA * 4, "A fits in the Qx/Ky region");
+  static constexpr int oTd = oRB;                            // [NB][16][LTD] E
+  static constexpr int szRB = cmax((2 * NB + 1) * DK * 4 + NB * DK * 4 + NFAR * DK * 4, NB * 16 * LTD * ES);
+  static constexpr int oR1 = oRB + (szRB + 15) / 16 * 16;
+  static constexpr int szR1 = cmax(BL * LD * ES, DK * LK * ES);
+  static constexpr int oR2 = oR1 + szR1;
+  static constexpr int szR2 = cmax(cmax(2 * BL * LD * ES, BL * LA * 4), BL * LD * ES + BL * LK * ES);
+  static constexpr int oR3 = oR2 + szR2;
+  static constexpr int szR3 = cmax(KP * LV * ES, DV * LK * ES);
+  static constexpr int oR4 = oR3 + szR3;
+  static constexpr int intra_bytes = oR4 + DK * LK * ES;
+  static constexpr int oKx = oR1, oWt = oR1;
+  static constexpr int oQx = oR2, oKy = oR2 + BL * LD * ES, oA = oR2;
+  static constexpr int oQd = oR2, oP = oR2 + BL * LD * ES;
+  static constexpr int oV = oR3, oUt = oR3;                  // V is [KP][LV] (rows >= BL stay 0)
+  static constexpr int oKdT = oR4;
+  static constexpr int oMt = intra_bytes;                    // [DK][LD] E   (chunk-serial only)
+  static constexpr int oQe = oMt + DK * LD * ES;             // [BL][LD] E
+  static constexpr int serial_bytes = oQe + BL * LD * ES;
   static_assert(serial_bytes <= 160 * 1024, "LDS budget");
-  static_assert(oKx % 16 == 0 && oV % 16 == 0 && oTd % 16 == 0, "tile alignment");
+  static_assert(oR1 % 16 == 0 && oR2 % 16 == 0 && oR3 % 16 == 0 && oR4 % 16 == 0 && oMt % 16 == 0, "alignment");
+  static_assert(NB * 256 * 4 <= DK * LK * ES, "pairwise scratch fits in R4");
 
-  // dense image of one block's state-pass operands (workspace)
-  static constexpr int wW = 0;                               // [BL][DK] E
-  static constexpr int wQd = wW + BL * DK * ES;              // [BL][DK] E
-  static constexpr int wP = wQd + BL * DK * ES;              // [BL][KP] E
-  static constexpr int wKdT = wP + BL * KP * ES;             // [DK][KP] E
-  static constexpr int wU = wKdT + DK * KP * ES;             // [BL][DV] E
-  static constexpr int wEgl = wU + BL * DV * ES;             // [DK] f32
-  static constexpr int wBytes = wEgl + DK * 4;
-  static_assert(wBytes % 16 == 0, "16-byte copies");
-  // padded staging copy of the image in LDS (state pass)
-  static constexpr int sW = 0;                               // [BL][LD]
-  static constexpr int sQd = sW + BL * LD * ES;              // [BL][LD]
-  static constexpr int sP = sQd + BL * LD * ES;              // [BL][LK]
-  static constexpr int sKdT = sP + BL * LK * ES;             // [DK][LK]
-  static constexpr int sU = sKdT + DK * LK * ES;             // [BL][DV] (dense)
-  static constexpr int sEgl = sU + BL * DV * ES;             // [DK] f32
-  static constexpr int sBytes = sEgl + DK * 4;
+  // ---- image of one block's state-pass operands (workspace):
+  //   Mt [DK][DK] and Qe [BL][DK], dense rows, staged through LDS by the
+  //   state pass; Ct and Ol in MFMA fragment order, [wave][tile][lane][4],
+  //   so each wave loads its own C tiles with one 8-byte load per lane.
+  static constexpr int TD = DK / 16;
+  static constexpr int wMt = 0;                              // [DK][DK] E  M^T
+  static constexpr int wQe = wMt + DK * DK * ES;             // [BL][DK] E
+  static constexpr int wCt = wQe + BL * DK * ES;             // [NW][TD][64][4] E  C^T
+  static constexpr int wOl = wCt + NW * TD * 256 * ES;       // [NW][NB][64][4] E
+  static constexpr int wBytes = wOl + NW * NB * 256 * ES;
+  static constexpr int wStaged = wCt;                        // bytes staged through LDS
+  static_assert(wBytes % 16 == 0 && wStaged % 16 == 0, "16-byte copies");
+  // ---- padded staging copy of Mt and Qe in LDS (state pass)
+  static constexpr int sMt = 0;                              // [DK][LD]
+  static constexpr int sQe = sMt + DK * LD * ES;             // [BL][LD]
+  static constexpr int sBytes = sQe + BL * LD * ES;
 
   // LDS offset (relative to a staging buffer) of the 16-byte chunk c of the image
   __device__ __forceinline__ static int stage_offset(int c) {
     const int b = 16 * c;
-    if (b < wQd) return sW + (b / (DK * ES)) * LD * ES + b % (DK * ES);
-    if (b < wP) { const int x = b - wQd; return sQd + (x / (DK * ES)) * LD * ES + x % (DK * ES); }
-    if (b < wKdT) { const int x = b - wP; return sP + (x / (KP * ES)) * LK * ES + x % (KP * ES); }
-    if (b < wU) { const int x = b - wKdT; return sKdT + (x / (KP * ES)) * LK * ES + x % (KP * ES); }
-    return sU + (b - wU);                    // U and Egl are copied densely
+    if (b < wQe) return sMt + (b / (DK * ES)) * LD * ES + b % (DK * ES);
+    const int x = b - wQe;
+    return sQe + (x / (DK * ES)) * LD * ES + x % (DK * ES);
   }
 };
 
@@ -148,14 +166,12 @@ struct Rows {
   __device__ __forceinline__ size_t row(int t) const { return (size_t)(bidx * T + t) * H + h; }
 };
 
-// Where the state-pass operands of a block go: LDS (chunk-serial kernel) or
-// the dense workspace image (chunk-parallel kernel).
+// Where a block's shared affine maps go: LDS (chunk-serial kernel) or the
+// workspace image (chunk-parallel kernel). C^T and Ol stay in registers.
 template <typename E>
 struct Sink {
-  E* Qd; int ldQd;      // [BL][.]
-  E* KdT; int ldKdT;    // [DK][.]
-  E* P; int ldP;        // [BL][.]
-  E* W; int ldW;        // [BL][.]
+  E* Mt; int ldMt;      // [DK][.]
+  E* Qe; int ldQe;      // [BL][.]
 };
 
 template <typename E, int DK, int DV, int BL>
@@ -165,46 +181,47 @@ struct Block {
   using Frag = typename MM::frag;
   static constexpr int NW = LY::NW, NT = LY::NT, NB = LY::NB, KP = LY::KP, KS = MM::KS;
   static constexpr int LD = LY::LD, LK = LY::LK, LV = LY::LV, LA = LY::LA, LTD = LY::LTD;
+  static constexpr int TPW = (NB * NB + NW - 1) / NW;      // Gram tiles per wave
 
   struct Smem {
     unsigned char* base;
-    E *Kx, *Qx, *Ky, *V, *Qd, *KdT, *P, *W;
-    float *A, *Td, *Gb, *Seg, *Egl, *EGs, *Wg, *Z, *M, *Y, *Fd, *Ff, *Ones;
+    E *Kx, *Qx, *Ky, *V, *Td, *Wt, *Ut, *Qd, *P, *KdT, *Mt, *Qe;
+    float *A, *Gb, *Seg, *Egl, *EGs, *Wg, *Z, *M, *Y, *Fd, *Ff, *Ones;
     int* Flag;
   };
 
   __device__ static Smem carve(unsigned char* smem) {
     Smem s;
     s.base = smem;
-    s.Kx = reinterpret_cast<E*>(smem + LY::oKx);
-    s.Qx = reinterpret_cast<E*>(smem + LY::oQx);
-    s.A = reinterpret_cast<float*>(smem + LY::oQx);    // A reuses Qx/Ky after the Grams
-    s.Ky = reinterpret_cast<E*>(smem + LY::oKy);
-    s.V = reinterpret_cast<E*>(smem + LY::oV);
-    s.Td = reinterpret_cast<float*>(smem + LY::oTd);
-    s.Qd = reinterpret_cast<E*>(smem + LY::oQd);
-    s.KdT = reinterpret_cast<E*>(smem + LY::oKdT);
-    s.P = reinterpret_cast<E*>(smem + LY::oP);
-    s.W = reinterpret_cast<E*>(smem + LY::oW);
-    s.Gb = reinterpret_cast<float*>(smem + LY::oGb);
-    s.Seg = reinterpret_cast<float*>(smem + LY::oSeg);
-    s.Egl = reinterpret_cast<float*>(smem + LY::oEgl);
-    s.EGs = reinterpret_cast<float*>(smem + LY::oEGs);
-    s.Wg = reinterpret_cast<float*>(smem + LY::oWg);
-    s.Z = reinterpret_cast<float*>(smem + LY::oZ);
-    s.M = reinterpret_cast<float*>(smem + LY::oM);
-    s.Y = reinterpret_cast<float*>(smem + LY::oY);
+    auto e = [&](int o) { return reinterpret_cast<E*>(smem + o); };
+    auto f = [&](int o) { return reinterpret_cast<float*>(smem + o); };
+    s.Kx = e(LY::oKx); s.Qx = e(LY::oQx); s.Ky = e(LY::oKy); s.V = e(LY::oV); s.Td = e(LY::oTd);
+    s.Wt = e(LY::oWt); s.Ut = e(LY::oUt); s.Qd = e(LY::oQd); s.P = e(LY::oP); s.KdT = e(LY::oKdT);
+    s.Mt = e(LY::oMt); s.Qe = e(LY::oQe);
+    s.A = f(LY::oA); s.Gb = f(LY::oGb); s.Seg = f(LY::oSeg); s.Egl = f(LY::oEgl); s.EGs = f(LY::oEGs);
+    s.Wg = f(LY::oWg); s.Z = f(LY::oZ); s.M = f(LY::oM); s.Y = f(LY::oY); s.Fd = f(LY::oFd);
+    s.Ff = f(LY::oFf); s.Ones = f(LY::oOnes);
     s.Flag = reinterpret_cast<int*>(smem + LY::oFlag);
-    s.Fd = reinterpret_cast<float*>(smem + LY::oFd);
-    s.Ff = reinterpret_cast<float*>(smem + LY::oFf);
-    s.Ones = reinterpret_cast<float*>(smem + LY::oOnes);
     return s;
   }
 
-  __device__ static Sink<E> lds_sink(const Smem& s) { return Sink<E>{s.Qd, LD, s.KdT, LK, s.P, LK, s.W, LD}; }
+  __device__ static Sink<E> lds_sink(const Smem& s) { return Sink<E>{s.Mt, LD, s.Qe, LD}; }
   __device__ static Sink<E> image_sink(unsigned char* img) {
-    return Sink<E>{reinterpret_cast<E*>(img + LY::wQd), DK, reinterpret_cast<E*>(img + LY::wKdT), KP,
-                   reinterpret_cast<E*>(img + LY::wP), KP, reinterpret_cast<E*>(img + LY::wW), DK};
+    return Sink<E>{reinterpret_cast<E*>(img + LY::wMt), DK, reinterpret_cast<E*>(img + LY::wQe), DK};
+  }
+  // this wave's C tiles <-> the fragment-ordered Ct / Ol arrays of an image
+  __device__ static void put_frags(unsigned char* img, const f32x4 (&CtR)[DK / 16], const f32x4 (&OlR)[NB]) {
+    const int wave = wave_id(), lane = threadIdx.x & 63;
+    E* ct = reinterpret_cast<E*>(img + LY::wCt) + (wave * (DK / 16) * 64 + lane) * 4;
+    E* ol = reinterpret_cast<E*>(img + LY::wOl) + (wave * NB * 64 + lane) * 4;
+#pragma unroll
+    for (int a = 0; a < DK / 16; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ct[a * 256 + i] = from_f32<E>(CtR[a][i]);
+#pragma unroll
+    for (int a = 0; a < NB; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ol[a * 256 + i] = from_f32<E>(OlR[a][i]);
   }
 
   __device__ static void zero_lds(unsigned char* smem, int bytes) {
@@ -213,11 +230,12 @@ struct Block {
 
   // -------------------------------------------------------------- gate pass
   // Loads tokens [t0, t0 + nvalid) and builds every decay-scaled operand.
-  // Thread (gd, gs) owns key column gd of 16-row sub-block gs. Rows past
+  // Thread (gd, gs) owns key column gd of 16-row sub-block gs; its Qd values
+  // stay in registers (qd) until the Qx/Ky region is free again. Rows past
   // nvalid read as zeros (k = q = v = w = g = 0), which leaves the state
   // untouched. Returns true if a sub-block's decay is too steep for the
   // factorised diagonal Grams. Ends with a barrier.
-  __device__ static bool gate_pass(const Smem& s, const Rows<E>& src, int t0, int nvalid, const Sink<E>& out) {
+  __device__ static bool gate_pass(const Smem& s, const Rows<E>& src, int t0, int nvalid, E (&qd)[16]) {
     const int tid = threadIdx.x;
     const int gs = wave_id() * 64 / DK, gd = tid % DK;
     if (tid == 0) s.Flag[0] = 0;
@@ -321,12 +339,12 @@ struct Block {
         s.Kx[r * LD + gd] = from_f32<E>(bb * kv[i] * e1);
         s.Qx[r * LD + gd] = from_f32<E>(qv[i] * eprev);
         s.Ky[r * LD + gd] = from_f32<E>(kv[i] * en);
-        out.Qd[r * out.ldQd + gd] = from_f32<E>(qv[i] * eprev * eGs);
+        qd[i] = from_f32<E>(qv[i] * eprev * eGs);
         kd[i] = from_f32<E>(kv[i] * en * eTail);
         eprev = e1;
       }
       // Kdec transposed: this thread's 16 rows are 16 consecutive elements
-      E* kdt = out.KdT + gd * out.ldKdT + 16 * gs;
+      E* kdt = s.KdT + gd * LK + 16 * gs;
 #pragma unroll
       for (int c = 0; c < 16 * LY::ES / 16; ++c)
         *reinterpret_cast<f32x4*>(kdt + c * (16 / LY::ES)) = *reinterpret_cast<const f32x4*>(kd + c * (16 / LY::ES));
@@ -336,31 +354,27 @@ struct Block {
   }
 
   // -------------------------------------------------------------- Grams A, P
-  // A (fp32) lands over the Qx/Ky region once every wave is done with them.
-  // Ends with a barrier.
+  // A (fp32) lands over the Qx/Ky region once every wave is done with them;
+  // the P tiles of this wave stay in registers (Pt) until solve() frees the
+  // region again. Ends with a barrier.
   __device__ static void grams(const Smem& s, const Rows<E>& src, int t0, int nvalid, bool fallback,
-                               const Sink<E>& out) {
+                               f32x4 (&Pt)[TPW]) {
     const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     const int gq = lane >> 4, cc = lane & 15;
-    constexpr int TPW = (NB * NB + NW - 1) / NW;     // tiles per wave
     f32x4 accA[TPW];
 #pragma unroll
     for (int k = 0; k < TPW; ++k) {
       accA[k] = zero4();
+      Pt[k] = zero4();
       const int tile = wave + k * NW;
       if (tile >= NB * NB) continue;
       const int I = tile / NB, J = tile % NB;
-      if (J > I) {                                   // above the diagonal: P is zero
-#pragma unroll
-        for (int i = 0; i < 4; ++i) out.P[(16 * I + 4 * gq + i) * out.ldP + 16 * J + cc] = from_f32<E>(0.f);
-        continue;
-      }
+      if (J > I) continue;                           // above the diagonal: zero
       const bool diag = (I == J), far = (J < I - 1);
       // left factor e^{Gs_I - Ge_J} for far pairs, right factor e^{Gs_J - Ge_J}
       // on the diagonal; other tiles multiply by ones (no branches)
       const float* fl = far ? s.Ff + ((I - 2) * (I - 1) / 2 + J) * DK : s.Ones;
       const float* fr = diag ? s.Fd + J * DK : s.Ones;
-      f32x4 acP = zero4();
       Frag ka[DK / KS], qa[DK / KS], kb[DK / KS];
 #pragma unroll
       for (int p = 0; p < DK / KS; ++p) {
@@ -368,6 +382,7 @@ struct Block {
         qa[p] = MM::ld_nat(s.Qx, LD, 16 * I + cc, p * KS);
         kb[p] = MM::ld_nat(s.Ky, LD, 16 * J + cc, p * KS);
       }
+      f32x4 acP = zero4();
 #pragma unroll
       for (int p = 0; p < DK / KS; ++p) {
         const Frag a = FragScale<E>::apply(ka[p], fl, p * KS);
@@ -381,13 +396,9 @@ struct Block {
         const int r = 16 * I + 4 * gq + i, j = 16 * J + cc;
         const bool keep = !diag || (j < r);
         accA[k][i] = keep ? accA[k][i] : 0.f;
-        out.P[r * out.ldP + j] = from_f32<E>(keep ? acP[i] : 0.f);
+        Pt[k][i] = keep ? to_f32(from_f32<E>(acP[i])) : 0.f;
       }
     }
-    // padding columns of P (only when BL < KP)
-    if constexpr (BL < KP)
-      for (int idx = tid; idx < BL * (KP - BL); idx += NT)
-        out.P[(idx / (KP - BL)) * out.ldP + BL + idx % (KP - BL)] = from_f32<E>(0.f);
     __syncthreads();                                 // Qx/Ky are free now
 #pragma unroll
     for (int k = 0; k < TPW; ++k) {
@@ -400,16 +411,28 @@ struct Block {
     }
     __syncthreads();
     if (fallback) {
-      grams_pairwise(s, src, t0, nvalid, out);
+      grams_pairwise(s, src, t0, nvalid, Pt);
       __syncthreads();
     }
   }
 
   // Diagonal sub-blocks rebuilt pairwise, straight from the raw gates in
   // global memory: used only for decays too steep for the factorised form.
-  // Slow but exact; needs no LDS scratch.
+  // Slow but exact. A entries go to LDS; the P entries reach the Pt registers
+  // of the wave that owns the tile through a scratch area in R4 (KdT is
+  // parked in registers meanwhile).
   __device__ static void grams_pairwise(const Smem& s, const Rows<E>& src, int t0, int nvalid,
-                                        const Sink<E>& out) {
+                                        f32x4 (&Pt)[TPW]) {
+    float* pdiag = reinterpret_cast<float*>(s.base + LY::oR4);    // scratch: [NB][16][16]
+    constexpr int KCH = DK * LK * LY::ES / 16;
+    constexpr int KPER = (KCH + NT - 1) / NT;
+    f32x4 keep[KPER];
+#pragma unroll
+    for (int j = 0; j < KPER; ++j) {
+      const int c = threadIdx.x + j * NT;
+      if (c < KCH) keep[j] = reinterpret_cast<const f32x4*>(s.KdT)[c];
+    }
+    __syncthreads();
     for (int item = threadIdx.x; item < NB * 120; item += NT) {
       const int I = item / 120;
       int p = item % 120, ri = 1;
@@ -430,18 +453,39 @@ struct Block {
         }
       }
       s.A[r * LA + j] = sa;
-      out.P[r * out.ldP + j] = from_f32<E>(sp);
+      pdiag[I * 256 + ri * 16 + ji] = to_f32(from_f32<E>(sp));
+    }
+    __syncthreads();
+    const int wave = wave_id(), lane = threadIdx.x & 63;
+    const int gq = lane >> 4, cc = lane & 15;
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      const int tile = wave + k * NW;
+      if (tile >= NB * NB) continue;
+      const int I = tile / NB, J = tile % NB;
+      if (I != J) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ri = 4 * gq + i;
+        Pt[k][i] = (cc < ri) ? pdiag[I * 256 + ri * 16 + cc] : 0.f;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KPER; ++j) {
+      const int c = threadIdx.x + j * NT;
+      if (c < KCH) reinterpret_cast<f32x4*>(s.KdT)[c] = keep[j];
     }
   }
 
   // -------------------------------------------------------------- (I + A_II)^{-1}
-  // Diagonal 16x16 blocks by forward substitution in fp32. Wave 0, lane
-  // (block ib = gq, column c = cc) keeps its whole column in registers.
+  // Diagonal 16x16 blocks by forward substitution in fp32, stored as E.
+  // Wave 0, lane (block ib = gq, column c = cc) keeps its column in registers.
   // Ends with a barrier.
   __device__ static void inverse_diag(const Smem& s) {
-    const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
+    const int lane = threadIdx.x & 63;
     const int ib = lane >> 4, c = lane & 15;
-    if (wave == 0 && ib < NB) {
+    if (wave_id() == 0 && ib < NB) {
       const float* Ablk = s.A + (16 * ib) * LA + 16 * ib;
       float t[16];
       float cur[16], nxt[16];
@@ -463,9 +507,9 @@ struct Block {
           for (int j = 0; j < 16; ++j) cur[j] = nxt[j];
         }
       }
-      float* Tb = s.Td + ib * 16 * LTD;
+      E* Tb = s.Td + ib * 16 * LTD;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) Tb[r * LTD + c] = t[r];
+      for (int r = 0; r < 16; ++r) Tb[r * LTD + c] = from_f32<E>(t[r]);
     }
     __syncthreads();
   }
@@ -474,14 +518,14 @@ struct Block {
   // Blocked forward substitution over 16-row sub-blocks:
   //   X_I = T_II (R_I - sum_{J<I} A_IJ X_J),  R = [b k e^{G} | w v],
   // with T_II the diagonal inverses. Wave w solves the two 16-column tiles
-  // 2w, 2w+1 of [W | U] (DK + DV = 32 NW columns) independently, keeping its
-  // X_J tiles in registers. W goes to the sink, U (rounded to E) overwrites
-  // the value tile in place. Ends with a barrier.
-  __device__ static void solve(const Smem& s, const Sink<E>& out) {
-    const int wave = wave_id(), lane = threadIdx.x & 63;
+  // 2w, 2w+1 of [W | U] (DK + DV = 32 NW columns), keeping its X_J tiles in
+  // registers. Once every operand is in registers the Qx/Ky/A region takes
+  // Qd (from the gate-pass registers) and P (from the Gram registers); the
+  // results go transposed (W^T over Kx, U^T over V) for the affine products.
+  // Ends with a barrier.
+  __device__ static void solve(const Smem& s, const E (&qd)[16], const f32x4 (&Pt)[TPW]) {
+    const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     const int gq = lane >> 4, cc = lane & 15;
-    // operands that do not depend on the recursion, loaded up front:
-    // right-hand sides R (C layout), A_IJ rows and T_II rows (fp32)
     // both column tiles of a wave lie on the same side of [W | U]
     const bool isW = 2 * wave < DK / 16;
     const int col0 = 32 * wave - (isW ? 0 : DK) + cc;
@@ -510,10 +554,30 @@ struct Block {
     f32x4 Arow[NB > 1 ? NB * (NB - 1) / 2 : 1], Trow[NB];
 #pragma unroll
     for (int I = 0; I < NB; ++I) {
-      Trow[I] = *reinterpret_cast<const f32x4*>(s.Td + I * 16 * LTD + cc * LTD + 4 * gq);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Trow[I][i] = to_f32(s.Td[I * 16 * LTD + cc * LTD + 4 * gq + i]);
 #pragma unroll
       for (int J = 0; J < I; ++J)
         Arow[I * (I - 1) / 2 + J] = *reinterpret_cast<const f32x4*>(s.A + (16 * I + cc) * LA + 16 * J + 4 * gq);
+    }
+    __syncthreads();                                 // Kx, A, V, Td fully read
+    // Qd and P into the Qx/Ky/A region
+    {
+      const int gs = wave * 64 / DK, gd = tid % DK;
+      if (gs < NB)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s.Qd[(16 * gs + i) * LD + gd] = qd[i];
+#pragma unroll
+      for (int k = 0; k < TPW; ++k) {
+        const int tile = wave + k * NW;
+        if (tile >= NB * NB) continue;
+        const int I = tile / NB, J = tile % NB;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s.P[(16 * I + 4 * gq + i) * LK + 16 * J + cc] = from_f32<E>(Pt[k][i]);
+      }
+      if constexpr (BL < KP)                         // padding columns of P
+        for (int idx = tid; idx < BL * (KP - BL); idx += NT)
+          s.P[(idx / (KP - BL)) * LK + BL + idx % (KP - BL)] = from_f32<E>(0.f);
     }
     f32x4 X[NB][2];
 #pragma unroll
@@ -531,72 +595,104 @@ struct Block {
         X[I][t] = x;
       }
     }
-    if (isW) {
+    // transposed stores: lane holds rows 4gq..4gq+3 of column col -> 4 consecutive
+    E* dst = isW ? s.Wt : s.Ut;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t) {
+      E* rowp = dst + (col0 + 16 * t) * LK;
 #pragma unroll
-        for (int I = 0; I < NB; ++I)
+      for (int I = 0; I < NB; ++I)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            out.W[(16 * I + 4 * gq + i) * out.ldW + col0 + 16 * t] = from_f32<E>(X[I][t][i]);
-    } else {
+        for (int i = 0; i < 4; ++i) rowp[16 * I + 4 * gq + i] = from_f32<E>(X[I][t][i]);
+      if constexpr (BL < KP)
+        for (int j = BL + 4 * gq; j < KP; j += 16)
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int I = 0; I < NB; ++I)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            s.V[(16 * I + 4 * gq + i) * LV + col0 + 16 * t] = from_f32<E>(X[I][t][i]);
+          for (int i = 0; i < 4; ++i) rowp[j + i] = from_f32<E>(0.f);
     }
     __syncthreads();
   }
 
-  // U tiles of this wave's 16 value channels, from the value tile after solve()
-  __device__ static void load_u(const Smem& s, f32x4 (&U)[NB]) {
+  // -------------------------------------------------------------- affine maps
+  //   Mt[d'][d] = e^{G_BL}[d] [d = d'] - sum_j Kdec[j][d'] W[j][d]
+  //   Qe[r][d]  = Qd[r][d] - sum_j P[r][j] W[j][d]
+  //   Ct[d'][e] = sum_j Kdec[j][d'] U[j][e]
+  //   Ol[r][e]  = sum_j P[r][j] U[j][e]
+  // Every product reads rows of a row-major left tile and rows of a
+  // transposed right tile (natural map over j); values are rounded to E.
+  // Mt and Qe tiles are spread over the waves and go to the sink; wave w
+  // computes the Ct and Ol tiles of its own value channels [16w, 16w+16) and
+  // keeps them in registers (CtR, OlR).
+  // Ends with a barrier.
+  __device__ static void affine(const Smem& s, const Sink<E>& out, f32x4 (&CtR)[DK / 16], f32x4 (&OlR)[NB]) {
     const int wave = wave_id(), lane = threadIdx.x & 63;
     const int gq = lane >> 4, cc = lane & 15;
+    constexpr int TD = DK / 16;                       // tiles along d (== along e)
+    auto product = [&](const E* left, int a, const E* right, int b, int nst) {
+      f32x4 acc = zero4();
+      for (int p = 0; p < nst; ++p)
+        acc = MM::mma(MM::ld_nat(left, LK, 16 * a + cc, p * KS), MM::ld_nat(right, LK, 16 * b + cc, p * KS), acc);
+      return acc;
+    };
+    // Mt and Qe over all waves
+    constexpr int NSH = TD * TD + NB * TD;
+    for (int tile = wave; tile < NSH; tile += NW) {
+      const bool isM = tile < TD * TD;
+      const int x = isM ? tile : tile - TD * TD;
+      const int a = x / TD, b = x % TD;
+      // P is lower-triangular: row block a needs j < 16 (a + 1) only
+      const f32x4 acc = isM ? product(s.KdT, a, s.Wt, b, MM::steps(KP)) : product(s.P, a, s.Wt, b, MM::steps(16 * (a + 1)));
+      E* dst = isM ? out.Mt : out.Qe;
+      const int ld = isM ? out.ldMt : out.ldQe;
 #pragma unroll
-    for (int rt = 0; rt < NB; ++rt)
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * a + 4 * gq + i, c = 16 * b + cc;
+        const float v = isM ? (r == c ? s.Egl[c] : 0.f) - acc[i] : to_f32(s.Qd[r * LD + c]) - acc[i];
+        dst[r * ld + c] = from_f32<E>(v);
+      }
+    }
+    // Ct and Ol of this wave's value channels
 #pragma unroll
-      for (int i = 0; i < 4; ++i) U[rt][i] = to_f32(s.V[(16 * rt + 4 * gq + i) * LV + 16 * wave + cc]);
+    for (int a = 0; a < TD; ++a) {
+      f32x4 acc = product(s.KdT, a, s.Ut, wave, MM::steps(KP));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = to_f32(from_f32<E>(acc[i]));
+      CtR[a] = acc;
+    }
+#pragma unroll
+    for (int a = 0; a < NB; ++a) {
+      f32x4 acc = product(s.P, a, s.Ut, wave, MM::steps(16 * (a + 1)));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = to_f32(from_f32<E>(acc[i]));
+      OlR[a] = acc;
+    }
+    __syncthreads();
   }
 
   // -------------------------------------------------------------- state and output
-  // Per wave (its 16 value channels): Delta = U - W S^T, O = Qd S^T + P Delta,
-  // S^T <- diag(e^{G_BL}) S^T + Kdec^T Delta. Operand tiles: W, Qd [BL][LD];
-  // P [BL][LK]; KdT [DK][LK]; Egl [DK].
-  __device__ static void state_step(const E* W, const E* Qd, const E* P, const E* KdT, const float* Egl,
-                                    const f32x4 (&U)[NB], f32x4 (&St)[DK / 16], f32x4 (&Ot)[NB]) {
+  // Per wave (its 16 value channels), with S^T held as C tiles:
+  //   O   = Qe S^T + Ol            (S at the block start)
+  //   S^T <- Mt S^T + Ct
+  // Mt [DK][ldm] and Qe [BL][ldq] are shared tiles; Ct and Ol are this
+  // wave's C tiles.
+  __device__ static void state_step(const E* Mt, int ldm, const E* Qe, int ldq, const f32x4 (&Ct)[DK / 16],
+                                    const f32x4 (&Ol)[NB], f32x4 (&St)[DK / 16], f32x4 (&Ot)[NB]) {
     const int lane = threadIdx.x & 63;
-    const int gq = lane >> 4, cc = lane & 15;
-    constexpr int NDT = KP / 16;                     // Delta tiles incl. padding
-    f32x4 D[NDT];
+    const int cc = lane & 15;
+    Frag sf[DK / KS];
 #pragma unroll
-    for (int rt = 0; rt < NDT; ++rt) D[rt] = zero4();
-#pragma unroll
-    for (int rt = 0; rt < NB; ++rt) {
-      f32x4 ws = zero4();
-#pragma unroll
-      for (int p = 0; p < DK / KS; ++p) ws = MM::mma(MM::ld_cp(W, LD, 16 * rt + cc, p), MM::from_c(St, p), ws);
-      D[rt] = U[rt] - ws;
-    }
+    for (int p = 0; p < DK / KS; ++p) sf[p] = MM::from_c(St, p);
 #pragma unroll
     for (int rt = 0; rt < NB; ++rt) {
-      f32x4 acc = zero4();
+      f32x4 acc = Ol[rt];
 #pragma unroll
-      for (int p = 0; p < DK / KS; ++p) acc = MM::mma(MM::ld_cp(Qd, LD, 16 * rt + cc, p), MM::from_c(St, p), acc);
-#pragma unroll
-      for (int p = 0; p < MM::steps(BL); ++p)
-        if (p < MM::steps(16 * (rt + 1))) acc = MM::mma(MM::ld_cp(P, LK, 16 * rt + cc, p), MM::from_c(D, p), acc);
+      for (int p = 0; p < DK / KS; ++p) acc = MM::mma(MM::ld_cp(Qe, ldq, 16 * rt + cc, p), sf[p], acc);
       Ot[rt] = acc;
     }
 #pragma unroll
     for (int dt = 0; dt < DK / 16; ++dt) {
-      f32x4 acc;
+      f32x4 acc = Ct[dt];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = St[dt][i] * Egl[16 * dt + 4 * gq + i];
-#pragma unroll
-      for (int p = 0; p < MM::steps(BL); ++p) acc = MM::mma(MM::ld_cp(KdT, LK, 16 * dt + cc, p), MM::from_c(D, p), acc);
+      for (int p = 0; p < DK / KS; ++p) acc = MM::mma(MM::ld_cp(Mt, ldm, 16 * dt + cc, p), sf[p], acc);
       St[dt] = acc;
     }
   }

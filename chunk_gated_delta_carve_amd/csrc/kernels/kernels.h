@@ -73,13 +73,15 @@ carve_chunk_serial_kernel(FwdArgs a) {
   for (int blk = 0; blk < nblk; ++blk) {
     const int t0 = blk * BL;
     const int nvalid = min(BL, T - t0);
-    const bool fallback = B::gate_pass(s, src, t0, nvalid, sink);
-    B::grams(s, src, t0, nvalid, fallback, sink);
+    E qd[16];
+    f32x4 Pt[B::TPW];
+    const bool fallback = B::gate_pass(s, src, t0, nvalid, qd);
+    B::grams(s, src, t0, nvalid, fallback, Pt);
     B::inverse_diag(s);
-    B::solve(s, sink);
-    f32x4 U[NB], Ot[NB];
-    B::load_u(s, U);
-    B::state_step(s.W, s.Qd, s.P, s.KdT, s.Egl, U, St, Ot);
+    B::solve(s, qd, Pt);
+    f32x4 CtR[DK / 16], OlR[NB], Ot[NB];
+    B::affine(s, sink, CtR, OlR);
+    B::state_step(s.Mt, LY::LD, s.Qe, LY::LD, CtR, OlR, St, Ot);
 #pragma unroll
     for (int rt = 0; rt < NB; ++rt)
 #pragma unroll
@@ -112,7 +114,7 @@ __global__ void __launch_bounds__((BlockLayout<E, DK, DV, BL>::NT))
 carve_intra_kernel(FwdArgs a) {
   using B = Block<E, DK, DV, BL>;
   using LY = typename B::LY;
-  constexpr int NT = LY::NT, NB = LY::NB;
+  constexpr int NT = LY::NT;
   static_assert(BL >= 32, "the image has no padding columns to clear");
   extern __shared__ __align__(16) unsigned char smem[];
   const auto s = B::carve(smem);
@@ -129,36 +131,36 @@ carve_intra_kernel(FwdArgs a) {
 
   for (int d = threadIdx.x; d < DK; d += NT) s.Z[d] = 0.f;   // no content projection
   __syncthreads();
-  const bool fallback = B::gate_pass(s, src, t0, nvalid, sink);
-  B::grams(s, src, t0, nvalid, fallback, sink);
+  E qd[16];
+  f32x4 Pt[B::TPW];
+  const bool fallback = B::gate_pass(s, src, t0, nvalid, qd);
+  B::grams(s, src, t0, nvalid, fallback, Pt);
   B::inverse_diag(s);
-  B::solve(s, sink);
-
-  // U (in the value tile) and e^{G_BL} to the image, 16-byte chunks
-  for (int i = threadIdx.x; i < DK; i += NT) reinterpret_cast<float*>(img + LY::wEgl)[i] = s.Egl[i];
-  constexpr int CPR = DV * LY::ES / 16;
-  for (int c = threadIdx.x; c < BL * CPR; c += NT) {
-    const int r = c / CPR, k = c % CPR;
-    *reinterpret_cast<f32x4*>(img + LY::wU + (r * DV) * LY::ES + 16 * k) =
-        *reinterpret_cast<const f32x4*>(s.V + r * LY::LV + k * (16 / LY::ES));
-  }
+  B::solve(s, qd, Pt);
+  f32x4 CtR[DK / 16], OlR[LY::NB];
+  B::affine(s, sink, CtR, OlR);
+  B::put_frags(img, CtR, OlR);
 }
 
 // One workgroup per (batch, head): the serial state pass and the output.
-// Block images stream through two LDS buffers (the next one is fetched into
-// registers while the current one is used). Outputs are staged in the U
-// region of the current buffer (U is in registers by then) and written as
-// 16-byte row chunks.
+// Each block's Mt and Qe stream through two LDS buffers (the next block's are
+// fetched into registers while the current block is used); each wave loads
+// its own C^T / Ol fragments straight into registers, one block ahead.
+// Outputs are staged in LDS over the current Qe tile once every wave has
+// used it, and written as 16-byte row chunks.
 template <typename E, int DK, int DV, int BL>
 __global__ void __launch_bounds__((BlockLayout<E, DK, DV, BL>::NT))
 carve_state_kernel(FwdArgs a) {
   using B = Block<E, DK, DV, BL>;
   using LY = typename B::LY;
-  constexpr int NT = LY::NT, NB = LY::NB, ES = LY::ES;
-  constexpr int CH = LY::wBytes / 16;                 // 16-byte chunks per image
+  constexpr int NT = LY::NT, NB = LY::NB, ES = LY::ES, TD = DK / 16;
+  constexpr int CH = LY::wStaged / 16;                // 16-byte chunks staged per image
   constexpr int PER = (CH + NT - 1) / NT;             // chunks per thread
   constexpr int OCPR = DV * ES / 16;                  // output chunks per row
+  constexpr int LO = DV + LY::PE;                     // pitch of the staged output
   static_assert(2 * LY::sBytes <= 160 * 1024, "staging buffers fit");
+  static_assert(BL * LO * ES <= BL * LY::LD * ES, "output staging fits over Qe");
+  static_assert(DV * ES % 16 == 0, "16-byte output rows");
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
@@ -176,64 +178,88 @@ carve_state_kernel(FwdArgs a) {
   const int mstart = T > 0 ? ((T - 1) / L) * L : 0;   // first token of the last chunk
   float m_part = 0.f;
 
-  f32x4 pre[PER];
-  auto fetch = [&](int blk) {
-    const f32x4* g = reinterpret_cast<const f32x4*>(imgs + (size_t)blk * LY::wBytes);
+  typedef E e4 __attribute__((ext_vector_type(4)));
+  // register sets for the images of the next PD blocks
+  constexpr int PD = DK == 64 ? 2 : 1;                 // prefetch depth
+  f32x4 pre[PD][PER];
+  e4 ctn[PD][TD], oln[PD][NB];
+  auto fetch = [&](int blk, f32x4 (&pr)[PER], e4 (&ct4)[TD], e4 (&ol4)[NB]) {
+    const unsigned char* img = imgs + (size_t)blk * LY::wBytes;
+    const f32x4* g = reinterpret_cast<const f32x4*>(img);
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int c = tid + j * NT;
-      if (c < CH) pre[j] = g[c];
+      if (c < CH) pr[j] = g[c];
     }
+    const e4* ct = reinterpret_cast<const e4*>(img + LY::wCt) + wave * TD * 64 + lane;
+    const e4* ol = reinterpret_cast<const e4*>(img + LY::wOl) + wave * NB * 64 + lane;
+#pragma unroll
+    for (int t = 0; t < TD; ++t) ct4[t] = ct[t * 64];
+#pragma unroll
+    for (int t = 0; t < NB; ++t) ol4[t] = ol[t * 64];
   };
-  auto deposit = [&](int buf) {
+  f32x4 CtR[TD], OlR[NB];
+  auto deposit = [&](int buf, const f32x4 (&pr)[PER], const e4 (&ct4)[TD], const e4 (&ol4)[NB]) {
     unsigned char* d = smem + buf * LY::sBytes;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int c = tid + j * NT;
-      if (c < CH) *reinterpret_cast<f32x4*>(d + LY::stage_offset(c)) = pre[j];
+      if (c < CH) *reinterpret_cast<f32x4*>(d + LY::stage_offset(c)) = pr[j];
     }
+#pragma unroll
+    for (int t = 0; t < TD; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) CtR[t][i] = to_f32(ct4[t][i]);
+#pragma unroll
+    for (int t = 0; t < NB; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) OlR[t][i] = to_f32(ol4[t][i]);
   };
-  if (nblk > 0) {
-    fetch(0);
-    deposit(0);
-  }
-  __syncthreads();
-  for (int blk = 0; blk < nblk; ++blk) {
-    const int cur = blk & 1;
-    if (blk + 1 < nblk) fetch(blk + 1);
-    const unsigned char* buf = smem + cur * LY::sBytes;
-    const E* Wm = reinterpret_cast<const E*>(buf + LY::sW);
-    const E* Qd = reinterpret_cast<const E*>(buf + LY::sQd);
-    const E* Pm = reinterpret_cast<const E*>(buf + LY::sP);
-    const E* KdT = reinterpret_cast<const E*>(buf + LY::sKdT);
-    const E* Ui = reinterpret_cast<const E*>(buf + LY::sU);
-    const float* Egl = reinterpret_cast<const float*>(buf + LY::sEgl);
-    f32x4 U[NB], Ot[NB];
-#pragma unroll
-    for (int rt = 0; rt < NB; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) U[rt][i] = to_f32(Ui[(16 * rt + 4 * gq + i) * DV + e0 + cc]);
-    B::state_step(Wm, Qd, Pm, KdT, Egl, U, St, Ot);
+  // one block: state and output from buffer `cur`; its successor waits in
+  // register set `nx`, and set `ld` receives the block PD ahead
+  auto step = [&](int blk, int cur, f32x4 (&prn)[PER], e4 (&ctx)[TD], e4 (&olx)[NB],
+                  f32x4 (&prl)[PER], e4 (&ctl)[TD], e4 (&oll)[NB]) {
+    if (blk + PD < nblk) fetch(blk + PD, prl, ctl, oll);
+    unsigned char* buf = smem + cur * LY::sBytes;
+    f32x4 Ot[NB];
+    B::state_step(reinterpret_cast<const E*>(buf + LY::sMt), LY::LD, reinterpret_cast<const E*>(buf + LY::sQe),
+                  LY::LD, CtR, OlR, St, Ot);
     const int t0 = blk * BL;
     const int nvalid = min(BL, T - t0);
-    E* so = const_cast<E*>(Ui);                      // [BL][DV], U already in registers
-    __syncthreads();                                 // every wave has read its U
+    E* so = reinterpret_cast<E*>(buf + LY::sQe);      // [BL][LO] over the used Qe tile
+    __syncthreads();                                 // every wave is done with Qe
 #pragma unroll
     for (int rt = 0; rt < NB; ++rt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rt + 4 * gq + i;
         if (t0 + r >= mstart) m_part += Ot[rt][i];   // rows past nvalid are exactly 0
-        so[r * DV + e0 + cc] = from_f32<E>(Ot[rt][i]);
+        so[r * LO + e0 + cc] = from_f32<E>(Ot[rt][i]);
       }
     __syncthreads();
     for (int c = tid; c < nvalid * OCPR; c += NT) {
       const int r = c / OCPR, k = c % OCPR;
       *reinterpret_cast<f32x4*>(O + ((size_t)(bidx * T + t0 + r) * H + h) * DV + k * (16 / ES)) =
-          *reinterpret_cast<const f32x4*>(so + r * DV + k * (16 / ES));
+          *reinterpret_cast<const f32x4*>(so + r * LO + k * (16 / ES));
     }
-    if (blk + 1 < nblk) deposit(cur ^ 1);
+    if (blk + 1 < nblk) deposit(cur ^ 1, prn, ctx, olx);
     __syncthreads();
+  };
+  if (nblk > 0) {
+    fetch(0, pre[0], ctn[0], oln[0]);
+    deposit(0, pre[0], ctn[0], oln[0]);
+    if (PD == 2 && nblk > 1) fetch(1, pre[0], ctn[0], oln[0]);
+  }
+  __syncthreads();
+  if constexpr (PD == 2) {
+    // set 0 holds block blk+1 at even blk, set 1 at odd blk
+    for (int blk = 0; blk < nblk; blk += 2) {
+      step(blk, 0, pre[0], ctn[0], oln[0], pre[1], ctn[1], oln[1]);
+      if (blk + 1 < nblk) step(blk + 1, 1, pre[1], ctn[1], oln[1], pre[0], ctn[0], oln[0]);
+    }
+  } else {
+    for (int blk = 0; blk < nblk; ++blk)
+      step(blk, blk & 1, pre[0], ctn[0], oln[0], pre[0], ctn[0], oln[0]);
   }
   if (a.state_out) B::store_state(a.state_out, bh, St);
   if (a.mean_out) {
