@@ -3,8 +3,9 @@
 One step = one forward pass of the CARVE layer over the batch (every stage of
 the path: gate prep, gated Grams and triangular inverse, W/U, the serial state
 pass, output and chunk mean), writing o, the final state and the final mean.
-Workload: B=4, H=12, T=2048, d_k=d_v=64, L=64, bf16 inputs with fp32
-accumulation, no content projection (seeded synthetic data).
+Default workload: B=4, H=12, T=2048, d_k=d_v=64, L=64, bf16 inputs with fp32
+accumulation, no content projection (seeded synthetic data); --workload picks
+another of the named shapes.
 
 Prints one JSON line. `roofline` covers the dominant kernel: algorithmic bytes
 per launch over its average duration, timed with HIP events on the stream the
@@ -29,12 +30,146 @@ def algorithmic_bytes(B, T, H, dk, dv, es, rank=0):
     return B * T * H * per_tok + H * rank * (dk + dv) * es + B * H * dv * dk * 4 + B * H * dv * 4
 
 
+def cpu_baseline(wl, inp, budget_s):
+    """Time the float64 oracle on this host, single-threaded, on a bounded sample
+    of the workload: whole sequences when one pass fits the budget, else a
+    prefix of every sequence sized to it. Returns head-token-rate in tokens/s
+    (batch rows x time steps, all heads), as the GPU value is."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import carve_forward
+    from chunk_gated_delta_carve_amd.workloads import to_f64
+
+    def run(Tp):
+        f = lambda k: np.ascontiguousarray(to_f64(inp[k][:, :Tp], wl.dtype))
+        ub = {}
+        if wl.rank > 0:
+            ub = dict(U_down=to_f64(inp["U_down"], wl.dtype), U_up=to_f64(inp["U_up"], wl.dtype))
+        t0 = time.perf_counter()
+        carve_forward(f("q"), f("k"), f("v"), f("g"), f("bx"), f("w"), wl.L, **ub)
+        return time.perf_counter() - t0
+
+    with threadpool_limits(1):
+        probe_T = min(wl.T, 2 * wl.L)
+        rate = probe_T / run(probe_T)                   # time steps per second (all B, H)
+        Tp = wl.T if wl.T / rate <= budget_s else max(wl.L, int(budget_s * rate) // wl.L * wl.L)
+        spent, steps, passes = 0.0, 0, 0
+        while spent < budget_s:
+            spent += run(Tp)
+            steps += Tp
+            passes += 1
+    what = ("the whole workload" if Tp == wl.T else f"the first {Tp} of {wl.T} time steps")
+    return {"value": wl.B * steps / spent, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{what} (B={wl.B}, all {wl.H} heads), {passes} pass(es), {spent:.1f} s, "
+                      "one thread"}
+
+
+KERNEL_SOURCES = ("chunk_gated_delta_carve_amd/csrc/carve_lib.hip",
+                  "chunk_gated_delta_carve_amd/csrc/kernels/common.h",
+                  "chunk_gated_delta_carve_amd/csrc/kernels/block.h",
+                  "chunk_gated_delta_carve_amd/csrc/kernels/kernels.h")
+COPY_BYTES = 256 * 1024 * 1024      # calibration copy: reads and writes this many bytes
+
+
+def sources_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(wl):
+    return os.path.join(ROOT, "profiles", f"carve_chunk_fwd_{wl.tag()}_hbm_traffic.md")
+
+
+def measured_traffic(wl):
+    """HBM bytes per launch from the committed rocprofv3 counter summary for this
+    workload, or None when there is none or the kernel sources have changed
+    since the counters were taken."""
+    path = traffic_file(wl)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for ln in f:
+            if ln.startswith("- ") and ": " in ln:
+                key, val = ln[2:].split(": ", 1)
+                fields[key.strip()] = val.strip().strip("`")
+    if fields.get("kernel sources sha256/16") != sources_sha():
+        return None
+    return float(fields["HBM bytes per launch"])
+
+
+def write_traffic_summary(wl, fetch_csv, write_csv, commands):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; csv output)
+    over `bench.py --calibrate-copy` into the summary that measured_traffic reads.
+    Each counter is scaled by what it reads for a plain copy of COPY_BYTES."""
+    import csv
+    from collections import defaultdict
+
+    def per_kernel(path, counter):
+        vals = defaultdict(list)
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    vals[r["Kernel_Name"]].append(float(r["Counter_Value"]) * 1024.0)   # KiB -> bytes
+        return vals
+
+    def copy_kernel(vals):
+        # the calibration copy is the only negation kernel in the process
+        cands = [(k, v) for k, v in vals.items() if "neg" in k.lower() and min(v) > 0.5 * COPY_BYTES]
+        if not cands:
+            raise SystemExit("no calibration copy kernel found in " + str(list(vals)))
+        return cands[0]
+
+    rows, scaled = [], 0.0
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        vals = per_kernel(path, counter)
+        cname, cv = copy_kernel(vals)
+        factor = (sum(cv) / len(cv)) / COPY_BYTES
+        for name, v in sorted(vals.items()):
+            if not name.startswith("void carve::") and "carve_" not in name:
+                continue
+            avg = sum(v) / len(v)
+            scaled += avg / factor
+            rows.append((counter, name.split("(")[0], len(v), avg, factor, avg / factor))
+        rows.append((counter, "calibration: " + cname.split("(")[0][:60], len(cv), sum(cv) / len(cv), factor,
+                     COPY_BYTES))
+    with open(traffic_file(wl), "w") as f:
+        f.write(f"# HBM traffic of carve_chunk_fwd, {wl.describe()}\n\n")
+        f.write("Counters from two rocprofv3 runs over the same committed command, one counter each:\n\n")
+        for c in commands:
+            f.write(f"    {c}\n")
+        f.write("\nEach per-dispatch value (KiB) is divided by the factor that the same counter reads for a "
+                f"plain device copy of {COPY_BYTES} bytes (read once, written once), run in the same process.\n\n")
+        f.write("| counter | kernel | dispatches | bytes per dispatch (raw) | copy factor | bytes (scaled) |\n")
+        f.write("|---|---|---|---|---|---|\n")
+        for r in rows:
+            f.write(f"| {r[0]} | `{r[1]}` | {r[2]} | {r[3]:.0f} | {r[4]:.4f} | {r[5]:.0f} |\n")
+        f.write(f"\n- HBM bytes per launch: {scaled:.0f}\n")
+        f.write(f"- algorithmic bytes per launch: {algorithmic_bytes(wl.B, wl.T, wl.H, wl.dk, wl.dv, 2 if wl.dtype == 'bf16' else 4, wl.rank)}\n")
+        f.write(f"- kernel sources sha256/16: `{sources_sha()}`\n")
+    print(open(traffic_file(wl)).read())
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="init_equiv",
+                    help="workload to time (default: the B4 H12 T2048 d64 L64 bf16 shape)")
+    ap.add_argument("--L", type=int, default=None, help="override the chunk length")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU work budget of the oracle baseline sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a plain device copy of known size first (for counter calibration)")
+    ap.add_argument("--write-traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the HBM traffic summary from two rocprofv3 --pmc csv files and exit")
+    ap.add_argument("--commands", nargs="*", default=[], help="commands recorded in the traffic summary")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -47,20 +182,35 @@ def main():
     from chunk_gated_delta_carve_amd import chunk_fwd
     from chunk_gated_delta_carve_amd.workloads import WORKLOADS, make_inputs, to_f64, to_torch
 
-    wl = WORKLOADS["init_equiv"]
+    wl = WORKLOADS[args.workload]
+    if args.L is not None:
+        wl = wl.with_(L=args.L)
+    if args.write_traffic_summary:
+        write_traffic_summary(wl, *args.write_traffic_summary, args.commands)
+        return
     inp = make_inputs(wl)
     t = {k: to_torch(v, wl.dtype) for k, v in inp.items()}
-    B, T, H, dk, dv, L = wl.B, wl.T, wl.H, wl.dk, wl.dv, wl.L
-    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device="cuda")
+    B, T, H, dk, dv, L, rank = wl.B, wl.T, wl.H, wl.dk, wl.dv, wl.L, wl.rank
+    tdtype = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    es = 2 if wl.dtype == "bf16" else 4
+    o = torch.empty((B, T, H, dv), dtype=tdtype, device="cuda")
     stream = torch.cuda.current_stream()
     from chunk_gated_delta_carve_amd import recurrent_ref_shapes
-    ws_bytes = int(recurrent_ref_shapes(B, H, T, dk, dv, L, 0, torch.bfloat16).workspace_bytes)
+    ws_bytes = int(recurrent_ref_shapes(B, H, T, dk, dv, L, rank, tdtype).workspace_bytes)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    ub = (t["U_down"], t["U_up"]) if rank > 0 else (None, None)
 
     def step():
-        return chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["bx"], t["w"], L=L, return_state=True, out=o,
-                         workspace=ws)
+        return chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["bx"], t["w"], L=L, ub_down=ub[0], ub_up=ub[1],
+                         return_state=True, out=o, workspace=ws)
 
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)                    # one elementwise kernel: reads and writes COPY_BYTES
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -93,9 +243,14 @@ def main():
         cold.append(s.elapsed_time(e))
     del flush
 
-    alg = algorithmic_bytes(B, T, H, dk, dv, 2)
+    alg = algorithmic_bytes(B, T, H, dk, dv, es, rank)
     achieved = alg / (avg_kernel_ms * 1e-3) / 1e9
     tokens = B * T
+    parallel = rank == 0 and wl.dtype == "bf16"
+    kernels = ("carve_intra_kernel + carve_state_kernel (one call)" if parallel
+               else "carve_chunk_serial_kernel")
+    workload = (f"carve_chunk_fwd B{B} H{H} T{T} dk{dk} dv{dv} L{L} {wl.dtype}, "
+                + ("no content projection" if rank == 0 else f"content projection rank {rank}"))
     line = {
         "metric": "tokens/s + MFMA/HBM roofline % of carve_chunk_fwd, B4 H12 T2048 d64 L64 bf16",
         "value": tokens / (ms_per_step * 1e-3),
@@ -107,24 +262,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), g=-softplus(N(0,1)), bx N(0,1), w=sigmoid(N(0,1)))",
-        "config": {"workload": "carve_chunk_fwd B4 H12 T2048 dk64 dv64 L64 bf16, no content projection",
-                   "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "L": L, "rank": 0},
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), g=-softplus(N(0,1)), bx N(0,1), "
+                "w=sigmoid(N(0,1))" + (f", U_b factors N(0,{wl.ub_std})" if rank else "") + ")",
+        "config": {"workload": workload, "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "L": L, "rank": rank},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "carve_intra_kernel + carve_state_kernel (one call)", "kernel_ms": avg_kernel_ms,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(wl),
+                     "kernel": kernels, "kernel_ms": avg_kernel_ms,
                      "algorithmic_bytes_per_launch": alg, "kernel_ms_cold_cache": float(np.median(cold))},
     }
     if not args.no_cpu_baseline:
-        from oracle import carve_forward
-        f = lambda k: to_f64(inp[k], wl.dtype)
-        tb = time.perf_counter()
-        carve_forward(f("q"), f("k"), f("v"), f("g"), f("bx"), f("w"), L)
-        cpu_s = time.perf_counter() - tb
-        line["cpu_baseline"] = {"value": tokens / cpu_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                                "sample": f"the whole workload (B={B}, T={T}, all {H} heads), one process, "
-                                          f"{cpu_s:.1f} s"}
+        line["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

@@ -23,8 +23,9 @@ int check_config(const carve_config* c) {
   if (!valid_width(c->dk) || !valid_width(c->dv) || c->dk != c->dv) return CARVE_EUNSUPPORTED;
   if (!valid_chunk(c->L)) return CARVE_EUNSUPPORTED;
   if (c->rank > 64) return CARVE_EUNSUPPORTED;
-  // offsets are computed in 64-bit, the grid in 32-bit
-  if ((int64_t)c->B * c->H > 0x7fffffffLL) return CARVE_EUNSUPPORTED;
+  // offsets are computed in 64-bit, grids in 32-bit (the state pass launches
+  // 8 (B H / 8 rounded up) (d_v / 16) single-wave workgroups)
+  if ((int64_t)c->B * c->H > 0x7fffffffLL / 8 - 8) return CARVE_EUNSUPPORTED;
   return CARVE_OK;
 }
 
@@ -82,15 +83,13 @@ hipError_t launch_parallel(const carve::FwdArgs& a, hipStream_t s) {
   auto intra = carve::carve_intra_kernel<E, D, D, BL>;
   auto state = carve::carve_state_kernel<E, D, D, BL>;
   hipError_t e = set_lds(intra, LY::intra_bytes);
-  constexpr int state_lds = 2 * LY::sBytes;
-  if (e == hipSuccess) e = set_lds(state, state_lds);
   if (e != hipSuccess) return e;
   if (nblk > 0) {
     hipLaunchKernelGGL(intra, dim3(a.B * a.H * nblk), dim3(LY::NT), LY::intra_bytes, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(state, dim3(a.B * a.H), dim3(LY::NT), state_lds, s, a);
+  hipLaunchKernelGGL(state, dim3(carve::state_grid(a.B * a.H, LY::NW)), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -31,6 +31,8 @@
 // LDS rows are padded by 16 bytes so that the 16 lanes of an MFMA fragment,
 // which read 16 consecutive rows, fall into different banks.
 #pragma once
+#include <type_traits>
+
 #include "common.h"
 
 namespace carve {
@@ -103,37 +105,29 @@ struct BlockLayout {
   static constexpr int oQd = oR2, oP = oR2 + BL * LD * ES;
   static constexpr int oV = oR3, oUt = oR3;                  // V is [KP][LV] (rows >= BL stay 0)
   static constexpr int oKdT = oR4;
-  static constexpr int oMt = intra_bytes;                    // [DK][LD] E   (chunk-serial only)
-  static constexpr int oQe = oMt + DK * LD * ES;             // [BL][LD] E
-  static constexpr int serial_bytes = oQe + BL * LD * ES;
+  // Mt and Qe as fragment units (see below), chunk-serial kernel only
+  static constexpr int TD = DK / 16;
+  static constexpr int NU = DK * ES / 64;                    // units per 16-row tile along d
+  static constexpr int oMt = intra_bytes;                    // [TD][NU][64] units
+  static constexpr int oQe = oMt + DK * DK * ES;             // [NB][NU][64] units
+  static constexpr int serial_bytes = oQe + BL * DK * ES;
   static_assert(serial_bytes <= 160 * 1024, "LDS budget");
   static_assert(oR1 % 16 == 0 && oR2 % 16 == 0 && oR3 % 16 == 0 && oR4 % 16 == 0 && oMt % 16 == 0, "alignment");
   static_assert(NB * 256 * 4 <= DK * LK * ES, "pairwise scratch fits in R4");
 
-  // ---- image of one block's state-pass operands (workspace):
-  //   Mt [DK][DK] and Qe [BL][DK], dense rows, staged through LDS by the
-  //   state pass; Ct and Ol in MFMA fragment order, [wave][tile][lane][4],
-  //   so each wave loads its own C tiles with one 8-byte load per lane.
-  static constexpr int TD = DK / 16;
-  static constexpr int wMt = 0;                              // [DK][DK] E  M^T
-  static constexpr int wQe = wMt + DK * DK * ES;             // [BL][DK] E
-  static constexpr int wCt = wQe + BL * DK * ES;             // [NW][TD][64][4] E  C^T
-  static constexpr int wOl = wCt + NW * TD * 256 * ES;       // [NW][NB][64][4] E
+  // ---- image of one block's state-pass operands (workspace), every part in
+  // the order in which a wave holds it, so each lane's share is contiguous:
+  //   Mt units [TD][NU][64 lanes][16 B]: A operands of M^T (rows d', k = d)
+  //   Qe units [NB][NU][64 lanes][16 B]: B operands of Qe^T (k = d, cols t)
+  //   Ct  [NW][TD][64 lanes][4] E: C tiles of C^T (rows d', cols e), per
+  //       16-channel value slice
+  //   Olt [NW][NB][64 lanes][4] E: C tiles of Ol^T (rows e, cols t), per slice
+  static constexpr int wMt = 0;
+  static constexpr int wQe = wMt + DK * DK * ES;
+  static constexpr int wCt = wQe + BL * DK * ES;
+  static constexpr int wOl = wCt + NW * TD * 256 * ES;
   static constexpr int wBytes = wOl + NW * NB * 256 * ES;
-  static constexpr int wStaged = wCt;                        // bytes staged through LDS
-  static_assert(wBytes % 16 == 0 && wStaged % 16 == 0, "16-byte copies");
-  // ---- padded staging copy of Mt and Qe in LDS (state pass)
-  static constexpr int sMt = 0;                              // [DK][LD]
-  static constexpr int sQe = sMt + DK * LD * ES;             // [BL][LD]
-  static constexpr int sBytes = sQe + BL * LD * ES;
-
-  // LDS offset (relative to a staging buffer) of the 16-byte chunk c of the image
-  __device__ __forceinline__ static int stage_offset(int c) {
-    const int b = 16 * c;
-    if (b < wQe) return sMt + (b / (DK * ES)) * LD * ES + b % (DK * ES);
-    const int x = b - wQe;
-    return sQe + (x / (DK * ES)) * LD * ES + x % (DK * ES);
-  }
+  static_assert(wBytes % 16 == 0, "16-byte units");
 };
 
 template <typename E>
@@ -166,12 +160,13 @@ struct Rows {
   __device__ __forceinline__ size_t row(int t) const { return (size_t)(bidx * T + t) * H + h; }
 };
 
-// Where a block's shared affine maps go: LDS (chunk-serial kernel) or the
-// workspace image (chunk-parallel kernel). C^T and Ol stay in registers.
+// Where a block's shared affine maps go, as fragment units: LDS (chunk-serial
+// kernel) or the workspace image (chunk-parallel kernel). C^T and Ol^T stay in
+// the registers of the wave that owns their value channels.
 template <typename E>
 struct Sink {
-  E* Mt; int ldMt;      // [DK][.]
-  E* Qe; int ldQe;      // [BL][.]
+  typename Mma<E>::unit* Mt;   // [TD][NU][64]
+  typename Mma<E>::unit* Qe;   // [NB][NU][64]
 };
 
 template <typename E, int DK, int DV, int BL>
@@ -179,7 +174,10 @@ struct Block {
   using LY = BlockLayout<E, DK, DV, BL>;
   using MM = Mma<E>;
   using Frag = typename MM::frag;
+  using Unit = typename MM::unit;
+  typedef E e4 __attribute__((ext_vector_type(4)));
   static constexpr int NW = LY::NW, NT = LY::NT, NB = LY::NB, KP = LY::KP, KS = MM::KS;
+  static constexpr int TD = LY::TD, NU = LY::NU, SPU = MM::SPU, UT = MM::UT;
   static constexpr int LD = LY::LD, LK = LY::LK, LV = LY::LV, LA = LY::LA, LTD = LY::LTD;
   static constexpr int TPW = (NB * NB + NW - 1) / NW;      // Gram tiles per wave
 
@@ -205,23 +203,22 @@ struct Block {
     return s;
   }
 
-  __device__ static Sink<E> lds_sink(const Smem& s) { return Sink<E>{s.Mt, LD, s.Qe, LD}; }
-  __device__ static Sink<E> image_sink(unsigned char* img) {
-    return Sink<E>{reinterpret_cast<E*>(img + LY::wMt), DK, reinterpret_cast<E*>(img + LY::wQe), DK};
+  __device__ static Sink<E> lds_sink(const Smem& s) {
+    return Sink<E>{reinterpret_cast<Unit*>(s.Mt), reinterpret_cast<Unit*>(s.Qe)};
   }
-  // this wave's C tiles <-> the fragment-ordered Ct / Ol arrays of an image
-  __device__ static void put_frags(unsigned char* img, const f32x4 (&CtR)[DK / 16], const f32x4 (&OlR)[NB]) {
+  __device__ static Sink<E> image_sink(unsigned char* img) {
+    return Sink<E>{reinterpret_cast<Unit*>(img + LY::wMt), reinterpret_cast<Unit*>(img + LY::wQe)};
+  }
+  // this wave's C^T and Ol^T tiles into an image (8 or 16 bytes per lane and tile)
+  __device__ static void put_frags(unsigned char* img, const f32x4 (&CtR)[TD], const f32x4 (&OltR)[NB]) {
     const int wave = wave_id(), lane = threadIdx.x & 63;
-    E* ct = reinterpret_cast<E*>(img + LY::wCt) + (wave * (DK / 16) * 64 + lane) * 4;
-    E* ol = reinterpret_cast<E*>(img + LY::wOl) + (wave * NB * 64 + lane) * 4;
+    e4* ct = reinterpret_cast<e4*>(img + LY::wCt) + wave * TD * 64 + lane;
+    e4* ol = reinterpret_cast<e4*>(img + LY::wOl) + wave * NB * 64 + lane;
+    auto cvt = [](f32x4 x) { return e4{from_f32<E>(x[0]), from_f32<E>(x[1]), from_f32<E>(x[2]), from_f32<E>(x[3])}; };
 #pragma unroll
-    for (int a = 0; a < DK / 16; ++a)
+    for (int a = 0; a < TD; ++a) ct[a * 64] = cvt(CtR[a]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ct[a * 256 + i] = from_f32<E>(CtR[a][i]);
-#pragma unroll
-    for (int a = 0; a < NB; ++a)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ol[a * 256 + i] = from_f32<E>(OlR[a][i]);
+    for (int a = 0; a < NB; ++a) ol[a * 64] = cvt(OltR[a]);
   }
 
   __device__ static void zero_lds(unsigned char* smem, int bytes) {
@@ -616,41 +613,47 @@ struct Block {
   //   Mt[d'][d] = e^{G_BL}[d] [d = d'] - sum_j Kdec[j][d'] W[j][d]
   //   Qe[r][d]  = Qd[r][d] - sum_j P[r][j] W[j][d]
   //   Ct[d'][e] = sum_j Kdec[j][d'] U[j][e]
-  //   Ol[r][e]  = sum_j P[r][j] U[j][e]
-  // Every product reads rows of a row-major left tile and rows of a
-  // transposed right tile (natural map over j); values are rounded to E.
-  // Mt and Qe tiles are spread over the waves and go to the sink; wave w
-  // computes the Ct and Ol tiles of its own value channels [16w, 16w+16) and
-  // keeps them in registers (CtR, OlR).
+  //   Olt[e][r] = sum_j P[r][j] U[j][e]
+  // Every product reads rows of two tiles whose columns run over j (natural
+  // map); values are rounded to E. Mt and Qe are computed transposed (C rows
+  // over d), so a lane's C values of UT adjacent tiles are exactly one
+  // operand unit over d: they go to the sink as 16-byte stores, spread over
+  // the waves. Wave w computes the Ct and Olt tiles of its own value
+  // channels [16w, 16w+16) and keeps them in registers (CtR, OltR).
   // Ends with a barrier.
-  __device__ static void affine(const Smem& s, const Sink<E>& out, f32x4 (&CtR)[DK / 16], f32x4 (&OlR)[NB]) {
+  __device__ static void affine(const Smem& s, const Sink<E>& out, f32x4 (&CtR)[TD], f32x4 (&OltR)[NB]) {
     const int wave = wave_id(), lane = threadIdx.x & 63;
     const int gq = lane >> 4, cc = lane & 15;
-    constexpr int TD = DK / 16;                       // tiles along d (== along e)
     auto product = [&](const E* left, int a, const E* right, int b, int nst) {
       f32x4 acc = zero4();
       for (int p = 0; p < nst; ++p)
         acc = MM::mma(MM::ld_nat(left, LK, 16 * a + cc, p * KS), MM::ld_nat(right, LK, 16 * b + cc, p * KS), acc);
       return acc;
     };
-    // Mt and Qe over all waves
-    constexpr int NSH = TD * TD + NB * TD;
-    for (int tile = wave; tile < NSH; tile += NW) {
-      const bool isM = tile < TD * TD;
-      const int x = isM ? tile : tile - TD * TD;
-      const int a = x / TD, b = x % TD;
-      // P is lower-triangular: row block a needs j < 16 (a + 1) only
-      const f32x4 acc = isM ? product(s.KdT, a, s.Wt, b, MM::steps(KP)) : product(s.P, a, s.Wt, b, MM::steps(16 * (a + 1)));
-      E* dst = isM ? out.Mt : out.Qe;
-      const int ld = isM ? out.ldMt : out.ldQe;
+    // units of Mt (rows d' = 16a + c) and then of Qe (rows r = 16a + c), dealt
+    // to the waves in turn
+    auto unit_job = [&](auto isM, int x) {
+      const int a = x / NU, u = x % NU;
+      f32x4 t[UT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * a + 4 * gq + i, c = 16 * b + cc;
-        const float v = isM ? (r == c ? s.Egl[c] : 0.f) - acc[i] : to_f32(s.Qd[r * LD + c]) - acc[i];
-        dst[r * ld + c] = from_f32<E>(v);
+      for (int j = 0; j < UT; ++j) {
+        const int b = UT * u + j;                     // 16-wide slice of d
+        // P is lower-triangular: row block a needs j < 16 (a + 1) only
+        const f32x4 acc = isM ? product(s.Wt, b, s.KdT, a, MM::steps(KP))
+                              : product(s.Wt, b, s.P, a, MM::steps(16 * (a + 1)));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d = 16 * b + 4 * gq + i, r = 16 * a + cc;
+          t[j][i] = isM ? (d == r ? s.Egl[d] : 0.f) - acc[i] : to_f32(s.Qd[r * LD + d]) - acc[i];
+        }
       }
-    }
-    // Ct and Ol of this wave's value channels
+      if constexpr (decltype(isM)::value) out.Mt[x * 64 + lane] = MM::pack(t);
+      else out.Qe[x * 64 + lane] = MM::pack(t);
+    };
+    constexpr int NMJ = TD * NU;
+    for (int x = wave; x < NMJ; x += NW) unit_job(std::true_type{}, x);
+    for (int x = ((wave - NMJ) % NW + NW) % NW; x < NB * NU; x += NW) unit_job(std::false_type{}, x);
+    // Ct and Olt of this wave's value channels
 #pragma unroll
     for (int a = 0; a < TD; ++a) {
       f32x4 acc = product(s.KdT, a, s.Ut, wave, MM::steps(KP));
@@ -660,59 +663,81 @@ struct Block {
     }
 #pragma unroll
     for (int a = 0; a < NB; ++a) {
-      f32x4 acc = product(s.P, a, s.Ut, wave, MM::steps(16 * (a + 1)));
+      f32x4 acc = product(s.Ut, wave, s.P, a, MM::steps(16 * (a + 1)));
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = to_f32(from_f32<E>(acc[i]));
-      OlR[a] = acc;
+      OltR[a] = acc;
     }
     __syncthreads();
   }
 
   // -------------------------------------------------------------- state and output
-  // Per wave (its 16 value channels), with S^T held as C tiles:
-  //   O   = Qe S^T + Ol            (S at the block start)
+  // One wave, 16 value channels, S^T held as C tiles (rows d, cols e):
+  //   O^T = S Qe^T + Ol^T      (S at the block start; tile rt holds tokens
+  //                             16 rt .. 16 rt + 15 as columns)
   //   S^T <- Mt S^T + Ct
-  // Mt [DK][ldm] and Qe [BL][ldq] are shared tiles; Ct and Ol are this
-  // wave's C tiles.
-  __device__ static void state_step(const E* Mt, int ldm, const E* Qe, int ldq, const f32x4 (&Ct)[DK / 16],
-                                    const f32x4 (&Ol)[NB], f32x4 (&St)[DK / 16], f32x4 (&Ot)[NB]) {
-    const int lane = threadIdx.x & 63;
-    const int cc = lane & 15;
+  // The S fragments serve as the A operand of the first product and the B
+  // operand of the second. mt(dt, u) and qe(rt, u) return operand units.
+  template <typename MtF, typename QeF>
+  __device__ static void state_step(MtF mt, QeF qe, const f32x4 (&Ct)[TD], const f32x4 (&Olt)[NB],
+                                    f32x4 (&St)[TD], f32x4 (&Ot)[NB]) {
     Frag sf[DK / KS];
 #pragma unroll
     for (int p = 0; p < DK / KS; ++p) sf[p] = MM::from_c(St, p);
 #pragma unroll
     for (int rt = 0; rt < NB; ++rt) {
-      f32x4 acc = Ol[rt];
+      f32x4 acc = Olt[rt];
 #pragma unroll
-      for (int p = 0; p < DK / KS; ++p) acc = MM::mma(MM::ld_cp(Qe, ldq, 16 * rt + cc, p), sf[p], acc);
+      for (int u = 0; u < NU; ++u) {
+        const Unit q = qe(rt, u);
+#pragma unroll
+        for (int j = 0; j < SPU; ++j) acc = MM::mma(sf[u * SPU + j], MM::step(q, j), acc);
+      }
       Ot[rt] = acc;
     }
 #pragma unroll
-    for (int dt = 0; dt < DK / 16; ++dt) {
+    for (int dt = 0; dt < TD; ++dt) {
       f32x4 acc = Ct[dt];
 #pragma unroll
-      for (int p = 0; p < DK / KS; ++p) acc = MM::mma(MM::ld_cp(Mt, ldm, 16 * dt + cc, p), sf[p], acc);
+      for (int u = 0; u < NU; ++u) {
+        const Unit m = mt(dt, u);
+#pragma unroll
+        for (int j = 0; j < SPU; ++j) acc = MM::mma(MM::step(m, j), sf[u * SPU + j], acc);
+      }
       St[dt] = acc;
     }
   }
 
-  // load/store S^T C tiles of this wave from/to a [B,H,DV,DK] fp32 tensor
-  __device__ static void load_state(const float* S, int bh, f32x4 (&St)[DK / 16]) {
-    const int wave = wave_id(), lane = threadIdx.x & 63;
+  // load/store the S^T C tiles of value slice `ws` from/to a [B,H,DV,DK] fp32 tensor
+  __device__ static void load_state(const float* S, int bh, int ws, f32x4 (&St)[TD]) {
+    const int lane = threadIdx.x & 63;
     const int gq = lane >> 4, cc = lane & 15;
 #pragma unroll
-    for (int dt = 0; dt < DK / 16; ++dt) {
-      if (S) St[dt] = *reinterpret_cast<const f32x4*>(S + ((size_t)bh * DV + 16 * wave + cc) * DK + 16 * dt + 4 * gq);
+    for (int dt = 0; dt < TD; ++dt) {
+      if (S) St[dt] = *reinterpret_cast<const f32x4*>(S + ((size_t)bh * DV + 16 * ws + cc) * DK + 16 * dt + 4 * gq);
       else St[dt] = zero4();
     }
   }
-  __device__ static void store_state(float* S, int bh, const f32x4 (&St)[DK / 16]) {
-    const int wave = wave_id(), lane = threadIdx.x & 63;
+  __device__ static void store_state(float* S, int bh, int ws, const f32x4 (&St)[TD]) {
+    const int lane = threadIdx.x & 63;
     const int gq = lane >> 4, cc = lane & 15;
 #pragma unroll
-    for (int dt = 0; dt < DK / 16; ++dt)
-      *reinterpret_cast<f32x4*>(S + ((size_t)bh * DV + 16 * wave + cc) * DK + 16 * dt + 4 * gq) = St[dt];
+    for (int dt = 0; dt < TD; ++dt)
+      *reinterpret_cast<f32x4*>(S + ((size_t)bh * DV + 16 * ws + cc) * DK + 16 * dt + 4 * gq) = St[dt];
+  }
+
+  // O^T tile rt of this slice: lane (g, c) writes token t0 + 16 rt + c, value
+  // channels e0 + 4g .. e0 + 4g + 3, one vector store per lane
+  __device__ static void store_out(E* O, const Rows<E>& src, int t0, int nvalid, int e0, const f32x4 (&Ot)[NB]) {
+    const int lane = threadIdx.x & 63;
+    const int gq = lane >> 4, cc = lane & 15;
+#pragma unroll
+    for (int rt = 0; rt < NB; ++rt) {
+      const int r = 16 * rt + cc;
+      if (r < nvalid)
+        *reinterpret_cast<e4*>(O + src.row(t0 + r) * DV + e0 + 4 * gq) =
+            e4{from_f32<E>(Ot[rt][0]), from_f32<E>(Ot[rt][1]), from_f32<E>(Ot[rt][2]), from_f32<E>(Ot[rt][3])};
+    }
   }
 };
 

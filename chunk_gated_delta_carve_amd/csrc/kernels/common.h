@@ -51,9 +51,20 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 // MFMA policy per operand type.
 template <typename M> struct Mma;
 
+// A "unit" is 16 bytes per lane (1 KiB per wave): the operand fragments of one
+// 16-row tile over KU consecutive reduction indices (c-pair map), i.e. SPU
+// instructions' worth. Units are what the state pass loads and stores.
 template <> struct Mma<bf16> {
   static constexpr int KS = 32;  // reduction length of one instruction
   typedef bf16x8 frag;
+  typedef bf16x8 unit;
+  static constexpr int KU = 32, SPU = 1, UT = 2;   // k per unit, steps per unit, C tiles per unit
+  __device__ __forceinline__ static frag step(unit u, int) { return u; }
+  // unit from C tiles of a transposed product: t[j] holds k = 16 (UT u + j) + 4g + i
+  __device__ __forceinline__ static unit pack(const f32x4* t) {
+    return unit{(bf16)t[0][0], (bf16)t[0][1], (bf16)t[0][2], (bf16)t[0][3],
+                (bf16)t[1][0], (bf16)t[1][1], (bf16)t[1][2], (bf16)t[1][3]};
+  }
   __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
@@ -90,6 +101,10 @@ template <> struct Mma<bf16> {
 template <> struct Mma<float> {
   static constexpr int KS = 4;
   typedef float frag;
+  typedef f32x4 unit;
+  static constexpr int KU = 16, SPU = 4, UT = 1;
+  __device__ __forceinline__ static frag step(unit u, int j) { return u[j]; }
+  __device__ __forceinline__ static unit pack(const f32x4* t) { return t[0]; }
   __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
   }
@@ -132,6 +147,15 @@ template <> struct Mma16<float> {
 __device__ __forceinline__ float sum_groups(float x) {
   x += __shfl_xor(x, 16);
   x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Sum over the 16 columns of a C tile row group: lanes 16g .. 16g+15.
+__device__ __forceinline__ f32x4 sum_cols(f32x4 x) {
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] += __shfl_xor(x[i], m);
   return x;
 }
 

@@ -44,7 +44,7 @@ carve_chunk_serial_kernel(FwdArgs a) {
   B::zero_lds(smem, LY::serial_bytes);
   const Sink<E> sink = B::lds_sink(s);
   f32x4 St[DK / 16];
-  B::load_state(a.state_in, bh, St);
+  B::load_state(a.state_in, bh, wave, St);
   __syncthreads();
   for (int e = tid; e < DV; e += NT) s.M[e] = a.mean_in ? a.mean_in[(size_t)bh * DV + e] : 0.f;
   __syncthreads();
@@ -68,8 +68,11 @@ carve_chunk_serial_kernel(FwdArgs a) {
   };
   content_bias();
 
-  float m_part = 0.f;                   // running column sum of O for this lane's channel
+  f32x4 m_part = zero4();               // running sums of O over tokens, channels e0 + 4g + i
   const int nblk = (T + BL - 1) / BL;
+  using Unit = typename B::Unit;
+  const Unit* mtu = sink.Mt;
+  const Unit* qeu = sink.Qe;
   for (int blk = 0; blk < nblk; ++blk) {
     const int t0 = blk * BL;
     const int nvalid = min(BL, T - t0);
@@ -79,30 +82,27 @@ carve_chunk_serial_kernel(FwdArgs a) {
     B::grams(s, src, t0, nvalid, fallback, Pt);
     B::inverse_diag(s);
     B::solve(s, qd, Pt);
-    f32x4 CtR[DK / 16], OlR[NB], Ot[NB];
-    B::affine(s, sink, CtR, OlR);
-    B::state_step(s.Mt, LY::LD, s.Qe, LY::LD, CtR, OlR, St, Ot);
+    f32x4 CtR[DK / 16], OltR[NB], Ot[NB];
+    B::affine(s, sink, CtR, OltR);
+    B::state_step([&](int dt, int u) { return mtu[(dt * LY::NU + u) * 64 + lane]; },
+                  [&](int rt, int u) { return qeu[(rt * LY::NU + u) * 64 + lane]; }, CtR, OltR, St, Ot);
 #pragma unroll
-    for (int rt = 0; rt < NB; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * gq + i;
-        m_part += Ot[rt][i];                       // rows past nvalid are exactly 0
-        if (r < nvalid) O[src.row(t0 + r) * DV + e0 + cc] = from_f32<E>(Ot[rt][i]);
-      }
+    for (int rt = 0; rt < NB; ++rt) m_part += Ot[rt];   // tokens past nvalid are exactly 0
+    B::store_out(O, src, t0, nvalid, e0, Ot);
     __syncthreads();
     const bool chunk_end = ((t0 + BL) % L == 0) || (t0 + BL >= T);
     if (chunk_end) {
       const int chunk = t0 / L;
       const int count = min(L, T - chunk * L);
-      const float tot = sum_groups(m_part);
-      if (gq == 0) s.M[e0 + cc] = tot / (float)count;
-      m_part = 0.f;
+      const f32x4 tot = sum_cols(m_part);
+      if (cc == 0)
+        *reinterpret_cast<f32x4*>(s.M + e0 + 4 * gq) = tot * (1.0f / (float)count);
+      m_part = zero4();
       __syncthreads();
       if (t0 + BL < T) content_bias();
     }
   }
-  if (a.state_out) B::store_state(a.state_out, bh, St);
+  if (a.state_out) B::store_state(a.state_out, bh, wave, St);
   if (a.mean_out)
     for (int e = tid; e < DV; e += NT) a.mean_out[(size_t)bh * DV + e] = s.M[e];
 }
@@ -137,137 +137,121 @@ carve_intra_kernel(FwdArgs a) {
   B::grams(s, src, t0, nvalid, fallback, Pt);
   B::inverse_diag(s);
   B::solve(s, qd, Pt);
-  f32x4 CtR[DK / 16], OlR[LY::NB];
-  B::affine(s, sink, CtR, OlR);
-  B::put_frags(img, CtR, OlR);
+  f32x4 CtR[DK / 16], OltR[LY::NB];
+  B::affine(s, sink, CtR, OltR);
+  B::put_frags(img, CtR, OltR);
 }
 
-// One workgroup per (batch, head): the serial state pass and the output.
-// Each block's Mt and Qe stream through two LDS buffers (the next block's are
-// fetched into registers while the current block is used); each wave loads
-// its own C^T / Ol fragments straight into registers, one block ahead.
-// Outputs are staged in LDS over the current Qe tile once every wave has
-// used it, and written as 16-byte row chunks.
+// Placement of the state pass: one single-wave workgroup per (batch, head,
+// 16-channel value slice). Workgroups are dealt to the XCDs round-robin, so
+// the NW slices of one (batch, head) are given ids that are equal modulo 8:
+// they then share one L2 for the block images they all read and for the
+// output rows they write together.
+__host__ __device__ inline int state_grid(int BH, int NW) { return (BH + 7) / 8 * 8 * NW; }
+__device__ inline bool state_place(int id, int BH, int NW, int& bh, int& ws) {
+  const int r = id / 8;
+  ws = r % NW;
+  bh = id % 8 + 8 * (r / NW);
+  return bh < BH;
+}
+
+// Register sets that hold one block's image for one wave.
 template <typename E, int DK, int DV, int BL>
-__global__ void __launch_bounds__((BlockLayout<E, DK, DV, BL>::NT))
+struct ImageRegs {
+  using B = Block<E, DK, DV, BL>;
+  using LY = typename B::LY;
+  using Unit = typename B::Unit;
+  using e4 = typename B::e4;
+  typename B::Unit mt[LY::TD][LY::NU], qe[LY::NB][LY::NU];
+  e4 ct[LY::TD], ol[LY::NB];
+  __device__ __forceinline__ void fetch(const unsigned char* img, int ws, int lane) {
+    const Unit* m = reinterpret_cast<const Unit*>(img + LY::wMt) + lane;
+    const Unit* q = reinterpret_cast<const Unit*>(img + LY::wQe) + lane;
+    const e4* c = reinterpret_cast<const e4*>(img + LY::wCt) + ws * LY::TD * 64 + lane;
+    const e4* o = reinterpret_cast<const e4*>(img + LY::wOl) + ws * LY::NB * 64 + lane;
+#pragma unroll
+    for (int t = 0; t < LY::TD; ++t)
+#pragma unroll
+      for (int u = 0; u < LY::NU; ++u) mt[t][u] = m[(t * LY::NU + u) * 64];
+#pragma unroll
+    for (int t = 0; t < LY::NB; ++t)
+#pragma unroll
+      for (int u = 0; u < LY::NU; ++u) qe[t][u] = q[(t * LY::NU + u) * 64];
+#pragma unroll
+    for (int t = 0; t < LY::TD; ++t) ct[t] = c[t * 64];
+#pragma unroll
+    for (int t = 0; t < LY::NB; ++t) ol[t] = o[t * 64];
+  }
+};
+
+// The serial state pass and the output: every wave runs its own value slice
+// through all blocks with no LDS and no barriers. A block's image is loaded
+// into registers PD blocks before it is used (PD + 1 register sets, rotated by
+// unrolling the block loop).
+template <typename E, int DK, int DV, int BL>
+__global__ void __launch_bounds__(64)
 carve_state_kernel(FwdArgs a) {
   using B = Block<E, DK, DV, BL>;
   using LY = typename B::LY;
-  constexpr int NT = LY::NT, NB = LY::NB, ES = LY::ES, TD = DK / 16;
-  constexpr int CH = LY::wStaged / 16;                // 16-byte chunks staged per image
-  constexpr int PER = (CH + NT - 1) / NT;             // chunks per thread
-  constexpr int OCPR = DV * ES / 16;                  // output chunks per row
-  constexpr int LO = DV + LY::PE;                     // pitch of the staged output
-  static_assert(2 * LY::sBytes <= 160 * 1024, "staging buffers fit");
-  static_assert(BL * LO * ES <= BL * LY::LD * ES, "output staging fits over Qe");
-  static_assert(DV * ES % 16 == 0, "16-byte output rows");
-  extern __shared__ __align__(16) unsigned char smem[];
-
-  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
+  using R = ImageRegs<E, DK, DV, BL>;
+  constexpr int NB = LY::NB, TD = LY::TD, NW = LY::NW;
+  constexpr int NS = DK == 64 ? 3 : 1;                 // register sets (prefetch depth NS - 1)
+  const int lane = threadIdx.x;
   const int gq = lane >> 4, cc = lane & 15;
-  const int bh = blockIdx.x;
   const int T = a.T, H = a.H, L = a.L;
-  const int bidx = bh / H, h = bh % H;
+  int bh, ws;
+  if (!state_place(blockIdx.x, a.B * H, NW, bh, ws)) return;
+  const int e0 = 16 * ws;
   const int nblk = (T + BL - 1) / BL;
-  const int e0 = 16 * wave;
   E* __restrict__ O = static_cast<E*>(a.o);
   const unsigned char* imgs = static_cast<const unsigned char*>(a.ws) + (size_t)bh * nblk * LY::wBytes;
+  const Rows<E> dst{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, T, H, bh / H, bh % H};
 
-  f32x4 St[DK / 16];
-  B::load_state(a.state_in, bh, St);
+  f32x4 St[TD];
+  B::load_state(a.state_in, bh, ws, St);
   const int mstart = T > 0 ? ((T - 1) / L) * L : 0;   // first token of the last chunk
-  float m_part = 0.f;
+  f32x4 m_part = zero4();
 
-  typedef E e4 __attribute__((ext_vector_type(4)));
-  // register sets for the images of the next PD blocks
-  constexpr int PD = DK == 64 ? 2 : 1;                 // prefetch depth
-  f32x4 pre[PD][PER];
-  e4 ctn[PD][TD], oln[PD][NB];
-  auto fetch = [&](int blk, f32x4 (&pr)[PER], e4 (&ct4)[TD], e4 (&ol4)[NB]) {
-    const unsigned char* img = imgs + (size_t)blk * LY::wBytes;
-    const f32x4* g = reinterpret_cast<const f32x4*>(img);
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int c = tid + j * NT;
-      if (c < CH) pr[j] = g[c];
-    }
-    const e4* ct = reinterpret_cast<const e4*>(img + LY::wCt) + wave * TD * 64 + lane;
-    const e4* ol = reinterpret_cast<const e4*>(img + LY::wOl) + wave * NB * 64 + lane;
-#pragma unroll
-    for (int t = 0; t < TD; ++t) ct4[t] = ct[t * 64];
-#pragma unroll
-    for (int t = 0; t < NB; ++t) ol4[t] = ol[t * 64];
-  };
-  f32x4 CtR[TD], OlR[NB];
-  auto deposit = [&](int buf, const f32x4 (&pr)[PER], const e4 (&ct4)[TD], const e4 (&ol4)[NB]) {
-    unsigned char* d = smem + buf * LY::sBytes;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int c = tid + j * NT;
-      if (c < CH) *reinterpret_cast<f32x4*>(d + LY::stage_offset(c)) = pr[j];
-    }
+  R set[NS];
+  auto step = [&](int blk, R& r) {
+    f32x4 Ct[TD], Olt[NB], Ot[NB];
 #pragma unroll
     for (int t = 0; t < TD; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) CtR[t][i] = to_f32(ct4[t][i]);
+      for (int i = 0; i < 4; ++i) Ct[t][i] = to_f32(r.ct[t][i]);
 #pragma unroll
     for (int t = 0; t < NB; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) OlR[t][i] = to_f32(ol4[t][i]);
-  };
-  // one block: state and output from buffer `cur`; its successor waits in
-  // register set `nx`, and set `ld` receives the block PD ahead
-  auto step = [&](int blk, int cur, f32x4 (&prn)[PER], e4 (&ctx)[TD], e4 (&olx)[NB],
-                  f32x4 (&prl)[PER], e4 (&ctl)[TD], e4 (&oll)[NB]) {
-    if (blk + PD < nblk) fetch(blk + PD, prl, ctl, oll);
-    unsigned char* buf = smem + cur * LY::sBytes;
-    f32x4 Ot[NB];
-    B::state_step(reinterpret_cast<const E*>(buf + LY::sMt), LY::LD, reinterpret_cast<const E*>(buf + LY::sQe),
-                  LY::LD, CtR, OlR, St, Ot);
+      for (int i = 0; i < 4; ++i) Olt[t][i] = to_f32(r.ol[t][i]);
+    B::state_step([&](int dt, int u) { return r.mt[dt][u]; }, [&](int rt, int u) { return r.qe[rt][u]; },
+                  Ct, Olt, St, Ot);
     const int t0 = blk * BL;
     const int nvalid = min(BL, T - t0);
-    E* so = reinterpret_cast<E*>(buf + LY::sQe);      // [BL][LO] over the used Qe tile
-    __syncthreads();                                 // every wave is done with Qe
 #pragma unroll
     for (int rt = 0; rt < NB; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * gq + i;
-        if (t0 + r >= mstart) m_part += Ot[rt][i];   // rows past nvalid are exactly 0
-        so[r * LO + e0 + cc] = from_f32<E>(Ot[rt][i]);
-      }
-    __syncthreads();
-    for (int c = tid; c < nvalid * OCPR; c += NT) {
-      const int r = c / OCPR, k = c % OCPR;
-      *reinterpret_cast<f32x4*>(O + ((size_t)(bidx * T + t0 + r) * H + h) * DV + k * (16 / ES)) =
-          *reinterpret_cast<const f32x4*>(so + r * LO + k * (16 / ES));
-    }
-    if (blk + 1 < nblk) deposit(cur ^ 1, prn, ctx, olx);
-    __syncthreads();
+      if (t0 + 16 * rt + cc >= mstart) m_part += Ot[rt];   // tokens past nvalid are exactly 0
+    B::store_out(O, dst, t0, nvalid, e0, Ot);
+    if (blk + NS < nblk) r.fetch(imgs + (size_t)(blk + NS) * LY::wBytes, ws, lane);
   };
-  if (nblk > 0) {
-    fetch(0, pre[0], ctn[0], oln[0]);
-    deposit(0, pre[0], ctn[0], oln[0]);
-    if (PD == 2 && nblk > 1) fetch(1, pre[0], ctn[0], oln[0]);
+#pragma unroll
+  for (int j = 0; j < NS; ++j)
+    if (j < nblk) set[j].fetch(imgs + (size_t)j * LY::wBytes, ws, lane);
+  for (int blk = 0; blk < nblk; blk += NS) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+      if (blk + j < nblk) step(blk + j, set[j]);
   }
-  __syncthreads();
-  if constexpr (PD == 2) {
-    // set 0 holds block blk+1 at even blk, set 1 at odd blk
-    for (int blk = 0; blk < nblk; blk += 2) {
-      step(blk, 0, pre[0], ctn[0], oln[0], pre[1], ctn[1], oln[1]);
-      if (blk + 1 < nblk) step(blk + 1, 1, pre[1], ctn[1], oln[1], pre[0], ctn[0], oln[0]);
-    }
-  } else {
-    for (int blk = 0; blk < nblk; ++blk)
-      step(blk, blk & 1, pre[0], ctn[0], oln[0], pre[0], ctn[0], oln[0]);
-  }
-  if (a.state_out) B::store_state(a.state_out, bh, St);
+  if (a.state_out) B::store_state(a.state_out, bh, ws, St);
   if (a.mean_out) {
-    const float tot = sum_groups(m_part);
-    if (T == 0) {
-      for (int e = tid; e < DV; e += NT) a.mean_out[(size_t)bh * DV + e] = a.mean_in ? a.mean_in[(size_t)bh * DV + e] : 0.f;
-    } else if (gq == 0) {
-      a.mean_out[(size_t)bh * DV + e0 + cc] = tot / (float)(T - mstart);
+    const f32x4 tot = sum_cols(m_part);
+    float* mo = a.mean_out + (size_t)bh * DV + e0 + 4 * gq;
+    if (cc == 0) {
+      if (T == 0) {
+        *reinterpret_cast<f32x4*>(mo) = a.mean_in ? *reinterpret_cast<const f32x4*>(a.mean_in + (size_t)bh * DV + e0 + 4 * gq)
+                                                  : zero4();
+      } else {
+        *reinterpret_cast<f32x4*>(mo) = tot * (1.0f / (float)(T - mstart));
+      }
     }
   }
 }

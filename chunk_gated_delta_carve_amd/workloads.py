@@ -49,6 +49,14 @@ class Workload:
     def head_tokens(self) -> int:
         return self.B * self.T * self.H
 
+    def tag(self) -> str:
+        """File-name tag, e.g. B4H12T2048_d64_L64_bf16 (plus _r16 with a content projection)."""
+        return f"B{self.B}H{self.H}T{self.T}_d{self.dk}_L{self.L}_{self.dtype}" + (f"_r{self.rank}" if self.rank else "")
+
+    def describe(self) -> str:
+        return (f"B={self.B} H={self.H} T={self.T} d_k={self.dk} d_v={self.dv} L={self.L} {self.dtype}, "
+                + (f"content projection rank {self.rank}" if self.rank else "no content projection"))
+
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
 
