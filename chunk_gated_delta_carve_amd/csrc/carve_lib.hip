@@ -13,6 +13,8 @@ namespace {
 
 thread_local char g_hip_msg[256] = "no HIP error recorded";
 
+size_t elem_bytes(int dtype) { return dtype == CARVE_F32 ? 4 : 2; }
+
 bool valid_width(int d) { return d == 64 || d == 128; }
 bool valid_chunk(int L) { return L == 16 || L == 32 || L == 64 || L == 128; }
 
@@ -26,10 +28,10 @@ int check_config(const carve_config* c) {
   // offsets are computed in 64-bit, grids in 32-bit (the state pass launches
   // 8 (B H / 8 rounded up) (d_v / 16) single-wave workgroups)
   if ((int64_t)c->B * c->H > 0x7fffffffLL / 8 - 8) return CARVE_EUNSUPPORTED;
+  // per-lane output offsets inside 16 token rows are 32-bit
+  if ((int64_t)16 * c->H * c->dv * elem_bytes(c->dtype) > 0x7fffffffLL) return CARVE_EUNSUPPORTED;
   return CARVE_OK;
 }
-
-size_t elem_bytes(int dtype) { return dtype == CARVE_F32 ? 4 : 2; }
 
 bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u); }
 

@@ -164,23 +164,27 @@ struct ImageRegs {
   using e4 = typename B::e4;
   typename B::Unit mt[LY::TD][LY::NU], qe[LY::NB][LY::NU];
   e4 ct[LY::TD], ol[LY::NB];
+  // img is uniform; every load is (uniform base + 16 lane), so addresses stay
+  // in scalar registers
   __device__ __forceinline__ void fetch(const unsigned char* img, int ws, int lane) {
-    const Unit* m = reinterpret_cast<const Unit*>(img + LY::wMt) + lane;
-    const Unit* q = reinterpret_cast<const Unit*>(img + LY::wQe) + lane;
-    const e4* c = reinterpret_cast<const e4*>(img + LY::wCt) + ws * LY::TD * 64 + lane;
-    const e4* o = reinterpret_cast<const e4*>(img + LY::wOl) + ws * LY::NB * 64 + lane;
+    const uint32_t lo = 16u * lane, lo8 = 8u * lane;
 #pragma unroll
     for (int t = 0; t < LY::TD; ++t)
 #pragma unroll
-      for (int u = 0; u < LY::NU; ++u) mt[t][u] = m[(t * LY::NU + u) * 64];
+      for (int u = 0; u < LY::NU; ++u)
+        mt[t][u] = *reinterpret_cast<const Unit*>(img + LY::wMt + (t * LY::NU + u) * 1024 + lo);
 #pragma unroll
     for (int t = 0; t < LY::NB; ++t)
 #pragma unroll
-      for (int u = 0; u < LY::NU; ++u) qe[t][u] = q[(t * LY::NU + u) * 64];
+      for (int u = 0; u < LY::NU; ++u)
+        qe[t][u] = *reinterpret_cast<const Unit*>(img + LY::wQe + (t * LY::NU + u) * 1024 + lo);
+    constexpr int CB = 64 * sizeof(e4);                     // bytes per C-tile record
 #pragma unroll
-    for (int t = 0; t < LY::TD; ++t) ct[t] = c[t * 64];
+    for (int t = 0; t < LY::TD; ++t)
+      ct[t] = *reinterpret_cast<const e4*>(img + LY::wCt + (ws * LY::TD + t) * CB + lo8 * (sizeof(e4) / 8));
 #pragma unroll
-    for (int t = 0; t < LY::NB; ++t) ol[t] = o[t * 64];
+    for (int t = 0; t < LY::NB; ++t)
+      ol[t] = *reinterpret_cast<const e4*>(img + LY::wOl + (ws * LY::NB + t) * CB + lo8 * (sizeof(e4) / 8));
   }
 };
 
@@ -195,7 +199,7 @@ carve_state_kernel(FwdArgs a) {
   using LY = typename B::LY;
   using R = ImageRegs<E, DK, DV, BL>;
   constexpr int NB = LY::NB, TD = LY::TD, NW = LY::NW;
-  constexpr int NS = DK == 64 ? 3 : 1;                 // register sets (prefetch depth NS - 1)
+  constexpr int NS = DK == 64 ? 2 : 1;                 // register sets (prefetch depth NS - 1)
   const int lane = threadIdx.x;
   const int gq = lane >> 4, cc = lane & 15;
   const int T = a.T, H = a.H, L = a.L;
@@ -205,7 +209,8 @@ carve_state_kernel(FwdArgs a) {
   const int nblk = (T + BL - 1) / BL;
   E* __restrict__ O = static_cast<E*>(a.o);
   const unsigned char* imgs = static_cast<const unsigned char*>(a.ws) + (size_t)bh * nblk * LY::wBytes;
-  const Rows<E> dst{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, T, H, bh / H, bh % H};
+  const int bidx = bh / H, h = bh % H;
+  const uint32_t olane = (uint32_t)(((size_t)cc * H * DV + (size_t)h * DV + e0 + 4 * gq) * sizeof(E));
 
   f32x4 St[TD];
   B::load_state(a.state_in, bh, ws, St);
@@ -213,7 +218,10 @@ carve_state_kernel(FwdArgs a) {
   f32x4 m_part = zero4();
 
   R set[NS];
-  auto step = [&](int blk, R& r) {
+  // The refill of a register set is unconditional (the block index is clamped
+  // into the image), so every set always has exactly one load group in flight
+  // and the waits before a block cover only that block's loads.
+  auto step = [&](int blk, R& r, bool refill) {
     f32x4 Ct[TD], Olt[NB], Ot[NB];
 #pragma unroll
     for (int t = 0; t < TD; ++t)
@@ -225,22 +233,35 @@ carve_state_kernel(FwdArgs a) {
       for (int i = 0; i < 4; ++i) Olt[t][i] = to_f32(r.ol[t][i]);
     B::state_step([&](int dt, int u) { return r.mt[dt][u]; }, [&](int rt, int u) { return r.qe[rt][u]; },
                   Ct, Olt, St, Ot);
+    if (refill) r.fetch(imgs + (size_t)min(blk + NS, nblk - 1) * LY::wBytes, ws, lane);
     const int t0 = blk * BL;
-    const int nvalid = min(BL, T - t0);
+    if (t0 + BL > mstart) {                           // the block reaches into the last chunk
 #pragma unroll
-    for (int rt = 0; rt < NB; ++rt)
-      if (t0 + 16 * rt + cc >= mstart) m_part += Ot[rt];   // tokens past nvalid are exactly 0
-    B::store_out(O, dst, t0, nvalid, e0, Ot);
-    if (blk + NS < nblk) r.fetch(imgs + (size_t)(blk + NS) * LY::wBytes, ws, lane);
+      for (int rt = 0; rt < NB; ++rt)
+        if (t0 + 16 * rt + cc >= mstart) m_part += Ot[rt];   // tokens past T are exactly 0
+    }
+    // O^T tile rt: lane (g, c) writes token t0 + 16 rt + c, channels e0 + 4g .. e0 + 4g + 3
+    E* ob = O + ((size_t)bidx * T + t0) * H * DV;     // uniform
+#pragma unroll
+    for (int rt = 0; rt < NB; ++rt) {
+      const typename B::e4 v{from_f32<E>(Ot[rt][0]), from_f32<E>(Ot[rt][1]), from_f32<E>(Ot[rt][2]),
+                             from_f32<E>(Ot[rt][3])};
+      if (t0 + 16 * rt + 16 <= T || t0 + 16 * rt + cc < T)
+        *reinterpret_cast<typename B::e4*>(reinterpret_cast<unsigned char*>(ob + (size_t)16 * rt * H * DV) + olane) = v;
+    }
   };
+  if (nblk > 0) {
 #pragma unroll
-  for (int j = 0; j < NS; ++j)
-    if (j < nblk) set[j].fetch(imgs + (size_t)j * LY::wBytes, ws, lane);
-  for (int blk = 0; blk < nblk; blk += NS) {
-#pragma unroll
-    for (int j = 0; j < NS; ++j)
-      if (blk + j < nblk) step(blk + j, set[j]);
+    for (int j = 0; j < NS; ++j) set[j].fetch(imgs + (size_t)min(j, nblk - 1) * LY::wBytes, ws, lane);
   }
+  int blk = 0;
+  for (; blk + NS <= nblk; blk += NS) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) step(blk + j, set[j], true);
+  }
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (blk + j < nblk) step(blk + j, set[j], false);
   if (a.state_out) B::store_state(a.state_out, bh, ws, St);
   if (a.mean_out) {
     const f32x4 tot = sum_cols(m_part);
