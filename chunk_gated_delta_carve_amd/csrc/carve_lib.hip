@@ -28,6 +28,8 @@ int check_config(const carve_config* c) {
   // offsets are computed in 64-bit, grids in 32-bit (the state pass launches
   // 8 (B H / 8 rounded up) (d_v / 16) single-wave workgroups)
   if ((int64_t)c->B * c->H > 0x7fffffffLL / 8 - 8) return CARVE_EUNSUPPORTED;
+  // (batch, head, block) items of the chunk-parallel kernels are counted in int
+  if ((int64_t)c->B * c->H * ((c->T + 63) / 64) > 0x7fffffffLL) return CARVE_EUNSUPPORTED;
   // per-lane output offsets inside 16 token rows are 32-bit
   if ((int64_t)16 * c->H * c->dv * elem_bytes(c->dtype) > 0x7fffffffLL) return CARVE_EUNSUPPORTED;
   return CARVE_OK;

@@ -83,8 +83,7 @@ struct BlockLayout {
   static constexpr int oZ = oWg + KP * 4;                    // [DK] f32
   static constexpr int oM = oZ + DK * 4;                     // [DV] f32
   static constexpr int oY = oM + DV * 4;                     // [64] f32
-  static constexpr int oOnes = oY + 64 * 4;                  // [DK] f32 all ones
-  static constexpr int oFlag = oOnes + DK * 4;               // int
+  static constexpr int oFlag = oY + 64 * 4;                  // int
   static constexpr int oRB = oFlag + 16;
   static constexpr int oGb = oRB;                            // [NB+1][DK] f32 (log2 units)
   static constexpr int oSeg = oGb + (NB + 1) * DK * 4;       // [NB][DK] f32
@@ -184,7 +183,7 @@ struct Block {
   struct Smem {
     unsigned char* base;
     E *Kx, *Qx, *Ky, *V, *Td, *Wt, *Ut, *Qd, *P, *KdT, *Mt, *Qe;
-    float *A, *Gb, *Seg, *Egl, *EGs, *Wg, *Z, *M, *Y, *Fd, *Ff, *Ones;
+    float *A, *Gb, *Seg, *Egl, *EGs, *Wg, *Z, *M, *Y, *Fd, *Ff;
     int* Flag;
   };
 
@@ -198,7 +197,7 @@ struct Block {
     s.Mt = e(LY::oMt); s.Qe = e(LY::oQe);
     s.A = f(LY::oA); s.Gb = f(LY::oGb); s.Seg = f(LY::oSeg); s.Egl = f(LY::oEgl); s.EGs = f(LY::oEGs);
     s.Wg = f(LY::oWg); s.Z = f(LY::oZ); s.M = f(LY::oM); s.Y = f(LY::oY); s.Fd = f(LY::oFd);
-    s.Ff = f(LY::oFf); s.Ones = f(LY::oOnes);
+    s.Ff = f(LY::oFf);
     s.Flag = reinterpret_cast<int*>(smem + LY::oFlag);
     return s;
   }
@@ -226,125 +225,197 @@ struct Block {
   }
 
   // -------------------------------------------------------------- gate pass
-  // Loads tokens [t0, t0 + nvalid) and builds every decay-scaled operand.
-  // Thread (gd, gs) owns key column gd of 16-row sub-block gs; its Qd values
-  // stay in registers (qd) until the Qx/Ky region is free again. Rows past
-  // nvalid read as zeros (k = q = v = w = g = 0), which leaves the state
-  // untouched. Returns true if a sub-block's decay is too steep for the
-  // factorised diagonal Grams. Ends with a barrier.
-  __device__ static bool gate_pass(const Smem& s, const Rows<E>& src, int t0, int nvalid, E (&qd)[16]) {
+  // Thread roles: wave w covers 16-row sub-block gs = w 64 / DK and key
+  // channels 64 (w mod DK/64) .. +63; lane (qr = l / 16, dq = l % 16) holds
+  // rows r0 .. r0 + 3 (r0 = 16 gs + 4 qr) of channels d0 .. d0 + 3
+  // (d0 = 64 (w mod DK/64) + 4 dq). Each row segment is one 8-byte (bf16)
+  // or 16-byte (fp32) load.
+  struct GateCoord {
+    int gs, r0, d0, qr;
+    __device__ GateCoord() {
+      const int wave = wave_id(), lane = threadIdx.x & 63;
+      gs = wave * 64 / DK;
+      qr = lane >> 4;
+      r0 = 16 * gs + 4 * qr;
+      d0 = (wave % (DK / 64)) * 64 + 4 * (lane & 15);
+    }
+    __device__ bool active() const { return gs < NB; }
+  };
+
+  // Raw token inputs of one block for this thread, straight from global
+  // memory. Loading is split from the gate arithmetic so a kernel can fetch
+  // the next block while it works on the current one. Rows past nvalid are
+  // clamped to the last valid row here and masked in gate_pass.
+  struct Raw {
+    static constexpr int CPR = DV * LY::ES / 16;         // 16-byte chunks per value row
+    static constexpr int NCH = BL * CPR;
+    static constexpr int VPER = (NCH + NT - 1) / NT;
+    e4 q[4], k[4], g[4], bx[4];
+    f32x4 v[VPER];
+    E w;
+    __device__ void load(const Rows<E>& src, int t0, int nvalid) {
+      const GateCoord gc;
+      const int tid = threadIdx.x;
+      if (gc.active()) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const size_t off = src.row(t0 + min(gc.r0 + i, nvalid - 1)) * DK + gc.d0;
+          q[i] = *reinterpret_cast<const e4*>(src.Q + off);
+          k[i] = *reinterpret_cast<const e4*>(src.K + off);
+          g[i] = *reinterpret_cast<const e4*>(src.G + off);
+          bx[i] = *reinterpret_cast<const e4*>(src.BX + off);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < VPER; ++j) {
+        const int c = tid + j * NT;
+        if (c < NCH) {
+          const int r = c / CPR, cc = c % CPR;
+          v[j] = *reinterpret_cast<const f32x4*>(src.V + src.row(t0 + min(r, nvalid - 1)) * DV + cc * (16 / LY::ES));
+        }
+      }
+      if (tid < BL) w = src.W[src.row(t0 + min(tid, nvalid - 1))];
+    }
+  };
+
+  // Builds every decay-scaled operand of the block from the raw inputs.
+  // G is the inclusive cumulative log-decay (log2 units): within a thread over
+  // its 4 rows, then across the 4 row quarters of the sub-block with lane
+  // shuffles, then across sub-blocks through LDS. Rows past nvalid act as
+  // k = q = v = w = g = 0, which leaves the state untouched. qd (Qd values,
+  // element 4i + j = row r0 + i, channel d0 + j) stays in registers until
+  // the Qx/Ky region is free again. Returns true if a sub-block's decay is too
+  // steep for the factorised diagonal Grams. Ends with a barrier.
+  __device__ static bool gate_pass(const Smem& s, const Raw& raw, int nvalid, E (&qd)[16]) {
+    const GateCoord gc;
     const int tid = threadIdx.x;
-    const int gs = wave_id() * 64 / DK, gd = tid % DK;
+    const int gs = gc.gs, r0 = gc.r0, d0 = gc.d0, qr = gc.qr;
     if (tid == 0) s.Flag[0] = 0;
-    for (int d = tid; d < DK; d += NT) s.Ones[d] = 1.f;
-    float gv[16], kv[16], qv[16], bv[16];
-    if (gs < NB) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = 16 * gs + i;
-        const int rc = min(r, nvalid - 1);           // clamped row: loads stay in bounds
-        const size_t off = src.row(t0 + rc) * DK + gd;
-        const float keep = r < nvalid ? 1.f : 0.f;
-        gv[i] = keep * ldg(src.G, off);
-        kv[i] = keep * ldg(src.K, off);
-        qv[i] = keep * ldg(src.Q, off);
-        bv[i] = ldg(src.BX, off);
+    for (int j = 0; j < Raw::VPER; ++j) {
+      const int c = tid + j * NT;
+      if (c < Raw::NCH) {
+        const int r = c / Raw::CPR, cc = c % Raw::CPR;
+        *reinterpret_cast<f32x4*>(s.V + r * LV + cc * (16 / LY::ES)) = r < nvalid ? raw.v[j] : zero4();
       }
     }
-    // values: 16-byte row chunks into the padded V tile
-    {
-      constexpr int CPR = DV * LY::ES / 16;          // chunks per row
-      constexpr int NCH = BL * CPR;
-      constexpr int PER = (NCH + NT - 1) / NT;
-      f32x4 vc[PER];
+    if (tid < BL) s.Wg[tid] = tid < nvalid ? to_f32(raw.w) : 0.f;
+    float pre[4][4];                                 // [row i][channel j]
+    f32x4 excl = zero4();
+    if (gc.active()) {
+      f32x4 run = zero4();
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int c = tid + j * NT;
-        if (c < NCH) {
-          const int r = c / CPR, cc = c % CPR;
-          const int rc = min(r, nvalid - 1);
-          vc[j] = *reinterpret_cast<const f32x4*>(src.V + src.row(t0 + rc) * DV + cc * (16 / LY::ES));
-          if (r >= nvalid) vc[j] = zero4();
+      for (int i = 0; i < 4; ++i) {
+        const float keep = r0 + i < nvalid ? 1.f : 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          run[j] += keep * to_f32(raw.g[i][j]) * kLog2e;
+          pre[i][j] = run[j];
         }
       }
+      // prefix over the row quarters: lanes dq, dq + 16, dq + 32, dq + 48
+      f32x4 incl = run;
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int c = tid + j * NT;
-        if (c < NCH) {
-          const int r = c / CPR, cc = c % CPR;
-          *reinterpret_cast<f32x4*>(s.V + r * LV + cc * (16 / LY::ES)) = vc[j];
-        }
+      for (int j = 0; j < 4; ++j) {
+        float y = __shfl_up(incl[j], 16);
+        if (qr >= 1) incl[j] += y;
+        y = __shfl_up(incl[j], 32);
+        if (qr >= 2) incl[j] += y;
+        y = __shfl_up(incl[j], 16);
+        excl[j] = qr >= 1 ? y : 0.f;
       }
-    }
-    for (int r = tid; r < BL; r += NT) {
-      const int rc = min(r, nvalid - 1);
-      const float ww = ldg(src.W, src.row(t0 + rc));
-      s.Wg[r] = r < nvalid ? ww : 0.f;
-    }
-    float run = 0.f;
-    if (gs < NB) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        run += gv[i] * kLog2e;
-        gv[i] = run;                                 // local inclusive G, log2 units
-      }
-      s.Seg[gs * DK + gd] = run;
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pre[i][j] += excl[j];   // G_r - G before the sub-block
+      if (qr == 3)
+        *reinterpret_cast<f32x4*>(s.Seg + gs * DK + d0) = f32x4{pre[3][0], pre[3][1], pre[3][2], pre[3][3]};
     }
     __syncthreads();
-    if (gs < NB) {
-      float base = 0.f, total = 0.f;
+    if (gc.active()) {
+      f32x4 base = zero4(), total = zero4(), seg = zero4();
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const float t = s.Seg[j * DK + gd];
-        if (j < gs) base += t;
+      for (int J = 0; J < NB; ++J) {
+        const f32x4 t = *reinterpret_cast<const f32x4*>(s.Seg + J * DK + d0);
+        if (J < gs) base += t;
+        if (J == gs) seg = t;
         total += t;
       }
-      const float Gs = base;                         // G before this sub-block
-      const float Ge = base + run;                   // G at its last row
-      const float eGs = fast_exp2(Gs);
-      s.Gb[gs * DK + gd] = Gs;
-      s.EGs[gs * DK + gd] = eGs;
-      if (gs == NB - 1) {
-        s.Gb[NB * DK + gd] = total;
-        s.Egl[gd] = fast_exp2(total);
+      const f32x4 Gs = base;                         // G before this sub-block
+      const f32x4 Ge = base + seg;                   // G at its last row
+      f32x4 eGs, eTail;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        eGs[j] = fast_exp2(Gs[j]);
+        eTail[j] = fast_exp2(total[j] - Ge[j]);
       }
-      if (Gs - Ge > kSpanLimit2) atomicOr(s.Flag, 1);
-      // Gram scaling factors of this column: diagonal sub-block gs, and the
-      // pairs (I, gs) with I > gs + 1
-      s.Fd[gs * DK + gd] = fast_exp2(Gs - Ge);
+      if (qr == 0) {
+        // per (sub-block, channel) tables: one lane row per sub-block
+        *reinterpret_cast<f32x4*>(s.Gb + gs * DK + d0) = Gs;
+        *reinterpret_cast<f32x4*>(s.EGs + gs * DK + d0) = eGs;
+        if (gs == NB - 1) {
+          *reinterpret_cast<f32x4*>(s.Gb + NB * DK + d0) = total;
+          f32x4 egl;
 #pragma unroll
-      for (int I = 0; I < NB; ++I) {
-        if (I > gs + 1) {
-          float gsI = 0.f;                           // G before sub-block I
+          for (int j = 0; j < 4; ++j) egl[j] = fast_exp2(total[j]);
+          *reinterpret_cast<f32x4*>(s.Egl + d0) = egl;
+        }
+        bool steep = false;
+        f32x4 fd;
 #pragma unroll
-          for (int j = 0; j < NB; ++j)
-            if (j < I) gsI += s.Seg[j * DK + gd];
-          s.Ff[((I - 2) * (I - 1) / 2 + gs) * DK + gd] = fast_exp2(gsI - Ge);
+        for (int j = 0; j < 4; ++j) {
+          steep |= Gs[j] - Ge[j] > kSpanLimit2;
+          fd[j] = fast_exp2(Gs[j] - Ge[j]);
+        }
+        if (steep) atomicOr(s.Flag, 1);
+        // Gram scaling factors: diagonal sub-block gs, and the pairs (I, gs)
+        // with I > gs + 1
+        *reinterpret_cast<f32x4*>(s.Fd + gs * DK + d0) = fd;
+#pragma unroll
+        for (int I = 0; I < NB; ++I) {
+          if (I > gs + 1) {
+            f32x4 gsI = zero4();                     // G before sub-block I
+#pragma unroll
+            for (int J = 0; J < NB; ++J)
+              if (J < I) gsI += *reinterpret_cast<const f32x4*>(s.Seg + J * DK + d0);
+            f32x4 ff;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ff[j] = fast_exp2(gsI[j] - Ge[j]);
+            *reinterpret_cast<f32x4*>(s.Ff + ((I - 2) * (I - 1) / 2 + gs) * DK + d0) = ff;
+          }
         }
       }
-      const float eTail = fast_exp2(total - Ge);
-      const float z = s.Z[gd];
-      float eprev = 1.f;                             // e^{G_{r-1} - Gs}
-      E kd[16];
+      const f32x4 z = *reinterpret_cast<const f32x4*>(s.Z + d0);
+      float eprev[4];                                // e^{G_{r-1} - Gs}
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = 16 * gs + i;
-        const float Gr = base + gv[i];
-        const float bb = sigmoid_f(bv[i] + z);
-        const float e1 = fast_exp2(Gr - Gs);         // <= 1
-        const float en = fast_exp2(Ge - Gr);         // <= 1
-        s.Kx[r * LD + gd] = from_f32<E>(bb * kv[i] * e1);
-        s.Qx[r * LD + gd] = from_f32<E>(qv[i] * eprev);
-        s.Ky[r * LD + gd] = from_f32<E>(kv[i] * en);
-        qd[i] = from_f32<E>(qv[i] * eprev * eGs);
-        kd[i] = from_f32<E>(kv[i] * en * eTail);
-        eprev = e1;
+      for (int j = 0; j < 4; ++j) eprev[j] = fast_exp2(excl[j]);
+      E kd[4][4];                                    // [channel j][row i]
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        e4 kx, qx, ky;
+        const float keep = r0 + i < nvalid ? 1.f : 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float kvij = keep * to_f32(raw.k[i][j]), qvij = keep * to_f32(raw.q[i][j]);
+          const float bb = sigmoid_f(to_f32(raw.bx[i][j]) + z[j]);
+          const float e1 = fast_exp2(pre[i][j]);                     // e^{G_r - Gs} <= 1
+          const float en = fast_exp2(seg[j] - pre[i][j]);            // e^{Ge - G_r} <= 1
+          kx[j] = from_f32<E>(bb * kvij * e1);
+          qx[j] = from_f32<E>(qvij * eprev[j]);
+          ky[j] = from_f32<E>(kvij * en);
+          qd[4 * i + j] = from_f32<E>(qvij * eprev[j] * eGs[j]);
+          kd[j][i] = from_f32<E>(kvij * en * eTail[j]);
+          eprev[j] = e1;
+        }
+        const int r = r0 + i;
+        *reinterpret_cast<e4*>(s.Kx + r * LD + d0) = kx;
+        *reinterpret_cast<e4*>(s.Qx + r * LD + d0) = qx;
+        *reinterpret_cast<e4*>(s.Ky + r * LD + d0) = ky;
       }
-      // Kdec transposed: this thread's 16 rows are 16 consecutive elements
-      E* kdt = s.KdT + gd * LK + 16 * gs;
+      // Kdec transposed: 4 consecutive rows of each channel
 #pragma unroll
-      for (int c = 0; c < 16 * LY::ES / 16; ++c)
-        *reinterpret_cast<f32x4*>(kdt + c * (16 / LY::ES)) = *reinterpret_cast<const f32x4*>(kd + c * (16 / LY::ES));
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<e4*>(s.KdT + (d0 + j) * LK + r0) = e4{kd[j][0], kd[j][1], kd[j][2], kd[j][3]};
     }
     __syncthreads();
     return s.Flag[0] != 0;
@@ -368,10 +439,6 @@ struct Block {
       const int I = tile / NB, J = tile % NB;
       if (J > I) continue;                           // above the diagonal: zero
       const bool diag = (I == J), far = (J < I - 1);
-      // left factor e^{Gs_I - Ge_J} for far pairs, right factor e^{Gs_J - Ge_J}
-      // on the diagonal; other tiles multiply by ones (no branches)
-      const float* fl = far ? s.Ff + ((I - 2) * (I - 1) / 2 + J) * DK : s.Ones;
-      const float* fr = diag ? s.Fd + J * DK : s.Ones;
       Frag ka[DK / KS], qa[DK / KS], kb[DK / KS];
 #pragma unroll
       for (int p = 0; p < DK / KS; ++p) {
@@ -379,14 +446,26 @@ struct Block {
         qa[p] = MM::ld_nat(s.Qx, LD, 16 * I + cc, p * KS);
         kb[p] = MM::ld_nat(s.Ky, LD, 16 * J + cc, p * KS);
       }
+      // far pairs: left operands times e^{Gs_I - Ge_J}; diagonal tiles: right
+      // operand times e^{Gs_J - Ge_J}; adjacent pairs need no factor. The tile
+      // kind is the same for the whole wave, so these are scalar branches.
+      if (far) {
+        const float* fl = s.Ff + ((I - 2) * (I - 1) / 2 + J) * DK;
+#pragma unroll
+        for (int p = 0; p < DK / KS; ++p) {
+          ka[p] = FragScale<E>::apply(ka[p], fl, p * KS);
+          qa[p] = FragScale<E>::apply(qa[p], fl, p * KS);
+        }
+      } else if (diag) {
+        const float* fr = s.Fd + J * DK;
+#pragma unroll
+        for (int p = 0; p < DK / KS; ++p) kb[p] = FragScale<E>::apply(kb[p], fr, p * KS);
+      }
       f32x4 acP = zero4();
 #pragma unroll
       for (int p = 0; p < DK / KS; ++p) {
-        const Frag a = FragScale<E>::apply(ka[p], fl, p * KS);
-        const Frag aq = FragScale<E>::apply(qa[p], fl, p * KS);
-        const Frag b = FragScale<E>::apply(kb[p], fr, p * KS);
-        accA[k] = MM::mma(a, b, accA[k]);
-        acP = MM::mma(aq, b, acP);
+        accA[k] = MM::mma(ka[p], kb[p], accA[k]);
+        acP = MM::mma(qa[p], kb[p], acP);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -560,10 +639,11 @@ struct Block {
     __syncthreads();                                 // Kx, A, V, Td fully read
     // Qd and P into the Qx/Ky/A region
     {
-      const int gs = wave * 64 / DK, gd = tid % DK;
-      if (gs < NB)
+      const GateCoord gc;
+      if (gc.active())
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s.Qd[(16 * gs + i) * LD + gd] = qd[i];
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<e4*>(s.Qd + (gc.r0 + i) * LD + gc.d0) = e4{qd[4 * i], qd[4 * i + 1], qd[4 * i + 2], qd[4 * i + 3]};
 #pragma unroll
       for (int k = 0; k < TPW; ++k) {
         const int tile = wave + k * NW;

@@ -73,12 +73,22 @@ carve_chunk_serial_kernel(FwdArgs a) {
   using Unit = typename B::Unit;
   const Unit* mtu = sink.Mt;
   const Unit* qeu = sink.Qe;
+  // With d_k = 64 the raw inputs of block blk + 1 are fetched while block blk
+  // is processed; wider heads have no registers to spare for that.
+  constexpr bool kPrefetch = DK == 64;
+  typename B::Raw raw;
+  if (kPrefetch && nblk > 0) raw.load(src, 0, min(BL, T));
   for (int blk = 0; blk < nblk; ++blk) {
     const int t0 = blk * BL;
     const int nvalid = min(BL, T - t0);
     E qd[16];
     f32x4 Pt[B::TPW];
-    const bool fallback = B::gate_pass(s, src, t0, nvalid, qd);
+    if (!kPrefetch) raw.load(src, t0, nvalid);
+    const bool fallback = B::gate_pass(s, raw, nvalid, qd);
+    if (kPrefetch) {
+      const int nb = min(blk + 1, nblk - 1);         // unconditional: keeps the load waits simple
+      raw.load(src, nb * BL, min(BL, T - nb * BL));
+    }
     B::grams(s, src, t0, nvalid, fallback, Pt);
     B::inverse_diag(s);
     B::solve(s, qd, Pt);
@@ -107,7 +117,7 @@ carve_chunk_serial_kernel(FwdArgs a) {
     for (int e = tid; e < DV; e += NT) a.mean_out[(size_t)bh * DV + e] = s.M[e];
 }
 
-// One workgroup per (block, batch, head): everything that does not depend on
+// One workgroup per (batch, head, block): everything that does not depend on
 // the state. Writes the block's state-pass operand image to the workspace.
 template <typename E, int DK, int DV, int BL>
 __global__ void __launch_bounds__((BlockLayout<E, DK, DV, BL>::NT))
@@ -121,24 +131,25 @@ carve_intra_kernel(FwdArgs a) {
 
   const int nblk = (a.T + BL - 1) / BL;
   const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk;
-  Rows<E> src{static_cast<const E*>(a.q), static_cast<const E*>(a.k), static_cast<const E*>(a.v),
-              static_cast<const E*>(a.g), static_cast<const E*>(a.bx), static_cast<const E*>(a.w),
-              a.T, a.H, bh / a.H, bh % a.H};
+  const Rows<E> src{static_cast<const E*>(a.q), static_cast<const E*>(a.k), static_cast<const E*>(a.v),
+                    static_cast<const E*>(a.g), static_cast<const E*>(a.bx), static_cast<const E*>(a.w),
+                    a.T, a.H, bh / a.H, bh % a.H};
   const int t0 = blk * BL;
   const int nvalid = min(BL, a.T - t0);
-  unsigned char* img = static_cast<unsigned char*>(a.ws) + ((size_t)bh * nblk + blk) * LY::wBytes;
-  const Sink<E> sink = B::image_sink(img);
+  unsigned char* img = static_cast<unsigned char*>(a.ws) + (size_t)blockIdx.x * LY::wBytes;
 
+  typename B::Raw raw;
+  raw.load(src, t0, nvalid);
   for (int d = threadIdx.x; d < DK; d += NT) s.Z[d] = 0.f;   // no content projection
   __syncthreads();
   E qd[16];
   f32x4 Pt[B::TPW];
-  const bool fallback = B::gate_pass(s, src, t0, nvalid, qd);
+  const bool fallback = B::gate_pass(s, raw, nvalid, qd);
   B::grams(s, src, t0, nvalid, fallback, Pt);
   B::inverse_diag(s);
   B::solve(s, qd, Pt);
   f32x4 CtR[DK / 16], OltR[LY::NB];
-  B::affine(s, sink, CtR, OltR);
+  B::affine(s, B::image_sink(img), CtR, OltR);
   B::put_frags(img, CtR, OltR);
 }
 
