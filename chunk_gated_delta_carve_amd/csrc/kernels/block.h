@@ -178,7 +178,23 @@ struct Block {
   static constexpr int NW = LY::NW, NT = LY::NT, NB = LY::NB, KP = LY::KP, KS = MM::KS;
   static constexpr int TD = LY::TD, NU = LY::NU, SPU = MM::SPU, UT = MM::UT;
   static constexpr int LD = LY::LD, LK = LY::LK, LV = LY::LV, LA = LY::LA, LTD = LY::LTD;
-  static constexpr int TPW = (NB * NB + NW - 1) / NW;      // Gram tiles per wave
+  // Lower-triangular 16x16 tiles (I, J), J <= I, of the Grams, dealt to the
+  // waves in the order: diagonal tiles, adjacent pairs (I = J + 1), then the
+  // far pairs by growing distance. Tile t goes to wave t mod NW as its
+  // (t / NW)-th tile; the kinds are spread evenly that way.
+  static constexpr int NTILE = NB * (NB + 1) / 2;
+  static constexpr int TPW = (NTILE + NW - 1) / NW;        // Gram tiles per wave
+  __device__ __forceinline__ static bool gram_tile(int wave, int k, int& I, int& J) {
+    int t = wave + k * NW;
+    if (t >= NTILE) return false;
+    if (t < NB) { I = J = t; return true; }
+    t -= NB;
+    for (int dist = 1; dist < NB; ++dist) {
+      if (t < NB - dist) { J = t; I = t + dist; return true; }
+      t -= NB - dist;
+    }
+    return false;
+  }
 
   struct Smem {
     unsigned char* base;
@@ -434,10 +450,8 @@ struct Block {
     for (int k = 0; k < TPW; ++k) {
       accA[k] = zero4();
       Pt[k] = zero4();
-      const int tile = wave + k * NW;
-      if (tile >= NB * NB) continue;
-      const int I = tile / NB, J = tile % NB;
-      if (J > I) continue;                           // above the diagonal: zero
+      int I, J;
+      if (!gram_tile(wave, k, I, J)) continue;
       const bool diag = (I == J), far = (J < I - 1);
       Frag ka[DK / KS], qa[DK / KS], kb[DK / KS];
 #pragma unroll
@@ -446,18 +460,12 @@ struct Block {
         qa[p] = MM::ld_nat(s.Qx, LD, 16 * I + cc, p * KS);
         kb[p] = MM::ld_nat(s.Ky, LD, 16 * J + cc, p * KS);
       }
-      // far pairs: left operands times e^{Gs_I - Ge_J}; diagonal tiles: right
-      // operand times e^{Gs_J - Ge_J}; adjacent pairs need no factor. The tile
-      // kind is the same for the whole wave, so these are scalar branches.
-      if (far) {
-        const float* fl = s.Ff + ((I - 2) * (I - 1) / 2 + J) * DK;
-#pragma unroll
-        for (int p = 0; p < DK / KS; ++p) {
-          ka[p] = FragScale<E>::apply(ka[p], fl, p * KS);
-          qa[p] = FragScale<E>::apply(qa[p], fl, p * KS);
-        }
-      } else if (diag) {
-        const float* fr = s.Fd + J * DK;
+      // The per-channel factor of a tile multiplies the shared right operand:
+      // e^{Gs_I - Ge_J} for far pairs, e^{Gs_J - Ge_J} on the diagonal;
+      // adjacent pairs need none. The tile kind is the same for the whole
+      // wave, so these are scalar branches.
+      if (far || diag) {
+        const float* fr = far ? s.Ff + ((I - 2) * (I - 1) / 2 + J) * DK : s.Fd + J * DK;
 #pragma unroll
         for (int p = 0; p < DK / KS; ++p) kb[p] = FragScale<E>::apply(kb[p], fr, p * KS);
       }
@@ -478,12 +486,16 @@ struct Block {
     __syncthreads();                                 // Qx/Ky are free now
 #pragma unroll
     for (int k = 0; k < TPW; ++k) {
-      const int tile = wave + k * NW;
-      if (tile >= NB * NB) continue;
-      const int I = tile / NB, J = tile % NB;
-      if (J > I) continue;
+      int I, J;
+      if (!gram_tile(wave, k, I, J)) continue;
+      if (I == J) {
+        // diagonal tiles are stored transposed (column c of the block is row
+        // c in memory), as the inverse walks them by column
+        *reinterpret_cast<f32x4*>(s.A + (16 * I + cc) * LA + 16 * J + 4 * gq) = accA[k];
+      } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s.A[(16 * I + 4 * gq + i) * LA + 16 * J + cc] = accA[k][i];
+        for (int i = 0; i < 4; ++i) s.A[(16 * I + 4 * gq + i) * LA + 16 * J + cc] = accA[k][i];
+      }
     }
     __syncthreads();
     if (fallback) {
@@ -528,7 +540,7 @@ struct Block {
           sp += ldg(src.Q, rowr + d) * kj * fast_exp2(dg);
         }
       }
-      s.A[r * LA + j] = sa;
+      s.A[(16 * I + ji) * LA + 16 * I + ri] = sa;   // diagonal blocks are stored transposed
       pdiag[I * 256 + ri * 16 + ji] = to_f32(from_f32<E>(sp));
     }
     __syncthreads();
@@ -536,10 +548,8 @@ struct Block {
     const int gq = lane >> 4, cc = lane & 15;
 #pragma unroll
     for (int k = 0; k < TPW; ++k) {
-      const int tile = wave + k * NW;
-      if (tile >= NB * NB) continue;
-      const int I = tile / NB, J = tile % NB;
-      if (I != J) continue;
+      int I, J;
+      if (!gram_tile(wave, k, I, J) || I != J) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int ri = 4 * gq + i;
@@ -556,31 +566,38 @@ struct Block {
 
   // -------------------------------------------------------------- (I + A_II)^{-1}
   // Diagonal 16x16 blocks by forward substitution in fp32, stored as E.
-  // Wave 0, lane (block ib = gq, column c = cc) keeps its column in registers.
-  // Ends with a barrier.
+  // Wave 0, lane (block ib = gq, column c = cc) computes column c of the
+  // inverse, walking the block column by column: once entry r is final, it
+  // is pushed into the running sums of every later row, so the dependent
+  // chain per step is one multiply-add. The diagonal blocks of A are stored
+  // transposed, so column r of a block is one contiguous row read by all 16
+  // lanes of the group. Ends with a barrier.
   __device__ static void inverse_diag(const Smem& s) {
     const int lane = threadIdx.x & 63;
     const int ib = lane >> 4, c = lane & 15;
     if (wave_id() == 0 && ib < NB) {
-      const float* Ablk = s.A + (16 * ib) * LA + 16 * ib;
-      float t[16];
-      float cur[16], nxt[16];
+      const float* At = s.A + (16 * ib) * LA + 16 * ib;   // At[r * LA + i] = A_II[i][r]
+      float acc[16], t[16];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) *reinterpret_cast<f32x4*>(cur + 4 * q4) = *reinterpret_cast<const f32x4*>(Ablk + LA + 4 * q4);
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+      f32x4 col[4];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) col[q4] = *reinterpret_cast<const f32x4*>(At + 4 * q4);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        if (r >= 1 && r + 1 < 16) {                    // fetch row r+1 while row r is reduced
+        f32x4 nxt[4];
+        if (r + 1 < 16) {                              // column r + 1 while column r is applied
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4)
-            if (4 * q4 < r + 1) *reinterpret_cast<f32x4*>(nxt + 4 * q4) = *reinterpret_cast<const f32x4*>(Ablk + (r + 1) * LA + 4 * q4);
+            if (4 * q4 + 3 > r + 1) nxt[q4] = *reinterpret_cast<const f32x4*>(At + (r + 1) * LA + 4 * q4);
         }
-        float acc = 0.f;
+        t[r] = (r == c) ? 1.f : ((r > c) ? -acc[r] : 0.f);
 #pragma unroll
-        for (int j = 0; j < r; ++j) acc += cur[j] * t[j];
-        t[r] = (r == c) ? 1.f : ((r > c) ? -acc : 0.f);
-        if (r >= 1 && r + 1 < 16) {
+        for (int i = r + 1; i < 16; ++i) acc[i] += col[i / 4][i % 4] * t[r];
+        if (r + 1 < 16) {
 #pragma unroll
-          for (int j = 0; j < 16; ++j) cur[j] = nxt[j];
+          for (int q4 = 0; q4 < 4; ++q4)
+            if (4 * q4 + 3 > r + 1) col[q4] = nxt[q4];
         }
       }
       E* Tb = s.Td + ib * 16 * LTD;
@@ -646,11 +663,18 @@ struct Block {
           *reinterpret_cast<e4*>(s.Qd + (gc.r0 + i) * LD + gc.d0) = e4{qd[4 * i], qd[4 * i + 1], qd[4 * i + 2], qd[4 * i + 3]};
 #pragma unroll
       for (int k = 0; k < TPW; ++k) {
-        const int tile = wave + k * NW;
-        if (tile >= NB * NB) continue;
-        const int I = tile / NB, J = tile % NB;
+        int I, J;
+        if (!gram_tile(wave, k, I, J)) continue;
 #pragma unroll
         for (int i = 0; i < 4; ++i) s.P[(16 * I + 4 * gq + i) * LK + 16 * J + cc] = from_f32<E>(Pt[k][i]);
+      }
+      // tiles above the diagonal are read as zeros by the affine products
+      constexpr int CPT = 16 * LY::ES;               // 16-byte chunks per 16x16 tile
+      for (int c = tid; c < NB * (NB - 1) / 2 * CPT; c += NT) {
+        int u = c / CPT, I = 0;
+        while (u >= NB - 1 - I) { u -= NB - 1 - I; ++I; }
+        const int J = I + 1 + u, row = (c % CPT) / LY::ES, part = c % LY::ES;
+        *reinterpret_cast<f32x4*>(s.P + (16 * I + row) * LK + 16 * J + part * (16 / LY::ES)) = zero4();
       }
       if constexpr (BL < KP)                         // padding columns of P
         for (int idx = tid; idx < BL * (KP - BL); idx += NT)
