@@ -82,18 +82,19 @@ template <int D>
 hipError_t launch_parallel(const carve::FwdArgs& a, hipStream_t s) {
   using E = carve::bf16;
   constexpr int BL = kParallelBlock;
-  using LY = carve::BlockLayout<E, D, D, BL>;
+  using LY = carve::BlockLayout<E, D, D, BL>;                        // state pass, images
+  using LI = carve::BlockLayout<E, D, D, BL, carve::kIntraWaves>;    // intra kernel
   const int nblk = (a.T + BL - 1) / BL;
   auto intra = carve::carve_intra_kernel<E, D, D, BL>;
   auto state = carve::carve_state_kernel<E, D, D, BL>;
-  hipError_t e = set_lds(intra, LY::intra_bytes);
+  hipError_t e = set_lds(intra, LI::intra_bytes);
   if (e != hipSuccess) return e;
   if (nblk > 0) {
-    hipLaunchKernelGGL(intra, dim3(a.B * a.H * nblk), dim3(LY::NT), LY::intra_bytes, s, a);
+    hipLaunchKernelGGL(intra, dim3(a.B * a.H * nblk), dim3(LI::NT), LI::intra_bytes, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(state, dim3(carve::state_grid(a.B * a.H, LY::NW)), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(state, dim3(carve::state_grid(a.B * a.H, LY::NW)), dim3(128), 0, s, a);
   return hipGetLastError();
 }
 

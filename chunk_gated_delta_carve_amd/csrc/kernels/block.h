@@ -50,15 +50,30 @@ constexpr float kSpanLimit2 = 96.0f;   // max decay (log2 units) inside a 16-row
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-template <typename E, int DK, int DV, int BL>
+// WV is the number of waves of a workgroup that runs the per-block stages;
+// by default one per 16-channel value slice. With more waves than slices,
+// every stage splits its work further (the chunk-parallel intra kernel does
+// that to shorten the latency of one block).
+template <typename E, int DK, int DV, int BL, int WV = DV / 16>
 struct BlockLayout {
   static_assert(DK % 32 == 0 && DV % 16 == 0 && DK == DV, "head widths");
   static_assert(BL == 16 || BL == 32 || BL == 64, "block length");
-  static constexpr int NW = DV / 16;                 // one wave per 16 value channels
-  static constexpr int NT = NW * 64;
+  static constexpr int NW = DV / 16;                 // 16-channel value slices
+  static constexpr int NWV = WV;                     // waves
+  static constexpr int NT = NWV * 64;
+  static constexpr int PARTS = NWV / NW;             // waves per value slice in the affine stage
+  static_assert(NWV % NW == 0, "whole value slices per wave group");
   static constexpr int NB = BL / 16;
   static constexpr int KP = BL < 32 ? 32 : BL;       // padded token-reduction width
-  static_assert(NT >= DK * NB, "one thread per (key column, sub-block) in the gate pass");
+  // Gate pass: a lane holds RPL consecutive rows of 4 key channels; a wave
+  // covers one segment of SR = 4 RPL rows and 64 channels; a 16-row sub-block
+  // has SPS segments (NSEG in the block).
+  static constexpr int RPL = BL * DK / (4 * NT) < 1 ? 1 : (BL * DK / (4 * NT) > 4 ? 4 : BL * DK / (4 * NT));
+  static constexpr int SR = 4 * RPL;
+  static constexpr int SPS = 16 / SR;
+  static constexpr int NSEG = BL / SR;
+  static_assert(BL * DK == 4 * RPL * NT || NSEG * (DK / 64) <= NWV, "gate pass lanes");
+  static_assert(NSEG * (DK / 64) <= NWV, "one wave per gate segment");
   static constexpr int ES = sizeof(E);
   static constexpr int PE = 16 / ES;                 // 16-byte row padding, in elements
   static constexpr int LD = DK + PE;                 // pitch of [.][DK] tiles
@@ -86,11 +101,11 @@ struct BlockLayout {
   static constexpr int oFlag = oY + 64 * 4;                  // int
   static constexpr int oRB = oFlag + 16;
   static constexpr int oGb = oRB;                            // [NB+1][DK] f32 (log2 units)
-  static constexpr int oSeg = oGb + (NB + 1) * DK * 4;       // [NB][DK] f32
-  static constexpr int oFd = oSeg + NB * DK * 4;             // [NB][DK] f32 e^{Gs_J - Ge_J}
+  static constexpr int oSeg = oGb + (NB + 1) * DK * 4;       // [NSEG][DK] f32
+  static constexpr int oFd = oSeg + NSEG * DK * 4;           // [NB][DK] f32 e^{Gs_J - Ge_J}
   static constexpr int oFf = oFd + NB * DK * 4;              // [NFAR][DK] f32 e^{Gs_I - Ge_J}
   static constexpr int oTd = oRB;                            // [NB][16][LTD] E
-  static constexpr int szRB = cmax((2 * NB + 1) * DK * 4 + NB * DK * 4 + NFAR * DK * 4, NB * 16 * LTD * ES);
+  static constexpr int szRB = cmax((NB + 1 + NSEG + NB + NFAR) * DK * 4, NB * 16 * LTD * ES);
   static constexpr int oR1 = oRB + (szRB + 15) / 16 * 16;
   static constexpr int szR1 = cmax(BL * LD * ES, DK * LK * ES);
   static constexpr int oR2 = oR1 + szR1;
@@ -118,15 +133,17 @@ struct BlockLayout {
   // the order in which a wave holds it, so each lane's share is contiguous:
   //   Mt units [TD][NU][64 lanes][16 B]: A operands of M^T (rows d', k = d)
   //   Qe units [NB][NU][64 lanes][16 B]: B operands of Qe^T (k = d, cols t)
-  //   Ct  [NW][TD][64 lanes][4] E: C tiles of C^T (rows d', cols e), per
-  //       16-channel value slice
-  //   Olt [NW][NB][64 lanes][4] E: C tiles of Ol^T (rows e, cols t), per slice
+  //   Ct  [NW][TD/2][64 lanes][2][4] E: C tiles of C^T (rows d', cols e)
+  //       per 16-channel value slice, two tiles side by side per lane
+  //   Olt [NW][NB/2][64 lanes][2][4] E: C tiles of Ol^T (rows e, cols t),
+  //       per slice, paired the same way
   static constexpr int wMt = 0;
   static constexpr int wQe = wMt + DK * DK * ES;
   static constexpr int wCt = wQe + BL * DK * ES;
   static constexpr int wOl = wCt + NW * TD * 256 * ES;
   static constexpr int wBytes = wOl + NW * NB * 256 * ES;
   static_assert(wBytes % 16 == 0, "16-byte units");
+  static_assert(TD % 2 == 0 && (BL < 32 || NB % 2 == 0), "C tiles pair up");
 };
 
 template <typename E>
@@ -168,24 +185,25 @@ struct Sink {
   typename Mma<E>::unit* Qe;   // [NB][NU][64]
 };
 
-template <typename E, int DK, int DV, int BL>
+template <typename E, int DK, int DV, int BL, int WV = DV / 16>
 struct Block {
-  using LY = BlockLayout<E, DK, DV, BL>;
+  using LY = BlockLayout<E, DK, DV, BL, WV>;
   using MM = Mma<E>;
   using Frag = typename MM::frag;
   using Unit = typename MM::unit;
   typedef E e4 __attribute__((ext_vector_type(4)));
-  static constexpr int NW = LY::NW, NT = LY::NT, NB = LY::NB, KP = LY::KP, KS = MM::KS;
+  static constexpr int NW = LY::NW, NWV = LY::NWV, NT = LY::NT, NB = LY::NB, KP = LY::KP, KS = MM::KS;
+  static constexpr int PARTS = LY::PARTS, CTP = LY::TD / PARTS, OLP = NB / PARTS;   // affine tiles per wave
   static constexpr int TD = LY::TD, NU = LY::NU, SPU = MM::SPU, UT = MM::UT;
   static constexpr int LD = LY::LD, LK = LY::LK, LV = LY::LV, LA = LY::LA, LTD = LY::LTD;
   // Lower-triangular 16x16 tiles (I, J), J <= I, of the Grams, dealt to the
   // waves in the order: diagonal tiles, adjacent pairs (I = J + 1), then the
-  // far pairs by growing distance. Tile t goes to wave t mod NW as its
-  // (t / NW)-th tile; the kinds are spread evenly that way.
+  // far pairs by growing distance. Tile t goes to wave t mod NWV as its
+  // (t / NWV)-th tile; the kinds are spread evenly that way.
   static constexpr int NTILE = NB * (NB + 1) / 2;
-  static constexpr int TPW = (NTILE + NW - 1) / NW;        // Gram tiles per wave
+  static constexpr int TPW = (NTILE + NWV - 1) / NWV;      // Gram tiles per wave
   __device__ __forceinline__ static bool gram_tile(int wave, int k, int& I, int& J) {
-    int t = wave + k * NW;
+    int t = wave + k * NWV;
     if (t >= NTILE) return false;
     if (t < NB) { I = J = t; return true; }
     t -= NB;
@@ -224,16 +242,23 @@ struct Block {
   __device__ static Sink<E> image_sink(unsigned char* img) {
     return Sink<E>{reinterpret_cast<Unit*>(img + LY::wMt), reinterpret_cast<Unit*>(img + LY::wQe)};
   }
-  // this wave's C^T and Ol^T tiles into an image (8 or 16 bytes per lane and tile)
-  __device__ static void put_frags(unsigned char* img, const f32x4 (&CtR)[TD], const f32x4 (&OltR)[NB]) {
+  // this wave's C^T and Ol^T tiles into an image: tiles 2i and 2i + 1 of a
+  // lane side by side (16 bytes per lane for bf16)
+  typedef E e8 __attribute__((ext_vector_type(8)));
+  __device__ static e8 pair(f32x4 x, f32x4 y) {
+    return e8{from_f32<E>(x[0]), from_f32<E>(x[1]), from_f32<E>(x[2]), from_f32<E>(x[3]),
+              from_f32<E>(y[0]), from_f32<E>(y[1]), from_f32<E>(y[2]), from_f32<E>(y[3])};
+  }
+  __device__ static void put_frags(unsigned char* img, const f32x4 (&CtR)[CTP], const f32x4 (&OltR)[OLP]) {
+    static_assert(CTP % 2 == 0 && OLP % 2 == 0, "paired tiles");
     const int wave = wave_id(), lane = threadIdx.x & 63;
-    e4* ct = reinterpret_cast<e4*>(img + LY::wCt) + wave * TD * 64 + lane;
-    e4* ol = reinterpret_cast<e4*>(img + LY::wOl) + wave * NB * 64 + lane;
-    auto cvt = [](f32x4 x) { return e4{from_f32<E>(x[0]), from_f32<E>(x[1]), from_f32<E>(x[2]), from_f32<E>(x[3])}; };
+    const int slice = wave % NW, part = wave / NW;
+    e8* ct = reinterpret_cast<e8*>(img + LY::wCt) + (slice * (TD / 2) + part * (CTP / 2)) * 64 + lane;
+    e8* ol = reinterpret_cast<e8*>(img + LY::wOl) + (slice * (NB / 2) + part * (OLP / 2)) * 64 + lane;
 #pragma unroll
-    for (int a = 0; a < TD; ++a) ct[a * 64] = cvt(CtR[a]);
+    for (int a = 0; a < CTP / 2; ++a) ct[a * 64] = pair(CtR[2 * a], CtR[2 * a + 1]);
 #pragma unroll
-    for (int a = 0; a < NB; ++a) ol[a * 64] = cvt(OltR[a]);
+    for (int a = 0; a < OLP / 2; ++a) ol[a * 64] = pair(OltR[2 * a], OltR[2 * a + 1]);
   }
 
   __device__ static void zero_lds(unsigned char* smem, int bytes) {
@@ -241,21 +266,24 @@ struct Block {
   }
 
   // -------------------------------------------------------------- gate pass
-  // Thread roles: wave w covers 16-row sub-block gs = w 64 / DK and key
-  // channels 64 (w mod DK/64) .. +63; lane (qr = l / 16, dq = l % 16) holds
-  // rows r0 .. r0 + 3 (r0 = 16 gs + 4 qr) of channels d0 .. d0 + 3
-  // (d0 = 64 (w mod DK/64) + 4 dq). Each row segment is one 8-byte (bf16)
-  // or 16-byte (fp32) load.
+  // Thread roles: wave w covers gate segment seg = w / (DK/64) (SR = 4 RPL
+  // consecutive rows; SPS segments per 16-row sub-block) and key channels
+  // 64 (w mod DK/64) .. +63; lane (qr = l / 16, dq = l % 16) holds rows
+  // r0 .. r0 + RPL - 1 (r0 = SR seg + RPL qr) of channels d0 .. d0 + 3
+  // (d0 = 64 (w mod DK/64) + 4 dq). Each row segment of a lane is one 8-byte
+  // (bf16) or 16-byte (fp32) load.
+  static constexpr int RPL = LY::RPL, SR = LY::SR, SPS = LY::SPS, NSEG = LY::NSEG;
   struct GateCoord {
-    int gs, r0, d0, qr;
+    int seg, gs, r0, d0, qr;
     __device__ GateCoord() {
       const int wave = wave_id(), lane = threadIdx.x & 63;
-      gs = wave * 64 / DK;
+      seg = wave / (DK / 64);
+      gs = seg / SPS;
       qr = lane >> 4;
-      r0 = 16 * gs + 4 * qr;
+      r0 = SR * seg + RPL * qr;
       d0 = (wave % (DK / 64)) * 64 + 4 * (lane & 15);
     }
-    __device__ bool active() const { return gs < NB; }
+    __device__ bool active() const { return seg < NSEG; }
   };
 
   // Raw token inputs of one block for this thread, straight from global
@@ -266,7 +294,7 @@ struct Block {
     static constexpr int CPR = DV * LY::ES / 16;         // 16-byte chunks per value row
     static constexpr int NCH = BL * CPR;
     static constexpr int VPER = (NCH + NT - 1) / NT;
-    e4 q[4], k[4], g[4], bx[4];
+    e4 q[RPL], k[RPL], g[RPL], bx[RPL];
     f32x4 v[VPER];
     E w;
     __device__ void load(const Rows<E>& src, int t0, int nvalid) {
@@ -274,7 +302,7 @@ struct Block {
       const int tid = threadIdx.x;
       if (gc.active()) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < RPL; ++i) {
           const size_t off = src.row(t0 + min(gc.r0 + i, nvalid - 1)) * DK + gc.d0;
           q[i] = *reinterpret_cast<const e4*>(src.Q + off);
           k[i] = *reinterpret_cast<const e4*>(src.K + off);
@@ -295,9 +323,9 @@ struct Block {
   };
 
   // Builds every decay-scaled operand of the block from the raw inputs.
-  // G is the inclusive cumulative log-decay (log2 units): within a thread over
-  // its 4 rows, then across the 4 row quarters of the sub-block with lane
-  // shuffles, then across sub-blocks through LDS. Rows past nvalid act as
+  // G is the inclusive cumulative log-decay (log2 units): within a lane over
+  // its RPL rows, then across the 4 row quarters of the segment with lane
+  // shuffles, then across segments through LDS. Rows past nvalid act as
   // k = q = v = w = g = 0, which leaves the state untouched. qd (Qd values,
   // element 4i + j = row r0 + i, channel d0 + j) stays in registers until
   // the Qx/Ky region is free again. Returns true if a sub-block's decay is too
@@ -305,7 +333,7 @@ struct Block {
   __device__ static bool gate_pass(const Smem& s, const Raw& raw, int nvalid, E (&qd)[16]) {
     const GateCoord gc;
     const int tid = threadIdx.x;
-    const int gs = gc.gs, r0 = gc.r0, d0 = gc.d0, qr = gc.qr;
+    const int sg = gc.seg, gs = gc.gs, r0 = gc.r0, d0 = gc.d0, qr = gc.qr;
     if (tid == 0) s.Flag[0] = 0;
 #pragma unroll
     for (int j = 0; j < Raw::VPER; ++j) {
@@ -316,12 +344,12 @@ struct Block {
       }
     }
     if (tid < BL) s.Wg[tid] = tid < nvalid ? to_f32(raw.w) : 0.f;
-    float pre[4][4];                                 // [row i][channel j]
+    float pre[RPL][4];                               // [row i][channel j]
     f32x4 excl = zero4();
     if (gc.active()) {
       f32x4 run = zero4();
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < RPL; ++i) {
         const float keep = r0 + i < nvalid ? 1.f : 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -341,22 +369,31 @@ struct Block {
         excl[j] = qr >= 1 ? y : 0.f;
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < RPL; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pre[i][j] += excl[j];   // G_r - G before the sub-block
+        for (int j = 0; j < 4; ++j) pre[i][j] += excl[j];   // G_r - G before the segment
       if (qr == 3)
-        *reinterpret_cast<f32x4*>(s.Seg + gs * DK + d0) = f32x4{pre[3][0], pre[3][1], pre[3][2], pre[3][3]};
+        *reinterpret_cast<f32x4*>(s.Seg + sg * DK + d0) =
+            f32x4{pre[RPL - 1][0], pre[RPL - 1][1], pre[RPL - 1][2], pre[RPL - 1][3]};
     }
     __syncthreads();
     if (gc.active()) {
-      f32x4 base = zero4(), total = zero4(), seg = zero4();
+      // base: G before the sub-block; offs: the segments of the sub-block
+      // before this one; seg: the whole sub-block (summed in the same order,
+      // so the last row of the sub-block reproduces it exactly)
+      f32x4 base = zero4(), offs = zero4(), seg = zero4(), total = zero4();
 #pragma unroll
-      for (int J = 0; J < NB; ++J) {
-        const f32x4 t = *reinterpret_cast<const f32x4*>(s.Seg + J * DK + d0);
-        if (J < gs) base += t;
-        if (J == gs) seg = t;
+      for (int S = 0; S < NSEG; ++S) {
+        const f32x4 t = *reinterpret_cast<const f32x4*>(s.Seg + S * DK + d0);
+        if (S < gs * SPS) base += t;
+        if (S >= gs * SPS && S < sg) offs += t;
+        if (S >= gs * SPS && S < (gs + 1) * SPS) seg += t;
         total += t;
       }
+#pragma unroll
+      for (int i = 0; i < RPL; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pre[i][j] = offs[j] + pre[i][j];   // G_r - Gs
       const f32x4 Gs = base;                         // G before this sub-block
       const f32x4 Ge = base + seg;                   // G at its last row
       f32x4 eGs, eTail;
@@ -365,8 +402,8 @@ struct Block {
         eGs[j] = fast_exp2(Gs[j]);
         eTail[j] = fast_exp2(total[j] - Ge[j]);
       }
-      if (qr == 0) {
-        // per (sub-block, channel) tables: one lane row per sub-block
+      if (qr == 0 && sg == gs * SPS) {
+        // per (sub-block, channel) tables: the first lane row of the sub-block
         *reinterpret_cast<f32x4*>(s.Gb + gs * DK + d0) = Gs;
         *reinterpret_cast<f32x4*>(s.EGs + gs * DK + d0) = eGs;
         if (gs == NB - 1) {
@@ -392,8 +429,8 @@ struct Block {
           if (I > gs + 1) {
             f32x4 gsI = zero4();                     // G before sub-block I
 #pragma unroll
-            for (int J = 0; J < NB; ++J)
-              if (J < I) gsI += *reinterpret_cast<const f32x4*>(s.Seg + J * DK + d0);
+            for (int S = 0; S < NSEG; ++S)
+              if (S < I * SPS) gsI += *reinterpret_cast<const f32x4*>(s.Seg + S * DK + d0);
             f32x4 ff;
 #pragma unroll
             for (int j = 0; j < 4; ++j) ff[j] = fast_exp2(gsI[j] - Ge[j]);
@@ -404,10 +441,10 @@ struct Block {
       const f32x4 z = *reinterpret_cast<const f32x4*>(s.Z + d0);
       float eprev[4];                                // e^{G_{r-1} - Gs}
 #pragma unroll
-      for (int j = 0; j < 4; ++j) eprev[j] = fast_exp2(excl[j]);
-      E kd[4][4];                                    // [channel j][row i]
+      for (int j = 0; j < 4; ++j) eprev[j] = fast_exp2(offs[j] + excl[j]);
+      E kd[4][RPL];                                  // [channel j][row i]
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < RPL; ++i) {
         e4 kx, qx, ky;
         const float keep = r0 + i < nvalid ? 1.f : 0.f;
 #pragma unroll
@@ -428,10 +465,19 @@ struct Block {
         *reinterpret_cast<e4*>(s.Qx + r * LD + d0) = qx;
         *reinterpret_cast<e4*>(s.Ky + r * LD + d0) = ky;
       }
-      // Kdec transposed: 4 consecutive rows of each channel
+      // Kdec transposed: RPL consecutive rows of each channel
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<e4*>(s.KdT + (d0 + j) * LK + r0) = e4{kd[j][0], kd[j][1], kd[j][2], kd[j][3]};
+      for (int j = 0; j < 4; ++j) {
+        E* dst = s.KdT + (d0 + j) * LK + r0;
+        if constexpr (RPL == 4) {
+          *reinterpret_cast<e4*>(dst) = e4{kd[j][0], kd[j][1], kd[j][2], kd[j][3]};
+        } else if constexpr (RPL == 2) {
+          typedef E e2 __attribute__((ext_vector_type(2)));
+          *reinterpret_cast<e2*>(dst) = e2{kd[j][0], kd[j][1]};
+        } else {
+          dst[0] = kd[j][0];
+        }
+      }
     }
     __syncthreads();
     return s.Flag[0] != 0;
@@ -610,24 +656,26 @@ struct Block {
   // -------------------------------------------------------------- [W | U] = (I + A)^{-1} [Kb | w V]
   // Blocked forward substitution over 16-row sub-blocks:
   //   X_I = T_II (R_I - sum_{J<I} A_IJ X_J),  R = [b k e^{G} | w v],
-  // with T_II the diagonal inverses. Wave w solves the two 16-column tiles
-  // 2w, 2w+1 of [W | U] (DK + DV = 32 NW columns), keeping its X_J tiles in
+  // with T_II the diagonal inverses. Wave w solves the CTW 16-column tiles
+  // CTW w .. CTW w + CTW - 1 of [W | U], keeping its X_J tiles in
   // registers. Once every operand is in registers the Qx/Ky/A region takes
   // Qd (from the gate-pass registers) and P (from the Gram registers); the
   // results go transposed (W^T over Kx, U^T over V) for the affine products.
   // Ends with a barrier.
+  static constexpr int CTW = (DK + DV) / 16 / NWV;         // [W | U] column tiles per wave
+  static_assert(CTW >= 1 && CTW * NWV * 16 == DK + DV && (DK / 16) % CTW == 0, "solve tiles");
   __device__ static void solve(const Smem& s, const E (&qd)[16], const f32x4 (&Pt)[TPW]) {
     const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     const int gq = lane >> 4, cc = lane & 15;
-    // both column tiles of a wave lie on the same side of [W | U]
-    const bool isW = 2 * wave < DK / 16;
-    const int col0 = 32 * wave - (isW ? 0 : DK) + cc;
-    f32x4 R[NB][2];
+    // all column tiles of a wave lie on the same side of [W | U]
+    const bool isW = CTW * wave < DK / 16;
+    const int col0 = 16 * CTW * wave - (isW ? 0 : DK) + cc;
+    f32x4 R[NB][CTW];
     if (isW) {
 #pragma unroll
       for (int I = 0; I < NB; ++I)
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < CTW; ++t)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 16 * I + 4 * gq + i, c = col0 + 16 * t;
@@ -637,7 +685,7 @@ struct Block {
 #pragma unroll
       for (int I = 0; I < NB; ++I)
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < CTW; ++t)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 16 * I + 4 * gq + i, c = col0 + 16 * t;
@@ -659,7 +707,7 @@ struct Block {
       const GateCoord gc;
       if (gc.active())
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < RPL; ++i)
           *reinterpret_cast<e4*>(s.Qd + (gc.r0 + i) * LD + gc.d0) = e4{qd[4 * i], qd[4 * i + 1], qd[4 * i + 2], qd[4 * i + 3]};
 #pragma unroll
       for (int k = 0; k < TPW; ++k) {
@@ -680,16 +728,18 @@ struct Block {
         for (int idx = tid; idx < BL * (KP - BL); idx += NT)
           s.P[(idx / (KP - BL)) * LK + BL + idx % (KP - BL)] = from_f32<E>(0.f);
     }
-    f32x4 X[NB][2];
+    f32x4 X[NB][CTW];
 #pragma unroll
     for (int I = 0; I < NB; ++I) {
-      f32x4 acc[2] = {R[I][0], R[I][1]};
+      f32x4 acc[CTW];
+#pragma unroll
+      for (int t = 0; t < CTW; ++t) acc[t] = R[I][t];
 #pragma unroll
       for (int J = 0; J < I; ++J)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) acc[t] = Mma16<E>::mma_a_cB(Arow[I * (I - 1) / 2 + J], X[J][t], acc[t], -1.f);
+        for (int t = 0; t < CTW; ++t) acc[t] = Mma16<E>::mma_a_cB(Arow[I * (I - 1) / 2 + J], X[J][t], acc[t], -1.f);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < CTW; ++t) {
         f32x4 x = Mma16<E>::mma_a_cB(Trow[I], acc[t], zero4(), 1.f);
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[i] = to_f32(from_f32<E>(x[i]));
@@ -699,12 +749,12 @@ struct Block {
     // transposed stores: lane holds rows 4gq..4gq+3 of column col -> 4 consecutive
     E* dst = isW ? s.Wt : s.Ut;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < CTW; ++t) {
       E* rowp = dst + (col0 + 16 * t) * LK;
 #pragma unroll
       for (int I = 0; I < NB; ++I)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rowp[16 * I + 4 * gq + i] = from_f32<E>(X[I][t][i]);
+        *reinterpret_cast<e4*>(rowp + 16 * I + 4 * gq) =
+            e4{from_f32<E>(X[I][t][0]), from_f32<E>(X[I][t][1]), from_f32<E>(X[I][t][2]), from_f32<E>(X[I][t][3])};
       if constexpr (BL < KP)
         for (int j = BL + 4 * gq; j < KP; j += 16)
 #pragma unroll
@@ -722,10 +772,11 @@ struct Block {
   // map); values are rounded to E. Mt and Qe are computed transposed (C rows
   // over d), so a lane's C values of UT adjacent tiles are exactly one
   // operand unit over d: they go to the sink as 16-byte stores, spread over
-  // the waves. Wave w computes the Ct and Olt tiles of its own value
-  // channels [16w, 16w+16) and keeps them in registers (CtR, OltR).
+  // the waves. Wave w computes the Ct and Olt tiles of value slice
+  // w mod NW, channels [16 slice, 16 slice + 16) (part w / NW of them when
+  // several waves share a slice), and keeps them in registers (CtR, OltR).
   // Ends with a barrier.
-  __device__ static void affine(const Smem& s, const Sink<E>& out, f32x4 (&CtR)[TD], f32x4 (&OltR)[NB]) {
+  __device__ static void affine(const Smem& s, const Sink<E>& out, f32x4 (&CtR)[CTP], f32x4 (&OltR)[OLP]) {
     const int wave = wave_id(), lane = threadIdx.x & 63;
     const int gq = lane >> 4, cc = lane & 15;
     auto product = [&](const E* left, int a, const E* right, int b, int nst) {
@@ -755,22 +806,25 @@ struct Block {
       else out.Qe[x * 64 + lane] = MM::pack(t);
     };
     constexpr int NMJ = TD * NU;
-    for (int x = wave; x < NMJ; x += NW) unit_job(std::true_type{}, x);
-    for (int x = ((wave - NMJ) % NW + NW) % NW; x < NB * NU; x += NW) unit_job(std::false_type{}, x);
-    // Ct and Olt of this wave's value channels
+    for (int x = wave; x < NMJ; x += NWV) unit_job(std::true_type{}, x);
+    for (int x = ((wave - NMJ) % NWV + NWV) % NWV; x < NB * NU; x += NWV) unit_job(std::false_type{}, x);
+    // Ct and Olt of this wave's value channels (part `part` of the tiles of
+    // slice `slice` when several waves share a slice)
+    const int slice = wave % NW, part = wave / NW;
 #pragma unroll
-    for (int a = 0; a < TD; ++a) {
-      f32x4 acc = product(s.KdT, a, s.Ut, wave, MM::steps(KP));
+    for (int j = 0; j < CTP; ++j) {
+      f32x4 acc = product(s.KdT, part * CTP + j, s.Ut, slice, MM::steps(KP));
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = to_f32(from_f32<E>(acc[i]));
-      CtR[a] = acc;
+      CtR[j] = acc;
     }
 #pragma unroll
-    for (int a = 0; a < NB; ++a) {
-      f32x4 acc = product(s.Ut, wave, s.P, a, MM::steps(16 * (a + 1)));
+    for (int j = 0; j < OLP; ++j) {
+      const int a = part * OLP + j;
+      f32x4 acc = product(s.Ut, slice, s.P, a, MM::steps(16 * (a + 1)));
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = to_f32(from_f32<E>(acc[i]));
-      OltR[a] = acc;
+      OltR[j] = acc;
     }
     __syncthreads();
   }
@@ -786,8 +840,18 @@ struct Block {
   __device__ static void state_step(MtF mt, QeF qe, const f32x4 (&Ct)[TD], const f32x4 (&Olt)[NB],
                                     f32x4 (&St)[TD], f32x4 (&Ot)[NB]) {
     Frag sf[DK / KS];
+    state_frags(St, sf);
+    state_out(qe, Olt, sf, Ot);
+    state_chain(mt, Ct, sf, St);
+  }
+  // the S operand fragments (bf16 or fp32) of the current state
+  __device__ static void state_frags(const f32x4 (&St)[TD], Frag (&sf)[DK / KS]) {
 #pragma unroll
     for (int p = 0; p < DK / KS; ++p) sf[p] = MM::from_c(St, p);
+  }
+  // O^T = S Qe^T + Ol^T from the fragments of S at the block start
+  template <typename QeF>
+  __device__ static void state_out(QeF qe, const f32x4 (&Olt)[NB], const Frag (&sf)[DK / KS], f32x4 (&Ot)[NB]) {
 #pragma unroll
     for (int rt = 0; rt < NB; ++rt) {
       f32x4 acc = Olt[rt];
@@ -799,6 +863,10 @@ struct Block {
       }
       Ot[rt] = acc;
     }
+  }
+  // S^T <- Mt S^T + Ct
+  template <typename MtF>
+  __device__ static void state_chain(MtF mt, const f32x4 (&Ct)[TD], const Frag (&sf)[DK / KS], f32x4 (&St)[TD]) {
 #pragma unroll
     for (int dt = 0; dt < TD; ++dt) {
       f32x4 acc = Ct[dt];

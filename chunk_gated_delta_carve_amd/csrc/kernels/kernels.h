@@ -117,12 +117,16 @@ carve_chunk_serial_kernel(FwdArgs a) {
     for (int e = tid; e < DV; e += NT) a.mean_out[(size_t)bh * DV + e] = s.M[e];
 }
 
+// Waves of an intra-kernel workgroup: eight, whatever the head width, so the
+// stages of one block split over more waves and each block finishes sooner.
+constexpr int kIntraWaves = 8;
+
 // One workgroup per (batch, head, block): everything that does not depend on
 // the state. Writes the block's state-pass operand image to the workspace.
 template <typename E, int DK, int DV, int BL>
-__global__ void __launch_bounds__((BlockLayout<E, DK, DV, BL>::NT))
+__global__ void __launch_bounds__((BlockLayout<E, DK, DV, BL, kIntraWaves>::NT))
 carve_intra_kernel(FwdArgs a) {
-  using B = Block<E, DK, DV, BL>;
+  using B = Block<E, DK, DV, BL, kIntraWaves>;
   using LY = typename B::LY;
   constexpr int NT = LY::NT;
   static_assert(BL >= 32, "the image has no padding columns to clear");
@@ -148,12 +152,12 @@ carve_intra_kernel(FwdArgs a) {
   B::grams(s, src, t0, nvalid, fallback, Pt);
   B::inverse_diag(s);
   B::solve(s, qd, Pt);
-  f32x4 CtR[DK / 16], OltR[LY::NB];
+  f32x4 CtR[B::CTP], OltR[B::OLP];
   B::affine(s, B::image_sink(img), CtR, OltR);
   B::put_frags(img, CtR, OltR);
 }
 
-// Placement of the state pass: one single-wave workgroup per (batch, head,
+// Placement of the state pass: one two-wave workgroup per (batch, head,
 // 16-channel value slice). Workgroups are dealt to the XCDs round-robin, so
 // the NW slices of one (batch, head) are given ids that are equal modulo 8:
 // they then share one L2 for the block images they all read and for the
@@ -166,123 +170,191 @@ __device__ inline bool state_place(int id, int BH, int NW, int& bh, int& ws) {
   return bh < BH;
 }
 
-// Register sets that hold one block's image for one wave.
-template <typename E, int DK, int DV, int BL>
-struct ImageRegs {
-  using B = Block<E, DK, DV, BL>;
-  using LY = typename B::LY;
-  using Unit = typename B::Unit;
-  using e4 = typename B::e4;
-  typename B::Unit mt[LY::TD][LY::NU], qe[LY::NB][LY::NU];
-  e4 ct[LY::TD], ol[LY::NB];
-  // img is uniform; every load is (uniform base + 16 lane), so addresses stay
-  // in scalar registers
-  __device__ __forceinline__ void fetch(const unsigned char* img, int ws, int lane) {
-    const uint32_t lo = 16u * lane, lo8 = 8u * lane;
-#pragma unroll
-    for (int t = 0; t < LY::TD; ++t)
-#pragma unroll
-      for (int u = 0; u < LY::NU; ++u)
-        mt[t][u] = *reinterpret_cast<const Unit*>(img + LY::wMt + (t * LY::NU + u) * 1024 + lo);
-#pragma unroll
-    for (int t = 0; t < LY::NB; ++t)
-#pragma unroll
-      for (int u = 0; u < LY::NU; ++u)
-        qe[t][u] = *reinterpret_cast<const Unit*>(img + LY::wQe + (t * LY::NU + u) * 1024 + lo);
-    constexpr int CB = 64 * sizeof(e4);                     // bytes per C-tile record
-#pragma unroll
-    for (int t = 0; t < LY::TD; ++t)
-      ct[t] = *reinterpret_cast<const e4*>(img + LY::wCt + (ws * LY::TD + t) * CB + lo8 * (sizeof(e4) / 8));
-#pragma unroll
-    for (int t = 0; t < LY::NB; ++t)
-      ol[t] = *reinterpret_cast<const e4*>(img + LY::wOl + (ws * LY::NB + t) * CB + lo8 * (sizeof(e4) / 8));
-  }
-};
+// Bounded waits between the two waves of a state-pass workgroup: polls of
+// an LDS counter (each sleeps about 64 cycles), far beyond any real wait.
+constexpr int kRingSpins = 1 << 22;
 
-// The serial state pass and the output: every wave runs its own value slice
-// through all blocks with no LDS and no barriers. A block's image is loaded
-// into registers PD blocks before it is used (PD + 1 register sets, rotated by
-// unrolling the block loop).
+// The serial state pass and the output of one (batch, head, value slice),
+// split over the two waves of a workgroup so that each keeps more blocks in
+// flight from memory:
+//   wave 0 (chain):  S^T <- M^T S^T + C^T through all blocks; before each
+//                    block it publishes the S operand fragments (the state
+//                    at the block start) in an LDS ring;
+//   wave 1 (output): O^T = S Q_eff^T + O_loc^T per block from the ring,
+//                    the output stores and the mean of the last chunk.
+// Each wave loads its part of a block image into registers NS - 1 blocks
+// ahead (NS register sets, rotated by unrolling the block loop); the loads
+// of the last sets are clamped into range so that every set always has one
+// load group in flight and the waits before a block cover only its loads.
 template <typename E, int DK, int DV, int BL>
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(128)
 carve_state_kernel(FwdArgs a) {
   using B = Block<E, DK, DV, BL>;
   using LY = typename B::LY;
-  using R = ImageRegs<E, DK, DV, BL>;
-  constexpr int NB = LY::NB, TD = LY::TD, NW = LY::NW;
-  constexpr int NS = DK == 64 ? 2 : 1;                 // register sets (prefetch depth NS - 1)
-  const int lane = threadIdx.x;
+  using Unit = typename B::Unit;
+  using Frag = typename B::Frag;
+  using e8 = typename B::e8;
+  constexpr int NB = LY::NB, TD = LY::TD, NU = LY::NU, NW = LY::NW, NF = DK / Mma<E>::KS;
+  constexpr int NS = DK == 64 ? 4 : 2;                 // register sets per wave
+  constexpr int R = 8;                                 // ring slots
+  __shared__ Frag ring[R][NF][64];
+  __shared__ int produced, consumed;
+
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int gq = lane >> 4, cc = lane & 15;
   const int T = a.T, H = a.H, L = a.L;
   int bh, ws;
-  if (!state_place(blockIdx.x, a.B * H, NW, bh, ws)) return;
+  if (!state_place(blockIdx.x, a.B * H, NW, bh, ws)) return;   // uniform per workgroup
   const int e0 = 16 * ws;
   const int nblk = (T + BL - 1) / BL;
-  E* __restrict__ O = static_cast<E*>(a.o);
+  if (threadIdx.x == 0) { produced = 0; consumed = 0; }
+  __syncthreads();
   const unsigned char* imgs = static_cast<const unsigned char*>(a.ws) + (size_t)bh * nblk * LY::wBytes;
-  const int bidx = bh / H, h = bh % H;
-  const uint32_t olane = (uint32_t)(((size_t)cc * H * DV + (size_t)h * DV + e0 + 4 * gq) * sizeof(E));
-
-  f32x4 St[TD];
-  B::load_state(a.state_in, bh, ws, St);
-  const int mstart = T > 0 ? ((T - 1) / L) * L : 0;   // first token of the last chunk
-  f32x4 m_part = zero4();
-
-  R set[NS];
-  // The refill of a register set is unconditional (the block index is clamped
-  // into the image), so every set always has exactly one load group in flight
-  // and the waits before a block cover only that block's loads.
-  auto step = [&](int blk, R& r, bool refill) {
-    f32x4 Ct[TD], Olt[NB], Ot[NB];
-#pragma unroll
-    for (int t = 0; t < TD; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Ct[t][i] = to_f32(r.ct[t][i]);
-#pragma unroll
-    for (int t = 0; t < NB; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Olt[t][i] = to_f32(r.ol[t][i]);
-    B::state_step([&](int dt, int u) { return r.mt[dt][u]; }, [&](int rt, int u) { return r.qe[rt][u]; },
-                  Ct, Olt, St, Ot);
-    if (refill) r.fetch(imgs + (size_t)min(blk + NS, nblk - 1) * LY::wBytes, ws, lane);
-    const int t0 = blk * BL;
-    if (t0 + BL > mstart) {                           // the block reaches into the last chunk
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt)
-        if (t0 + 16 * rt + cc >= mstart) m_part += Ot[rt];   // tokens past T are exactly 0
+  auto img = [&](int blk) { return imgs + (size_t)min(blk, nblk - 1) * LY::wBytes; };
+  bool lost = false;                                   // a wait ran out
+  auto wait_for = [&](auto ready) {
+    for (int spin = 0; spin < kRingSpins && !lost; ++spin) {
+      if (ready()) return;
+      __builtin_amdgcn_s_sleep(1);
     }
-    // O^T tile rt: lane (g, c) writes token t0 + 16 rt + c, channels e0 + 4g .. e0 + 4g + 3
-    E* ob = O + ((size_t)bidx * T + t0) * H * DV;     // uniform
-#pragma unroll
-    for (int rt = 0; rt < NB; ++rt) {
-      const typename B::e4 v{from_f32<E>(Ot[rt][0]), from_f32<E>(Ot[rt][1]), from_f32<E>(Ot[rt][2]),
-                             from_f32<E>(Ot[rt][3])};
-      if (t0 + 16 * rt + 16 <= T || t0 + 16 * rt + cc < T)
-        *reinterpret_cast<typename B::e4*>(reinterpret_cast<unsigned char*>(ob + (size_t)16 * rt * H * DV) + olane) = v;
-    }
+    lost = true;
   };
-  if (nblk > 0) {
+  auto load_acq = [](int* p) { return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP); };
+  auto store_rel = [](int* p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP); };
+  auto unpair = [](e8 x, f32x4& lo, f32x4& hi) {
 #pragma unroll
-    for (int j = 0; j < NS; ++j) set[j].fetch(imgs + (size_t)min(j, nblk - 1) * LY::wBytes, ws, lane);
-  }
-  int blk = 0;
-  for (; blk + NS <= nblk; blk += NS) {
+    for (int i = 0; i < 4; ++i) { lo[i] = to_f32(x[i]); hi[i] = to_f32(x[4 + i]); }
+  };
+  const uint32_t lo16 = 16u * lane;
+
+  if (wave == 0) {
+    // ------------------------------------------------------------ chain
+    struct Set { Unit mt[TD][NU]; e8 ct[TD / 2]; };
+    auto fetch = [&](Set& r, int blk) {
+      const unsigned char* p = img(blk);
 #pragma unroll
-    for (int j = 0; j < NS; ++j) step(blk + j, set[j], true);
-  }
+      for (int t = 0; t < TD; ++t)
 #pragma unroll
-  for (int j = 0; j < NS - 1; ++j)
-    if (blk + j < nblk) step(blk + j, set[j], false);
-  if (a.state_out) B::store_state(a.state_out, bh, ws, St);
-  if (a.mean_out) {
-    const f32x4 tot = sum_cols(m_part);
-    float* mo = a.mean_out + (size_t)bh * DV + e0 + 4 * gq;
-    if (cc == 0) {
-      if (T == 0) {
-        *reinterpret_cast<f32x4*>(mo) = a.mean_in ? *reinterpret_cast<const f32x4*>(a.mean_in + (size_t)bh * DV + e0 + 4 * gq)
-                                                  : zero4();
-      } else {
-        *reinterpret_cast<f32x4*>(mo) = tot * (1.0f / (float)(T - mstart));
+        for (int u = 0; u < NU; ++u)
+          r.mt[t][u] = *reinterpret_cast<const Unit*>(p + LY::wMt + (t * NU + u) * 1024 + lo16);
+#pragma unroll
+      for (int t = 0; t < TD / 2; ++t)
+        r.ct[t] = *reinterpret_cast<const e8*>(p + LY::wCt + (ws * (TD / 2) + t) * 1024 + lo16);
+    };
+    f32x4 St[TD];
+    B::load_state(a.state_in, bh, ws, St);
+    // the initial state lands before any image load is issued; otherwise the
+    // waits in the block loop cannot tell its loads from the prefetches
+    __builtin_amdgcn_s_waitcnt(0);
+    Set set[NS];
+    int seen = 0;                                     // last value of `consumed` read
+    auto step = [&](int blk, Set& r, bool refill) {
+      Frag sf[NF];
+      B::state_frags(St, sf);
+      // Publish the previous block (its ring writes finished long ago, so the
+      // release costs nothing), then make sure slot blk % R is free.
+      store_rel(&produced, blk);
+      if (blk - seen >= R) wait_for([&] { seen = load_acq(&consumed); return blk - seen < R; });
+#pragma unroll
+      for (int p = 0; p < NF; ++p) ring[blk % R][p][lane] = sf[p];
+      f32x4 Ct[TD];
+#pragma unroll
+      for (int t = 0; t < TD / 2; ++t) unpair(r.ct[t], Ct[2 * t], Ct[2 * t + 1]);
+      B::state_chain([&](int dt, int u) { return r.mt[dt][u]; }, Ct, sf, St);
+      if (refill) fetch(r, blk + NS);
+    };
+    if (nblk > 0) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) fetch(set[j], j);
+    }
+    int blk = 0;
+    for (; blk + NS <= nblk; blk += NS) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) step(blk + j, set[j], true);
+    }
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j)
+      if (blk + j < nblk) step(blk + j, set[j], false);
+    store_rel(&produced, nblk);
+    if (lost) {
+      const float nan = __builtin_nanf("");
+#pragma unroll
+      for (int t = 0; t < TD; ++t) St[t] = f32x4{nan, nan, nan, nan};
+    }
+    if (a.state_out) B::store_state(a.state_out, bh, ws, St);
+  } else {
+    // ------------------------------------------------------------ output
+    struct Set { Unit qe[NB][NU]; e8 ol[NB / 2]; };
+    auto fetch = [&](Set& r, int blk) {
+      const unsigned char* p = img(blk);
+#pragma unroll
+      for (int t = 0; t < NB; ++t)
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+          r.qe[t][u] = *reinterpret_cast<const Unit*>(p + LY::wQe + (t * NU + u) * 1024 + lo16);
+#pragma unroll
+      for (int t = 0; t < NB / 2; ++t)
+        r.ol[t] = *reinterpret_cast<const e8*>(p + LY::wOl + (ws * (NB / 2) + t) * 1024 + lo16);
+    };
+    E* __restrict__ O = static_cast<E*>(a.o);
+    const int bidx = bh / H, h = bh % H;
+    const uint32_t olane = (uint32_t)(((size_t)cc * H * DV + (size_t)h * DV + e0 + 4 * gq) * sizeof(E));
+    const int mstart = T > 0 ? ((T - 1) / L) * L : 0;   // first token of the last chunk
+    f32x4 m_part = zero4();
+    Set set[NS];
+    int seen = 0;                                     // last value of `produced` read
+    auto step = [&](int blk, Set& r, bool refill) {
+      // release the slots of every earlier block (their ring reads are done),
+      // then wait until this block's fragments are published
+      store_rel(&consumed, blk);
+      if (seen <= blk) wait_for([&] { seen = load_acq(&produced); return seen > blk; });
+      Frag sf[NF];
+#pragma unroll
+      for (int p = 0; p < NF; ++p) sf[p] = ring[blk % R][p][lane];
+      f32x4 Olt[NB], Ot[NB];
+#pragma unroll
+      for (int t = 0; t < NB / 2; ++t) unpair(r.ol[t], Olt[2 * t], Olt[2 * t + 1]);
+      B::state_out([&](int rt, int u) { return r.qe[rt][u]; }, Olt, sf, Ot);
+      if (refill) fetch(r, blk + NS);
+      const int t0 = blk * BL;
+      if (t0 + BL > mstart) {                         // the block reaches into the last chunk
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt)
+          if (t0 + 16 * rt + cc >= mstart) m_part += Ot[rt];   // tokens past T are exactly 0
+      }
+      // O^T tile rt: lane (g, c) writes token t0 + 16 rt + c, channels e0 + 4g .. e0 + 4g + 3
+      E* ob = O + ((size_t)bidx * T + t0) * H * DV;     // uniform
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt) {
+        const typename B::e4 v{from_f32<E>(Ot[rt][0]), from_f32<E>(Ot[rt][1]), from_f32<E>(Ot[rt][2]),
+                               from_f32<E>(Ot[rt][3])};
+        if (t0 + 16 * rt + 16 <= T || t0 + 16 * rt + cc < T)
+          *reinterpret_cast<typename B::e4*>(reinterpret_cast<unsigned char*>(ob + (size_t)16 * rt * H * DV) + olane) = v;
+      }
+    };
+    if (nblk > 0) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) fetch(set[j], j);
+    }
+    int blk = 0;
+    for (; blk + NS <= nblk; blk += NS) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) step(blk + j, set[j], true);
+    }
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j)
+      if (blk + j < nblk) step(blk + j, set[j], false);
+    if (lost) m_part = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+    if (a.mean_out) {
+      const f32x4 tot = sum_cols(m_part);
+      float* mo = a.mean_out + (size_t)bh * DV + e0 + 4 * gq;
+      if (cc == 0) {
+        if (T == 0) {
+          *reinterpret_cast<f32x4*>(mo) = a.mean_in ? *reinterpret_cast<const f32x4*>(a.mean_in + (size_t)bh * DV + e0 + 4 * gq)
+                                                    : zero4();
+        } else {
+          *reinterpret_cast<f32x4*>(mo) = tot * (1.0f / (float)(T - mstart));
+        }
       }
     }
   }
