@@ -26,7 +26,7 @@ int check_config(const carve_config* c) {
   if (!valid_chunk(c->L)) return CARVE_EUNSUPPORTED;
   if (c->rank > 64) return CARVE_EUNSUPPORTED;
   // offsets are computed in 64-bit, grids in 32-bit (the state pass launches
-  // 8 (B H / 8 rounded up) (d_v / 16) single-wave workgroups)
+  // 8 (B H / 8 rounded up) (d_v / 16) workgroups)
   if ((int64_t)c->B * c->H > 0x7fffffffLL / 8 - 8) return CARVE_EUNSUPPORTED;
   // (batch, head, block) items of the chunk-parallel kernels are counted in int
   if ((int64_t)c->B * c->H * ((c->T + 63) / 64) > 0x7fffffffLL) return CARVE_EUNSUPPORTED;
@@ -94,7 +94,7 @@ hipError_t launch_parallel(const carve::FwdArgs& a, hipStream_t s) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(state, dim3(carve::state_grid(a.B * a.H, LY::NW)), dim3(128), 0, s, a);
+  hipLaunchKernelGGL(state, dim3(carve::state_grid(a.B * a.H, LY::NW)), dim3(carve::kStateThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -157,11 +157,15 @@ carve_intra_kernel(FwdArgs a) {
   B::put_frags(img, CtR, OltR);
 }
 
-// Placement of the state pass: one two-wave workgroup per (batch, head,
-// 16-channel value slice). Workgroups are dealt to the XCDs round-robin, so
-// the NW slices of one (batch, head) are given ids that are equal modulo 8:
-// they then share one L2 for the block images they all read and for the
-// output rows they write together.
+// Output waves of a state-pass workgroup, next to its one chain wave.
+constexpr int kOutWaves = 2;
+constexpr int kStateThreads = 64 * (1 + kOutWaves);
+
+// Placement of the state pass: one workgroup per (batch, head, 16-channel
+// value slice). Workgroups are dealt to the XCDs round-robin, so the NW
+// slices of one (batch, head) are given ids that are equal modulo 8: they
+// then share one L2 for the block images they all read and for the output
+// rows they write together.
 __host__ __device__ inline int state_grid(int BH, int NW) { return (BH + 7) / 8 * 8 * NW; }
 __device__ inline bool state_place(int id, int BH, int NW, int& bh, int& ws) {
   const int r = id / 8;
@@ -170,24 +174,26 @@ __device__ inline bool state_place(int id, int BH, int NW, int& bh, int& ws) {
   return bh < BH;
 }
 
-// Bounded waits between the two waves of a state-pass workgroup: polls of
-// an LDS counter (each sleeps about 64 cycles), far beyond any real wait.
+// Bounded waits between the waves of a state-pass workgroup: polls of an
+// LDS counter (each sleeps about 64 cycles), far beyond any real wait.
 constexpr int kRingSpins = 1 << 22;
 
 // The serial state pass and the output of one (batch, head, value slice),
-// split over the two waves of a workgroup so that each keeps more blocks in
-// flight from memory:
-//   wave 0 (chain):  S^T <- M^T S^T + C^T through all blocks; before each
-//                    block it publishes the S operand fragments (the state
-//                    at the block start) in an LDS ring;
-//   wave 1 (output): O^T = S Q_eff^T + O_loc^T per block from the ring,
-//                    the output stores and the mean of the last chunk.
-// Each wave loads its part of a block image into registers NS - 1 blocks
-// ahead (NS register sets, rotated by unrolling the block loop); the loads
-// of the last sets are clamped into range so that every set always has one
-// load group in flight and the waits before a block cover only its loads.
+// split over the waves of a workgroup. Every wave is bound by the latency of
+// its image loads, so the work is spread to keep more blocks in flight:
+//   wave 0 (chain):     S^T <- M^T S^T + C^T through all blocks; before each
+//                       block it publishes the S operand fragments (the
+//                       state at the block start) in an LDS ring;
+//   waves 1..K (output): wave 1 + o takes blocks o, o + K, o + 2K, ...:
+//                       O^T = S Q_eff^T + O_loc^T from the ring, the output
+//                       stores and its share of the last chunk's mean.
+// Each wave loads its part of a block image into registers several of its
+// blocks ahead (register sets rotated by unrolling its block loop); the
+// loads of the last sets are clamped into range so that every set always
+// has one load group in flight and the waits before a block cover only its
+// own loads.
 template <typename E, int DK, int DV, int BL>
-__global__ void __launch_bounds__(128)
+__global__ void __launch_bounds__(kStateThreads)
 carve_state_kernel(FwdArgs a) {
   using B = Block<E, DK, DV, BL>;
   using LY = typename B::LY;
@@ -195,10 +201,13 @@ carve_state_kernel(FwdArgs a) {
   using Frag = typename B::Frag;
   using e8 = typename B::e8;
   constexpr int NB = LY::NB, TD = LY::TD, NU = LY::NU, NW = LY::NW, NF = DK / Mma<E>::KS;
-  constexpr int NS = DK == 64 ? 4 : 2;                 // register sets per wave
+  constexpr int K = kOutWaves;
+  constexpr int NSC = DK == 64 ? 8 : 2;                // register sets of the chain wave
+  constexpr int NSO = DK == 64 ? 4 : 2;                // register sets of an output wave
   constexpr int R = 8;                                 // ring slots
   __shared__ Frag ring[R][NF][64];
-  __shared__ int produced, consumed;
+  __shared__ int produced, consumed[K];
+  __shared__ __align__(16) float mtot[K][16];
 
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int gq = lane >> 4, cc = lane & 15;
@@ -207,7 +216,8 @@ carve_state_kernel(FwdArgs a) {
   if (!state_place(blockIdx.x, a.B * H, NW, bh, ws)) return;   // uniform per workgroup
   const int e0 = 16 * ws;
   const int nblk = (T + BL - 1) / BL;
-  if (threadIdx.x == 0) { produced = 0; consumed = 0; }
+  if (threadIdx.x == 0) produced = 0;
+  if (threadIdx.x < K) consumed[threadIdx.x] = 0;
   __syncthreads();
   const unsigned char* imgs = static_cast<const unsigned char*>(a.ws) + (size_t)bh * nblk * LY::wBytes;
   auto img = [&](int blk) { return imgs + (size_t)min(blk, nblk - 1) * LY::wBytes; };
@@ -226,6 +236,7 @@ carve_state_kernel(FwdArgs a) {
     for (int i = 0; i < 4; ++i) { lo[i] = to_f32(x[i]); hi[i] = to_f32(x[4 + i]); }
   };
   const uint32_t lo16 = 16u * lane;
+  const int mstart = T > 0 ? ((T - 1) / L) * L : 0;   // first token of the last chunk
 
   if (wave == 0) {
     // ------------------------------------------------------------ chain
@@ -246,34 +257,42 @@ carve_state_kernel(FwdArgs a) {
     // the initial state lands before any image load is issued; otherwise the
     // waits in the block loop cannot tell its loads from the prefetches
     __builtin_amdgcn_s_waitcnt(0);
-    Set set[NS];
-    int seen = 0;                                     // last value of `consumed` read
+    Set set[NSC];
+    int done = 0;                                     // every block below it has been read from the ring
     auto step = [&](int blk, Set& r, bool refill) {
       Frag sf[NF];
       B::state_frags(St, sf);
       // Publish the previous block (its ring writes finished long ago, so the
-      // release costs nothing), then make sure slot blk % R is free.
+      // release costs nothing), then make sure slot blk % R is free: block
+      // blk - R must have been read by its output wave.
       store_rel(&produced, blk);
-      if (blk - seen >= R) wait_for([&] { seen = load_acq(&consumed); return blk - seen < R; });
+      if (blk - done >= R)
+        wait_for([&] {
+          int m = load_acq(&consumed[0]);
+#pragma unroll
+          for (int o = 1; o < K; ++o) m = min(m, load_acq(&consumed[o]));
+          done = m;
+          return blk - done < R;
+        });
 #pragma unroll
       for (int p = 0; p < NF; ++p) ring[blk % R][p][lane] = sf[p];
       f32x4 Ct[TD];
 #pragma unroll
       for (int t = 0; t < TD / 2; ++t) unpair(r.ct[t], Ct[2 * t], Ct[2 * t + 1]);
       B::state_chain([&](int dt, int u) { return r.mt[dt][u]; }, Ct, sf, St);
-      if (refill) fetch(r, blk + NS);
+      if (refill) fetch(r, blk + NSC);
     };
     if (nblk > 0) {
 #pragma unroll
-      for (int j = 0; j < NS; ++j) fetch(set[j], j);
+      for (int j = 0; j < NSC; ++j) fetch(set[j], j);
     }
     int blk = 0;
-    for (; blk + NS <= nblk; blk += NS) {
+    for (; blk + NSC <= nblk; blk += NSC) {
 #pragma unroll
-      for (int j = 0; j < NS; ++j) step(blk + j, set[j], true);
+      for (int j = 0; j < NSC; ++j) step(blk + j, set[j], true);
     }
 #pragma unroll
-    for (int j = 0; j < NS - 1; ++j)
+    for (int j = 0; j < NSC - 1; ++j)
       if (blk + j < nblk) step(blk + j, set[j], false);
     store_rel(&produced, nblk);
     if (lost) {
@@ -284,6 +303,7 @@ carve_state_kernel(FwdArgs a) {
     if (a.state_out) B::store_state(a.state_out, bh, ws, St);
   } else {
     // ------------------------------------------------------------ output
+    const int o = wave - 1;
     struct Set { Unit qe[NB][NU]; e8 ol[NB / 2]; };
     auto fetch = [&](Set& r, int blk) {
       const unsigned char* p = img(blk);
@@ -299,14 +319,13 @@ carve_state_kernel(FwdArgs a) {
     E* __restrict__ O = static_cast<E*>(a.o);
     const int bidx = bh / H, h = bh % H;
     const uint32_t olane = (uint32_t)(((size_t)cc * H * DV + (size_t)h * DV + e0 + 4 * gq) * sizeof(E));
-    const int mstart = T > 0 ? ((T - 1) / L) * L : 0;   // first token of the last chunk
     f32x4 m_part = zero4();
-    Set set[NS];
+    Set set[NSO];
     int seen = 0;                                     // last value of `produced` read
     auto step = [&](int blk, Set& r, bool refill) {
-      // release the slots of every earlier block (their ring reads are done),
-      // then wait until this block's fragments are published
-      store_rel(&consumed, blk);
+      // release the slots of this wave's earlier blocks (their ring reads are
+      // done), then wait until this block's fragments are published
+      store_rel(&consumed[o], blk);
       if (seen <= blk) wait_for([&] { seen = load_acq(&produced); return seen > blk; });
       Frag sf[NF];
 #pragma unroll
@@ -315,7 +334,7 @@ carve_state_kernel(FwdArgs a) {
 #pragma unroll
       for (int t = 0; t < NB / 2; ++t) unpair(r.ol[t], Olt[2 * t], Olt[2 * t + 1]);
       B::state_out([&](int rt, int u) { return r.qe[rt][u]; }, Olt, sf, Ot);
-      if (refill) fetch(r, blk + NS);
+      if (refill) fetch(r, blk + NSO * K);
       const int t0 = blk * BL;
       if (t0 + BL > mstart) {                         // the block reaches into the last chunk
 #pragma unroll
@@ -332,30 +351,35 @@ carve_state_kernel(FwdArgs a) {
           *reinterpret_cast<typename B::e4*>(reinterpret_cast<unsigned char*>(ob + (size_t)16 * rt * H * DV) + olane) = v;
       }
     };
-    if (nblk > 0) {
+    // this wave's blocks: o + K i for i < mine
+    const int mine = nblk > o ? (nblk - o + K - 1) / K : 0;
 #pragma unroll
-      for (int j = 0; j < NS; ++j) fetch(set[j], j);
+    for (int j = 0; j < NSO; ++j)
+      if (mine > 0) fetch(set[j], o + K * j);
+    int i = 0;
+    for (; i + NSO <= mine; i += NSO) {
+#pragma unroll
+      for (int j = 0; j < NSO; ++j) step(o + K * (i + j), set[j], true);
     }
-    int blk = 0;
-    for (; blk + NS <= nblk; blk += NS) {
 #pragma unroll
-      for (int j = 0; j < NS; ++j) step(blk + j, set[j], true);
-    }
-#pragma unroll
-    for (int j = 0; j < NS - 1; ++j)
-      if (blk + j < nblk) step(blk + j, set[j], false);
+    for (int j = 0; j < NSO - 1; ++j)
+      if (i + j < mine) step(o + K * (i + j), set[j], false);
+    store_rel(&consumed[o], nblk);
     if (lost) m_part = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-    if (a.mean_out) {
-      const f32x4 tot = sum_cols(m_part);
-      float* mo = a.mean_out + (size_t)bh * DV + e0 + 4 * gq;
-      if (cc == 0) {
-        if (T == 0) {
-          *reinterpret_cast<f32x4*>(mo) = a.mean_in ? *reinterpret_cast<const f32x4*>(a.mean_in + (size_t)bh * DV + e0 + 4 * gq)
-                                                    : zero4();
-        } else {
-          *reinterpret_cast<f32x4*>(mo) = tot * (1.0f / (float)(T - mstart));
-        }
-      }
+    const f32x4 tot = sum_cols(m_part);
+    if (cc == 0) *reinterpret_cast<f32x4*>(&mtot[o][4 * gq]) = tot;
+  }
+  __syncthreads();
+  // the mean of the last chunk's outputs, from the output waves' shares
+  if (a.mean_out && wave == 1 && lane < 16) {
+    float* mo = a.mean_out + (size_t)bh * DV + e0 + lane;
+    if (T == 0) {
+      *mo = a.mean_in ? a.mean_in[(size_t)bh * DV + e0 + lane] : 0.f;
+    } else {
+      float tot = 0.f;
+#pragma unroll
+      for (int o = 0; o < K; ++o) tot += mtot[o][lane];
+      *mo = tot * (1.0f / (float)(T - mstart));
     }
   }
 }
