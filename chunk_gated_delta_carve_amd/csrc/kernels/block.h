@@ -85,7 +85,7 @@ struct BlockLayout {
 
   // ---- LDS. Persistent small arrays, then regions whose contents change
   // once their first occupant is dead:
-  //   RB: Gb, Seg, Fd, Ff (gate pass -> Grams), then Td (inverse -> solve)
+  //   RB: Seg, Fd, Ff (gate pass -> Grams), then Td (inverse -> solve)
   //   R1: Kx (gate -> solve), then Wt = W^T (solve -> affine)
   //   R2: Qx, Ky (gate -> Grams), then A (Grams -> solve), then Qd, P (-> affine)
   //   R3: V (gate -> solve), then Ut = U^T (solve -> affine)
@@ -100,12 +100,11 @@ struct BlockLayout {
   static constexpr int oY = oM + DV * 4;                     // [64] f32
   static constexpr int oFlag = oY + 64 * 4;                  // int
   static constexpr int oRB = oFlag + 16;
-  static constexpr int oGb = oRB;                            // [NB+1][DK] f32 (log2 units)
-  static constexpr int oSeg = oGb + (NB + 1) * DK * 4;       // [NSEG][DK] f32
+  static constexpr int oSeg = oRB;                           // [NSEG][DK] f32
   static constexpr int oFd = oSeg + NSEG * DK * 4;           // [NB][DK] f32 e^{Gs_J - Ge_J}
   static constexpr int oFf = oFd + NB * DK * 4;              // [NFAR][DK] f32 e^{Gs_I - Ge_J}
   static constexpr int oTd = oRB;                            // [NB][16][LTD] E
-  static constexpr int szRB = cmax((NB + 1 + NSEG + NB + NFAR) * DK * 4, NB * 16 * LTD * ES);
+  static constexpr int szRB = cmax((NSEG + NB + NFAR) * DK * 4, NB * 16 * LTD * ES);
   static constexpr int oR1 = oRB + (szRB + 15) / 16 * 16;
   static constexpr int szR1 = cmax(BL * LD * ES, DK * LK * ES);
   static constexpr int oR2 = oR1 + szR1;
@@ -217,7 +216,7 @@ struct Block {
   struct Smem {
     unsigned char* base;
     E *Kx, *Qx, *Ky, *V, *Td, *Wt, *Ut, *Qd, *P, *KdT, *Mt, *Qe;
-    float *A, *Gb, *Seg, *Egl, *EGs, *Wg, *Z, *M, *Y, *Fd, *Ff;
+    float *A, *Seg, *Egl, *EGs, *Wg, *Z, *M, *Y, *Fd, *Ff;
     int* Flag;
   };
 
@@ -229,7 +228,7 @@ struct Block {
     s.Kx = e(LY::oKx); s.Qx = e(LY::oQx); s.Ky = e(LY::oKy); s.V = e(LY::oV); s.Td = e(LY::oTd);
     s.Wt = e(LY::oWt); s.Ut = e(LY::oUt); s.Qd = e(LY::oQd); s.P = e(LY::oP); s.KdT = e(LY::oKdT);
     s.Mt = e(LY::oMt); s.Qe = e(LY::oQe);
-    s.A = f(LY::oA); s.Gb = f(LY::oGb); s.Seg = f(LY::oSeg); s.Egl = f(LY::oEgl); s.EGs = f(LY::oEGs);
+    s.A = f(LY::oA); s.Seg = f(LY::oSeg); s.Egl = f(LY::oEgl); s.EGs = f(LY::oEGs);
     s.Wg = f(LY::oWg); s.Z = f(LY::oZ); s.M = f(LY::oM); s.Y = f(LY::oY); s.Fd = f(LY::oFd);
     s.Ff = f(LY::oFf);
     s.Flag = reinterpret_cast<int*>(smem + LY::oFlag);
@@ -346,14 +345,23 @@ struct Block {
     if (tid < BL) s.Wg[tid] = tid < nvalid ? to_f32(raw.w) : 0.f;
     float pre[RPL][4];                               // [row i][channel j]
     f32x4 excl = zero4();
+    // k, q, g of this lane's rows; in a ragged last block the rows past
+    // nvalid are zeroed here (the block-uniform branch skips this otherwise)
+    e4 rk[RPL], rq[RPL], rg[RPL];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) { rk[i] = raw.k[i]; rq[i] = raw.q[i]; rg[i] = raw.g[i]; }
+    if (nvalid < BL) {
+#pragma unroll
+      for (int i = 0; i < RPL; ++i)
+        if (r0 + i >= nvalid) { rk[i] = e4{}; rq[i] = e4{}; rg[i] = e4{}; }
+    }
     if (gc.active()) {
       f32x4 run = zero4();
 #pragma unroll
       for (int i = 0; i < RPL; ++i) {
-        const float keep = r0 + i < nvalid ? 1.f : 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          run[j] += keep * to_f32(raw.g[i][j]) * kLog2e;
+          run[j] += to_f32(rg[i][j]) * kLog2e;
           pre[i][j] = run[j];
         }
       }
@@ -378,24 +386,41 @@ struct Block {
     }
     __syncthreads();
     if (gc.active()) {
-      // base: G before the sub-block; offs: the segments of the sub-block
-      // before this one; seg: the whole sub-block (summed in the same order,
-      // so the last row of the sub-block reproduces it exactly)
-      f32x4 base = zero4(), offs = zero4(), seg = zero4(), total = zero4();
+      // Segment totals -> sub-block sums sb_I (segments added in order from
+      // zero) -> prefix P_I = sb_0 + ... + sb_{I-1}, the log-decay before
+      // sub-block I. Gs = P_gs, Ge = P_{gs+1} (so Ge of one sub-block is
+      // exactly Gs of the next), total = P_NB. offs: the segments of this
+      // sub-block before this one, added in the same order as sb, so the
+      // last row of the sub-block reproduces sb_gs exactly.
+      f32x4 sb[NB];
 #pragma unroll
-      for (int S = 0; S < NSEG; ++S) {
-        const f32x4 t = *reinterpret_cast<const f32x4*>(s.Seg + S * DK + d0);
-        if (S < gs * SPS) base += t;
-        if (S >= gs * SPS && S < sg) offs += t;
-        if (S >= gs * SPS && S < (gs + 1) * SPS) seg += t;
-        total += t;
+      for (int I = 0; I < NB; ++I) {
+        sb[I] = *reinterpret_cast<const f32x4*>(s.Seg + (I * SPS) * DK + d0);
+#pragma unroll
+        for (int t = 1; t < SPS; ++t) sb[I] += *reinterpret_cast<const f32x4*>(s.Seg + (I * SPS + t) * DK + d0);
       }
+      f32x4 offs = zero4();
+      if constexpr (SPS > 1) {
+        const int first = gs * SPS;                  // wave-uniform
+#pragma unroll
+        for (int t = 0; t < SPS - 1; ++t)
+          if (first + t < sg) offs += *reinterpret_cast<const f32x4*>(s.Seg + (first + t) * DK + d0);
+      }
+      // P_I for I <= NB; Gs/Ge picked by the wave-uniform gs
+      f32x4 P[NB + 1];
+      P[0] = zero4();
+#pragma unroll
+      for (int I = 0; I < NB; ++I) P[I + 1] = P[I] + sb[I];
+      f32x4 Gs = P[0], seg = sb[0];
+#pragma unroll
+      for (int I = 1; I < NB; ++I)
+        if (gs == I) { Gs = P[I]; seg = sb[I]; }
+      const f32x4 Ge = Gs + seg;                     // = P[gs + 1], the same sum
+      const f32x4 total = P[NB];
 #pragma unroll
       for (int i = 0; i < RPL; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) pre[i][j] = offs[j] + pre[i][j];   // G_r - Gs
-      const f32x4 Gs = base;                         // G before this sub-block
-      const f32x4 Ge = base + seg;                   // G at its last row
       f32x4 eGs, eTail;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -404,10 +429,8 @@ struct Block {
       }
       if (qr == 0 && sg == gs * SPS) {
         // per (sub-block, channel) tables: the first lane row of the sub-block
-        *reinterpret_cast<f32x4*>(s.Gb + gs * DK + d0) = Gs;
         *reinterpret_cast<f32x4*>(s.EGs + gs * DK + d0) = eGs;
         if (gs == NB - 1) {
-          *reinterpret_cast<f32x4*>(s.Gb + NB * DK + d0) = total;
           f32x4 egl;
 #pragma unroll
           for (int j = 0; j < 4; ++j) egl[j] = fast_exp2(total[j]);
@@ -425,15 +448,11 @@ struct Block {
         // with I > gs + 1
         *reinterpret_cast<f32x4*>(s.Fd + gs * DK + d0) = fd;
 #pragma unroll
-        for (int I = 0; I < NB; ++I) {
+        for (int I = 2; I < NB; ++I) {
           if (I > gs + 1) {
-            f32x4 gsI = zero4();                     // G before sub-block I
-#pragma unroll
-            for (int S = 0; S < NSEG; ++S)
-              if (S < I * SPS) gsI += *reinterpret_cast<const f32x4*>(s.Seg + S * DK + d0);
             f32x4 ff;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ff[j] = fast_exp2(gsI[j] - Ge[j]);
+            for (int j = 0; j < 4; ++j) ff[j] = fast_exp2(P[I][j] - Ge[j]);
             *reinterpret_cast<f32x4*>(s.Ff + ((I - 2) * (I - 1) / 2 + gs) * DK + d0) = ff;
           }
         }
@@ -446,10 +465,9 @@ struct Block {
 #pragma unroll
       for (int i = 0; i < RPL; ++i) {
         e4 kx, qx, ky;
-        const float keep = r0 + i < nvalid ? 1.f : 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float kvij = keep * to_f32(raw.k[i][j]), qvij = keep * to_f32(raw.q[i][j]);
+          const float kvij = to_f32(rk[i][j]), qvij = to_f32(rq[i][j]);
           const float bb = sigmoid_f(to_f32(raw.bx[i][j]) + z[j]);
           const float e1 = fast_exp2(pre[i][j]);                     // e^{G_r - Gs} <= 1
           const float en = fast_exp2(seg[j] - pre[i][j]);            // e^{Ge - G_r} <= 1
