@@ -80,6 +80,7 @@ struct BlockLayout {
   static constexpr int LK = KP + PE;                 // pitch of [.][KP] tiles
   static constexpr int LV = DV + PE;                 // pitch of [.][DV] tiles
   static constexpr int LA = BL + 4;                  // pitch of A (fp32)
+  static constexpr int LAE = LA * 4 / ES;            // the same rows as E: off-diagonal tiles of -A
   static constexpr int LTD = 16 + PE;                // pitch of the diagonal inverses (E)
   static constexpr int NFAR = NB > 2 ? (NB - 1) * (NB - 2) / 2 : 1;   // sub-block pairs J < I-1
 
@@ -194,7 +195,7 @@ struct Block {
   static constexpr int NW = LY::NW, NWV = LY::NWV, NT = LY::NT, NB = LY::NB, KP = LY::KP, KS = MM::KS;
   static constexpr int PARTS = LY::PARTS, CTP = LY::TD / PARTS, OLP = NB / PARTS;   // affine tiles per wave
   static constexpr int TD = LY::TD, NU = LY::NU, SPU = MM::SPU, UT = MM::UT;
-  static constexpr int LD = LY::LD, LK = LY::LK, LV = LY::LV, LA = LY::LA, LTD = LY::LTD;
+  static constexpr int LD = LY::LD, LK = LY::LK, LV = LY::LV, LA = LY::LA, LAE = LY::LAE, LTD = LY::LTD;
   // Lower-triangular 16x16 tiles (I, J), J <= I, of the Grams, dealt to the
   // waves in the order: diagonal tiles, adjacent pairs (I = J + 1), then the
   // far pairs by growing distance. Tile t goes to wave t mod NWV as its
@@ -215,7 +216,7 @@ struct Block {
 
   struct Smem {
     unsigned char* base;
-    E *Kx, *Qx, *Ky, *V, *Td, *Wt, *Ut, *Qd, *P, *KdT, *Mt, *Qe;
+    E *Kx, *Qx, *Ky, *V, *Td, *Wt, *Ut, *Qd, *P, *KdT, *Mt, *Qe, *An;
     float *A, *Seg, *Egl, *EGs, *Wg, *Z, *M, *Y, *Fd, *Ff;
     int* Flag;
   };
@@ -227,7 +228,7 @@ struct Block {
     auto f = [&](int o) { return reinterpret_cast<float*>(smem + o); };
     s.Kx = e(LY::oKx); s.Qx = e(LY::oQx); s.Ky = e(LY::oKy); s.V = e(LY::oV); s.Td = e(LY::oTd);
     s.Wt = e(LY::oWt); s.Ut = e(LY::oUt); s.Qd = e(LY::oQd); s.P = e(LY::oP); s.KdT = e(LY::oKdT);
-    s.Mt = e(LY::oMt); s.Qe = e(LY::oQe);
+    s.Mt = e(LY::oMt); s.Qe = e(LY::oQe); s.An = e(LY::oA);
     s.A = f(LY::oA); s.Seg = f(LY::oSeg); s.Egl = f(LY::oEgl); s.EGs = f(LY::oEGs);
     s.Wg = f(LY::oWg); s.Z = f(LY::oZ); s.M = f(LY::oM); s.Y = f(LY::oY); s.Fd = f(LY::oFd);
     s.Ff = f(LY::oFf);
@@ -557,8 +558,10 @@ struct Block {
         // c in memory), as the inverse walks them by column
         *reinterpret_cast<f32x4*>(s.A + (16 * I + cc) * LA + 16 * J + 4 * gq) = accA[k];
       } else {
+        // -A_IJ in operand precision, row r at the start of the fp32 row r:
+        // for J < I it ends before the fp32 diagonal tile of the same rows
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s.A[(16 * I + 4 * gq + i) * LA + 16 * J + cc] = accA[k][i];
+        for (int i = 0; i < 4; ++i) s.An[(16 * I + 4 * gq + i) * LAE + 16 * J + cc] = from_f32<E>(-accA[k][i]);
       }
     }
     __syncthreads();
@@ -710,14 +713,14 @@ struct Block {
             R[I][t][i] = s.Wg[r] * to_f32(s.V[r * LV + c]);              // w v
           }
     }
-    f32x4 Arow[NB > 1 ? NB * (NB - 1) / 2 : 1], Trow[NB];
+    using M16 = Mma16<E>;
+    e4 Arow[NB > 1 ? NB * (NB - 1) / 2 : 1], Trow[NB];   // A operands: -A_IJ, T_II
 #pragma unroll
     for (int I = 0; I < NB; ++I) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Trow[I][i] = to_f32(s.Td[I * 16 * LTD + cc * LTD + 4 * gq + i]);
+      Trow[I] = *reinterpret_cast<const e4*>(s.Td + I * 16 * LTD + cc * LTD + 4 * gq);
 #pragma unroll
       for (int J = 0; J < I; ++J)
-        Arow[I * (I - 1) / 2 + J] = *reinterpret_cast<const f32x4*>(s.A + (16 * I + cc) * LA + 16 * J + 4 * gq);
+        Arow[I * (I - 1) / 2 + J] = *reinterpret_cast<const e4*>(s.An + (16 * I + cc) * LAE + 16 * J + 4 * gq);
     }
     __syncthreads();                                 // Kx, A, V, Td fully read
     // Qd and P into the Qx/Ky/A region
@@ -746,7 +749,7 @@ struct Block {
         for (int idx = tid; idx < BL * (KP - BL); idx += NT)
           s.P[(idx / (KP - BL)) * LK + BL + idx % (KP - BL)] = from_f32<E>(0.f);
     }
-    f32x4 X[NB][CTW];
+    e4 X[NB][CTW];                                  // [W | U] tiles, operand precision
 #pragma unroll
     for (int I = 0; I < NB; ++I) {
       f32x4 acc[CTW];
@@ -755,14 +758,9 @@ struct Block {
 #pragma unroll
       for (int J = 0; J < I; ++J)
 #pragma unroll
-        for (int t = 0; t < CTW; ++t) acc[t] = Mma16<E>::mma_a_cB(Arow[I * (I - 1) / 2 + J], X[J][t], acc[t], -1.f);
+        for (int t = 0; t < CTW; ++t) acc[t] = M16::mma(Arow[I * (I - 1) / 2 + J], X[J][t], acc[t]);
 #pragma unroll
-      for (int t = 0; t < CTW; ++t) {
-        f32x4 x = Mma16<E>::mma_a_cB(Trow[I], acc[t], zero4(), 1.f);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = to_f32(from_f32<E>(x[i]));
-        X[I][t] = x;
-      }
+      for (int t = 0; t < CTW; ++t) X[I][t] = M16::round(M16::mma(Trow[I], M16::round(acc[t]), zero4()));
     }
     // transposed stores: lane holds rows 4gq..4gq+3 of column col -> 4 consecutive
     E* dst = isW ? s.Wt : s.Ut;
@@ -771,8 +769,7 @@ struct Block {
       E* rowp = dst + (col0 + 16 * t) * LK;
 #pragma unroll
       for (int I = 0; I < NB; ++I)
-        *reinterpret_cast<e4*>(rowp + 16 * I + 4 * gq) =
-            e4{from_f32<E>(X[I][t][0]), from_f32<E>(X[I][t][1]), from_f32<E>(X[I][t][2]), from_f32<E>(X[I][t][3])};
+        *reinterpret_cast<e4*>(rowp + 16 * I + 4 * gq) = X[I][t];
       if constexpr (BL < KP)
         for (int j = BL + 4 * gq; j < KP; j += 16)
 #pragma unroll

@@ -121,27 +121,44 @@ template <> struct Mma<float> {
 
 // 16x16x16 product whose B operand is one C tile (bf16: one instruction with
 // the natural 4-slot map, which coincides with the C layout; f32: four
-// 16x16x4 instructions). The A operand is a lane's 4 fp32 values of row c,
+// 16x16x4 instructions). The A operand is a lane's 4 values of row c,
 // k = 4g + i.
 template <typename M> struct Mma16;
 template <> struct Mma16<bf16> {
-  // A operand given as 4 fp32 values (row c, k = 4g + i), B from a C tile
-  __device__ __forceinline__ static f32x4 mma_a_cB(f32x4 a, f32x4 b, f32x4 c, float sign) {
+  typedef bf16x4 e4;
+  // operands already in bf16: a = A[c][4g + i], b = B[4g + i][c] (a C tile)
+  __device__ __forceinline__ static f32x4 mma(e4 a, e4 b, f32x4 c) {
     typedef short s4 __attribute__((ext_vector_type(4)));
-    bf16x4 av{(bf16)(sign * a[0]), (bf16)(sign * a[1]), (bf16)(sign * a[2]), (bf16)(sign * a[3])};
-    bf16x4 bv{(bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, av),
-                                                      __builtin_bit_cast(s4, bv), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, a), __builtin_bit_cast(s4, b),
+                                                      c, 0, 0, 0);
+  }
+  // a C tile rounded to operand precision
+  __device__ __forceinline__ static e4 round(f32x4 x) {
+    return e4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
   }
 };
 template <> struct Mma16<float> {
-  __device__ __forceinline__ static f32x4 mma_a_cB(f32x4 a, f32x4 b, f32x4 c, float sign) {
+  typedef f32x4 e4;
+  __device__ __forceinline__ static f32x4 mma(e4 a, e4 b, f32x4 c) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
-      c = __builtin_amdgcn_mfma_f32_16x16x4f32(sign * a[p], b[p], c, 0, 0, 0);
+    for (int p = 0; p < 4; ++p) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[p], b[p], c, 0, 0, 0);
     return c;
   }
+  __device__ __forceinline__ static e4 round(f32x4 x) { return x; }
 };
+
+// DPP lane moves (gfx9 encodings): CTRL 0xB1 = quad_perm [1,0,3,2] (lane
+// xor 1), 0x4E = quad_perm [2,3,0,1] (lane xor 2), 0x114 = row_shr:4 (lane i
+// reads lane i - 4 of its 16-lane row; lanes without a source read 0).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+// sum over the four lanes of a quad, in every lane of it
+__device__ __forceinline__ float quad_sum(float x) {
+  x += dpp_mov<0xB1>(x);
+  return x + dpp_mov<0x4E>(x);
+}
 
 // Sum over the four row groups of a C tile column: lanes c, c+16, c+32, c+48.
 __device__ __forceinline__ float sum_groups(float x) {

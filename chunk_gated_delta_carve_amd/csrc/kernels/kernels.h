@@ -20,6 +20,9 @@
 
 namespace carve {
 
+// Largest rank of the content projection (checked on the host).
+constexpr int kMaxRank = 64;
+
 template <typename E, int DK, int DV, int BL>
 __global__ void __launch_bounds__((BlockLayout<E, DK, DV, BL>::NT))
 carve_chunk_serial_kernel(FwdArgs a) {
@@ -50,20 +53,62 @@ carve_chunk_serial_kernel(FwdArgs a) {
   for (int e = tid; e < DV; e += NT) s.M[e] = a.mean_in ? a.mean_in[(size_t)bh * DV + e] : 0.f;
   __syncthreads();
 
+  // The content projection of this head stays in registers for the whole
+  // sequence (the bias is recomputed at every chunk boundary, on the serial
+  // chain, so it must not wait for memory):
+  //   y_r = sum_e U_down[h][r][e] m[e]: eight lanes per row r (lane group
+  //       gi = lane / 8 of wave w takes r = 8 (w + NWV k) + gi), lane
+  //       c = lane % 8 holds e in [c DV/8, (c + 1) DV/8): ud(k, i);
+  //   z_d = sum_r U_up[h][d][r] y_r: four lanes per key channel (d = tid / 4),
+  //       lane q = tid % 4 holds r = q + 4 i: uu(i).
+  // Values stay in the input type, two per register; the partial sums are
+  // combined with DPP lane moves inside quads and rows.
+  constexpr int NWV = NT / 64, RK = (kMaxRank + 8 * NWV - 1) / (8 * NWV), EPR = DV / 8, RPT = kMaxRank / 4;
+  static_assert(NT == 4 * DK && EPR % 2 == 0 && RPT % 2 == 0, "four threads per key channel");
+  typedef E e2 __attribute__((ext_vector_type(2)));
+  const int zd = tid >> 2, zq = tid & 3, gi = lane >> 3, gc = lane & 7;
+  e2 ud[RK][EPR / 2], uu[RPT / 2];
+#pragma unroll
+  for (int k = 0; k < RK; ++k) {
+    const int r = 8 * (wave + NWV * k) + gi;
+#pragma unroll
+    for (int i = 0; i < EPR; ++i)
+      ud[k][i / 2][i % 2] = r < rank ? Ud[((size_t)h * rank + r) * DV + gc * EPR + i] : from_f32<E>(0.f);
+  }
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r = zq + 4 * i;
+    uu[i / 2][i % 2] = r < rank ? Uu[((size_t)h * DK + zd) * rank + r] : from_f32<E>(0.f);
+  }
   // z = U_up (U_down m) into s.Z (all threads call; ends with a barrier)
   auto content_bias = [&]() {
     if (rank > 0) {
-      for (int r = tid; r < rank; r += NT) {
-        float y = 0.f;
-        for (int e = 0; e < DV; ++e) y += ldg(Ud, ((size_t)h * rank + r) * DV + e) * s.M[e];
-        s.Y[r] = y;
+      float me[EPR];
+#pragma unroll
+      for (int i = 0; i < EPR; i += 4) {
+        const f32x4 m4 = *reinterpret_cast<const f32x4*>(s.M + gc * EPR + i);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) me[i + t] = m4[t];
+      }
+#pragma unroll
+      for (int k = 0; k < RK; ++k) {
+        if (8 * (wave + NWV * k) < rank) {           // wave-uniform
+          float p = 0.f;
+#pragma unroll
+          for (int i = 0; i < EPR; ++i) p += to_f32(ud[k][i / 2][i % 2]) * me[i];
+          p = quad_sum(p);
+          p += dpp_mov<0x114>(p);                    // lanes 4..7 of a group: the group's sum
+          const int r = 8 * (wave + NWV * k) + gi;
+          if (gc == 7 && r < rank) s.Y[r] = p;
+        }
       }
       __syncthreads();
-      for (int d = tid; d < DK; d += NT) {
-        float z = 0.f;
-        for (int r = 0; r < rank; ++r) z += ldg(Uu, ((size_t)h * DK + d) * rank + r) * s.Y[r];
-        s.Z[d] = z;
-      }
+      float z = 0.f;
+#pragma unroll
+      for (int i = 0; i < RPT; ++i)
+        if (zq + 4 * i < rank) z += to_f32(uu[i / 2][i % 2]) * s.Y[zq + 4 * i];
+      z = quad_sum(z);
+      if (zq == 0) s.Z[zd] = z;
     }
     __syncthreads();
   };
