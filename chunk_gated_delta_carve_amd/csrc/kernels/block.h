@@ -330,6 +330,9 @@ struct Block {
   // element 4i + j = row r0 + i, channel d0 + j) stays in registers until
   // the Qx/Ky region is free again. Returns true if a sub-block's decay is too
   // steep for the factorised diagonal Grams. Ends with a barrier.
+  // kContent: the erase logits carry the content bias z from s.Z; without a
+  // content projection z = 0 and s.Z is not read here.
+  template <bool kContent = true>
   __device__ static bool gate_pass(const Smem& s, const Raw& raw, int nvalid, E (&qd)[16]) {
     const GateCoord gc;
     const int tid = threadIdx.x;
@@ -458,7 +461,7 @@ struct Block {
           }
         }
       }
-      const f32x4 z = *reinterpret_cast<const f32x4*>(s.Z + d0);
+      const f32x4 z = kContent ? *reinterpret_cast<const f32x4*>(s.Z + d0) : zero4();
       float eprev[4];                                // e^{G_{r-1} - Gs}
 #pragma unroll
       for (int j = 0; j < 4; ++j) eprev[j] = fast_exp2(offs[j] + excl[j]);
@@ -865,34 +868,33 @@ struct Block {
     for (int p = 0; p < DK / KS; ++p) sf[p] = MM::from_c(St, p);
   }
   // O^T = S Qe^T + Ol^T from the fragments of S at the block start
+  // (reduction steps outermost, so consecutive instructions write different
+  // tiles and never wait for each other's results)
   template <typename QeF>
   __device__ static void state_out(QeF qe, const f32x4 (&Olt)[NB], const Frag (&sf)[DK / KS], f32x4 (&Ot)[NB]) {
 #pragma unroll
-    for (int rt = 0; rt < NB; ++rt) {
-      f32x4 acc = Olt[rt];
+    for (int rt = 0; rt < NB; ++rt) Ot[rt] = Olt[rt];
 #pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        const Unit q = qe(rt, u);
+    for (int u = 0; u < NU; ++u)
 #pragma unroll
-        for (int j = 0; j < SPU; ++j) acc = MM::mma(sf[u * SPU + j], MM::step(q, j), acc);
-      }
-      Ot[rt] = acc;
-    }
+      for (int j = 0; j < SPU; ++j)
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt) Ot[rt] = MM::mma(sf[u * SPU + j], MM::step(qe(rt, u), j), Ot[rt]);
   }
   // S^T <- Mt S^T + Ct
   template <typename MtF>
   __device__ static void state_chain(MtF mt, const f32x4 (&Ct)[TD], const Frag (&sf)[DK / KS], f32x4 (&St)[TD]) {
+    f32x4 acc[TD];
 #pragma unroll
-    for (int dt = 0; dt < TD; ++dt) {
-      f32x4 acc = Ct[dt];
+    for (int dt = 0; dt < TD; ++dt) acc[dt] = Ct[dt];
 #pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        const Unit m = mt(dt, u);
+    for (int u = 0; u < NU; ++u)
 #pragma unroll
-        for (int j = 0; j < SPU; ++j) acc = MM::mma(MM::step(m, j), sf[u * SPU + j], acc);
-      }
-      St[dt] = acc;
-    }
+      for (int j = 0; j < SPU; ++j)
+#pragma unroll
+        for (int dt = 0; dt < TD; ++dt) acc[dt] = MM::mma(MM::step(mt(dt, u), j), sf[u * SPU + j], acc[dt]);
+#pragma unroll
+    for (int dt = 0; dt < TD; ++dt) St[dt] = acc[dt];
   }
 
   // load/store the S^T C tiles of value slice `ws` from/to a [B,H,DV,DK] fp32 tensor

@@ -190,11 +190,12 @@ carve_intra_kernel(FwdArgs a) {
 
   typename B::Raw raw;
   raw.load(src, t0, nvalid);
-  for (int d = threadIdx.x; d < DK; d += NT) s.Z[d] = 0.f;   // no content projection
-  __syncthreads();
+  // no content projection: the gate pass takes z = 0 without reading s.Z; the
+  // zeros here serve only the pairwise fallback, several barriers later
+  for (int d = threadIdx.x; d < DK; d += NT) s.Z[d] = 0.f;
   E qd[16];
   f32x4 Pt[B::TPW];
-  const bool fallback = B::gate_pass(s, raw, nvalid, qd);
+  const bool fallback = B::template gate_pass<false>(s, raw, nvalid, qd);
   B::grams(s, src, t0, nvalid, fallback, Pt);
   B::inverse_diag(s);
   B::solve(s, qd, Pt);
