@@ -30,8 +30,11 @@ int check_config(const carve_config* c) {
   if ((int64_t)c->B * c->H > 0x7fffffffLL / 8 - 8) return CARVE_EUNSUPPORTED;
   // (batch, head, block) items of the chunk-parallel kernels are counted in int
   if ((int64_t)c->B * c->H * ((c->T + 63) / 64) > 0x7fffffffLL) return CARVE_EUNSUPPORTED;
-  // per-lane output offsets inside 16 token rows are 32-bit
+  // per-lane output offsets inside 16 token rows are 32-bit, and so are the
+  // per-lane input offsets inside one block of up to 64 token rows
   if ((int64_t)16 * c->H * c->dv * elem_bytes(c->dtype) > 0x7fffffffLL) return CARVE_EUNSUPPORTED;
+  if ((int64_t)64 * c->H * (c->dk > c->dv ? c->dk : c->dv) * elem_bytes(c->dtype) > 0xffffffffLL)
+    return CARVE_EUNSUPPORTED;
   return CARVE_OK;
 }
 

@@ -297,28 +297,39 @@ struct Block {
     e4 q[RPL], k[RPL], g[RPL], bx[RPL];
     f32x4 v[VPER];
     E w;
+    // Addresses are a block-uniform base per tensor plus a 32-bit per-lane
+    // byte offset (rows of a block lie within 64 H d elements; the host
+    // keeps that below 2^32 bytes), shared by the four [., d_k] tensors.
     __device__ void load(const Rows<E>& src, int t0, int nvalid) {
       const GateCoord gc;
       const int tid = threadIdx.x;
+      const size_t r0 = src.row(t0);                       // uniform
+      const uint32_t hk = (uint32_t)src.H * DK, hv = (uint32_t)src.H * DV;
+      auto at = [](const E* base, uint32_t bytes) {
+        return reinterpret_cast<const unsigned char*>(base) + bytes;
+      };
       if (gc.active()) {
+        const E *Qb = src.Q + r0 * DK, *Kb = src.K + r0 * DK, *Gb = src.G + r0 * DK, *Bb = src.BX + r0 * DK;
 #pragma unroll
         for (int i = 0; i < RPL; ++i) {
-          const size_t off = src.row(t0 + min(gc.r0 + i, nvalid - 1)) * DK + gc.d0;
-          q[i] = *reinterpret_cast<const e4*>(src.Q + off);
-          k[i] = *reinterpret_cast<const e4*>(src.K + off);
-          g[i] = *reinterpret_cast<const e4*>(src.G + off);
-          bx[i] = *reinterpret_cast<const e4*>(src.BX + off);
+          const uint32_t off = ((uint32_t)min(gc.r0 + i, nvalid - 1) * hk + gc.d0) * (uint32_t)sizeof(E);
+          q[i] = *reinterpret_cast<const e4*>(at(Qb, off));
+          k[i] = *reinterpret_cast<const e4*>(at(Kb, off));
+          g[i] = *reinterpret_cast<const e4*>(at(Gb, off));
+          bx[i] = *reinterpret_cast<const e4*>(at(Bb, off));
         }
       }
+      const E* Vb = src.V + r0 * DV;
 #pragma unroll
       for (int j = 0; j < VPER; ++j) {
         const int c = tid + j * NT;
         if (c < NCH) {
           const int r = c / CPR, cc = c % CPR;
-          v[j] = *reinterpret_cast<const f32x4*>(src.V + src.row(t0 + min(r, nvalid - 1)) * DV + cc * (16 / LY::ES));
+          const uint32_t off = ((uint32_t)min(r, nvalid - 1) * hv + cc * (16 / LY::ES)) * (uint32_t)sizeof(E);
+          v[j] = *reinterpret_cast<const f32x4*>(at(Vb, off));
         }
       }
-      if (tid < BL) w = src.W[src.row(t0 + min(tid, nvalid - 1))];
+      if (tid < BL) w = src.W[r0 + (size_t)min(tid, nvalid - 1) * src.H];
     }
   };
 
@@ -472,7 +483,7 @@ struct Block {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float kvij = to_f32(rk[i][j]), qvij = to_f32(rq[i][j]);
-          const float bb = sigmoid_f(to_f32(raw.bx[i][j]) + z[j]);
+          const float bb = sigmoid_f(kContent ? to_f32(raw.bx[i][j]) + z[j] : to_f32(raw.bx[i][j]));
           const float e1 = fast_exp2(pre[i][j]);                     // e^{G_r - Gs} <= 1
           const float en = fast_exp2(seg[j] - pre[i][j]);            // e^{Ge - G_r} <= 1
           kx[j] = from_f32<E>(bb * kvij * e1);
@@ -794,6 +805,9 @@ struct Block {
   // w mod NW, channels [16 slice, 16 slice + 16) (part w / NW of them when
   // several waves share a slice), and keeps them in registers (CtR, OltR).
   // Ends with a barrier.
+  // kRound: round CtR and OltR to E here (they seed fp32 accumulators);
+  // callers that only store them as E leave the rounding to that store.
+  template <bool kRound = true>
   __device__ static void affine(const Smem& s, const Sink<E>& out, f32x4 (&CtR)[CTP], f32x4 (&OltR)[OLP]) {
     const int wave = wave_id(), lane = threadIdx.x & 63;
     const int gq = lane >> 4, cc = lane & 15;
@@ -806,7 +820,10 @@ struct Block {
     // units of Mt (rows d' = 16a + c) and then of Qe (rows r = 16a + c), dealt
     // to the waves in turn
     auto unit_job = [&](auto isM, int x) {
-      const int a = x / NU, u = x % NU;
+      const int a = x / NU, u = x % NU, r = 16 * a + cc;
+      // the diagonal of Mt: element (r, d = r) of tile b = a sits in lane
+      // (g, c) with c = 4g + i
+      const float eg = isM ? s.Egl[r] : 0.f;
       f32x4 t[UT];
 #pragma unroll
       for (int j = 0; j < UT; ++j) {
@@ -814,11 +831,10 @@ struct Block {
         // P is lower-triangular: row block a needs j < 16 (a + 1) only
         const f32x4 acc = isM ? product(s.Wt, b, s.KdT, a, MM::steps(KP))
                               : product(s.Wt, b, s.P, a, MM::steps(16 * (a + 1)));
+        const e4 qd4 = isM ? e4{} : *reinterpret_cast<const e4*>(s.Qd + r * LD + 16 * b + 4 * gq);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d = 16 * b + 4 * gq + i, r = 16 * a + cc;
-          t[j][i] = isM ? (d == r ? s.Egl[d] : 0.f) - acc[i] : to_f32(s.Qd[r * LD + d]) - acc[i];
-        }
+        for (int i = 0; i < 4; ++i)
+          t[j][i] = isM ? (b == a && cc == 4 * gq + i ? eg : 0.f) - acc[i] : to_f32(qd4[i]) - acc[i];
       }
       if constexpr (decltype(isM)::value) out.Mt[x * 64 + lane] = MM::pack(t);
       else out.Qe[x * 64 + lane] = MM::pack(t);
@@ -832,16 +848,18 @@ struct Block {
 #pragma unroll
     for (int j = 0; j < CTP; ++j) {
       f32x4 acc = product(s.KdT, part * CTP + j, s.Ut, slice, MM::steps(KP));
+      if constexpr (kRound)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = to_f32(from_f32<E>(acc[i]));
+        for (int i = 0; i < 4; ++i) acc[i] = to_f32(from_f32<E>(acc[i]));
       CtR[j] = acc;
     }
 #pragma unroll
     for (int j = 0; j < OLP; ++j) {
       const int a = part * OLP + j;
       f32x4 acc = product(s.Ut, slice, s.P, a, MM::steps(16 * (a + 1)));
+      if constexpr (kRound)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = to_f32(from_f32<E>(acc[i]));
+        for (int i = 0; i < 4; ++i) acc[i] = to_f32(from_f32<E>(acc[i]));
       OltR[j] = acc;
     }
     __syncthreads();

@@ -200,7 +200,7 @@ carve_intra_kernel(FwdArgs a) {
   B::inverse_diag(s);
   B::solve(s, qd, Pt);
   f32x4 CtR[B::CTP], OltR[B::OLP];
-  B::affine(s, B::image_sink(img), CtR, OltR);
+  B::template affine<false>(s, B::image_sink(img), CtR, OltR);   // put_frags rounds them
   B::put_frags(img, CtR, OltR);
 }
 
