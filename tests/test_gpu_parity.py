@@ -8,7 +8,8 @@ over the full sequence length and those pairs are compared exactly.
 import numpy as np
 import pytest
 
-from chunk_gated_delta_carve_amd.workloads import WORKLOADS, LSWEEP_CHUNKS, make_inputs, to_f64, to_torch
+from chunk_gated_delta_carve_amd.workloads import (WORKLOADS, LSWEEP_CHUNKS, bf16_bits_from_f32, make_inputs, to_f64,
+                                                   to_torch)
 from oracle import carve_forward
 
 pytestmark = pytest.mark.gpu
@@ -189,6 +190,8 @@ EDGE = [
     ("par-ragged-100-L16", "bf16", 1, 3, 100, 64, 16, 0),
     ("par-d128-ragged-200-L128", "bf16", 2, 2, 200, 128, 128, 0),
     ("par-d128-L64", "bf16", 1, 3, 512, 128, 64, 0),
+    # 13 blocks: the state pass's prefetch loops end in partial rounds
+    ("par-nblk13", "bf16", 2, 3, 832, 64, 64, 0),
 ]
 
 
@@ -272,6 +275,32 @@ def test_hard_decay_memoryless_and_finite(torch_cuda):
     got = run_gpu(torch_cuda, inp, wl.dtype, wl.L)
     ref = run_oracle(inp, wl.dtype, wl.L)
     assert_parity(got, ref, TOL["f32"], "hard decay")
+
+
+def test_steep_decay_chunk_parallel(torch_cuda):
+    """bf16 without a projection (the chunk-parallel pair): half the key
+    channels decay by e^-10 per token, so a 16-token sub-block spans far more
+    than the factorised Grams allow and the pairwise rebuild runs; the other
+    half keep a long memory, so the result is far from trivial."""
+    wl = WORKLOADS["init_equiv"].with_(B=1, H=3, T=320, seed=3003)
+    inp = make_inputs(wl)
+    g = np.empty(inp["g"].shape, np.float32)
+    g[..., : wl.dk // 2] = -10.0
+    g[..., wl.dk // 2:] = -0.02
+    inp["g"] = bf16_bits_from_f32(g)
+    say("case steep decay, chunk-parallel", wl)
+    got = run_gpu(torch_cuda, inp, wl.dtype, wl.L)
+    ref = run_oracle(inp, wl.dtype, wl.L)
+    assert_parity(got, ref, TOL["bf16"], "steep decay (parallel)")
+
+
+def test_deterministic_chunk_parallel(torch_cuda):
+    wl = WORKLOADS["init_equiv"].with_(B=2, T=1024)
+    inp = make_inputs(wl)
+    a = run_gpu(torch_cuda, inp, wl.dtype, wl.L)
+    b = run_gpu(torch_cuda, inp, wl.dtype, wl.L)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
 
 
 def test_delta_rule_special_case(torch_cuda):
