@@ -73,7 +73,7 @@ hipError_t set_lds(K kern, int bytes) {
 
 template <typename E, int D, int BL>
 hipError_t launch_serial(const carve::FwdArgs& a, hipStream_t s) {
-  using LY = carve::BlockLayout<E, D, D, BL>;
+  using LY = carve::BlockLayout<E, D, D, BL, carve::serial_waves<D, BL>()>;
   auto kern = carve::carve_chunk_serial_kernel<E, D, D, BL>;
   hipError_t e = set_lds(kern, LY::serial_bytes);
   if (e != hipSuccess) return e;

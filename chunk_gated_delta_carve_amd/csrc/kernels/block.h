@@ -124,7 +124,15 @@ struct BlockLayout {
   static constexpr int NU = DK * ES / 64;                    // units per 16-row tile along d
   static constexpr int oMt = intra_bytes;                    // [TD][NU][64] units
   static constexpr int oQe = oMt + DK * DK * ES;             // [NB][NU][64] units
-  static constexpr int serial_bytes = oQe + BL * DK * ES;
+  // chunk-serial kernel with PARTS > 1 waves per value slice: the S operand
+  // fragments of every slice, double-buffered by block parity, and the
+  // parts' sums for the chunk mean
+  static constexpr int NFR = DK / (ES == 2 ? 32 : 4);         // operand fragments of S along d
+  static constexpr int FRB = ES == 2 ? 16 : 4;                // bytes per lane of one fragment
+  static constexpr int oXc = oQe + BL * DK * ES;             // [2][NW][NFR][64] fragments
+  static constexpr int szXc = PARTS > 1 ? 2 * NW * NFR * 64 * FRB : 0;
+  static constexpr int oMp = oXc + szXc;                     // [PARTS][DV] f32
+  static constexpr int serial_bytes = oMp + (PARTS > 1 ? PARTS * DV * 4 : 0);
   static_assert(serial_bytes <= 160 * 1024, "LDS budget");
   static_assert(oR1 % 16 == 0 && oR2 % 16 == 0 && oR3 % 16 == 0 && oR4 % 16 == 0 && oMt % 16 == 0, "alignment");
   static_assert(NB * 256 * 4 <= DK * LK * ES, "pairwise scratch fits in R4");

@@ -23,17 +23,31 @@ namespace carve {
 // Largest rank of the content projection (checked on the host).
 constexpr int kMaxRank = 64;
 
+// Waves of a chunk-serial workgroup: eight at d_k = 64 with blocks of 32 or
+// 64 tokens (two waves then share each 16-channel value slice of the state,
+// each holding half of its key-channel tiles), else one per value slice.
+template <int DK, int BL>
+constexpr int serial_waves() { return DK == 64 && BL >= 32 ? 8 : DK / 16; }
+
 template <typename E, int DK, int DV, int BL>
-__global__ void __launch_bounds__((BlockLayout<E, DK, DV, BL>::NT))
+__global__ void __launch_bounds__((BlockLayout<E, DK, DV, BL, serial_waves<DK, BL>()>::NT))
 carve_chunk_serial_kernel(FwdArgs a) {
-  using B = Block<E, DK, DV, BL>;
+  using B = Block<E, DK, DV, BL, serial_waves<DK, BL>()>;
   using LY = typename B::LY;
-  constexpr int NT = LY::NT, NB = LY::NB;
+  using MM = Mma<E>;
+  using Frag = typename B::Frag;
+  constexpr int NT = LY::NT, NB = LY::NB, TD = LY::TD, NU = LY::NU, NW = LY::NW, SPU = MM::SPU;
+  constexpr int PARTS = LY::PARTS, TDP = TD / PARTS, NBP = NB / PARTS;   // state / output tiles per wave
+  constexpr int NF = LY::NFR, NFP = NF / PARTS;                         // S fragments, per wave
+  static_assert(TDP * PARTS == TD && NBP * PARTS == NB && NFP * PARTS == NF && NBP >= 1, "tile parts");
   extern __shared__ __align__(16) unsigned char smem[];
   const auto s = B::carve(smem);
 
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int gq = lane >> 4, cc = lane & 15;
+  // value slice of this wave and its part: state tiles [TDP part, TDP (part + 1)),
+  // output tiles [NBP part, NBP (part + 1))
+  const int slice = wave % NW, part = wave / NW;
   const int bh = blockIdx.x;
   Rows<E> src{static_cast<const E*>(a.q), static_cast<const E*>(a.k), static_cast<const E*>(a.v),
               static_cast<const E*>(a.g), static_cast<const E*>(a.bx), static_cast<const E*>(a.w),
@@ -43,13 +57,28 @@ carve_chunk_serial_kernel(FwdArgs a) {
   E* __restrict__ O = static_cast<E*>(a.o);
   const E* Ud = static_cast<const E*>(a.ub_down);
   const E* Uu = static_cast<const E*>(a.ub_up);
-  const int e0 = 16 * wave;
+  const int e0 = 16 * slice;
+  Frag* xc = reinterpret_cast<Frag*>(smem + LY::oXc);        // [2][NW][NF][64]
+  float* Mp = reinterpret_cast<float*>(smem + LY::oMp);      // [PARTS][DV]
 
   B::zero_lds(smem, LY::serial_bytes);
   const Sink<E> sink = B::lds_sink(s);
-  f32x4 St[DK / 16];
-  B::load_state(a.state_in, bh, wave, St);
-  __syncthreads();
+  // this wave's C tiles of S^T: rows d = 16 (TDP part + t) + 4g + i, column e0 + c
+  f32x4 St[TDP];
+  {
+    const float* Sin = a.state_in ? a.state_in + ((size_t)bh * DV + e0 + cc) * DK + 4 * gq : nullptr;
+#pragma unroll
+    for (int t = 0; t < TDP; ++t) St[t] = Sin ? *reinterpret_cast<const f32x4*>(Sin + 16 * (TDP * part + t)) : zero4();
+  }
+  // this wave's S operand fragments into the exchange buffer of parity p
+  auto share = [&](int p) {
+    if constexpr (PARTS > 1) {
+#pragma unroll
+      for (int q = 0; q < NFP; ++q) xc[((p * NW + slice) * NF + NFP * part + q) * 64 + lane] = MM::from_c(St, q);
+    }
+  };
+  __syncthreads();                                   // the LDS clear is complete
+  share(0);
   for (int e = tid; e < DV; e += NT) s.M[e] = a.mean_in ? a.mean_in[(size_t)bh * DV + e] : 0.f;
   __syncthreads();
 
@@ -59,14 +88,15 @@ carve_chunk_serial_kernel(FwdArgs a) {
   //   y_r = sum_e U_down[h][r][e] m[e]: eight lanes per row r (lane group
   //       gi = lane / 8 of wave w takes r = 8 (w + NWV k) + gi), lane
   //       c = lane % 8 holds e in [c DV/8, (c + 1) DV/8): ud(k, i);
-  //   z_d = sum_r U_up[h][d][r] y_r: four lanes per key channel (d = tid / 4),
-  //       lane q = tid % 4 holds r = q + 4 i: uu(i).
+  //   z_d = sum_r U_up[h][d][r] y_r: TPD = NT / DK lanes per key channel
+  //       (d = tid / TPD), lane q = tid % TPD holds r = q + TPD i: uu(i).
   // Values stay in the input type, two per register; the partial sums are
   // combined with DPP lane moves inside quads and rows.
-  constexpr int NWV = NT / 64, RK = (kMaxRank + 8 * NWV - 1) / (8 * NWV), EPR = DV / 8, RPT = kMaxRank / 4;
-  static_assert(NT == 4 * DK && EPR % 2 == 0 && RPT % 2 == 0, "four threads per key channel");
+  constexpr int NWV = NT / 64, RK = (kMaxRank + 8 * NWV - 1) / (8 * NWV), EPR = DV / 8;
+  constexpr int TPD = NT / DK, RPT = kMaxRank / TPD;
+  static_assert((TPD == 4 || TPD == 8) && EPR % 4 == 0 && RPT % 2 == 0, "lanes per key channel");
   typedef E e2 __attribute__((ext_vector_type(2)));
-  const int zd = tid >> 2, zq = tid & 3, gi = lane >> 3, gc = lane & 7;
+  const int zd = tid / TPD, zq = tid % TPD, gi = lane >> 3, gc = lane & 7;
   e2 ud[RK][EPR / 2], uu[RPT / 2];
 #pragma unroll
   for (int k = 0; k < RK; ++k) {
@@ -77,7 +107,7 @@ carve_chunk_serial_kernel(FwdArgs a) {
   }
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const int r = zq + 4 * i;
+    const int r = zq + TPD * i;
     uu[i / 2][i % 2] = r < rank ? Uu[((size_t)h * DK + zd) * rank + r] : from_f32<E>(0.f);
   }
   // z = U_up (U_down m) into s.Z (all threads call; ends with a barrier)
@@ -106,9 +136,10 @@ carve_chunk_serial_kernel(FwdArgs a) {
       float z = 0.f;
 #pragma unroll
       for (int i = 0; i < RPT; ++i)
-        if (zq + 4 * i < rank) z += to_f32(uu[i / 2][i % 2]) * s.Y[zq + 4 * i];
+        if (zq + TPD * i < rank) z += to_f32(uu[i / 2][i % 2]) * s.Y[zq + TPD * i];
       z = quad_sum(z);
-      if (zq == 0) s.Z[zd] = z;
+      if constexpr (TPD == 8) z += dpp_mov<0x114>(z);  // lanes 4..7 of an eight: the total
+      if (zq == TPD - 1) s.Z[zd] = z;
     }
     __syncthreads();
   };
@@ -138,27 +169,73 @@ carve_chunk_serial_kernel(FwdArgs a) {
     B::grams(s, src, t0, nvalid, fallback, Pt);
     B::inverse_diag(s);
     B::solve(s, qd, Pt);
-    f32x4 CtR[DK / 16], OltR[NB], Ot[NB];
-    B::affine(s, sink, CtR, OltR);
-    B::state_step([&](int dt, int u) { return mtu[(dt * LY::NU + u) * 64 + lane]; },
-                  [&](int rt, int u) { return qeu[(rt * LY::NU + u) * 64 + lane]; }, CtR, OltR, St, Ot);
+    f32x4 CtR[TDP], OltR[NBP], Ot[NBP];
+    B::affine(s, sink, CtR, OltR);                   // ends with a barrier
+    // S operand fragments of the state at the block start: this wave's from
+    // its registers, the other parts' from the exchange buffer
+    Frag sf[NF];
 #pragma unroll
-    for (int rt = 0; rt < NB; ++rt) m_part += Ot[rt];   // tokens past nvalid are exactly 0
-    B::store_out(O, src, t0, nvalid, e0, Ot);
+    for (int p = 0; p < NF; ++p) {
+      if (PARTS == 1 || p / NFP == part) sf[p] = MM::from_c(St, p % NFP);
+      else sf[p] = xc[(((blk & 1) * NW + slice) * NF + p) * 64 + lane];
+    }
+    // O^T = S Qe^T + Ol^T and S^T <- Mt S^T + Ct for this wave's tiles
+    // (reduction steps outermost)
+#pragma unroll
+    for (int j = 0; j < NBP; ++j) Ot[j] = OltR[j];
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+      for (int i = 0; i < SPU; ++i) {
+#pragma unroll
+        for (int j = 0; j < NBP; ++j)
+          Ot[j] = MM::mma(sf[u * SPU + i], MM::step(qeu[((NBP * part + j) * NU + u) * 64 + lane], i), Ot[j]);
+#pragma unroll
+        for (int t = 0; t < TDP; ++t)
+          CtR[t] = MM::mma(MM::step(mtu[((TDP * part + t) * NU + u) * 64 + lane], i), sf[u * SPU + i], CtR[t]);
+      }
+#pragma unroll
+    for (int t = 0; t < TDP; ++t) St[t] = CtR[t];
+    share((blk + 1) & 1);
+#pragma unroll
+    for (int j = 0; j < NBP; ++j) m_part += Ot[j];   // tokens past nvalid are exactly 0
+    // O^T tile NBP part + j: lane (g, c) writes token t0 + 16 (NBP part + j) + c,
+    // channels e0 + 4g .. e0 + 4g + 3
+#pragma unroll
+    for (int j = 0; j < NBP; ++j) {
+      const int r = 16 * (NBP * part + j) + cc;
+      if (r < nvalid)
+        *reinterpret_cast<typename B::e4*>(O + src.row(t0 + r) * DV + e0 + 4 * gq) =
+            typename B::e4{from_f32<E>(Ot[j][0]), from_f32<E>(Ot[j][1]), from_f32<E>(Ot[j][2]), from_f32<E>(Ot[j][3])};
+    }
     __syncthreads();
     const bool chunk_end = ((t0 + BL) % L == 0) || (t0 + BL >= T);
     if (chunk_end) {
       const int chunk = t0 / L;
       const int count = min(L, T - chunk * L);
       const f32x4 tot = sum_cols(m_part);
-      if (cc == 0)
-        *reinterpret_cast<f32x4*>(s.M + e0 + 4 * gq) = tot * (1.0f / (float)count);
+      if constexpr (PARTS == 1) {
+        if (cc == 0) *reinterpret_cast<f32x4*>(s.M + e0 + 4 * gq) = tot * (1.0f / (float)count);
+      } else {
+        if (cc == 0) *reinterpret_cast<f32x4*>(Mp + part * DV + e0 + 4 * gq) = tot;
+        __syncthreads();
+        for (int e = tid; e < DV; e += NT) {
+          float m = 0.f;
+#pragma unroll
+          for (int p = 0; p < PARTS; ++p) m += Mp[p * DV + e];
+          s.M[e] = m * (1.0f / (float)count);
+        }
+      }
       m_part = zero4();
       __syncthreads();
       if (t0 + BL < T) content_bias();
     }
   }
-  if (a.state_out) B::store_state(a.state_out, bh, wave, St);
+  if (a.state_out) {
+    float* So = a.state_out + ((size_t)bh * DV + e0 + cc) * DK + 4 * gq;
+#pragma unroll
+    for (int t = 0; t < TDP; ++t) *reinterpret_cast<f32x4*>(So + 16 * (TDP * part + t)) = St[t];
+  }
   if (a.mean_out)
     for (int e = tid; e < DV; e += NT) a.mean_out[(size_t)bh * DV + e] = s.M[e];
 }
