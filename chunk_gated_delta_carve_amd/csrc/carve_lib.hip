@@ -190,7 +190,7 @@ extern "C" const char* carve_error_string(int code) {
   switch (code) {
     case CARVE_OK: return "ok";
     case CARVE_EINVAL: return "invalid argument (NULL required pointer, negative size, bad rank or overlapping output)";
-    case CARVE_EUNSUPPORTED: return "unsupported configuration (dk/dv in {64,128} with dk == dv, L in {16,32,64,128}, rank <= 64)";
+    case CARVE_EUNSUPPORTED: return "unsupported configuration (dk/dv in {64,128} with dk == dv, L in {16,32,64,128}, rank <= 64, sizes within 32-bit indexing)";
     case CARVE_EALIGN: return "a tensor pointer is not 16-byte aligned";
     case CARVE_EWORKSPACE: return "workspace smaller than carve_recurrent_ref_shapes() requires";
     case CARVE_EHIP: return g_hip_msg;

@@ -47,7 +47,8 @@ extern "C" {
 typedef enum {
   CARVE_OK = 0,
   CARVE_EINVAL = 1,        /* NULL required pointer, negative size, bad rank */
-  CARVE_EUNSUPPORTED = 2,  /* d_k/d_v not in {64,128}, L not in {16,32,64,128}, d_k != d_v */
+  CARVE_EUNSUPPORTED = 2,  /* d_k/d_v not in {64,128}, L not in {16,32,64,128}, d_k != d_v,
+                              rank > 64, or a size past the kernels' 32-bit index range */
   CARVE_EALIGN = 3,        /* a pointer is not 16-byte aligned */
   CARVE_EWORKSPACE = 4,    /* workspace smaller than carve_recurrent_ref_shapes() asks */
   CARVE_EHIP = 5           /* a HIP launch failed; carve_error_string(CARVE_EHIP) has the text */

@@ -62,6 +62,10 @@ def test_shape_contract(L):
     (dict(L=48), _lib.CARVE_EUNSUPPORTED),
     (dict(L=256), _lib.CARVE_EUNSUPPORTED),
     (dict(rank=65), _lib.CARVE_EUNSUPPORTED),
+    # 64 token rows of one head exceed 32-bit byte offsets (the 16-row output
+    # limit alone would still pass)
+    (dict(B=1, H=300000, dk=128, dv=128, dtype=_lib.CARVE_BF16), _lib.CARVE_EUNSUPPORTED),
+    (dict(B=1, H=60000, dk=128, dv=128, dtype=_lib.CARVE_BF16), _lib.CARVE_OK),
     (dict(T=-1), _lib.CARVE_EINVAL),
     (dict(B=-2), _lib.CARVE_EINVAL),
     (dict(rank=-1), _lib.CARVE_EINVAL),
