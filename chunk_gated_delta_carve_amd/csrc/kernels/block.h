@@ -880,14 +880,6 @@ struct Block {
   //   S^T <- Mt S^T + Ct
   // The S fragments serve as the A operand of the first product and the B
   // operand of the second. mt(dt, u) and qe(rt, u) return operand units.
-  template <typename MtF, typename QeF>
-  __device__ static void state_step(MtF mt, QeF qe, const f32x4 (&Ct)[TD], const f32x4 (&Olt)[NB],
-                                    f32x4 (&St)[TD], f32x4 (&Ot)[NB]) {
-    Frag sf[DK / KS];
-    state_frags(St, sf);
-    state_out(qe, Olt, sf, Ot);
-    state_chain(mt, Ct, sf, St);
-  }
   // the S operand fragments (bf16 or fp32) of the current state
   __device__ static void state_frags(const f32x4 (&St)[TD], Frag (&sf)[DK / KS]) {
 #pragma unroll
@@ -939,20 +931,6 @@ struct Block {
 #pragma unroll
     for (int dt = 0; dt < TD; ++dt)
       *reinterpret_cast<f32x4*>(S + ((size_t)bh * DV + 16 * ws + cc) * DK + 16 * dt + 4 * gq) = St[dt];
-  }
-
-  // O^T tile rt of this slice: lane (g, c) writes token t0 + 16 rt + c, value
-  // channels e0 + 4g .. e0 + 4g + 3, one vector store per lane
-  __device__ static void store_out(E* O, const Rows<E>& src, int t0, int nvalid, int e0, const f32x4 (&Ot)[NB]) {
-    const int lane = threadIdx.x & 63;
-    const int gq = lane >> 4, cc = lane & 15;
-#pragma unroll
-    for (int rt = 0; rt < NB; ++rt) {
-      const int r = 16 * rt + cc;
-      if (r < nvalid)
-        *reinterpret_cast<e4*>(O + src.row(t0 + r) * DV + e0 + 4 * gq) =
-            e4{from_f32<E>(Ot[rt][0]), from_f32<E>(Ot[rt][1]), from_f32<E>(Ot[rt][2]), from_f32<E>(Ot[rt][3])};
-    }
   }
 };
 
