@@ -707,7 +707,13 @@ struct Block {
   // Ends with a barrier.
   static constexpr int CTW = (DK + DV) / 16 / NWV;         // [W | U] column tiles per wave
   static_assert(CTW >= 1 && CTW * NWV * 16 == DK + DV && (DK / 16) % CTW == 0, "solve tiles");
-  __device__ static void solve(const Smem& s, const E (&qd)[16], const f32x4 (&Pt)[TPW]) {
+  // kImage = false: W^T and U^T go to LDS for affine(). kImage = true (the
+  // chunk-parallel intra kernel): the block's affine maps are formed at once
+  // from the X tiles in registers and written to the image at img (see
+  // image_from_x); no W^T / U^T round trip through LDS.
+  template <bool kImage = false>
+  __device__ static void solve(const Smem& s, const E (&qd)[16], const f32x4 (&Pt)[TPW],
+                               unsigned char* img = nullptr) {
     const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     const int gq = lane >> 4, cc = lane & 15;
     // all column tiles of a wave lie on the same side of [W | U]
@@ -784,6 +790,11 @@ struct Block {
 #pragma unroll
       for (int t = 0; t < CTW; ++t) X[I][t] = M16::round(M16::mma(Trow[I], M16::round(acc[t]), zero4()));
     }
+    if constexpr (kImage) {
+      __syncthreads();                               // P, Qd and KdT are complete
+      image_from_x(s, X, isW, col0 - cc, img);
+      return;
+    }
     // transposed stores: lane holds rows 4gq..4gq+3 of column col -> 4 consecutive
     E* dst = isW ? s.Wt : s.Ut;
 #pragma unroll
@@ -798,6 +809,85 @@ struct Block {
           for (int i = 0; i < 4; ++i) rowp[j + i] = from_f32<E>(0.f);
     }
     __syncthreads();
+  }
+
+  // -------------------------------------------------------------- affine maps from X
+  // The block's affine maps from the [W | U] column tiles x0 .. x0 + 16 CTW
+  // of this wave, held as C tiles X[I][t] (rows j = 16 I + 4g + i, column
+  // x0 + 16 t + c), with every product taking X as one operand and K_dec^T,
+  // P or Q_dec from LDS as the other:
+  //   W tiles (x = k):  M[k][d] = e^{G_BL}[d] [k = d] - sum_j W[j][k] Kdec[j][d]
+  //                     Qe[r][k] = Qd[r][k] - sum_j P[r][j] W[j][k]
+  //     With X^T as the A operand, lane (g, c) gets k = x + 4g + i against
+  //     d = 16 D + c (or r = 16 R + c): one half of an image unit of M^T (or
+  //     Q_eff), written as an 8-byte store.
+  //   U tiles (x = e, one value slice each):
+  //                     C^T[d][e] = sum_j Kdec[j][d] U[j][e]   (K_dec^T as A, X as B)
+  //                     Ol^T[e][r] = sum_j U[j][e] P[r][j]      (X^T as A, P^T as B)
+  //     C tiles, written in the image's pairs.
+  // P is strictly lower triangular: row block R takes j < 16 (R + 1) only.
+  __device__ static void image_from_x(const Smem& s, const e4 (&X)[NB][CTW], bool isW, int x0,
+                                      unsigned char* img) {
+    using M16 = Mma16<E>;
+    static_assert(sizeof(E) == 2 && KP == BL, "bf16 images of full 32- or 64-token blocks");
+    const int lane = threadIdx.x & 63, gq = lane >> 4, cc = lane & 15;
+    // B (or A) operand rows from LDS: 4 values j = 16 I + 4g .. + 3 of row `row`
+    auto rd = [&](const E* base, int pitch, int row, int I) {
+      return *reinterpret_cast<const e4*>(base + row * pitch + 16 * I + 4 * gq);
+    };
+    if (isW) {
+#pragma unroll
+      for (int t = 0; t < CTW; ++t) {
+        const int kt = x0 / 16 + t, u = kt / 2, half = kt % 2;
+#pragma unroll
+        for (int D = 0; D < TD; ++D) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int I = 0; I < NB; ++I) acc = M16::mma(X[I][t], rd(s.KdT, LK, 16 * D + cc, I), acc);
+          const float eg = s.Egl[16 * D + cc];
+          e4 v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            v[i] = from_f32<E>((16 * kt + 4 * gq + i == 16 * D + cc ? eg : 0.f) - acc[i]);
+          *reinterpret_cast<e4*>(img + LY::wMt + ((D * NU + u) * 64 + lane) * 16 + half * 8) = v;
+        }
+#pragma unroll
+        for (int R = 0; R < NB; ++R) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int I = 0; I <= R; ++I) acc = M16::mma(X[I][t], rd(s.P, LK, 16 * R + cc, I), acc);
+          const e4 q = *reinterpret_cast<const e4*>(s.Qd + (16 * R + cc) * LD + 16 * kt + 4 * gq);
+          e4 v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = from_f32<E>(to_f32(q[i]) - acc[i]);
+          *reinterpret_cast<e4*>(img + LY::wQe + ((R * NU + u) * 64 + lane) * 16 + half * 8) = v;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < CTW; ++t) {
+        const int slice = x0 / 16 + t;
+        f32x4 Ct[TD], Ol[NB];
+#pragma unroll
+        for (int D = 0; D < TD; ++D) {
+          Ct[D] = zero4();
+#pragma unroll
+          for (int I = 0; I < NB; ++I) Ct[D] = M16::mma(rd(s.KdT, LK, 16 * D + cc, I), X[I][t], Ct[D]);
+        }
+#pragma unroll
+        for (int R = 0; R < NB; ++R) {
+          Ol[R] = zero4();
+#pragma unroll
+          for (int I = 0; I <= R; ++I) Ol[R] = M16::mma(X[I][t], rd(s.P, LK, 16 * R + cc, I), Ol[R]);
+        }
+        e8* ct = reinterpret_cast<e8*>(img + LY::wCt) + slice * (TD / 2) * 64 + lane;
+        e8* ol = reinterpret_cast<e8*>(img + LY::wOl) + slice * (NB / 2) * 64 + lane;
+#pragma unroll
+        for (int a = 0; a < TD / 2; ++a) ct[a * 64] = pair(Ct[2 * a], Ct[2 * a + 1]);
+#pragma unroll
+        for (int a = 0; a < NB / 2; ++a) ol[a * 64] = pair(Ol[2 * a], Ol[2 * a + 1]);
+      }
+    }
   }
 
   // -------------------------------------------------------------- affine maps

@@ -275,10 +275,7 @@ carve_intra_kernel(FwdArgs a) {
   const bool fallback = B::template gate_pass<false>(s, raw, nvalid, qd);
   B::grams(s, src, t0, nvalid, fallback, Pt);
   B::inverse_diag(s);
-  B::solve(s, qd, Pt);
-  f32x4 CtR[B::CTP], OltR[B::OLP];
-  B::template affine<false>(s, B::image_sink(img), CtR, OltR);   // put_frags rounds them
-  B::put_frags(img, CtR, OltR);
+  B::template solve<true>(s, qd, Pt, img);           // also writes the block's image
 }
 
 // Output waves of a state-pass workgroup, next to its one chain wave.
