@@ -184,9 +184,10 @@ struct Rows {
   __device__ __forceinline__ size_t row(int t) const { return (size_t)(bidx * T + t) * H + h; }
 };
 
-// Where a block's shared affine maps go, as fragment units: LDS (chunk-serial
-// kernel) or the workspace image (chunk-parallel kernel). C^T and Ol^T stay in
-// the registers of the wave that owns their value channels.
+// Where affine() puts a block's shared affine maps, as fragment units (LDS of
+// the chunk-serial kernel). C^T and Ol^T stay in the registers of the waves
+// that own their value channels. (The chunk-parallel intra kernel writes all
+// four straight to its workspace image instead: image_from_x.)
 template <typename E>
 struct Sink {
   typename Mma<E>::unit* Mt;   // [TD][NU][64]
@@ -247,26 +248,12 @@ struct Block {
   __device__ static Sink<E> lds_sink(const Smem& s) {
     return Sink<E>{reinterpret_cast<Unit*>(s.Mt), reinterpret_cast<Unit*>(s.Qe)};
   }
-  __device__ static Sink<E> image_sink(unsigned char* img) {
-    return Sink<E>{reinterpret_cast<Unit*>(img + LY::wMt), reinterpret_cast<Unit*>(img + LY::wQe)};
-  }
-  // this wave's C^T and Ol^T tiles into an image: tiles 2i and 2i + 1 of a
-  // lane side by side (16 bytes per lane for bf16)
+  // two C tiles of a lane side by side, as the image holds C^T and Ol^T
+  // (16 bytes per lane for bf16)
   typedef E e8 __attribute__((ext_vector_type(8)));
   __device__ static e8 pair(f32x4 x, f32x4 y) {
     return e8{from_f32<E>(x[0]), from_f32<E>(x[1]), from_f32<E>(x[2]), from_f32<E>(x[3]),
               from_f32<E>(y[0]), from_f32<E>(y[1]), from_f32<E>(y[2]), from_f32<E>(y[3])};
-  }
-  __device__ static void put_frags(unsigned char* img, const f32x4 (&CtR)[CTP], const f32x4 (&OltR)[OLP]) {
-    static_assert(CTP % 2 == 0 && OLP % 2 == 0, "paired tiles");
-    const int wave = wave_id(), lane = threadIdx.x & 63;
-    const int slice = wave % NW, part = wave / NW;
-    e8* ct = reinterpret_cast<e8*>(img + LY::wCt) + (slice * (TD / 2) + part * (CTP / 2)) * 64 + lane;
-    e8* ol = reinterpret_cast<e8*>(img + LY::wOl) + (slice * (NB / 2) + part * (OLP / 2)) * 64 + lane;
-#pragma unroll
-    for (int a = 0; a < CTP / 2; ++a) ct[a * 64] = pair(CtR[2 * a], CtR[2 * a + 1]);
-#pragma unroll
-    for (int a = 0; a < OLP / 2; ++a) ol[a * 64] = pair(OltR[2 * a], OltR[2 * a + 1]);
   }
 
   __device__ static void zero_lds(unsigned char* smem, int bytes) {
@@ -702,15 +689,14 @@ struct Block {
   // with T_II the diagonal inverses. Wave w solves the CTW 16-column tiles
   // CTW w .. CTW w + CTW - 1 of [W | U], keeping its X_J tiles in
   // registers. Once every operand is in registers the Qx/Ky/A region takes
-  // Qd (from the gate-pass registers) and P (from the Gram registers); the
-  // results go transposed (W^T over Kx, U^T over V) for the affine products.
-  // Ends with a barrier.
+  // Qd (from the gate-pass registers) and P (from the Gram registers).
+  // kImage = false: the results go transposed (W^T over Kx, U^T over V) for
+  // affine(); ends with a barrier. kImage = true (the chunk-parallel intra
+  // kernel): after a barrier the block's affine maps are formed at once from
+  // the X tiles in registers and written to the image at img (see
+  // image_from_x); no W^T / U^T round trip through LDS, and no final barrier.
   static constexpr int CTW = (DK + DV) / 16 / NWV;         // [W | U] column tiles per wave
   static_assert(CTW >= 1 && CTW * NWV * 16 == DK + DV && (DK / 16) % CTW == 0, "solve tiles");
-  // kImage = false: W^T and U^T go to LDS for affine(). kImage = true (the
-  // chunk-parallel intra kernel): the block's affine maps are formed at once
-  // from the X tiles in registers and written to the image at img (see
-  // image_from_x); no W^T / U^T round trip through LDS.
   template <bool kImage = false>
   __device__ static void solve(const Smem& s, const E (&qd)[16], const f32x4 (&Pt)[TPW],
                                unsigned char* img = nullptr) {
@@ -903,9 +889,6 @@ struct Block {
   // w mod NW, channels [16 slice, 16 slice + 16) (part w / NW of them when
   // several waves share a slice), and keeps them in registers (CtR, OltR).
   // Ends with a barrier.
-  // kRound: round CtR and OltR to E here (they seed fp32 accumulators);
-  // callers that only store them as E leave the rounding to that store.
-  template <bool kRound = true>
   __device__ static void affine(const Smem& s, const Sink<E>& out, f32x4 (&CtR)[CTP], f32x4 (&OltR)[OLP]) {
     const int wave = wave_id(), lane = threadIdx.x & 63;
     const int gq = lane >> 4, cc = lane & 15;
@@ -946,18 +929,16 @@ struct Block {
 #pragma unroll
     for (int j = 0; j < CTP; ++j) {
       f32x4 acc = product(s.KdT, part * CTP + j, s.Ut, slice, MM::steps(KP));
-      if constexpr (kRound)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = to_f32(from_f32<E>(acc[i]));
+      for (int i = 0; i < 4; ++i) acc[i] = to_f32(from_f32<E>(acc[i]));
       CtR[j] = acc;
     }
 #pragma unroll
     for (int j = 0; j < OLP; ++j) {
       const int a = part * OLP + j;
       f32x4 acc = product(s.Ut, slice, s.P, a, MM::steps(16 * (a + 1)));
-      if constexpr (kRound)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = to_f32(from_f32<E>(acc[i]));
+      for (int i = 0; i < 4; ++i) acc[i] = to_f32(from_f32<E>(acc[i]));
       OltR[j] = acc;
     }
     __syncthreads();
