@@ -11,10 +11,11 @@
 //       workgroup per block); each block's state-pass operands go to a
 //       workspace, and a per-(batch, head) kernel then runs only the serial
 //       state update and the output.
-// Both schedules call the same device functions in the same order and round
-// the same intermediates to the input type. The chunk-parallel pair splits a
-// block's stages over more waves, so a few fp32 sums run in another order: the
-// two schedules agree to rounding, not bit for bit.
+// Both schedules compute the same per-block quantities and round the same
+// intermediates to the input type. The chunk-parallel pair forms the affine
+// maps with other products (from the solve's registers) and splits stages
+// over the waves differently, so some fp32 sums run in another order: the two
+// schedules agree to rounding, not bit for bit.
 #pragma once
 #include "block.h"
 
