@@ -10,7 +10,10 @@ another of the named shapes.
 Prints one JSON line. `roofline` covers one call of the layer (its kernels
 run back to back on one stream): algorithmic bytes per call over the GPU time
 per call, taken from one pair of HIP events recorded on that stream around the
-timed steps. `cpu_baseline` is the float64 oracle timed on this host.
+timed steps. `mfma` is the matrix-core roofline of the same call (algorithmic
+FLOPs over the same time, against the dense peak of the input type), with the
+committed rocprofv3 matrix-core counters when they match the kernel sources.
+`cpu_baseline` is the float64 oracle timed on this host.
 """
 import argparse
 import json
@@ -22,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}    # dense matrix-core peaks per input type
 
 
 def algorithmic_bytes(B, T, H, dk, dv, es, rank=0):
@@ -29,6 +33,22 @@ def algorithmic_bytes(B, T, H, dk, dv, es, rank=0):
     the fp32 final state and the fp32 final mean."""
     per_tok = (4 * dk + dv + 1 + dv) * es
     return B * T * H * per_tok + H * rank * (dk + dv) * es + B * H * dv * dk * 4 + B * H * dv * 4
+
+
+def algorithmic_flops(B, T, H, dk, dv, L, rank=0):
+    """FLOPs of the triangle-aware WY chunk form (2 per multiply-add), per chunk
+    of L tokens: the gated Grams A and P (L(L-1)/2 d_k each), the unit-lower
+    inverse (L(L-1)(L-2)/6), W and U (L(L+1)/2 (d_k + d_v)), the residual, the
+    state update and the inter-chunk readout (3 L d_k d_v), the masked
+    intra-chunk readout (L(L-1)/2 d_v), the content bias and the chunk mean
+    (r (d_k + d_v) + L d_v). Work an implementation adds on top (the affine maps
+    of the two-pass split) is not counted."""
+    def chunk(l):
+        mac = (l * (l - 1) * dk + l * (l - 1) * (l - 2) // 6 + l * (l + 1) // 2 * (dk + dv)
+               + 3 * l * dk * dv + l * (l - 1) // 2 * dv + rank * (dk + dv) + l * dv)
+        return 2 * mac
+    full, tail = divmod(T, L)
+    return B * H * (full * chunk(L) + (chunk(tail) if tail else 0))
 
 
 def cpu_baseline(wl, inp, budget_s):
@@ -162,6 +182,84 @@ def write_traffic_summary(wl, fetch_csv, write_csv, commands):
     print(open(traffic_file(wl)).read())
 
 
+def mfma_file(wl):
+    return os.path.join(ROOT, "profiles", f"carve_chunk_fwd_{wl.tag()}_mfma.md")
+
+
+def measured_mfma(wl):
+    """Matrix-core counters per call from the committed rocprofv3 summary for this
+    workload ({"mfma_flops": executed MFMA FLOPs, "mfma_busy": busy fraction of
+    the SIMDs' matrix cores over the kernels' active time}), or None when there is
+    none or the kernel sources have changed since the counters were taken."""
+    path = mfma_file(wl)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for ln in f:
+            if ln.startswith("- ") and ": " in ln:
+                key, val = ln[2:].split(": ", 1)
+                fields[key.strip()] = val.strip().strip("`")
+    if fields.get("kernel sources sha256/16") != sources_sha():
+        return None
+    return {"mfma_flops": float(fields["executed MFMA FLOPs per launch"]),
+            "mfma_busy": float(fields["MFMA busy fraction (time-weighted)"])}
+
+
+def write_mfma_summary(wl, pmc_csv, trace_csv, commands):
+    """Turn a rocprofv3 --pmc run (MfmaUtil, MfmaFlopsBF16 and MfmaFlopsF32; csv)
+    and a --kernel-trace --stats run (for the kernels' durations) over bench.py
+    into the summary that measured_mfma reads."""
+    import csv
+    from collections import defaultdict
+
+    vals = defaultdict(lambda: defaultdict(list))
+    with open(pmc_csv) as f:
+        for r in csv.DictReader(f):
+            if "carve_" in r["Kernel_Name"]:
+                vals[r["Kernel_Name"].split("(")[0]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    dur = {}
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            if "carve_" in r["Name"]:
+                dur[r["Name"].split("(")[0]] = float(r["MinNs"]) * 1e-9
+    rows, flops_tot, busy_w, t_tot = [], 0.0, 0.0, 0.0
+    for name, c in sorted(vals.items()):
+        avg = {k: sum(v) / len(v) for k, v in c.items()}
+        fl = avg.get("MfmaFlopsBF16", 0.0) + avg.get("MfmaFlopsF32", 0.0)
+        util = avg.get("MfmaUtil", 0.0) / 100.0
+        t = dur.get(name)
+        rows.append((name, len(c.get("MfmaUtil", [])), fl, util, t))
+        flops_tot += fl
+        if t:
+            busy_w += util * t
+            t_tot += t
+    alg = algorithmic_flops(wl.B, wl.T, wl.H, wl.dk, wl.dv, wl.L, wl.rank)
+    peak = MFMA_PEAK_TFLOPS["bf16" if wl.dtype == "bf16" else "f32"]
+    with open(mfma_file(wl), "w") as f:
+        f.write(f"# Matrix-core use of carve_chunk_fwd, {wl.describe()}\n\n")
+        f.write("Counters from one rocprofv3 --pmc run (derived metrics MfmaUtil = busy cycles of the "
+                "SIMDs' matrix cores over GRBM_GUI_ACTIVE x SIMD count, MfmaFlopsBF16/F32 = MFMA "
+                "operations x 512), durations (fastest call) from one --kernel-trace --stats run of the "
+                "same command:\n\n")
+        for cmd in commands:
+            f.write(f"    {cmd}\n")
+        f.write("\n| kernel | dispatches | executed MFMA FLOPs per dispatch | MFMA busy | duration (us) | "
+                "executed TFLOP/s | fraction of peak |\n|---|---|---|---|---|---|---|\n")
+        for name, n, fl, util, t in rows:
+            rate = fl / t / 1e12 if t else float("nan")
+            f.write(f"| `{name}` | {n} | {fl:.4g} | {100 * util:.1f}% | "
+                    f"{(t or float('nan')) * 1e6:.2f} | {rate:.1f} | {rate / peak:.4f} |\n")
+        f.write(f"\nPeak: {peak} TFLOP/s dense ({wl.dtype} inputs). The algorithmic count of the method "
+                "(triangle-aware WY chunk form, what bench.py reports as mfma.achieved) is below the "
+                "executed count: the two-pass split forms each block's affine maps as extra products.\n\n")
+        f.write(f"- executed MFMA FLOPs per launch: {flops_tot:.0f}\n")
+        f.write(f"- algorithmic FLOPs per launch: {alg}\n")
+        f.write(f"- MFMA busy fraction (time-weighted): {busy_w / t_tot if t_tot else 0.0:.4f}\n")
+        f.write(f"- kernel sources sha256/16: `{sources_sha()}`\n")
+    print(open(mfma_file(wl)).read())
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,7 +275,10 @@ def main():
                     help="run a plain device copy of known size first (for counter calibration)")
     ap.add_argument("--write-traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic summary from two rocprofv3 --pmc csv files and exit")
-    ap.add_argument("--commands", nargs="*", default=[], help="commands recorded in the traffic summary")
+    ap.add_argument("--write-mfma-summary", nargs=2, metavar=("PMC_CSV", "STATS_CSV"),
+                    help="write the matrix-core summary from a rocprofv3 --pmc csv (MfmaUtil, MfmaFlopsBF16, "
+                         "MfmaFlopsF32) and a --kernel-trace --stats csv, and exit")
+    ap.add_argument("--commands", nargs="*", default=[], help="commands recorded in a counter summary")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -195,6 +296,9 @@ def main():
         wl = wl.with_(L=args.L)
     if args.write_traffic_summary:
         write_traffic_summary(wl, *args.write_traffic_summary, args.commands)
+        return
+    if args.write_mfma_summary:
+        write_mfma_summary(wl, *args.write_mfma_summary, args.commands)
         return
     inp = make_inputs(wl)
     t = {k: to_torch(v, wl.dtype) for k, v in inp.items()}
@@ -253,6 +357,9 @@ def main():
 
     alg = algorithmic_bytes(B, T, H, dk, dv, es, rank)
     achieved = alg / (avg_kernel_ms * 1e-3) / 1e9
+    flops = algorithmic_flops(B, T, H, dk, dv, L, rank)
+    tflops = flops / (avg_kernel_ms * 1e-3) / 1e12
+    mfma_peak = MFMA_PEAK_TFLOPS["bf16" if wl.dtype == "bf16" else "f32"]
     tokens = B * T
     parallel = rank == 0 and wl.dtype == "bf16"
     kernels = ("carve_intra_kernel + carve_state_kernel (one call)" if parallel
@@ -278,6 +385,10 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(wl),
                      "kernel": kernels, "kernel_ms": avg_kernel_ms,
                      "algorithmic_bytes_per_launch": alg, "kernel_ms_cold_cache": float(np.median(cold))},
+        # the matrix-core roofline of the same call: not the bound (the path's
+        # FLOP per byte is far below the MFMA/HBM ridge), reported beside it
+        "mfma": {"achieved": tflops, "peak": mfma_peak, "unit": "TFLOP/s", "frac": tflops / mfma_peak,
+                 "algorithmic_flops_per_launch": flops, "counters": measured_mfma(wl)},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
