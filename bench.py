@@ -342,6 +342,31 @@ def main():
     ms_per_step = 1e3 * wall / args.steps
     avg_kernel_ms = ev_start.elapsed_time(ev_end) / args.steps   # GPU time of one call
 
+    # single calls, each between its own pair of events: median and minimum
+    single = []
+    for _ in range(20):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        step()
+        e.record(stream)
+        torch.cuda.synchronize()
+        single.append(s.elapsed_time(e))
+
+    # reference: what a plain device copy (one elementwise kernel that reads and
+    # writes COPY_BYTES) reaches on this GPU
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for _ in range(10):
+        torch.neg(src, out=dst)
+    e.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * COPY_BYTES * 10 / (s.elapsed_time(e) * 1e-3) / 1e9
+    del src, dst
+
     # the same launch with the caches flushed before it (512 MB write, untimed)
     flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
     cold = []
@@ -384,7 +409,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(wl),
                      "kernel": kernels, "kernel_ms": avg_kernel_ms,
-                     "algorithmic_bytes_per_launch": alg, "kernel_ms_cold_cache": float(np.median(cold))},
+                     "algorithmic_bytes_per_launch": alg, "kernel_ms_cold_cache": float(np.median(cold)),
+                     "kernel_ms_single_median": float(np.median(single)),
+                     "kernel_ms_single_min": float(np.min(single)), "copy_kernel_gbs": copy_gbs},
         # the matrix-core roofline of the same call: not the bound (the path's
         # FLOP per byte is far below the MFMA/HBM ridge), reported beside it
         "mfma": {"achieved": tflops, "peak": mfma_peak, "unit": "TFLOP/s", "frac": tflops / mfma_peak,
