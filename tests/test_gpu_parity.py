@@ -192,6 +192,8 @@ EDGE = [
     ("par-d128-L64", "bf16", 1, 3, 512, 128, 64, 0),
     # 13 blocks: the state pass's prefetch loops end in partial rounds
     ("par-nblk13", "bf16", 2, 3, 832, 64, 64, 0),
+    # 15 (batch, head) pairs: the state pass's placement groups of eight end part-full
+    ("par-BH15", "bf16", 3, 5, 256, 64, 64, 0),
 ]
 
 
