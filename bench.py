@@ -281,7 +281,7 @@ def main():
     ap.add_argument("--commands", nargs="*", default=[], help="commands recorded in a counter summary")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(every (batch, head) pair is independent, so sharding is data placement)", file=sys.stderr)
         sys.exit(2)
 
