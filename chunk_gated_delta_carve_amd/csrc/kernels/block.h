@@ -375,16 +375,18 @@ struct Block {
           pre[i][j] = run[j];
         }
       }
-      // prefix over the row quarters: lanes dq, dq + 16, dq + 32, dq + 48
-      f32x4 incl = run;
+      // exclusive prefix over the row quarters (lanes dq, dq + 16, dq + 32,
+      // dq + 48) with cross-row lane swaps: the 16-lane swap gives each odd
+      // row the total of the row below it and each row its pair's total; the
+      // 32-lane swap gives rows 2 and 3 the total of rows 0 and 1
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float y = __shfl_up(incl[j], 16);
-        if (qr >= 1) incl[j] += y;
-        y = __shfl_up(incl[j], 32);
-        if (qr >= 2) incl[j] += y;
-        y = __shfl_up(incl[j], 16);
-        excl[j] = qr >= 1 ? y : 0.f;
+        const unsigned v = __float_as_uint(run[j]);
+        const auto p16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        const float even = __uint_as_float(p16[0]), odd = __uint_as_float(p16[1]);
+        const unsigned pair = __float_as_uint(even + odd);
+        const float low = __uint_as_float(__builtin_amdgcn_permlane32_swap(pair, pair, false, false)[0]);
+        excl[j] = qr == 0 ? 0.f : qr == 1 ? even : qr == 2 ? low : even + low;
       }
 #pragma unroll
       for (int i = 0; i < RPL; ++i)
@@ -419,8 +421,9 @@ struct Block {
       // P_I for I <= NB; Gs/Ge picked by the wave-uniform gs
       f32x4 P[NB + 1];
       P[0] = zero4();
+      P[1] = sb[0];
 #pragma unroll
-      for (int I = 0; I < NB; ++I) P[I + 1] = P[I] + sb[I];
+      for (int I = 1; I < NB; ++I) P[I + 1] = P[I] + sb[I];
       f32x4 Gs = P[0], seg = sb[0];
 #pragma unroll
       for (int I = 1; I < NB; ++I)
