@@ -44,7 +44,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["sigmoid", "carve_forward", "content_gate_bias"]
+__all__ = ["sigmoid", "carve_forward", "carve_step", "content_gate_bias"]
 
 
 def sigmoid(x: np.ndarray) -> np.ndarray:
@@ -65,6 +65,25 @@ def content_gate_bias(m: np.ndarray, U_down: np.ndarray | None,
         return None
     y = np.einsum("hre,bhe->bhr", U_down, m)        # U_down m: [B, H, r]
     return np.einsum("hdr,bhr->bhd", U_up, y)       # U_up (U_down m): [B, H, d_k]
+
+
+def _token(S, q, k, v, g, bx, w, z):
+    """One token of the recurrence for every (batch, head), in float64.
+
+    S [B, H, d_v, d_k]; q, k, g, bx [B, H, d_k]; v [B, H, d_v]; w [B, H];
+    z [B, H, d_k] or None. Returns (o_t, S_t):
+      b   = sigmoid(bx + z)                       [S3], key axis only [S2]
+      o_t = S q                                   readout before the update [S3]
+      S   = S diag(exp(g))                        key-axis decay [S5], R2
+      S   = S - (S (b*k)) k^T + w v k^T           erase then write [S4], R1
+    """
+    b = sigmoid(bx if z is None else bx + z)                     # [B, H, dk]
+    ot = np.einsum("bhed,bhd->bhe", S, q)                        # o_t = S_{t-1} q_t
+    S = S * np.exp(g)[:, :, None, :]                             # decay columns (key axis)
+    r = np.einsum("bhed,bhd->bhe", S, b * k)                     # erase-weighted retrieval
+    delta = w[:, :, None] * v - r                                # [B, H, dv]
+    S = S + delta[:, :, :, None] * k[:, :, None, :]
+    return ot, S
 
 
 def carve_forward(q, k, v, g, bx, w, L, U_down=None, U_up=None,
@@ -106,14 +125,39 @@ def carve_forward(q, k, v, g, bx, w, L, U_down=None, U_up=None,
         acc = np.zeros((B, H, dv))
         t_end = min(T, (c + 1) * L)                              # reading R6
         for t in range(c * L, t_end):
-            logit = bx[:, t] if z is None else bx[:, t] + z
-            b = sigmoid(logit)                                   # [B, H, dk]
-            ot = np.einsum("bhed,bhd->bhe", S, q[:, t])          # o_t = S_{t-1} q_t
+            ot, S = _token(S, q[:, t], k[:, t], v[:, t], g[:, t], bx[:, t], w[:, t], z)
             o[:, t] = ot
             acc += ot
-            S = S * np.exp(g[:, t])[:, :, None, :]               # decay columns (key axis)
-            r = np.einsum("bhed,bhd->bhe", S, b * k[:, t])        # erase-weighted retrieval
-            delta = w[:, t, :, None] * v[:, t] - r               # [B, H, dv]
-            S = S + delta[:, :, :, None] * k[:, t][:, :, None, :]
         m = acc / (t_end - c * L)
     return o, S, m
+
+
+def carve_step(state, mean_prev, chunk_acc, pos, q, k, v, g, bx, w, L,
+               U_down=None, U_up=None):
+    """One decode step: token `pos` (0 <= pos < L) of its chunk, for every
+    (batch, head), in float64.
+
+    Arguments (any float dtype; upcast to float64):
+      state      : [B, H, d_v, d_k]  the state before this token
+      mean_prev  : [B, H, d_v]       mean of the previous chunk's outputs (R3)
+      chunk_acc  : [B, H, d_v]       sum of this chunk's outputs before this token
+      q, k, g, bx: [B, H, d_k];  v: [B, H, d_v];  w: [B, H]
+      U_down, U_up as in carve_forward.
+    Returns (o [B, H, d_v], state, mean_prev, chunk_acc) after the token. At
+    the chunk's last position (pos == L - 1) the chunk's mean replaces
+    mean_prev and the sum restarts from zero. Stepping tokens 0 .. T-1 with
+    pos = t mod L from (state_in, mean_in, 0) reproduces carve_forward's o and
+    state; after a whole chunk, mean_prev is its m_c.
+    """
+    f = lambda x: np.asarray(x, dtype=np.float64)
+    if not 0 <= pos < L:
+        raise ValueError("pos must lie in [0, L)")
+    Ud = None if U_down is None else f(U_down)
+    Uu = None if U_up is None else f(U_up)
+    m = f(mean_prev)
+    z = content_gate_bias(m, Ud, Uu)                              # gate of this chunk (R3)
+    ot, S = _token(f(state), f(q), f(k), f(v), f(g), f(bx), f(w), z)
+    acc = f(chunk_acc) + ot
+    if pos == L - 1:
+        m, acc = acc / L, np.zeros_like(acc)
+    return ot, S, m, acc

@@ -13,7 +13,7 @@ import os
 import numpy as np
 import pytest
 
-from oracle import carve_forward, sigmoid
+from oracle import carve_forward, carve_step, sigmoid
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -332,3 +332,63 @@ def test_empty_sequence_passes_state_through():
     assert o.shape == (1, 0, 2, 3)
     np.testing.assert_array_equal(S, S_in)
     np.testing.assert_array_equal(m, m_in)
+
+
+# ---------------------------------------------------------------- decode step
+
+def test_step_hand_worked_example():
+    """The 4-token hand-worked pass (tests/golden), taken one decode step at a
+    time: every output, the final state and both chunk means."""
+    fx = json.load(open(os.path.join(HERE, "golden", "hand_worked_content_gate.json")))
+    tok = lambda key, t: np.array(fx[key][t], dtype=np.float64)   # [B, H, d]
+    Ud = np.array(fx["U_down"])
+    Uu = np.log(np.array(fx["U_up_exp"]))
+    L = fx["L"]
+    S = np.array(fx["state_in"], dtype=np.float64)
+    m = np.zeros((1, 1, 1))
+    acc = np.zeros((1, 1, 1))
+    means = []
+    for t in range(4):
+        p = tok("bx_sigmoid", t)
+        o, S, m, acc = carve_step(S, m, acc, t % L, tok("q", t), tok("k", t), tok("v", t),
+                                  np.log(tok("g_exp", t)), np.log(p / (1 - p)), np.array(fx["w"][t]), L, Ud, Uu)
+        np.testing.assert_allclose(o, tok("expected_o", t), rtol=0, atol=1e-12)
+        if t % L == L - 1:
+            means.append(float(m[0, 0, 0]))
+            assert not acc.any()
+    np.testing.assert_allclose(S, np.array(fx["expected_state_out"]), rtol=0, atol=1e-12)
+    # m0 = (4 + 1) / 2 (derivation in the fixture), m1 = the fixture's mean_out
+    np.testing.assert_allclose(means, [2.5, np.array(fx["expected_mean_out"]).item()], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("T,L", [(10, 4), (8, 4), (7, 1), (5, 8)])
+def test_step_sequence_equals_forward(T, L):
+    """Stepping t = 0 .. T-1 with pos = t mod L from (state_in, mean_in, 0)
+    gives the forward pass's outputs and state; after the last whole chunk the
+    carried mean is that chunk's mean, and a partial last chunk's mean is the
+    carried sum over its tokens."""
+    rng = np.random.default_rng(T * 10 + L)
+    B, H, dk, dv, r = 2, 3, 5, 4, 3
+    q, k, v, g, bx, w, Ud, Uu = rand_inputs(rng, B, T, H, dk, dv, rank=r)
+    S_in = rng.standard_normal((B, H, dv, dk))
+    m_in = rng.standard_normal((B, H, dv))
+    o_ref, S_ref, m_ref = carve_forward(q, k, v, g, bx, w, L, Ud, Uu, state_in=S_in, mean_in=m_in)
+    S, m, acc = S_in.copy(), m_in.copy(), np.zeros((B, H, dv))
+    for t in range(T):
+        o, S, m, acc = carve_step(S, m, acc, t % L, q[:, t], k[:, t], v[:, t], g[:, t], bx[:, t], w[:, t],
+                                  L, Ud, Uu)
+        np.testing.assert_allclose(o, o_ref[:, t], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(S, S_ref, rtol=0, atol=1e-13)
+    tail = T % L
+    if tail == 0:
+        np.testing.assert_allclose(m, m_ref, rtol=0, atol=1e-13)
+    else:
+        np.testing.assert_allclose(acc / tail, m_ref, rtol=0, atol=1e-13)
+
+
+def test_step_rejects_position_outside_chunk():
+    rng = np.random.default_rng(3)
+    q, k, v, g, bx, w, _, _ = rand_inputs(rng, 1, 1, 1, 2, 2)
+    with pytest.raises(ValueError):
+        carve_step(np.zeros((1, 1, 2, 2)), np.zeros((1, 1, 2)), np.zeros((1, 1, 2)), 4,
+                   q[:, 0], k[:, 0], v[:, 0], g[:, 0], bx[:, 0], w[:, 0], 4)
