@@ -260,6 +260,131 @@ def write_mfma_summary(wl, pmc_csv, trace_csv, commands):
     print(open(mfma_file(wl)).read())
 
 
+def decode_bytes(B, H, dk, dv, es, rank=0):
+    """Bytes one decode step must move: read the token's q, k, g, b_x, v, w and
+    the U_b factors, read and write the fp32 state, mean and chunk sum, write o."""
+    return (B * H * ((4 * dk + dv + 1) * es + dv * es) + H * rank * (dk + dv) * es
+            + 2 * B * H * (dv * dk + 2 * dv) * 4)
+
+
+def decode_cpu_baseline(wl, inp, budget_s):
+    """The float64 oracle's decode step, single-threaded, on a bounded number of
+    steps of the same workload. Returns tokens/s (batch rows per second)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import carve_step
+    from chunk_gated_delta_carve_amd.workloads import to_f64
+
+    f = lambda key: to_f64(inp[key], wl.dtype)
+    x = {key: f(key) for key in ("q", "k", "v", "g", "bx", "w")}
+    Ud, Uu = (f("U_down"), f("U_up")) if wl.rank else (None, None)
+    S = np.zeros((wl.B, wl.H, wl.dv, wl.dk))
+    m = np.zeros((wl.B, wl.H, wl.dv))
+    acc = np.zeros_like(m)
+    steps, spent = 0, 0.0
+    with threadpool_limits(1):
+        while spent < budget_s:
+            s = steps % wl.T
+            t0 = time.perf_counter()
+            _, S, m, acc = carve_step(S, m, acc, s % wl.L, *(x[key][:, s] for key in ("q", "k", "v", "g", "bx", "w")),
+                                      wl.L, Ud, Uu)
+            spent += time.perf_counter() - t0
+            steps += 1
+    return {"value": wl.B * steps / spent, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} decode steps of the workload (B={wl.B}, all {wl.H} heads), {spent:.1f} s, one thread"}
+
+
+def bench_decode(args, wl):
+    """Decode steps (carve_recurrent_step), each one token of every (batch,
+    head), cycling through the workload's T tokens with pos = step mod L. A
+    serving loop launches them from a HIP graph: one chunk of L steps is
+    captured once and replayed, so the timed region is whole replays (the
+    step count rounds up to a multiple of L). The same steps launched one call
+    at a time from Python are timed as well (`kernel_ms_eager`): there the
+    per-call host work, not the GPU, sets the pace."""
+    import numpy as np
+    import torch
+
+    from chunk_gated_delta_carve_amd.api import recurrent_step
+    from chunk_gated_delta_carve_amd.workloads import make_inputs, to_torch
+
+    inp = make_inputs(wl)
+    t = {k: to_torch(v, wl.dtype) for k, v in inp.items()}
+    toks = [{k: t[k][:, s].clone() for k in ("q", "k", "v", "g", "bx", "w")} for s in range(wl.T)]
+    ub = (t["U_down"], t["U_up"]) if wl.rank else (None, None)
+    B, H, dk, dv, L = wl.B, wl.H, wl.dk, wl.dv, wl.L
+    S = torch.zeros((B, H, dv, dk), dtype=torch.float32, device="cuda")
+    m = torch.zeros((B, H, dv), dtype=torch.float32, device="cuda")
+    acc = torch.zeros_like(m)
+    o = torch.empty((B, H, dv), dtype=toks[0]["q"].dtype, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        x = toks[i % wl.T]
+        recurrent_step(x["q"], x["k"], x["v"], x["g"], x["bx"], x["w"], S, m, acc, i % L, L, *ub, out=o)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev_start, ev_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev_start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev_end.record(stream)
+    torch.cuda.synchronize()
+    kernel_ms_eager = ev_start.elapsed_time(ev_end) / args.steps
+
+    # one chunk of steps (positions 0 .. L-1) in a graph
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(L):
+                step(i)
+    stream.wait_stream(side)
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, (args.steps + L - 1) // L)
+    t0 = time.perf_counter()
+    ev_start.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    ev_end.record(stream)
+    torch.cuda.synchronize()
+    steps = reps * L
+    ms_per_step = 1e3 * (time.perf_counter() - t0) / steps
+    kernel_ms = ev_start.elapsed_time(ev_end) / steps
+    es = 2 if wl.dtype == "bf16" else 4
+    alg = decode_bytes(B, H, dk, dv, es, wl.rank)
+    achieved = alg / (kernel_ms * 1e-3) / 1e9
+    line = {
+        "metric": "tokens/s of carve_recurrent_step (decode), one token per (batch, head) per step",
+        "value": B / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded; distributions as for carve_chunk_fwd)",
+        "config": {"workload": f"carve_recurrent_step B{B} H{H} dk{dk} dv{dv} L{L} {wl.dtype}, "
+                               + (f"content projection rank {wl.rank}" if wl.rank else "no content projection"),
+                   "B": B, "H": H, "dk": dk, "dv": dv, "L": L, "rank": wl.rank},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "carve_step_kernel",
+                     "kernel_ms": kernel_ms, "algorithmic_bytes_per_launch": alg,
+                     "kernel_ms_eager": kernel_ms_eager},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = decode_cpu_baseline(wl, inp, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -267,7 +392,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="init_equiv",
-                    help="workload to time (default: the B4 H12 T2048 d64 L64 bf16 shape)")
+                    help="workload to time (default: the B4 H12 T2048 d64 L64 bf16 shape; "
+                         "`decode` times the one-token step instead)")
     ap.add_argument("--L", type=int, default=None, help="override the chunk length")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU work budget of the oracle baseline sample")
@@ -294,6 +420,9 @@ def main():
     wl = WORKLOADS[args.workload]
     if args.L is not None:
         wl = wl.with_(L=args.L)
+    if args.workload == "decode":
+        bench_decode(args, wl)
+        return
     if args.write_traffic_summary:
         write_traffic_summary(wl, *args.write_traffic_summary, args.commands)
         return

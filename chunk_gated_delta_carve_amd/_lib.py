@@ -8,7 +8,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcarve.so
 
 CARVE_OK, CARVE_EINVAL, CARVE_EUNSUPPORTED, CARVE_EALIGN, CARVE_EWORKSPACE, CARVE_EHIP = range(6)
 CARVE_F32, CARVE_BF16 = 0, 1
-EXPORTED = ("carve_recurrent_ref_shapes", "carve_chunk_fwd", "carve_error_string")
+EXPORTED = ("carve_recurrent_ref_shapes", "carve_chunk_fwd", "carve_recurrent_step", "carve_error_string")
 
 
 class CarveConfig(ctypes.Structure):
@@ -44,6 +44,8 @@ def lib() -> ctypes.CDLL:
         L.carve_recurrent_ref_shapes.restype = ctypes.c_int
         L.carve_chunk_fwd.argtypes = [ctypes.POINTER(CarveConfig)] + [vp] * 14 + [ctypes.c_size_t, vp]
         L.carve_chunk_fwd.restype = ctypes.c_int
+        L.carve_recurrent_step.argtypes = [ctypes.POINTER(CarveConfig), ctypes.c_int32] + [vp] * 13
+        L.carve_recurrent_step.restype = ctypes.c_int
         L.carve_error_string.argtypes = [ctypes.c_int]
         L.carve_error_string.restype = ctypes.c_char_p
         _lib = L

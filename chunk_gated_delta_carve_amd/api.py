@@ -88,3 +88,42 @@ def chunk_fwd(q, k, v, g, bx, w, L=64, ub_down=None, ub_up=None, state_in=None, 
     if return_state:
         return o, state_out, mean_out
     return o
+
+
+def recurrent_step(q, k, v, g, bx, w, state, mean_prev, chunk_acc, pos, L, ub_down=None, ub_up=None,
+                   out=None, stream=None):
+    """One decode step for every (batch, head). Shapes: q, k, g, bx [B,H,dk];
+    v [B,H,dv]; w [B,H]; state [B,H,dv,dk] fp32, mean_prev and chunk_acc
+    [B,H,dv] fp32 (all three updated in place); pos is the token's position
+    within its chunk of L tokens. Returns o [B,H,dv]."""
+    if q.device.type != "cuda":
+        raise ValueError("recurrent_step runs on the GPU only; move the inputs to a cuda device")
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dt, dev = q.dtype, q.device
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    if (ub_down is None) != (ub_up is None):
+        raise ValueError("ub_down and ub_up come together")
+    rank = 0 if ub_down is None else int(ub_down.shape[1])
+    for name, t, shp in (("q", q, (B, H, dk)), ("k", k, (B, H, dk)), ("v", v, (B, H, dv)),
+                         ("g", g, (B, H, dk)), ("bx", bx, (B, H, dk)), ("w", w, (B, H))):
+        _need(t, name, shp, dt, dev)
+    if rank:
+        _need(ub_down, "ub_down", (H, rank, dv), dt, dev)
+        _need(ub_up, "ub_up", (H, dk, rank), dt, dev)
+    for name, t, shp in (("state", state, (B, H, dv, dk)), ("mean_prev", mean_prev, (B, H, dv)),
+                         ("chunk_acc", chunk_acc, (B, H, dv))):
+        if t is None:
+            raise ValueError(f"{name} is required")
+        _need(t, name, shp, torch.float32, dev)
+    o = out if out is not None else torch.empty((B, H, dv), dtype=dt, device=dev)
+    _need(o, "out", (B, H, dv), dt, dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    code = _lib.lib().carve_recurrent_step(
+        ctypes.byref(make_config(B, H, 1, dk, dv, L, rank, dt)), ctypes.c_int32(pos),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(bx), _ptr(w), _ptr(ub_down), _ptr(ub_up),
+        _ptr(state), _ptr(mean_prev), _ptr(chunk_acc), _ptr(o), ctypes.c_void_p(stream))
+    _lib.check(code)
+    return o

@@ -3,11 +3,13 @@
 // (and unit-testable) on a machine without a GPU.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdio>
 #include <cstring>
 
 #include "carve.h"
 #include "kernels/kernels.h"
+#include "kernels/step.h"
 
 namespace {
 
@@ -65,10 +67,27 @@ int64_t parallel_workspace_bytes(const carve_config* c) {
   return (int64_t)c->B * c->H * nblk * img;
 }
 
+// Raises a kernel's dynamic-LDS limit to `bytes`. The attribute only ever
+// needs raising, so the largest value set so far is kept per kernel and device
+// and the driver is called only to go beyond it: later calls (and launches
+// inside a graph capture) make no attribute call at all.
+constexpr int kMaxDevices = 64;
 template <typename K>
 hipError_t set_lds(K kern, int bytes) {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  static std::atomic<int> set_bytes[kMaxDevices];
+  auto raise = [&] {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  };
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return raise();
+  int cur = set_bytes[dev].load(std::memory_order_acquire);
+  if (cur >= bytes) return hipSuccess;
+  const hipError_t e = raise();
+  if (e != hipSuccess) return e;
+  while (cur < bytes && !set_bytes[dev].compare_exchange_weak(cur, bytes, std::memory_order_acq_rel)) {
+  }
+  return hipSuccess;
 }
 
 template <typename E, int D, int BL>
@@ -112,6 +131,16 @@ hipError_t dispatch_block(const carve::FwdArgs& a, int bl, hipStream_t s) {
       if constexpr (sizeof(E) == 4 && D == 128) return hipErrorInvalidValue;
       else return launch_serial<E, D, 64>(a, s);
   }
+}
+
+template <typename E, int D>
+hipError_t launch_step(const carve::StepArgs& a, hipStream_t s) {
+  auto kern = carve::carve_step_kernel<E, D>;
+  const int lds = 2 * a.rank * D * (int)sizeof(E);   // the head's U_down and U_up
+  hipError_t e = set_lds(kern, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(a.B * a.H), dim3(4 * D), lds, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -179,6 +208,59 @@ extern "C" int carve_chunk_fwd(const carve_config* cfg,
     e = cfg->dk == 64 ? dispatch_block<carve::bf16, 64>(a, bl, s) : dispatch_block<carve::bf16, 128>(a, bl, s);
   else
     e = cfg->dk == 64 ? dispatch_block<float, 64>(a, bl, s) : dispatch_block<float, 128>(a, bl, s);
+  if (e != hipSuccess) {
+    std::snprintf(g_hip_msg, sizeof(g_hip_msg), "%s", hipGetErrorString(e));
+    return CARVE_EHIP;
+  }
+  return CARVE_OK;
+}
+
+extern "C" int carve_recurrent_step(const carve_config* cfg, int32_t pos,
+                                    const void* q, const void* k, const void* v,
+                                    const void* g, const void* bx, const void* w,
+                                    const void* ub_down, const void* ub_up,
+                                    float* state, float* mean_prev, float* chunk_acc,
+                                    void* o, void* stream) {
+  carve_shapes sh;
+  int st = carve_recurrent_ref_shapes(cfg, &sh);
+  if (st != CARVE_OK) return st;
+  if (cfg->T != 1 || pos < 0 || pos >= cfg->L) return CARVE_EINVAL;
+  const bool heads = (int64_t)cfg->B * cfg->H > 0;
+  if (heads && (!q || !k || !v || !g || !bx || !w || !o || !state || !mean_prev || !chunk_acc))
+    return CARVE_EINVAL;
+  const bool content = cfg->rank > 0;
+  if (content && heads && (!ub_down || !ub_up)) return CARVE_EINVAL;
+  const void* ptrs[] = {q, k, v, g, bx, w, content ? ub_down : nullptr, content ? ub_up : nullptr,
+                        state, mean_prev, chunk_acc, o};
+  for (const void* p : ptrs)
+    if (misaligned(p)) return CARVE_EALIGN;
+  const size_t es = elem_bytes(cfg->dtype);
+  const struct { const void* p; size_t n; } ins[] = {
+      {q, (size_t)sh.q * es}, {k, (size_t)sh.k * es}, {v, (size_t)sh.v * es},
+      {g, (size_t)sh.g * es}, {bx, (size_t)sh.bx * es}, {w, (size_t)sh.w * es},
+      {content ? ub_down : nullptr, (size_t)sh.ub_down * es}, {content ? ub_up : nullptr, (size_t)sh.ub_up * es}};
+  const struct { const void* p; size_t n; } outs[] = {
+      {o, (size_t)sh.o * es}, {state, (size_t)sh.state * 4}, {mean_prev, (size_t)sh.mean * 4},
+      {chunk_acc, (size_t)sh.mean * 4}};
+  for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+    for (const auto& in : ins)
+      if (overlaps(outs[i].p, outs[i].n, in.p, in.n)) return CARVE_EINVAL;
+    for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+      if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return CARVE_EINVAL;
+  }
+  if (!heads) return CARVE_OK;
+
+  carve::StepArgs a;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.bx = bx; a.w = w;
+  a.ub_down = ub_down; a.ub_up = ub_up;
+  a.state = state; a.mean_prev = mean_prev; a.chunk_acc = chunk_acc; a.o = o;
+  a.B = cfg->B; a.H = cfg->H; a.L = cfg->L; a.rank = cfg->rank; a.pos = pos;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (cfg->dtype == CARVE_BF16)
+    e = cfg->dk == 64 ? launch_step<carve::bf16, 64>(a, s) : launch_step<carve::bf16, 128>(a, s);
+  else
+    e = cfg->dk == 64 ? launch_step<float, 64>(a, s) : launch_step<float, 128>(a, s);
   if (e != hipSuccess) {
     std::snprintf(g_hip_msg, sizeof(g_hip_msg), "%s", hipGetErrorString(e));
     return CARVE_EHIP;

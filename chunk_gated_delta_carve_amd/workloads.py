@@ -73,6 +73,9 @@ WORKLOADS = {
     # fp32 case whose content projection is large enough to move the output
     # far beyond the fp32 tolerance, so parity proves the content path runs
     "content_test": Workload("content_test", 1, 2, 1024, 64, 64, 64, "f32", 16, 1.0, 1006),
+    # decode steps: one token of 64 x 12 (batch, head) pairs per step; T is the
+    # number of distinct tokens drawn (one chunk), cycled by the benchmark
+    "decode": Workload("decode", 64, 12, 64, 64, 64, 64, "bf16", 16, 0.05, 1007),
 }
 LSWEEP_CHUNKS = (16, 32, 64, 128)
 

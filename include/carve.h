@@ -31,7 +31,8 @@
  *   - Tensors are dense, row-major, 16-byte aligned, no strides.
  *   - Every argument check runs before the first HIP call, so invalid
  *     arguments are reported (and testable) without a GPU.
- *   - The library keeps no state; concurrent calls need distinct outputs.
+ *   - The library keeps no state beyond a per-device record of the kernels'
+ *     LDS limits it has raised; concurrent calls need distinct outputs.
  *   - Errors are returned as a carve_status code; nothing is thrown.
  */
 #ifndef CARVE_H
@@ -107,6 +108,38 @@ int carve_chunk_fwd(const carve_config* cfg,
                     const float* state_in, const float* mean_in,
                     void* o, float* state_out, float* mean_out,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* One decode step: the token recurrence of the header comment for a single
+ * token of every (batch, head), for serving loops that produce one token at a
+ * time. The caller carries three fp32 tensors from step to step:
+ *   state      [B,H,dv,dk]  S before this token; updated in place
+ *   mean_prev  [B,H,dv]     the mean of the previous chunk's outputs, which
+ *                           gates this token (section 2.1: one chunk stale);
+ *                           replaced by this chunk's mean at its last position
+ *   chunk_acc  [B,H,dv]     sum of this chunk's outputs before this token; the
+ *                           token's output is added, and it restarts from zero
+ *                           after the chunk's last position
+ * and `pos`, the token's position within its chunk (0 <= pos < L). Stepping
+ * tokens t = 0, 1, ... with pos = t mod L from (state_in, mean_in, zeros)
+ * gives carve_chunk_fwd's outputs and final state; after a whole chunk,
+ * mean_prev holds its mean (for a partial last chunk, carve_chunk_fwd's
+ * mean_out is chunk_acc divided by the tokens it holds).
+ *   cfg        B, H, dk, dv, L, rank, dtype as for carve_chunk_fwd; T must be 1
+ *   q, k, g, bx [B,H,dk] dtype; v [B,H,dv] dtype; w [B,H] dtype: this token
+ *              ([B,1,H,.] in the layout of carve_chunk_fwd)
+ *   ub_down, ub_up as for carve_chunk_fwd
+ *   o          [B,H,dv] dtype: this token's output
+ * state, mean_prev and chunk_acc are required (when B H > 0); none of o,
+ * state, mean_prev and chunk_acc may overlap each other or an input. Returns
+ * CARVE_EINVAL for T != 1, pos outside [0, L), a missing pointer or an
+ * overlap, and the status codes of carve_chunk_fwd otherwise. Needs no
+ * workspace. */
+int carve_recurrent_step(const carve_config* cfg, int32_t pos,
+                         const void* q, const void* k, const void* v,
+                         const void* g, const void* bx, const void* w,
+                         const void* ub_down, const void* ub_up,
+                         float* state, float* mean_prev, float* chunk_acc,
+                         void* o, void* stream);
 
 /* Static text for a status code. For CARVE_EHIP it returns the HIP error text
  * of the most recent failure on the calling thread. */

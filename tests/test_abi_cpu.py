@@ -129,3 +129,32 @@ def test_error_strings(L):
     for code in range(6):
         assert len(_lib.error_string(code)) > 0
     assert "unknown" in _lib.error_string(99)
+
+
+def call_step(L, c, pos=0, **ptrs):
+    names = ["q", "k", "v", "g", "bx", "w", "ub_down", "ub_up", "state", "mean_prev", "chunk_acc", "o"]
+    step = 1 << 24
+    base = {n: FAKE + i * step for i, n in enumerate(names)}
+    base.update(ptrs)
+    args = [ctypes.c_void_p(base[n]) if base[n] is not None else None for n in names]
+    return L.carve_recurrent_step(ctypes.byref(c) if c is not None else None, ctypes.c_int32(pos), *args, None)
+
+
+def test_step_argument_errors(L):
+    c = cfg(T=1)
+    assert call_step(L, None) == _lib.CARVE_EINVAL
+    assert call_step(L, cfg(T=2)) == _lib.CARVE_EINVAL               # one token per call
+    assert call_step(L, c, pos=-1) == _lib.CARVE_EINVAL
+    assert call_step(L, c, pos=64) == _lib.CARVE_EINVAL               # pos < L
+    assert call_step(L, cfg(T=1, L=16), pos=16) == _lib.CARVE_EINVAL
+    for n in ("q", "w", "o", "state", "mean_prev", "chunk_acc", "ub_up"):
+        assert call_step(L, c, **{n: None}) == _lib.CARVE_EINVAL, n
+    assert call_step(L, c, v=FAKE + 2 * (1 << 24) + 8) == _lib.CARVE_EALIGN
+    assert call_step(L, c, chunk_acc=FAKE + 4) == _lib.CARVE_EALIGN
+    assert call_step(L, c, o=FAKE + 64) == _lib.CARVE_EINVAL          # o overlaps q
+    assert call_step(L, c, state=FAKE + 3 * (1 << 24)) == _lib.CARVE_EINVAL    # state overlaps g
+    assert call_step(L, c, mean_prev=FAKE + 8 * (1 << 24) + 16) == _lib.CARVE_EINVAL   # inside state
+    assert call_step(L, cfg(T=1, dk=96, dv=96)) == _lib.CARVE_EUNSUPPORTED
+    # rank 0 needs no projection factors; nothing to do without heads
+    assert call_step(L, cfg(T=1, rank=0, B=0), ub_down=None, ub_up=None) == _lib.CARVE_OK
+    assert call_step(L, cfg(T=1, B=0)) == _lib.CARVE_OK
