@@ -119,10 +119,13 @@ def _sigmoid(x: np.ndarray) -> np.ndarray:
     return 0.5 * (1.0 + np.tanh(0.5 * x))
 
 
-def make_inputs(wl: Workload) -> dict:
+def make_inputs(wl: Workload, decay_logits: bool = False) -> dict:
     """Draw one workload's inputs. Returns storage arrays (float32, or uint16 bf16 bits).
 
-    Keys: q, k, v, g, bx, w, and U_down, U_up when wl.rank > 0.
+    Keys: q, k, v, g, bx, w, and U_down, U_up when wl.rank > 0. With
+    decay_logits, g holds the raw N(0,1) draws themselves (the decay logits,
+    before the activation) instead of -softplus of them; every other tensor
+    and the draw order are unchanged.
     """
     rng = np.random.Generator(np.random.PCG64(wl.seed))
     B, T, H, dk, dv = wl.B, wl.T, wl.H, wl.dk, wl.dv
@@ -137,7 +140,9 @@ def make_inputs(wl: Workload) -> dict:
         out[name] = _cast(x, wl.dtype)
         del x
     out["v"] = _cast(draw((B, T, H, dv)), wl.dtype)
-    out["g"] = _cast(-_softplus(draw((B, T, H, dk))), wl.dtype)
+    a = draw((B, T, H, dk))
+    out["g"] = _cast(a if decay_logits else -_softplus(a), wl.dtype)
+    del a
     out["bx"] = _cast(draw((B, T, H, dk)), wl.dtype)
     out["w"] = _cast(_sigmoid(draw((B, T, H))), wl.dtype)
     if wl.rank > 0:

@@ -23,6 +23,8 @@ Recurrent with Value Efficiency for Chunk-Parallel Linear Attention"):
        broadcast over all value channels.
   [S5] same, §2.3 "Key-Axis Decay und Fusion": exponential decay on the key
        axis only.
+  [S5'] same, §2.3: the decay activation may be applied inside the kernel
+       ("gate-in-kernel"), so the activated tensor is never stored.
   [S6] same, closing "Limitations" paragraph: sequences shorter than two
        chunks receive no content signal.
   [S7] aisea.builders paper card, "Key figure": the chunk mean of the previous
@@ -39,12 +41,15 @@ Readings where the pages leave a step open (each listed in the design notes):
   R5  No 1/sqrt(d_k) scale on q.
   R6  T need not be a multiple of L: the last chunk may be partial, and its
       mean is taken over the tokens it holds (it can only reach mean_out).
+  R9  The decay activation (not named on the pages) is g = -softplus(a) of a
+      raw decay logit a: it maps every real a to a log-decay below zero, so
+      exp(g) = sigmoid(-a) lies in (0, 1).
 """
 from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["sigmoid", "carve_forward", "carve_step", "content_gate_bias"]
+__all__ = ["sigmoid", "decay_from_logits", "carve_forward", "carve_step", "content_gate_bias"]
 
 
 def sigmoid(x: np.ndarray) -> np.ndarray:
@@ -52,6 +57,14 @@ def sigmoid(x: np.ndarray) -> np.ndarray:
     x = np.asarray(x, dtype=np.float64)
     e = np.exp(-np.abs(x))
     return np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def decay_from_logits(a: np.ndarray) -> np.ndarray:
+    """Log-decay g = -softplus(a) = -log(1 + e^a) from raw decay logits a, in
+    float64 ([S5], [S5'], reading R9). Evaluated as -(max(a, 0) + log1p(e^{-|a|}))
+    so no intermediate overflows and tiny decays keep their relative accuracy."""
+    a = np.asarray(a, dtype=np.float64)
+    return -(np.maximum(a, 0.0) + np.log1p(np.exp(-np.abs(a))))
 
 
 def content_gate_bias(m: np.ndarray, U_down: np.ndarray | None,

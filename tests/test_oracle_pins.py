@@ -13,7 +13,7 @@ import os
 import numpy as np
 import pytest
 
-from oracle import carve_forward, carve_step, sigmoid
+from oracle import carve_forward, carve_step, decay_from_logits, sigmoid
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -392,3 +392,46 @@ def test_step_rejects_position_outside_chunk():
     with pytest.raises(ValueError):
         carve_step(np.zeros((1, 1, 2, 2)), np.zeros((1, 1, 2)), np.zeros((1, 1, 2)), 4,
                    q[:, 0], k[:, 0], v[:, 0], g[:, 0], bx[:, 0], w[:, 0], 4)
+
+
+# ---------------------------------------------------------------- decay activation
+
+def test_decay_from_logits_closed_forms():
+    """g = -softplus(a): g(0) = -ln 2; a = ln 3 gives exp(g) = 1/4 exactly in
+    closed form; exp(g(a)) = 1 / (1 + e^a), so the decay factor falls as the
+    logit rises; g(a) - g(-a) = -a; and d g / d a = -1 / (1 + e^{-a})."""
+    assert decay_from_logits(0.0) == pytest.approx(-np.log(2.0), rel=1e-15)
+    assert np.exp(decay_from_logits(np.log(3.0))) == pytest.approx(0.25, rel=1e-15)
+    a = np.linspace(-30.0, 30.0, 121)
+    np.testing.assert_allclose(np.exp(decay_from_logits(a)), 1.0 / (1.0 + np.exp(a)), rtol=1e-13, atol=0)
+    np.testing.assert_allclose(decay_from_logits(a) - decay_from_logits(-a), -a, rtol=0, atol=1e-13)
+    h = 1e-6
+    fd = (decay_from_logits(a + h) - decay_from_logits(a - h)) / (2 * h)
+    np.testing.assert_allclose(fd, -1.0 / (1.0 + np.exp(-a)), rtol=0, atol=1e-8)
+    assert np.all(decay_from_logits(a) < 0)
+
+
+def test_decay_from_logits_extremes():
+    """Neither end overflows or loses its leading term: g(800) = -800 (the
+    decay is e^-800), and g(-50) = -e^-50 (1 - e^-50 / 2 + ...), a decay within
+    1e-22 of one that must not round to zero."""
+    assert decay_from_logits(800.0) == -800.0
+    assert decay_from_logits(1e4) == -1e4
+    assert decay_from_logits(-50.0) == pytest.approx(-np.exp(-50.0), rel=1e-15, abs=0)
+    assert decay_from_logits(-700.0) == pytest.approx(-np.exp(-700.0), rel=1e-15, abs=0)   # e^-700 is still normal
+
+
+def test_decay_logits_in_the_layer():
+    """The activation composed with the layer: logits of +1e4 are the hard
+    decay (every token wipes the state), and logits of -50 leave the state
+    undecayed to within 1e-21, so the layer is the ungated rule on those."""
+    rng = np.random.default_rng(17)
+    B, T, H, dk, dv = 1, 8, 2, 6, 4
+    q, k, v, _, bx, w, _, _ = rand_inputs(rng, B, T, H, dk, dv)
+    o_hard, _, _ = carve_forward(q, k, v, decay_from_logits(np.full_like(k, 1e4)), bx, w, 4)
+    ref = w[:, :-1, :, None] * v[:, :-1] * np.sum(k[:, :-1] * q[:, 1:], axis=-1, keepdims=True)
+    np.testing.assert_allclose(o_hard[:, 1:], ref, atol=1e-13)
+    o_none, S_none, _ = carve_forward(q, k, v, decay_from_logits(np.full_like(k, -50.0)), bx, w, 4)
+    o_zero, S_zero, _ = carve_forward(q, k, v, np.zeros_like(k), bx, w, 4)
+    np.testing.assert_allclose(o_none, o_zero, atol=1e-18)
+    np.testing.assert_allclose(S_none, S_zero, atol=1e-18)
