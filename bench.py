@@ -308,7 +308,8 @@ def bench_decode(args, wl):
     from chunk_gated_delta_carve_amd.api import recurrent_step
     from chunk_gated_delta_carve_amd.workloads import make_inputs, to_torch
 
-    inp = make_inputs(wl)
+    logits = args.decay_logits
+    inp = make_inputs(wl, decay_logits=logits)
     t = {k: to_torch(v, wl.dtype) for k, v in inp.items()}
     toks = [{k: t[k][:, s].clone() for k in ("q", "k", "v", "g", "bx", "w")} for s in range(wl.T)]
     ub = (t["U_down"], t["U_up"]) if wl.rank else (None, None)
@@ -321,7 +322,8 @@ def bench_decode(args, wl):
 
     def step(i):
         x = toks[i % wl.T]
-        recurrent_step(x["q"], x["k"], x["v"], x["g"], x["bx"], x["w"], S, m, acc, i % L, L, *ub, out=o)
+        recurrent_step(x["q"], x["k"], x["v"], x["g"], x["bx"], x["w"], S, m, acc, i % L, L, *ub, out=o,
+                       decay_logits=logits)
 
     for i in range(args.warmup):
         step(i)
@@ -374,13 +376,14 @@ def bench_decode(args, wl):
         "data": "synthetic (seeded; distributions as for carve_chunk_fwd)",
         "config": {"workload": f"carve_recurrent_step B{B} H{H} dk{dk} dv{dv} L{L} {wl.dtype}, "
                                + (f"content projection rank {wl.rank}" if wl.rank else "no content projection"),
-                   "B": B, "H": H, "dk": dk, "dv": dv, "L": L, "rank": wl.rank},
+                   "B": B, "H": H, "dk": dk, "dv": dv, "L": L, "rank": wl.rank,
+                   "decay_input": "raw logits, -softplus in-kernel" if logits else "log-decay g"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "carve_step_kernel",
                      "kernel_ms": kernel_ms, "algorithmic_bytes_per_launch": alg,
                      "kernel_ms_eager": kernel_ms_eager},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not logits:
         line["cpu_baseline"] = decode_cpu_baseline(wl, inp, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
@@ -395,6 +398,9 @@ def main():
                     help="workload to time (default: the B4 H12 T2048 d64 L64 bf16 shape; "
                          "`decode` times the one-token step instead)")
     ap.add_argument("--L", type=int, default=None, help="override the chunk length")
+    ap.add_argument("--decay-logits", action="store_true",
+                    help="pass raw decay logits and let the kernels form g = -softplus(.) (CARVE_DECAY_LOGITS); "
+                         "also times the unfused alternative (a torch softplus pass, then the plain call)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU work budget of the oracle baseline sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -429,7 +435,8 @@ def main():
     if args.write_mfma_summary:
         write_mfma_summary(wl, *args.write_mfma_summary, args.commands)
         return
-    inp = make_inputs(wl)
+    logits = args.decay_logits
+    inp = make_inputs(wl, decay_logits=logits)
     t = {k: to_torch(v, wl.dtype) for k, v in inp.items()}
     B, T, H, dk, dv, L, rank = wl.B, wl.T, wl.H, wl.dk, wl.dv, wl.L, wl.rank
     tdtype = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
@@ -443,6 +450,14 @@ def main():
 
     def step():
         return chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["bx"], t["w"], L=L, ub_down=ub[0], ub_up=ub[1],
+                         return_state=True, out=o, workspace=ws, decay_logits=logits)
+
+    g_buf = torch.empty_like(t["g"])
+
+    def unfused_step():
+        # what a caller without the fused activation runs: materialise g, then the plain call
+        torch.neg(torch.nn.functional.softplus(t["g"]), out=g_buf)
+        return chunk_fwd(t["q"], t["k"], t["v"], g_buf, t["bx"], t["w"], L=L, ub_down=ub[0], ub_up=ub[1],
                          return_state=True, out=o, workspace=ws)
 
     if args.calibrate_copy:
@@ -509,6 +524,18 @@ def main():
         cold.append(s.elapsed_time(e))
     del flush
 
+    unfused_ms = None
+    if logits:
+        for _ in range(3):
+            unfused_step()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        for _ in range(args.steps):
+            unfused_step()
+        e.record(stream)
+        torch.cuda.synchronize()
+        unfused_ms = s.elapsed_time(e) / args.steps
+
     alg = algorithmic_bytes(B, T, H, dk, dv, es, rank)
     achieved = alg / (avg_kernel_ms * 1e-3) / 1e9
     flops = algorithmic_flops(B, T, H, dk, dv, L, rank)
@@ -532,11 +559,15 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": wl.dtype,
-        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), g=-softplus(N(0,1)), bx N(0,1), "
-                "w=sigmoid(N(0,1))" + (f", U_b factors N(0,{wl.ub_std})" if rank else "") + ")",
-        "config": {"workload": workload, "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "L": L, "rank": rank},
+        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), "
+                + ("g = raw decay logits N(0,1), activated in-kernel" if logits else "g=-softplus(N(0,1))")
+                + ", bx N(0,1), w=sigmoid(N(0,1))" + (f", U_b factors N(0,{wl.ub_std})" if rank else "") + ")",
+        "config": {"workload": workload, "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "L": L, "rank": rank,
+                   "decay_input": "raw logits, -softplus in-kernel" if logits else "log-decay g"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(wl),
+                     "frac": achieved / HBM_PEAK_GBS,
+                     # the committed counter summaries are of the plain-g launch
+                     "traffic": None if logits else measured_traffic(wl),
                      "kernel": kernels, "kernel_ms": avg_kernel_ms,
                      "algorithmic_bytes_per_launch": alg, "kernel_ms_cold_cache": float(np.median(cold)),
                      "kernel_ms_single_median": float(np.median(single)),
@@ -544,9 +575,12 @@ def main():
         # the matrix-core roofline of the same call: not the bound (the path's
         # FLOP per byte is far below the MFMA/HBM ridge), reported beside it
         "mfma": {"achieved": tflops, "peak": mfma_peak, "unit": "TFLOP/s", "frac": tflops / mfma_peak,
-                 "algorithmic_flops_per_launch": flops, "counters": measured_mfma(wl)},
+                 "algorithmic_flops_per_launch": flops, "counters": None if logits else measured_mfma(wl)},
     }
-    if not args.no_cpu_baseline:
+    if logits:
+        line["unfused"] = {"kernel_ms": unfused_ms, "what": "torch softplus + neg into a g tensor, then the "
+                           "plain call (the g round trip through HBM that the fused activation avoids)"}
+    if not args.no_cpu_baseline and not logits:
         line["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 

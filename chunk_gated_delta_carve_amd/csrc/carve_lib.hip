@@ -27,6 +27,7 @@ int check_config(const carve_config* c) {
   if (!valid_width(c->dk) || !valid_width(c->dv) || c->dk != c->dv) return CARVE_EUNSUPPORTED;
   if (!valid_chunk(c->L)) return CARVE_EUNSUPPORTED;
   if (c->rank > 64) return CARVE_EUNSUPPORTED;
+  if (c->flags & ~CARVE_DECAY_LOGITS) return CARVE_EINVAL;
   // offsets are computed in 64-bit, grids in 32-bit (the state pass launches
   // 8 (B H / 8 rounded up) (d_v / 16) workgroups)
   if ((int64_t)c->B * c->H > 0x7fffffffLL / 8 - 8) return CARVE_EUNSUPPORTED;
@@ -90,24 +91,24 @@ hipError_t set_lds(K kern, int bytes) {
   return hipSuccess;
 }
 
-template <typename E, int D, int BL>
+template <typename E, int D, int BL, bool LG>
 hipError_t launch_serial(const carve::FwdArgs& a, hipStream_t s) {
   using LY = carve::BlockLayout<E, D, D, BL, carve::serial_waves<D, BL>()>;
-  auto kern = carve::carve_chunk_serial_kernel<E, D, D, BL>;
+  auto kern = carve::carve_chunk_serial_kernel<E, D, D, BL, LG>;
   hipError_t e = set_lds(kern, LY::serial_bytes);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(a.B * a.H), dim3(LY::NT), LY::serial_bytes, s, a);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool LG>
 hipError_t launch_parallel(const carve::FwdArgs& a, hipStream_t s) {
   using E = carve::bf16;
   constexpr int BL = kParallelBlock;
   using LY = carve::BlockLayout<E, D, D, BL>;                        // state pass, images
   using LI = carve::BlockLayout<E, D, D, BL, carve::kIntraWaves>;    // intra kernel
   const int nblk = (a.T + BL - 1) / BL;
-  auto intra = carve::carve_intra_kernel<E, D, D, BL>;
+  auto intra = carve::carve_intra_kernel<E, D, D, BL, LG>;
   auto state = carve::carve_state_kernel<E, D, D, BL>;
   hipError_t e = set_lds(intra, LI::intra_bytes);
   if (e != hipSuccess) return e;
@@ -120,17 +121,27 @@ hipError_t launch_parallel(const carve::FwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename E, int D>
+template <typename E, int D, bool LG>
 hipError_t dispatch_block(const carve::FwdArgs& a, int bl, hipStream_t s) {
   switch (bl) {
-    case 16: return launch_serial<E, D, 16>(a, s);
+    case 16: return launch_serial<E, D, 16, LG>(a, s);
     case 32:
       if constexpr (sizeof(E) == 4 && D == 128) return hipErrorInvalidValue;
-      else return launch_serial<E, D, 32>(a, s);
+      else return launch_serial<E, D, 32, LG>(a, s);
     default:
       if constexpr (sizeof(E) == 4 && D == 128) return hipErrorInvalidValue;
-      else return launch_serial<E, D, 64>(a, s);
+      else return launch_serial<E, D, 64, LG>(a, s);
   }
+}
+
+// dtype, width and schedule dispatch of the forward pass for one decay mode
+template <bool LG>
+hipError_t dispatch_fwd(const carve_config* cfg, const carve::FwdArgs& a, hipStream_t s) {
+  const int bl = serial_block(cfg);
+  if (chunk_parallel(cfg)) return cfg->dk == 64 ? launch_parallel<64, LG>(a, s) : launch_parallel<128, LG>(a, s);
+  if (cfg->dtype == CARVE_BF16)
+    return cfg->dk == 64 ? dispatch_block<carve::bf16, 64, LG>(a, bl, s) : dispatch_block<carve::bf16, 128, LG>(a, bl, s);
+  return cfg->dk == 64 ? dispatch_block<float, 64, LG>(a, bl, s) : dispatch_block<float, 128, LG>(a, bl, s);
 }
 
 template <typename E, int D>
@@ -200,14 +211,7 @@ extern "C" int carve_chunk_fwd(const carve_config* cfg,
   a.B = cfg->B; a.H = cfg->H; a.T = cfg->T; a.L = cfg->L; a.rank = cfg->rank;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int bl = serial_block(cfg);
-  hipError_t e;
-  if (chunk_parallel(cfg))
-    e = cfg->dk == 64 ? launch_parallel<64>(a, s) : launch_parallel<128>(a, s);
-  else if (cfg->dtype == CARVE_BF16)
-    e = cfg->dk == 64 ? dispatch_block<carve::bf16, 64>(a, bl, s) : dispatch_block<carve::bf16, 128>(a, bl, s);
-  else
-    e = cfg->dk == 64 ? dispatch_block<float, 64>(a, bl, s) : dispatch_block<float, 128>(a, bl, s);
+  const hipError_t e = (cfg->flags & CARVE_DECAY_LOGITS) ? dispatch_fwd<true>(cfg, a, s) : dispatch_fwd<false>(cfg, a, s);
   if (e != hipSuccess) {
     std::snprintf(g_hip_msg, sizeof(g_hip_msg), "%s", hipGetErrorString(e));
     return CARVE_EHIP;
@@ -255,6 +259,7 @@ extern "C" int carve_recurrent_step(const carve_config* cfg, int32_t pos,
   a.ub_down = ub_down; a.ub_up = ub_up;
   a.state = state; a.mean_prev = mean_prev; a.chunk_acc = chunk_acc; a.o = o;
   a.B = cfg->B; a.H = cfg->H; a.L = cfg->L; a.rank = cfg->rank; a.pos = pos;
+  a.logits = (cfg->flags & CARVE_DECAY_LOGITS) != 0;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (cfg->dtype == CARVE_BF16)
@@ -271,7 +276,7 @@ extern "C" int carve_recurrent_step(const carve_config* cfg, int32_t pos,
 extern "C" const char* carve_error_string(int code) {
   switch (code) {
     case CARVE_OK: return "ok";
-    case CARVE_EINVAL: return "invalid argument (NULL required pointer, negative size, bad rank or overlapping output)";
+    case CARVE_EINVAL: return "invalid argument (NULL required pointer, negative size, unknown flag or overlapping output)";
     case CARVE_EUNSUPPORTED: return "unsupported configuration (dk/dv in {64,128} with dk == dv, L in {16,32,64,128}, rank <= 64, sizes within 32-bit indexing)";
     case CARVE_EALIGN: return "a tensor pointer is not 16-byte aligned";
     case CARVE_EWORKSPACE: return "workspace smaller than carve_recurrent_ref_shapes() requires";

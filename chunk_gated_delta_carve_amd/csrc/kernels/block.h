@@ -4,7 +4,8 @@
 // With S the state at the block start, G_r the inclusive cumulative log-decay
 // inside the block (G_{-1} = 0), b_r = sigmoid(bx_r + z) and z = U_b m_{c-1}
 // (gist.science technical summary, §2.1 "Content-Aware Erase via Output
-// Reuse"; §2.2 scalar write gate; §2.3 key-axis decay):
+// Reuse"; §2.2 scalar write gate; §2.3 key-axis decay, whose activation
+// g = -softplus(a) of raw logits a the kLogits variants apply as they read g):
 //   A_rj  = sum_d b_r k_r k_j e^{G_r - G_j}          (j < r)
 //   P_rj  = sum_d q_r k_j e^{G_{r-1} - G_j}          (j < r)
 //   [W | U] = (I + A)^{-1} [b k e^{G_r} | w v]       (WY form)
@@ -337,8 +338,9 @@ struct Block {
   // the Qx/Ky region is free again. Returns true if a sub-block's decay is too
   // steep for the factorised diagonal Grams. Ends with a barrier.
   // kContent: the erase logits carry the content bias z from s.Z; without a
-  // content projection z = 0 and s.Z is not read here.
-  template <bool kContent = true>
+  // content projection z = 0 and s.Z is not read here. kLogits: the decay
+  // input holds raw logits a and g = -softplus(a).
+  template <bool kContent = true, bool kLogits = false>
   __device__ static bool gate_pass(const Smem& s, const Raw& raw, int nvalid, E (&qd)[16]) {
     const GateCoord gc;
     const int tid = threadIdx.x;
@@ -371,7 +373,10 @@ struct Block {
       for (int i = 0; i < RPL; ++i) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          run[j] += to_f32(rg[i][j]) * kLog2e;
+          // log-decay in log2 units; a zeroed logit is not a zero decay, so
+          // with logits the padding rows are masked after the activation
+          if constexpr (kLogits) run[j] += r0 + i < nvalid ? decay_log2<true>(to_f32(rg[i][j])) : 0.f;
+          else run[j] += to_f32(rg[i][j]) * kLog2e;
           pre[i][j] = run[j];
         }
       }
@@ -518,6 +523,7 @@ struct Block {
   // A (fp32) lands over the Qx/Ky region once every wave is done with them;
   // the P tiles of this wave stay in registers (Pt) until solve() frees the
   // region again. Ends with a barrier.
+  template <bool kLogits = false>
   __device__ static void grams(const Smem& s, const Rows<E>& src, int t0, int nvalid, bool fallback,
                                f32x4 (&Pt)[TPW]) {
     const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
@@ -578,7 +584,7 @@ struct Block {
     }
     __syncthreads();
     if (fallback) {
-      grams_pairwise(s, src, t0, nvalid, Pt);
+      grams_pairwise<kLogits>(s, src, t0, nvalid, Pt);
       __syncthreads();
     }
   }
@@ -588,6 +594,7 @@ struct Block {
   // Slow but exact. A entries go to LDS; the P entries reach the Pt registers
   // of the wave that owns the tile through a scratch area in R4 (KdT is
   // parked in registers meanwhile).
+  template <bool kLogits = false>
   __device__ static void grams_pairwise(const Smem& s, const Rows<E>& src, int t0, int nvalid,
                                         f32x4 (&Pt)[TPW]) {
     float* pdiag = reinterpret_cast<float*>(s.base + LY::oR4);    // scratch: [NB][16][16]
@@ -611,8 +618,8 @@ struct Block {
         const size_t rowr = src.row(t0 + r) * DK, rowj = src.row(t0 + j) * DK;
         for (int d = 0; d < DK; ++d) {
           float dg = 0.f;                          // G_{r-1} - G_j, log2 units
-          for (int t = j + 1; t < r; ++t) dg += ldg(src.G, src.row(t0 + t) * DK + d) * kLog2e;
-          const float gr = ldg(src.G, rowr + d) * kLog2e;
+          for (int t = j + 1; t < r; ++t) dg += decay_log2<kLogits>(ldg(src.G, src.row(t0 + t) * DK + d));
+          const float gr = decay_log2<kLogits>(ldg(src.G, rowr + d));
           const float kj = ldg(src.K, rowj + d);
           const float br = sigmoid_f(ldg(src.BX, rowr + d) + s.Z[d]);
           sa += br * ldg(src.K, rowr + d) * kj * fast_exp2(dg + gr);

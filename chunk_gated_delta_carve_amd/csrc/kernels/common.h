@@ -38,7 +38,17 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Log-decay in log2 units from the decay input: g itself, or, with kLogits,
+// g = -softplus(a) from a raw decay logit a, evaluated as
+// -(max(a, 0) log2 e + log2(1 + 2^{-|a| log2 e})) so neither end overflows.
+template <bool kLogits>
+__device__ __forceinline__ float decay_log2(float x) {
+  if constexpr (kLogits) return -(fmaxf(x, 0.f) * kLog2e + fast_log2(1.f + fast_exp2(-fabsf(x) * kLog2e)));
+  else return x * kLog2e;
+}
 
 // logistic(x) = 1 / (1 + e^{-x}); saturates cleanly at both ends
 __device__ __forceinline__ float sigmoid_f(float x) {

@@ -30,7 +30,9 @@ constexpr int kMaxRank = 64;
 template <int DK, int BL>
 constexpr int serial_waves() { return DK == 64 && BL >= 32 ? 8 : DK / 16; }
 
-template <typename E, int DK, int DV, int BL>
+// kLogits: the decay input g holds raw decay logits a, and the log-decay is
+// -softplus(a), formed where g is read.
+template <typename E, int DK, int DV, int BL, bool kLogits>
 __global__ void __launch_bounds__((BlockLayout<E, DK, DV, BL, serial_waves<DK, BL>()>::NT))
 carve_chunk_serial_kernel(FwdArgs a) {
   using B = Block<E, DK, DV, BL, serial_waves<DK, BL>()>;
@@ -162,12 +164,12 @@ carve_chunk_serial_kernel(FwdArgs a) {
     E qd[16];
     f32x4 Pt[B::TPW];
     if (!kPrefetch) raw.load(src, t0, nvalid);
-    const bool fallback = B::gate_pass(s, raw, nvalid, qd);
+    const bool fallback = B::template gate_pass<true, kLogits>(s, raw, nvalid, qd);
     if (kPrefetch) {
       const int nb = min(blk + 1, nblk - 1);         // unconditional: keeps the load waits simple
       raw.load(src, nb * BL, min(BL, T - nb * BL));
     }
-    B::grams(s, src, t0, nvalid, fallback, Pt);
+    B::template grams<kLogits>(s, src, t0, nvalid, fallback, Pt);
     B::inverse_diag(s);
     B::solve(s, qd, Pt);
     f32x4 CtR[TDP], OltR[NBP], Ot[NBP];
@@ -247,7 +249,8 @@ constexpr int kIntraWaves = 8;
 
 // One workgroup per (batch, head, block): everything that does not depend on
 // the state. Writes the block's state-pass operand image to the workspace.
-template <typename E, int DK, int DV, int BL>
+// kLogits as for the chunk-serial kernel.
+template <typename E, int DK, int DV, int BL, bool kLogits>
 __global__ void __launch_bounds__((BlockLayout<E, DK, DV, BL, kIntraWaves>::NT))
 carve_intra_kernel(FwdArgs a) {
   using B = Block<E, DK, DV, BL, kIntraWaves>;
@@ -273,8 +276,8 @@ carve_intra_kernel(FwdArgs a) {
   for (int d = threadIdx.x; d < DK; d += NT) s.Z[d] = 0.f;
   E qd[16];
   f32x4 Pt[B::TPW];
-  const bool fallback = B::template gate_pass<false>(s, raw, nvalid, qd);
-  B::grams(s, src, t0, nvalid, fallback, Pt);
+  const bool fallback = B::template gate_pass<false, kLogits>(s, raw, nvalid, qd);
+  B::template grams<kLogits>(s, src, t0, nvalid, fallback, Pt);
   B::inverse_diag(s);
   B::template solve<true>(s, qd, Pt, img);           // also writes the block's image
 }

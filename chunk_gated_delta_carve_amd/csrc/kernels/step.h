@@ -26,6 +26,7 @@ struct StepArgs {
   float* state; float* mean_prev; float* chunk_acc;
   void* o;
   int B, H, L, rank, pos;
+  int logits;   // nonzero: g holds raw decay logits a, and exp(g) = sigmoid(-a)
 };
 
 template <typename E, int D>
@@ -56,7 +57,8 @@ carve_step_kernel(StepArgs a) {
   if (tid < D) {
     qs[tid] = to_f32(q[tok + tid]);
     ks[tid] = to_f32(k[tok + tid]);
-    dec[tid] = fast_exp2(to_f32(g[tok + tid]) * kLog2e);
+    const float gx = to_f32(g[tok + tid]);
+    dec[tid] = a.logits ? sigmoid_f(-gx) : fast_exp2(gx * kLog2e);
     bxs[tid] = to_f32(bx[tok + tid]);
     vs[tid] = to_f32(v[tok + tid]);
     ms[tid] = a.mean_prev[tok + tid];

@@ -12,7 +12,10 @@
  *                                   b = sigmoid(b_x + U_b m), one chunk stale;
  *   section 2.2 (scalar write)      one write gate w per head and token,
  *                                   broadcast over the value channels;
- *   section 2.3 (key-axis decay)    exponential decay exp(g) on the key axis.
+ *   section 2.3 (key-axis decay)    exponential decay exp(g) on the key axis;
+ *                                   the activation that turns the decay
+ *                                   logits into g may run inside the kernel
+ *                                   ("gate-in-kernel", CARVE_DECAY_LOGITS).
  * Per token (readings: b scales the retrieval key; decay precedes erase):
  *   o_t = S q_t;  S <- S diag(exp(g_t)) (I - (b_t * k_t) k_t^T) + w_t v_t k_t^T
  * with b_t = sigmoid(bx_t + U_up (U_down m_{c-1})) for every token of chunk c,
@@ -47,7 +50,7 @@ extern "C" {
 
 typedef enum {
   CARVE_OK = 0,
-  CARVE_EINVAL = 1,        /* NULL required pointer, negative size, bad rank */
+  CARVE_EINVAL = 1,        /* NULL required pointer, negative size, unknown flag bit */
   CARVE_EUNSUPPORTED = 2,  /* d_k/d_v not in {64,128}, L not in {16,32,64,128}, d_k != d_v,
                               rank > 64, or a size past the kernels' 32-bit index range */
   CARVE_EALIGN = 3,        /* a pointer is not 16-byte aligned */
@@ -57,12 +60,23 @@ typedef enum {
 
 typedef enum { CARVE_F32 = 0, CARVE_BF16 = 1 } carve_dtype;
 
+/* Bits of carve_config.flags.
+ *   CARVE_DECAY_LOGITS  the g tensor holds raw decay logits a instead of the
+ *                       log-decay, and the kernels form g = -softplus(a)
+ *                       = -log(1 + e^a) themselves (the decay activation of
+ *                       section 2.3 applied in-kernel), so the caller never
+ *                       materialises the activated tensor. Any real a is
+ *                       valid; exp(g) = sigmoid(-a) lies in (0, 1). */
+enum { CARVE_DECAY_LOGITS = 1 };
+
 /* Problem description. B batch, H heads, T tokens, dk key width, dv value
  * width, L chunk length of the content signal, rank of U_b (0 = no content
- * projection), dtype of every activation tensor and of U_down/U_up. */
+ * projection), dtype of every activation tensor and of U_down/U_up, flags a
+ * bitwise OR of the bits above (0 for none; an unknown bit is CARVE_EINVAL). */
 typedef struct {
   int32_t B, H, T, dk, dv, L, rank;
   int32_t dtype; /* carve_dtype */
+  int32_t flags; /* CARVE_DECAY_LOGITS or 0 */
 } carve_config;
 
 /* Element counts of every tensor (not bytes), and the workspace size in bytes. */
@@ -84,7 +98,8 @@ int carve_recurrent_ref_shapes(const carve_config* cfg, carve_shapes* out);
 /* Forward pass of the CARVE layer (see the header comment for the math).
  *   q, k       [B,T,H,dk] dtype   query and key (used as given: no scaling)
  *   v          [B,T,H,dv] dtype   value
- *   g          [B,T,H,dk] dtype   log-decay, expected <= 0
+ *   g          [B,T,H,dk] dtype   log-decay, expected <= 0; with
+ *                                 CARVE_DECAY_LOGITS the raw decay logits
  *   bx         [B,T,H,dk] dtype   erase logit
  *   w          [B,T,H]    dtype   scalar write gate
  *   ub_down    [H,rank,dv] dtype, ub_up [H,dk,rank] dtype: U_b = ub_up @ ub_down

@@ -38,9 +38,9 @@ def test_exports_every_declared_symbol(L):
 
 
 def cfg(**kw):
-    base = dict(B=2, H=3, T=100, dk=64, dv=64, L=64, rank=4, dtype=_lib.CARVE_BF16)
+    base = dict(B=2, H=3, T=100, dk=64, dv=64, L=64, rank=4, dtype=_lib.CARVE_BF16, flags=0)
     base.update(kw)
-    return _lib.CarveConfig(*(base[n] for n in ("B", "H", "T", "dk", "dv", "L", "rank", "dtype")))
+    return _lib.CarveConfig(*(base[n] for n in ("B", "H", "T", "dk", "dv", "L", "rank", "dtype", "flags")))
 
 
 def test_shape_contract(L):
@@ -70,6 +70,9 @@ def test_shape_contract(L):
     (dict(B=-2), _lib.CARVE_EINVAL),
     (dict(rank=-1), _lib.CARVE_EINVAL),
     (dict(dtype=7), _lib.CARVE_EINVAL),
+    (dict(flags=_lib.CARVE_DECAY_LOGITS), _lib.CARVE_OK),
+    (dict(flags=2), _lib.CARVE_EINVAL),
+    (dict(flags=-1), _lib.CARVE_EINVAL),
 ])
 def test_config_rejected(L, kw, code):
     out = _lib.CarveShapes()
