@@ -1,2 +1,3 @@
 """CPU oracle (test infrastructure only; never imported by the product path)."""
-from .carve_oracle import carve_forward, carve_step, content_gate_bias, decay_from_logits, sigmoid  # noqa: F401
+from .carve_oracle import (carve_backward, carve_forward, carve_step, content_gate_bias,  # noqa: F401
+                           decay_from_logits, sigmoid)

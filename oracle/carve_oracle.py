@@ -44,12 +44,18 @@ Readings where the pages leave a step open (each listed in the design notes):
   R9  The decay activation (not named on the pages) is g = -softplus(a) of a
       raw decay logit a: it maps every real a to a log-decay below zero, so
       exp(g) = sigmoid(-a) lies in (0, 1).
+  R10 Gradients (the pages train the layer but give no backward pass) are
+      the exact derivatives of the forward pass as defined here, through every
+      path it has: the stale chunk mean m_{c-1} passes gradient back to the
+      previous chunk's outputs and to mean_in, and U_down, U_up receive theirs
+      through the gate.
 """
 from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["sigmoid", "decay_from_logits", "carve_forward", "carve_step", "content_gate_bias"]
+__all__ = ["sigmoid", "decay_from_logits", "carve_forward", "carve_step", "carve_backward",
+           "content_gate_bias"]
 
 
 def sigmoid(x: np.ndarray) -> np.ndarray:
@@ -174,3 +180,100 @@ def carve_step(state, mean_prev, chunk_acc, pos, q, k, v, g, bx, w, L,
     if pos == L - 1:
         m, acc = acc / L, np.zeros_like(acc)
     return ot, S, m, acc
+
+
+def carve_backward(q, k, v, g, bx, w, L, do, U_down=None, U_up=None,
+                   state_in=None, mean_in=None, dstate_out=None, dmean_out=None):
+    """Gradients of carve_forward in float64 (reading R10), by the adjoint of
+    the token recurrence taken backwards through the sequence.
+
+    Arguments as for carve_forward, plus the gradients of a scalar loss with
+    respect to its outputs: do [B, T, H, d_v], and optionally dstate_out
+    [B, H, d_v, d_k] and dmean_out [B, H, d_v] (zeros when None).
+    Returns a dict with dq, dk, dg, dbx [B, T, H, d_k], dv [B, T, H, d_v],
+    dw [B, T, H], dU_down [H, r, d_v] and dU_up [H, d_k, r] (None without a
+    projection), dstate_in [B, H, d_v, d_k] and dmean_in [B, H, d_v].
+
+    With S' = S diag(e^g), r = S' (b*k), delta = w v - r and S_t = S' + delta k^T,
+    the adjoint of one token, given dS (of S_t) and the token's total output
+    gradient do_t, is
+      d delta = dS k          dk  = dS^T delta + (S'^T dr) * b,   dr = -d delta
+      dv = w d delta          dw  = <d delta, v>
+      dS' = dS + dr (b*k)^T   dg  = sum over rows of dS' * S'
+      db  = (S'^T dr) * k     dbx = db * b (1 - b)
+      dq  = S_{t-1}^T do_t    dS_{t-1} = dS' diag(e^g) + do_t q^T.
+    The output gradient of token t in chunk c adds dm_c / n_c, where n_c is
+    the chunk's token count and dm_c collects dmean_out (last chunk) and the
+    gradient that chunk c + 1's gate sends back through z = U_up (U_down m_c).
+    """
+    f = lambda x: np.asarray(x, dtype=np.float64)
+    q, k, v, g, bx, w, do = map(f, (q, k, v, g, bx, w, do))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if L < 1:
+        raise ValueError("L must be positive")
+    Ud = None if U_down is None else f(U_down)
+    Uu = None if U_up is None else f(U_up)
+    content = Ud is not None and Uu is not None and Ud.shape[1] > 0
+
+    # forward pass, keeping each token's state before it and each chunk's gate input
+    S = np.zeros((B, H, dv, dk)) if state_in is None else f(state_in).copy()
+    m = np.zeros((B, H, dv)) if mean_in is None else f(mean_in).copy()
+    nc = (T + L - 1) // L
+    S_before = np.empty((B, T, H, dv, dk))
+    b_all = np.empty((B, T, H, dk))
+    gate_mean = []                                   # m_{c-1} for each chunk c
+    for c in range(nc):
+        gate_mean.append(m)
+        z = content_gate_bias(m, Ud, Uu)
+        acc = np.zeros((B, H, dv))
+        t_end = min(T, (c + 1) * L)
+        for t in range(c * L, t_end):
+            S_before[:, t] = S
+            b_all[:, t] = sigmoid(bx[:, t] if z is None else bx[:, t] + z)
+            ot, S = _token(S, q[:, t], k[:, t], v[:, t], g[:, t], bx[:, t], w[:, t], z)
+            acc += ot
+        m = acc / (t_end - c * L)
+
+    dS = np.zeros((B, H, dv, dk)) if dstate_out is None else f(dstate_out).copy()
+    dmo = np.zeros((B, H, dv)) if dmean_out is None else f(dmean_out)
+    grads = {n: np.zeros_like(x) for n, x in (("dq", q), ("dk", k), ("dv", v), ("dg", g), ("dbx", bx),
+                                               ("dw", w))}
+    dUd = None if Ud is None else np.zeros_like(Ud)
+    dUu = None if Uu is None else np.zeros_like(Uu)
+    dm = np.zeros((B, H, dv))                        # gradient of m_c from chunk c + 1's gate
+    for c in reversed(range(nc)):
+        t0, t1 = c * L, min(T, (c + 1) * L)
+        dmc = dm + (dmo if c == nc - 1 else 0.0)
+        dz = np.zeros((B, H, dk))
+        for t in reversed(range(t0, t1)):
+            Sp, b = S_before[:, t], b_all[:, t]
+            qt, kt, vt, gt, wt = q[:, t], k[:, t], v[:, t], g[:, t], w[:, t]
+            dec = np.exp(gt)
+            Sd = Sp * dec[:, :, None, :]                                  # S'
+            bk = b * kt
+            delta = wt[:, :, None] * vt - np.einsum("bhed,bhd->bhe", Sd, bk)
+            dot = do[:, t] + dmc / (t1 - t0)
+            ddelta = np.einsum("bhed,bhd->bhe", dS, kt)
+            dr = -ddelta
+            sdr = np.einsum("bhed,bhe->bhd", Sd, dr)                       # S'^T dr
+            dSd = dS + dr[:, :, :, None] * bk[:, :, None, :]
+            grads["dk"][:, t] = np.einsum("bhed,bhe->bhd", dS, delta) + sdr * b
+            grads["dv"][:, t] = wt[:, :, None] * ddelta
+            grads["dw"][:, t] = np.sum(ddelta * vt, axis=-1)
+            grads["dg"][:, t] = np.sum(dSd * Sd, axis=-2)
+            grads["dbx"][:, t] = sdr * kt * b * (1.0 - b)
+            grads["dq"][:, t] = np.einsum("bhed,bhe->bhd", Sp, dot)
+            dz += grads["dbx"][:, t]
+            dS = dSd * dec[:, :, None, :] + dot[:, :, :, None] * qt[:, :, None, :]
+        if content:                                   # z = U_up y, y = U_down m_{c-1}
+            mp = gate_mean[c]
+            y = np.einsum("hre,bhe->bhr", Ud, mp)
+            dUu += np.einsum("bhd,bhr->hdr", dz, y)
+            dy = np.einsum("hdr,bhd->bhr", Uu, dz)
+            dUd += np.einsum("bhr,bhe->hre", dy, mp)
+            dm = np.einsum("hre,bhr->bhe", Ud, dy)
+        else:
+            dm = np.zeros((B, H, dv))
+    grads.update(dU_down=dUd, dU_up=dUu, dstate_in=dS, dmean_in=dm if nc else dmo.copy())
+    return grads

@@ -13,7 +13,7 @@ import os
 import numpy as np
 import pytest
 
-from oracle import carve_forward, carve_step, decay_from_logits, sigmoid
+from oracle import carve_backward, carve_forward, carve_step, decay_from_logits, sigmoid
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -435,3 +435,86 @@ def test_decay_logits_in_the_layer():
     o_zero, S_zero, _ = carve_forward(q, k, v, np.zeros_like(k), bx, w, 4)
     np.testing.assert_allclose(o_none, o_zero, atol=1e-18)
     np.testing.assert_allclose(S_none, S_zero, atol=1e-18)
+
+
+# ---------------------------------------------------------------- gradients
+
+GRAD_OF = {"q": "dq", "k": "dk", "v": "dv", "g": "dg", "bx": "dbx", "w": "dw", "U_down": "dU_down",
+           "U_up": "dU_up", "state_in": "dstate_in", "mean_in": "dmean_in"}
+
+
+def fd_gradients(args, L, do, dSo, dmo, h=1e-6):
+    """Central differences of J = <do, o> + <dSo, state_out> + <dmo, mean_out>
+    with respect to every element of every input: the derivative of the
+    forward pass itself, independent of the adjoint's formulas."""
+    def J(a):
+        o, S, m = carve_forward(a["q"], a["k"], a["v"], a["g"], a["bx"], a["w"], L, a["U_down"], a["U_up"],
+                                state_in=a["state_in"], mean_in=a["mean_in"])
+        return np.sum(o * do) + np.sum(S * dSo) + np.sum(m * dmo)
+    out = {}
+    for name in GRAD_OF:
+        x = args[name]
+        if x is None:
+            continue
+        fd = np.zeros_like(x)
+        for i in np.ndindex(x.shape):
+            a = dict(args)
+            xp = x.copy(); xp[i] += h; a[name] = xp
+            jp = J(a)
+            xm = x.copy(); xm[i] -= h; a[name] = xm
+            fd[i] = (jp - J(a)) / (2 * h)
+        out[name] = fd
+    return out
+
+
+@pytest.mark.parametrize("T,L,rank", [(7, 3, 2), (6, 3, 0), (5, 8, 2), (9, 2, 1), (4, 1, 2)])
+def test_backward_matches_finite_differences(T, L, rank):
+    """Every gradient the oracle's adjoint returns (inputs, gates, projection
+    factors, incoming state and mean) equals the finite-difference derivative
+    of the pinned forward pass: whole and ragged last chunks, with and without
+    a content projection, a single chunk (T < L) and L = 1."""
+    rng = np.random.default_rng(100 * T + 10 * L + rank)
+    B, H, dk, dv = 1, 2, 3, 2
+    q, k, v, g, bx, w, Ud, Uu = rand_inputs(rng, B, T, H, dk, dv, rank=rank, ub_std=0.8)
+    args = dict(q=q, k=k, v=v, g=g, bx=bx, w=w, U_down=Ud, U_up=Uu,
+                state_in=rng.standard_normal((B, H, dv, dk)), mean_in=rng.standard_normal((B, H, dv)))
+    do = rng.standard_normal((B, T, H, dv))
+    dSo = rng.standard_normal((B, H, dv, dk))
+    dmo = rng.standard_normal((B, H, dv))
+    got = carve_backward(q, k, v, g, bx, w, L, do, Ud, Uu, args["state_in"], args["mean_in"], dSo, dmo)
+    fd = fd_gradients(args, L, do, dSo, dmo)
+    for name, ref in fd.items():
+        x = got[GRAD_OF[name]]
+        err = np.abs(x - ref).max() / max(np.abs(ref).max(), 1e-12)
+        assert err < 1e-7, f"{name}: relative error {err:.2e}"
+    if rank == 0:
+        assert got["dU_down"] is None and got["dU_up"] is None
+    if T <= L and rank:
+        # one chunk from a zero incoming mean: the gate never sees a content
+        # signal, so the projection gets no gradient
+        zero_mean = carve_backward(q, k, v, g, bx, w, L, do, Ud, Uu, args["state_in"], None, dSo, dmo)
+        assert not zero_mean["dU_down"].any() and not zero_mean["dU_up"].any()
+
+
+def test_backward_without_state_and_mean_gradients():
+    """Absent dstate_out and dmean_out count as zeros: with rank 0 the incoming
+    mean then gets no gradient, and doubling do doubles every gradient."""
+    rng = np.random.default_rng(5)
+    q, k, v, g, bx, w, _, _ = rand_inputs(rng, 2, 6, 1, 3, 2)
+    do = rng.standard_normal((2, 6, 1, 2))
+    a = carve_backward(q, k, v, g, bx, w, 4, do)
+    b = carve_backward(q, k, v, g, bx, w, 4, 2 * do)
+    assert not a["dmean_in"].any()
+    for n in ("dq", "dk", "dv", "dg", "dbx", "dw", "dstate_in"):
+        np.testing.assert_allclose(b[n], 2 * a[n], rtol=1e-13, atol=1e-15)
+
+
+def test_backward_empty_sequence_passes_gradients_through():
+    rng = np.random.default_rng(6)
+    B, H, dk, dv = 2, 1, 3, 2
+    z = np.zeros((B, 0, H, dk))
+    dSo, dmo = rng.standard_normal((B, H, dv, dk)), rng.standard_normal((B, H, dv))
+    got = carve_backward(z, z, np.zeros((B, 0, H, dv)), z, z, np.zeros((B, 0, H)), 4,
+                         np.zeros((B, 0, H, dv)), dstate_out=dSo, dmean_out=dmo)
+    np.testing.assert_array_equal(got["dstate_in"], dSo)
+    np.testing.assert_array_equal(got["dmean_in"], dmo)
