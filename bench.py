@@ -260,6 +260,117 @@ def write_mfma_summary(wl, pmc_csv, trace_csv, commands):
     print(open(mfma_file(wl)).read())
 
 
+def backward_bytes(B, T, H, dk, dv, es, rank=0):
+    """Bytes the backward pass must move: read q, k, g, bx, v, w and d_o (+ U_b
+    factors), write dq, dk, dg, dbx, dv, dw (+ the factors' fp32 gradients) and
+    the fp32 gradients of the incoming state and mean."""
+    reads = B * T * H * (4 * dk + 2 * dv + 1) * es + H * rank * (dk + dv) * es
+    writes = B * T * H * (4 * dk + dv + 1) * es + H * rank * (dk + dv) * 4 + B * H * (dv * dk + dv) * 4
+    return reads + writes
+
+
+def backward_cpu_baseline(wl, inp, do, budget_s):
+    """The float64 oracle's backward pass, single-threaded, on a prefix of every
+    sequence sized to the budget (at most 256 time steps: the oracle keeps every
+    token's state). Returns tokens/s as the GPU value is."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import carve_backward
+    from chunk_gated_delta_carve_amd.workloads import to_f64
+
+    def run(Tp):
+        f = lambda x: np.ascontiguousarray(to_f64(x[:, :Tp], wl.dtype))
+        ub = {}
+        if wl.rank > 0:
+            ub = dict(U_down=to_f64(inp["U_down"], wl.dtype), U_up=to_f64(inp["U_up"], wl.dtype))
+        t0 = time.perf_counter()
+        carve_backward(*(f(inp[k]) for k in ("q", "k", "v", "g", "bx", "w")), wl.L, f(do), **ub)
+        return time.perf_counter() - t0
+
+    with threadpool_limits(1):
+        probe_T = min(wl.T, wl.L)
+        rate = probe_T / run(probe_T)
+        Tp = min(wl.T, 256, max(wl.L, int(budget_s * rate) // wl.L * wl.L))
+        spent, steps, passes = 0.0, 0, 0
+        while spent < budget_s:
+            spent += run(Tp)
+            steps += Tp
+            passes += 1
+    return {"value": wl.B * steps / spent, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"the first {Tp} of {wl.T} time steps (B={wl.B}, all {wl.H} heads), {passes} pass(es), "
+                      f"{spent:.1f} s, one thread"}
+
+
+def bench_backward(args, wl):
+    """carve_chunk_bwd on the workload, from seeded output gradients d_o (no
+    state or mean gradients, as in a training step that starts from zeros):
+    K back-to-back calls between two HIP events on the launch stream."""
+    import numpy as np
+    import torch
+
+    from chunk_gated_delta_carve_amd import chunk_bwd
+    from chunk_gated_delta_carve_amd.workloads import bf16_bits_from_f32, make_inputs, to_torch
+
+    inp = make_inputs(wl, decay_logits=args.decay_logits)
+    t = {k: to_torch(v, wl.dtype) for k, v in inp.items()}
+    B, T, H, dk, dv, L, rank = wl.B, wl.T, wl.H, wl.dk, wl.dv, wl.L, wl.rank
+    do = np.random.default_rng(wl.seed + 17).standard_normal((B, T, H, dv)).astype(np.float32)
+    do = do if wl.dtype == "f32" else bf16_bits_from_f32(do)
+    d_o = to_torch(do, wl.dtype)
+    ub = (t["U_down"], t["U_up"]) if rank else (None, None)
+    from chunk_gated_delta_carve_amd import recurrent_ref_shapes
+    tdtype = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    ws = torch.empty(int(recurrent_ref_shapes(B, H, T, dk, dv, L, rank, tdtype).bwd_workspace_bytes),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    out = None
+
+    def step():
+        nonlocal out
+        out = chunk_bwd(*(t[k] for k in ("q", "k", "v", "g", "bx", "w")), d_o, L=L, ub_down=ub[0], ub_up=ub[1],
+                        decay_logits=args.decay_logits, workspace=ws, out=out)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    ev_start, ev_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev_start.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = 1e3 * (time.perf_counter() - t0) / args.steps
+    kernel_ms = ev_start.elapsed_time(ev_end) / args.steps
+    es = 2 if wl.dtype == "bf16" else 4
+    alg = backward_bytes(B, T, H, dk, dv, es, rank)
+    achieved = alg / (kernel_ms * 1e-3) / 1e9
+    line = {
+        "metric": f"tokens/s of carve_chunk_bwd (backward), B{B} H{H} T{T} d{dk} L{L} {wl.dtype}",
+        "value": B * T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded; inputs as for carve_chunk_fwd, d_o N(0,1))",
+        "config": {"workload": f"carve_chunk_bwd B{B} H{H} T{T} dk{dk} dv{dv} L{L} {wl.dtype}, "
+                               + (f"content projection rank {rank}" if rank else "no content projection"),
+                   "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "L": L, "rank": rank,
+                   "decay_input": "raw logits, -softplus in-kernel" if args.decay_logits else "log-decay g"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "carve_bwd_kernel",
+                     "kernel_ms": kernel_ms, "algorithmic_bytes_per_launch": alg},
+    }
+    if not args.no_cpu_baseline and not args.decay_logits:
+        line["cpu_baseline"] = backward_cpu_baseline(wl, inp, do, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
 def decode_bytes(B, H, dk, dv, es, rank=0):
     """Bytes one decode step must move: read the token's q, k, g, b_x, v, w and
     the U_b factors, read and write the fp32 state, mean and chunk sum, write o."""
@@ -403,6 +514,8 @@ def main():
                          "also times the unfused alternative (a torch softplus pass, then the plain call)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU work budget of the oracle baseline sample")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass carve_chunk_bwd on the workload instead of the forward")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain device copy of known size first (for counter calibration)")
     ap.add_argument("--write-traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -428,6 +541,9 @@ def main():
         wl = wl.with_(L=args.L)
     if args.workload == "decode":
         bench_decode(args, wl)
+        return
+    if args.backward:
+        bench_backward(args, wl)
         return
     if args.write_traffic_summary:
         write_traffic_summary(wl, *args.write_traffic_summary, args.commands)

@@ -1,11 +1,12 @@
-"""MI355X-native CARVE chunk-parallel forward pass (HIP kernels for gfx950 behind a C ABI).
+"""MI355X-native CARVE chunk-parallel layer (HIP kernels for gfx950 behind a C ABI): forward
+pass, backward pass and decode step.
 
-`chunk_fwd`, `recurrent_step` and `recurrent_ref_shapes` are imported lazily so that the input
+`chunk_fwd`, `chunk_bwd`, `recurrent_step` and `recurrent_ref_shapes` are imported lazily so that the input
 generator (`workloads`) and the build script work without torch or the
 compiled library.
 """
 
-__all__ = ["chunk_fwd", "recurrent_step", "recurrent_ref_shapes"]
+__all__ = ["chunk_fwd", "chunk_bwd", "recurrent_step", "recurrent_ref_shapes"]
 
 
 def __getattr__(name):

@@ -9,7 +9,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcarve.so
 CARVE_OK, CARVE_EINVAL, CARVE_EUNSUPPORTED, CARVE_EALIGN, CARVE_EWORKSPACE, CARVE_EHIP = range(6)
 CARVE_F32, CARVE_BF16 = 0, 1
 CARVE_DECAY_LOGITS = 1
-EXPORTED = ("carve_recurrent_ref_shapes", "carve_chunk_fwd", "carve_recurrent_step", "carve_error_string")
+EXPORTED = ("carve_recurrent_ref_shapes", "carve_chunk_fwd", "carve_chunk_bwd", "carve_recurrent_step",
+            "carve_error_string")
 
 
 class CarveConfig(ctypes.Structure):
@@ -19,7 +20,7 @@ class CarveConfig(ctypes.Structure):
 class CarveShapes(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in
                 ("q", "k", "v", "g", "bx", "w", "ub_down", "ub_up", "o", "state", "mean",
-                 "workspace_bytes")]
+                 "workspace_bytes", "bwd_workspace_bytes")]
 
 
 class CarveError(RuntimeError):
@@ -45,6 +46,8 @@ def lib() -> ctypes.CDLL:
         L.carve_recurrent_ref_shapes.restype = ctypes.c_int
         L.carve_chunk_fwd.argtypes = [ctypes.POINTER(CarveConfig)] + [vp] * 14 + [ctypes.c_size_t, vp]
         L.carve_chunk_fwd.restype = ctypes.c_int
+        L.carve_chunk_bwd.argtypes = [ctypes.POINTER(CarveConfig)] + [vp] * 24 + [ctypes.c_size_t, vp]
+        L.carve_chunk_bwd.restype = ctypes.c_int
         L.carve_recurrent_step.argtypes = [ctypes.POINTER(CarveConfig), ctypes.c_int32] + [vp] * 13
         L.carve_recurrent_step.restype = ctypes.c_int
         L.carve_error_string.argtypes = [ctypes.c_int]

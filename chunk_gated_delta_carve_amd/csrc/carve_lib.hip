@@ -9,6 +9,7 @@
 
 #include "carve.h"
 #include "kernels/kernels.h"
+#include "kernels/bwd.h"
 #include "kernels/step.h"
 
 namespace {
@@ -68,16 +69,17 @@ int64_t parallel_workspace_bytes(const carve_config* c) {
   return (int64_t)c->B * c->H * nblk * img;
 }
 
-// Raises a kernel's dynamic-LDS limit to `bytes`. The attribute only ever
-// needs raising, so the largest value set so far is kept per kernel and device
-// and the driver is called only to go beyond it: later calls (and launches
-// inside a graph capture) make no attribute call at all.
+// Raises kernel Kern's dynamic-LDS limit to `bytes`. The attribute only ever
+// needs raising, so the largest value set so far is kept per kernel (one
+// instantiation of this function per kernel) and device, and the driver is
+// called only to go beyond it: later calls (and launches inside a graph
+// capture) make no attribute call at all.
 constexpr int kMaxDevices = 64;
-template <typename K>
-hipError_t set_lds(K kern, int bytes) {
+template <auto Kern>
+hipError_t set_lds(int bytes) {
   static std::atomic<int> set_bytes[kMaxDevices];
   auto raise = [&] {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(Kern),
                                hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   };
   int dev = -1;
@@ -94,8 +96,8 @@ hipError_t set_lds(K kern, int bytes) {
 template <typename E, int D, int BL, bool LG>
 hipError_t launch_serial(const carve::FwdArgs& a, hipStream_t s) {
   using LY = carve::BlockLayout<E, D, D, BL, carve::serial_waves<D, BL>()>;
-  auto kern = carve::carve_chunk_serial_kernel<E, D, D, BL, LG>;
-  hipError_t e = set_lds(kern, LY::serial_bytes);
+  constexpr auto kern = carve::carve_chunk_serial_kernel<E, D, D, BL, LG>;
+  hipError_t e = set_lds<kern>(LY::serial_bytes);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(a.B * a.H), dim3(LY::NT), LY::serial_bytes, s, a);
   return hipGetLastError();
@@ -108,9 +110,9 @@ hipError_t launch_parallel(const carve::FwdArgs& a, hipStream_t s) {
   using LY = carve::BlockLayout<E, D, D, BL>;                        // state pass, images
   using LI = carve::BlockLayout<E, D, D, BL, carve::kIntraWaves>;    // intra kernel
   const int nblk = (a.T + BL - 1) / BL;
-  auto intra = carve::carve_intra_kernel<E, D, D, BL, LG>;
+  constexpr auto intra = carve::carve_intra_kernel<E, D, D, BL, LG>;
   auto state = carve::carve_state_kernel<E, D, D, BL>;
-  hipError_t e = set_lds(intra, LI::intra_bytes);
+  hipError_t e = set_lds<intra>(LI::intra_bytes);
   if (e != hipSuccess) return e;
   if (nblk > 0) {
     hipLaunchKernelGGL(intra, dim3(a.B * a.H * nblk), dim3(LI::NT), LI::intra_bytes, s, a);
@@ -144,11 +146,36 @@ hipError_t dispatch_fwd(const carve_config* cfg, const carve::FwdArgs& a, hipStr
   return cfg->dk == 64 ? dispatch_block<float, 64, LG>(a, bl, s) : dispatch_block<float, 128, LG>(a, bl, s);
 }
 
+template <typename E, int D, bool LG>
+hipError_t launch_bwd(const carve::BwdArgs& a, hipStream_t s) {
+  using LY = carve::BwdLayout<D>;
+  constexpr auto kern = carve::carve_bwd_kernel<E, D, LG>;
+  hipError_t e = set_lds<kern>(LY::bytes);
+  if (e != hipSuccess) return e;
+  if ((int64_t)a.B * a.H > 0) {
+    hipLaunchKernelGGL(kern, dim3(a.B * a.H), dim3(LY::NT), LY::bytes, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.rank == 0 || a.H == 0) return hipSuccess;
+  // the projection factors' gradients, summed over the batch (zeros for B = 0)
+  const carve::BwdWs lay(D, a.T, a.L, a.rank);
+  const size_t n = 2 * (size_t)a.rank * D * a.H;
+  hipLaunchKernelGGL(carve::carve_bwd_ub_kernel<D>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     a.ws, lay.total, lay.dud, a.B, a.H, a.rank, a.d_ub_down, a.d_ub_up);
+  return hipGetLastError();
+}
+
+template <typename E, bool LG>
+hipError_t dispatch_bwd_width(const carve_config* cfg, const carve::BwdArgs& a, hipStream_t s) {
+  return cfg->dk == 64 ? launch_bwd<E, 64, LG>(a, s) : launch_bwd<E, 128, LG>(a, s);
+}
+
 template <typename E, int D>
 hipError_t launch_step(const carve::StepArgs& a, hipStream_t s) {
-  auto kern = carve::carve_step_kernel<E, D>;
+  constexpr auto kern = carve::carve_step_kernel<E, D>;
   const int lds = 2 * a.rank * D * (int)sizeof(E);   // the head's U_down and U_up
-  hipError_t e = set_lds(kern, lds);
+  hipError_t e = set_lds<kern>(lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(a.B * a.H), dim3(4 * D), lds, s, a);
   return hipGetLastError();
@@ -169,6 +196,8 @@ extern "C" int carve_recurrent_ref_shapes(const carve_config* cfg, carve_shapes*
   out->state = B * H * dv * dk;
   out->mean = B * H * dv;
   out->workspace_bytes = chunk_parallel(cfg) ? parallel_workspace_bytes(cfg) : 0;
+  out->bwd_workspace_bytes = (int64_t)cfg->B * cfg->H * 4 *
+                             (int64_t)carve::BwdWs(cfg->dk, cfg->T, cfg->L, cfg->rank).total;
   return CARVE_OK;
 }
 
@@ -212,6 +241,87 @@ extern "C" int carve_chunk_fwd(const carve_config* cfg,
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const hipError_t e = (cfg->flags & CARVE_DECAY_LOGITS) ? dispatch_fwd<true>(cfg, a, s) : dispatch_fwd<false>(cfg, a, s);
+  if (e != hipSuccess) {
+    std::snprintf(g_hip_msg, sizeof(g_hip_msg), "%s", hipGetErrorString(e));
+    return CARVE_EHIP;
+  }
+  return CARVE_OK;
+}
+
+extern "C" int carve_chunk_bwd(const carve_config* cfg,
+                               const void* q, const void* k, const void* v,
+                               const void* g, const void* bx, const void* w,
+                               const void* ub_down, const void* ub_up,
+                               const float* state_in, const float* mean_in,
+                               const void* d_o, const float* d_state_out, const float* d_mean_out,
+                               void* dq, void* dk, void* dv, void* dg, void* dbx, void* dw,
+                               float* d_ub_down, float* d_ub_up, float* d_state_in, float* d_mean_in,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  carve_shapes sh;
+  int st = carve_recurrent_ref_shapes(cfg, &sh);
+  if (st != CARVE_OK) return st;
+  const bool tokens = sh.q > 0;
+  if (tokens && (!q || !k || !v || !g || !bx || !w || !d_o || !dq || !dk || !dv || !dg || !dbx || !dw))
+    return CARVE_EINVAL;
+  const bool content = cfg->rank > 0;
+  if (content && cfg->H > 0 && (!d_ub_down || !d_ub_up)) return CARVE_EINVAL;
+  if (content && (int64_t)cfg->B * cfg->H > 0 && (!ub_down || !ub_up)) return CARVE_EINVAL;
+  const void* ptrs[] = {q, k, v, g, bx, w, content ? ub_down : nullptr, content ? ub_up : nullptr,
+                        state_in, mean_in, d_o, d_state_out, d_mean_out, dq, dk, dv, dg, dbx, dw,
+                        content ? d_ub_down : nullptr, content ? d_ub_up : nullptr, d_state_in, d_mean_in,
+                        workspace};
+  for (const void* p : ptrs)
+    if (misaligned(p)) return CARVE_EALIGN;
+  if (workspace_bytes < (size_t)sh.bwd_workspace_bytes) return CARVE_EWORKSPACE;
+  if (sh.bwd_workspace_bytes > 0 && (int64_t)cfg->B * cfg->H > 0 && !workspace) return CARVE_EINVAL;
+  const size_t es = elem_bytes(cfg->dtype);
+  struct Span { const void* p; size_t n; };
+  const Span ins[] = {
+      {q, (size_t)sh.q * es}, {k, (size_t)sh.k * es}, {v, (size_t)sh.v * es},
+      {g, (size_t)sh.g * es}, {bx, (size_t)sh.bx * es}, {w, (size_t)sh.w * es},
+      {content ? ub_down : nullptr, (size_t)sh.ub_down * es}, {content ? ub_up : nullptr, (size_t)sh.ub_up * es},
+      {state_in, (size_t)sh.state * 4}, {mean_in, (size_t)sh.mean * 4}, {d_o, (size_t)sh.o * es}};
+  // d_state_out and d_mean_out may be the very buffers that receive
+  // d_state_in and d_mean_in (each element is read before it is written, by
+  // the same thread); any other overlap is an error
+  const Span grads_out[] = {{d_state_out, (size_t)sh.state * 4}, {d_mean_out, (size_t)sh.mean * 4}};
+  const Span outs[] = {
+      {dq, (size_t)sh.q * es}, {dk, (size_t)sh.k * es}, {dv, (size_t)sh.v * es}, {dg, (size_t)sh.g * es},
+      {dbx, (size_t)sh.bx * es}, {dw, (size_t)sh.w * es},
+      {content ? d_ub_down : nullptr, (size_t)sh.ub_down * 4}, {content ? d_ub_up : nullptr, (size_t)sh.ub_up * 4},
+      {d_state_in, (size_t)sh.state * 4}, {d_mean_in, (size_t)sh.mean * 4},
+      {workspace, (size_t)sh.bwd_workspace_bytes}};
+  constexpr size_t NO = sizeof(outs) / sizeof(outs[0]);
+  for (size_t i = 0; i < NO; ++i) {
+    for (const auto& in : ins)
+      if (overlaps(outs[i].p, outs[i].n, in.p, in.n)) return CARVE_EINVAL;
+    for (size_t j = 0; j < 2; ++j) {
+      const bool allowed = (i == 8 && j == 0 && outs[i].p == grads_out[j].p) ||
+                           (i == 9 && j == 1 && outs[i].p == grads_out[j].p);
+      if (!allowed && overlaps(outs[i].p, outs[i].n, grads_out[j].p, grads_out[j].n)) return CARVE_EINVAL;
+    }
+    for (size_t j = i + 1; j < NO; ++j)
+      if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return CARVE_EINVAL;
+  }
+  if ((int64_t)cfg->B * cfg->H == 0 && !(content && cfg->H > 0)) return CARVE_OK;
+
+  carve::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.bx = bx; a.w = w;
+  a.ub_down = ub_down; a.ub_up = ub_up;
+  a.state_in = state_in; a.mean_in = mean_in;
+  a.d_o = d_o; a.d_state_out = d_state_out; a.d_mean_out = d_mean_out;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbx = dbx; a.dw = dw;
+  a.d_state_in = d_state_in; a.d_mean_in = d_mean_in;
+  a.d_ub_down = d_ub_down; a.d_ub_up = d_ub_up;
+  a.ws = static_cast<float*>(workspace);
+  a.B = cfg->B; a.H = cfg->H; a.T = cfg->T; a.L = cfg->L; a.rank = cfg->rank;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool lg = (cfg->flags & CARVE_DECAY_LOGITS) != 0;
+  hipError_t e;
+  if (cfg->dtype == CARVE_BF16)
+    e = lg ? dispatch_bwd_width<carve::bf16, true>(cfg, a, s) : dispatch_bwd_width<carve::bf16, false>(cfg, a, s);
+  else
+    e = lg ? dispatch_bwd_width<float, true>(cfg, a, s) : dispatch_bwd_width<float, false>(cfg, a, s);
   if (e != hipSuccess) {
     std::snprintf(g_hip_msg, sizeof(g_hip_msg), "%s", hipGetErrorString(e));
     return CARVE_EHIP;

@@ -85,7 +85,8 @@ typedef struct {
   int64_t ub_down, ub_up;      /* content projection factors (0 when rank == 0) */
   int64_t o;                   /* output */
   int64_t state, mean;         /* optional fp32 state_in/out and mean_in/out */
-  int64_t workspace_bytes;     /* device scratch the caller must provide */
+  int64_t workspace_bytes;     /* device scratch carve_chunk_fwd needs */
+  int64_t bwd_workspace_bytes; /* device scratch carve_chunk_bwd needs */
 } carve_shapes;
 
 /* Validates `cfg` and fills `out` with the shape contract of the recurrence:
@@ -122,6 +123,40 @@ int carve_chunk_fwd(const carve_config* cfg,
                     const void* ub_down, const void* ub_up,
                     const float* state_in, const float* mean_in,
                     void* o, float* state_out, float* mean_out,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward pass: gradients of a scalar loss with respect to every input of
+ * carve_chunk_fwd, from its gradients with respect to the outputs. The pages
+ * train the layer but give no backward pass; these are the exact derivatives
+ * of the recurrence in the header comment through every path it has: the
+ * stale chunk mean m_{c-1} that gates chunk c passes gradient back to chunk
+ * c-1's outputs (and to mean_in for chunk 0), and U_down, U_up receive
+ * theirs through the erase gate.
+ *   cfg, q .. mean_in   exactly as given to carve_chunk_fwd (the forward pass
+ *                       is recomputed; nothing from it is kept)
+ *   d_o         [B,T,H,dv] dtype   gradient of o (required when B T H > 0)
+ *   d_state_out [B,H,dv,dk] fp32 or NULL (zeros)
+ *   d_mean_out  [B,H,dv] fp32 or NULL (zeros)
+ *   dq, dk, dg, dbx [B,T,H,dk], dv [B,T,H,dv], dw [B,T,H]: dtype, written.
+ *               With CARVE_DECAY_LOGITS, dg is the gradient of the raw logit.
+ *   d_ub_down [H,rank,dv], d_ub_up [H,dk,rank]: fp32, written (summed over
+ *               the batch); required when rank > 0 and H > 0
+ *   d_state_in [B,H,dv,dk], d_mean_in [B,H,dv]: fp32 or NULL (not written).
+ *               They may be the same buffers as d_state_out and d_mean_out.
+ *   workspace   at least shapes.bwd_workspace_bytes of device scratch: the
+ *               state at every chunk start and one chunk's per-token states,
+ *               4 (nc + L) dk dv bytes per (batch, head) plus small vectors
+ * No output may overlap an input, another output or the workspace, except
+ * for the two aliases above. Results are deterministic (no atomics).
+ * Returns the status codes of carve_chunk_fwd. */
+int carve_chunk_bwd(const carve_config* cfg,
+                    const void* q, const void* k, const void* v,
+                    const void* g, const void* bx, const void* w,
+                    const void* ub_down, const void* ub_up,
+                    const float* state_in, const float* mean_in,
+                    const void* d_o, const float* d_state_out, const float* d_mean_out,
+                    void* dq, void* dk, void* dv, void* dg, void* dbx, void* dw,
+                    float* d_ub_down, float* d_ub_up, float* d_state_in, float* d_mean_in,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* One decode step: the token recurrence of the header comment for a single

@@ -161,3 +161,48 @@ def test_step_argument_errors(L):
     # rank 0 needs no projection factors; nothing to do without heads
     assert call_step(L, cfg(T=1, rank=0, B=0), ub_down=None, ub_up=None) == _lib.CARVE_OK
     assert call_step(L, cfg(T=1, B=0)) == _lib.CARVE_OK
+
+
+BWD_NAMES = ["q", "k", "v", "g", "bx", "w", "ub_down", "ub_up", "state_in", "mean_in", "d_o", "d_state_out",
+             "d_mean_out", "dq", "dk", "dv", "dg", "dbx", "dw", "d_ub_down", "d_ub_up", "d_state_in", "d_mean_in",
+             "workspace"]
+
+
+def call_bwd(L, c, ws_bytes=None, **ptrs):
+    step = 1 << 24
+    base = {n: FAKE + i * step for i, n in enumerate(BWD_NAMES)}
+    base.update(ptrs)
+    if ws_bytes is None:
+        out = _lib.CarveShapes()
+        ok = c is not None and L.carve_recurrent_ref_shapes(ctypes.byref(c), ctypes.byref(out)) == _lib.CARVE_OK
+        ws_bytes = out.bwd_workspace_bytes if ok else 0
+    args = [ctypes.c_void_p(base[n]) if base[n] is not None else None for n in BWD_NAMES]
+    return L.carve_chunk_bwd(ctypes.byref(c) if c is not None else None, *args, ctypes.c_size_t(ws_bytes), None)
+
+
+def test_bwd_workspace_size():
+    """The backward workspace holds, per (batch, head), the fp32 state at every
+    chunk start and one chunk's per-token states, plus small per-chunk vectors."""
+    sh = _lib.ref_shapes(cfg())                      # B2 H3 T100 d64 L64 rank 4: two chunks
+    per_bh = 2 * 64 * 64 + 64 * 64 * 64 + 2 * 2 * 64 + 2 * 4 + 2 * 4 * 64
+    assert sh.bwd_workspace_bytes == 6 * 4 * ((per_bh + 3) // 4 * 4)
+    assert _lib.ref_shapes(cfg(B=0)).bwd_workspace_bytes == 0
+
+
+def test_bwd_argument_errors(L):
+    c = cfg()
+    assert call_bwd(L, None) == _lib.CARVE_EINVAL
+    for n in ("q", "d_o", "dq", "dk", "dv", "dg", "dbx", "dw", "d_ub_down", "d_ub_up", "ub_up"):
+        assert call_bwd(L, c, **{n: None}) == _lib.CARVE_EINVAL, n
+    assert call_bwd(L, c, dk=FAKE + 14 * (1 << 24) + 4) == _lib.CARVE_EALIGN
+    assert call_bwd(L, c, d_mean_in=FAKE + 22 * (1 << 24) + 8) == _lib.CARVE_EALIGN
+    assert call_bwd(L, c, ws_bytes=_lib.ref_shapes(c).bwd_workspace_bytes - 16) == _lib.CARVE_EWORKSPACE
+    assert call_bwd(L, c, dq=FAKE + 64) == _lib.CARVE_EINVAL                        # dq overlaps q
+    assert call_bwd(L, c, dk=FAKE + 23 * (1 << 24) + 4096) == _lib.CARVE_EINVAL     # dk inside the workspace
+    assert call_bwd(L, c, dv=FAKE + 10 * (1 << 24) + 16) == _lib.CARVE_EINVAL       # dv overlaps d_o
+    # d_state_in may be d_state_out itself, but not a shifted view of it
+    assert call_bwd(L, c, d_state_in=FAKE + 11 * (1 << 24) + 16) == _lib.CARVE_EINVAL
+    assert call_bwd(L, cfg(dk=96, dv=96)) == _lib.CARVE_EUNSUPPORTED
+    assert call_bwd(L, cfg(flags=4)) == _lib.CARVE_EINVAL
+    # nothing to compute and no projection: no HIP call, success
+    assert call_bwd(L, cfg(B=0, rank=0), ub_down=None, ub_up=None, d_ub_down=None, d_ub_up=None) == _lib.CARVE_OK

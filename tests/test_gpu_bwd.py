@@ -1,0 +1,173 @@
+"""Parity of the HIP backward pass (carve_chunk_bwd) against the float64
+oracle's adjoint (carve_backward, itself pinned by finite differences of the
+forward pass), through the C ABI.
+
+Error metric (per gradient tensor): max |x - ref| / max |ref|, with the bars
+of the forward pass (1e-4 for fp32 inputs, 2e-2 for bf16 inputs). The
+kernels compute in fp32 throughout; bf16 gradients are rounded once on store.
+"""
+import numpy as np
+import pytest
+
+from chunk_gated_delta_carve_amd.workloads import WORKLOADS, make_inputs, to_f64, to_torch
+from oracle import carve_backward, decay_from_logits, sigmoid
+
+pytestmark = pytest.mark.gpu
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+KEYS = ("q", "k", "v", "g", "bx", "w")
+NAMES = {"dq": "dq", "dk": "dk", "dv": "dv", "dg": "dg", "dbx": "dbx", "dw": "dw", "dub_down": "dU_down",
+         "dub_up": "dU_up", "d_state_in": "dstate_in", "d_mean_in": "dmean_in"}
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def rel_err(x, ref):
+    return float(np.abs(x - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    from chunk_gated_delta_carve_amd import _lib
+    _lib.lib()                                   # loud failure if the library is missing
+    return torch
+
+
+def workload(name, dtype, B, H, T, d, L, rank, seed):
+    return WORKLOADS["tiny"].with_(name=name, dtype=dtype, B=B, H=H, T=T, dk=d, dv=d, L=L, rank=rank,
+                                   ub_std=0.5, seed=seed)
+
+
+def cotangents(B, H, T, d, dtype, seed, with_state=True):
+    """Seeded output gradients: d_o in the input dtype, d_state_out and
+    d_mean_out in fp32 (None without state), and the initial state and mean."""
+    from chunk_gated_delta_carve_amd.workloads import bf16_bits_from_f32
+    rng = np.random.default_rng(seed)
+    do = rng.standard_normal((B, T, H, d)).astype(np.float32)
+    do = do if dtype == "f32" else bf16_bits_from_f32(do)
+    if not with_state:
+        return do, None, None, None, None
+    f = lambda *s: (0.3 * rng.standard_normal(s)).astype(np.float32)
+    return do, f(B, H, d, d), f(B, H, d), f(B, H, d, d), f(B, H, d)
+
+
+def bwd_gpu(torch, inp, dtype, L, do, dSo, dmo, S_in, m_in, logits=False, alias=False):
+    from chunk_gated_delta_carve_amd import chunk_bwd
+    t = {k: to_torch(v, dtype) for k, v in inp.items()}
+    cu = lambda x: None if x is None else torch.from_numpy(x).cuda()
+    dSo_t, dmo_t = cu(dSo), cu(dmo)
+    out = chunk_bwd(*(t[k] for k in KEYS), to_torch(do, dtype), L=L, ub_down=t.get("U_down"), ub_up=t.get("U_up"),
+                    state_in=cu(S_in), mean_in=cu(m_in), d_state_out=dSo_t, d_mean_out=dmo_t, decay_logits=logits,
+                    d_state_in=dSo_t if alias else None, d_mean_in=dmo_t if alias else None)
+    torch.cuda.synchronize()
+    return {n: None if x is None else x.float().cpu().numpy() for n, x in out.items()}
+
+
+def bwd_oracle(inp, dtype, L, do, dSo, dmo, S_in, m_in, logits=False):
+    f = lambda key: to_f64(inp[key], dtype)
+    g = f("g")
+    if logits:
+        g = decay_from_logits(g)
+    ref = carve_backward(f("q"), f("k"), f("v"), g, f("bx"), f("w"), L, to_f64(do, dtype),
+                         f("U_down") if "U_down" in inp else None, f("U_up") if "U_up" in inp else None,
+                         None if S_in is None else S_in.astype(np.float64),
+                         None if m_in is None else m_in.astype(np.float64),
+                         None if dSo is None else dSo.astype(np.float64),
+                         None if dmo is None else dmo.astype(np.float64))
+    if logits:                                   # d/da of g = -softplus(a) is -sigmoid(a)
+        ref["dg"] = ref["dg"] * -sigmoid(f("g"))
+    return ref
+
+
+def assert_grads(got, ref, tol, what):
+    errs = {}
+    for n, rn in NAMES.items():
+        if ref[rn] is None:
+            assert got[n] is None, f"{what}: {n} should be absent"
+            continue
+        x = got[n]
+        assert np.all(np.isfinite(x)), f"{what}: non-finite {n}"
+        errs[n] = rel_err(x, ref[rn])
+    say(f"{what}: " + ", ".join(f"{n} {e:.2e}" for n, e in errs.items()))
+    for n, e in errs.items():
+        assert e <= tol, f"{what}: {n} rel err {e:.3e} > {tol}"
+
+
+BWD_CASES = [
+    # name, dtype, B, H, T, d, L, rank
+    ("f32-d64-L16-r8-ragged-75", "f32", 1, 2, 75, 64, 16, 8),
+    ("f32-d128-L32-r4", "f32", 1, 2, 64, 128, 32, 4),
+    ("f32-d64-L64-r0-ragged-130", "f32", 2, 2, 130, 64, 64, 0),
+    ("bf16-d64-L64-r0", "bf16", 2, 3, 192, 64, 64, 0),
+    ("bf16-d128-L128-r16-ragged-150", "bf16", 1, 2, 150, 128, 128, 16),
+    ("bf16-d64-L32-r64-ragged-100", "bf16", 2, 1, 100, 64, 32, 64),
+    ("f32-T1", "f32", 2, 2, 1, 64, 64, 8),
+]
+
+
+@pytest.mark.parametrize("name,dtype,B,H,T,d,L,rank", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_backward_matches_oracle(torch_cuda, name, dtype, B, H, T, d, L, rank):
+    wl = workload(name, dtype, B, H, T, d, L, rank, 6000 + T)
+    say("case", wl)
+    inp = make_inputs(wl)
+    do, dSo, dmo, S_in, m_in = cotangents(B, H, T, d, dtype, 6100 + T)
+    got = bwd_gpu(torch_cuda, inp, dtype, L, do, dSo, dmo, S_in, m_in)
+    assert_grads(got, bwd_oracle(inp, dtype, L, do, dSo, dmo, S_in, m_in), TOL[dtype], name)
+
+
+def test_backward_without_state_gradients(torch_cuda):
+    """No incoming state or mean and no state or mean gradients (the usual
+    training call): absent tensors are zeros on both sides."""
+    wl = workload("plain", "bf16", 2, 2, 256, 64, 64, 8, 6200)
+    inp = make_inputs(wl)
+    do = cotangents(2, 2, 256, 64, "bf16", 6201, with_state=False)[0]
+    got = bwd_gpu(torch_cuda, inp, "bf16", 64, do, None, None, None, None)
+    assert_grads(got, bwd_oracle(inp, "bf16", 64, do, None, None, None, None), TOL["bf16"], "no state")
+
+
+def test_backward_with_decay_logits(torch_cuda):
+    """Raw decay logits: dg is the gradient of the logit a, dg_g * (-sigmoid(a))."""
+    wl = workload("logits", "f32", 1, 2, 96, 64, 32, 8, 6300)
+    inp = make_inputs(wl, decay_logits=True)
+    do, dSo, dmo, S_in, m_in = cotangents(1, 2, 96, 64, "f32", 6301)
+    got = bwd_gpu(torch_cuda, inp, "f32", 32, do, dSo, dmo, S_in, m_in, logits=True)
+    assert_grads(got, bwd_oracle(inp, "f32", 32, do, dSo, dmo, S_in, m_in, logits=True), TOL["f32"], "logits")
+
+
+def test_backward_in_place_state_gradients(torch_cuda):
+    """d_state_in and d_mean_in written over d_state_out and d_mean_out."""
+    wl = workload("alias", "f32", 2, 2, 80, 64, 16, 4, 6400)
+    inp = make_inputs(wl)
+    do, dSo, dmo, S_in, m_in = cotangents(2, 2, 80, 64, "f32", 6401)
+    ref = bwd_oracle(inp, "f32", 16, do, dSo, dmo, S_in, m_in)
+    got = bwd_gpu(torch_cuda, inp, "f32", 16, do, dSo.copy(), dmo.copy(), S_in, m_in, alias=True)
+    assert_grads(got, ref, TOL["f32"], "in place")
+
+
+def test_backward_empty_sequence(torch_cuda):
+    """T = 0: the state and mean gradients pass through; the projection gets zeros."""
+    torch = torch_cuda
+    from chunk_gated_delta_carve_amd import chunk_bwd
+    B, H, d, r = 2, 3, 64, 4
+    z = lambda *s: torch.zeros(*s, device="cuda", dtype=torch.bfloat16)
+    dSo = torch.randn(B, H, d, d, device="cuda")
+    dmo = torch.randn(B, H, d, device="cuda")
+    out = chunk_bwd(z(B, 0, H, d), z(B, 0, H, d), z(B, 0, H, d), z(B, 0, H, d), z(B, 0, H, d), z(B, 0, H),
+                    z(B, 0, H, d), L=64, ub_down=z(H, r, d), ub_up=z(H, d, r), d_state_out=dSo, d_mean_out=dmo)
+    torch.cuda.synchronize()
+    assert torch.equal(out["d_state_in"], dSo) and torch.equal(out["d_mean_in"], dmo)
+    assert not out["dub_down"].any() and not out["dub_up"].any()
+
+
+def test_backward_deterministic(torch_cuda):
+    wl = workload("det", "bf16", 2, 2, 200, 64, 64, 16, 6500)
+    inp = make_inputs(wl)
+    do, dSo, dmo, S_in, m_in = cotangents(2, 2, 200, 64, "bf16", 6501)
+    a = bwd_gpu(torch_cuda, inp, "bf16", 64, do, dSo, dmo, S_in, m_in)
+    b = bwd_gpu(torch_cuda, inp, "bf16", 64, do, dSo, dmo, S_in, m_in)
+    for n in a:
+        if a[n] is not None:
+            assert np.array_equal(a[n], b[n]), n
