@@ -363,7 +363,9 @@ def bench_backward(args, wl):
                    "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "L": L, "rank": rank,
                    "decay_input": "raw logits, -softplus in-kernel" if args.decay_logits else "log-decay g"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "carve_bwd_kernel",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": ("carve_bwd_split_kernel + carve_bwd_finish_kernel (one call)" if rank == 0
+                                else "carve_bwd_kernel + carve_bwd_ub_kernel (one call)"),
                      "kernel_ms": kernel_ms, "algorithmic_bytes_per_launch": alg},
     }
     if not args.no_cpu_baseline and not args.decay_logits:

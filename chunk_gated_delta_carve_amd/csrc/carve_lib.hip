@@ -148,6 +148,21 @@ hipError_t dispatch_fwd(const carve_config* cfg, const carve::FwdArgs& a, hipStr
 
 template <typename E, int D, bool LG>
 hipError_t launch_bwd(const carve::BwdArgs& a, hipStream_t s) {
+  if (a.rank == 0) {
+    // row-sliced schedule, then the sum over the slices
+    using SL = carve::SplitLayout<D>;
+    constexpr auto split = carve::carve_bwd_split_kernel<E, D, LG>;
+    hipError_t e = set_lds<split>(SL::bytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(split, dim3(a.B * a.H * SL::S), dim3(SL::NT), SL::bytes, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t n = (size_t)a.B * a.T * a.H * D;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL((carve::carve_bwd_finish_kernel<E, D, LG>), dim3((unsigned)((n + 255) / 256)), dim3(256),
+                       0, s, a);
+    return hipGetLastError();
+  }
   using LY = carve::BwdLayout<D>;
   constexpr auto kern = carve::carve_bwd_kernel<E, D, LG>;
   hipError_t e = set_lds<kern>(LY::bytes);

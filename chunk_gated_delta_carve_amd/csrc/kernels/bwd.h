@@ -51,8 +51,11 @@ struct BwdArgs {
 // Workspace of one (batch, head), in floats: the chunk checkpoints and the
 // recomputed states of one chunk first (16-byte aligned), then the per-chunk
 // gate vectors and the projection factors' partial gradients.
+// Without a projection (rank 0) the row-sliced schedule also keeps, per
+// token and row slice, the slice's column sums (4 D floats) and its share of
+// dw, for the kernel that adds up the slices.
 struct BwdWs {
-  size_t ckpt, sbuf, z, m, y, dud, duu, total;
+  size_t ckpt, sbuf, z, m, y, dud, duu, part, wpart, total;
   __host__ __device__ BwdWs(int D, int T, int L, int rank) {
     const size_t nc = (size_t)(T + L - 1) / L, DD = (size_t)D * D;
     ckpt = 0;
@@ -62,7 +65,10 @@ struct BwdWs {
     y = m + nc * D;
     dud = y + nc * rank;
     duu = dud + (size_t)rank * D;
-    total = (duu + (size_t)D * rank + 3) & ~(size_t)3;
+    part = (duu + (size_t)D * rank + 3) & ~(size_t)3;
+    const size_t slices = rank == 0 ? (size_t)D / 16 : 0;
+    wpart = part + (size_t)T * slices * 4 * D;
+    total = (wpart + (size_t)T * slices + 3) & ~(size_t)3;
   }
 };
 
@@ -85,6 +91,17 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
+// Workgroup barrier that orders LDS only: this wave's LDS operations complete
+// and become visible to the workgroup, while its global loads (prefetches)
+// and stores stay in flight. No thread here passes global data to another
+// thread of its workgroup (each reads back only what it wrote itself), so
+// the kernel's barriers need no more than this.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <int D>
 struct BwdLayout {
   static constexpr int NT = 4 * D, NW = NT / 64, CW = D / 4;
@@ -92,9 +109,16 @@ struct BwdLayout {
   // PPW partial rows (4 with two DPP steps, 2 with the extra pair step)
   static constexpr int PPW = D == 64 ? 4 : 2;
   static constexpr int NP = NW * PPW;
+  // tokens staged per LDS block (a divisor of every chunk length), and the
+  // (token, channel) elements each thread stages
+  static constexpr int NB = D == 64 ? 16 : 8;
+  static constexpr int EPT = NB * D / NT;
+  // tokens ahead that the states before a token are loaded (register ring
+  // of PD + 1 sets; two ahead where the registers allow it)
+  static constexpr int PD = D == 64 ? 2 : 1;
   static constexpr int TOKF = 6 * D + 4;              // q, k, dec, b, v, dout, w (+pad)
-  static constexpr int oTok = 0;                      // 3 token buffers
-  static constexpr int oPart = oTok + 3 * TOKF;       // 2 x [NP][4][D]
+  static constexpr int oBlk = 0;                      // 2 x [NB][TOKF] token blocks
+  static constexpr int oPart = oBlk + 2 * NB * TOKF;  // 2 x [NP][4][D]
   static constexpr int oWp = oPart + 2 * NP * 4 * D;  // 2 x [16] dw partials
   static constexpr int oZ = oWp + 32;                 // gate bias z of the chunk
   static constexpr int oM = oZ + D;                   // gate mean m_{c-1} of the chunk
@@ -106,13 +130,14 @@ struct BwdLayout {
   static constexpr int floats = oDy + 64;
   static constexpr int bytes = floats * 4;
   static_assert(TOKF % 4 == 0 && oPart % 4 == 0, "16-byte aligned LDS arrays");
+  static_assert(EPT * NT == NB * D && NB <= 16, "whole staging shares");
 };
 
 template <typename E, int D, bool kLogits>
 __global__ void __launch_bounds__(4 * D)
 carve_bwd_kernel(BwdArgs a) {
   using LY = BwdLayout<D>;
-  constexpr int NT = LY::NT, CW = LY::CW, NP = LY::NP, TOKF = LY::TOKF;
+  constexpr int NT = LY::NT, CW = LY::CW, NP = LY::NP, TOKF = LY::TOKF, NB = LY::NB, EPT = LY::EPT;
   constexpr size_t DD = (size_t)D * D;
   extern __shared__ __align__(16) float lds[];
   float* part0 = lds + LY::oPart;
@@ -143,22 +168,46 @@ carve_bwd_kernel(BwdArgs a) {
   const E* Ud = static_cast<const E*>(a.ub_down) + (size_t)h * rank * D;   // [rank][D]
   const E* Uu = static_cast<const E*>(a.ub_up) + (size_t)h * D * rank;     // [D][rank]
   auto tok_at = [&](int t) { return ((size_t)bi * T + t) * H + h; };      // row of [B, T, H, .]
-  auto tokbuf = [&](int i) { return lds + LY::oTok + (i % 3) * TOKF; };
+  auto blockbuf = [&](int i) { return lds + LY::oBlk + (i & 1) * NB * TOKF; };
 
-  // the token's vectors into an LDS buffer (threads d < D): q, k, the decay
-  // factor, the erase gate b (with this chunk's z), v, and with `grad` the
-  // total output gradient dout = do + dm_c / n_c
-  auto stage = [&](float* tb, int t, bool grad) {
-    if (tid < D) {
-      const size_t off = tok_at(t) * D + tid;
-      tb[tid] = to_f32(Q[off]);
-      tb[D + tid] = to_f32(K[off]);
-      tb[2 * D + tid] = fast_exp2(decay_log2<kLogits>(to_f32(G[off])));
-      tb[3 * D + tid] = sigmoid_f(to_f32(BX[off]) + zs[tid]);
-      tb[4 * D + tid] = to_f32(V[off]);
-      if (grad) tb[5 * D + tid] = to_f32(DO[off]) + dmcs[tid];
+  // Token blocks: nb <= NB consecutive tokens from tb0, staged into LDS as
+  // [token][q | k | dec | b | v | dout | w]. Loading (raw values into
+  // registers) is split from storing (decay factor and erase gate formed, the
+  // chunk's dm_c / n_c added to do) so the next block's loads overlap the
+  // current block's work. Element r of a thread is (token, channel) =
+  // divmod(tid + r NT, D).
+  struct Staged { float q[EPT], k[EPT], g[EPT], bx[EPT], v[EPT], dout[EPT], w; };
+  auto load_block = [&](Staged& st, int tb0, int nb, bool grad) {
+#pragma unroll
+    for (int r = 0; r < EPT; ++r) {
+      const int idx = tid + r * NT, j = idx / D, d = idx % D;
+      if (j < nb) {
+        const size_t off = tok_at(tb0 + j) * D + d;
+        st.q[r] = to_f32(Q[off]);
+        st.k[r] = to_f32(K[off]);
+        st.g[r] = to_f32(G[off]);
+        st.bx[r] = to_f32(BX[off]);
+        st.v[r] = to_f32(V[off]);
+        st.dout[r] = grad ? to_f32(DO[off]) : 0.f;
+      }
     }
-    if (tid == 0) tb[6 * D] = to_f32(W[tok_at(t)]);
+    if (tid < nb) st.w = to_f32(W[tok_at(tb0 + tid)]);
+  };
+  auto store_block = [&](float* buf, const Staged& st, int nb) {
+#pragma unroll
+    for (int r = 0; r < EPT; ++r) {
+      const int idx = tid + r * NT, j = idx / D, d = idx % D;
+      if (j < nb) {
+        float* tb = buf + j * TOKF;
+        tb[d] = st.q[r];
+        tb[D + d] = st.k[r];
+        tb[2 * D + d] = fast_exp2(decay_log2<kLogits>(st.g[r]));
+        tb[3 * D + d] = sigmoid_f(st.bx[r] + zs[d]);
+        tb[4 * D + d] = st.v[r];
+        tb[5 * D + d] = st.dout[r] + dmcs[d];
+      }
+    }
+    if (tid < nb) buf[tid * TOKF + 6 * D] = st.w;
   };
 
   // the content gate of a chunk from the mean in ms: ys = U_down m, zs = U_up ys
@@ -180,25 +229,44 @@ carve_bwd_kernel(BwdArgs a) {
 
   // one token of the forward recurrence on this lane's row segment
   auto advance = [&](f32x4 (&s)[CW / 4], const float* tb) {
-    const float* tq = tb;
     const float* tk = tb + D;
     const float* td = tb + 2 * D;
     const float* tbb = tb + 3 * D;
-    float pr = 0.f;
+    f32x4 pr = zero4();                              // four independent partial sums
 #pragma unroll
     for (int j = 0; j < CW / 4; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = c0 + 4 * j + i;
         s[j][i] *= td[c];
-        pr += s[j][i] * (tbb[c] * tk[c]);
+        pr[i] += s[j][i] * (tbb[c] * tk[c]);
       }
-    (void)tq;
-    const float delta = tb[6 * D] * tb[4 * D + e] - quad_sum(pr);
+    const float delta = tb[6 * D] * tb[4 * D + e] - quad_sum((pr[0] + pr[1]) + (pr[2] + pr[3]));
 #pragma unroll
     for (int j = 0; j < CW / 4; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) s[j][i] += delta * tk[c0 + 4 * j + i];
+  };
+
+  // Forward over the tokens [t0, t1) of one chunk from the state in s, block
+  // by block; `per_token(t, tb)` runs before each token's update.
+  Staged st;
+  auto sweep = [&](f32x4 (&s)[CW / 4], int t0, int t1, auto per_token) {
+    const int nblk = (t1 - t0 + NB - 1) / NB;
+    load_block(st, t0, min(NB, t1 - t0), false);
+    store_block(blockbuf(0), st, min(NB, t1 - t0));
+    lds_barrier();
+    for (int jb = 0; jb < nblk; ++jb) {
+      const int tb0 = t0 + jb * NB, nb = min(NB, t1 - tb0);
+      const float* buf = blockbuf(jb);
+      if (jb + 1 < nblk) load_block(st, tb0 + NB, min(NB, t1 - tb0 - NB), false);
+      for (int j = 0; j < nb; ++j) {
+        per_token(tb0 + j, buf + j * TOKF);
+        advance(s, buf + j * TOKF);
+      }
+      if (jb + 1 < nblk) store_block(blockbuf(jb + 1), st, min(NB, t1 - tb0 - NB));
+      lds_barrier();
+    }
   };
 
   // ---------------------------------------------------------------- forward sweep
@@ -211,6 +279,7 @@ carve_bwd_kernel(BwdArgs a) {
   if (tid < D) {
     ms[tid] = a.mean_in ? a.mean_in[(size_t)bh * D + tid] : 0.f;
     zs[tid] = 0.f;
+    dmcs[tid] = 0.f;
   }
   // the projection factors' partial gradients of this (batch, head) start at
   // zero; each element is cleared and later updated by the same thread
@@ -218,7 +287,7 @@ carve_bwd_kernel(BwdArgs a) {
     ws[lay.dud + idx] = 0.f;
     ws[lay.duu + idx] = 0.f;
   }
-  __syncthreads();
+  lds_barrier();
   for (int c = 0; c < nc; ++c) {
     const int t0 = c * L, t1 = min(T, t0 + L);
     float* ck = ws + lay.ckpt + (size_t)c * DD + (size_t)e * D + c0;
@@ -231,14 +300,10 @@ carve_bwd_kernel(BwdArgs a) {
         ws[lay.m + (size_t)c * D + tid] = ms[tid];
       }
       if (tid < rank) ws[lay.y + (size_t)c * rank + tid] = ys[tid];
-      __syncthreads();
+      lds_barrier();
     }
-    stage(tokbuf(0), t0, false);
-    __syncthreads();
     float acc = 0.f;
-    for (int t = t0; t < t1; ++t) {
-      const float* tb = tokbuf(t - t0);
-      if (t + 1 < t1) stage(tokbuf(t - t0 + 1), t + 1, false);
+    sweep(s, t0, t1, [&](int, const float* tb) {
       if (content) {                                 // o_t = S_{t-1} q_t feeds the chunk mean
         float po = 0.f;
 #pragma unroll
@@ -247,11 +312,9 @@ carve_bwd_kernel(BwdArgs a) {
           for (int i = 0; i < 4; ++i) po += s[j][i] * tb[c0 + 4 * j + i];
         acc += quad_sum(po);
       }
-      advance(s, tb);
-      __syncthreads();
-    }
+    });
     if (content && seg == 0) ms[e] = acc / (float)(t1 - t0);
-    __syncthreads();
+    lds_barrier();
   }
 
   // ---------------------------------------------------------------- reverse sweep
@@ -262,20 +325,18 @@ carve_bwd_kernel(BwdArgs a) {
     for (int j = 0; j < CW / 4; ++j) ds[j] = dso ? reinterpret_cast<const f32x4*>(dso)[j] : zero4();
   }
   if (tid < D) dms[tid] = 0.f;
-  __syncthreads();
+  lds_barrier();
   const int ro = tid / D, rcol = tid % D;            // this thread's output: dk, dbx, dg or dq of column rcol
   float* sbuf = ws + lay.sbuf + (size_t)e * D + c0;
   for (int c = nc - 1; c >= 0; --c) {
     const int t0 = c * L, t1 = min(T, t0 + L), n = t1 - t0;
     if (tid < D) {
-      float dm = dms[tid];
-      if (c == nc - 1 && a.d_mean_out) dm += a.d_mean_out[(size_t)bh * D + tid];
-      dmcs[tid] = dm / (float)n;
       zs[tid] = content ? ws[lay.z + (size_t)c * D + tid] : 0.f;
       if (content) ms[tid] = ws[lay.m + (size_t)c * D + tid];
+      dmcs[tid] = 0.f;                                // the recompute stages no output gradient
     }
     if (tid < rank) ys[tid] = ws[lay.y + (size_t)c * rank + tid];
-    __syncthreads();
+    lds_barrier();
 
     // states before each token of the chunk, from its checkpoint
     {
@@ -283,56 +344,66 @@ carve_bwd_kernel(BwdArgs a) {
 #pragma unroll
       for (int j = 0; j < CW / 4; ++j) s[j] = reinterpret_cast<const f32x4*>(ck)[j];
     }
-    stage(tokbuf(0), t0, false);
-    __syncthreads();
-    for (int t = t0; t < t1; ++t) {
+    sweep(s, t0, t1, [&](int t, const float*) {
       float* sb = sbuf + (size_t)(t - t0) * DD;
 #pragma unroll
       for (int j = 0; j < CW / 4; ++j) reinterpret_cast<f32x4*>(sb)[j] = s[j];
-      const float* tb = tokbuf(t - t0);
-      if (t + 1 < t1) stage(tokbuf(t - t0 + 1), t + 1, false);
-      advance(s, tb);
-      __syncthreads();
+    });
+    if (tid < D) {
+      float dm = dms[tid];
+      if (c == nc - 1 && a.d_mean_out) dm += a.d_mean_out[(size_t)bh * D + tid];
+      dmcs[tid] = dm / (float)n;
     }
+    lds_barrier();
 
-    // backward through the chunk's tokens
-    stage(tokbuf(0), t1 - 1, true);
-    f32x4 sp[CW / 4];
+    // backward through the chunk's tokens: blocks of NB from the last, each
+    // from its last token. The states before the tokens come from the
+    // workspace through a ring of PD + 1 register sets, each load issued PD
+    // tokens before its use; the loop is unrolled over the ring so every set
+    // keeps a fixed register name while its load is in flight.
+    const int nblk = (n + NB - 1) / NB;
     {
-      const float* sb = sbuf + (size_t)(n - 1) * DD;
-#pragma unroll
-      for (int j = 0; j < CW / 4; ++j) sp[j] = reinterpret_cast<const f32x4*>(sb)[j];
+      const int tb0 = t0 + (nblk - 1) * NB, nb = t1 - tb0;
+      load_block(st, tb0, nb, true);
+      store_block(blockbuf(0), st, nb);
     }
-    __syncthreads();
+    constexpr int PD = LY::PD, RING = PD + 1;
+    f32x4 ring[RING][CW / 4];
+    auto load_state = [&](f32x4 (&dst)[CW / 4], int t) {
+      const float* sb = sbuf + (size_t)(t - t0) * DD;
+#pragma unroll
+      for (int jj = 0; jj < CW / 4; ++jj) dst[jj] = reinterpret_cast<const f32x4*>(sb)[jj];
+    };
+#pragma unroll
+    for (int k = 0; k < PD; ++k)
+      if (k < n) load_state(ring[k], t1 - 1 - k);
+    lds_barrier();
     float dz = 0.f;
-    for (int i = 0; i < n; ++i) {
+
+    auto step = [&](int i, const f32x4 (&sp)[CW / 4], f32x4 (&nxt)[CW / 4]) {
       const int t = t1 - 1 - i;
-      const float* tb = tokbuf(i);
+      const int jb = (t - t0) / NB, tb0 = t0 + jb * NB, j = t - tb0, kb = nblk - 1 - jb;
+      if (t - PD >= t0) load_state(nxt, t - PD);
+      if (t == min(tb0 + NB, t1) - 1 && jb > 0) load_block(st, tb0 - NB, NB, true);
+      const float* tb = blockbuf(kb) + j * TOKF;
       float* pb = part0 + (i & 1) * NP * 4 * D;
       float* wpb = wp0 + (i & 1) * 16;
-      f32x4 spn[CW / 4];
-      if (i + 1 < n) {
-        const float* sb = sbuf + (size_t)(n - 2 - i) * DD;
-#pragma unroll
-        for (int j = 0; j < CW / 4; ++j) spn[j] = reinterpret_cast<const f32x4*>(sb)[j];
-        stage(tokbuf(i + 1), t - 1, true);
-      }
       const float* tq = tb;
       const float* tk = tb + D;
       const float* td = tb + 2 * D;
       const float* tbb = tb + 3 * D;
       const float wt = tb[6 * D], dout = tb[5 * D + e];
-      float pr = 0.f, pdd = 0.f;
+      f32x4 pr4 = zero4(), pdd4 = zero4();           // four independent partial sums each
 #pragma unroll
-      for (int j = 0; j < CW / 4; ++j)
+      for (int jj = 0; jj < CW / 4; ++jj)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-          const int cc = c0 + 4 * j + ii;
-          pr += sp[j][ii] * td[cc] * (tbb[cc] * tk[cc]);
-          pdd += ds[j][ii] * tk[cc];
+          const int cc = c0 + 4 * jj + ii;
+          pr4[ii] += sp[jj][ii] * td[cc] * (tbb[cc] * tk[cc]);
+          pdd4[ii] += ds[jj][ii] * tk[cc];
         }
-      const float delta = wt * tb[4 * D + e] - quad_sum(pr);
-      const float ddelta = quad_sum(pdd);
+      const float delta = wt * tb[4 * D + e] - quad_sum((pr4[0] + pr4[1]) + (pr4[2] + pr4[3]));
+      const float ddelta = quad_sum((pdd4[0] + pdd4[1]) + (pdd4[2] + pdd4[3]));
       const float dr = -ddelta;
       if (seg == 0) static_cast<E*>(a.dv)[tok_at(t) * D + e] = from_f32<E>(wt * ddelta);
       // dw: sum over the rows of d delta * v
@@ -344,19 +415,19 @@ carve_bwd_kernel(BwdArgs a) {
       // column partials of dS^T delta, S'^T dr, dS' * S' and S^T dout, four
       // columns at a time, summed over this wave's rows
 #pragma unroll
-      for (int j = 0; j < CW / 4; ++j) {
+      for (int jj = 0; jj < CW / 4; ++jj) {
         f32x4 p1, p2, p3, p4;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-          const int cc = c0 + 4 * j + ii;
+          const int cc = c0 + 4 * jj + ii;
           const float dec = td[cc];
-          const float sd = sp[j][ii] * dec;
-          const float dsd = ds[j][ii] + dr * (tbb[cc] * tk[cc]);
-          p1[ii] = ds[j][ii] * delta;
+          const float sd = sp[jj][ii] * dec;
+          const float dsd = ds[jj][ii] + dr * (tbb[cc] * tk[cc]);
+          p1[ii] = ds[jj][ii] * delta;
           p2[ii] = sd * dr;
           p3[ii] = dsd * sd;
-          p4[ii] = sp[j][ii] * dout;
-          ds[j][ii] = dsd * dec + dout * tq[cc];
+          p4[ii] = sp[jj][ii] * dout;
+          ds[jj][ii] = dsd * dec + dout * tq[cc];
         }
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
@@ -375,37 +446,37 @@ carve_bwd_kernel(BwdArgs a) {
         const bool writer = LY::PPW == 4 ? (lane & 12) == 0 : (lane & 28) == 0;
         if (writer) {
           const int p = wave * LY::PPW + (LY::PPW == 4 ? (lane >> 4) : (lane >> 5));
-          float* dst = pb + (size_t)p * 4 * D + c0 + 4 * j;
+          float* dst = pb + (size_t)p * 4 * D + c0 + 4 * jj;
           *reinterpret_cast<f32x4*>(dst) = p1;
           *reinterpret_cast<f32x4*>(dst + D) = p2;
           *reinterpret_cast<f32x4*>(dst + 2 * D) = p3;
           *reinterpret_cast<f32x4*>(dst + 3 * D) = p4;
         }
       }
-      __syncthreads();
+      lds_barrier();
       // finish the column sums: thread (ro, rcol) forms one output element
       {
-        float P = 0.f, P2 = 0.f;
-        const int qsel = ro == 0 ? 0 : ro == 1 ? 1 : ro;   // dk: P1 (+ P2), dbx: P2, dg: P3, dq: P4
+        f32x4 P = zero4(), P2 = zero4();
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-          P += pb[(size_t)p * 4 * D + qsel * D + rcol];
-          if (ro == 0) P2 += pb[(size_t)p * 4 * D + D + rcol];
+          P[p & 3] += pb[(size_t)p * 4 * D + ro * D + rcol];
+          if (ro == 0) P2[p & 3] += pb[(size_t)p * 4 * D + D + rcol];
         }
+        const float Ps = (P[0] + P[1]) + (P[2] + P[3]);
         const size_t off = tok_at(t) * D + rcol;
         const float b = tbb[rcol], kk = tk[rcol];
-        if (ro == 0) {
-          static_cast<E*>(a.dk)[off] = from_f32<E>(P + P2 * b);
-        } else if (ro == 1) {
-          const float dbx = P * kk * b * (1.f - b);
+        if (ro == 0) {                                 // dk = dS^T delta + (S'^T dr) b
+          static_cast<E*>(a.dk)[off] = from_f32<E>(Ps + ((P2[0] + P2[1]) + (P2[2] + P2[3])) * b);
+        } else if (ro == 1) {                          // dbx = (S'^T dr) k b (1 - b)
+          const float dbx = Ps * kk * b * (1.f - b);
           static_cast<E*>(a.dbx)[off] = from_f32<E>(dbx);
           dz += dbx;
         } else if (ro == 2) {
           // dg, or with raw logits a (g = -softplus(a)) da = dg (e^g - 1)
-          const float dg = kLogits ? P * (td[rcol] - 1.f) : P;
+          const float dg = kLogits ? Ps * (td[rcol] - 1.f) : Ps;
           static_cast<E*>(a.dg)[off] = from_f32<E>(dg);
-        } else {
-          static_cast<E*>(a.dq)[off] = from_f32<E>(P);
+        } else {                                       // dq = S^T dout
+          static_cast<E*>(a.dq)[off] = from_f32<E>(Ps);
         }
         if (tid == 0) {
           float dw = 0.f;
@@ -414,16 +485,23 @@ carve_bwd_kernel(BwdArgs a) {
           static_cast<E*>(a.dw)[tok_at(t)] = from_f32<E>(dw);
         }
       }
-      if (i + 1 < n) {
-#pragma unroll
-        for (int j = 0; j < CW / 4; ++j) sp[j] = spn[j];
+      if (j == 0 && jb > 0) {                          // the block's last token: stage the next block
+        store_block(blockbuf(kb + 1), st, NB);
+        lds_barrier();
+      }
+    };
+    for (int i = 0; i < n; i += RING) {
+      step(i, ring[0], ring[PD % RING]);
+      if (i + 1 < n) step(i + 1, ring[1 % RING], ring[(1 + PD) % RING]);
+      if constexpr (RING > 2) {
+        if (i + 2 < n) step(i + 2, ring[2 % RING], ring[(2 + PD) % RING]);
       }
     }
 
     // the chunk's gate: z = U_up y, y = U_down m_{c-1}
     if (content) {
       if (ro == 1) dzs[rcol] = dz;
-      __syncthreads();
+      lds_barrier();
       const int r = tid >> 2, sub = tid & 3;
       if (r < rank) {
         float p = 0.f;
@@ -433,7 +511,7 @@ carve_bwd_kernel(BwdArgs a) {
       }
       for (int idx = tid; idx < D * rank; idx += NT)       // dU_up[d][i] += dz_d y_i
         ws[lay.duu + idx] += dzs[idx / rank] * ys[idx % rank];
-      __syncthreads();
+      lds_barrier();
       for (int idx = tid; idx < rank * D; idx += NT)       // dU_down[i][e] += dy_i m_e
         ws[lay.dud + idx] += dys[idx / D] * ms[idx % D];
       if (tid < D) {
@@ -441,7 +519,7 @@ carve_bwd_kernel(BwdArgs a) {
         for (int r2 = 0; r2 < rank; ++r2) dm += to_f32(Ud[(size_t)r2 * D + tid]) * dys[r2];
         dms[tid] = dm;
       }
-      __syncthreads();
+      lds_barrier();
     }
   }
 
@@ -456,6 +534,324 @@ carve_bwd_kernel(BwdArgs a) {
     if (nc == 0) dm = a.d_mean_out ? a.d_mean_out[(size_t)bh * D + tid] : 0.f;
     else dm = content ? dms[tid] : 0.f;
     a.d_mean_in[(size_t)bh * D + tid] = dm;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Row-sliced schedule without a content projection. The gates then do not
+// depend on the outputs, so the rows of S (value channels) evolve
+// independently and the adjoint of each row needs only its own row: a head's
+// rows are split into D / 16 slices, one workgroup each, spreading a head
+// over several compute units. Four waves of four rows, sixteen lanes per row,
+// each lane holding CW = D / 16 consecutive columns of S and dS. Row sums are
+// four DPP rotations inside a 16-lane row; the column sums over a wave's four
+// rows are two lane swaps, over the four waves an LDS pass, and over the
+// slices a second kernel (carve_bwd_finish_kernel) that also forms dk, dbx,
+// dg and dq from them.
+template <int D>
+struct SplitLayout {
+  static constexpr int NT = 256, ROWS = 16, S = D / ROWS, CW = D / 16;
+  // tokens per staged block: enough work per block to cover the latency of
+  // the next block's global loads (blocks never cross a chunk boundary; a
+  // chunk shorter than NB makes short blocks); 16 at d = 128, where 32 would
+  // not leave the registers to keep the staged values unspilled
+  static constexpr int NB = D == 64 ? 32 : 16;
+  static constexpr int TOKF = 4 * D + 2 * ROWS + 4;   // q, k, dec, b | v, dout of the slice rows | w
+  static constexpr int EPT = NB * D / NT;             // (token, channel) elements staged per thread
+  static constexpr int PD = 2;                        // states loaded this many tokens ahead
+  static constexpr int oBlk = 0;                      // 2 x [NB][TOKF]
+  static constexpr int oPart = oBlk + 2 * NB * TOKF;  // 2 x [4 waves][4][D]
+  static constexpr int oWp = oPart + 2 * 4 * 4 * D;   // 2 x [4] dw partials
+  static constexpr int floats = oWp + 8;
+  static constexpr int bytes = floats * 4;
+  static_assert(TOKF % 4 == 0 && oPart % 4 == 0 && EPT * NT == NB * D && NB * ROWS % NT == 0 && NB <= NT,
+                "layout");
+};
+
+// sum over the 16 lanes of a DPP row, in every lane of it
+__device__ __forceinline__ float sum_row16(float x) {
+  x += dpp_mov<0x128>(x);   // row_ror:8
+  x += dpp_mov<0x124>(x);   // row_ror:4
+  x += dpp_mov<0x122>(x);   // row_ror:2
+  return x + dpp_mov<0x121>(x);   // row_ror:1
+}
+
+template <typename E, int D, bool kLogits>
+__global__ void __launch_bounds__(256)
+carve_bwd_split_kernel(BwdArgs a) {
+  using LY = SplitLayout<D>;
+  constexpr int NT = LY::NT, CW = LY::CW, NB = LY::NB, TOKF = LY::TOKF, EPT = LY::EPT, S = LY::S;
+  constexpr int ROWS = LY::ROWS, PD = LY::PD, RING = PD + 1;
+  constexpr size_t DD = (size_t)D * D;
+  extern __shared__ __align__(16) float lds[];
+  float* part0 = lds + LY::oPart;
+  float* wp0 = lds + LY::oWp;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int slice = blockIdx.x % S, bh = blockIdx.x / S, bi = bh / a.H, h = bh % a.H;
+  const int rl = wave * 4 + (lane >> 4);              // row within the slice
+  const int e = slice * ROWS + rl, cl = lane & 15, c0 = cl * CW;
+  const int T = a.T, L = a.L, H = a.H;
+  const int nc = (T + L - 1) / L;
+  const BwdWs lay(D, T, L, 0);
+  float* ws = a.ws + (size_t)bh * lay.total;
+  const E* Q = static_cast<const E*>(a.q);
+  const E* K = static_cast<const E*>(a.k);
+  const E* V = static_cast<const E*>(a.v);
+  const E* G = static_cast<const E*>(a.g);
+  const E* BX = static_cast<const E*>(a.bx);
+  const E* W = static_cast<const E*>(a.w);
+  const E* DO = static_cast<const E*>(a.d_o);
+  auto tok_at = [&](int t) { return ((size_t)bi * T + t) * H + h; };
+  auto blockbuf = [&](int i) { return lds + LY::oBlk + (i & 1) * NB * TOKF; };
+
+  // token blocks: [token][q | k | dec | b | v, dout of the slice's rows | w]
+  constexpr int RPT = NB * ROWS / NT;
+  struct Staged { float q[EPT], k[EPT], g[EPT], bx[EPT], v[RPT], dout[RPT], w; };
+  auto load_block = [&](Staged& st, int tb0, int nb, bool grad) {
+#pragma unroll
+    for (int r = 0; r < EPT; ++r) {
+      const int idx = tid + r * NT, j = idx / D, d = idx % D;
+      if (j < nb) {
+        const size_t off = tok_at(tb0 + j) * D + d;
+        st.q[r] = to_f32(Q[off]);
+        st.k[r] = to_f32(K[off]);
+        st.g[r] = to_f32(G[off]);
+        st.bx[r] = to_f32(BX[off]);
+      }
+    }
+#pragma unroll
+    for (int r2 = 0; r2 < RPT; ++r2) {               // NB x ROWS (token, row) pairs, RPT per thread
+      const int idx = tid + r2 * NT, j = idx / ROWS, r = idx % ROWS;
+      if (j < nb) {
+        const size_t off = tok_at(tb0 + j) * D + slice * ROWS + r;
+        st.v[r2] = to_f32(V[off]);
+        st.dout[r2] = grad ? to_f32(DO[off]) : 0.f;
+      }
+    }
+    if (tid < nb) st.w = to_f32(W[tok_at(tb0 + tid)]);
+  };
+  auto store_block = [&](float* buf, const Staged& st, int nb, float dmc) {
+#pragma unroll
+    for (int r = 0; r < EPT; ++r) {
+      const int idx = tid + r * NT, j = idx / D, d = idx % D;
+      if (j < nb) {
+        float* tb = buf + j * TOKF;
+        tb[d] = st.q[r];
+        tb[D + d] = st.k[r];
+        tb[2 * D + d] = fast_exp2(decay_log2<kLogits>(st.g[r]));
+        tb[3 * D + d] = sigmoid_f(st.bx[r]);
+      }
+    }
+#pragma unroll
+    for (int r2 = 0; r2 < RPT; ++r2) {
+      const int idx = tid + r2 * NT, j = idx / ROWS, r = idx % ROWS;
+      if (j < nb) {
+        buf[j * TOKF + 4 * D + r] = st.v[r2];
+        // dout of row r: do plus this row's share of d_mean_out (last chunk)
+        const float dm = dmc != 0.f ? dmc * a.d_mean_out[(size_t)bh * D + slice * ROWS + r] : 0.f;
+        buf[j * TOKF + 4 * D + ROWS + r] = st.dout[r2] + dm;
+      }
+    }
+    if (tid < nb) buf[tid * TOKF + 4 * D + 2 * ROWS] = st.w;
+  };
+  auto advance = [&](float (&s)[CW], const float* tb) {
+    const float* tk = tb + D;
+    const float* td = tb + 2 * D;
+    const float* tbb = tb + 3 * D;
+    float pr = 0.f;
+#pragma unroll
+    for (int j = 0; j < CW; ++j) {
+      s[j] *= td[c0 + j];
+      pr += s[j] * (tbb[c0 + j] * tk[c0 + j]);
+    }
+    const float delta = tb[4 * D + 2 * ROWS] * tb[4 * D + rl] - sum_row16(pr);
+#pragma unroll
+    for (int j = 0; j < CW; ++j) s[j] += delta * tk[c0 + j];
+  };
+  Staged st;
+  auto sweep = [&](float (&s)[CW], int t0, int t1, auto per_token) {
+    const int nblk = (t1 - t0 + NB - 1) / NB;
+    load_block(st, t0, min(NB, t1 - t0), false);
+    store_block(blockbuf(0), st, min(NB, t1 - t0), 0.f);
+    lds_barrier();
+    for (int jb = 0; jb < nblk; ++jb) {
+      const int tb0 = t0 + jb * NB, nb = min(NB, t1 - tb0);
+      const float* buf = blockbuf(jb);
+      if (jb + 1 < nblk) load_block(st, tb0 + NB, min(NB, t1 - tb0 - NB), false);
+      for (int j = 0; j < nb; ++j) {
+        per_token(tb0 + j);
+        advance(s, buf + j * TOKF);
+      }
+      if (jb + 1 < nblk) store_block(blockbuf(jb + 1), st, min(NB, t1 - tb0 - NB), 0.f);
+      lds_barrier();
+    }
+  };
+  auto ld = [&](float (&dst)[CW], const float* src) {
+#pragma unroll
+    for (int j = 0; j < CW; j += 4) *reinterpret_cast<f32x4*>(dst + j) = *reinterpret_cast<const f32x4*>(src + j);
+  };
+  auto st4 = [&](float* dst, const float (&src)[CW]) {
+#pragma unroll
+    for (int j = 0; j < CW; j += 4) *reinterpret_cast<f32x4*>(dst + j) = *reinterpret_cast<const f32x4*>(src + j);
+  };
+
+  // forward sweep: this slice's rows of the state at every chunk start
+  float s[CW];
+  const size_t rowoff = (size_t)e * D + c0;
+  if (a.state_in) ld(s, a.state_in + (size_t)bh * DD + rowoff);
+  else
+#pragma unroll
+    for (int j = 0; j < CW; ++j) s[j] = 0.f;
+  for (int c = 0; c < nc; ++c) {
+    const int t0 = c * L, t1 = min(T, t0 + L);
+    st4(ws + lay.ckpt + (size_t)c * DD + rowoff, s);
+    sweep(s, t0, t1, [](int) {});
+  }
+
+  // reverse sweep
+  float ds[CW];
+  if (a.d_state_out) ld(ds, a.d_state_out + (size_t)bh * DD + rowoff);
+  else
+#pragma unroll
+    for (int j = 0; j < CW; ++j) ds[j] = 0.f;
+  float* sbuf = ws + lay.sbuf + rowoff;
+  float* gpart = ws + lay.part;                       // [T][S][4][D]
+  float* gw = ws + lay.wpart;                         // [T][S]
+  for (int c = nc - 1; c >= 0; --c) {
+    const int t0 = c * L, t1 = min(T, t0 + L), n = t1 - t0;
+    ld(s, ws + lay.ckpt + (size_t)c * DD + rowoff);
+    sweep(s, t0, t1, [&](int t) { st4(sbuf + (size_t)(t - t0) * DD, s); });
+    // output gradients of the last chunk carry d_mean_out / n (the mean of
+    // its outputs); without a projection nothing else reaches them
+    const float dmc = (c == nc - 1 && a.d_mean_out) ? 1.f / (float)n : 0.f;
+    const int nblk = (n + NB - 1) / NB;
+    {
+      const int tb0 = t0 + (nblk - 1) * NB, nb = t1 - tb0;
+      load_block(st, tb0, nb, true);
+      store_block(blockbuf(0), st, nb, dmc);
+    }
+    float ring[RING][CW];
+#pragma unroll
+    for (int k = 0; k < PD; ++k)
+      if (k < n) ld(ring[k], sbuf + (size_t)(n - 1 - k) * DD);
+    lds_barrier();
+
+    auto step = [&](int i, const float (&sp)[CW], float (&nxt)[CW]) {
+      const int t = t1 - 1 - i;
+      const int jb = (t - t0) / NB, tb0 = t0 + jb * NB, j = t - tb0, kb = nblk - 1 - jb;
+      if (t - PD >= t0) ld(nxt, sbuf + (size_t)(t - PD - t0) * DD);
+      if (t == min(tb0 + NB, t1) - 1 && jb > 0) load_block(st, tb0 - NB, NB, true);
+      const float* tb = blockbuf(kb) + j * TOKF;
+      float* pb = part0 + (i & 1) * 4 * 4 * D;
+      float* wpb = wp0 + (i & 1) * 4;
+      const float* tq = tb;
+      const float* tk = tb + D;
+      const float* td = tb + 2 * D;
+      const float* tbb = tb + 3 * D;
+      const float wt = tb[4 * D + 2 * ROWS], ve = tb[4 * D + rl], dout = tb[4 * D + ROWS + rl];
+      float pr = 0.f, pdd = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < CW; ++jj) {
+        pr += sp[jj] * td[c0 + jj] * (tbb[c0 + jj] * tk[c0 + jj]);
+        pdd += ds[jj] * tk[c0 + jj];
+      }
+      const float delta = wt * ve - sum_row16(pr);
+      const float ddelta = sum_row16(pdd);
+      const float dr = -ddelta;
+      if (cl == 0) static_cast<E*>(a.dv)[tok_at(t) * D + e] = from_f32<E>(wt * ddelta);
+      {                                                // dw share of this wave's four rows
+        float pw = cl == 0 ? ddelta * ve : 0.f;
+        pw = sum_halves(sum_row_pairs(pw));
+        if (lane == 0) wpb[wave] = pw;
+      }
+      float p1[CW], p2[CW], p3[CW], p4[CW];
+#pragma unroll
+      for (int jj = 0; jj < CW; ++jj) {
+        const int cc = c0 + jj;
+        const float dec = td[cc];
+        const float sd = sp[jj] * dec;
+        const float dsd = ds[jj] + dr * (tbb[cc] * tk[cc]);
+        p1[jj] = sum_halves(sum_row_pairs(ds[jj] * delta));
+        p2[jj] = sum_halves(sum_row_pairs(sd * dr));
+        p3[jj] = sum_halves(sum_row_pairs(dsd * sd));
+        p4[jj] = sum_halves(sum_row_pairs(sp[jj] * dout));
+        ds[jj] = dsd * dec + dout * tq[cc];
+      }
+      if (lane < 16) {                                 // one row of lanes writes the wave's sums
+        float* dst = pb + wave * 4 * D + c0;
+#pragma unroll
+        for (int jj = 0; jj < CW; jj += 4) {
+          *reinterpret_cast<f32x4*>(dst + jj) = f32x4{p1[jj], p1[jj + 1], p1[jj + 2], p1[jj + 3]};
+          *reinterpret_cast<f32x4*>(dst + D + jj) = f32x4{p2[jj], p2[jj + 1], p2[jj + 2], p2[jj + 3]};
+          *reinterpret_cast<f32x4*>(dst + 2 * D + jj) = f32x4{p3[jj], p3[jj + 1], p3[jj + 2], p3[jj + 3]};
+          *reinterpret_cast<f32x4*>(dst + 3 * D + jj) = f32x4{p4[jj], p4[jj + 1], p4[jj + 2], p4[jj + 3]};
+        }
+      }
+      lds_barrier();
+      // the slice's column sums (four waves) to the partial buffer
+      float* gp = gpart + ((size_t)t * S + slice) * 4 * D;
+#pragma unroll
+      for (int o = tid; o < 4 * D; o += NT)
+        gp[o] = (pb[o] + pb[4 * D + o]) + (pb[8 * D + o] + pb[12 * D + o]);
+      if (tid == 0) gw[(size_t)t * S + slice] = (wpb[0] + wpb[1]) + (wpb[2] + wpb[3]);
+      if (j == 0 && jb > 0) {                          // the block's last token: stage the next block
+        store_block(blockbuf(kb + 1), st, NB, dmc);
+        lds_barrier();
+      }
+    };
+    for (int i = 0; i < n; i += RING) {
+      step(i, ring[0], ring[PD % RING]);
+      if (i + 1 < n) step(i + 1, ring[1 % RING], ring[(1 + PD) % RING]);
+      if (i + 2 < n) step(i + 2, ring[2 % RING], ring[(2 + PD) % RING]);
+    }
+  }
+  if (a.d_state_in) st4(a.d_state_in + (size_t)bh * DD + rowoff, ds);
+  if (a.d_mean_in && cl == 0) {
+    // without a projection the incoming mean reaches nothing unless T = 0,
+    // when the mean passes straight through
+    const float dm = (nc == 0 && a.d_mean_out) ? a.d_mean_out[(size_t)bh * D + e] : 0.f;
+    a.d_mean_in[(size_t)bh * D + e] = dm;
+  }
+}
+
+// Sums the row slices' column sums of every (batch, token, head) and forms
+// dk = P1 + P2 b, dbx = P2 k b (1 - b), dg = P3 (da = P3 (e^g - 1) with raw
+// logits) and dq = P4, with b, k and the decay recomputed from the inputs;
+// and dw from the slices' shares. One thread per (token row, channel).
+template <typename E, int D, bool kLogits>
+__global__ void __launch_bounds__(256)
+carve_bwd_finish_kernel(BwdArgs a) {
+  constexpr int S = D / 16;
+  const size_t rows = (size_t)a.B * a.T * a.H;
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * D) return;
+  const size_t row = idx / D;                          // (b, t, h) in [B, T, H] order
+  const int d = (int)(idx % D);
+  const int h = (int)(row % a.H);
+  const size_t bt = row / a.H;
+  const int t = (int)(bt % a.T), bi = (int)(bt / a.T);
+  const BwdWs lay(D, a.T, a.L, 0);
+  const float* ws = a.ws + ((size_t)bi * a.H + h) * lay.total;
+  const float* gp = ws + lay.part + (size_t)t * S * 4 * D + d;
+  float P[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int sl = 0; sl < S; ++sl)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) P[q] += gp[(sl * 4 + q) * D];
+  const size_t off = row * D + d;
+  const float kk = to_f32(static_cast<const E*>(a.k)[off]);
+  const float b = sigmoid_f(to_f32(static_cast<const E*>(a.bx)[off]));
+  const float dec = fast_exp2(decay_log2<kLogits>(to_f32(static_cast<const E*>(a.g)[off])));
+  static_cast<E*>(a.dk)[off] = from_f32<E>(P[0] + P[1] * b);
+  static_cast<E*>(a.dbx)[off] = from_f32<E>(P[1] * kk * b * (1.f - b));
+  static_cast<E*>(a.dg)[off] = from_f32<E>(kLogits ? P[2] * (dec - 1.f) : P[2]);
+  static_cast<E*>(a.dq)[off] = from_f32<E>(P[3]);
+  if (d == 0) {
+    float dw = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < S; ++sl) dw += ws[lay.wpart + (size_t)t * S + sl];
+    static_cast<E*>(a.dw)[row] = from_f32<E>(dw);
   }
 }
 

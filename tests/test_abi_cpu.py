@@ -187,6 +187,11 @@ def test_bwd_workspace_size():
     per_bh = 2 * 64 * 64 + 64 * 64 * 64 + 2 * 2 * 64 + 2 * 4 + 2 * 4 * 64
     assert sh.bwd_workspace_bytes == 6 * 4 * ((per_bh + 3) // 4 * 4)
     assert _lib.ref_shapes(cfg(B=0)).bwd_workspace_bytes == 0
+    # without a projection the rows of a head are split into d / 16 slices, and
+    # each token keeps every slice's four column sums and its dw share
+    sh0 = _lib.ref_shapes(cfg(rank=0))
+    per_bh0 = 2 * 64 * 64 + 64 * 64 * 64 + 2 * 2 * 64 + 100 * 4 * (4 * 64 + 1)
+    assert sh0.bwd_workspace_bytes == 6 * 4 * ((per_bh0 + 3) // 4 * 4)
 
 
 def test_bwd_argument_errors(L):

@@ -105,6 +105,10 @@ BWD_CASES = [
     ("bf16-d128-L128-r16-ragged-150", "bf16", 1, 2, 150, 128, 128, 16),
     ("bf16-d64-L32-r64-ragged-100", "bf16", 2, 1, 100, 64, 32, 64),
     ("f32-T1", "f32", 2, 2, 1, 64, 64, 8),
+    # without a projection: the row-sliced schedule (D / 16 workgroups per head)
+    ("bf16-d128-L64-r0-ragged-200", "bf16", 1, 2, 200, 128, 64, 0),
+    ("f32-d128-L16-r0-T1", "f32", 2, 1, 1, 128, 16, 0),
+    ("f32-d64-L32-r0-ragged-47", "f32", 3, 1, 47, 64, 32, 0),
 ]
 
 
@@ -128,9 +132,10 @@ def test_backward_without_state_gradients(torch_cuda):
     assert_grads(got, bwd_oracle(inp, "bf16", 64, do, None, None, None, None), TOL["bf16"], "no state")
 
 
-def test_backward_with_decay_logits(torch_cuda):
+@pytest.mark.parametrize("rank", [0, 8])
+def test_backward_with_decay_logits(torch_cuda, rank):
     """Raw decay logits: dg is the gradient of the logit a, dg_g * (-sigmoid(a))."""
-    wl = workload("logits", "f32", 1, 2, 96, 64, 32, 8, 6300)
+    wl = workload("logits", "f32", 1, 2, 96, 64, 32, rank, 6300)
     inp = make_inputs(wl, decay_logits=True)
     do, dSo, dmo, S_in, m_in = cotangents(1, 2, 96, 64, "f32", 6301)
     got = bwd_gpu(torch_cuda, inp, "f32", 32, do, dSo, dmo, S_in, m_in, logits=True)
@@ -147,23 +152,27 @@ def test_backward_in_place_state_gradients(torch_cuda):
     assert_grads(got, ref, TOL["f32"], "in place")
 
 
-def test_backward_empty_sequence(torch_cuda):
+@pytest.mark.parametrize("r", [0, 4])
+def test_backward_empty_sequence(torch_cuda, r):
     """T = 0: the state and mean gradients pass through; the projection gets zeros."""
     torch = torch_cuda
     from chunk_gated_delta_carve_amd import chunk_bwd
-    B, H, d, r = 2, 3, 64, 4
+    B, H, d = 2, 3, 64
     z = lambda *s: torch.zeros(*s, device="cuda", dtype=torch.bfloat16)
     dSo = torch.randn(B, H, d, d, device="cuda")
     dmo = torch.randn(B, H, d, device="cuda")
     out = chunk_bwd(z(B, 0, H, d), z(B, 0, H, d), z(B, 0, H, d), z(B, 0, H, d), z(B, 0, H, d), z(B, 0, H),
-                    z(B, 0, H, d), L=64, ub_down=z(H, r, d), ub_up=z(H, d, r), d_state_out=dSo, d_mean_out=dmo)
+                    z(B, 0, H, d), L=64, ub_down=z(H, r, d) if r else None, ub_up=z(H, d, r) if r else None,
+                    d_state_out=dSo, d_mean_out=dmo)
     torch.cuda.synchronize()
     assert torch.equal(out["d_state_in"], dSo) and torch.equal(out["d_mean_in"], dmo)
-    assert not out["dub_down"].any() and not out["dub_up"].any()
+    if r:
+        assert not out["dub_down"].any() and not out["dub_up"].any()
 
 
-def test_backward_deterministic(torch_cuda):
-    wl = workload("det", "bf16", 2, 2, 200, 64, 64, 16, 6500)
+@pytest.mark.parametrize("rank", [0, 16])
+def test_backward_deterministic(torch_cuda, rank):
+    wl = workload("det", "bf16", 2, 2, 200, 64, 64, rank, 6500)
     inp = make_inputs(wl)
     do, dSo, dmo, S_in, m_in = cotangents(2, 2, 200, 64, "bf16", 6501)
     a = bwd_gpu(torch_cuda, inp, "bf16", 64, do, dSo, dmo, S_in, m_in)
