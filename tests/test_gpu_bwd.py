@@ -180,3 +180,71 @@ def test_backward_deterministic(torch_cuda, rank):
     for n in a:
         if a[n] is not None:
             assert np.array_equal(a[n], b[n]), n
+
+
+@pytest.mark.parametrize("wlname,rank", [("init_equiv", 0), ("init_equiv", 16)], ids=["headline-r0", "headline-r16"])
+def test_backward_full_size_sampled(torch_cuda, wlname, rank):
+    """The benchmarked shape (B4 H12 T2048 d64 L64 bf16) in the launch bench.py
+    times, from N(0,1) output gradients; the oracle recomputes sampled
+    (batch, head) pairs over the full sequence (the pairs are independent, so
+    their gradients need no other pair). With a projection the factors'
+    gradients sum over the batch and are not compared here."""
+    torch = torch_cuda
+    from chunk_gated_delta_carve_amd.workloads import bf16_bits_from_f32
+    wl = WORKLOADS[wlname].with_(rank=rank, ub_std=0.05)
+    say("case full size", wl)
+    inp = make_inputs(wl)
+    B, T, H, d = wl.B, wl.T, wl.H, wl.dv
+    do = bf16_bits_from_f32(np.random.default_rng(6600 + rank).standard_normal((B, T, H, d)).astype(np.float32))
+    got = bwd_gpu(torch, inp, "bf16", wl.L, do, None, None, None, None)
+    for b, h in ((0, 0), (3, 11)):
+        sub = {k: (v[b:b + 1, :, h:h + 1] if k not in ("U_down", "U_up") else v[h:h + 1]) for k, v in inp.items()}
+        sub["w"] = inp["w"][b:b + 1, :, h:h + 1]
+        ref = bwd_oracle(sub, "bf16", wl.L, do[b:b + 1, :, h:h + 1], None, None, None, None)
+        pick = {n: (None if x is None or n in ("dub_down", "dub_up") else
+                    (x[b:b + 1] if n in ("d_state_in", "d_mean_in") else x[b:b + 1, :, h:h + 1]))
+                for n, x in got.items()}
+        pick["d_state_in"] = got["d_state_in"][b:b + 1, h:h + 1]
+        pick["d_mean_in"] = got["d_mean_in"][b:b + 1, h:h + 1]
+        ref["dU_down"] = ref["dU_up"] = None
+        assert_grads(pick, ref, TOL["bf16"], f"full size rank {rank} pair ({b}, {h})")
+
+
+@pytest.mark.parametrize("rank", [0, 8])
+def test_backward_graph_replays_match_eager(torch_cuda, rank):
+    """carve_chunk_bwd captured in a HIP graph (outputs and workspace
+    allocated before the capture) and replayed, with eager work on the
+    stream between replays, gives bit for bit the eager call's gradients."""
+    torch = torch_cuda
+    from chunk_gated_delta_carve_amd import chunk_bwd, recurrent_ref_shapes
+    wl = workload("graph", "bf16", 2, 2, 160, 64, 64, rank, 6700 + rank)
+    inp = make_inputs(wl)
+    t = {k: to_torch(v, "bf16") for k, v in inp.items()}
+    do = to_torch(cotangents(2, 2, 160, 64, "bf16", 6701, with_state=False)[0], "bf16")
+    ws = torch.empty(int(recurrent_ref_shapes(2, 2, 160, 64, 64, 64, rank, torch.bfloat16).bwd_workspace_bytes),
+                     dtype=torch.uint8, device="cuda")
+    ub = dict(ub_down=t["U_down"], ub_up=t["U_up"]) if rank else {}
+    args = [t[k] for k in KEYS] + [do]
+    eager = chunk_bwd(*args, L=64, workspace=ws, **ub)
+    eager = {n: None if x is None else x.clone() for n, x in eager.items()}
+    out = chunk_bwd(*args, L=64, workspace=ws, **ub)              # buffers the graph writes
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            chunk_bwd(*args, L=64, workspace=ws, out=out, stream=side.cuda_stream, **ub)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for i in range(3):
+        for x in out.values():
+            if x is not None:
+                x.fill_(7.0)                                    # the replay must rewrite every output
+        graph.replay()
+        scratch = torch.ones(1 << 20, device="cuda").sum()      # eager work between replays
+        torch.cuda.synchronize()
+        for n, x in eager.items():
+            if x is not None:
+                assert torch.equal(out[n], x), f"replay {i}: {n}"
+        assert float(scratch) == float(1 << 20)
