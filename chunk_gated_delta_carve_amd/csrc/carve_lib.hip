@@ -287,6 +287,11 @@ extern "C" int carve_chunk_bwd(const carve_config* cfg,
                         workspace};
   for (const void* p : ptrs)
     if (misaligned(p)) return CARVE_EALIGN;
+  // one-dimensional grids of the slice-sum (one thread per gradient element)
+  // and batch-sum kernels, 256 threads per block
+  if ((int64_t)cfg->B * cfg->T * cfg->H * cfg->dk / 256 >= 0x7fffffffLL ||
+      2 * (int64_t)cfg->rank * cfg->dk * cfg->H / 256 >= 0x7fffffffLL)
+    return CARVE_EUNSUPPORTED;
   if (workspace_bytes < (size_t)sh.bwd_workspace_bytes) return CARVE_EWORKSPACE;
   if (sh.bwd_workspace_bytes > 0 && (int64_t)cfg->B * cfg->H > 0 && !workspace) return CARVE_EINVAL;
   const size_t es = elem_bytes(cfg->dtype);

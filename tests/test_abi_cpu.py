@@ -208,6 +208,12 @@ def test_bwd_argument_errors(L):
     # d_state_in may be d_state_out itself, but not a shifted view of it
     assert call_bwd(L, c, d_state_in=FAKE + 11 * (1 << 24) + 16) == _lib.CARVE_EINVAL
     assert call_bwd(L, cfg(dk=96, dv=96)) == _lib.CARVE_EUNSUPPORTED
+    # within the forward's index limits, but one thread per gradient element
+    # would exceed a one-dimensional grid
+    big = cfg(B=64, H=1, T=1 << 30, dk=128, dv=128, L=64, rank=0)
+    assert L.carve_recurrent_ref_shapes(ctypes.byref(big), ctypes.byref(_lib.CarveShapes())) == _lib.CARVE_OK
+    assert call_bwd(L, big, ws_bytes=0, ub_down=None, ub_up=None, d_ub_down=None, d_ub_up=None) \
+        == _lib.CARVE_EUNSUPPORTED
     assert call_bwd(L, cfg(flags=4)) == _lib.CARVE_EINVAL
     # nothing to compute and no projection: no HIP call, success
     assert call_bwd(L, cfg(B=0, rank=0), ub_down=None, ub_up=None, d_ub_down=None, d_ub_up=None) == _lib.CARVE_OK
