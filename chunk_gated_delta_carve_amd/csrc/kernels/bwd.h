@@ -17,19 +17,25 @@
 // and dout of a token in chunk c adds dm_c / n_c (n_c tokens in the chunk),
 // where dm_c is what chunk c + 1's gate z = U_up (U_down m_c) sends back.
 //
-// Schedule: one workgroup per (batch, head), four lanes per state row e, lane
-// quarter p holding columns [p D/4, (p + 1) D/4) of S and of dS in registers.
-//   1. A forward sweep stores the state at every chunk start, and each
-//      chunk's gate bias z, gate mean m_{c-1} and U_down m_{c-1}.
+// Both schedules below share the plan:
+//   1. A forward sweep stores the state at every chunk start (and, with a
+//      projection, each chunk's gate bias z, gate mean m_{c-1} and
+//      U_down m_{c-1}).
 //   2. For each chunk from the last: the chunk's states before each token are
 //      recomputed from its checkpoint into the workspace, then the tokens are
-//      walked backwards with dS in registers. Row sums (r, d delta) are quad
-//      reductions; the column sums behind dk, db, dg and dq are reduced over
-//      the rows of each wave with DPP row rotations and over the waves through
-//      LDS, one barrier per token. At the chunk's start the gate's gradient
-//      gives dU_up, dU_down (per (batch, head) partial sums) and dm_{c-1}.
-// A second kernel sums the projection factors' partial gradients over the
-// batch, in a fixed order.
+//      walked backwards with dS in registers. Token inputs are staged into
+//      LDS a block of tokens at a time.
+// With a content projection (carve_bwd_kernel): one workgroup per (batch,
+// head), four lanes per state row e, lane quarter p holding columns
+// [p D/4, (p + 1) D/4) of S and dS. Row sums (r, d delta) are quad
+// reductions; the column sums behind dk, db, dg and dq are reduced over the
+// rows of each wave with DPP row rotations and over the waves through LDS,
+// one barrier per token. At each chunk's start the gate's gradient gives
+// dU_up, dU_down (per (batch, head) partial sums) and dm_{c-1}; a second
+// kernel sums the partials over the batch in a fixed order.
+// Without a projection the rows are independent and a head is split over
+// several workgroups (carve_bwd_split_kernel and carve_bwd_finish_kernel,
+// further down).
 #pragma once
 
 #include "common.h"
