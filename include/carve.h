@@ -145,7 +145,9 @@ int carve_chunk_fwd(const carve_config* cfg,
  *               They may be the same buffers as d_state_out and d_mean_out.
  *   workspace   at least shapes.bwd_workspace_bytes of device scratch: the
  *               state at every chunk start and one chunk's per-token states,
- *               4 (nc + L) dk dv bytes per (batch, head) plus small vectors
+ *               4 (nc + L) dk dv bytes per (batch, head), plus small vectors;
+ *               with rank == 0 also every token's per-slice column sums,
+ *               4 T (dk / 16) (4 dk + 1) bytes per (batch, head)
  * No output may overlap an input, another output or the workspace, except
  * for the two aliases above. Results are deterministic (no atomics).
  * Returns the status codes of carve_chunk_fwd. */
