@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -217,3 +218,21 @@ def test_bwd_argument_errors(L):
     assert call_bwd(L, cfg(flags=4)) == _lib.CARVE_EINVAL
     # nothing to compute and no projection: no HIP call, success
     assert call_bwd(L, cfg(B=0, rank=0), ub_down=None, ub_up=None, d_ub_down=None, d_ub_up=None) == _lib.CARVE_OK
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """Without the compiled library the binding raises at first use; no path
+    of the package falls back to another implementation (checked in a fresh
+    interpreter whose library path points at nothing)."""
+    code = (
+        "import sys\n"
+        f"sys.path.insert(0, {ROOT!r})\n"
+        "from chunk_gated_delta_carve_amd import _lib\n"
+        f"_lib.LIB_PATH = {str(tmp_path / 'absent.so')!r}\n"
+        "try:\n"
+        "    _lib.lib()\n"
+        "except ImportError as e:\n"
+        "    print('raised', 'no fallback' in str(e))\n"
+    )
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.stdout.strip() == "raised True", r.stdout + r.stderr
