@@ -146,39 +146,57 @@ hipError_t dispatch_fwd(const carve_config* cfg, const carve::FwdArgs& a, hipStr
   return cfg->dk == 64 ? dispatch_block<float, 64, LG>(a, bl, s) : dispatch_block<float, 128, LG>(a, bl, s);
 }
 
-template <typename E, int D, bool LG>
-hipError_t launch_bwd(const carve::BwdArgs& a, hipStream_t s) {
-  if (a.rank == 0) {
-    // row-sliced schedule, then the sum over the slices
-    using SL = carve::SplitLayout<D>;
-    constexpr auto split = carve::carve_bwd_split_kernel<E, D, LG>;
-    hipError_t e = set_lds<split>(SL::bytes);
-    if (e != hipSuccess) return e;
+// Row-lane schedule (all widths without a projection; d = 64 with one): the
+// sliced kernel, then the sum over its slices that forms dk, dbx, dg, dq, dw.
+template <typename E, int D, bool LG, bool CONTENT>
+hipError_t launch_row_lane(const carve::BwdArgs& a, hipStream_t s) {
+  using SL = carve::SplitLayout<D, CONTENT>;
+  constexpr auto split = carve::carve_bwd_split_kernel<E, D, LG, CONTENT>;
+  hipError_t e = set_lds<split>(SL::bytes);
+  if (e != hipSuccess) return e;
+  if ((int64_t)a.B * a.H > 0) {
     hipLaunchKernelGGL(split, dim3(a.B * a.H * SL::S), dim3(SL::NT), SL::bytes, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t n = (size_t)a.B * a.T * a.H * D;
-    if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL((carve::carve_bwd_finish_kernel<E, D, LG>), dim3((unsigned)((n + 255) / 256)), dim3(256),
-                       0, s, a);
-    return hipGetLastError();
   }
-  using LY = carve::BwdLayout<D>;
-  constexpr auto kern = carve::carve_bwd_kernel<E, D, LG>;
-  hipError_t e = set_lds<kern>(LY::bytes);
-  if (e != hipSuccess) return e;
-  if ((int64_t)a.B * a.H > 0) {
-    hipLaunchKernelGGL(kern, dim3(a.B * a.H), dim3(LY::NT), LY::bytes, s, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (a.rank == 0 || a.H == 0) return hipSuccess;
-  // the projection factors' gradients, summed over the batch (zeros for B = 0)
+  const size_t n = (size_t)a.B * a.T * a.H * D;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL((carve::carve_bwd_finish_kernel<E, D, LG, CONTENT>), dim3((unsigned)((n + 255) / 256)),
+                     dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// the projection factors' gradients, summed over the batch (zeros for B = 0)
+template <int D>
+hipError_t launch_ub_sum(const carve::BwdArgs& a, hipStream_t s) {
+  if (a.H == 0) return hipSuccess;
   const carve::BwdWs lay(D, a.T, a.L, a.rank);
   const size_t n = 2 * (size_t)a.rank * D * a.H;
   hipLaunchKernelGGL(carve::carve_bwd_ub_kernel<D>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                      a.ws, lay.total, lay.dud, a.B, a.H, a.rank, a.d_ub_down, a.d_ub_up);
   return hipGetLastError();
+}
+
+template <typename E, int D, bool LG>
+hipError_t launch_bwd(const carve::BwdArgs& a, hipStream_t s) {
+  if (a.rank == 0) return launch_row_lane<E, D, LG, false>(a, s);
+  hipError_t e;
+  if constexpr (D == 64) {
+    e = launch_row_lane<E, D, LG, true>(a, s);
+  } else {
+    // one workgroup per (batch, head), four lanes per row: a row-lane
+    // workgroup holding all 128 rows would need 32 waves
+    using LY = carve::BwdLayout<D>;
+    constexpr auto kern = carve::carve_bwd_kernel<E, D, LG>;
+    e = set_lds<kern>(LY::bytes);
+    if (e != hipSuccess) return e;
+    if ((int64_t)a.B * a.H > 0) {
+      hipLaunchKernelGGL(kern, dim3(a.B * a.H), dim3(LY::NT), LY::bytes, s, a);
+      e = hipGetLastError();
+    }
+  }
+  if (e != hipSuccess) return e;
+  return launch_ub_sum<D>(a, s);
 }
 
 template <typename E, bool LG>

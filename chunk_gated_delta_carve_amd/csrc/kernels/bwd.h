@@ -57,9 +57,14 @@ struct BwdArgs {
 // Workspace of one (batch, head), in floats: the chunk checkpoints and the
 // recomputed states of one chunk first (16-byte aligned), then the per-chunk
 // gate vectors and the projection factors' partial gradients.
-// Without a projection (rank 0) the row-sliced schedule also keeps, per
-// token and row slice, the slice's column sums (4 D floats) and its share of
-// dw, for the kernel that adds up the slices.
+// Row slices of the row-lane schedule (below): D / 16 without a projection;
+// one slice of all D rows with a projection at D = 64; none otherwise (the
+// per-head schedule).
+__host__ __device__ constexpr int bwd_slices(int D, int rank) { return rank == 0 ? D / 16 : (D == 64 ? 1 : 0); }
+
+// The row-lane schedule also keeps, per token and row slice, the slice's
+// column sums (4 D floats) and its share of dw, for the kernel that adds up
+// the slices and forms dk, dbx, dg and dq.
 struct BwdWs {
   size_t ckpt, sbuf, z, m, y, dud, duu, part, wpart, total;
   __host__ __device__ BwdWs(int D, int T, int L, int rank) {
@@ -72,7 +77,7 @@ struct BwdWs {
     dud = y + nc * rank;
     duu = dud + (size_t)rank * D;
     part = (duu + (size_t)D * rank + 3) & ~(size_t)3;
-    const size_t slices = rank == 0 ? (size_t)D / 16 : 0;
+    const size_t slices = (size_t)bwd_slices(D, rank);
     wpart = part + (size_t)T * slices * 4 * D;
     total = (wpart + (size_t)T * slices + 3) & ~(size_t)3;
   }
@@ -544,34 +549,48 @@ carve_bwd_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Row-sliced schedule without a content projection. The gates then do not
-// depend on the outputs, so the rows of S (value channels) evolve
-// independently and the adjoint of each row needs only its own row: a head's
-// rows are split into D / 16 slices, one workgroup each, spreading a head
-// over several compute units. Four waves of four rows, sixteen lanes per row,
-// each lane holding CW = D / 16 consecutive columns of S and dS. Row sums are
-// four DPP rotations inside a 16-lane row; the column sums over a wave's four
-// rows are two lane swaps, over the four waves an LDS pass, and over the
-// slices a second kernel (carve_bwd_finish_kernel) that also forms dk, dbx,
-// dg and dq from them.
-template <int D>
+// Row-lane schedule: sixteen lanes per state row, each lane holding CW = D/16
+// consecutive columns of S and dS; waves of four rows. Row sums are four DPP
+// rotations inside a 16-lane row; the column sums over a wave's four rows
+// are two lane swaps, over the workgroup's waves an LDS pass, and over the
+// workgroups of a head a second kernel (carve_bwd_finish_kernel) that also
+// forms dk, dbx, dg and dq from them.
+//   Without a projection (kContent false) the gates do not depend on the
+//   outputs, so the rows of S evolve independently: a head's rows are split
+//   into D / 16 slices of four waves, one workgroup each, spreading a head
+//   over several compute units.
+//   With a projection (kContent true, D = 64) chunk c's gate reads the mean
+//   of chunk c-1's outputs over every row, so one workgroup of D / 4 waves
+//   holds all rows of a head (four waves per SIMD, hiding each other's
+//   latency). It forms the chunk means and gates in the forward sweep, and in
+//   the reverse sweep dz = sum of dbx over each chunk (from the per-token
+//   column sums), then dm_{c-1} (fed into the previous chunk's output
+//   gradients) and the per-(batch, head) partial sums of dU_up and dU_down.
+template <int D, bool kContent>
 struct SplitLayout {
-  static constexpr int NT = 256, ROWS = 16, S = D / ROWS, CW = D / 16;
+  static constexpr int ROWS = kContent ? D : 16, NW = ROWS / 4, NT = 64 * NW;
+  static constexpr int S = D / ROWS, CW = D / 16;
+  static_assert(S == bwd_slices(D, kContent ? 1 : 0), "slices of the workspace layout");
   // tokens per staged block: enough work per block to cover the latency of
   // the next block's global loads (blocks never cross a chunk boundary; a
-  // chunk shorter than NB makes short blocks); 16 at d = 128, where 32 would
-  // not leave the registers to keep the staged values unspilled
-  static constexpr int NB = D == 64 ? 32 : 16;
-  static constexpr int TOKF = 4 * D + 2 * ROWS + 4;   // q, k, dec, b | v, dout of the slice rows | w
+  // chunk shorter than NB makes short blocks); 16 at d = 128 and in the
+  // 16-wave workgroups, where 32 would not leave the registers to keep the
+  // staged values unspilled
+  static constexpr int NB = D == 64 && !kContent ? 32 : 16;
+  static constexpr int TOKF = 4 * D + 2 * ROWS + 4;   // q, k, dec, b | v, dout of the rows | w
   static constexpr int EPT = NB * D / NT;             // (token, channel) elements staged per thread
+  static constexpr int RPT = NB * ROWS / NT;          // (token, row) pairs of v and do per thread
   static constexpr int PD = 2;                        // states loaded this many tokens ahead
   static constexpr int oBlk = 0;                      // 2 x [NB][TOKF]
-  static constexpr int oPart = oBlk + 2 * NB * TOKF;  // 2 x [4 waves][4][D]
-  static constexpr int oWp = oPart + 2 * 4 * 4 * D;   // 2 x [4] dw partials
-  static constexpr int floats = oWp + 8;
+  static constexpr int oPart = oBlk + 2 * NB * TOKF;  // 2 x [NW waves][4][D]
+  static constexpr int oWp = oPart + 2 * NW * 4 * D;  // 2 x [NW] dw partials
+  static constexpr int oVec = oWp + 2 * NW;           // per-chunk vectors (projection only)
+  static constexpr int oZ = oVec, oM = oZ + D, oDm = oM + D, oDmc = oDm + D, oDz = oDmc + D, oY = oDz + D,
+                       oDy = oY + 64;
+  static constexpr int floats = oDy + 64;
   static constexpr int bytes = floats * 4;
-  static_assert(TOKF % 4 == 0 && oPart % 4 == 0 && EPT * NT == NB * D && NB * ROWS % NT == 0 && NB <= NT,
-                "layout");
+  static_assert(TOKF % 4 == 0 && oPart % 4 == 0 && EPT * NT == NB * D && RPT * NT == NB * ROWS && NB <= NT &&
+                NT <= 1024 && (!kContent || 4 * D <= NT), "layout");
 };
 
 // sum over the 16 lanes of a DPP row, in every lane of it
@@ -582,24 +601,31 @@ __device__ __forceinline__ float sum_row16(float x) {
   return x + dpp_mov<0x121>(x);   // row_ror:1
 }
 
-template <typename E, int D, bool kLogits>
-__global__ void __launch_bounds__(256)
+template <typename E, int D, bool kLogits, bool kContent>
+__global__ void __launch_bounds__((SplitLayout<D, kContent>::NT))
 carve_bwd_split_kernel(BwdArgs a) {
-  using LY = SplitLayout<D>;
-  constexpr int NT = LY::NT, CW = LY::CW, NB = LY::NB, TOKF = LY::TOKF, EPT = LY::EPT, S = LY::S;
-  constexpr int ROWS = LY::ROWS, PD = LY::PD, RING = PD + 1;
+  using LY = SplitLayout<D, kContent>;
+  constexpr int NT = LY::NT, NW = LY::NW, CW = LY::CW, NB = LY::NB, TOKF = LY::TOKF, EPT = LY::EPT;
+  constexpr int S = LY::S, ROWS = LY::ROWS, RPT = LY::RPT, PD = LY::PD, RING = PD + 1;
   constexpr size_t DD = (size_t)D * D;
   extern __shared__ __align__(16) float lds[];
   float* part0 = lds + LY::oPart;
   float* wp0 = lds + LY::oWp;
+  float* zs = lds + LY::oZ;       // chunk's gate bias z (zero without a projection)
+  float* ms = lds + LY::oM;       // chunk's gate mean m_{c-1}
+  float* dms = lds + LY::oDm;     // dm of the chunk's outputs from the next chunk's gate
+  float* dmcs = lds + LY::oDmc;   // per row: dm_c / n_c, added to each output gradient
+  float* dzs = lds + LY::oDz;
+  float* ys = lds + LY::oY;
+  float* dys = lds + LY::oDy;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int slice = blockIdx.x % S, bh = blockIdx.x / S, bi = bh / a.H, h = bh % a.H;
   const int rl = wave * 4 + (lane >> 4);              // row within the slice
   const int e = slice * ROWS + rl, cl = lane & 15, c0 = cl * CW;
-  const int T = a.T, L = a.L, H = a.H;
+  const int T = a.T, L = a.L, H = a.H, rank = kContent ? a.rank : 0;
   const int nc = (T + L - 1) / L;
-  const BwdWs lay(D, T, L, 0);
+  const BwdWs lay(D, T, L, rank);
   float* ws = a.ws + (size_t)bh * lay.total;
   const E* Q = static_cast<const E*>(a.q);
   const E* K = static_cast<const E*>(a.k);
@@ -608,11 +634,13 @@ carve_bwd_split_kernel(BwdArgs a) {
   const E* BX = static_cast<const E*>(a.bx);
   const E* W = static_cast<const E*>(a.w);
   const E* DO = static_cast<const E*>(a.d_o);
+  const E* Ud = static_cast<const E*>(a.ub_down) + (size_t)h * rank * D;   // [rank][D]
+  const E* Uu = static_cast<const E*>(a.ub_up) + (size_t)h * D * rank;     // [D][rank]
   auto tok_at = [&](int t) { return ((size_t)bi * T + t) * H + h; };
   auto blockbuf = [&](int i) { return lds + LY::oBlk + (i & 1) * NB * TOKF; };
 
-  // token blocks: [token][q | k | dec | b | v, dout of the slice's rows | w]
-  constexpr int RPT = NB * ROWS / NT;
+  // token blocks: [token][q | k | dec | b | v, dout of the rows | w]; b uses
+  // the chunk's z, and dout adds the row's dm_c / n_c
   struct Staged { float q[EPT], k[EPT], g[EPT], bx[EPT], v[RPT], dout[RPT], w; };
   auto load_block = [&](Staged& st, int tb0, int nb, bool grad) {
 #pragma unroll
@@ -627,7 +655,7 @@ carve_bwd_split_kernel(BwdArgs a) {
       }
     }
 #pragma unroll
-    for (int r2 = 0; r2 < RPT; ++r2) {               // NB x ROWS (token, row) pairs, RPT per thread
+    for (int r2 = 0; r2 < RPT; ++r2) {
       const int idx = tid + r2 * NT, j = idx / ROWS, r = idx % ROWS;
       if (j < nb) {
         const size_t off = tok_at(tb0 + j) * D + slice * ROWS + r;
@@ -637,7 +665,7 @@ carve_bwd_split_kernel(BwdArgs a) {
     }
     if (tid < nb) st.w = to_f32(W[tok_at(tb0 + tid)]);
   };
-  auto store_block = [&](float* buf, const Staged& st, int nb, float dmc) {
+  auto store_block = [&](float* buf, const Staged& st, int nb) {
 #pragma unroll
     for (int r = 0; r < EPT; ++r) {
       const int idx = tid + r * NT, j = idx / D, d = idx % D;
@@ -646,7 +674,7 @@ carve_bwd_split_kernel(BwdArgs a) {
         tb[d] = st.q[r];
         tb[D + d] = st.k[r];
         tb[2 * D + d] = fast_exp2(decay_log2<kLogits>(st.g[r]));
-        tb[3 * D + d] = sigmoid_f(st.bx[r]);
+        tb[3 * D + d] = sigmoid_f(st.bx[r] + zs[d]);
       }
     }
 #pragma unroll
@@ -654,9 +682,7 @@ carve_bwd_split_kernel(BwdArgs a) {
       const int idx = tid + r2 * NT, j = idx / ROWS, r = idx % ROWS;
       if (j < nb) {
         buf[j * TOKF + 4 * D + r] = st.v[r2];
-        // dout of row r: do plus this row's share of d_mean_out (last chunk)
-        const float dm = dmc != 0.f ? dmc * a.d_mean_out[(size_t)bh * D + slice * ROWS + r] : 0.f;
-        buf[j * TOKF + 4 * D + ROWS + r] = st.dout[r2] + dm;
+        buf[j * TOKF + 4 * D + ROWS + r] = st.dout[r2] + dmcs[r];
       }
     }
     if (tid < nb) buf[tid * TOKF + 4 * D + 2 * ROWS] = st.w;
@@ -676,23 +702,42 @@ carve_bwd_split_kernel(BwdArgs a) {
     for (int j = 0; j < CW; ++j) s[j] += delta * tk[c0 + j];
   };
   Staged st;
+  // forward over the tokens [t0, t1) of one chunk from the state in s;
+  // per_token(t, tb) runs before each token's update
   auto sweep = [&](float (&s)[CW], int t0, int t1, auto per_token) {
     const int nblk = (t1 - t0 + NB - 1) / NB;
     load_block(st, t0, min(NB, t1 - t0), false);
-    store_block(blockbuf(0), st, min(NB, t1 - t0), 0.f);
+    store_block(blockbuf(0), st, min(NB, t1 - t0));
     lds_barrier();
     for (int jb = 0; jb < nblk; ++jb) {
       const int tb0 = t0 + jb * NB, nb = min(NB, t1 - tb0);
       const float* buf = blockbuf(jb);
       if (jb + 1 < nblk) load_block(st, tb0 + NB, min(NB, t1 - tb0 - NB), false);
       for (int j = 0; j < nb; ++j) {
-        per_token(tb0 + j);
+        per_token(tb0 + j, buf + j * TOKF);
         advance(s, buf + j * TOKF);
       }
-      if (jb + 1 < nblk) store_block(blockbuf(jb + 1), st, min(NB, t1 - tb0 - NB), 0.f);
+      if (jb + 1 < nblk) store_block(blockbuf(jb + 1), st, min(NB, t1 - tb0 - NB));
       lds_barrier();
     }
   };
+  // the content gate of a chunk from the mean in ms: ys = U_down m, zs = U_up ys
+  auto gate = [&]() {
+    const int r = tid >> 2, sub = tid & 3;
+    if (r < rank) {                                  // uniform across each quad
+      float p = 0.f;
+      for (int j = sub; j < D; j += 4) p += to_f32(Ud[(size_t)r * D + j]) * ms[j];
+      p = quad_sum(p);
+      if (sub == 0) ys[r] = p;
+    }
+    __syncthreads();
+    if (tid < D) {
+      float z = 0.f;
+      for (int i = 0; i < rank; ++i) z += to_f32(Uu[(size_t)tid * rank + i]) * ys[i];
+      zs[tid] = z;
+    }
+  };
+  const size_t rowoff = (size_t)e * D + c0;
   auto ld = [&](float (&dst)[CW], const float* src) {
 #pragma unroll
     for (int j = 0; j < CW; j += 4) *reinterpret_cast<f32x4*>(dst + j) = *reinterpret_cast<const f32x4*>(src + j);
@@ -702,20 +747,53 @@ carve_bwd_split_kernel(BwdArgs a) {
     for (int j = 0; j < CW; j += 4) *reinterpret_cast<f32x4*>(dst + j) = *reinterpret_cast<const f32x4*>(src + j);
   };
 
-  // forward sweep: this slice's rows of the state at every chunk start
+  // ---------------------------------------------------------------- forward sweep
   float s[CW];
-  const size_t rowoff = (size_t)e * D + c0;
   if (a.state_in) ld(s, a.state_in + (size_t)bh * DD + rowoff);
   else
 #pragma unroll
     for (int j = 0; j < CW; ++j) s[j] = 0.f;
+  if (tid < D) {
+    zs[tid] = 0.f;
+    dmcs[tid] = 0.f;
+    dms[tid] = 0.f;
+    if (kContent) ms[tid] = a.mean_in ? a.mean_in[(size_t)bh * D + tid] : 0.f;
+  }
+  if constexpr (kContent) {
+    // this (batch, head)'s partial projection gradients start at zero; each
+    // element is cleared and later updated by the same thread
+    for (int idx = tid; idx < rank * D; idx += NT) {
+      ws[lay.dud + idx] = 0.f;
+      ws[lay.duu + idx] = 0.f;
+    }
+  }
+  __syncthreads();
   for (int c = 0; c < nc; ++c) {
     const int t0 = c * L, t1 = min(T, t0 + L);
     st4(ws + lay.ckpt + (size_t)c * DD + rowoff, s);
-    sweep(s, t0, t1, [](int) {});
+    if constexpr (kContent) {
+      gate();
+      if (tid < D) {
+        ws[lay.z + (size_t)c * D + tid] = zs[tid];
+        ws[lay.m + (size_t)c * D + tid] = ms[tid];
+      }
+      if (tid < rank) ws[lay.y + (size_t)c * rank + tid] = ys[tid];
+      __syncthreads();
+      float acc = 0.f;                                 // this row's outputs over the chunk
+      sweep(s, t0, t1, [&](int, const float* tb) {
+        float po = 0.f;
+#pragma unroll
+        for (int j = 0; j < CW; ++j) po += s[j] * tb[c0 + j];
+        acc += sum_row16(po);
+      });
+      if (cl == 0) ms[e] = acc / (float)(t1 - t0);
+      __syncthreads();
+    } else {
+      sweep(s, t0, t1, [](int, const float*) {});
+    }
   }
 
-  // reverse sweep
+  // ---------------------------------------------------------------- reverse sweep
   float ds[CW];
   if (a.d_state_out) ld(ds, a.d_state_out + (size_t)bh * DD + rowoff);
   else
@@ -726,22 +804,38 @@ carve_bwd_split_kernel(BwdArgs a) {
   float* gw = ws + lay.wpart;                         // [T][S]
   for (int c = nc - 1; c >= 0; --c) {
     const int t0 = c * L, t1 = min(T, t0 + L), n = t1 - t0;
+    if (tid < D) {
+      if (kContent) {
+        zs[tid] = ws[lay.z + (size_t)c * D + tid];
+        ms[tid] = ws[lay.m + (size_t)c * D + tid];
+      }
+      dmcs[tid] = 0.f;                                // the recompute stages no output gradient
+    }
+    if (kContent && tid < rank) ys[tid] = ws[lay.y + (size_t)c * rank + tid];
+    __syncthreads();
     ld(s, ws + lay.ckpt + (size_t)c * DD + rowoff);
-    sweep(s, t0, t1, [&](int t) { st4(sbuf + (size_t)(t - t0) * DD, s); });
-    // output gradients of the last chunk carry d_mean_out / n (the mean of
-    // its outputs); without a projection nothing else reaches them
-    const float dmc = (c == nc - 1 && a.d_mean_out) ? 1.f / (float)n : 0.f;
+    sweep(s, t0, t1, [&](int t, const float*) { st4(sbuf + (size_t)(t - t0) * DD, s); });
+    // each output gradient of the chunk gains dm_c / n: dm_c from the next
+    // chunk's gate (with a projection) and, for the last chunk, d_mean_out
+    if (tid < ROWS) {
+      const int row = slice * ROWS + tid;
+      float dm = kContent ? dms[row] : 0.f;
+      if (c == nc - 1 && a.d_mean_out) dm += a.d_mean_out[(size_t)bh * D + row];
+      dmcs[tid] = dm / (float)n;
+    }
+    __syncthreads();
     const int nblk = (n + NB - 1) / NB;
     {
       const int tb0 = t0 + (nblk - 1) * NB, nb = t1 - tb0;
       load_block(st, tb0, nb, true);
-      store_block(blockbuf(0), st, nb, dmc);
+      store_block(blockbuf(0), st, nb);
     }
     float ring[RING][CW];
 #pragma unroll
     for (int k = 0; k < PD; ++k)
       if (k < n) ld(ring[k], sbuf + (size_t)(n - 1 - k) * DD);
     lds_barrier();
+    float dz = 0.f;                                    // this thread's column of dz (projection)
 
     auto step = [&](int i, const float (&sp)[CW], float (&nxt)[CW]) {
       const int t = t1 - 1 - i;
@@ -749,8 +843,8 @@ carve_bwd_split_kernel(BwdArgs a) {
       if (t - PD >= t0) ld(nxt, sbuf + (size_t)(t - PD - t0) * DD);
       if (t == min(tb0 + NB, t1) - 1 && jb > 0) load_block(st, tb0 - NB, NB, true);
       const float* tb = blockbuf(kb) + j * TOKF;
-      float* pb = part0 + (i & 1) * 4 * 4 * D;
-      float* wpb = wp0 + (i & 1) * 4;
+      float* pb = part0 + (i & 1) * NW * 4 * D;
+      float* wpb = wp0 + (i & 1) * NW;
       const float* tq = tb;
       const float* tk = tb + D;
       const float* td = tb + 2 * D;
@@ -795,14 +889,29 @@ carve_bwd_split_kernel(BwdArgs a) {
         }
       }
       lds_barrier();
-      // the slice's column sums (four waves) to the partial buffer
-      float* gp = gpart + ((size_t)t * S + slice) * 4 * D;
+      // the workgroup's column sums (over its waves) to the partial buffer,
+      // output o = quantity * D + column; with a projection 4 D <= NT and
+      // thread o keeps its column of dz (dbx summed over the chunk)
 #pragma unroll
-      for (int o = tid; o < 4 * D; o += NT)
-        gp[o] = (pb[o] + pb[4 * D + o]) + (pb[8 * D + o] + pb[12 * D + o]);
-      if (tid == 0) gw[(size_t)t * S + slice] = (wpb[0] + wpb[1]) + (wpb[2] + wpb[3]);
+      for (int o = tid; o < 4 * D; o += NT) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int w = 0; w < NW; ++w) acc[w & 3] += pb[w * 4 * D + o];
+        const float P = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        gpart[((size_t)t * S + slice) * 4 * D + o] = P;
+        if (kContent && o >= D && o < 2 * D) {
+          const float b = tbb[o - D];
+          dz += P * tk[o - D] * b * (1.f - b);
+        }
+      }
+      if (tid == 0) {
+        float dw = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) dw += wpb[w];
+        gw[(size_t)t * S + slice] = dw;
+      }
       if (j == 0 && jb > 0) {                          // the block's last token: stage the next block
-        store_block(blockbuf(kb + 1), st, NB, dmc);
+        store_block(blockbuf(kb + 1), st, NB);
         lds_barrier();
       }
     };
@@ -811,24 +920,51 @@ carve_bwd_split_kernel(BwdArgs a) {
       if (i + 1 < n) step(i + 1, ring[1 % RING], ring[(1 + PD) % RING]);
       if (i + 2 < n) step(i + 2, ring[2 % RING], ring[(2 + PD) % RING]);
     }
+
+    // the chunk's gate: z = U_up y, y = U_down m_{c-1}
+    if constexpr (kContent) {
+      if (tid >= D && tid < 2 * D) dzs[tid - D] = dz;
+      __syncthreads();
+      const int r = tid >> 2, sub = tid & 3;
+      if (r < rank) {
+        float p = 0.f;
+        for (int d = sub; d < D; d += 4) p += to_f32(Uu[(size_t)d * rank + r]) * dzs[d];
+        p = quad_sum(p);
+        if (sub == 0) dys[r] = p;
+      }
+      for (int idx = tid; idx < D * rank; idx += NT)       // dU_up[d][i] += dz_d y_i
+        ws[lay.duu + idx] += dzs[idx / rank] * ys[idx % rank];
+      __syncthreads();
+      for (int idx = tid; idx < rank * D; idx += NT)       // dU_down[i][e] += dy_i m_e
+        ws[lay.dud + idx] += dys[idx / D] * ms[idx % D];
+      if (tid < D) {
+        float dm = 0.f;
+        for (int r2 = 0; r2 < rank; ++r2) dm += to_f32(Ud[(size_t)r2 * D + tid]) * dys[r2];
+        dms[tid] = dm;
+      }
+      __syncthreads();
+    }
   }
   if (a.d_state_in) st4(a.d_state_in + (size_t)bh * DD + rowoff, ds);
   if (a.d_mean_in && cl == 0) {
-    // without a projection the incoming mean reaches nothing unless T = 0,
-    // when the mean passes straight through
-    const float dm = (nc == 0 && a.d_mean_out) ? a.d_mean_out[(size_t)bh * D + e] : 0.f;
+    // the incoming mean gates chunk 0 (with a projection); with T = 0 it
+    // passes straight through to mean_out
+    float dm;
+    if (nc == 0) dm = a.d_mean_out ? a.d_mean_out[(size_t)bh * D + e] : 0.f;
+    else dm = kContent ? dms[e] : 0.f;
     a.d_mean_in[(size_t)bh * D + e] = dm;
   }
 }
 
 // Sums the row slices' column sums of every (batch, token, head) and forms
 // dk = P1 + P2 b, dbx = P2 k b (1 - b), dg = P3 (da = P3 (e^g - 1) with raw
-// logits) and dq = P4, with b, k and the decay recomputed from the inputs;
-// and dw from the slices' shares. One thread per (token row, channel).
-template <typename E, int D, bool kLogits>
+// logits) and dq = P4, with b (using the chunk's z with a projection), k and
+// the decay recomputed from the inputs; and dw from the slices' shares. One
+// thread per (token row, channel).
+template <typename E, int D, bool kLogits, bool kContent>
 __global__ void __launch_bounds__(256)
 carve_bwd_finish_kernel(BwdArgs a) {
-  constexpr int S = D / 16;
+  constexpr int S = SplitLayout<D, kContent>::S;
   const size_t rows = (size_t)a.B * a.T * a.H;
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= rows * D) return;
@@ -837,7 +973,7 @@ carve_bwd_finish_kernel(BwdArgs a) {
   const int h = (int)(row % a.H);
   const size_t bt = row / a.H;
   const int t = (int)(bt % a.T), bi = (int)(bt / a.T);
-  const BwdWs lay(D, a.T, a.L, 0);
+  const BwdWs lay(D, a.T, a.L, kContent ? a.rank : 0);
   const float* ws = a.ws + ((size_t)bi * a.H + h) * lay.total;
   const float* gp = ws + lay.part + (size_t)t * S * 4 * D + d;
   float P[4] = {0.f, 0.f, 0.f, 0.f};
@@ -847,7 +983,8 @@ carve_bwd_finish_kernel(BwdArgs a) {
     for (int q = 0; q < 4; ++q) P[q] += gp[(sl * 4 + q) * D];
   const size_t off = row * D + d;
   const float kk = to_f32(static_cast<const E*>(a.k)[off]);
-  const float b = sigmoid_f(to_f32(static_cast<const E*>(a.bx)[off]));
+  const float z = kContent ? ws[lay.z + (size_t)(t / a.L) * D + d] : 0.f;
+  const float b = sigmoid_f(to_f32(static_cast<const E*>(a.bx)[off]) + z);
   const float dec = fast_exp2(decay_log2<kLogits>(to_f32(static_cast<const E*>(a.g)[off])));
   static_cast<E*>(a.dk)[off] = from_f32<E>(P[0] + P[1] * b);
   static_cast<E*>(a.dbx)[off] = from_f32<E>(P[1] * kk * b * (1.f - b));

@@ -183,10 +183,17 @@ def call_bwd(L, c, ws_bytes=None, **ptrs):
 
 def test_bwd_workspace_size():
     """The backward workspace holds, per (batch, head), the fp32 state at every
-    chunk start and one chunk's per-token states, plus small per-chunk vectors."""
+    chunk start and one chunk's per-token states, small per-chunk vectors, and
+    every token's column sums per row slice (one slice of all rows with a
+    projection at d = 64, d / 16 slices without one, none at d = 128 with one)."""
     sh = _lib.ref_shapes(cfg())                      # B2 H3 T100 d64 L64 rank 4: two chunks
-    per_bh = 2 * 64 * 64 + 64 * 64 * 64 + 2 * 2 * 64 + 2 * 4 + 2 * 4 * 64
+    vecs = 2 * 2 * 64 + 2 * 4 + 2 * 4 * 64           # z and m per chunk, U_down m per chunk, dU partials
+    per_bh = 2 * 64 * 64 + 64 * 64 * 64 + vecs
+    per_bh = (per_bh + 3) // 4 * 4 + 100 * 1 * (4 * 64 + 1)
     assert sh.bwd_workspace_bytes == 6 * 4 * ((per_bh + 3) // 4 * 4)
+    sh128 = _lib.ref_shapes(cfg(dk=128, dv=128))
+    per_bh128 = 2 * 128 * 128 + 64 * 128 * 128 + 2 * 2 * 128 + 2 * 4 + 2 * 4 * 128
+    assert sh128.bwd_workspace_bytes == 6 * 4 * ((per_bh128 + 3) // 4 * 4)
     assert _lib.ref_shapes(cfg(B=0)).bwd_workspace_bytes == 0
     # without a projection the rows of a head are split into d / 16 slices, and
     # each token keeps every slice's four column sums and its dw share
