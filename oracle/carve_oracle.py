@@ -49,13 +49,18 @@ Readings where the pages leave a step open (each listed in the design notes):
       path it has: the stale chunk mean m_{c-1} passes gradient back to the
       previous chunk's outputs and to mean_in, and U_down, U_up receive theirs
       through the gate.
+  R11 In-kernel normalisation of q and k (the workload recipes L2-normalise
+      them per token) is q / max(|q|, 1e-12) over d_k for each (batch, token,
+      head), applied before anything else reads them.
 """
 from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["sigmoid", "decay_from_logits", "carve_forward", "carve_step", "carve_backward",
-           "content_gate_bias"]
+__all__ = ["sigmoid", "decay_from_logits", "l2_normalize", "l2_normalize_backward", "carve_forward",
+           "carve_step", "carve_backward", "content_gate_bias"]
+
+NORM_EPS = 1e-12
 
 
 def sigmoid(x: np.ndarray) -> np.ndarray:
@@ -71,6 +76,25 @@ def decay_from_logits(a: np.ndarray) -> np.ndarray:
     so no intermediate overflows and tiny decays keep their relative accuracy."""
     a = np.asarray(a, dtype=np.float64)
     return -(np.maximum(a, 0.0) + np.log1p(np.exp(-np.abs(a))))
+
+
+def l2_normalize(x: np.ndarray) -> np.ndarray:
+    """x / max(|x|, 1e-12) over the last axis, in float64 (reading R11)."""
+    x = np.asarray(x, dtype=np.float64)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return x / np.maximum(n, NORM_EPS)
+
+
+def l2_normalize_backward(x: np.ndarray, dxhat: np.ndarray) -> np.ndarray:
+    """Gradient with respect to x of l2_normalize(x), given the gradient of
+    its output: (dxhat - xhat <xhat, dxhat>) / |x| where |x| > 1e-12 (the
+    projection that removes the radial part), dxhat / 1e-12 below it."""
+    x = np.asarray(x, dtype=np.float64)
+    dxhat = np.asarray(dxhat, dtype=np.float64)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    xhat = x / np.maximum(n, NORM_EPS)
+    radial = xhat * np.sum(xhat * dxhat, axis=-1, keepdims=True)
+    return np.where(n > NORM_EPS, (dxhat - radial) / np.maximum(n, NORM_EPS), dxhat / NORM_EPS)
 
 
 def content_gate_bias(m: np.ndarray, U_down: np.ndarray | None,

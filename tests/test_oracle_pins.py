@@ -13,7 +13,8 @@ import os
 import numpy as np
 import pytest
 
-from oracle import carve_backward, carve_forward, carve_step, decay_from_logits, sigmoid
+from oracle import (carve_backward, carve_forward, carve_step, decay_from_logits, l2_normalize,
+                    l2_normalize_backward, sigmoid)
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -518,3 +519,66 @@ def test_backward_empty_sequence_passes_gradients_through():
                          np.zeros((B, 0, H, dv)), dstate_out=dSo, dmean_out=dmo)
     np.testing.assert_array_equal(got["dstate_in"], dSo)
     np.testing.assert_array_equal(got["dmean_in"], dmo)
+
+
+# ---------------------------------------------------------------- q, k normalisation
+
+def test_l2_normalize_closed_forms():
+    """Unit norm per token; a positive scale of a token changes nothing; a
+    vector along an axis maps to that axis; the zero vector stays zero."""
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((2, 5, 3, 6))
+    y = l2_normalize(x)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), 1.0, rtol=1e-14)
+    c = rng.uniform(0.01, 50.0, size=(2, 5, 3, 1))
+    np.testing.assert_allclose(l2_normalize(c * x), y, rtol=1e-13, atol=1e-15)
+    np.testing.assert_array_equal(l2_normalize(np.array([0.0, -3.0, 0.0])), np.array([0.0, -1.0, 0.0]))
+    np.testing.assert_array_equal(l2_normalize(np.zeros(4)), np.zeros(4))
+
+
+def test_l2_normalize_backward_matches_finite_differences():
+    """The chain rule through the normalisation equals central differences of
+    <dy, l2_normalize(x)>, and it has no radial part: <x, dx> = 0 (a scale of
+    x does not change the output)."""
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal((3, 7))
+    dy = rng.standard_normal((3, 7))
+    got = l2_normalize_backward(x, dy)
+    h, fd = 1e-6, np.zeros_like(x)
+    for i in np.ndindex(x.shape):
+        xp, xm = x.copy(), x.copy()
+        xp[i] += h
+        xm[i] -= h
+        fd[i] = (np.sum(dy * l2_normalize(xp)) - np.sum(dy * l2_normalize(xm))) / (2 * h)
+    np.testing.assert_allclose(got, fd, rtol=0, atol=1e-8)
+    np.testing.assert_allclose(np.sum(got * x, axis=-1), 0.0, atol=1e-12)
+
+
+def test_normalised_layer_is_scale_invariant_and_its_gradients_compose():
+    """The layer on normalised q, k does not see a per-token scale of q or k,
+    and the composed backward (the layer's gradients of q, k taken through the
+    normalisation) equals central differences of the composed forward."""
+    rng = np.random.default_rng(23)
+    B, T, H, dk, dv, L = 1, 6, 2, 3, 2, 3
+    q, k, v, g, bx, w, Ud, Uu = rand_inputs(rng, B, T, H, dk, dv, rank=2, ub_std=0.8)
+    q = q * rng.uniform(0.2, 5.0, size=(B, T, H, 1))        # raw, not unit-norm
+    k = k * rng.uniform(0.2, 5.0, size=(B, T, H, 1))
+    fwd = lambda qq, kk: carve_forward(l2_normalize(qq), l2_normalize(kk), v, g, bx, w, L, Ud, Uu)
+    o1, S1, m1 = fwd(q, k)
+    o2, S2, m2 = fwd(3.0 * q, 0.5 * k)
+    np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(S2, S1, rtol=1e-12, atol=1e-14)
+    do = rng.standard_normal((B, T, H, dv))
+    gr = carve_backward(l2_normalize(q), l2_normalize(k), v, g, bx, w, L, do, Ud, Uu)
+    dq = l2_normalize_backward(q, gr["dq"])
+    dk_ = l2_normalize_backward(k, gr["dk"])
+    J = lambda qq, kk: np.sum(fwd(qq, kk)[0] * do)
+    h = 1e-6
+    for x, got, which in ((q, dq, 0), (k, dk_, 1)):
+        fd = np.zeros_like(x)
+        for i in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[i] += h
+            xm[i] -= h
+            fd[i] = ((J(xp, k) - J(xm, k)) if which == 0 else (J(q, xp) - J(q, xm))) / (2 * h)
+        np.testing.assert_allclose(got, fd, rtol=0, atol=1e-7 * max(1.0, np.abs(fd).max()))
