@@ -516,6 +516,9 @@ def main():
                          "also times the unfused alternative (a torch softplus pass, then the plain call)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU work budget of the oracle baseline sample")
+    ap.add_argument("--qk-l2norm", action="store_true",
+                    help="let the kernels normalise q and k per token (CARVE_QK_L2NORM); also times the unfused "
+                         "alternative (torch normalises q and k, then the plain call)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass carve_chunk_bwd on the workload instead of the forward")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -553,7 +556,8 @@ def main():
     if args.write_mfma_summary:
         write_mfma_summary(wl, *args.write_mfma_summary, args.commands)
         return
-    logits = args.decay_logits
+    logits, norm = args.decay_logits, args.qk_l2norm
+    special = logits or norm                           # an input mode other than the profiled one
     inp = make_inputs(wl, decay_logits=logits)
     t = {k: to_torch(v, wl.dtype) for k, v in inp.items()}
     B, T, H, dk, dv, L, rank = wl.B, wl.T, wl.H, wl.dk, wl.dv, wl.L, wl.rank
@@ -568,14 +572,22 @@ def main():
 
     def step():
         return chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["bx"], t["w"], L=L, ub_down=ub[0], ub_up=ub[1],
-                         return_state=True, out=o, workspace=ws, decay_logits=logits)
+                         return_state=True, out=o, workspace=ws, decay_logits=logits, qk_l2norm=norm)
 
     g_buf = torch.empty_like(t["g"])
 
     def unfused_step():
-        # what a caller without the fused activation runs: materialise g, then the plain call
-        torch.neg(torch.nn.functional.softplus(t["g"]), out=g_buf)
-        return chunk_fwd(t["q"], t["k"], t["v"], g_buf, t["bx"], t["w"], L=L, ub_down=ub[0], ub_up=ub[1],
+        # what a caller without the fused input handling runs: materialise g
+        # and/or the normalised q and k, then the plain call
+        g = t["g"]
+        if logits:
+            torch.neg(torch.nn.functional.softplus(t["g"]), out=g_buf)
+            g = g_buf
+        q, k = t["q"], t["k"]
+        if norm:
+            q = torch.nn.functional.normalize(q, dim=-1, eps=1e-12)
+            k = torch.nn.functional.normalize(k, dim=-1, eps=1e-12)
+        return chunk_fwd(q, k, t["v"], g, t["bx"], t["w"], L=L, ub_down=ub[0], ub_up=ub[1],
                          return_state=True, out=o, workspace=ws)
 
     if args.calibrate_copy:
@@ -643,7 +655,7 @@ def main():
     del flush
 
     unfused_ms = None
-    if logits:
+    if special:
         for _ in range(3):
             unfused_step()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -681,11 +693,12 @@ def main():
                 + ("g = raw decay logits N(0,1), activated in-kernel" if logits else "g=-softplus(N(0,1))")
                 + ", bx N(0,1), w=sigmoid(N(0,1))" + (f", U_b factors N(0,{wl.ub_std})" if rank else "") + ")",
         "config": {"workload": workload, "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "L": L, "rank": rank,
-                   "decay_input": "raw logits, -softplus in-kernel" if logits else "log-decay g"},
+                   "decay_input": "raw logits, -softplus in-kernel" if logits else "log-decay g",
+                   "qk": "normalised in-kernel" if norm else "used as given"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     # the committed counter summaries are of the plain-g launch
-                     "traffic": None if logits else measured_traffic(wl),
+                     # the committed counter summaries are of the plain launch
+                     "traffic": None if special else measured_traffic(wl),
                      "kernel": kernels, "kernel_ms": avg_kernel_ms,
                      "algorithmic_bytes_per_launch": alg, "kernel_ms_cold_cache": float(np.median(cold)),
                      "kernel_ms_single_median": float(np.median(single)),
@@ -693,12 +706,13 @@ def main():
         # the matrix-core roofline of the same call: not the bound (the path's
         # FLOP per byte is far below the MFMA/HBM ridge), reported beside it
         "mfma": {"achieved": tflops, "peak": mfma_peak, "unit": "TFLOP/s", "frac": tflops / mfma_peak,
-                 "algorithmic_flops_per_launch": flops, "counters": None if logits else measured_mfma(wl)},
+                 "algorithmic_flops_per_launch": flops, "counters": None if special else measured_mfma(wl)},
     }
-    if logits:
-        line["unfused"] = {"kernel_ms": unfused_ms, "what": "torch softplus + neg into a g tensor, then the "
-                           "plain call (the g round trip through HBM that the fused activation avoids)"}
-    if not args.no_cpu_baseline and not logits:
+    if special:
+        line["unfused"] = {"kernel_ms": unfused_ms, "what": "torch forms " + " and ".join(
+            (["-softplus(a) into a g tensor"] if logits else []) + (["normalised q and k"] if norm else []))
+            + ", then the plain call (the round trip through HBM that the fused form avoids)"}
+    if not args.no_cpu_baseline and not special:
         line["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 

@@ -9,6 +9,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcarve.so
 CARVE_OK, CARVE_EINVAL, CARVE_EUNSUPPORTED, CARVE_EALIGN, CARVE_EWORKSPACE, CARVE_EHIP = range(6)
 CARVE_F32, CARVE_BF16 = 0, 1
 CARVE_DECAY_LOGITS = 1
+CARVE_QK_L2NORM = 2
 EXPORTED = ("carve_recurrent_ref_shapes", "carve_chunk_fwd", "carve_chunk_bwd", "carve_recurrent_step",
             "carve_error_string")
 

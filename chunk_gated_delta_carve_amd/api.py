@@ -16,9 +16,10 @@ from . import _lib
 _DTYPES = {torch.float32: _lib.CARVE_F32, torch.bfloat16: _lib.CARVE_BF16}
 
 
-def make_config(B, H, T, dk, dv, L, rank, dtype, decay_logits=False) -> _lib.CarveConfig:
+def make_config(B, H, T, dk, dv, L, rank, dtype, decay_logits=False, qk_l2norm=False) -> _lib.CarveConfig:
+    flags = (_lib.CARVE_DECAY_LOGITS if decay_logits else 0) | (_lib.CARVE_QK_L2NORM if qk_l2norm else 0)
     return _lib.CarveConfig(B, H, T, dk, dv, L, rank, _DTYPES[dtype] if isinstance(dtype, torch.dtype) else dtype,
-                            _lib.CARVE_DECAY_LOGITS if decay_logits else 0)
+                            flags)
 
 
 def recurrent_ref_shapes(B, H, T, dk, dv, L, rank=0, dtype=torch.bfloat16) -> _lib.CarveShapes:
@@ -43,12 +44,13 @@ def _need(t, name, shape, dtype, device):
 
 
 def chunk_fwd(q, k, v, g, bx, w, L=64, ub_down=None, ub_up=None, state_in=None, mean_in=None,
-              return_state=False, out=None, workspace=None, stream=None, decay_logits=False):
+              return_state=False, out=None, workspace=None, stream=None, decay_logits=False, qk_l2norm=False):
     """CARVE forward pass. Shapes: q, k, g, bx [B,T,H,dk]; v [B,T,H,dv]; w [B,T,H];
     ub_down [H,r,dv]; ub_up [H,dk,r]; state_in [B,H,dv,dk] fp32; mean_in [B,H,dv] fp32.
     With decay_logits, g holds raw decay logits a and the kernels use the
-    log-decay -softplus(a). Returns o [B,T,H,dv] (and (state_out, mean_out)
-    when return_state)."""
+    log-decay -softplus(a). With qk_l2norm, q and k are divided per token by
+    their L2 norms inside the kernels. Returns o [B,T,H,dv] (and (state_out,
+    mean_out) when return_state)."""
     if q.device.type != "cuda":
         raise ValueError("chunk_fwd runs on the GPU only; move the inputs to a cuda device")
     B, T, H, dk = q.shape
@@ -68,7 +70,7 @@ def chunk_fwd(q, k, v, g, bx, w, L=64, ub_down=None, ub_up=None, state_in=None, 
     _need(state_in, "state_in", (B, H, dv, dk), torch.float32, dev)
     _need(mean_in, "mean_in", (B, H, dv), torch.float32, dev)
 
-    cfg = make_config(B, H, T, dk, dv, L, rank, dt, decay_logits)
+    cfg = make_config(B, H, T, dk, dv, L, rank, dt, decay_logits, qk_l2norm)
     sh = _lib.ref_shapes(cfg)
     o = out if out is not None else torch.empty((B, T, H, dv), dtype=dt, device=dev)
     _need(o, "out", (B, T, H, dv), dt, dev)
@@ -95,7 +97,7 @@ def chunk_fwd(q, k, v, g, bx, w, L=64, ub_down=None, ub_up=None, state_in=None, 
 
 def chunk_bwd(q, k, v, g, bx, w, d_o, L=64, ub_down=None, ub_up=None, state_in=None, mean_in=None,
               d_state_out=None, d_mean_out=None, decay_logits=False, workspace=None, stream=None,
-              d_state_in=None, d_mean_in=None, out=None):
+              d_state_in=None, d_mean_in=None, out=None, qk_l2norm=False):
     """Gradients of chunk_fwd's inputs from the gradients of its outputs.
     q .. mean_in and L as given to chunk_fwd; d_o [B,T,H,dv] in the input
     dtype; d_state_out [B,H,dv,dk] and d_mean_out [B,H,dv] fp32 or None.
@@ -124,7 +126,7 @@ def chunk_bwd(q, k, v, g, bx, w, d_o, L=64, ub_down=None, ub_up=None, state_in=N
     for name, t, shp in (("state_in", state_in, (B, H, dv, dk)), ("mean_in", mean_in, (B, H, dv)),
                          ("d_state_out", d_state_out, (B, H, dv, dk)), ("d_mean_out", d_mean_out, (B, H, dv))):
         _need(t, name, shp, torch.float32, dev)
-    cfg = make_config(B, H, T, dk, dv, L, rank, dt, decay_logits)
+    cfg = make_config(B, H, T, dk, dv, L, rank, dt, decay_logits, qk_l2norm)
     sh = _lib.ref_shapes(cfg)
     empty = lambda shp, dtype=dt: torch.empty(shp, dtype=dtype, device=dev)
     if out is not None:
@@ -164,7 +166,7 @@ def chunk_bwd(q, k, v, g, bx, w, d_o, L=64, ub_down=None, ub_up=None, state_in=N
 
 
 def recurrent_step(q, k, v, g, bx, w, state, mean_prev, chunk_acc, pos, L, ub_down=None, ub_up=None,
-                   out=None, stream=None, decay_logits=False):
+                   out=None, stream=None, decay_logits=False, qk_l2norm=False):
     """One decode step for every (batch, head). Shapes: q, k, g, bx [B,H,dk];
     v [B,H,dv]; w [B,H]; state [B,H,dv,dk] fp32, mean_prev and chunk_acc
     [B,H,dv] fp32 (all three updated in place); pos is the token's position
@@ -196,7 +198,7 @@ def recurrent_step(q, k, v, g, bx, w, state, mean_prev, chunk_acc, pos, L, ub_do
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
     code = _lib.lib().carve_recurrent_step(
-        ctypes.byref(make_config(B, H, 1, dk, dv, L, rank, dt, decay_logits)), ctypes.c_int32(pos),
+        ctypes.byref(make_config(B, H, 1, dk, dv, L, rank, dt, decay_logits, qk_l2norm)), ctypes.c_int32(pos),
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(bx), _ptr(w), _ptr(ub_down), _ptr(ub_up),
         _ptr(state), _ptr(mean_prev), _ptr(chunk_acc), _ptr(o), ctypes.c_void_p(stream))
     _lib.check(code)

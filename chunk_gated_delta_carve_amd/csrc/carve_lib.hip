@@ -28,7 +28,7 @@ int check_config(const carve_config* c) {
   if (!valid_width(c->dk) || !valid_width(c->dv) || c->dk != c->dv) return CARVE_EUNSUPPORTED;
   if (!valid_chunk(c->L)) return CARVE_EUNSUPPORTED;
   if (c->rank > 64) return CARVE_EUNSUPPORTED;
-  if (c->flags & ~CARVE_DECAY_LOGITS) return CARVE_EINVAL;
+  if (c->flags & ~(CARVE_DECAY_LOGITS | CARVE_QK_L2NORM)) return CARVE_EINVAL;
   // offsets are computed in 64-bit, grids in 32-bit (the state pass launches
   // 8 (B H / 8 rounded up) (d_v / 16) workgroups)
   if ((int64_t)c->B * c->H > 0x7fffffffLL / 8 - 8) return CARVE_EUNSUPPORTED;
@@ -93,24 +93,24 @@ hipError_t set_lds(int bytes) {
   return hipSuccess;
 }
 
-template <typename E, int D, int BL, bool LG>
+template <typename E, int D, int BL, bool LG, bool NRM>
 hipError_t launch_serial(const carve::FwdArgs& a, hipStream_t s) {
   using LY = carve::BlockLayout<E, D, D, BL, carve::serial_waves<D, BL>()>;
-  constexpr auto kern = carve::carve_chunk_serial_kernel<E, D, D, BL, LG>;
+  constexpr auto kern = carve::carve_chunk_serial_kernel<E, D, D, BL, LG, NRM>;
   hipError_t e = set_lds<kern>(LY::serial_bytes);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(a.B * a.H), dim3(LY::NT), LY::serial_bytes, s, a);
   return hipGetLastError();
 }
 
-template <int D, bool LG>
+template <int D, bool LG, bool NRM>
 hipError_t launch_parallel(const carve::FwdArgs& a, hipStream_t s) {
   using E = carve::bf16;
   constexpr int BL = kParallelBlock;
   using LY = carve::BlockLayout<E, D, D, BL>;                        // state pass, images
   using LI = carve::BlockLayout<E, D, D, BL, carve::kIntraWaves>;    // intra kernel
   const int nblk = (a.T + BL - 1) / BL;
-  constexpr auto intra = carve::carve_intra_kernel<E, D, D, BL, LG>;
+  constexpr auto intra = carve::carve_intra_kernel<E, D, D, BL, LG, NRM>;
   auto state = carve::carve_state_kernel<E, D, D, BL>;
   hipError_t e = set_lds<intra>(LI::intra_bytes);
   if (e != hipSuccess) return e;
@@ -123,27 +123,30 @@ hipError_t launch_parallel(const carve::FwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename E, int D, bool LG>
+template <typename E, int D, bool LG, bool NRM>
 hipError_t dispatch_block(const carve::FwdArgs& a, int bl, hipStream_t s) {
   switch (bl) {
-    case 16: return launch_serial<E, D, 16, LG>(a, s);
+    case 16: return launch_serial<E, D, 16, LG, NRM>(a, s);
     case 32:
       if constexpr (sizeof(E) == 4 && D == 128) return hipErrorInvalidValue;
-      else return launch_serial<E, D, 32, LG>(a, s);
+      else return launch_serial<E, D, 32, LG, NRM>(a, s);
     default:
       if constexpr (sizeof(E) == 4 && D == 128) return hipErrorInvalidValue;
-      else return launch_serial<E, D, 64, LG>(a, s);
+      else return launch_serial<E, D, 64, LG, NRM>(a, s);
   }
 }
 
-// dtype, width and schedule dispatch of the forward pass for one decay mode
-template <bool LG>
+// dtype, width and schedule dispatch of the forward pass for one input mode
+// (raw decay logits or not, q and k normalised or not)
+template <bool LG, bool NRM>
 hipError_t dispatch_fwd(const carve_config* cfg, const carve::FwdArgs& a, hipStream_t s) {
   const int bl = serial_block(cfg);
-  if (chunk_parallel(cfg)) return cfg->dk == 64 ? launch_parallel<64, LG>(a, s) : launch_parallel<128, LG>(a, s);
+  if (chunk_parallel(cfg))
+    return cfg->dk == 64 ? launch_parallel<64, LG, NRM>(a, s) : launch_parallel<128, LG, NRM>(a, s);
   if (cfg->dtype == CARVE_BF16)
-    return cfg->dk == 64 ? dispatch_block<carve::bf16, 64, LG>(a, bl, s) : dispatch_block<carve::bf16, 128, LG>(a, bl, s);
-  return cfg->dk == 64 ? dispatch_block<float, 64, LG>(a, bl, s) : dispatch_block<float, 128, LG>(a, bl, s);
+    return cfg->dk == 64 ? dispatch_block<carve::bf16, 64, LG, NRM>(a, bl, s)
+                         : dispatch_block<carve::bf16, 128, LG, NRM>(a, bl, s);
+  return cfg->dk == 64 ? dispatch_block<float, 64, LG, NRM>(a, bl, s) : dispatch_block<float, 128, LG, NRM>(a, bl, s);
 }
 
 // Row-lane schedule (all widths without a projection; d = 64 with one): the
@@ -170,15 +173,26 @@ hipError_t launch_row_lane(const carve::BwdArgs& a, hipStream_t s) {
 template <int D>
 hipError_t launch_ub_sum(const carve::BwdArgs& a, hipStream_t s) {
   if (a.H == 0) return hipSuccess;
-  const carve::BwdWs lay(D, a.T, a.L, a.rank);
+  const carve::BwdWs lay(D, a.T, a.L, a.rank, a.norm != 0);
   const size_t n = 2 * (size_t)a.rank * D * a.H;
   hipLaunchKernelGGL(carve::carve_bwd_ub_kernel<D>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                      a.ws, lay.total, lay.dud, a.B, a.H, a.rank, a.d_ub_down, a.d_ub_up);
   return hipGetLastError();
 }
 
+// q, k normalisation around the backward: inverse norms before it, the
+// chain rule through the normalisation after it (one wave per token row)
+template <typename E, int D, bool NORMS>
+hipError_t launch_norm(const carve::BwdArgs& a, hipStream_t s) {
+  const size_t rows = (size_t)a.B * a.T * a.H;
+  if (!a.norm || rows == 0) return hipSuccess;
+  hipLaunchKernelGGL((carve::carve_bwd_norm_kernel<E, D, NORMS>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
+                     a);
+  return hipGetLastError();
+}
+
 template <typename E, int D, bool LG>
-hipError_t launch_bwd(const carve::BwdArgs& a, hipStream_t s) {
+hipError_t launch_bwd_core(const carve::BwdArgs& a, hipStream_t s) {
   if (a.rank == 0) return launch_row_lane<E, D, LG, false>(a, s);
   hipError_t e;
   if constexpr (D == 64) {
@@ -197,6 +211,15 @@ hipError_t launch_bwd(const carve::BwdArgs& a, hipStream_t s) {
   }
   if (e != hipSuccess) return e;
   return launch_ub_sum<D>(a, s);
+}
+
+template <typename E, int D, bool LG>
+hipError_t launch_bwd(const carve::BwdArgs& a, hipStream_t s) {
+  hipError_t e = launch_norm<E, D, true>(a, s);
+  if (e != hipSuccess) return e;
+  e = launch_bwd_core<E, D, LG>(a, s);
+  if (e != hipSuccess) return e;
+  return launch_norm<E, D, false>(a, s);
 }
 
 template <typename E, bool LG>
@@ -229,8 +252,9 @@ extern "C" int carve_recurrent_ref_shapes(const carve_config* cfg, carve_shapes*
   out->state = B * H * dv * dk;
   out->mean = B * H * dv;
   out->workspace_bytes = chunk_parallel(cfg) ? parallel_workspace_bytes(cfg) : 0;
-  out->bwd_workspace_bytes = (int64_t)cfg->B * cfg->H * 4 *
-                             (int64_t)carve::BwdWs(cfg->dk, cfg->T, cfg->L, cfg->rank).total;
+  out->bwd_workspace_bytes =
+      (int64_t)cfg->B * cfg->H * 4 *
+      (int64_t)carve::BwdWs(cfg->dk, cfg->T, cfg->L, cfg->rank, (cfg->flags & CARVE_QK_L2NORM) != 0).total;
   return CARVE_OK;
 }
 
@@ -273,7 +297,9 @@ extern "C" int carve_chunk_fwd(const carve_config* cfg,
   a.B = cfg->B; a.H = cfg->H; a.T = cfg->T; a.L = cfg->L; a.rank = cfg->rank;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const hipError_t e = (cfg->flags & CARVE_DECAY_LOGITS) ? dispatch_fwd<true>(cfg, a, s) : dispatch_fwd<false>(cfg, a, s);
+  const bool lg = (cfg->flags & CARVE_DECAY_LOGITS) != 0, nrm = (cfg->flags & CARVE_QK_L2NORM) != 0;
+  const hipError_t e = lg ? (nrm ? dispatch_fwd<true, true>(cfg, a, s) : dispatch_fwd<true, false>(cfg, a, s))
+                          : (nrm ? dispatch_fwd<false, true>(cfg, a, s) : dispatch_fwd<false, false>(cfg, a, s));
   if (e != hipSuccess) {
     std::snprintf(g_hip_msg, sizeof(g_hip_msg), "%s", hipGetErrorString(e));
     return CARVE_EHIP;
@@ -353,6 +379,7 @@ extern "C" int carve_chunk_bwd(const carve_config* cfg,
   a.d_ub_down = d_ub_down; a.d_ub_up = d_ub_up;
   a.ws = static_cast<float*>(workspace);
   a.B = cfg->B; a.H = cfg->H; a.T = cfg->T; a.L = cfg->L; a.rank = cfg->rank;
+  a.norm = (cfg->flags & CARVE_QK_L2NORM) != 0;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool lg = (cfg->flags & CARVE_DECAY_LOGITS) != 0;
   hipError_t e;
@@ -408,6 +435,7 @@ extern "C" int carve_recurrent_step(const carve_config* cfg, int32_t pos,
   a.state = state; a.mean_prev = mean_prev; a.chunk_acc = chunk_acc; a.o = o;
   a.B = cfg->B; a.H = cfg->H; a.L = cfg->L; a.rank = cfg->rank; a.pos = pos;
   a.logits = (cfg->flags & CARVE_DECAY_LOGITS) != 0;
+  a.norm = (cfg->flags & CARVE_QK_L2NORM) != 0;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (cfg->dtype == CARVE_BF16)

@@ -291,11 +291,15 @@ struct Block {
     static constexpr int NCH = BL * CPR;
     static constexpr int VPER = (NCH + NT - 1) / NT;
     e4 q[RPL], k[RPL], g[RPL], bx[RPL];
+    // with q, k normalisation at d_k = 128: this lane's rows at the channels
+    // 64 away (held by the partner wave), so each row's norm is one 16-lane sum
+    e4 qo[DK == 128 ? RPL : 1], ko[DK == 128 ? RPL : 1];
     f32x4 v[VPER];
     E w;
     // Addresses are a block-uniform base per tensor plus a 32-bit per-lane
     // byte offset (rows of a block lie within 64 H d elements; the host
     // keeps that below 2^32 bytes), shared by the four [., d_k] tensors.
+    template <bool kNorm = false>
     __device__ void load(const Rows<E>& src, int t0, int nvalid) {
       const GateCoord gc;
       const int tid = threadIdx.x;
@@ -313,6 +317,11 @@ struct Block {
           k[i] = *reinterpret_cast<const e4*>(at(Kb, off));
           g[i] = *reinterpret_cast<const e4*>(at(Gb, off));
           bx[i] = *reinterpret_cast<const e4*>(at(Bb, off));
+          if constexpr (kNorm && DK == 128) {
+            const uint32_t offo = ((uint32_t)min(gc.r0 + i, nvalid - 1) * hk + (gc.d0 ^ 64)) * (uint32_t)sizeof(E);
+            qo[i] = *reinterpret_cast<const e4*>(at(Qb, offo));
+            ko[i] = *reinterpret_cast<const e4*>(at(Kb, offo));
+          }
         }
       }
       const E* Vb = src.V + r0 * DV;
@@ -339,8 +348,9 @@ struct Block {
   // steep for the factorised diagonal Grams. Ends with a barrier.
   // kContent: the erase logits carry the content bias z from s.Z; without a
   // content projection z = 0 and s.Z is not read here. kLogits: the decay
-  // input holds raw logits a and g = -softplus(a).
-  template <bool kContent = true, bool kLogits = false>
+  // input holds raw logits a and g = -softplus(a). kNorm: q and k are used
+  // per token divided by their L2 norms over d_k (max(|x|, 1e-12)).
+  template <bool kContent = true, bool kLogits = false, bool kNorm = false>
   __device__ static bool gate_pass(const Smem& s, const Raw& raw, int nvalid, E (&qd)[16]) {
     const GateCoord gc;
     const int tid = threadIdx.x;
@@ -366,6 +376,26 @@ struct Block {
 #pragma unroll
       for (int i = 0; i < RPL; ++i)
         if (r0 + i >= nvalid) { rk[i] = e4{}; rq[i] = e4{}; rg[i] = e4{}; }
+    }
+    float ik[RPL], iq[RPL];                          // inverse norms of this lane's k, q rows
+    if constexpr (kNorm) {
+#pragma unroll
+      for (int i = 0; i < RPL; ++i) {
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float kv = to_f32(raw.k[i][j]), qv = to_f32(raw.q[i][j]);
+          sk += kv * kv;
+          sq += qv * qv;
+          if constexpr (DK == 128) {
+            const float ko = to_f32(raw.ko[i][j]), qo = to_f32(raw.qo[i][j]);
+            sk += ko * ko;
+            sq += qo * qo;
+          }
+        }
+        ik[i] = inv_norm(sum_row16(sk));
+        iq[i] = inv_norm(sum_row16(sq));
+      }
     }
     if (gc.active()) {
       f32x4 run = zero4();
@@ -485,7 +515,11 @@ struct Block {
         e4 kx, qx, ky;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float kvij = to_f32(rk[i][j]), qvij = to_f32(rq[i][j]);
+          float kvij = to_f32(rk[i][j]), qvij = to_f32(rq[i][j]);
+          if constexpr (kNorm) {
+            kvij *= ik[i];
+            qvij *= iq[i];
+          }
           const float bb = sigmoid_f(kContent ? to_f32(raw.bx[i][j]) + z[j] : to_f32(raw.bx[i][j]));
           const float e1 = fast_exp2(pre[i][j]);                     // e^{G_r - Gs} <= 1
           const float en = fast_exp2(seg[j] - pre[i][j]);            // e^{Ge - G_r} <= 1
@@ -523,7 +557,7 @@ struct Block {
   // A (fp32) lands over the Qx/Ky region once every wave is done with them;
   // the P tiles of this wave stay in registers (Pt) until solve() frees the
   // region again. Ends with a barrier.
-  template <bool kLogits = false>
+  template <bool kLogits = false, bool kNorm = false>
   __device__ static void grams(const Smem& s, const Rows<E>& src, int t0, int nvalid, bool fallback,
                                f32x4 (&Pt)[TPW]) {
     const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
@@ -584,7 +618,7 @@ struct Block {
     }
     __syncthreads();
     if (fallback) {
-      grams_pairwise<kLogits>(s, src, t0, nvalid, Pt);
+      grams_pairwise<kLogits, kNorm>(s, src, t0, nvalid, Pt);
       __syncthreads();
     }
   }
@@ -594,7 +628,7 @@ struct Block {
   // Slow but exact. A entries go to LDS; the P entries reach the Pt registers
   // of the wave that owns the tile through a scratch area in R4 (KdT is
   // parked in registers meanwhile).
-  template <bool kLogits = false>
+  template <bool kLogits = false, bool kNorm = false>
   __device__ static void grams_pairwise(const Smem& s, const Rows<E>& src, int t0, int nvalid,
                                         f32x4 (&Pt)[TPW]) {
     float* pdiag = reinterpret_cast<float*>(s.base + LY::oR4);    // scratch: [NB][16][16]
@@ -613,7 +647,7 @@ struct Block {
       while (p >= ri) { p -= ri; ++ri; }
       const int ji = p;
       const int r = 16 * I + ri, j = 16 * I + ji;
-      float sa = 0.f, sp = 0.f;
+      float sa = 0.f, sp = 0.f, nkr = 0.f, nkj = 0.f, nqr = 0.f;   // squared norms (kNorm)
       if (r < nvalid) {
         const size_t rowr = src.row(t0 + r) * DK, rowj = src.row(t0 + j) * DK;
         for (int d = 0; d < DK; ++d) {
@@ -622,8 +656,18 @@ struct Block {
           const float gr = decay_log2<kLogits>(ldg(src.G, rowr + d));
           const float kj = ldg(src.K, rowj + d);
           const float br = sigmoid_f(ldg(src.BX, rowr + d) + s.Z[d]);
-          sa += br * ldg(src.K, rowr + d) * kj * fast_exp2(dg + gr);
-          sp += ldg(src.Q, rowr + d) * kj * fast_exp2(dg);
+          const float kr = ldg(src.K, rowr + d), qr = ldg(src.Q, rowr + d);
+          sa += br * kr * kj * fast_exp2(dg + gr);
+          sp += qr * kj * fast_exp2(dg);
+          if constexpr (kNorm) {
+            nkr += kr * kr;
+            nkj += kj * kj;
+            nqr += qr * qr;
+          }
+        }
+        if constexpr (kNorm) {
+          sa *= inv_norm(nkr) * inv_norm(nkj);
+          sp *= inv_norm(nqr) * inv_norm(nkj);
         }
       }
       s.A[(16 * I + ji) * LA + 16 * I + ri] = sa;   // diagonal blocks are stored transposed

@@ -52,6 +52,7 @@ struct BwdArgs {
   float* d_ub_down; float* d_ub_up;
   float* ws;
   int B, H, T, L, rank;
+  int norm;   // nonzero: q, k are used over their L2 norms (inverse norms in the workspace)
 };
 
 // Workspace of one (batch, head), in floats: the chunk checkpoints and the
@@ -65,9 +66,12 @@ __host__ __device__ constexpr int bwd_slices(int D, int rank) { return rank == 0
 // The row-lane schedule also keeps, per token and row slice, the slice's
 // column sums (4 D floats) and its share of dw, for the kernel that adds up
 // the slices and forms dk, dbx, dg and dq.
+// With q, k normalisation it also keeps every token's inverse norms of q
+// and k and the fp32 gradients of the normalised q and k, which a last
+// kernel takes through the normalisation.
 struct BwdWs {
-  size_t ckpt, sbuf, z, m, y, dud, duu, part, wpart, total;
-  __host__ __device__ BwdWs(int D, int T, int L, int rank) {
+  size_t ckpt, sbuf, z, m, y, dud, duu, part, wpart, nrm, dqh, dkh, total;
+  __host__ __device__ BwdWs(int D, int T, int L, int rank, bool norm) {
     const size_t nc = (size_t)(T + L - 1) / L, DD = (size_t)D * D;
     ckpt = 0;
     sbuf = ckpt + nc * DD;
@@ -79,7 +83,11 @@ struct BwdWs {
     part = (duu + (size_t)D * rank + 3) & ~(size_t)3;
     const size_t slices = (size_t)bwd_slices(D, rank);
     wpart = part + (size_t)T * slices * 4 * D;
-    total = (wpart + (size_t)T * slices + 3) & ~(size_t)3;
+    nrm = (wpart + (size_t)T * slices + 3) & ~(size_t)3;
+    const size_t tn = norm ? (size_t)T : 0;
+    dqh = nrm + 2 * tn;
+    dkh = dqh + tn * D;
+    total = (dkh + tn * D + 3) & ~(size_t)3;
   }
 };
 
@@ -88,18 +96,6 @@ struct BwdWs {
 __device__ __forceinline__ float sum_row_quads(float x) {
   x += dpp_mov<0x128>(x);   // row_ror:8
   return x + dpp_mov<0x124>(x);   // row_ror:4
-}
-// Sum of the two 16-lane rows of each pair (rows 0 and 1, rows 2 and 3).
-__device__ __forceinline__ float sum_row_pairs(float x) {
-  const unsigned u = __float_as_uint(x);
-  const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
-// Sum of the two halves of the wave.
-__device__ __forceinline__ float sum_halves(float x) {
-  const unsigned u = __float_as_uint(x);
-  const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
 // Workgroup barrier that orders LDS only: this wave's LDS operations complete
@@ -167,7 +163,7 @@ carve_bwd_kernel(BwdArgs a) {
   const int T = a.T, L = a.L, H = a.H, rank = a.rank;
   const int nc = (T + L - 1) / L;
   const bool content = rank > 0;
-  const BwdWs lay(D, T, L, rank);
+  const BwdWs lay(D, T, L, rank, a.norm != 0);
   float* ws = a.ws + (size_t)bh * lay.total;
   const E* Q = static_cast<const E*>(a.q);
   const E* K = static_cast<const E*>(a.k);
@@ -196,6 +192,10 @@ carve_bwd_kernel(BwdArgs a) {
         const size_t off = tok_at(tb0 + j) * D + d;
         st.q[r] = to_f32(Q[off]);
         st.k[r] = to_f32(K[off]);
+        if (a.norm) {                                 // q, k over their norms (uniform branch)
+          st.q[r] *= ws[lay.nrm + 2 * (size_t)(tb0 + j)];
+          st.k[r] *= ws[lay.nrm + 2 * (size_t)(tb0 + j) + 1];
+        }
         st.g[r] = to_f32(G[off]);
         st.bx[r] = to_f32(BX[off]);
         st.v[r] = to_f32(V[off]);
@@ -477,7 +477,9 @@ carve_bwd_kernel(BwdArgs a) {
         const size_t off = tok_at(t) * D + rcol;
         const float b = tbb[rcol], kk = tk[rcol];
         if (ro == 0) {                                 // dk = dS^T delta + (S'^T dr) b
-          static_cast<E*>(a.dk)[off] = from_f32<E>(Ps + ((P2[0] + P2[1]) + (P2[2] + P2[3])) * b);
+          const float dkv = Ps + ((P2[0] + P2[1]) + (P2[2] + P2[3])) * b;
+          if (a.norm) ws[lay.dkh + (size_t)t * D + rcol] = dkv;   // gradient of the normalised k
+          else static_cast<E*>(a.dk)[off] = from_f32<E>(dkv);
         } else if (ro == 1) {                          // dbx = (S'^T dr) k b (1 - b)
           const float dbx = Ps * kk * b * (1.f - b);
           static_cast<E*>(a.dbx)[off] = from_f32<E>(dbx);
@@ -487,7 +489,8 @@ carve_bwd_kernel(BwdArgs a) {
           const float dg = kLogits ? Ps * (td[rcol] - 1.f) : Ps;
           static_cast<E*>(a.dg)[off] = from_f32<E>(dg);
         } else {                                       // dq = S^T dout
-          static_cast<E*>(a.dq)[off] = from_f32<E>(Ps);
+          if (a.norm) ws[lay.dqh + (size_t)t * D + rcol] = Ps;
+          else static_cast<E*>(a.dq)[off] = from_f32<E>(Ps);
         }
         if (tid == 0) {
           float dw = 0.f;
@@ -593,14 +596,6 @@ struct SplitLayout {
                 NT <= 1024 && (!kContent || 4 * D <= NT), "layout");
 };
 
-// sum over the 16 lanes of a DPP row, in every lane of it
-__device__ __forceinline__ float sum_row16(float x) {
-  x += dpp_mov<0x128>(x);   // row_ror:8
-  x += dpp_mov<0x124>(x);   // row_ror:4
-  x += dpp_mov<0x122>(x);   // row_ror:2
-  return x + dpp_mov<0x121>(x);   // row_ror:1
-}
-
 template <typename E, int D, bool kLogits, bool kContent>
 __global__ void __launch_bounds__((SplitLayout<D, kContent>::NT))
 carve_bwd_split_kernel(BwdArgs a) {
@@ -625,7 +620,7 @@ carve_bwd_split_kernel(BwdArgs a) {
   const int e = slice * ROWS + rl, cl = lane & 15, c0 = cl * CW;
   const int T = a.T, L = a.L, H = a.H, rank = kContent ? a.rank : 0;
   const int nc = (T + L - 1) / L;
-  const BwdWs lay(D, T, L, rank);
+  const BwdWs lay(D, T, L, rank, a.norm != 0);
   float* ws = a.ws + (size_t)bh * lay.total;
   const E* Q = static_cast<const E*>(a.q);
   const E* K = static_cast<const E*>(a.k);
@@ -650,6 +645,10 @@ carve_bwd_split_kernel(BwdArgs a) {
         const size_t off = tok_at(tb0 + j) * D + d;
         st.q[r] = to_f32(Q[off]);
         st.k[r] = to_f32(K[off]);
+        if (a.norm) {                                 // q, k over their norms (uniform branch)
+          st.q[r] *= ws[lay.nrm + 2 * (size_t)(tb0 + j)];
+          st.k[r] *= ws[lay.nrm + 2 * (size_t)(tb0 + j) + 1];
+        }
         st.g[r] = to_f32(G[off]);
         st.bx[r] = to_f32(BX[off]);
       }
@@ -973,8 +972,8 @@ carve_bwd_finish_kernel(BwdArgs a) {
   const int h = (int)(row % a.H);
   const size_t bt = row / a.H;
   const int t = (int)(bt % a.T), bi = (int)(bt / a.T);
-  const BwdWs lay(D, a.T, a.L, kContent ? a.rank : 0);
-  const float* ws = a.ws + ((size_t)bi * a.H + h) * lay.total;
+  const BwdWs lay(D, a.T, a.L, kContent ? a.rank : 0, a.norm != 0);
+  float* ws = a.ws + ((size_t)bi * a.H + h) * lay.total;
   const float* gp = ws + lay.part + (size_t)t * S * 4 * D + d;
   float P[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -982,19 +981,84 @@ carve_bwd_finish_kernel(BwdArgs a) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) P[q] += gp[(sl * 4 + q) * D];
   const size_t off = row * D + d;
-  const float kk = to_f32(static_cast<const E*>(a.k)[off]);
+  float kk = to_f32(static_cast<const E*>(a.k)[off]);
+  if (a.norm) kk *= ws[lay.nrm + 2 * (size_t)t + 1];
   const float z = kContent ? ws[lay.z + (size_t)(t / a.L) * D + d] : 0.f;
   const float b = sigmoid_f(to_f32(static_cast<const E*>(a.bx)[off]) + z);
   const float dec = fast_exp2(decay_log2<kLogits>(to_f32(static_cast<const E*>(a.g)[off])));
-  static_cast<E*>(a.dk)[off] = from_f32<E>(P[0] + P[1] * b);
   static_cast<E*>(a.dbx)[off] = from_f32<E>(P[1] * kk * b * (1.f - b));
   static_cast<E*>(a.dg)[off] = from_f32<E>(kLogits ? P[2] * (dec - 1.f) : P[2]);
-  static_cast<E*>(a.dq)[off] = from_f32<E>(P[3]);
+  if (a.norm) {                                        // gradients of the normalised q, k
+    ws[lay.dkh + (size_t)t * D + d] = P[0] + P[1] * b;
+    ws[lay.dqh + (size_t)t * D + d] = P[3];
+  } else {
+    static_cast<E*>(a.dk)[off] = from_f32<E>(P[0] + P[1] * b);
+    static_cast<E*>(a.dq)[off] = from_f32<E>(P[3]);
+  }
   if (d == 0) {
     float dw = 0.f;
 #pragma unroll
     for (int sl = 0; sl < S; ++sl) dw += ws[lay.wpart + (size_t)t * S + sl];
     static_cast<E*>(a.dw)[row] = from_f32<E>(dw);
+  }
+}
+
+// q, k normalisation around the backward pass: one wave per (batch, token,
+// head) row, D / 64 channels per lane.
+//   carve_bwd_norms_kernel: the inverse norms 1 / max(|x|, 1e-12) of the row's
+//   q and k, into the workspace of its (batch, head).
+//   carve_bwd_unnorm_kernel: from the gradients g of the normalised q and k,
+//   the gradients of the raw ones, (g - xh <xh, g>) / max(|x|, 1e-12) with
+//   xh = x / max(|x|, 1e-12) (g / 1e-12 for a row of norm at most 1e-12).
+template <typename E, int D, bool kNorms>
+__global__ void __launch_bounds__(256)
+carve_bwd_norm_kernel(BwdArgs a) {
+  constexpr int CPL = D / 64;
+  const size_t row = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) / 64;   // (b, t, h)
+  const int lane = threadIdx.x & 63;
+  if (row >= (size_t)a.B * a.T * a.H) return;          // whole waves leave together
+  const int h = (int)(row % a.H);
+  const size_t bt = row / a.H;
+  const int t = (int)(bt % a.T), bi = (int)(bt / a.T);
+  const BwdWs lay(D, a.T, a.L, a.rank, true);
+  float* ws = a.ws + ((size_t)bi * a.H + h) * lay.total;
+  const E* Q = static_cast<const E*>(a.q) + row * D;
+  const E* K = static_cast<const E*>(a.k) + row * D;
+  float q[CPL], k[CPL], sq = 0.f, sk = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    q[c] = to_f32(Q[lane + 64 * c]);
+    k[c] = to_f32(K[lane + 64 * c]);
+    sq += q[c] * q[c];
+    sk += k[c] * k[c];
+  }
+  const float iq = inv_norm(wave_sum(sq)), ik = inv_norm(wave_sum(sk));
+  if constexpr (kNorms) {
+    if (lane == 0) {
+      ws[lay.nrm + 2 * (size_t)t] = iq;
+      ws[lay.nrm + 2 * (size_t)t + 1] = ik;
+    }
+  } else {
+    const float* gq = ws + lay.dqh + (size_t)t * D;
+    const float* gk = ws + lay.dkh + (size_t)t * D;
+    float dq = 0.f, dk = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      dq += q[c] * iq * gq[lane + 64 * c];
+      dk += k[c] * ik * gk[lane + 64 * c];
+    }
+    dq = wave_sum(dq);
+    dk = wave_sum(dk);
+    E* DQ = static_cast<E*>(a.dq) + row * D;
+    E* DK = static_cast<E*>(a.dk) + row * D;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int d = lane + 64 * c;
+      const float vq = iq >= 1e12f ? gq[d] * iq : (gq[d] - q[c] * iq * dq) * iq;
+      const float vk = ik >= 1e12f ? gk[d] * ik : (gk[d] - k[c] * ik * dk) * ik;
+      DQ[d] = from_f32<E>(vq);
+      DK[d] = from_f32<E>(vk);
+    }
   }
 }
 

@@ -169,6 +169,30 @@ __device__ __forceinline__ float quad_sum(float x) {
   x += dpp_mov<0xB1>(x);
   return x + dpp_mov<0x4E>(x);
 }
+// sum over the 16 lanes of a DPP row, in every lane of it
+__device__ __forceinline__ float sum_row16(float x) {
+  x += dpp_mov<0x128>(x);   // row_ror:8
+  x += dpp_mov<0x124>(x);   // row_ror:4
+  x += dpp_mov<0x122>(x);   // row_ror:2
+  return x + dpp_mov<0x121>(x);   // row_ror:1
+}
+// Sum of the two 16-lane rows of each pair (rows 0 and 1, rows 2 and 3).
+__device__ __forceinline__ float sum_row_pairs(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+// Sum of the two halves of the wave.
+__device__ __forceinline__ float sum_halves(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+// Sum over all 64 lanes of the wave, in every lane.
+__device__ __forceinline__ float wave_sum(float x) { return sum_halves(sum_row_pairs(sum_row16(x))); }
+// 1 / max(sqrt(ss), 1e-12): the inverse L2 norm of a vector whose sum of
+// squares is ss, guarded as x / max(|x|, eps) for a zero vector
+__device__ __forceinline__ float inv_norm(float ss) { return 1.f / fmaxf(sqrtf(ss), 1e-12f); }
 
 // Sum over the four row groups of a C tile column: lanes c, c+16, c+32, c+48.
 __device__ __forceinline__ float sum_groups(float x) {

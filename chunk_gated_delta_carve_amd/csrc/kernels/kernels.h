@@ -31,8 +31,9 @@ template <int DK, int BL>
 constexpr int serial_waves() { return DK == 64 && BL >= 32 ? 8 : DK / 16; }
 
 // kLogits: the decay input g holds raw decay logits a, and the log-decay is
-// -softplus(a), formed where g is read.
-template <typename E, int DK, int DV, int BL, bool kLogits>
+// -softplus(a), formed where g is read. kNorm: q and k are divided per token
+// by their L2 norms over d_k where they are read.
+template <typename E, int DK, int DV, int BL, bool kLogits, bool kNorm>
 __global__ void __launch_bounds__((BlockLayout<E, DK, DV, BL, serial_waves<DK, BL>()>::NT))
 carve_chunk_serial_kernel(FwdArgs a) {
   using B = Block<E, DK, DV, BL, serial_waves<DK, BL>()>;
@@ -157,19 +158,19 @@ carve_chunk_serial_kernel(FwdArgs a) {
   // is processed; wider heads have no registers to spare for that.
   constexpr bool kPrefetch = DK == 64;
   typename B::Raw raw;
-  if (kPrefetch && nblk > 0) raw.load(src, 0, min(BL, T));
+  if (kPrefetch && nblk > 0) raw.template load<kNorm>(src, 0, min(BL, T));
   for (int blk = 0; blk < nblk; ++blk) {
     const int t0 = blk * BL;
     const int nvalid = min(BL, T - t0);
     E qd[16];
     f32x4 Pt[B::TPW];
-    if (!kPrefetch) raw.load(src, t0, nvalid);
-    const bool fallback = B::template gate_pass<true, kLogits>(s, raw, nvalid, qd);
+    if (!kPrefetch) raw.template load<kNorm>(src, t0, nvalid);
+    const bool fallback = B::template gate_pass<true, kLogits, kNorm>(s, raw, nvalid, qd);
     if (kPrefetch) {
       const int nb = min(blk + 1, nblk - 1);         // unconditional: keeps the load waits simple
-      raw.load(src, nb * BL, min(BL, T - nb * BL));
+      raw.template load<kNorm>(src, nb * BL, min(BL, T - nb * BL));
     }
-    B::template grams<kLogits>(s, src, t0, nvalid, fallback, Pt);
+    B::template grams<kLogits, kNorm>(s, src, t0, nvalid, fallback, Pt);
     B::inverse_diag(s);
     B::solve(s, qd, Pt);
     f32x4 CtR[TDP], OltR[NBP], Ot[NBP];
@@ -249,8 +250,8 @@ constexpr int kIntraWaves = 8;
 
 // One workgroup per (batch, head, block): everything that does not depend on
 // the state. Writes the block's state-pass operand image to the workspace.
-// kLogits as for the chunk-serial kernel.
-template <typename E, int DK, int DV, int BL, bool kLogits>
+// kLogits and kNorm as for the chunk-serial kernel.
+template <typename E, int DK, int DV, int BL, bool kLogits, bool kNorm>
 __global__ void __launch_bounds__((BlockLayout<E, DK, DV, BL, kIntraWaves>::NT))
 carve_intra_kernel(FwdArgs a) {
   using B = Block<E, DK, DV, BL, kIntraWaves>;
@@ -270,14 +271,14 @@ carve_intra_kernel(FwdArgs a) {
   unsigned char* img = static_cast<unsigned char*>(a.ws) + (size_t)blockIdx.x * LY::wBytes;
 
   typename B::Raw raw;
-  raw.load(src, t0, nvalid);
+  raw.template load<kNorm>(src, t0, nvalid);
   // no content projection: the gate pass takes z = 0 without reading s.Z; the
   // zeros here serve only the pairwise fallback, several barriers later
   for (int d = threadIdx.x; d < DK; d += NT) s.Z[d] = 0.f;
   E qd[16];
   f32x4 Pt[B::TPW];
-  const bool fallback = B::template gate_pass<false, kLogits>(s, raw, nvalid, qd);
-  B::template grams<kLogits>(s, src, t0, nvalid, fallback, Pt);
+  const bool fallback = B::template gate_pass<false, kLogits, kNorm>(s, raw, nvalid, qd);
+  B::template grams<kLogits, kNorm>(s, src, t0, nvalid, fallback, Pt);
   B::inverse_diag(s);
   B::template solve<true>(s, qd, Pt, img);           // also writes the block's image
 }

@@ -27,6 +27,7 @@ struct StepArgs {
   void* o;
   int B, H, L, rank, pos;
   int logits;   // nonzero: g holds raw decay logits a, and exp(g) = sigmoid(-a)
+  int norm;     // nonzero: q and k are divided by their L2 norms (max(|x|, 1e-12))
 };
 
 template <typename E, int D>
@@ -35,7 +36,7 @@ carve_step_kernel(StepArgs a) {
   constexpr int NT = 4 * D, CW = D / 4;                // threads, columns per lane
   static_assert(CW % 4 == 0, "whole float4 column groups");
   __shared__ __align__(16) float qs[D], ks[D], dec[D], bk[D], vs[D], ms[D], bxs[D];
-  __shared__ float ys[64], wsc;
+  __shared__ float ys[64], wsc, nrm[4];
   // this head's U_down [rank][D] and U_up [D][rank] (dynamic LDS, sized by the rank)
   extern __shared__ __align__(16) unsigned char dyn[];
   E* uds = reinterpret_cast<E*>(dyn);
@@ -73,6 +74,26 @@ carve_step_kernel(StepArgs a) {
     }
   }
   __syncthreads();
+  if (a.norm) {                                        // q, k over their L2 norms (uniform branch)
+    if (tid < D) {
+      const float sq = wave_sum(qs[tid] * qs[tid]), sk = wave_sum(ks[tid] * ks[tid]);
+      if ((tid & 63) == 0) {
+        nrm[2 * (tid >> 6)] = sq;
+        nrm[2 * (tid >> 6) + 1] = sk;
+      }
+    }
+    __syncthreads();
+    if (tid < D) {
+      float sq = nrm[0], sk = nrm[1];
+      if (D == 128) {
+        sq += nrm[2];
+        sk += nrm[3];
+      }
+      qs[tid] *= inv_norm(sq);
+      ks[tid] *= inv_norm(sk);
+    }
+    __syncthreads();
+  }
   // erase gate of this chunk: z = U_up (U_down m_prev), b = sigmoid(bx + z)
   if (a.rank > 0) {
     const int r = tid >> 2, sub = tid & 3;             // four lanes per rank row

@@ -66,8 +66,12 @@ typedef enum { CARVE_F32 = 0, CARVE_BF16 = 1 } carve_dtype;
  *                       = -log(1 + e^a) themselves (the decay activation of
  *                       section 2.3 applied in-kernel), so the caller never
  *                       materialises the activated tensor. Any real a is
- *                       valid; exp(g) = sigmoid(-a) lies in (0, 1). */
-enum { CARVE_DECAY_LOGITS = 1 };
+ *                       valid; exp(g) = sigmoid(-a) lies in (0, 1).
+ *   CARVE_QK_L2NORM     q and k are raw: the kernels divide each token's q
+ *                       and k by their L2 norms over dk (x / max(|x|, 1e-12))
+ *                       before using them, so the caller need not normalise
+ *                       them in a separate pass. */
+enum { CARVE_DECAY_LOGITS = 1, CARVE_QK_L2NORM = 2 };
 
 /* Problem description. B batch, H heads, T tokens, dk key width, dv value
  * width, L chunk length of the content signal, rank of U_b (0 = no content
@@ -76,7 +80,7 @@ enum { CARVE_DECAY_LOGITS = 1 };
 typedef struct {
   int32_t B, H, T, dk, dv, L, rank;
   int32_t dtype; /* carve_dtype */
-  int32_t flags; /* CARVE_DECAY_LOGITS or 0 */
+  int32_t flags; /* a bitwise OR of CARVE_DECAY_LOGITS and CARVE_QK_L2NORM, or 0 */
 } carve_config;
 
 /* Element counts of every tensor (not bytes), and the workspace size in bytes. */

@@ -72,7 +72,9 @@ def test_shape_contract(L):
     (dict(rank=-1), _lib.CARVE_EINVAL),
     (dict(dtype=7), _lib.CARVE_EINVAL),
     (dict(flags=_lib.CARVE_DECAY_LOGITS), _lib.CARVE_OK),
-    (dict(flags=2), _lib.CARVE_EINVAL),
+    (dict(flags=_lib.CARVE_QK_L2NORM), _lib.CARVE_OK),
+    (dict(flags=_lib.CARVE_DECAY_LOGITS | _lib.CARVE_QK_L2NORM), _lib.CARVE_OK),
+    (dict(flags=4), _lib.CARVE_EINVAL),
     (dict(flags=-1), _lib.CARVE_EINVAL),
 ])
 def test_config_rejected(L, kw, code):
