@@ -151,10 +151,10 @@ hipError_t dispatch_fwd(const carve_config* cfg, const carve::FwdArgs& a, hipStr
 
 // Row-lane schedule (all widths without a projection; d = 64 with one): the
 // sliced kernel, then the sum over its slices that forms dk, dbx, dg, dq, dw.
-template <typename E, int D, bool LG, bool CONTENT>
+template <typename E, int D, bool LG, bool CONTENT, bool NRM>
 hipError_t launch_row_lane(const carve::BwdArgs& a, hipStream_t s) {
   using SL = carve::SplitLayout<D, CONTENT>;
-  constexpr auto split = carve::carve_bwd_split_kernel<E, D, LG, CONTENT>;
+  constexpr auto split = carve::carve_bwd_split_kernel<E, D, LG, CONTENT, NRM>;
   hipError_t e = set_lds<split>(SL::bytes);
   if (e != hipSuccess) return e;
   if ((int64_t)a.B * a.H > 0) {
@@ -164,7 +164,7 @@ hipError_t launch_row_lane(const carve::BwdArgs& a, hipStream_t s) {
   }
   const size_t n = (size_t)a.B * a.T * a.H * D;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL((carve::carve_bwd_finish_kernel<E, D, LG, CONTENT>), dim3((unsigned)((n + 255) / 256)),
+  hipLaunchKernelGGL((carve::carve_bwd_finish_kernel<E, D, LG, CONTENT, NRM>), dim3((unsigned)((n + 255) / 256)),
                      dim3(256), 0, s, a);
   return hipGetLastError();
 }
@@ -191,17 +191,17 @@ hipError_t launch_norm(const carve::BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename E, int D, bool LG>
+template <typename E, int D, bool LG, bool NRM>
 hipError_t launch_bwd_core(const carve::BwdArgs& a, hipStream_t s) {
-  if (a.rank == 0) return launch_row_lane<E, D, LG, false>(a, s);
+  if (a.rank == 0) return launch_row_lane<E, D, LG, false, NRM>(a, s);
   hipError_t e;
   if constexpr (D == 64) {
-    e = launch_row_lane<E, D, LG, true>(a, s);
+    e = launch_row_lane<E, D, LG, true, NRM>(a, s);
   } else {
     // one workgroup per (batch, head), four lanes per row: a row-lane
     // workgroup holding all 128 rows would need 32 waves
     using LY = carve::BwdLayout<D>;
-    constexpr auto kern = carve::carve_bwd_kernel<E, D, LG>;
+    constexpr auto kern = carve::carve_bwd_kernel<E, D, LG, NRM>;
     e = set_lds<kern>(LY::bytes);
     if (e != hipSuccess) return e;
     if ((int64_t)a.B * a.H > 0) {
@@ -217,7 +217,7 @@ template <typename E, int D, bool LG>
 hipError_t launch_bwd(const carve::BwdArgs& a, hipStream_t s) {
   hipError_t e = launch_norm<E, D, true>(a, s);
   if (e != hipSuccess) return e;
-  e = launch_bwd_core<E, D, LG>(a, s);
+  e = a.norm ? launch_bwd_core<E, D, LG, true>(a, s) : launch_bwd_core<E, D, LG, false>(a, s);
   if (e != hipSuccess) return e;
   return launch_norm<E, D, false>(a, s);
 }

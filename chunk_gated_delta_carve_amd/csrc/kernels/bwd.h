@@ -140,7 +140,7 @@ struct BwdLayout {
   static_assert(EPT * NT == NB * D && NB <= 16, "whole staging shares");
 };
 
-template <typename E, int D, bool kLogits>
+template <typename E, int D, bool kLogits, bool kNorm>
 __global__ void __launch_bounds__(4 * D)
 carve_bwd_kernel(BwdArgs a) {
   using LY = BwdLayout<D>;
@@ -163,7 +163,7 @@ carve_bwd_kernel(BwdArgs a) {
   const int T = a.T, L = a.L, H = a.H, rank = a.rank;
   const int nc = (T + L - 1) / L;
   const bool content = rank > 0;
-  const BwdWs lay(D, T, L, rank, a.norm != 0);
+  const BwdWs lay(D, T, L, rank, kNorm);
   float* ws = a.ws + (size_t)bh * lay.total;
   const E* Q = static_cast<const E*>(a.q);
   const E* K = static_cast<const E*>(a.k);
@@ -192,7 +192,7 @@ carve_bwd_kernel(BwdArgs a) {
         const size_t off = tok_at(tb0 + j) * D + d;
         st.q[r] = to_f32(Q[off]);
         st.k[r] = to_f32(K[off]);
-        if (a.norm) {                                 // q, k over their norms (uniform branch)
+        if constexpr (kNorm) {                        // q, k over their norms
           st.q[r] *= ws[lay.nrm + 2 * (size_t)(tb0 + j)];
           st.k[r] *= ws[lay.nrm + 2 * (size_t)(tb0 + j) + 1];
         }
@@ -478,7 +478,7 @@ carve_bwd_kernel(BwdArgs a) {
         const float b = tbb[rcol], kk = tk[rcol];
         if (ro == 0) {                                 // dk = dS^T delta + (S'^T dr) b
           const float dkv = Ps + ((P2[0] + P2[1]) + (P2[2] + P2[3])) * b;
-          if (a.norm) ws[lay.dkh + (size_t)t * D + rcol] = dkv;   // gradient of the normalised k
+          if constexpr (kNorm) ws[lay.dkh + (size_t)t * D + rcol] = dkv;   // gradient of the normalised k
           else static_cast<E*>(a.dk)[off] = from_f32<E>(dkv);
         } else if (ro == 1) {                          // dbx = (S'^T dr) k b (1 - b)
           const float dbx = Ps * kk * b * (1.f - b);
@@ -489,7 +489,7 @@ carve_bwd_kernel(BwdArgs a) {
           const float dg = kLogits ? Ps * (td[rcol] - 1.f) : Ps;
           static_cast<E*>(a.dg)[off] = from_f32<E>(dg);
         } else {                                       // dq = S^T dout
-          if (a.norm) ws[lay.dqh + (size_t)t * D + rcol] = Ps;
+          if constexpr (kNorm) ws[lay.dqh + (size_t)t * D + rcol] = Ps;
           else static_cast<E*>(a.dq)[off] = from_f32<E>(Ps);
         }
         if (tid == 0) {
@@ -596,7 +596,7 @@ struct SplitLayout {
                 NT <= 1024 && (!kContent || 4 * D <= NT), "layout");
 };
 
-template <typename E, int D, bool kLogits, bool kContent>
+template <typename E, int D, bool kLogits, bool kContent, bool kNorm>
 __global__ void __launch_bounds__((SplitLayout<D, kContent>::NT))
 carve_bwd_split_kernel(BwdArgs a) {
   using LY = SplitLayout<D, kContent>;
@@ -620,7 +620,7 @@ carve_bwd_split_kernel(BwdArgs a) {
   const int e = slice * ROWS + rl, cl = lane & 15, c0 = cl * CW;
   const int T = a.T, L = a.L, H = a.H, rank = kContent ? a.rank : 0;
   const int nc = (T + L - 1) / L;
-  const BwdWs lay(D, T, L, rank, a.norm != 0);
+  const BwdWs lay(D, T, L, rank, kNorm);
   float* ws = a.ws + (size_t)bh * lay.total;
   const E* Q = static_cast<const E*>(a.q);
   const E* K = static_cast<const E*>(a.k);
@@ -645,7 +645,7 @@ carve_bwd_split_kernel(BwdArgs a) {
         const size_t off = tok_at(tb0 + j) * D + d;
         st.q[r] = to_f32(Q[off]);
         st.k[r] = to_f32(K[off]);
-        if (a.norm) {                                 // q, k over their norms (uniform branch)
+        if constexpr (kNorm) {                        // q, k over their norms
           st.q[r] *= ws[lay.nrm + 2 * (size_t)(tb0 + j)];
           st.k[r] *= ws[lay.nrm + 2 * (size_t)(tb0 + j) + 1];
         }
@@ -960,7 +960,7 @@ carve_bwd_split_kernel(BwdArgs a) {
 // logits) and dq = P4, with b (using the chunk's z with a projection), k and
 // the decay recomputed from the inputs; and dw from the slices' shares. One
 // thread per (token row, channel).
-template <typename E, int D, bool kLogits, bool kContent>
+template <typename E, int D, bool kLogits, bool kContent, bool kNorm>
 __global__ void __launch_bounds__(256)
 carve_bwd_finish_kernel(BwdArgs a) {
   constexpr int S = SplitLayout<D, kContent>::S;
@@ -972,7 +972,7 @@ carve_bwd_finish_kernel(BwdArgs a) {
   const int h = (int)(row % a.H);
   const size_t bt = row / a.H;
   const int t = (int)(bt % a.T), bi = (int)(bt / a.T);
-  const BwdWs lay(D, a.T, a.L, kContent ? a.rank : 0, a.norm != 0);
+  const BwdWs lay(D, a.T, a.L, kContent ? a.rank : 0, kNorm);
   float* ws = a.ws + ((size_t)bi * a.H + h) * lay.total;
   const float* gp = ws + lay.part + (size_t)t * S * 4 * D + d;
   float P[4] = {0.f, 0.f, 0.f, 0.f};
@@ -982,13 +982,13 @@ carve_bwd_finish_kernel(BwdArgs a) {
     for (int q = 0; q < 4; ++q) P[q] += gp[(sl * 4 + q) * D];
   const size_t off = row * D + d;
   float kk = to_f32(static_cast<const E*>(a.k)[off]);
-  if (a.norm) kk *= ws[lay.nrm + 2 * (size_t)t + 1];
+  if constexpr (kNorm) kk *= ws[lay.nrm + 2 * (size_t)t + 1];
   const float z = kContent ? ws[lay.z + (size_t)(t / a.L) * D + d] : 0.f;
   const float b = sigmoid_f(to_f32(static_cast<const E*>(a.bx)[off]) + z);
   const float dec = fast_exp2(decay_log2<kLogits>(to_f32(static_cast<const E*>(a.g)[off])));
   static_cast<E*>(a.dbx)[off] = from_f32<E>(P[1] * kk * b * (1.f - b));
   static_cast<E*>(a.dg)[off] = from_f32<E>(kLogits ? P[2] * (dec - 1.f) : P[2]);
-  if (a.norm) {                                        // gradients of the normalised q, k
+  if constexpr (kNorm) {                               // gradients of the normalised q, k
     ws[lay.dkh + (size_t)t * D + d] = P[0] + P[1] * b;
     ws[lay.dqh + (size_t)t * D + d] = P[3];
   } else {
