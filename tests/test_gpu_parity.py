@@ -325,3 +325,37 @@ def test_deterministic(torch_cuda):
     b = run_gpu(torch_cuda, inp, wl.dtype, wl.L)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("rank", [0, 8], ids=["chunk-parallel", "chunk-serial"])
+def test_forward_graph_replays_match_eager(torch_cuda, rank):
+    """carve_chunk_fwd captured in a HIP graph (output, state buffers and
+    workspace allocated before the capture) and replayed, with eager work on
+    the stream between replays, gives bit for bit the eager call's results."""
+    torch = torch_cuda
+    from chunk_gated_delta_carve_amd import chunk_fwd, recurrent_ref_shapes
+    wl = WORKLOADS["init_equiv"].with_(B=2, H=3, T=320, rank=rank, ub_std=0.05, seed=3100 + rank)
+    inp = make_inputs(wl)
+    t = {k: to_torch(v, wl.dtype) for k, v in inp.items()}
+    ub = dict(ub_down=t["U_down"], ub_up=t["U_up"]) if rank else {}
+    ws = torch.empty(max(16, int(recurrent_ref_shapes(2, 3, 320, 64, 64, 64, rank, torch.bfloat16).workspace_bytes)),
+                     dtype=torch.uint8, device="cuda")
+    args = [t[k] for k in ("q", "k", "v", "g", "bx", "w")]
+    ref = [x.clone() for x in chunk_fwd(*args, L=64, return_state=True, workspace=ws, **ub)]
+    o = torch.empty_like(ref[0])
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            chunk_fwd(*args, L=64, out=o, workspace=ws, stream=side.cuda_stream, **ub)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for i in range(3):
+        o.fill_(7.0)                                       # the replay must rewrite the output
+        graph.replay()
+        scratch = torch.ones(1 << 20, device="cuda").sum()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref[0]), f"replay {i}"
+        assert float(scratch) == float(1 << 20)
