@@ -10,6 +10,7 @@ CARVE_OK, CARVE_EINVAL, CARVE_EUNSUPPORTED, CARVE_EALIGN, CARVE_EWORKSPACE, CARV
 CARVE_F32, CARVE_BF16 = 0, 1
 CARVE_DECAY_LOGITS = 1
 CARVE_QK_L2NORM = 2
+CARVE_DETACH_MEAN = 4
 EXPORTED = ("carve_recurrent_ref_shapes", "carve_chunk_fwd", "carve_chunk_bwd", "carve_recurrent_step",
             "carve_error_string")
 

@@ -16,8 +16,10 @@ from . import _lib
 _DTYPES = {torch.float32: _lib.CARVE_F32, torch.bfloat16: _lib.CARVE_BF16}
 
 
-def make_config(B, H, T, dk, dv, L, rank, dtype, decay_logits=False, qk_l2norm=False) -> _lib.CarveConfig:
-    flags = (_lib.CARVE_DECAY_LOGITS if decay_logits else 0) | (_lib.CARVE_QK_L2NORM if qk_l2norm else 0)
+def make_config(B, H, T, dk, dv, L, rank, dtype, decay_logits=False, qk_l2norm=False,
+                detach_mean=False) -> _lib.CarveConfig:
+    flags = ((_lib.CARVE_DECAY_LOGITS if decay_logits else 0) | (_lib.CARVE_QK_L2NORM if qk_l2norm else 0)
+             | (_lib.CARVE_DETACH_MEAN if detach_mean else 0))
     return _lib.CarveConfig(B, H, T, dk, dv, L, rank, _DTYPES[dtype] if isinstance(dtype, torch.dtype) else dtype,
                             flags)
 
@@ -97,7 +99,7 @@ def chunk_fwd(q, k, v, g, bx, w, L=64, ub_down=None, ub_up=None, state_in=None, 
 
 def chunk_bwd(q, k, v, g, bx, w, d_o, L=64, ub_down=None, ub_up=None, state_in=None, mean_in=None,
               d_state_out=None, d_mean_out=None, decay_logits=False, workspace=None, stream=None,
-              d_state_in=None, d_mean_in=None, out=None, qk_l2norm=False):
+              d_state_in=None, d_mean_in=None, out=None, qk_l2norm=False, detach_mean=False):
     """Gradients of chunk_fwd's inputs from the gradients of its outputs.
     q .. mean_in and L as given to chunk_fwd; d_o [B,T,H,dv] in the input
     dtype; d_state_out [B,H,dv,dk] and d_mean_out [B,H,dv] fp32 or None.
@@ -105,7 +107,9 @@ def chunk_bwd(q, k, v, g, bx, w, d_o, L=64, ub_down=None, ub_up=None, state_in=N
     d_mean_out themselves); allocated when None. Returns a dict with dq, dk,
     dv, dg, dbx, dw (input dtype), dub_down, dub_up (fp32, None without a
     projection), d_state_in and d_mean_in (fp32). `out`: an earlier call's
-    returned dict, whose tensors are written again instead of new ones."""
+    returned dict, whose tensors are written again instead of new ones.
+    detach_mean: the content gate's chunk means are constants (no gradient
+    through them to earlier outputs or mean_in; U_down, U_up still get theirs)."""
     if q.device.type != "cuda":
         raise ValueError("chunk_bwd runs on the GPU only; move the inputs to a cuda device")
     B, T, H, dk = q.shape
@@ -126,7 +130,7 @@ def chunk_bwd(q, k, v, g, bx, w, d_o, L=64, ub_down=None, ub_up=None, state_in=N
     for name, t, shp in (("state_in", state_in, (B, H, dv, dk)), ("mean_in", mean_in, (B, H, dv)),
                          ("d_state_out", d_state_out, (B, H, dv, dk)), ("d_mean_out", d_mean_out, (B, H, dv))):
         _need(t, name, shp, torch.float32, dev)
-    cfg = make_config(B, H, T, dk, dv, L, rank, dt, decay_logits, qk_l2norm)
+    cfg = make_config(B, H, T, dk, dv, L, rank, dt, decay_logits, qk_l2norm, detach_mean)
     sh = _lib.ref_shapes(cfg)
     empty = lambda shp, dtype=dt: torch.empty(shp, dtype=dtype, device=dev)
     if out is not None:

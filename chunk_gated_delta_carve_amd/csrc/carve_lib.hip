@@ -28,7 +28,7 @@ int check_config(const carve_config* c) {
   if (!valid_width(c->dk) || !valid_width(c->dv) || c->dk != c->dv) return CARVE_EUNSUPPORTED;
   if (!valid_chunk(c->L)) return CARVE_EUNSUPPORTED;
   if (c->rank > 64) return CARVE_EUNSUPPORTED;
-  if (c->flags & ~(CARVE_DECAY_LOGITS | CARVE_QK_L2NORM)) return CARVE_EINVAL;
+  if (c->flags & ~(CARVE_DECAY_LOGITS | CARVE_QK_L2NORM | CARVE_DETACH_MEAN)) return CARVE_EINVAL;
   // offsets are computed in 64-bit, grids in 32-bit (the state pass launches
   // 8 (B H / 8 rounded up) (d_v / 16) workgroups)
   if ((int64_t)c->B * c->H > 0x7fffffffLL / 8 - 8) return CARVE_EUNSUPPORTED;
@@ -380,6 +380,7 @@ extern "C" int carve_chunk_bwd(const carve_config* cfg,
   a.ws = static_cast<float*>(workspace);
   a.B = cfg->B; a.H = cfg->H; a.T = cfg->T; a.L = cfg->L; a.rank = cfg->rank;
   a.norm = (cfg->flags & CARVE_QK_L2NORM) != 0;
+  a.detach = (cfg->flags & CARVE_DETACH_MEAN) != 0;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool lg = (cfg->flags & CARVE_DECAY_LOGITS) != 0;
   hipError_t e;

@@ -53,6 +53,7 @@ struct BwdArgs {
   float* ws;
   int B, H, T, L, rank;
   int norm;   // nonzero: q, k are used over their L2 norms (inverse norms in the workspace)
+  int detach; // nonzero: the gate's chunk means are constants (no dm from the gate)
 };
 
 // Workspace of one (batch, head), in floats: the chunk checkpoints and the
@@ -531,7 +532,7 @@ carve_bwd_kernel(BwdArgs a) {
       if (tid < D) {
         float dm = 0.f;
         for (int r2 = 0; r2 < rank; ++r2) dm += to_f32(Ud[(size_t)r2 * D + tid]) * dys[r2];
-        dms[tid] = dm;
+        dms[tid] = a.detach ? 0.f : dm;
       }
       lds_barrier();
     }
@@ -939,7 +940,7 @@ carve_bwd_split_kernel(BwdArgs a) {
       if (tid < D) {
         float dm = 0.f;
         for (int r2 = 0; r2 < rank; ++r2) dm += to_f32(Ud[(size_t)r2 * D + tid]) * dys[r2];
-        dms[tid] = dm;
+        dms[tid] = a.detach ? 0.f : dm;
       }
       __syncthreads();
     }

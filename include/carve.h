@@ -70,8 +70,16 @@ typedef enum { CARVE_F32 = 0, CARVE_BF16 = 1 } carve_dtype;
  *   CARVE_QK_L2NORM     q and k are raw: the kernels divide each token's q
  *                       and k by their L2 norms over dk (x / max(|x|, 1e-12))
  *                       before using them, so the caller need not normalise
- *                       them in a separate pass. */
-enum { CARVE_DECAY_LOGITS = 1, CARVE_QK_L2NORM = 2 };
+ *                       them in a separate pass.
+ *   CARVE_DETACH_MEAN   backward only (the forward and the step ignore it):
+ *                       the chunk means that feed the content gate are taken
+ *                       as constants, as when a training loop detaches them.
+ *                       U_down and U_up still get their gradients through the
+ *                       gate; no gradient reaches earlier outputs or mean_in
+ *                       through it (d_mean_out still reaches the last chunk's
+ *                       outputs). Without the bit the gradients are the exact
+ *                       ones, through every stale mean. */
+enum { CARVE_DECAY_LOGITS = 1, CARVE_QK_L2NORM = 2, CARVE_DETACH_MEAN = 4 };
 
 /* Problem description. B batch, H heads, T tokens, dk key width, dv value
  * width, L chunk length of the content signal, rank of U_b (0 = no content
@@ -80,7 +88,7 @@ enum { CARVE_DECAY_LOGITS = 1, CARVE_QK_L2NORM = 2 };
 typedef struct {
   int32_t B, H, T, dk, dv, L, rank;
   int32_t dtype; /* carve_dtype */
-  int32_t flags; /* a bitwise OR of CARVE_DECAY_LOGITS and CARVE_QK_L2NORM, or 0 */
+  int32_t flags; /* a bitwise OR of the CARVE_* bits above, or 0 */
 } carve_config;
 
 /* Element counts of every tensor (not bytes), and the workspace size in bytes. */

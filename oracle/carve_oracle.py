@@ -207,7 +207,7 @@ def carve_step(state, mean_prev, chunk_acc, pos, q, k, v, g, bx, w, L,
 
 
 def carve_backward(q, k, v, g, bx, w, L, do, U_down=None, U_up=None,
-                   state_in=None, mean_in=None, dstate_out=None, dmean_out=None):
+                   state_in=None, mean_in=None, dstate_out=None, dmean_out=None, detach_mean=False):
     """Gradients of carve_forward in float64 (reading R10), by the adjoint of
     the token recurrence taken backwards through the sequence.
 
@@ -229,6 +229,9 @@ def carve_backward(q, k, v, g, bx, w, L, do, U_down=None, U_up=None,
     The output gradient of token t in chunk c adds dm_c / n_c, where n_c is
     the chunk's token count and dm_c collects dmean_out (last chunk) and the
     gradient that chunk c + 1's gate sends back through z = U_up (U_down m_c).
+    With detach_mean the gate means are taken as constants: the gates still
+    pass gradient to U_down and U_up, but none reaches earlier outputs or
+    mean_in through them (the other reading of R10).
     """
     f = lambda x: np.asarray(x, dtype=np.float64)
     q, k, v, g, bx, w, do = map(f, (q, k, v, g, bx, w, do))
@@ -296,7 +299,7 @@ def carve_backward(q, k, v, g, bx, w, L, do, U_down=None, U_up=None,
             dUu += np.einsum("bhd,bhr->hdr", dz, y)
             dy = np.einsum("hdr,bhd->bhr", Uu, dz)
             dUd += np.einsum("bhr,bhe->hre", dy, mp)
-            dm = np.einsum("hre,bhr->bhe", Ud, dy)
+            dm = np.zeros((B, H, dv)) if detach_mean else np.einsum("hre,bhr->bhe", Ud, dy)
         else:
             dm = np.zeros((B, H, dv))
     grads.update(dU_down=dUd, dU_up=dUu, dstate_in=dS, dmean_in=dm if nc else dmo.copy())

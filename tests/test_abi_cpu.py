@@ -74,7 +74,9 @@ def test_shape_contract(L):
     (dict(flags=_lib.CARVE_DECAY_LOGITS), _lib.CARVE_OK),
     (dict(flags=_lib.CARVE_QK_L2NORM), _lib.CARVE_OK),
     (dict(flags=_lib.CARVE_DECAY_LOGITS | _lib.CARVE_QK_L2NORM), _lib.CARVE_OK),
-    (dict(flags=4), _lib.CARVE_EINVAL),
+    (dict(flags=_lib.CARVE_DETACH_MEAN), _lib.CARVE_OK),
+    (dict(flags=7), _lib.CARVE_OK),
+    (dict(flags=8), _lib.CARVE_EINVAL),
     (dict(flags=-1), _lib.CARVE_EINVAL),
 ])
 def test_config_rejected(L, kw, code):
@@ -224,7 +226,7 @@ def test_bwd_argument_errors(L):
     assert L.carve_recurrent_ref_shapes(ctypes.byref(big), ctypes.byref(_lib.CarveShapes())) == _lib.CARVE_OK
     assert call_bwd(L, big, ws_bytes=0, ub_down=None, ub_up=None, d_ub_down=None, d_ub_up=None) \
         == _lib.CARVE_EUNSUPPORTED
-    assert call_bwd(L, cfg(flags=4)) == _lib.CARVE_EINVAL
+    assert call_bwd(L, cfg(flags=8)) == _lib.CARVE_EINVAL
     # nothing to compute and no projection: no HIP call, success
     assert call_bwd(L, cfg(B=0, rank=0), ub_down=None, ub_up=None, d_ub_down=None, d_ub_up=None) == _lib.CARVE_OK
 

@@ -54,19 +54,19 @@ def cotangents(B, H, T, d, dtype, seed, with_state=True):
     return do, f(B, H, d, d), f(B, H, d), f(B, H, d, d), f(B, H, d)
 
 
-def bwd_gpu(torch, inp, dtype, L, do, dSo, dmo, S_in, m_in, logits=False, alias=False):
+def bwd_gpu(torch, inp, dtype, L, do, dSo, dmo, S_in, m_in, logits=False, alias=False, detach=False):
     from chunk_gated_delta_carve_amd import chunk_bwd
     t = {k: to_torch(v, dtype) for k, v in inp.items()}
     cu = lambda x: None if x is None else torch.from_numpy(x).cuda()
     dSo_t, dmo_t = cu(dSo), cu(dmo)
     out = chunk_bwd(*(t[k] for k in KEYS), to_torch(do, dtype), L=L, ub_down=t.get("U_down"), ub_up=t.get("U_up"),
                     state_in=cu(S_in), mean_in=cu(m_in), d_state_out=dSo_t, d_mean_out=dmo_t, decay_logits=logits,
-                    d_state_in=dSo_t if alias else None, d_mean_in=dmo_t if alias else None)
+                    d_state_in=dSo_t if alias else None, d_mean_in=dmo_t if alias else None, detach_mean=detach)
     torch.cuda.synchronize()
     return {n: None if x is None else x.float().cpu().numpy() for n, x in out.items()}
 
 
-def bwd_oracle(inp, dtype, L, do, dSo, dmo, S_in, m_in, logits=False):
+def bwd_oracle(inp, dtype, L, do, dSo, dmo, S_in, m_in, logits=False, detach=False):
     f = lambda key: to_f64(inp[key], dtype)
     g = f("g")
     if logits:
@@ -76,7 +76,7 @@ def bwd_oracle(inp, dtype, L, do, dSo, dmo, S_in, m_in, logits=False):
                          None if S_in is None else S_in.astype(np.float64),
                          None if m_in is None else m_in.astype(np.float64),
                          None if dSo is None else dSo.astype(np.float64),
-                         None if dmo is None else dmo.astype(np.float64))
+                         None if dmo is None else dmo.astype(np.float64), detach_mean=detach)
     if logits:                                   # d/da of g = -softplus(a) is -sigmoid(a)
         ref["dg"] = ref["dg"] * -sigmoid(f("g"))
     return ref
@@ -140,6 +140,38 @@ def test_backward_with_decay_logits(torch_cuda, rank):
     do, dSo, dmo, S_in, m_in = cotangents(1, 2, 96, 64, "f32", 6301)
     got = bwd_gpu(torch_cuda, inp, "f32", 32, do, dSo, dmo, S_in, m_in, logits=True)
     assert_grads(got, bwd_oracle(inp, "f32", 32, do, dSo, dmo, S_in, m_in, logits=True), TOL["f32"], "logits")
+
+
+DETACH_CASES = [
+    # both content schedules (one workgroup per head at d 64, the per-head
+    # kernel at d 128) and the projection-free one, where the bit changes nothing
+    ("f32-d64-L16-r8-ragged-75", "f32", 1, 2, 75, 64, 16, 8),
+    ("bf16-d128-L32-r4-ragged-90", "bf16", 1, 2, 90, 128, 32, 4),
+    ("bf16-d64-L64-r0", "bf16", 1, 2, 130, 64, 64, 0),
+]
+
+
+@pytest.mark.parametrize("name,dtype,B,H,T,d,L,rank", DETACH_CASES, ids=[c[0] for c in DETACH_CASES])
+def test_backward_with_detached_means(torch_cuda, name, dtype, B, H, T, d, L, rank):
+    """CARVE_DETACH_MEAN: gradients with the gate's chunk means held constant
+    match the oracle's detached gradients; with a projection they differ from
+    the full ones (so the bit took effect), without one they are the same."""
+    wl = workload("detach-" + name, dtype, B, H, T, d, L, rank, 6600 + T)
+    say("case detach", wl)
+    inp = make_inputs(wl)
+    do, dSo, dmo, S_in, m_in = cotangents(B, H, T, d, dtype, 6700 + T)
+    got = bwd_gpu(torch_cuda, inp, dtype, L, do, dSo, dmo, S_in, m_in, detach=True)
+    ref = bwd_oracle(inp, dtype, L, do, dSo, dmo, S_in, m_in, detach=True)
+    assert_grads(got, ref, TOL[dtype], "detached " + name)
+    full = bwd_oracle(inp, dtype, L, do, dSo, dmo, S_in, m_in)
+    moved = rel_err(full["dq"], ref["dq"])
+    say(f"full vs detached oracle dq: {moved:.2e}")
+    if not rank:
+        assert moved == 0
+        return
+    assert not got["d_mean_in"].any() and np.abs(full["dmean_in"]).max() > 0.02
+    if dtype == "f32":
+        assert moved > 10 * TOL[dtype]
 
 
 def test_backward_in_place_state_gradients(torch_cuda):

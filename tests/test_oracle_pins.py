@@ -582,3 +582,47 @@ def test_normalised_layer_is_scale_invariant_and_its_gradients_compose():
             xm[i] -= h
             fd[i] = ((J(xp, k) - J(xm, k)) if which == 0 else (J(q, xp) - J(q, xm))) / (2 * h)
         np.testing.assert_allclose(got, fd, rtol=0, atol=1e-7 * max(1.0, np.abs(fd).max()))
+
+
+def test_detached_mean_gradients_are_those_of_the_frozen_gate_layer():
+    """With detach_mean, the gradients equal central differences of the layer
+    whose gate means are frozen at their values (stepped with carve_step, the
+    mean of each chunk replaced by the original run's): the projection still
+    gets its gradient, mean_in gets none, and they differ from the full
+    gradients."""
+    rng = np.random.default_rng(31)
+    B, T, H, dk, dv, L, r = 1, 7, 2, 3, 2, 3, 2
+    q, k, v, g, bx, w, Ud, Uu = rand_inputs(rng, B, T, H, dk, dv, rank=r, ub_std=0.8)
+    S_in = rng.standard_normal((B, H, dv, dk))
+    m_in = rng.standard_normal((B, H, dv))
+    do = rng.standard_normal((B, T, H, dv))
+    # the gate means of the original run: mean_in, then each whole chunk's mean
+    o0, _, _ = carve_forward(q, k, v, g, bx, w, L, Ud, Uu, state_in=S_in, mean_in=m_in)
+    means = [m_in] + [o0[:, c * L:(c + 1) * L].mean(axis=1) for c in range((T - 1) // L)]
+
+    def J(a):
+        S, acc = S_in.copy(), np.zeros((B, H, dv))
+        total = 0.0
+        for t in range(T):
+            o, S, _, acc = carve_step(S, means[t // L], acc, t % L, a["q"][:, t], a["k"][:, t], v[:, t], a["g"][:, t],
+                                      a["bx"][:, t], w[:, t], L, a["U_down"], a["U_up"])
+            total += np.sum(o * do[:, t])
+        return total
+    args = dict(q=q, k=k, g=g, bx=bx, U_down=Ud, U_up=Uu)
+    got = carve_backward(q, k, v, g, bx, w, L, do, Ud, Uu, S_in, m_in, detach_mean=True)
+    full = carve_backward(q, k, v, g, bx, w, L, do, Ud, Uu, S_in, m_in)
+    h = 1e-6
+    for name, gname in (("q", "dq"), ("k", "dk"), ("g", "dg"), ("bx", "dbx"), ("U_down", "dU_down"),
+                        ("U_up", "dU_up")):
+        x = args[name]
+        fd = np.zeros_like(x)
+        for i in np.ndindex(x.shape):
+            a = dict(args)
+            xp = x.copy(); xp[i] += h; a[name] = xp
+            jp = J(a)
+            xm = x.copy(); xm[i] -= h; a[name] = xm
+            fd[i] = (jp - J(a)) / (2 * h)
+        err = np.abs(got[gname] - fd).max() / max(np.abs(fd).max(), 1e-12)
+        assert err < 1e-7, f"{name}: {err:.2e}"
+    assert not got["dmean_in"].any()
+    assert np.abs(full["dq"] - got["dq"]).max() > 1e-3       # the mean path does carry gradient
