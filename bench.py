@@ -301,6 +301,17 @@ def backward_cpu_baseline(wl, inp, do, budget_s):
                       f"{spent:.1f} s, one thread"}
 
 
+def backward_kernels(wl, rank):
+    """The kernels one carve_chunk_bwd call launches on this workload."""
+    if rank == 0:
+        pre = ("carve_intra_kernel + carve_state_kernel (chunk-start states) + "
+               if wl.dtype == "bf16" and wl.L % 64 == 0 else "")
+        return pre + "carve_bwd_split_kernel + carve_bwd_finish_kernel (one call)"
+    if wl.dk == 64:
+        return "carve_bwd_split_kernel + carve_bwd_finish_kernel + carve_bwd_ub_kernel (one call)"
+    return "carve_bwd_kernel + carve_bwd_ub_kernel (one call)"
+
+
 def bench_backward(args, wl):
     """carve_chunk_bwd on the workload, from seeded output gradients d_o (no
     state or mean gradients, as in a training step that starts from zeros):
@@ -364,8 +375,7 @@ def bench_backward(args, wl):
                    "decay_input": "raw logits, -softplus in-kernel" if args.decay_logits else "log-decay g"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": ("carve_bwd_split_kernel + carve_bwd_finish_kernel (one call)" if rank == 0
-                                else "carve_bwd_kernel + carve_bwd_ub_kernel (one call)"),
+                     "kernel": backward_kernels(wl, rank),
                      "kernel_ms": kernel_ms, "algorithmic_bytes_per_launch": alg},
     }
     if not args.no_cpu_baseline and not args.decay_logits:

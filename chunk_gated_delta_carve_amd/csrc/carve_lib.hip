@@ -69,6 +69,25 @@ int64_t parallel_workspace_bytes(const carve_config* c) {
   return (int64_t)c->B * c->H * nblk * img;
 }
 
+// Without a projection in bf16, when L is a whole number of the forward's
+// 64-token blocks, the backward takes its chunk-start states from the forward
+// pair's state pass (tens of microseconds) instead of a serial sweep over all
+// tokens. The pair's block images and an output it does not need follow the
+// backward's own workspace.
+bool bwd_from_forward(const carve_config* c) { return chunk_parallel(c) && c->L % kParallelBlock == 0; }
+
+struct BwdBytes {
+  int64_t img, o, total;   // byte offsets of the forward's images and output, and the size
+};
+BwdBytes bwd_bytes(const carve_config* c) {
+  const int64_t B = c->B, H = c->H, T = c->T;
+  const int64_t own = B * H * 4 * (int64_t)carve::BwdWs(c->dk, c->T, c->L, c->rank, (c->flags & CARVE_QK_L2NORM) != 0).total;
+  if (!bwd_from_forward(c)) return {0, 0, own};
+  const int64_t img = (own + 255) & ~(int64_t)255;
+  const int64_t o = img + parallel_workspace_bytes(c);
+  return {img, o, o + B * T * H * c->dv * (int64_t)sizeof(carve::bf16)};
+}
+
 // Raises kernel Kern's dynamic-LDS limit to `bytes`. The attribute only ever
 // needs raising, so the largest value set so far is kept per kernel (one
 // instantiation of this function per kernel) and device, and the driver is
@@ -103,7 +122,7 @@ hipError_t launch_serial(const carve::FwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D, bool LG, bool NRM>
+template <int D, bool LG, bool NRM, bool CKPT = false>
 hipError_t launch_parallel(const carve::FwdArgs& a, hipStream_t s) {
   using E = carve::bf16;
   constexpr int BL = kParallelBlock;
@@ -111,7 +130,7 @@ hipError_t launch_parallel(const carve::FwdArgs& a, hipStream_t s) {
   using LI = carve::BlockLayout<E, D, D, BL, carve::kIntraWaves>;    // intra kernel
   const int nblk = (a.T + BL - 1) / BL;
   constexpr auto intra = carve::carve_intra_kernel<E, D, D, BL, LG, NRM>;
-  auto state = carve::carve_state_kernel<E, D, D, BL>;
+  auto state = carve::carve_state_kernel<E, D, D, BL, CKPT>;
   hipError_t e = set_lds<intra>(LI::intra_bytes);
   if (e != hipSuccess) return e;
   if (nblk > 0) {
@@ -147,6 +166,25 @@ hipError_t dispatch_fwd(const carve_config* cfg, const carve::FwdArgs& a, hipStr
     return cfg->dk == 64 ? dispatch_block<carve::bf16, 64, LG, NRM>(a, bl, s)
                          : dispatch_block<carve::bf16, 128, LG, NRM>(a, bl, s);
   return cfg->dk == 64 ? dispatch_block<float, 64, LG, NRM>(a, bl, s) : dispatch_block<float, 128, LG, NRM>(a, bl, s);
+}
+
+hipError_t dispatch_fwd_flags(const carve_config* cfg, const carve::FwdArgs& a, hipStream_t s) {
+  const bool lg = (cfg->flags & CARVE_DECAY_LOGITS) != 0, nrm = (cfg->flags & CARVE_QK_L2NORM) != 0;
+  return lg ? (nrm ? dispatch_fwd<true, true>(cfg, a, s) : dispatch_fwd<true, false>(cfg, a, s))
+            : (nrm ? dispatch_fwd<false, true>(cfg, a, s) : dispatch_fwd<false, false>(cfg, a, s));
+}
+
+// the chunk-parallel pair with the checkpointing state pass (the backward's
+// chunk-start states; bf16 without a projection only)
+template <bool LG, bool NRM>
+hipError_t dispatch_fwd_ckpt(const carve_config* cfg, const carve::FwdArgs& a, hipStream_t s) {
+  return cfg->dk == 64 ? launch_parallel<64, LG, NRM, true>(a, s) : launch_parallel<128, LG, NRM, true>(a, s);
+}
+
+hipError_t dispatch_fwd_ckpt_flags(const carve_config* cfg, const carve::FwdArgs& a, hipStream_t s) {
+  const bool lg = (cfg->flags & CARVE_DECAY_LOGITS) != 0, nrm = (cfg->flags & CARVE_QK_L2NORM) != 0;
+  return lg ? (nrm ? dispatch_fwd_ckpt<true, true>(cfg, a, s) : dispatch_fwd_ckpt<true, false>(cfg, a, s))
+            : (nrm ? dispatch_fwd_ckpt<false, true>(cfg, a, s) : dispatch_fwd_ckpt<false, false>(cfg, a, s));
 }
 
 // Row-lane schedule (all widths without a projection; d = 64 with one): the
@@ -252,9 +290,7 @@ extern "C" int carve_recurrent_ref_shapes(const carve_config* cfg, carve_shapes*
   out->state = B * H * dv * dk;
   out->mean = B * H * dv;
   out->workspace_bytes = chunk_parallel(cfg) ? parallel_workspace_bytes(cfg) : 0;
-  out->bwd_workspace_bytes =
-      (int64_t)cfg->B * cfg->H * 4 *
-      (int64_t)carve::BwdWs(cfg->dk, cfg->T, cfg->L, cfg->rank, (cfg->flags & CARVE_QK_L2NORM) != 0).total;
+  out->bwd_workspace_bytes = bwd_bytes(cfg).total;
   return CARVE_OK;
 }
 
@@ -295,11 +331,9 @@ extern "C" int carve_chunk_fwd(const carve_config* cfg,
   a.o = o; a.state_out = state_out; a.mean_out = mean_out;
   a.ws = workspace;
   a.B = cfg->B; a.H = cfg->H; a.T = cfg->T; a.L = cfg->L; a.rank = cfg->rank;
+  a.ckpt = nullptr; a.ckpt_bh = 0; a.ckpt_shift = 0;
 
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const bool lg = (cfg->flags & CARVE_DECAY_LOGITS) != 0, nrm = (cfg->flags & CARVE_QK_L2NORM) != 0;
-  const hipError_t e = lg ? (nrm ? dispatch_fwd<true, true>(cfg, a, s) : dispatch_fwd<true, false>(cfg, a, s))
-                          : (nrm ? dispatch_fwd<false, true>(cfg, a, s) : dispatch_fwd<false, false>(cfg, a, s));
+  const hipError_t e = dispatch_fwd_flags(cfg, a, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     std::snprintf(g_hip_msg, sizeof(g_hip_msg), "%s", hipGetErrorString(e));
     return CARVE_EHIP;
@@ -381,13 +415,31 @@ extern "C" int carve_chunk_bwd(const carve_config* cfg,
   a.B = cfg->B; a.H = cfg->H; a.T = cfg->T; a.L = cfg->L; a.rank = cfg->rank;
   a.norm = (cfg->flags & CARVE_QK_L2NORM) != 0;
   a.detach = (cfg->flags & CARVE_DETACH_MEAN) != 0;
+  a.pre_ckpt = bwd_from_forward(cfg) && cfg->T > 0;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool lg = (cfg->flags & CARVE_DECAY_LOGITS) != 0;
-  hipError_t e;
-  if (cfg->dtype == CARVE_BF16)
-    e = lg ? dispatch_bwd_width<carve::bf16, true>(cfg, a, s) : dispatch_bwd_width<carve::bf16, false>(cfg, a, s);
-  else
-    e = lg ? dispatch_bwd_width<float, true>(cfg, a, s) : dispatch_bwd_width<float, false>(cfg, a, s);
+  hipError_t e = hipSuccess;
+  if (a.pre_ckpt) {
+    // the forward pair writes the state at every chunk start into the
+    // backward's checkpoints (chunk c starts at block c L / 64)
+    const BwdBytes bb = bwd_bytes(cfg);
+    unsigned char* wsb = static_cast<unsigned char*>(workspace);
+    carve::FwdArgs f;
+    f.q = q; f.k = k; f.v = v; f.g = g; f.bx = bx; f.w = w;
+    f.ub_down = nullptr; f.ub_up = nullptr;
+    f.state_in = state_in; f.mean_in = mean_in;
+    f.o = wsb + bb.o; f.state_out = nullptr; f.mean_out = nullptr;
+    f.ws = wsb + bb.img;
+    f.B = cfg->B; f.H = cfg->H; f.T = cfg->T; f.L = cfg->L; f.rank = 0;
+    f.ckpt = static_cast<float*>(workspace);
+    f.ckpt_bh = carve::BwdWs(cfg->dk, cfg->T, cfg->L, 0, a.norm != 0).total;
+    f.ckpt_shift = cfg->L == 2 * kParallelBlock ? 1 : 0;
+    e = dispatch_fwd_ckpt_flags(cfg, f, s);
+  }
+  if (e == hipSuccess)
+    e = cfg->dtype == CARVE_BF16
+            ? (lg ? dispatch_bwd_width<carve::bf16, true>(cfg, a, s) : dispatch_bwd_width<carve::bf16, false>(cfg, a, s))
+            : (lg ? dispatch_bwd_width<float, true>(cfg, a, s) : dispatch_bwd_width<float, false>(cfg, a, s));
   if (e != hipSuccess) {
     std::snprintf(g_hip_msg, sizeof(g_hip_msg), "%s", hipGetErrorString(e));
     return CARVE_EHIP;

@@ -45,6 +45,10 @@ struct FwdArgs {
   void* o; float* state_out; float* mean_out;
   void* ws;
   int B, H, T, L, rank;
+  // the state pass's checkpointing variant only: fp32 state [dv][dk] at the
+  // start of every (1 << ckpt_shift)-th block, the k-th at
+  // ckpt + bh ckpt_bh + k dv dk
+  float* ckpt; size_t ckpt_bh; int ckpt_shift;
 };
 
 constexpr float kSpanLimit2 = 96.0f;   // max decay (log2 units) inside a 16-row sub-block

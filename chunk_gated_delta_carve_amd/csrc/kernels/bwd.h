@@ -54,6 +54,7 @@ struct BwdArgs {
   int B, H, T, L, rank;
   int norm;   // nonzero: q, k are used over their L2 norms (inverse norms in the workspace)
   int detach; // nonzero: the gate's chunk means are constants (no dm from the gate)
+  int pre_ckpt; // nonzero: the chunk-start states are already in the workspace (no forward sweep)
 };
 
 // Workspace of one (batch, head), in floats: the chunk checkpoints and the
@@ -768,7 +769,8 @@ carve_bwd_split_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
-  for (int c = 0; c < nc; ++c) {
+  const int nsweep = kContent || !a.pre_ckpt ? nc : 0;
+  for (int c = 0; c < nsweep; ++c) {
     const int t0 = c * L, t1 = min(T, t0 + L);
     st4(ws + lay.ckpt + (size_t)c * DD + rowoff, s);
     if constexpr (kContent) {

@@ -318,7 +318,9 @@ constexpr int kRingSpins = 1 << 22;
 // loads of the last sets are clamped into range so that every set always
 // has one load group in flight and the waits before a block cover only its
 // own loads.
-template <typename E, int DK, int DV, int BL>
+// kCkpt: the chain also stores the state entering every (1 << ckpt_shift)-th
+// block at a.ckpt (a variant of its own, so the plain pass carries no check).
+template <typename E, int DK, int DV, int BL, bool kCkpt = false>
 __global__ void __launch_bounds__(kStateThreads)
 carve_state_kernel(FwdArgs a) {
   using B = Block<E, DK, DV, BL>;
@@ -388,6 +390,14 @@ carve_state_kernel(FwdArgs a) {
     auto step = [&](int blk, Set& r, bool refill) {
       Frag sf[NF];
       B::state_frags(St, sf);
+      if constexpr (kCkpt) {
+        if ((blk & ((1 << a.ckpt_shift) - 1)) == 0) {   // the state entering the block
+          float* S = a.ckpt + (size_t)bh * a.ckpt_bh + (size_t)(blk >> a.ckpt_shift) * (DV * DK);
+#pragma unroll
+          for (int dt = 0; dt < TD; ++dt)
+            *reinterpret_cast<f32x4*>(S + (size_t)(e0 + cc) * DK + 16 * dt + 4 * gq) = St[dt];
+        }
+      }
       // Publish the previous block (its ring writes finished long ago, so the
       // release costs nothing), then make sure slot blk % R is free: block
       // blk - R must have been read by its output wave.

@@ -159,7 +159,10 @@ int carve_chunk_fwd(const carve_config* cfg,
  *               state at every chunk start and one chunk's per-token states,
  *               4 (nc + L) dk dv bytes per (batch, head), plus small vectors;
  *               with rank == 0 also every token's per-slice column sums,
- *               4 T (dk / 16) (4 dk + 1) bytes per (batch, head)
+ *               4 T (dk / 16) (4 dk + 1) bytes per (batch, head); in bf16
+ *               with rank == 0 and L a multiple of 64, also the forward
+ *               pair's block images and an output, since the chunk-start
+ *               states then come from the forward's chunk-parallel state pass
  * No output may overlap an input, another output or the workspace, except
  * for the two aliases above. Results are deterministic (no atomics).
  * Returns the status codes of carve_chunk_fwd. */

@@ -189,7 +189,9 @@ def test_bwd_workspace_size():
     """The backward workspace holds, per (batch, head), the fp32 state at every
     chunk start and one chunk's per-token states, small per-chunk vectors, and
     every token's column sums per row slice (one slice of all rows with a
-    projection at d = 64, d / 16 slices without one, none at d = 128 with one)."""
+    projection at d = 64, d / 16 slices without one, none at d = 128 with one);
+    in bf16 without a projection and with L a multiple of 64, also the
+    forward pair's block images and output."""
     sh = _lib.ref_shapes(cfg())                      # B2 H3 T100 d64 L64 rank 4: two chunks
     vecs = 2 * 2 * 64 + 2 * 4 + 2 * 4 * 64           # z and m per chunk, U_down m per chunk, dU partials
     per_bh = 2 * 64 * 64 + 64 * 64 * 64 + vecs
@@ -201,9 +203,17 @@ def test_bwd_workspace_size():
     assert _lib.ref_shapes(cfg(B=0)).bwd_workspace_bytes == 0
     # without a projection the rows of a head are split into d / 16 slices, and
     # each token keeps every slice's four column sums and its dw share
-    sh0 = _lib.ref_shapes(cfg(rank=0))
     per_bh0 = 2 * 64 * 64 + 64 * 64 * 64 + 2 * 2 * 64 + 100 * 4 * (4 * 64 + 1)
-    assert sh0.bwd_workspace_bytes == 6 * 4 * ((per_bh0 + 3) // 4 * 4)
+    own0 = 6 * 4 * ((per_bh0 + 3) // 4 * 4)
+    assert _lib.ref_shapes(cfg(rank=0, dtype=_lib.CARVE_F32)).bwd_workspace_bytes == own0
+    per_bh32 = 4 * 64 * 64 + 32 * 64 * 64 + 4 * 2 * 64 + 100 * 4 * (4 * 64 + 1)   # L = 32: four chunks
+    assert _lib.ref_shapes(cfg(rank=0, L=32)).bwd_workspace_bytes == 6 * 4 * per_bh32
+    # in bf16 with L a multiple of 64 the forward pair supplies the chunk-start
+    # states: its block images and an output follow, 256-byte aligned
+    sh0 = _lib.ref_shapes(cfg(rank=0))
+    fwd = sh0.workspace_bytes
+    assert fwd > 0
+    assert sh0.bwd_workspace_bytes == (own0 + 255) // 256 * 256 + fwd + 2 * 100 * 3 * 64 * 2
 
 
 def test_bwd_argument_errors(L):

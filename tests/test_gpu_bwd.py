@@ -109,6 +109,12 @@ BWD_CASES = [
     ("bf16-d128-L64-r0-ragged-200", "bf16", 1, 2, 200, 128, 64, 0),
     ("f32-d128-L16-r0-T1", "f32", 2, 1, 1, 128, 16, 0),
     ("f32-d64-L32-r0-ragged-47", "f32", 3, 1, 47, 64, 32, 0),
+    # bf16 without a projection: chunk-start states from the forward pair when
+    # L is a multiple of its 64-token blocks (every block or every other one),
+    # from the backward's own sweep otherwise
+    ("bf16-d64-L128-r0-ragged-300", "bf16", 2, 2, 300, 64, 128, 0),
+    ("bf16-d128-L128-r0-ragged-129", "bf16", 1, 2, 129, 128, 128, 0),
+    ("bf16-d64-L32-r0-ragged-100", "bf16", 2, 2, 100, 64, 32, 0),
 ]
 
 
@@ -132,14 +138,18 @@ def test_backward_without_state_gradients(torch_cuda):
     assert_grads(got, bwd_oracle(inp, "bf16", 64, do, None, None, None, None), TOL["bf16"], "no state")
 
 
-@pytest.mark.parametrize("rank", [0, 8])
-def test_backward_with_decay_logits(torch_cuda, rank):
-    """Raw decay logits: dg is the gradient of the logit a, dg_g * (-sigmoid(a))."""
-    wl = workload("logits", "f32", 1, 2, 96, 64, 32, rank, 6300)
+@pytest.mark.parametrize("dtype,L,rank", [("f32", 32, 0), ("f32", 32, 8), ("bf16", 64, 0)],
+                         ids=["f32-r0", "f32-r8", "bf16-r0-forward-checkpoints"])
+def test_backward_with_decay_logits(torch_cuda, dtype, L, rank):
+    """Raw decay logits: dg is the gradient of the logit a, dg_g * (-sigmoid(a)).
+    In bf16 without a projection the forward pair forms the chunk-start states
+    from the same raw logits."""
+    wl = workload("logits", dtype, 1, 2, 96 if dtype == "f32" else 200, 64, L, rank, 6300)
+    T = wl.T
     inp = make_inputs(wl, decay_logits=True)
-    do, dSo, dmo, S_in, m_in = cotangents(1, 2, 96, 64, "f32", 6301)
-    got = bwd_gpu(torch_cuda, inp, "f32", 32, do, dSo, dmo, S_in, m_in, logits=True)
-    assert_grads(got, bwd_oracle(inp, "f32", 32, do, dSo, dmo, S_in, m_in, logits=True), TOL["f32"], "logits")
+    do, dSo, dmo, S_in, m_in = cotangents(1, 2, T, 64, dtype, 6301)
+    got = bwd_gpu(torch_cuda, inp, dtype, L, do, dSo, dmo, S_in, m_in, logits=True)
+    assert_grads(got, bwd_oracle(inp, dtype, L, do, dSo, dmo, S_in, m_in, logits=True), TOL[dtype], "logits")
 
 
 DETACH_CASES = [
