@@ -20,7 +20,9 @@
 // Both schedules below share the plan:
 //   1. A forward sweep stores the state at every chunk start (and, with a
 //      projection, each chunk's gate bias z, gate mean m_{c-1} and
-//      U_down m_{c-1}).
+//      U_down m_{c-1}). Without a projection, in bf16 with L a multiple of
+//      64, the forward's chunk-parallel pair has already written those
+//      states (pre_ckpt) and the sweep is skipped.
 //   2. For each chunk from the last: the chunk's states before each token are
 //      recomputed from its checkpoint into the workspace, then the tokens are
 //      walked backwards with dS in registers. Token inputs are staged into
