@@ -88,8 +88,7 @@ def cpu_baseline(wl, inp, budget_s):
 KERNEL_SOURCES = ("chunk_gated_delta_carve_amd/csrc/carve_lib.hip",
                   "chunk_gated_delta_carve_amd/csrc/kernels/common.h",
                   "chunk_gated_delta_carve_amd/csrc/kernels/block.h",
-                  "chunk_gated_delta_carve_amd/csrc/kernels/kernels.h",
-                  "chunk_gated_delta_carve_amd/csrc/kernels/fused.h")
+                  "chunk_gated_delta_carve_amd/csrc/kernels/kernels.h")
 COPY_BYTES = 256 * 1024 * 1024      # calibration copy: reads and writes this many bytes
 
 
@@ -530,9 +529,6 @@ def main():
     ap.add_argument("--qk-l2norm", action="store_true",
                     help="let the kernels normalise q and k per token (CARVE_QK_L2NORM); also times the unfused "
                          "alternative (torch normalises q and k, then the plain call)")
-    ap.add_argument("--two-pass", action="store_true",
-                    help="bf16 d=64 without a projection: run the two-launch chunk-parallel schedule "
-                         "(CARVE_TWO_PASS) instead of the one-pass one")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass carve_chunk_bwd on the workload instead of the forward")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -580,17 +576,13 @@ def main():
     o = torch.empty((B, T, H, dv), dtype=tdtype, device="cuda")
     stream = torch.cuda.current_stream()
     from chunk_gated_delta_carve_amd import recurrent_ref_shapes
-    from chunk_gated_delta_carve_amd.api import make_config
-    from chunk_gated_delta_carve_amd import _lib as carve_lib
-    ws_bytes = int(carve_lib.ref_shapes(make_config(B, H, T, dk, dv, L, rank, tdtype, logits, norm,
-                                                    two_pass=args.two_pass)).workspace_bytes)
-    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")   # zero-filled once (one-pass flags)
+    ws_bytes = int(recurrent_ref_shapes(B, H, T, dk, dv, L, rank, tdtype).workspace_bytes)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     ub = (t["U_down"], t["U_up"]) if rank > 0 else (None, None)
 
     def step():
         return chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["bx"], t["w"], L=L, ub_down=ub[0], ub_up=ub[1],
-                         return_state=True, out=o, workspace=ws, decay_logits=logits, qk_l2norm=norm,
-                         two_pass=args.two_pass)
+                         return_state=True, out=o, workspace=ws, decay_logits=logits, qk_l2norm=norm)
 
     g_buf = torch.empty_like(t["g"])
 
@@ -606,7 +598,7 @@ def main():
             q = torch.nn.functional.normalize(q, dim=-1, eps=1e-12)
             k = torch.nn.functional.normalize(k, dim=-1, eps=1e-12)
         return chunk_fwd(q, k, t["v"], g, t["bx"], t["w"], L=L, ub_down=ub[0], ub_up=ub[1],
-                         return_state=True, out=o, workspace=ws, two_pass=args.two_pass)
+                         return_state=True, out=o, workspace=ws)
 
     if args.calibrate_copy:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
@@ -691,8 +683,8 @@ def main():
     mfma_peak = MFMA_PEAK_TFLOPS["bf16" if wl.dtype == "bf16" else "f32"]
     tokens = B * T
     parallel = rank == 0 and wl.dtype == "bf16"
-    kernels = (("carve_fused_kernel" if dk == 64 else "carve_intra_kernel + carve_state_kernel (one call)")
-               if parallel else "carve_chunk_serial_kernel")
+    kernels = ("carve_intra_kernel + carve_state_kernel (one call)" if parallel
+               else "carve_chunk_serial_kernel")
     workload = (f"carve_chunk_fwd B{B} H{H} T{T} dk{dk} dv{dv} L{L} {wl.dtype}, "
                 + ("no content projection" if rank == 0 else f"content projection rank {rank}"))
     line = {

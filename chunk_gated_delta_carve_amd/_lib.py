@@ -11,7 +11,6 @@ CARVE_F32, CARVE_BF16 = 0, 1
 CARVE_DECAY_LOGITS = 1
 CARVE_QK_L2NORM = 2
 CARVE_DETACH_MEAN = 4
-CARVE_TWO_PASS = 8
 EXPORTED = ("carve_recurrent_ref_shapes", "carve_chunk_fwd", "carve_chunk_bwd", "carve_recurrent_step",
             "carve_error_string")
 
@@ -23,7 +22,7 @@ class CarveConfig(ctypes.Structure):
 class CarveShapes(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in
                 ("q", "k", "v", "g", "bx", "w", "ub_down", "ub_up", "o", "state", "mean",
-                 "workspace_bytes", "bwd_workspace_bytes", "workspace_zero_bytes")]
+                 "workspace_bytes", "bwd_workspace_bytes")]
 
 
 class CarveError(RuntimeError):

@@ -17,50 +17,15 @@ _DTYPES = {torch.float32: _lib.CARVE_F32, torch.bfloat16: _lib.CARVE_BF16}
 
 
 def make_config(B, H, T, dk, dv, L, rank, dtype, decay_logits=False, qk_l2norm=False,
-                detach_mean=False, two_pass=False) -> _lib.CarveConfig:
+                detach_mean=False) -> _lib.CarveConfig:
     flags = ((_lib.CARVE_DECAY_LOGITS if decay_logits else 0) | (_lib.CARVE_QK_L2NORM if qk_l2norm else 0)
-             | (_lib.CARVE_DETACH_MEAN if detach_mean else 0) | (_lib.CARVE_TWO_PASS if two_pass else 0))
+             | (_lib.CARVE_DETACH_MEAN if detach_mean else 0))
     return _lib.CarveConfig(B, H, T, dk, dv, L, rank, _DTYPES[dtype] if isinstance(dtype, torch.dtype) else dtype,
                             flags)
 
 
 def recurrent_ref_shapes(B, H, T, dk, dv, L, rank=0, dtype=torch.bfloat16) -> _lib.CarveShapes:
     return _lib.ref_shapes(make_config(B, H, T, dk, dv, L, rank, dtype))
-
-
-# Workspaces of the one-pass forward schedule, one per (device, stream). Its
-# flag prefix must be zero when a call starts; a completed call leaves it zero
-# for the next call of the same shape, and the prefix is zeroed again (on the
-# call's stream, ahead of it) when the shape changes. The buffer is only ever
-# handed to one-pass calls; other schedules get a fresh scratch buffer.
-_FWD_WS = {}
-
-
-def forward_workspace(nbytes, device, stream, zero_bytes=0, layout=None):
-    """The cached one-pass forward workspace for (device, stream) with at
-    least nbytes bytes, its first zero_bytes bytes zero at the next call on
-    `stream` when `layout` (the flag layout: batch x heads, blocks) differs
-    from the previous call's."""
-    key = (device.index, int(stream))
-    entry = _FWD_WS.get(key)
-    if entry is None or entry[0].numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
-        torch.cuda.synchronize(device)          # zero before any stream uses it
-        entry = [ws, layout]
-        _FWD_WS[key] = entry
-    elif layout is not None and entry[1] != layout and zero_bytes:
-        s = torch.cuda.ExternalStream(int(stream), device=device) if int(stream) else torch.cuda.default_stream(device)
-        with torch.cuda.stream(s):
-            entry[0][:zero_bytes].zero_()
-    if layout is not None:
-        entry[1] = layout
-    return entry[0]
-
-
-def workspace_error(ws) -> int:
-    """The sticky error word at the start of a forward workspace (0: no
-    bounded wait ran out and no exchange crossed an XCD). Synchronises."""
-    return int(ws[:4].view(torch.int32).item())
 
 
 def _ptr(t):
@@ -81,19 +46,13 @@ def _need(t, name, shape, dtype, device):
 
 
 def chunk_fwd(q, k, v, g, bx, w, L=64, ub_down=None, ub_up=None, state_in=None, mean_in=None,
-              return_state=False, out=None, workspace=None, stream=None, decay_logits=False, qk_l2norm=False,
-              two_pass=False):
+              return_state=False, out=None, workspace=None, stream=None, decay_logits=False, qk_l2norm=False):
     """CARVE forward pass. Shapes: q, k, g, bx [B,T,H,dk]; v [B,T,H,dv]; w [B,T,H];
     ub_down [H,r,dv]; ub_up [H,dk,r]; state_in [B,H,dv,dk] fp32; mean_in [B,H,dv] fp32.
     With decay_logits, g holds raw decay logits a and the kernels use the
     log-decay -softplus(a). With qk_l2norm, q and k are divided per token by
-    their L2 norms inside the kernels. two_pass selects the two-launch
-    chunk-parallel schedule where the one-pass one would run. A workspace
-    passed in must have its flag prefix (workspace_zero_bytes of
-    recurrent_ref_shapes) zero, as carve.h states: zero-fill it before its
-    first use and whenever B, H or T change; without one, a cached
-    workspace per (device, stream) is used and kept that way. Returns o
-    [B,T,H,dv] (and (state_out, mean_out) when return_state)."""
+    their L2 norms inside the kernels. Returns o [B,T,H,dv] (and (state_out,
+    mean_out) when return_state)."""
     if q.device.type != "cuda":
         raise ValueError("chunk_fwd runs on the GPU only; move the inputs to a cuda device")
     B, T, H, dk = q.shape
@@ -113,7 +72,7 @@ def chunk_fwd(q, k, v, g, bx, w, L=64, ub_down=None, ub_up=None, state_in=None, 
     _need(state_in, "state_in", (B, H, dv, dk), torch.float32, dev)
     _need(mean_in, "mean_in", (B, H, dv), torch.float32, dev)
 
-    cfg = make_config(B, H, T, dk, dv, L, rank, dt, decay_logits, qk_l2norm, two_pass=two_pass)
+    cfg = make_config(B, H, T, dk, dv, L, rank, dt, decay_logits, qk_l2norm)
     sh = _lib.ref_shapes(cfg)
     o = out if out is not None else torch.empty((B, T, H, dv), dtype=dt, device=dev)
     _need(o, "out", (B, T, H, dv), dt, dev)
@@ -122,13 +81,10 @@ def chunk_fwd(q, k, v, g, bx, w, L=64, ub_down=None, ub_up=None, state_in=None, 
         state_out = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
         mean_out = torch.empty((B, H, dv), dtype=torch.float32, device=dev)
     ws_bytes = int(sh.workspace_bytes)
+    if ws_bytes and (workspace is None or workspace.numel() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
-    if ws_bytes and workspace is None:
-        workspace = (forward_workspace(ws_bytes, dev, stream, int(sh.workspace_zero_bytes), (B * H, (T + 63) // 64))
-                     if sh.workspace_zero_bytes else torch.empty(ws_bytes, dtype=torch.uint8, device=dev))
-    if ws_bytes and workspace.numel() < ws_bytes:
-        raise ValueError(f"workspace: {workspace.numel()} bytes, the call needs {ws_bytes}")
     code = _lib.lib().carve_chunk_fwd(
         ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(bx), _ptr(w),
         _ptr(ub_down), _ptr(ub_up), _ptr(state_in), _ptr(mean_in),

@@ -9,7 +9,6 @@
 
 #include "carve.h"
 #include "kernels/kernels.h"
-#include "kernels/fused.h"
 #include "kernels/bwd.h"
 #include "kernels/step.h"
 
@@ -28,10 +27,8 @@ int check_config(const carve_config* c) {
   if (c->dtype != CARVE_F32 && c->dtype != CARVE_BF16) return CARVE_EINVAL;
   if (!valid_width(c->dk) || !valid_width(c->dv) || c->dk != c->dv) return CARVE_EUNSUPPORTED;
   if (!valid_chunk(c->L)) return CARVE_EUNSUPPORTED;
-  // the one-pass schedule's grid (chain workgroups, then eight per head group and block)
-  if (carve::fused_grid(c->B * c->H, (c->T + 63) / 64) > 0x7fffffffLL) return CARVE_EUNSUPPORTED;
   if (c->rank > 64) return CARVE_EUNSUPPORTED;
-  if (c->flags & ~(CARVE_DECAY_LOGITS | CARVE_QK_L2NORM | CARVE_DETACH_MEAN | CARVE_TWO_PASS)) return CARVE_EINVAL;
+  if (c->flags & ~(CARVE_DECAY_LOGITS | CARVE_QK_L2NORM | CARVE_DETACH_MEAN)) return CARVE_EINVAL;
   // offsets are computed in 64-bit, grids in 32-bit (the state pass launches
   // 8 (B H / 8 rounded up) (d_v / 16) workgroups)
   if ((int64_t)c->B * c->H > 0x7fffffffLL / 8 - 8) return CARVE_EUNSUPPORTED;
@@ -64,18 +61,6 @@ int serial_block(const carve_config* c) {
 // the chunk-parallel schedule (intra + state kernels, block length 64) is used.
 bool chunk_parallel(const carve_config* c) { return c->rank == 0 && c->dtype == CARVE_BF16; }
 constexpr int kParallelBlock = 64;
-
-// The one-pass schedule (carve_fused_kernel): bf16, d = 64, no projection,
-// unless the caller asks for the two-launch pair.
-bool one_pass(const carve_config* c) {
-  return chunk_parallel(c) && c->dk == 64 && !(c->flags & CARVE_TWO_PASS);
-}
-
-int64_t fused_workspace_bytes(const carve_config* c) {
-  const int64_t nblk = (c->T + kParallelBlock - 1) / kParallelBlock;
-  if ((int64_t)c->B * c->H * nblk == 0) return 0;   // nothing is exchanged (T = 0 passes the state through)
-  return carve::FusedWs((int64_t)c->B * c->H, nblk).total;
-}
 
 int64_t parallel_workspace_bytes(const carve_config* c) {
   const int64_t nblk = (c->T + kParallelBlock - 1) / kParallelBlock;
@@ -157,17 +142,6 @@ hipError_t launch_parallel(const carve::FwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool LG, bool NRM>
-hipError_t launch_fused(const carve::FwdArgs& a, hipStream_t s) {
-  using LI = carve::BlockLayout<carve::bf16, 64, 64, kParallelBlock, carve::kIntraWaves>;
-  constexpr auto kern = carve::carve_fused_kernel<LG, NRM>;
-  hipError_t e = set_lds<kern>(LI::intra_bytes);
-  if (e != hipSuccess) return e;
-  const int BH = a.B * a.H, nblk = (a.T + kParallelBlock - 1) / kParallelBlock;
-  hipLaunchKernelGGL(kern, dim3((unsigned)carve::fused_grid(BH, nblk)), dim3(LI::NT), LI::intra_bytes, s, a);
-  return hipGetLastError();
-}
-
 template <typename E, int D, bool LG, bool NRM>
 hipError_t dispatch_block(const carve::FwdArgs& a, int bl, hipStream_t s) {
   switch (bl) {
@@ -186,7 +160,6 @@ hipError_t dispatch_block(const carve::FwdArgs& a, int bl, hipStream_t s) {
 template <bool LG, bool NRM>
 hipError_t dispatch_fwd(const carve_config* cfg, const carve::FwdArgs& a, hipStream_t s) {
   const int bl = serial_block(cfg);
-  if (one_pass(cfg)) return launch_fused<LG, NRM>(a, s);
   if (chunk_parallel(cfg))
     return cfg->dk == 64 ? launch_parallel<64, LG, NRM>(a, s) : launch_parallel<128, LG, NRM>(a, s);
   if (cfg->dtype == CARVE_BF16)
@@ -316,12 +289,8 @@ extern "C" int carve_recurrent_ref_shapes(const carve_config* cfg, carve_shapes*
   out->ub_up = H * dk * r;
   out->state = B * H * dv * dk;
   out->mean = B * H * dv;
-  out->workspace_bytes = one_pass(cfg) ? fused_workspace_bytes(cfg)
-                        : chunk_parallel(cfg) ? parallel_workspace_bytes(cfg) : 0;
+  out->workspace_bytes = chunk_parallel(cfg) ? parallel_workspace_bytes(cfg) : 0;
   out->bwd_workspace_bytes = bwd_bytes(cfg).total;
-  out->workspace_zero_bytes = out->workspace_bytes > 0 && one_pass(cfg)
-                                  ? carve::FusedWs((int64_t)cfg->B * cfg->H, (cfg->T + kParallelBlock - 1) / kParallelBlock).mc
-                                  : 0;
   return CARVE_OK;
 }
 

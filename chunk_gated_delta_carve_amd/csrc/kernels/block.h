@@ -317,8 +317,8 @@ struct Block {
 #pragma unroll
         for (int i = 0; i < RPL; ++i) {
           const uint32_t off = ((uint32_t)min(gc.r0 + i, nvalid - 1) * hk + gc.d0) * (uint32_t)sizeof(E);
-          // read once: streaming (non-temporal) loads, so they do not push
-          // data that is read again out of the L2 (with d_k = 128 and
+          // read once: streaming (non-temporal) loads, so that they do not
+          // push the workspace images out of the caches (with d_k = 128 and
           // normalisation the partner wave reads q, k rows a second time)
           if constexpr (kNorm && DK == 128) {
             q[i] = *reinterpret_cast<const e4*>(at(Qb, off));
@@ -766,17 +766,6 @@ struct Block {
   template <bool kImage = false>
   __device__ static void solve(const Smem& s, const E (&qd)[16], const f32x4 (&Pt)[TPW],
                                unsigned char* img = nullptr) {
-    if constexpr (kImage)
-      solve_then<true>(s, qd, Pt, [&](const e4 (&X)[NB][CTW], bool isW, int x0) { image_from_x(s, X, isW, x0, img); });
-    else
-      solve_then<false>(s, qd, Pt, 0);
-  }
-  // The solve with a finishing stage of the caller's choice: with kFinish,
-  // after a barrier (P, Qd and KdT complete in LDS), fin(X, isW, x0) receives
-  // this wave's [W | U] tiles; no final barrier. Without kFinish, the
-  // transposed stores for affine() and a final barrier, as solve<false>.
-  template <bool kFinish, typename Fin>
-  __device__ static void solve_then(const Smem& s, const E (&qd)[16], const f32x4 (&Pt)[TPW], Fin fin) {
     const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     const int gq = lane >> 4, cc = lane & 15;
     // all column tiles of a wave lie on the same side of [W | U]
@@ -853,9 +842,9 @@ struct Block {
 #pragma unroll
       for (int t = 0; t < CTW; ++t) X[I][t] = M16::round(M16::mma(Trow[I], M16::round(acc[t]), zero4()));
     }
-    if constexpr (kFinish) {
+    if constexpr (kImage) {
       __syncthreads();                               // P, Qd and KdT are complete
-      fin(X, isW, col0 - cc);
+      image_from_x(s, X, isW, col0 - cc, img);
       return;
     }
     // transposed stores: lane holds rows 4gq..4gq+3 of column col -> 4 consecutive

@@ -78,18 +78,8 @@ typedef enum { CARVE_F32 = 0, CARVE_BF16 = 1 } carve_dtype;
  *                       gate; no gradient reaches earlier outputs or mean_in
  *                       through it (d_mean_out still reaches the last chunk's
  *                       outputs). Without the bit the gradients are the exact
- *                       ones, through every stale mean.
- *   CARVE_TWO_PASS      forward only: with bf16 inputs, dk = dv = 64 and no
- *                       content projection, run the two-launch chunk-parallel
- *                       schedule (a per-block kernel writes every block's
- *                       state-pass operands to the workspace, a per-head
- *                       kernel then carries the state) instead of the
- *                       default one-pass schedule. Both give the same o and
- *                       state bit for bit; the bit exists to compare them
- *                       and as a fallback on a device whose workgroup
- *                       placement the one-pass schedule cannot use (see
- *                       carve_chunk_fwd). Other configurations ignore it. */
-enum { CARVE_DECAY_LOGITS = 1, CARVE_QK_L2NORM = 2, CARVE_DETACH_MEAN = 4, CARVE_TWO_PASS = 8 };
+ *                       ones, through every stale mean. */
+enum { CARVE_DECAY_LOGITS = 1, CARVE_QK_L2NORM = 2, CARVE_DETACH_MEAN = 4 };
 
 /* Problem description. B batch, H heads, T tokens, dk key width, dv value
  * width, L chunk length of the content signal, rank of U_b (0 = no content
@@ -109,10 +99,6 @@ typedef struct {
   int64_t state, mean;         /* optional fp32 state_in/out and mean_in/out */
   int64_t workspace_bytes;     /* device scratch carve_chunk_fwd needs */
   int64_t bwd_workspace_bytes; /* device scratch carve_chunk_bwd needs */
-  int64_t workspace_zero_bytes; /* leading bytes of carve_chunk_fwd's workspace that
-                                   must be zero before its first use (the one-pass
-                                   schedule's error word and ready flags; 0 when the
-                                   schedule keeps no flags) */
 } carve_shapes;
 
 /* Validates `cfg` and fills `out` with the shape contract of the recurrence:
@@ -139,25 +125,10 @@ int carve_recurrent_ref_shapes(const carve_config* cfg, carve_shapes* out);
  *              receives the mean of the last (possibly partial) chunk, or
  *              mean_in when T == 0.
  *   workspace  device scratch of at least shapes.workspace_bytes (may be NULL
- *              when that is 0). The one-pass schedule (bf16, dk = dv = 64,
- *              rank 0, CARVE_TWO_PASS clear) keeps ready flags in it: its
- *              first shapes.workspace_zero_bytes bytes must be zero when the
- *              call starts. A call that completes leaves them zero, so one
- *              zero-fill serves any number of one-pass calls of the same B, H
- *              and T on this workspace. The flag layout depends on B, H and
- *              T, and the rest of the workspace is scratch, so zero-fill the
- *              prefix again before a call of another shape, or after the
- *              workspace served any other call.
- *              The first 4 bytes are then a sticky error word: nonzero when
- *              a bounded wait of the kernels ran out (bit 0) or workgroups
- *              that exchange data through the L2 did not share an XCD (bit
- *              1); the affected outputs are NaN. Zero-fill it again before
- *              reusing such a workspace, and pass CARVE_TWO_PASS on a device
- *              that sets bit 1.
+ *              when that is 0)
  *   stream     hipStream_t as void*
  * B, H or T may be 0 (nothing to compute; with T == 0 the state and mean pass
- * through). T need not be a multiple of L. Calls that share a workspace must
- * not overlap in time. */
+ * through). T need not be a multiple of L. */
 int carve_chunk_fwd(const carve_config* cfg,
                     const void* q, const void* k, const void* v,
                     const void* g, const void* bx, const void* w,
