@@ -7,13 +7,17 @@ Default workload: B=4, H=12, T=2048, d_k=d_v=64, L=64, bf16 inputs with fp32
 accumulation, no content projection (seeded synthetic data); --workload picks
 another of the named shapes.
 
-Prints one JSON line. `roofline` covers one call of the layer (its kernels
-run back to back on one stream): algorithmic bytes per call over the GPU time
-per call, taken from one pair of HIP events recorded on that stream around the
-timed steps. `mfma` is the matrix-core roofline of the same call (algorithmic
-FLOPs over the same time, against the dense peak of the input type), with the
-committed rocprofv3 matrix-core counters when they match the kernel sources.
-`cpu_baseline` is the float64 oracle timed on this host.
+Prints one JSON line. The timed steps run back to back and rotate through
+several copies of the inputs, so that no step finds its inputs in the 256 MB
+Infinity Cache. `roofline` covers one call of the layer (its kernels run back
+to back on one stream): algorithmic bytes per call over the GPU time per call,
+taken from one pair of HIP events recorded on that stream around the timed
+steps; the same call timed on one input copy, and single calls after a 512 MB
+cache flush, are reported beside it. `mfma` is the matrix-core roofline of the
+same call (algorithmic FLOPs over the same time, against the dense peak of the
+input type), with the committed rocprofv3 matrix-core counters when they match
+the kernel sources. `cpu_baseline` is the float64 oracle timed on this host's
+cores (worker processes over the independent (batch, head) pairs).
 """
 import argparse
 import json
@@ -51,38 +55,99 @@ def algorithmic_flops(B, T, H, dk, dv, L, rank=0):
     return B * H * (full * chunk(L) + (chunk(tail) if tail else 0))
 
 
-def cpu_baseline(wl, inp, budget_s):
-    """Time the float64 oracle on this host, single-threaded, on a bounded sample
-    of the workload: whole sequences when one pass fits the budget, else a
-    prefix of every sequence sized to it. Returns head-token-rate in tokens/s
-    (batch rows x time steps, all heads), as the GPU value is."""
-    import numpy as np
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_workers():
+    """Worker processes for the oracle baseline: the CPUs this process may run
+    on, at most 16 (a one-GPU share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _oracle_task(args):
+    """One worker's share of the oracle baseline (runs in a spawned process
+    with BLAS limited to one thread): `passes` runs of the float64 oracle over
+    a group of (batch, head) pairs. Returns the wall-clock start and end."""
     from threadpoolctl import threadpool_limits
     from oracle import carve_forward
+    x, L, ub, passes = args
+    with threadpool_limits(1):
+        t0 = time.time()
+        for _ in range(passes):
+            carve_forward(*x, L, **ub)
+        return t0, time.time()
+
+
+def cpu_baseline(wl, inp, budget_s):
+    """Time the float64 oracle on this host's cores, on a bounded sample of the
+    workload. The (batch, head) pairs are independent, so they are split into
+    one group per worker process (BLAS at one thread each) and the groups run
+    in parallel; the sample is whole sequences when the work fits the budget,
+    else a prefix of every sequence sized to it. Returns the head-token rate in
+    tokens/s (batch rows x time steps, all heads), as the GPU value is, over
+    the wall time of the parallel passes."""
+    import multiprocessing as mp
+    import numpy as np
     from chunk_gated_delta_carve_amd.workloads import to_f64
 
-    def run(Tp):
-        f = lambda k: np.ascontiguousarray(to_f64(inp[k][:, :Tp], wl.dtype))
-        ub = {}
-        if wl.rank > 0:
-            ub = dict(U_down=to_f64(inp["U_down"], wl.dtype), U_up=to_f64(inp["U_up"], wl.dtype))
-        t0 = time.perf_counter()
-        carve_forward(f("q"), f("k"), f("v"), f("g"), f("bx"), f("w"), wl.L, **ub)
-        return time.perf_counter() - t0
+    nw = oracle_workers()
+    pairs = [(b, h) for b in range(wl.B) for h in range(wl.H)]
+    groups = [pairs[i::nw] for i in range(nw) if pairs[i::nw]]
 
-    with threadpool_limits(1):
-        probe_T = min(wl.T, 2 * wl.L)
-        rate = probe_T / run(probe_T)                   # time steps per second (all B, H)
-        Tp = wl.T if wl.T / rate <= budget_s else max(wl.L, int(budget_s * rate) // wl.L * wl.L)
-        spent, steps, passes = 0.0, 0, 0
-        while spent < budget_s:
-            spent += run(Tp)
-            steps += Tp
-            passes += 1
+    def tasks(Tp):
+        out = []
+        for grp in groups:
+            x = [np.ascontiguousarray(to_f64(np.stack([inp[k][b, :Tp, h] for b, h in grp], axis=1)[None], wl.dtype))
+                 for k in ("q", "k", "v", "g", "bx", "w")]
+            ub = {}
+            if wl.rank > 0:
+                hs = [h for _, h in grp]
+                ub = dict(U_down=to_f64(inp["U_down"][hs], wl.dtype), U_up=to_f64(inp["U_up"][hs], wl.dtype))
+            out.append((x, wl.L, ub))
+        return out
+
+    env = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    for k in env:
+        os.environ[k] = "1"                            # inherited by the spawned workers
+    try:
+        with mp.get_context("spawn").Pool(len(groups)) as pool:
+            def run(Tp, passes):
+                spans = pool.map(_oracle_task, [t + (passes,) for t in tasks(Tp)])
+                return max(e for _, e in spans) - min(b for b, _ in spans)
+            run(min(wl.T, wl.L), 1)                           # start-up and imports, untimed
+            probe_T = min(wl.T, 2 * wl.L)
+            rate = probe_T / run(probe_T, 1)                  # time steps per second, all pairs
+            Tp = wl.T if wl.T / rate <= budget_s else max(wl.L, int(budget_s * rate) // wl.L * wl.L)
+            per = max(1, int(budget_s * rate / Tp))
+            wall, passes = 0.0, 0
+            while wall < budget_s:
+                wall += run(Tp, per)
+                passes += per
+            steps = Tp * passes
+    finally:
+        for k, v in env.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
     what = ("the whole workload" if Tp == wl.T else f"the first {Tp} of {wl.T} time steps")
-    return {"value": wl.B * steps / spent, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{what} (B={wl.B}, all {wl.H} heads), {passes} pass(es), {spent:.1f} s, "
-                      "one thread"}
+    return {"value": wl.B * steps / wall, "unit": "tokens/s", "cores": len(groups), "kind": "oracle",
+            "sample": f"{what} (B={wl.B}, all {wl.H} heads), {passes} pass(es), {wall:.1f} s wall; "
+                      f"{len(groups)} worker processes over the (batch, head) pairs, one BLAS thread each, "
+                      f"on {cpu_model()}"}
 
 
 KERNEL_SOURCES = ("chunk_gated_delta_carve_amd/csrc/carve_lib.hip",
@@ -524,6 +589,9 @@ def main():
     ap.add_argument("--decay-logits", action="store_true",
                     help="pass raw decay logits and let the kernels form g = -softplus(.) (CARVE_DECAY_LOGITS); "
                          "also times the unfused alternative (a torch softplus pass, then the plain call)")
+    ap.add_argument("--input-copies", type=int, default=4,
+                    help="input copies the timed steps rotate through, so that no step finds its inputs in "
+                         "the 256 MB Infinity Cache (1: every step reads the same inputs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU work budget of the oracle baseline sample")
     ap.add_argument("--qk-l2norm", action="store_true",
@@ -580,8 +648,17 @@ def main():
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     ub = (t["U_down"], t["U_up"]) if rank > 0 else (None, None)
 
-    def step():
-        return chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["bx"], t["w"], L=L, ub_down=ub[0], ub_up=ub[1],
+    # Input copies that the timed steps rotate through: a copy is read again
+    # only after the other copies' steps have streamed far more than the 256
+    # MB Infinity Cache, so every timed step reads its inputs from HBM.
+    copies = [t] + [{k: v.clone() for k, v in t.items()} for _ in range(max(1, args.input_copies) - 1)]
+    rot = [0]
+
+    def step(x=None):
+        if x is None:
+            x = copies[rot[0] % len(copies)]
+            rot[0] += 1
+        return chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["bx"], x["w"], L=L, ub_down=ub[0], ub_up=ub[1],
                          return_state=True, out=o, workspace=ws, decay_logits=logits, qk_l2norm=norm)
 
     g_buf = torch.empty_like(t["g"])
@@ -611,8 +688,9 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: K back-to-back steps between two HIP events on the launch
-    # stream (no events between the steps, so nothing but the steps runs there)
+    # timed region: K back-to-back steps, rotating through the input copies,
+    # between two HIP events on the launch stream (no events between the steps,
+    # so nothing but the steps runs there)
     ev_start = torch.cuda.Event(enable_timing=True)
     ev_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -625,6 +703,15 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = 1e3 * wall / args.steps
     avg_kernel_ms = ev_start.elapsed_time(ev_end) / args.steps   # GPU time of one call
+
+    # the same, every step on one input copy (its inputs stay in the caches)
+    s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s_.record(stream)
+    for _ in range(args.steps):
+        step(copies[0])
+    e_.record(stream)
+    torch.cuda.synchronize()
+    same_input_ms = s_.elapsed_time(e_) / args.steps
 
     # single calls, each between its own pair of events: median and minimum
     single = []
@@ -651,7 +738,7 @@ def main():
     copy_gbs = 2 * COPY_BYTES * 10 / (s.elapsed_time(e) * 1e-3) / 1e9
     del src, dst
 
-    # the same launch with the caches flushed before it (512 MB write, untimed)
+    # single calls with every cache flushed before each (a 512 MB write, untimed)
     flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
     cold = []
     for _ in range(10):
@@ -710,7 +797,12 @@ def main():
                      # the committed counter summaries are of the plain launch
                      "traffic": None if special else measured_traffic(wl),
                      "kernel": kernels, "kernel_ms": avg_kernel_ms,
-                     "algorithmic_bytes_per_launch": alg, "kernel_ms_cold_cache": float(np.median(cold)),
+                     "timing": f"HIP events around {args.steps} back-to-back calls that rotate through "
+                               f"{len(copies)} copies of the inputs (each copy's inputs are out of the "
+                               "caches when it is read again)",
+                     "algorithmic_bytes_per_launch": alg,
+                     "kernel_ms_same_input": same_input_ms,
+                     "kernel_ms_flushed_median": float(np.median(cold)),
                      "kernel_ms_single_median": float(np.median(single)),
                      "kernel_ms_single_min": float(np.min(single)), "copy_kernel_gbs": copy_gbs},
         # the matrix-core roofline of the same call: not the bound (the path's
