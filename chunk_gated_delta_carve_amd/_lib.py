@@ -11,8 +11,8 @@ CARVE_F32, CARVE_BF16 = 0, 1
 CARVE_DECAY_LOGITS = 1
 CARVE_QK_L2NORM = 2
 CARVE_DETACH_MEAN = 4
-EXPORTED = ("carve_recurrent_ref_shapes", "carve_chunk_fwd", "carve_chunk_bwd", "carve_recurrent_step",
-            "carve_error_string")
+EXPORTED = ("carve_recurrent_ref_shapes", "carve_chunk_fwd", "carve_chunk_fwd_noalloc", "carve_chunk_bwd",
+            "carve_recurrent_step", "carve_error_string")
 
 
 class CarveConfig(ctypes.Structure):
@@ -48,6 +48,8 @@ def lib() -> ctypes.CDLL:
         L.carve_recurrent_ref_shapes.restype = ctypes.c_int
         L.carve_chunk_fwd.argtypes = [ctypes.POINTER(CarveConfig)] + [vp] * 14 + [ctypes.c_size_t, vp]
         L.carve_chunk_fwd.restype = ctypes.c_int
+        L.carve_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(CarveConfig)] + [vp] * 14
+        L.carve_chunk_fwd_noalloc.restype = ctypes.c_int
         L.carve_chunk_bwd.argtypes = [ctypes.POINTER(CarveConfig)] + [vp] * 24 + [ctypes.c_size_t, vp]
         L.carve_chunk_bwd.restype = ctypes.c_int
         L.carve_recurrent_step.argtypes = [ctypes.POINTER(CarveConfig), ctypes.c_int32] + [vp] * 13

@@ -294,17 +294,17 @@ extern "C" int carve_recurrent_ref_shapes(const carve_config* cfg, carve_shapes*
   return CARVE_OK;
 }
 
-extern "C" int carve_chunk_fwd(const carve_config* cfg,
-                               const void* q, const void* k, const void* v,
-                               const void* g, const void* bx, const void* w,
-                               const void* ub_down, const void* ub_up,
-                               const float* state_in, const float* mean_in,
-                               void* o, float* state_out, float* mean_out,
-                               void* workspace, size_t workspace_bytes, void* stream) {
-  carve_shapes sh;
-  int st = carve_recurrent_ref_shapes(cfg, &sh);
+namespace {
+
+// Argument checks of the forward entry points (no HIP call): fills `sh` and
+// returns CARVE_OK when the call may go ahead.
+int fwd_check(const carve_config* cfg, const void* q, const void* k, const void* v, const void* g, const void* bx,
+              const void* w, const void* ub_down, const void* ub_up, const float* state_in, const float* mean_in,
+              const void* o, const float* state_out, const float* mean_out, const void* workspace,
+              size_t workspace_bytes, carve_shapes* sh) {
+  int st = carve_recurrent_ref_shapes(cfg, sh);
   if (st != CARVE_OK) return st;
-  const bool tokens = sh.q > 0;
+  const bool tokens = sh->q > 0;
   if (tokens && (!q || !k || !v || !g || !bx || !w || !o)) return CARVE_EINVAL;
   const bool content = cfg->rank > 0;
   if (content && (int64_t)cfg->B * cfg->H > 0 && (!ub_down || !ub_up)) return CARVE_EINVAL;
@@ -312,18 +312,27 @@ extern "C" int carve_chunk_fwd(const carve_config* cfg,
                         state_in, mean_in, o, state_out, mean_out, workspace};
   for (const void* p : ptrs)
     if (misaligned(p)) return CARVE_EALIGN;
-  if (workspace_bytes < (size_t)sh.workspace_bytes) return CARVE_EWORKSPACE;
+  if (workspace_bytes < (size_t)sh->workspace_bytes) return CARVE_EWORKSPACE;
   const size_t es = elem_bytes(cfg->dtype);
-  const size_t ob = (size_t)sh.o * es;
+  const size_t ob = (size_t)sh->o * es;
   const struct { const void* p; size_t n; } ins[] = {
-      {q, (size_t)sh.q * es}, {k, (size_t)sh.k * es}, {v, (size_t)sh.v * es},
-      {g, (size_t)sh.g * es}, {bx, (size_t)sh.bx * es}, {w, (size_t)sh.w * es},
-      {state_in, (size_t)sh.state * 4}, {mean_in, (size_t)sh.mean * 4}};
+      {q, (size_t)sh->q * es}, {k, (size_t)sh->k * es}, {v, (size_t)sh->v * es},
+      {g, (size_t)sh->g * es}, {bx, (size_t)sh->bx * es}, {w, (size_t)sh->w * es},
+      {state_in, (size_t)sh->state * 4}, {mean_in, (size_t)sh->mean * 4}};
   for (const auto& in : ins)
     if (overlaps(o, ob, in.p, in.n)) return CARVE_EINVAL;
-  if ((int64_t)cfg->B * cfg->H == 0) return CARVE_OK;
-  if (!tokens && !state_out && !mean_out) return CARVE_OK;
+  return CARVE_OK;
+}
 
+// Whether a checked forward call has any work to queue.
+bool fwd_has_work(const carve_config* cfg, const carve_shapes& sh, const float* state_out, const float* mean_out) {
+  if ((int64_t)cfg->B * cfg->H == 0) return false;
+  return sh.q > 0 || state_out || mean_out;
+}
+
+int fwd_launch(const carve_config* cfg, const void* q, const void* k, const void* v, const void* g, const void* bx,
+               const void* w, const void* ub_down, const void* ub_up, const float* state_in, const float* mean_in,
+               void* o, float* state_out, float* mean_out, void* workspace, void* stream) {
   carve::FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.g = g; a.bx = bx; a.w = w;
   a.ub_down = ub_down; a.ub_up = ub_up;
@@ -339,6 +348,74 @@ extern "C" int carve_chunk_fwd(const carve_config* cfg,
     return CARVE_EHIP;
   }
   return CARVE_OK;
+}
+
+// Scratch of carve_chunk_fwd_noalloc: the two-launch schedule's block images
+// (the only workspace any forward schedule uses), in a fixed device array
+// that every GPU the library runs on holds until the process ends. In host
+// code `scratch` names a host-side stand-in, never device memory: its device
+// address on the current device comes from hipGetSymbolAddress, looked up
+// once per device and kept in noalloc_scratch.
+constexpr size_t kNoAllocScratch = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratch];
+std::atomic<void*> noalloc_scratch[kMaxDevices];
+
+hipError_t noalloc_scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = noalloc_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // with `dev` current: its copy of the array
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    noalloc_scratch[dev].store(p, std::memory_order_release);   // racing first calls store the same address
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" int carve_chunk_fwd(const carve_config* cfg,
+                               const void* q, const void* k, const void* v,
+                               const void* g, const void* bx, const void* w,
+                               const void* ub_down, const void* ub_up,
+                               const float* state_in, const float* mean_in,
+                               void* o, float* state_out, float* mean_out,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  carve_shapes sh;
+  const int st = fwd_check(cfg, q, k, v, g, bx, w, ub_down, ub_up, state_in, mean_in, o, state_out, mean_out,
+                           workspace, workspace_bytes, &sh);
+  if (st != CARVE_OK) return st;
+  if (!fwd_has_work(cfg, sh, state_out, mean_out)) return CARVE_OK;
+  return fwd_launch(cfg, q, k, v, g, bx, w, ub_down, ub_up, state_in, mean_in, o, state_out, mean_out, workspace,
+                    stream);
+}
+
+extern "C" int carve_chunk_fwd_noalloc(const carve_config* cfg,
+                                       const void* q, const void* k, const void* v,
+                                       const void* g, const void* bx, const void* w,
+                                       const void* ub_down, const void* ub_up,
+                                       const float* state_in, const float* mean_in,
+                                       void* o, float* state_out, float* mean_out, void* stream) {
+  carve_shapes sh;
+  // the fixed scratch stands in for the workspace: a problem that needs more
+  // is CARVE_EWORKSPACE
+  const int st = fwd_check(cfg, q, k, v, g, bx, w, ub_down, ub_up, state_in, mean_in, o, state_out, mean_out,
+                           nullptr, kNoAllocScratch, &sh);
+  if (st != CARVE_OK) return st;
+  if (!fwd_has_work(cfg, sh, state_out, mean_out)) return CARVE_OK;
+  void* ws = nullptr;
+  if (sh.workspace_bytes > 0) {
+    const hipError_t e = noalloc_scratch_ptr(&ws);
+    if (e != hipSuccess) {
+      std::snprintf(g_hip_msg, sizeof(g_hip_msg), "%s", hipGetErrorString(e));
+      return CARVE_EHIP;
+    }
+  }
+  return fwd_launch(cfg, q, k, v, g, bx, w, ub_down, ub_up, state_in, mean_in, o, state_out, mean_out, ws, stream);
 }
 
 extern "C" int carve_chunk_bwd(const carve_config* cfg,
@@ -508,7 +585,7 @@ extern "C" const char* carve_error_string(int code) {
     case CARVE_EINVAL: return "invalid argument (NULL required pointer, negative size, unknown flag or overlapping output)";
     case CARVE_EUNSUPPORTED: return "unsupported configuration (dk/dv in {64,128} with dk == dv, L in {16,32,64,128}, rank <= 64, sizes within 32-bit indexing)";
     case CARVE_EALIGN: return "a tensor pointer is not 16-byte aligned";
-    case CARVE_EWORKSPACE: return "workspace smaller than carve_recurrent_ref_shapes() requires";
+    case CARVE_EWORKSPACE: return "workspace smaller than carve_recurrent_ref_shapes() requires (for carve_chunk_fwd_noalloc: the problem needs more workspace than its fixed 64 MiB scratch)";
     case CARVE_EHIP: return g_hip_msg;
     default: return "unknown status code";
   }

@@ -137,6 +137,25 @@ int carve_chunk_fwd(const carve_config* cfg,
                     void* o, float* state_out, float* mean_out,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* carve_chunk_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code recorded under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation. Arguments and results are
+ * those of carve_chunk_fwd (bit for bit: the same kernels run). The library
+ * allocates nothing for the call: where a schedule needs workspace (bf16 with
+ * no content projection: the two-launch pair's block images), it uses a fixed
+ * 64 MiB device array that every GPU the library runs on holds until the
+ * process ends. A problem that needs more (shapes.workspace_bytes > 64 MiB,
+ * e.g. more than 2048 (batch, head, 64-token block) triples at dk = dv = 64)
+ * is CARVE_EWORKSPACE, before any HIP call. All calls on one GPU share that
+ * array, so calls that overlap in time on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller. */
+int carve_chunk_fwd_noalloc(const carve_config* cfg,
+                            const void* q, const void* k, const void* v,
+                            const void* g, const void* bx, const void* w,
+                            const void* ub_down, const void* ub_up,
+                            const float* state_in, const float* mean_in,
+                            void* o, float* state_out, float* mean_out, void* stream);
+
 /* Backward pass: gradients of a scalar loss with respect to every input of
  * carve_chunk_fwd, from its gradients with respect to the outputs. The pages
  * train the layer but give no backward pass; these are the exact derivatives

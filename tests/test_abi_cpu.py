@@ -257,3 +257,31 @@ def test_missing_library_fails_loudly(tmp_path):
     )
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
     assert r.stdout.strip() == "raised True", r.stdout + r.stderr
+
+
+def test_noalloc_argument_errors(L):
+    """carve_chunk_fwd_noalloc checks its arguments as carve_chunk_fwd does,
+    before any HIP call, and rejects a problem whose workspace would exceed
+    its fixed 64 MiB scratch."""
+    def call(c, **ptrs):
+        names = ["q", "k", "v", "g", "bx", "w", "ub_down", "ub_up", "state_in", "mean_in", "o", "state_out",
+                 "mean_out"]
+        base = {n: None for n in names}
+        for i, n in enumerate(["q", "k", "v", "g", "bx", "w", "ub_down", "ub_up", "o"]):
+            base[n] = FAKE + i * (1 << 24)
+        base.update(ptrs)
+        args = [ctypes.c_void_p(base[n]) if base[n] is not None else None for n in names]
+        return L.carve_chunk_fwd_noalloc(ctypes.byref(c) if c is not None else None, *args, None)
+    assert call(None) == _lib.CARVE_EINVAL
+    assert call(cfg(), q=None) == _lib.CARVE_EINVAL
+    assert call(cfg(), k=FAKE + 4) == _lib.CARVE_EALIGN
+    assert call(cfg(), o=FAKE + 64) == _lib.CARVE_EINVAL
+    assert call(cfg(dk=96, dv=96)) == _lib.CARVE_EUNSUPPORTED
+    assert call(cfg(B=0)) == _lib.CARVE_OK
+    assert call(cfg(T=0)) == _lib.CARVE_OK
+    # 2048 (batch, head, 64-token block) triples of 32 KiB images fill the scratch exactly
+    fits = cfg(B=1, H=16, T=128 * 64, rank=0)
+    assert _lib.ref_shapes(fits).workspace_bytes == 64 << 20
+    over = cfg(B=1, H=16, T=128 * 64 + 1, rank=0)
+    assert _lib.ref_shapes(over).workspace_bytes > 64 << 20
+    assert call(over, ub_down=None, ub_up=None, o=FAKE + 12 * (1 << 24) + (1 << 30)) == _lib.CARVE_EWORKSPACE
