@@ -4,7 +4,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcarve.so")
+# CARVE_LIB_PATH may name another build of the same library (the host
+# sanitizer build, build.py --sanitize); by default the in-tree libcarve.so.
+LIB_PATH = os.environ.get("CARVE_LIB_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcarve.so")
 
 CARVE_OK, CARVE_EINVAL, CARVE_EUNSUPPORTED, CARVE_EALIGN, CARVE_EWORKSPACE, CARVE_EHIP = range(6)
 CARVE_F32, CARVE_BF16 = 0, 1

@@ -24,16 +24,27 @@ FLAGS = [
 ]
 
 
-def build_library(verbose: bool = True) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *SOURCES, "-o", tmp]
+# Host-side sanitizers for the C ABI layer (argument checks, shape contract,
+# dispatch): AddressSanitizer and UndefinedBehaviorSanitizer on the host pass
+# only; the device code is built as usual. The result is a separate library,
+# loaded in place of libcarve.so by pointing CARVE_LIB_PATH at it, with the
+# ASan runtime preloaded into the Python process.
+SANITIZE_LIB = os.path.join(PKG, "libcarve_asan.so")
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+
+
+def build_library(verbose: bool = True, sanitize: bool = False) -> str:
+    out = SANITIZE_LIB if sanitize else LIB
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, *(SANITIZE_FLAGS if sanitize else []), *SOURCES, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    build_library()
+    build_library(sanitize="--sanitize" in sys.argv[1:])
     sys.exit(0)
