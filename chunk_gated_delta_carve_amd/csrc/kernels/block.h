@@ -707,44 +707,43 @@ struct Block {
   }
 
   // -------------------------------------------------------------- (I + A_II)^{-1}
-  // Diagonal 16x16 blocks by forward substitution in fp32, stored as E.
-  // Wave 0, lane (block ib = gq, column c = cc) computes column c of the
-  // inverse, walking the block column by column: once entry r is final, it
-  // is pushed into the running sums of every later row, so the dependent
-  // chain per step is one multiply-add. The diagonal blocks of A are stored
-  // transposed, so column r of a block is one contiguous row read by all 16
-  // lanes of the group. Ends with a barrier.
+  // Diagonal 16x16 blocks, one per wave, as a product of four factors on the
+  // matrix cores: with P = -A_II strictly lower triangular (P^16 = 0),
+  //   (I + A_II)^{-1} = sum_k P^k = (I + P)(I + P^2)(I + P^4)(I + P^8),
+  // three squarings and three products in fp32 (16x16x4 steps, so the
+  // result is the fp32 inverse up to rounding), stored as E. The instruction
+  // takes its left operand by rows, so a product X Y needs X in the
+  // transposed layout (lane (g, c) holds row c, columns 4g..4g+3) and Y in the
+  // C layout (rows 4g..4g+3 of column c): (X Y)_C = mma(X_T, Y_C), and
+  // (X Y)_T = (Y^T X^T)_C = mma(Y_C, X_T). The powers of P are formed in both
+  // layouts, the running product R only in the transposed one, which is also
+  // the row-major order in which the solve reads the inverse. The diagonal
+  // blocks of A are stored transposed (column c of the block is row c in
+  // memory). Ends with a barrier.
   __device__ static void inverse_diag(const Smem& s) {
-    const int lane = threadIdx.x & 63;
-    const int ib = lane >> 4, c = lane & 15;
-    if (wave_id() == 0 && ib < NB) {
-      const float* At = s.A + (16 * ib) * LA + 16 * ib;   // At[r * LA + i] = A_II[i][r]
-      float acc[16], t[16];
+    const int wave = wave_id(), lane = threadIdx.x & 63;
+    const int gq = lane >> 4, cc = lane & 15;
+    if (wave < NB) {
+      using M16 = Mma16<float>;
+      const float* At = s.A + (16 * wave) * LA + 16 * wave;   // At[r * LA + i] = A_II[i][r]
+      f32x4 Pc = *reinterpret_cast<const f32x4*>(At + cc * LA + 4 * gq), Pt;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-      f32x4 col[4];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) col[q4] = *reinterpret_cast<const f32x4*>(At + 4 * q4);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        f32x4 nxt[4];
-        if (r + 1 < 16) {                              // column r + 1 while column r is applied
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4)
-            if (4 * q4 + 3 > r + 1) nxt[q4] = *reinterpret_cast<const f32x4*>(At + (r + 1) * LA + 4 * q4);
-        }
-        t[r] = (r == c) ? 1.f : ((r > c) ? -acc[r] : 0.f);
-#pragma unroll
-        for (int i = r + 1; i < 16; ++i) acc[i] += col[i / 4][i % 4] * t[r];
-        if (r + 1 < 16) {
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4)
-            if (4 * q4 + 3 > r + 1) col[q4] = nxt[q4];
-        }
+      for (int i = 0; i < 4; ++i) {
+        Pc[i] = -Pc[i];
+        Pt[i] = -At[(4 * gq + i) * LA + cc];
       }
-      E* Tb = s.Td + ib * 16 * LTD;
+      f32x4 Rt = Pt;                                   // R = I + P
 #pragma unroll
-      for (int r = 0; r < 16; ++r) Tb[r * LTD + c] = from_f32<E>(t[r]);
+      for (int i = 0; i < 4; ++i)
+        if (4 * gq + i == cc) Rt[i] += 1.f;
+      const f32x4 P2c = M16::mma(Pt, Pc, zero4()), P2t = M16::mma(Pc, Pt, zero4());
+      Rt += M16::mma(P2c, Rt, zero4());                // R <- R (I + P^2)
+      const f32x4 P4c = M16::mma(P2t, P2c, zero4()), P4t = M16::mma(P2c, P2t, zero4());
+      Rt += M16::mma(P4c, Rt, zero4());                // R <- R (I + P^4)
+      const f32x4 P8c = M16::mma(P4t, P4c, zero4());
+      Rt += M16::mma(P8c, Rt, zero4());                // R <- R (I + P^8)
+      *reinterpret_cast<e4*>(s.Td + wave * 16 * LTD + cc * LTD + 4 * gq) =
+          e4{from_f32<E>(Rt[0]), from_f32<E>(Rt[1]), from_f32<E>(Rt[2]), from_f32<E>(Rt[3])};
     }
     __syncthreads();
   }
