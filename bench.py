@@ -22,6 +22,7 @@ cores (worker processes over the independent (batch, head) pairs).
 import argparse
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -227,7 +228,7 @@ def write_traffic_summary(wl, fetch_csv, write_csv, commands):
                 continue
             avg = sum(v) / len(v)
             scaled += avg / factor
-            rows.append((counter, name.split("(")[0], len(v), avg, factor, avg / factor))
+            rows.append((counter, _demangle([name])[0], len(v), avg, factor, avg / factor))
         rows.append((counter, "calibration: " + cname.split("(")[0][:60], len(cv), sum(cv) / len(cv), factor,
                      COPY_BYTES))
     with open(traffic_file(wl), "w") as f:
@@ -282,12 +283,12 @@ def write_mfma_summary(wl, pmc_csv, trace_csv, commands):
     with open(pmc_csv) as f:
         for r in csv.DictReader(f):
             if "carve_" in r["Kernel_Name"]:
-                vals[r["Kernel_Name"].split("(")[0]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+                vals[_demangle([r["Kernel_Name"]])[0]][r["Counter_Name"]].append(float(r["Counter_Value"]))
     dur = {}
     with open(trace_csv) as f:
         for r in csv.DictReader(f):
             if "carve_" in r["Name"]:
-                dur[r["Name"].split("(")[0]] = float(r["MinNs"]) * 1e-9
+                dur[_demangle([r["Name"]])[0]] = float(r["MinNs"]) * 1e-9
     rows, flops_tot, busy_w, t_tot = [], 0.0, 0.0, 0.0
     for name, c in sorted(vals.items()):
         avg = {k: sum(v) / len(v) for k, v in c.items()}
@@ -317,12 +318,85 @@ def write_mfma_summary(wl, pmc_csv, trace_csv, commands):
                     f"{(t or float('nan')) * 1e6:.2f} | {rate:.1f} | {rate / peak:.4f} |\n")
         f.write(f"\nPeak: {peak} TFLOP/s dense ({wl.dtype} inputs). The algorithmic count of the method "
                 "(triangle-aware WY chunk form, what bench.py reports as mfma.achieved) is below the "
-                "executed count: the two-pass split forms each block's affine maps as extra products.\n\n")
+                "executed count: the kernels form each block's affine maps (M, C, Q_eff, O_loc) as extra products, "
+                "and the diagonal inverses as products of powers.\n\n")
         f.write(f"- executed MFMA FLOPs per launch: {flops_tot:.0f}\n")
         f.write(f"- algorithmic FLOPs per launch: {alg}\n")
         f.write(f"- MFMA busy fraction (time-weighted): {busy_w / t_tot if t_tot else 0.0:.4f}\n")
         f.write(f"- kernel sources sha256/16: `{sources_sha()}`\n")
     print(open(mfma_file(wl)).read())
+
+
+def trace_file(wl):
+    return os.path.join(ROOT, "profiles", f"carve_chunk_fwd_{wl.tag()}_kernel_trace.md")
+
+
+def _demangle(names):
+    """Readable names of this library's kernels (carve::<kernel><template
+    arguments>: bf16 or float, integers, booleans); other names shortened."""
+    import re
+    out = []
+    for n in names:
+        m = re.match(r"_ZN5carve(\d+)(\w+?)I(.*)EEv", n)
+        if m and len(m.group(2)) >= int(m.group(1)):
+            kname = m.group(2)[:int(m.group(1))]
+            rest = m.group(2)[int(m.group(1)):] + "I" + m.group(3)
+            args = re.findall(r"DF16b|Lb[01]E|Li\d+E|(?<![A-Za-z])f", rest.split("I", 1)[1])
+            conv = {"DF16b": "bf16", "f": "float", "Lb0E": "false", "Lb1E": "true"}
+            out.append(f"{kname}<" + ",".join(conv.get(x, x[2:-1]) for x in args) + ">")
+        else:
+            n = n.split("(")[0]
+            out.append(n if len(n) <= 90 else n[:87] + "...")
+    return out
+
+
+def write_trace_summary(wl, stats_csv, bench_log, commands):
+    """Turn a rocprofv3 --kernel-trace --stats run (csv) over bench.py, and the
+    JSON line of the same command run without the profiler, into a short
+    per-kernel summary for this workload."""
+    import csv
+    import json
+    with open(stats_csv) as f:
+        rows = list(csv.DictReader(f))
+    names = _demangle([r["Name"] for r in rows])
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    line = None
+    with open(bench_log) as f:
+        for ln in f:
+            if ln.startswith("{"):
+                line = json.loads(ln)
+    with open(trace_file(wl), "w") as f:
+        f.write(f"# Kernel trace: carve_chunk_fwd, {wl.describe()}\n\n")
+        f.write("Commands (run from the repository root on one MI355X; the first without the profiler):\n\n")
+        for c in commands:
+            f.write(f"    {c}\n")
+        f.write("\nPer-kernel statistics of the profiled run (`run_kernel_stats.csv`). Every call of "
+                "carve_chunk_fwd launches its kernels once; bench.py makes warm-up, back-to-back, "
+                "same-input, single and cold-cache calls, so the averages mix cache states (the fill "
+                "kernel is the untimed 512 MB cache flush before each cold-cache call, the negation kernel "
+                "the device-copy reference):\n\n")
+        f.write("| kernel | calls | average (us) | min (us) | max (us) | share |\n|---|---|---|---|---|---|\n")
+        for r, n in zip(rows, names):
+            f.write(f"| `{n}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                    f"{float(r['MaxNs']) / 1e3:.2f} | {100 * float(r['TotalDurationNs']) / total:.1f}% |\n")
+        carve = [(r, n) for r, n in zip(rows, names) if "carve_" in r["Name"]]
+        f.write(f"\n- sum of the CARVE kernels' averages per call: "
+                f"{sum(float(r['AverageNs']) for r, _ in carve) / 1e3:.2f} us\n")
+        if line:
+            rf = line["roofline"]
+            f.write(f"- without the profiler: {line['value']:.4g} tokens/s, `ms_per_step` {line['ms_per_step']:.4f}, "
+                    f"`kernel_ms` {rf['kernel_ms']:.4f} ({rf['timing'].split(',')[0]}), HBM fraction "
+                    f"{rf['frac']:.4f} of {rf['peak']:.0f} GB/s")
+            mf = line.get("mfma") or {}
+            if mf.get("frac") is not None:
+                f.write(f", MFMA fraction {mf['frac']:.4f} (algorithmic FLOPs)")
+            f.write(f"; same-input {rf.get('kernel_ms_same_input', float('nan')):.4f} ms, flushed-cache median "
+                    f"{rf.get('kernel_ms_flushed_median', float('nan')):.4f} ms\n")
+            cb = line.get("cpu_baseline")
+            if cb:
+                f.write(f"- oracle on the host: {cb['value']:.4g} {cb['unit']} ({cb['cores']} workers; {cb['sample']})\n")
+        f.write(f"- kernel sources sha256/16: `{sources_sha()}`\n")
+    print(open(trace_file(wl)).read())
 
 
 def backward_bytes(B, T, H, dk, dv, es, rank=0):
@@ -606,6 +680,9 @@ def main():
     ap.add_argument("--write-mfma-summary", nargs=2, metavar=("PMC_CSV", "STATS_CSV"),
                     help="write the matrix-core summary from a rocprofv3 --pmc csv (MfmaUtil, MfmaFlopsBF16, "
                          "MfmaFlopsF32) and a --kernel-trace --stats csv, and exit")
+    ap.add_argument("--write-trace-summary", nargs=2, metavar=("STATS_CSV", "BENCH_LOG"),
+                    help="write the kernel-trace summary from a rocprofv3 --kernel-trace --stats csv and the log "
+                         "of the same command run without the profiler, and exit")
     ap.add_argument("--commands", nargs="*", default=[], help="commands recorded in a counter summary")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -633,6 +710,9 @@ def main():
         return
     if args.write_mfma_summary:
         write_mfma_summary(wl, *args.write_mfma_summary, args.commands)
+        return
+    if args.write_trace_summary:
+        write_trace_summary(wl, *args.write_trace_summary, args.commands)
         return
     logits, norm = args.decay_logits, args.qk_l2norm
     special = logits or norm                           # an input mode other than the profiled one

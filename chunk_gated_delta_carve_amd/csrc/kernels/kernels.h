@@ -154,27 +154,34 @@ carve_chunk_serial_kernel(FwdArgs a) {
   using Unit = typename B::Unit;
   const Unit* mtu = sink.Mt;
   const Unit* qeu = sink.Qe;
-  // With d_k = 64 the raw inputs of block blk + 1 are fetched while block blk
-  // is processed; wider heads have no registers to spare for that.
-  constexpr bool kPrefetch = DK == 64;
+  // Where the raw inputs of a block are fetched: with d_k = 64, those of
+  // block blk + 1 as soon as the gate pass has consumed those of block blk.
+  // Wider heads have no registers to spare during the Grams and the solve;
+  // with 64-token blocks the fetch of block blk + 1 then waits until the
+  // affine maps of block blk are formed (the output, the chunk mean and the
+  // content bias still hide its latency), and shorter blocks fetch their own
+  // inputs just before their gate pass (measured faster there).
+  constexpr int kFetch = DK == 64 ? 0 : BL == 64 ? 1 : 2;   // after the gate pass, after affine, in place
   typename B::Raw raw;
-  if (kPrefetch && nblk > 0) raw.template load<kNorm>(src, 0, min(BL, T));
+  if (kFetch < 2 && nblk > 0) raw.template load<kNorm>(src, 0, min(BL, T));
+  auto fetch_next = [&](int blk) {
+    const int nb = min(blk + 1, nblk - 1);           // unconditional: keeps the load waits simple
+    raw.template load<kNorm>(src, nb * BL, min(BL, T - nb * BL));
+  };
   for (int blk = 0; blk < nblk; ++blk) {
     const int t0 = blk * BL;
     const int nvalid = min(BL, T - t0);
     E qd[16];
     f32x4 Pt[B::TPW];
-    if (!kPrefetch) raw.template load<kNorm>(src, t0, nvalid);
+    if (kFetch == 2) raw.template load<kNorm>(src, t0, nvalid);
     const bool fallback = B::template gate_pass<true, kLogits, kNorm>(s, raw, nvalid, qd);
-    if (kPrefetch) {
-      const int nb = min(blk + 1, nblk - 1);         // unconditional: keeps the load waits simple
-      raw.template load<kNorm>(src, nb * BL, min(BL, T - nb * BL));
-    }
+    if (kFetch == 0) fetch_next(blk);
     B::template grams<kLogits, kNorm>(s, src, t0, nvalid, fallback, Pt);
     B::inverse_diag(s);
     B::solve(s, qd, Pt);
     f32x4 CtR[TDP], OltR[NBP], Ot[NBP];
     B::affine(s, sink, CtR, OltR);                   // ends with a barrier
+    if (kFetch == 1) fetch_next(blk);
     // S operand fragments of the state at the block start: this wave's from
     // its registers, the other parts' from the exchange buffer
     Frag sf[NF];
