@@ -327,8 +327,9 @@ def write_mfma_summary(wl, pmc_csv, trace_csv, commands):
     print(open(mfma_file(wl)).read())
 
 
-def trace_file(wl):
-    return os.path.join(ROOT, "profiles", f"carve_chunk_fwd_{wl.tag()}_kernel_trace.md")
+def trace_file(wl, backward=False):
+    kind = "bwd" if backward else "fwd"
+    return os.path.join(ROOT, "profiles", f"carve_chunk_{kind}_{wl.tag()}_kernel_trace.md")
 
 
 def _demangle(names):
@@ -350,7 +351,7 @@ def _demangle(names):
     return out
 
 
-def write_trace_summary(wl, stats_csv, bench_log, commands):
+def write_trace_summary(wl, stats_csv, bench_log, commands, backward=False):
     """Turn a rocprofv3 --kernel-trace --stats run (csv) over bench.py, and the
     JSON line of the same command run without the profiler, into a short
     per-kernel summary for this workload."""
@@ -365,16 +366,21 @@ def write_trace_summary(wl, stats_csv, bench_log, commands):
         for ln in f:
             if ln.startswith("{"):
                 line = json.loads(ln)
-    with open(trace_file(wl), "w") as f:
-        f.write(f"# Kernel trace: carve_chunk_fwd, {wl.describe()}\n\n")
+    path = trace_file(wl, backward)
+    with open(path, "w") as f:
+        f.write(f"# Kernel trace: carve_chunk_{'bwd' if backward else 'fwd'}, {wl.describe()}\n\n")
         f.write("Commands (run from the repository root on one MI355X; the first without the profiler):\n\n")
         for c in commands:
             f.write(f"    {c}\n")
-        f.write("\nPer-kernel statistics of the profiled run (`run_kernel_stats.csv`). Every call of "
-                "carve_chunk_fwd launches its kernels once; bench.py makes warm-up, back-to-back, "
-                "same-input, single and cold-cache calls, so the averages mix cache states (the fill "
-                "kernel is the untimed 512 MB cache flush before each cold-cache call, the negation kernel "
-                "the device-copy reference):\n\n")
+        if backward:
+            f.write("\nPer-kernel statistics of the profiled run (`run_kernel_stats.csv`). Every call of "
+                    "carve_chunk_bwd launches its kernels once (warm-up and timed calls):\n\n")
+        else:
+            f.write("\nPer-kernel statistics of the profiled run (`run_kernel_stats.csv`). Every call of "
+                    "carve_chunk_fwd launches its kernels once; bench.py makes warm-up, back-to-back, "
+                    "same-input, single and cold-cache calls, so the averages mix cache states (the fill "
+                    "kernel is the untimed 512 MB cache flush before each cold-cache call, the negation kernel "
+                    "the device-copy reference):\n\n")
         f.write("| kernel | calls | average (us) | min (us) | max (us) | share |\n|---|---|---|---|---|---|\n")
         for r, n in zip(rows, names):
             f.write(f"| `{n}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
@@ -384,19 +390,22 @@ def write_trace_summary(wl, stats_csv, bench_log, commands):
                 f"{sum(float(r['AverageNs']) for r, _ in carve) / 1e3:.2f} us\n")
         if line:
             rf = line["roofline"]
+            timing = rf.get("timing", "HIP events around the timed calls").split(",")[0]
             f.write(f"- without the profiler: {line['value']:.4g} tokens/s, `ms_per_step` {line['ms_per_step']:.4f}, "
-                    f"`kernel_ms` {rf['kernel_ms']:.4f} ({rf['timing'].split(',')[0]}), HBM fraction "
+                    f"`kernel_ms` {rf['kernel_ms']:.4f} ({timing}), HBM fraction "
                     f"{rf['frac']:.4f} of {rf['peak']:.0f} GB/s")
             mf = line.get("mfma") or {}
             if mf.get("frac") is not None:
                 f.write(f", MFMA fraction {mf['frac']:.4f} (algorithmic FLOPs)")
-            f.write(f"; same-input {rf.get('kernel_ms_same_input', float('nan')):.4f} ms, flushed-cache median "
-                    f"{rf.get('kernel_ms_flushed_median', float('nan')):.4f} ms\n")
+            if "kernel_ms_same_input" in rf:
+                f.write(f"; same-input {rf['kernel_ms_same_input']:.4f} ms, flushed-cache median "
+                        f"{rf.get('kernel_ms_flushed_median', float('nan')):.4f} ms")
+            f.write("\n")
             cb = line.get("cpu_baseline")
             if cb:
                 f.write(f"- oracle on the host: {cb['value']:.4g} {cb['unit']} ({cb['cores']} workers; {cb['sample']})\n")
         f.write(f"- kernel sources sha256/16: `{sources_sha()}`\n")
-    print(open(trace_file(wl)).read())
+    print(open(path).read())
 
 
 def backward_bytes(B, T, H, dk, dv, es, rank=0):
@@ -699,12 +708,6 @@ def main():
     wl = WORKLOADS[args.workload]
     if args.L is not None:
         wl = wl.with_(L=args.L)
-    if args.workload == "decode":
-        bench_decode(args, wl)
-        return
-    if args.backward:
-        bench_backward(args, wl)
-        return
     if args.write_traffic_summary:
         write_traffic_summary(wl, *args.write_traffic_summary, args.commands)
         return
@@ -712,7 +715,13 @@ def main():
         write_mfma_summary(wl, *args.write_mfma_summary, args.commands)
         return
     if args.write_trace_summary:
-        write_trace_summary(wl, *args.write_trace_summary, args.commands)
+        write_trace_summary(wl, *args.write_trace_summary, args.commands, backward=args.backward)
+        return
+    if args.workload == "decode":
+        bench_decode(args, wl)
+        return
+    if args.backward:
+        bench_backward(args, wl)
         return
     logits, norm = args.decay_logits, args.qk_l2norm
     special = logits or norm                           # an input mode other than the profiled one

@@ -81,7 +81,8 @@ struct BwdBytes {
 };
 BwdBytes bwd_bytes(const carve_config* c) {
   const int64_t B = c->B, H = c->H, T = c->T;
-  const int64_t own = B * H * 4 * (int64_t)carve::BwdWs(c->dk, c->T, c->L, c->rank, (c->flags & CARVE_QK_L2NORM) != 0).total;
+  const int64_t own = B * H * 4 * (int64_t)carve::BwdWs(c->dk, c->T, c->L, c->rank, (c->flags & CARVE_QK_L2NORM) != 0,
+                                                       bwd_from_forward(c) && c->T > 0).total;
   if (!bwd_from_forward(c)) return {0, 0, own};
   const int64_t img = (own + 255) & ~(int64_t)255;
   const int64_t o = img + parallel_workspace_bytes(c);
@@ -195,8 +196,21 @@ hipError_t launch_row_lane(const carve::BwdArgs& a, hipStream_t s) {
   constexpr auto split = carve::carve_bwd_split_kernel<E, D, LG, CONTENT, NRM>;
   hipError_t e = set_lds<split>(SL::bytes);
   if (e != hipSuccess) return e;
+  // chunk groups (no projection, chunk-start states from the forward pair):
+  // the dS sweep first, then every group's workgroups at once
+  const int groups = carve::bwd_groups(a.T, a.L, CONTENT ? a.rank : 0, a.pre_ckpt != 0);
+  if constexpr (!CONTENT) {
+    if (groups > 1 && (int64_t)a.B * a.H > 0) {
+      constexpr auto sweep = carve::carve_bwd_split_kernel<E, D, LG, false, NRM, true>;
+      e = set_lds<sweep>(SL::bytes);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(sweep, dim3(a.B * a.H * SL::S), dim3(SL::NT), SL::bytes, s, a);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
   if ((int64_t)a.B * a.H > 0) {
-    hipLaunchKernelGGL(split, dim3(a.B * a.H * SL::S), dim3(SL::NT), SL::bytes, s, a);
+    hipLaunchKernelGGL(split, dim3(a.B * a.H * SL::S * groups), dim3(SL::NT), SL::bytes, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -211,7 +225,7 @@ hipError_t launch_row_lane(const carve::BwdArgs& a, hipStream_t s) {
 template <int D>
 hipError_t launch_ub_sum(const carve::BwdArgs& a, hipStream_t s) {
   if (a.H == 0) return hipSuccess;
-  const carve::BwdWs lay(D, a.T, a.L, a.rank, a.norm != 0);
+  const carve::BwdWs lay(D, a.T, a.L, a.rank, a.norm != 0, a.pre_ckpt != 0);
   const size_t n = 2 * (size_t)a.rank * D * a.H;
   hipLaunchKernelGGL(carve::carve_bwd_ub_kernel<D>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                      a.ws, lay.total, lay.dud, a.B, a.H, a.rank, a.d_ub_down, a.d_ub_up);
@@ -445,7 +459,8 @@ extern "C" int carve_chunk_bwd(const carve_config* cfg,
   // one-dimensional grids of the slice-sum (one thread per gradient element)
   // and batch-sum kernels, 256 threads per block
   if ((int64_t)cfg->B * cfg->T * cfg->H * cfg->dk / 256 >= 0x7fffffffLL ||
-      2 * (int64_t)cfg->rank * cfg->dk * cfg->H / 256 >= 0x7fffffffLL)
+      2 * (int64_t)cfg->rank * cfg->dk * cfg->H / 256 >= 0x7fffffffLL ||
+      (int64_t)cfg->B * cfg->H * (cfg->dk / 16) * carve::kBwdGroups >= 0x7fffffffLL)   // row slices x chunk groups
     return CARVE_EUNSUPPORTED;
   if (workspace_bytes < (size_t)sh.bwd_workspace_bytes) return CARVE_EWORKSPACE;
   if (sh.bwd_workspace_bytes > 0 && (int64_t)cfg->B * cfg->H > 0 && !workspace) return CARVE_EINVAL;
@@ -509,7 +524,7 @@ extern "C" int carve_chunk_bwd(const carve_config* cfg,
     f.ws = wsb + bb.img;
     f.B = cfg->B; f.H = cfg->H; f.T = cfg->T; f.L = cfg->L; f.rank = 0;
     f.ckpt = static_cast<float*>(workspace);
-    f.ckpt_bh = carve::BwdWs(cfg->dk, cfg->T, cfg->L, 0, a.norm != 0).total;
+    f.ckpt_bh = carve::BwdWs(cfg->dk, cfg->T, cfg->L, 0, a.norm != 0, true).total;
     f.ckpt_shift = cfg->L == 2 * kParallelBlock ? 1 : 0;
     e = dispatch_fwd_ckpt_flags(cfg, f, s);
   }

@@ -59,9 +59,22 @@ struct BwdArgs {
   int pre_ckpt; // nonzero: the chunk-start states are already in the workspace (no forward sweep)
 };
 
+// Chunk groups of the row-lane schedule without a projection when the
+// chunk-start states come from the forward pair (pre_ckpt): the state
+// gradient at every chunk end is first carried back over all tokens alone
+// (the dS sweep: its recurrence needs the inputs, not the forward states),
+// and then up to kBwdGroups workgroups per row slice walk disjoint runs of
+// chunks at once. Otherwise one workgroup walks all chunks.
+constexpr int kBwdGroups = 8;
+__host__ __device__ inline int bwd_groups(int T, int L, int rank, bool pre_ckpt) {
+  const int nc = L > 0 ? (T + L - 1) / L : 0;
+  return pre_ckpt && rank == 0 && nc > 1 ? (nc < kBwdGroups ? nc : kBwdGroups) : 1;
+}
+
 // Workspace of one (batch, head), in floats: the chunk checkpoints and the
-// recomputed states of one chunk first (16-byte aligned), then the per-chunk
-// gate vectors and the projection factors' partial gradients.
+// recomputed states of one chunk per chunk group first (16-byte aligned),
+// then, with several groups, the state gradient at every chunk end, then the
+// per-chunk gate vectors and the projection factors' partial gradients.
 // Row slices of the row-lane schedule (below): D / 16 without a projection;
 // one slice of all D rows with a projection at D = 64; none otherwise (the
 // per-head schedule).
@@ -74,12 +87,15 @@ __host__ __device__ constexpr int bwd_slices(int D, int rank) { return rank == 0
 // and k and the fp32 gradients of the normalised q and k, which a last
 // kernel takes through the normalisation.
 struct BwdWs {
-  size_t ckpt, sbuf, z, m, y, dud, duu, part, wpart, nrm, dqh, dkh, total;
-  __host__ __device__ BwdWs(int D, int T, int L, int rank, bool norm) {
+  size_t ckpt, sbuf, dsck, z, m, y, dud, duu, part, wpart, nrm, dqh, dkh, total;
+  int groups;
+  __host__ __device__ BwdWs(int D, int T, int L, int rank, bool norm, bool pre_ckpt) {
     const size_t nc = (size_t)(T + L - 1) / L, DD = (size_t)D * D;
+    groups = bwd_groups(T, L, rank, pre_ckpt);
     ckpt = 0;
     sbuf = ckpt + nc * DD;
-    z = sbuf + (size_t)L * DD;
+    dsck = sbuf + (size_t)groups * L * DD;
+    z = dsck + (groups > 1 ? nc * DD : 0);
     m = z + nc * D;
     y = m + nc * D;
     dud = y + nc * rank;
@@ -167,7 +183,7 @@ carve_bwd_kernel(BwdArgs a) {
   const int T = a.T, L = a.L, H = a.H, rank = a.rank;
   const int nc = (T + L - 1) / L;
   const bool content = rank > 0;
-  const BwdWs lay(D, T, L, rank, kNorm);
+  const BwdWs lay(D, T, L, rank, kNorm, a.pre_ckpt != 0);
   float* ws = a.ws + (size_t)bh * lay.total;
   const E* Q = static_cast<const E*>(a.q);
   const E* K = static_cast<const E*>(a.k);
@@ -578,12 +594,11 @@ struct SplitLayout {
   static constexpr int ROWS = kContent ? D : 16, NW = ROWS / 4, NT = 64 * NW;
   static constexpr int S = D / ROWS, CW = D / 16;
   static_assert(S == bwd_slices(D, kContent ? 1 : 0), "slices of the workspace layout");
-  // tokens per staged block: enough work per block to cover the latency of
-  // the next block's global loads (blocks never cross a chunk boundary; a
-  // chunk shorter than NB makes short blocks); 16 at d = 128 and in the
-  // 16-wave workgroups, where 32 would not leave the registers to keep the
-  // staged values unspilled
-  static constexpr int NB = D == 64 && !kContent ? 32 : 16;
+  // tokens per staged block (blocks never cross a chunk boundary; a chunk
+  // shorter than NB makes short blocks): 16, so that three workgroups fit a
+  // CU's LDS and hide each other's latency (32 tokens took 83 KiB, one
+  // workgroup per CU)
+  static constexpr int NB = 16;
   static constexpr int TOKF = 4 * D + 2 * ROWS + 4;   // q, k, dec, b | v, dout of the rows | w
   static constexpr int EPT = NB * D / NT;             // (token, channel) elements staged per thread
   static constexpr int RPT = NB * ROWS / NT;          // (token, row) pairs of v and do per thread
@@ -600,9 +615,13 @@ struct SplitLayout {
                 NT <= 1024 && (!kContent || 4 * D <= NT), "layout");
 };
 
-template <typename E, int D, bool kLogits, bool kContent, bool kNorm>
+// kDsSweep: the dS sweep of the chunk groups (no projection): the state
+// gradient carried back over every token from d_state_out, stored at each
+// chunk end; nothing else is written.
+template <typename E, int D, bool kLogits, bool kContent, bool kNorm, bool kDsSweep = false>
 __global__ void __launch_bounds__((SplitLayout<D, kContent>::NT))
 carve_bwd_split_kernel(BwdArgs a) {
+  static_assert(!(kDsSweep && kContent), "the dS sweep runs without a projection only");
   using LY = SplitLayout<D, kContent>;
   constexpr int NT = LY::NT, NW = LY::NW, CW = LY::CW, NB = LY::NB, TOKF = LY::TOKF, EPT = LY::EPT;
   constexpr int S = LY::S, ROWS = LY::ROWS, RPT = LY::RPT, PD = LY::PD, RING = PD + 1;
@@ -619,12 +638,18 @@ carve_bwd_split_kernel(BwdArgs a) {
   float* dys = lds + LY::oDy;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int slice = blockIdx.x % S, bh = blockIdx.x / S, bi = bh / a.H, h = bh % a.H;
-  const int rl = wave * 4 + (lane >> 4);              // row within the slice
-  const int e = slice * ROWS + rl, cl = lane & 15, c0 = cl * CW;
   const int T = a.T, L = a.L, H = a.H, rank = kContent ? a.rank : 0;
   const int nc = (T + L - 1) / L;
-  const BwdWs lay(D, T, L, rank, kNorm);
+  const BwdWs lay(D, T, L, rank, kNorm, a.pre_ckpt != 0);
+  // workgroup: (batch, head), chunk group (the dS sweep has one), row slice
+  const int NG = kDsSweep ? 1 : lay.groups;
+  const int slice = blockIdx.x % S, grp = (blockIdx.x / S) % NG, bh = blockIdx.x / S / NG;
+  const int bi = bh / a.H, h = bh % a.H;
+  const int cpg = (nc + lay.groups - 1) / lay.groups;  // chunks per group
+  const int c_lo = kDsSweep ? 0 : grp * cpg, c_hi = kDsSweep ? nc : min(nc, c_lo + cpg);
+  if (c_lo >= c_hi && grp > 0) return;                 // an empty group (uniform per workgroup)
+  const int rl = wave * 4 + (lane >> 4);              // row within the slice
+  const int e = slice * ROWS + rl, cl = lane & 15, c0 = cl * CW;
   float* ws = a.ws + (size_t)bh * lay.total;
   const E* Q = static_cast<const E*>(a.q);
   const E* K = static_cast<const E*>(a.k);
@@ -639,34 +664,34 @@ carve_bwd_split_kernel(BwdArgs a) {
   auto blockbuf = [&](int i) { return lds + LY::oBlk + (i & 1) * NB * TOKF; };
 
   // token blocks: [token][q | k | dec | b | v, dout of the rows | w]; b uses
-  // the chunk's z, and dout adds the row's dm_c / n_c
-  struct Staged { float q[EPT], k[EPT], g[EPT], bx[EPT], v[RPT], dout[RPT], w; };
+  // the chunk's z, and dout adds the row's dm_c / n_c. The loads of a block
+  // keep the inputs' own type and are converted only when the block is
+  // staged into LDS, so they stay in flight while the previous block is
+  // worked on; the token index is clamped into the block (rows past nb are
+  // loaded again and never staged), so no load sits under a branch.
+  struct Staged { E q[EPT], k[EPT], g[EPT], bx[EPT], v[RPT], dout[RPT], w; float nq[kNorm ? EPT : 1], nk[kNorm ? EPT : 1]; };
   auto load_block = [&](Staged& st, int tb0, int nb, bool grad) {
 #pragma unroll
     for (int r = 0; r < EPT; ++r) {
-      const int idx = tid + r * NT, j = idx / D, d = idx % D;
-      if (j < nb) {
-        const size_t off = tok_at(tb0 + j) * D + d;
-        st.q[r] = to_f32(Q[off]);
-        st.k[r] = to_f32(K[off]);
-        if constexpr (kNorm) {                        // q, k over their norms
-          st.q[r] *= ws[lay.nrm + 2 * (size_t)(tb0 + j)];
-          st.k[r] *= ws[lay.nrm + 2 * (size_t)(tb0 + j) + 1];
-        }
-        st.g[r] = to_f32(G[off]);
-        st.bx[r] = to_f32(BX[off]);
+      const int idx = tid + r * NT, j = min(idx / D, nb - 1), d = idx % D;
+      const size_t off = tok_at(tb0 + j) * D + d;
+      st.q[r] = Q[off];
+      st.k[r] = K[off];
+      st.g[r] = G[off];
+      st.bx[r] = BX[off];
+      if constexpr (kNorm) {                          // the tokens' inverse norms of q and k
+        st.nq[r] = ws[lay.nrm + 2 * (size_t)(tb0 + j)];
+        st.nk[r] = ws[lay.nrm + 2 * (size_t)(tb0 + j) + 1];
       }
     }
 #pragma unroll
     for (int r2 = 0; r2 < RPT; ++r2) {
-      const int idx = tid + r2 * NT, j = idx / ROWS, r = idx % ROWS;
-      if (j < nb) {
-        const size_t off = tok_at(tb0 + j) * D + slice * ROWS + r;
-        st.v[r2] = to_f32(V[off]);
-        st.dout[r2] = grad ? to_f32(DO[off]) : 0.f;
-      }
+      const int idx = tid + r2 * NT, j = min(idx / ROWS, nb - 1), r = idx % ROWS;
+      const size_t off = tok_at(tb0 + j) * D + slice * ROWS + r;
+      st.v[r2] = V[off];
+      st.dout[r2] = grad ? DO[off] : from_f32<E>(0.f);
     }
-    if (tid < nb) st.w = to_f32(W[tok_at(tb0 + tid)]);
+    st.w = W[tok_at(tb0 + min(tid, nb - 1))];
   };
   auto store_block = [&](float* buf, const Staged& st, int nb) {
 #pragma unroll
@@ -674,21 +699,26 @@ carve_bwd_split_kernel(BwdArgs a) {
       const int idx = tid + r * NT, j = idx / D, d = idx % D;
       if (j < nb) {
         float* tb = buf + j * TOKF;
-        tb[d] = st.q[r];
-        tb[D + d] = st.k[r];
-        tb[2 * D + d] = fast_exp2(decay_log2<kLogits>(st.g[r]));
-        tb[3 * D + d] = sigmoid_f(st.bx[r] + zs[d]);
+        float qv = to_f32(st.q[r]), kv = to_f32(st.k[r]);
+        if constexpr (kNorm) {                        // q, k over their norms
+          qv *= st.nq[r];
+          kv *= st.nk[r];
+        }
+        tb[d] = qv;
+        tb[D + d] = kv;
+        tb[2 * D + d] = fast_exp2(decay_log2<kLogits>(to_f32(st.g[r])));
+        tb[3 * D + d] = sigmoid_f(to_f32(st.bx[r]) + zs[d]);
       }
     }
 #pragma unroll
     for (int r2 = 0; r2 < RPT; ++r2) {
       const int idx = tid + r2 * NT, j = idx / ROWS, r = idx % ROWS;
       if (j < nb) {
-        buf[j * TOKF + 4 * D + r] = st.v[r2];
-        buf[j * TOKF + 4 * D + ROWS + r] = st.dout[r2] + dmcs[r];
+        buf[j * TOKF + 4 * D + r] = to_f32(st.v[r2]);
+        buf[j * TOKF + 4 * D + ROWS + r] = to_f32(st.dout[r2]) + dmcs[r];
       }
     }
-    if (tid < nb) buf[tid * TOKF + 4 * D + 2 * ROWS] = st.w;
+    if (tid < nb) buf[tid * TOKF + 4 * D + 2 * ROWS] = to_f32(st.w);
   };
   auto advance = [&](float (&s)[CW], const float* tb) {
     const float* tk = tb + D;
@@ -797,16 +827,78 @@ carve_bwd_split_kernel(BwdArgs a) {
     }
   }
 
+  if constexpr (kDsSweep) {
+    // -------------------------------------------------------------- dS sweep
+    // The reverse walk's recurrence of the state gradient alone: per token,
+    // with d delta = dS k,
+    //   dS <- (dS - d delta (b k)^T) diag(e^g) + dout q^T,
+    // which needs the inputs but not the forward states. dsck[c] receives the
+    // dS that enters the reverse walk of chunk c (its value at the chunk's
+    // end); chunk 0 is walked by its group only. The tokens of chunks nc - 1
+    // .. 1 are one stream of NB-token blocks from the end (L is a multiple of
+    // NB here, so no block crosses a chunk boundary), their loads issued two
+    // blocks ahead through three register sets.
+    float ds[CW];
+    if (a.d_state_out) ld(ds, a.d_state_out + (size_t)bh * DD + rowoff);
+    else
+#pragma unroll
+      for (int j = 0; j < CW; ++j) ds[j] = 0.f;
+    float* dsck = ws + lay.dsck + rowoff;
+    const int tl0 = (nc - 1) * L;                        // first token of the last chunk
+    // this row's share of d_mean_out, added to each output gradient of the last chunk
+    const float dml = a.d_mean_out ? a.d_mean_out[(size_t)bh * D + e] / (float)(T - tl0) : 0.f;
+    const int nbt = (T + NB - 1) / NB, nwalk = nbt - L / NB;   // blocks of chunks nc - 1 .. 1
+    auto tb0_of = [&](int kb) { return (nbt - 1 - kb) * NB; };
+    auto nb_of = [&](int kb) { return min(NB, T - tb0_of(kb)); };
+    Staged sets[3];
+    load_block(sets[0], tb0_of(0), nb_of(0), true);
+    if (1 < nwalk) load_block(sets[1], tb0_of(1), nb_of(1), true);
+    store_block(blockbuf(0), sets[0], nb_of(0));
+    lds_barrier();
+    auto block = [&](int kb, Staged& next2, Staged& next1) {
+      const int tb0 = tb0_of(kb), nb = nb_of(kb), c = tb0 / L;
+      if (kb + 2 < nwalk) load_block(next2, tb0_of(kb + 2), nb_of(kb + 2), true);
+      if (tb0 + nb == min(T, (c + 1) * L)) st4(dsck + (size_t)c * DD, ds);   // entering chunk c
+      const float dm = tb0 >= tl0 ? dml : 0.f;
+      const float* buf = blockbuf(kb);
+#pragma unroll 4
+      for (int j = nb - 1; j >= 0; --j) {
+        const float* tb = buf + j * TOKF;
+        float pdd = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < CW; ++jj) pdd += ds[jj] * tb[D + c0 + jj];
+        const float ddelta = sum_row16(pdd);
+        const float dout = tb[4 * D + ROWS + rl] + dm;
+#pragma unroll
+        for (int jj = 0; jj < CW; ++jj) {
+          const int cc = c0 + jj;
+          ds[jj] = (ds[jj] - ddelta * (tb[3 * D + cc] * tb[D + cc])) * tb[2 * D + cc] + dout * tb[cc];
+        }
+      }
+      if (kb + 1 < nwalk) store_block(blockbuf(kb + 1), next1, nb_of(kb + 1));
+      lds_barrier();
+    };
+    for (int kb = 0; kb < nwalk; kb += 3) {
+      block(kb, sets[2], sets[1]);
+      if (kb + 1 < nwalk) block(kb + 1, sets[0], sets[2]);
+      if (kb + 2 < nwalk) block(kb + 2, sets[1], sets[0]);
+    }
+    st4(dsck, ds);                                       // entering chunk 0
+    return;
+  }
+
   // ---------------------------------------------------------------- reverse sweep
+  // this group's chunks [c_lo, c_hi), from the dS at the end of its last one
   float ds[CW];
-  if (a.d_state_out) ld(ds, a.d_state_out + (size_t)bh * DD + rowoff);
+  if (lay.groups > 1) ld(ds, ws + lay.dsck + (size_t)(c_hi - 1) * DD + rowoff);
+  else if (a.d_state_out) ld(ds, a.d_state_out + (size_t)bh * DD + rowoff);
   else
 #pragma unroll
     for (int j = 0; j < CW; ++j) ds[j] = 0.f;
-  float* sbuf = ws + lay.sbuf + rowoff;
+  float* sbuf = ws + lay.sbuf + (size_t)grp * L * DD + rowoff;
   float* gpart = ws + lay.part;                       // [T][S][4][D]
   float* gw = ws + lay.wpart;                         // [T][S]
-  for (int c = nc - 1; c >= 0; --c) {
+  for (int c = c_hi - 1; c >= c_lo; --c) {
     const int t0 = c * L, t1 = min(T, t0 + L), n = t1 - t0;
     if (tid < D) {
       if (kContent) {
@@ -949,6 +1041,7 @@ carve_bwd_split_kernel(BwdArgs a) {
       __syncthreads();
     }
   }
+  if (grp > 0) return;                                // the incoming gradients belong to group 0
   if (a.d_state_in) st4(a.d_state_in + (size_t)bh * DD + rowoff, ds);
   if (a.d_mean_in && cl == 0) {
     // the incoming mean gates chunk 0 (with a projection); with T = 0 it
@@ -977,7 +1070,7 @@ carve_bwd_finish_kernel(BwdArgs a) {
   const int h = (int)(row % a.H);
   const size_t bt = row / a.H;
   const int t = (int)(bt % a.T), bi = (int)(bt / a.T);
-  const BwdWs lay(D, a.T, a.L, kContent ? a.rank : 0, kNorm);
+  const BwdWs lay(D, a.T, a.L, kContent ? a.rank : 0, kNorm, a.pre_ckpt != 0);
   float* ws = a.ws + ((size_t)bi * a.H + h) * lay.total;
   const float* gp = ws + lay.part + (size_t)t * S * 4 * D + d;
   float P[4] = {0.f, 0.f, 0.f, 0.f};
@@ -1025,7 +1118,7 @@ carve_bwd_norm_kernel(BwdArgs a) {
   const int h = (int)(row % a.H);
   const size_t bt = row / a.H;
   const int t = (int)(bt % a.T), bi = (int)(bt / a.T);
-  const BwdWs lay(D, a.T, a.L, a.rank, true);
+  const BwdWs lay(D, a.T, a.L, a.rank, true, a.pre_ckpt != 0);
   float* ws = a.ws + ((size_t)bi * a.H + h) * lay.total;
   const E* Q = static_cast<const E*>(a.q) + row * D;
   const E* K = static_cast<const E*>(a.k) + row * D;

@@ -154,14 +154,15 @@ carve_chunk_serial_kernel(FwdArgs a) {
   using Unit = typename B::Unit;
   const Unit* mtu = sink.Mt;
   const Unit* qeu = sink.Qe;
-  // Where the raw inputs of a block are fetched: with d_k = 64, those of
-  // block blk + 1 as soon as the gate pass has consumed those of block blk.
-  // Wider heads have no registers to spare during the Grams and the solve;
-  // with 64-token blocks the fetch of block blk + 1 then waits until the
-  // affine maps of block blk are formed (the output, the chunk mean and the
-  // content bias still hide its latency), and shorter blocks fetch their own
-  // inputs just before their gate pass (measured faster there).
-  constexpr int kFetch = DK == 64 ? 0 : BL == 64 ? 1 : 2;   // after the gate pass, after affine, in place
+  // Where the raw inputs of a block are fetched: with d_k = 64 or 16-token
+  // blocks, those of block blk + 1 as soon as the gate pass has consumed
+  // those of block blk. Wider heads with longer blocks have no registers to
+  // spare during the Grams and the solve: with 64-token blocks the fetch of
+  // block blk + 1 waits until the affine maps of block blk are formed (the
+  // output, the chunk mean and the content bias still hide its latency);
+  // 32-token blocks fetch their own inputs just before their gate pass
+  // (measured faster than after the affine maps).
+  constexpr int kFetch = DK == 64 || BL == 16 ? 0 : BL == 64 ? 1 : 2;   // after the gate pass, after affine, in place
   typename B::Raw raw;
   if (kFetch < 2 && nblk > 0) raw.template load<kNorm>(src, 0, min(BL, T));
   auto fetch_next = [&](int blk) {
@@ -477,6 +478,11 @@ carve_state_kernel(FwdArgs a) {
 #pragma unroll
       for (int t = 0; t < NB / 2; ++t) unpair(r.ol[t], Olt[2 * t], Olt[2 * t + 1]);
       B::state_out([&](int rt, int u) { return r.qe[rt][u]; }, Olt, sf, Ot);
+      if (lost) {                                     // the ring slot may be stale: poison o too
+        const float nan = __builtin_nanf("");
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt) Ot[rt] = f32x4{nan, nan, nan, nan};
+      }
       if (refill) fetch(r, blk + NSO * K);
       const int t0 = blk * BL;
       if (t0 + BL > mstart) {                         // the block reaches into the last chunk

@@ -128,7 +128,12 @@ int carve_recurrent_ref_shapes(const carve_config* cfg, carve_shapes* out);
  *              when that is 0)
  *   stream     hipStream_t as void*
  * B, H or T may be 0 (nothing to compute; with T == 0 the state and mean pass
- * through). T need not be a multiple of L. */
+ * through). T need not be a multiple of L.
+ * The chunk-parallel state pass hands block states between the waves of a
+ * workgroup through LDS with bounded waits. A wait that runs out (none has
+ * ever been observed; it would take a hardware fault) writes NaN to the
+ * affected output tiles, state and mean instead of hanging; the call still
+ * returns CARVE_OK, since the kernels run after it returns. */
 int carve_chunk_fwd(const carve_config* cfg,
                     const void* q, const void* k, const void* v,
                     const void* g, const void* bx, const void* w,
@@ -181,7 +186,11 @@ int carve_chunk_fwd_noalloc(const carve_config* cfg,
  *               4 T (dk / 16) (4 dk + 1) bytes per (batch, head); in bf16
  *               with rank == 0 and L a multiple of 64, also the forward
  *               pair's block images and an output, since the chunk-start
- *               states then come from the forward's chunk-parallel state pass
+ *               states then come from the forward's chunk-parallel state pass;
+ *               the chunks are then walked in up to 8 groups at once, which
+ *               takes one chunk's per-token states per group and the state
+ *               gradient at every chunk end, 4 (G L + nc) dk dv bytes per
+ *               (batch, head) in place of 4 L dk dv
  * No output may overlap an input, another output or the workspace, except
  * for the two aliases above. Results are deterministic (no atomics).
  * Returns the status codes of carve_chunk_fwd. */

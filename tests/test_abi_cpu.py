@@ -209,11 +209,21 @@ def test_bwd_workspace_size():
     per_bh32 = 4 * 64 * 64 + 32 * 64 * 64 + 4 * 2 * 64 + 100 * 4 * (4 * 64 + 1)   # L = 32: four chunks
     assert _lib.ref_shapes(cfg(rank=0, L=32)).bwd_workspace_bytes == 6 * 4 * per_bh32
     # in bf16 with L a multiple of 64 the forward pair supplies the chunk-start
-    # states: its block images and an output follow, 256-byte aligned
+    # states, and the chunks are walked in groups (here both chunks at once):
+    # one chunk's states per group and the state gradient at every chunk end;
+    # the pair's block images and an output follow, 256-byte aligned
     sh0 = _lib.ref_shapes(cfg(rank=0))
     fwd = sh0.workspace_bytes
     assert fwd > 0
-    assert sh0.bwd_workspace_bytes == (own0 + 255) // 256 * 256 + fwd + 2 * 100 * 3 * 64 * 2
+    per_bh_pre = 2 * 64 * 64 + 2 * 64 * 64 * 64 + 2 * 64 * 64 + 2 * 2 * 64 + 100 * 4 * (4 * 64 + 1)
+    own_pre = 6 * 4 * ((per_bh_pre + 3) // 4 * 4)
+    assert sh0.bwd_workspace_bytes == (own_pre + 255) // 256 * 256 + fwd + 2 * 100 * 3 * 64 * 2
+    # at most eight groups: 40 chunks of 64 tokens
+    long_pre = _lib.ref_shapes(cfg(rank=0, T=2560))
+    per_bh_long = 40 * 64 * 64 + 8 * 64 * 64 * 64 + 40 * 64 * 64 + 40 * 2 * 64 + 2560 * 4 * (4 * 64 + 1)
+    own_long = 6 * 4 * ((per_bh_long + 3) // 4 * 4)
+    assert long_pre.bwd_workspace_bytes == ((own_long + 255) // 256 * 256 + long_pre.workspace_bytes
+                                            + 2 * 2560 * 3 * 64 * 2)
 
 
 def test_bwd_argument_errors(L):
