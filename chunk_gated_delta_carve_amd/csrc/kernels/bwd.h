@@ -66,6 +66,10 @@ struct BwdArgs {
 // and then up to kBwdGroups workgroups per row slice walk disjoint runs of
 // chunks at once. Otherwise one workgroup walks all chunks.
 constexpr int kBwdGroups = 8;
+// Tokens per sub-block of the row-lane reverse walk: the walk keeps a
+// sub-block's recomputed states in registers and stores only the state at
+// each sub-block start.
+constexpr int kBwdSub = 8;
 __host__ __device__ inline int bwd_groups(int T, int L, int rank, bool pre_ckpt) {
   const int nc = L > 0 ? (T + L - 1) / L : 0;
   return pre_ckpt && rank == 0 && nc > 1 ? (nc < kBwdGroups ? nc : kBwdGroups) : 1;
@@ -87,14 +91,18 @@ __host__ __device__ constexpr int bwd_slices(int D, int rank) { return rank == 0
 // and k and the fp32 gradients of the normalised q and k, which a last
 // kernel takes through the normalisation.
 struct BwdWs {
-  size_t ckpt, sbuf, dsck, z, m, y, dud, duu, part, wpart, nrm, dqh, dkh, total;
+  size_t ckpt, sbuf, sbuf_group, dsck, z, m, y, dud, duu, part, wpart, nrm, dqh, dkh, total;
   int groups;
   __host__ __device__ BwdWs(int D, int T, int L, int rank, bool norm, bool pre_ckpt) {
     const size_t nc = (size_t)(T + L - 1) / L, DD = (size_t)D * D;
     groups = bwd_groups(T, L, rank, pre_ckpt);
     ckpt = 0;
     sbuf = ckpt + nc * DD;
-    dsck = sbuf + (size_t)groups * L * DD;
+    // recomputed states of one chunk per group: every token's for the
+    // one-workgroup-per-head kernel (d = 128 with a projection), every
+    // sub-block start for the row-lane kernel
+    sbuf_group = (rank > 0 && D == 128 ? (size_t)L : (size_t)(L + kBwdSub - 1) / kBwdSub) * DD;
+    dsck = sbuf + (size_t)groups * sbuf_group;
     z = dsck + (groups > 1 ? nc * DD : 0);
     m = z + nc * D;
     y = m + nc * D;
@@ -199,30 +207,29 @@ carve_bwd_kernel(BwdArgs a) {
 
   // Token blocks: nb <= NB consecutive tokens from tb0, staged into LDS as
   // [token][q | k | dec | b | v | dout | w]. Loading (raw values into
-  // registers) is split from storing (decay factor and erase gate formed, the
-  // chunk's dm_c / n_c added to do) so the next block's loads overlap the
-  // current block's work. Element r of a thread is (token, channel) =
-  // divmod(tid + r NT, D).
-  struct Staged { float q[EPT], k[EPT], g[EPT], bx[EPT], v[EPT], dout[EPT], w; };
+  // registers, in the inputs' type, the token index clamped into the block so
+  // no load sits under a branch) is split from storing (values converted,
+  // decay factor and erase gate formed, the chunk's dm_c / n_c added to do)
+  // so the next block's loads stay in flight during the current block's
+  // work. Element r of a thread is (token, channel) = divmod(tid + r NT, D).
+  struct Staged { E q[EPT], k[EPT], g[EPT], bx[EPT], v[EPT], dout[EPT], w; float nq[kNorm ? EPT : 1], nk[kNorm ? EPT : 1]; };
   auto load_block = [&](Staged& st, int tb0, int nb, bool grad) {
 #pragma unroll
     for (int r = 0; r < EPT; ++r) {
-      const int idx = tid + r * NT, j = idx / D, d = idx % D;
-      if (j < nb) {
-        const size_t off = tok_at(tb0 + j) * D + d;
-        st.q[r] = to_f32(Q[off]);
-        st.k[r] = to_f32(K[off]);
-        if constexpr (kNorm) {                        // q, k over their norms
-          st.q[r] *= ws[lay.nrm + 2 * (size_t)(tb0 + j)];
-          st.k[r] *= ws[lay.nrm + 2 * (size_t)(tb0 + j) + 1];
-        }
-        st.g[r] = to_f32(G[off]);
-        st.bx[r] = to_f32(BX[off]);
-        st.v[r] = to_f32(V[off]);
-        st.dout[r] = grad ? to_f32(DO[off]) : 0.f;
+      const int idx = tid + r * NT, j = min(idx / D, nb - 1), d = idx % D;
+      const size_t off = tok_at(tb0 + j) * D + d;
+      st.q[r] = Q[off];
+      st.k[r] = K[off];
+      if constexpr (kNorm) {                          // the tokens' inverse norms of q and k
+        st.nq[r] = ws[lay.nrm + 2 * (size_t)(tb0 + j)];
+        st.nk[r] = ws[lay.nrm + 2 * (size_t)(tb0 + j) + 1];
       }
+      st.g[r] = G[off];
+      st.bx[r] = BX[off];
+      st.v[r] = V[off];
+      st.dout[r] = grad ? DO[off] : from_f32<E>(0.f);
     }
-    if (tid < nb) st.w = to_f32(W[tok_at(tb0 + tid)]);
+    st.w = W[tok_at(tb0 + min(tid, nb - 1))];
   };
   auto store_block = [&](float* buf, const Staged& st, int nb) {
 #pragma unroll
@@ -230,15 +237,20 @@ carve_bwd_kernel(BwdArgs a) {
       const int idx = tid + r * NT, j = idx / D, d = idx % D;
       if (j < nb) {
         float* tb = buf + j * TOKF;
-        tb[d] = st.q[r];
-        tb[D + d] = st.k[r];
-        tb[2 * D + d] = fast_exp2(decay_log2<kLogits>(st.g[r]));
-        tb[3 * D + d] = sigmoid_f(st.bx[r] + zs[d]);
-        tb[4 * D + d] = st.v[r];
-        tb[5 * D + d] = st.dout[r] + dmcs[d];
+        float qv = to_f32(st.q[r]), kv = to_f32(st.k[r]);
+        if constexpr (kNorm) {                        // q, k over their norms
+          qv *= st.nq[r];
+          kv *= st.nk[r];
+        }
+        tb[d] = qv;
+        tb[D + d] = kv;
+        tb[2 * D + d] = fast_exp2(decay_log2<kLogits>(to_f32(st.g[r])));
+        tb[3 * D + d] = sigmoid_f(to_f32(st.bx[r]) + zs[d]);
+        tb[4 * D + d] = to_f32(st.v[r]);
+        tb[5 * D + d] = to_f32(st.dout[r]) + dmcs[d];
       }
     }
-    if (tid < nb) buf[tid * TOKF + 6 * D] = st.w;
+    if (tid < nb) buf[tid * TOKF + 6 * D] = to_f32(st.w);
   };
 
   // the content gate of a chunk from the mean in ms: ys = U_down m, zs = U_up ys
@@ -602,7 +614,6 @@ struct SplitLayout {
   static constexpr int TOKF = 4 * D + 2 * ROWS + 4;   // q, k, dec, b | v, dout of the rows | w
   static constexpr int EPT = NB * D / NT;             // (token, channel) elements staged per thread
   static constexpr int RPT = NB * ROWS / NT;          // (token, row) pairs of v and do per thread
-  static constexpr int PD = 2;                        // states loaded this many tokens ahead
   static constexpr int oBlk = 0;                      // 2 x [NB][TOKF]
   static constexpr int oPart = oBlk + 2 * NB * TOKF;  // 2 x [NW waves][4][D]
   static constexpr int oWp = oPart + 2 * NW * 4 * D;  // 2 x [NW] dw partials
@@ -624,7 +635,8 @@ carve_bwd_split_kernel(BwdArgs a) {
   static_assert(!(kDsSweep && kContent), "the dS sweep runs without a projection only");
   using LY = SplitLayout<D, kContent>;
   constexpr int NT = LY::NT, NW = LY::NW, CW = LY::CW, NB = LY::NB, TOKF = LY::TOKF, EPT = LY::EPT;
-  constexpr int S = LY::S, ROWS = LY::ROWS, RPT = LY::RPT, PD = LY::PD, RING = PD + 1;
+  constexpr int S = LY::S, ROWS = LY::ROWS, RPT = LY::RPT, SB = kBwdSub;
+  static_assert(NB % SB == 0, "a sub-block lies inside one staged block");
   constexpr size_t DD = (size_t)D * D;
   extern __shared__ __align__(16) float lds[];
   float* part0 = lds + LY::oPart;
@@ -895,7 +907,7 @@ carve_bwd_split_kernel(BwdArgs a) {
   else
 #pragma unroll
     for (int j = 0; j < CW; ++j) ds[j] = 0.f;
-  float* sbuf = ws + lay.sbuf + (size_t)grp * L * DD + rowoff;
+  float* sbuf = ws + lay.sbuf + (size_t)grp * lay.sbuf_group + rowoff;
   float* gpart = ws + lay.part;                       // [T][S][4][D]
   float* gw = ws + lay.wpart;                         // [T][S]
   for (int c = c_hi - 1; c >= c_lo; --c) {
@@ -910,7 +922,10 @@ carve_bwd_split_kernel(BwdArgs a) {
     if (kContent && tid < rank) ys[tid] = ws[lay.y + (size_t)c * rank + tid];
     __syncthreads();
     ld(s, ws + lay.ckpt + (size_t)c * DD + rowoff);
-    sweep(s, t0, t1, [&](int t, const float*) { st4(sbuf + (size_t)(t - t0) * DD, s); });
+    // the state before every sub-block (every SB tokens from the chunk start)
+    sweep(s, t0, t1, [&](int t, const float*) {
+      if ((t - t0) % SB == 0) st4(sbuf + (size_t)((t - t0) / SB) * DD, s);
+    });
     // each output gradient of the chunk gains dm_c / n: dm_c from the next
     // chunk's gate (with a projection) and, for the last chunk, d_mean_out
     if (tid < ROWS) {
@@ -926,17 +941,18 @@ carve_bwd_split_kernel(BwdArgs a) {
       load_block(st, tb0, nb, true);
       store_block(blockbuf(0), st, nb);
     }
-    float ring[RING][CW];
-#pragma unroll
-    for (int k = 0; k < PD; ++k)
-      if (k < n) ld(ring[k], sbuf + (size_t)(n - 1 - k) * DD);
     lds_barrier();
     float dz = 0.f;                                    // this thread's column of dz (projection)
+    // the staged inputs of token t (its block is in LDS while the walk is in it)
+    auto tokbuf = [&](int t) {
+      const int jb = (t - t0) / NB;
+      return blockbuf(nblk - 1 - jb) + (t - t0 - jb * NB) * TOKF;
+    };
 
-    auto step = [&](int i, const float (&sp)[CW], float (&nxt)[CW]) {
-      const int t = t1 - 1 - i;
+    // token t's adjoint step, sp the state before the token
+    auto step = [&](int t, const float (&sp)[CW]) {
+      const int i = t1 - 1 - t;
       const int jb = (t - t0) / NB, tb0 = t0 + jb * NB, j = t - tb0, kb = nblk - 1 - jb;
-      if (t - PD >= t0) ld(nxt, sbuf + (size_t)(t - PD - t0) * DD);
       if (t == min(tb0 + NB, t1) - 1 && jb > 0) load_block(st, tb0 - NB, NB, true);
       const float* tb = blockbuf(kb) + j * TOKF;
       float* pb = part0 + (i & 1) * NW * 4 * D;
@@ -1011,10 +1027,25 @@ carve_bwd_split_kernel(BwdArgs a) {
         lds_barrier();
       }
     };
-    for (int i = 0; i < n; i += RING) {
-      step(i, ring[0], ring[PD % RING]);
-      if (i + 1 < n) step(i + 1, ring[1 % RING], ring[(1 + PD) % RING]);
-      if (i + 2 < n) step(i + 2, ring[2 % RING], ring[(2 + PD) % RING]);
+    // sub-blocks from the chunk's end: their states recomputed into registers
+    // from the stored sub-block start (a sub-block lies inside one staged
+    // block), then walked backwards
+    const int nsb = (n + SB - 1) / SB;
+    for (int q = nsb - 1; q >= 0; --q) {
+      const int s0 = t0 + q * SB, s1 = min(t1, s0 + SB);
+      float sts[SB][CW];
+      ld(sts[0], sbuf + (size_t)q * DD);
+#pragma unroll
+      for (int u = 1; u < SB; ++u) {
+        if (s0 + u < s1) {
+#pragma unroll
+          for (int jj = 0; jj < CW; ++jj) sts[u][jj] = sts[u - 1][jj];
+          advance(sts[u], tokbuf(s0 + u - 1));
+        }
+      }
+#pragma unroll
+      for (int u = SB - 1; u >= 0; --u)
+        if (s0 + u < s1) step(s0 + u, sts[u]);
     }
 
     // the chunk's gate: z = U_up y, y = U_down m_{c-1}

@@ -180,17 +180,22 @@ int carve_chunk_fwd_noalloc(const carve_config* cfg,
  *   d_state_in [B,H,dv,dk], d_mean_in [B,H,dv]: fp32 or NULL (not written).
  *               They may be the same buffers as d_state_out and d_mean_out.
  *   workspace   at least shapes.bwd_workspace_bytes of device scratch: the
- *               state at every chunk start and one chunk's per-token states,
- *               4 (nc + L) dk dv bytes per (batch, head), plus small vectors;
+ *               state at every chunk start and one chunk's recomputed states,
+ *               4 (nc + L) dk dv bytes per (batch, head) at dk = 128 with a
+ *               projection, 4 (nc + ceil(L / 8)) dk dv otherwise, plus small
+ *               vectors;
  *               with rank == 0 also every token's per-slice column sums,
  *               4 T (dk / 16) (4 dk + 1) bytes per (batch, head); in bf16
  *               with rank == 0 and L a multiple of 64, also the forward
  *               pair's block images and an output, since the chunk-start
  *               states then come from the forward's chunk-parallel state pass;
  *               the chunks are then walked in up to 8 groups at once, which
- *               takes one chunk's per-token states per group and the state
- *               gradient at every chunk end, 4 (G L + nc) dk dv bytes per
- *               (batch, head) in place of 4 L dk dv
+ *               takes one chunk's recomputed states per group and the state
+ *               gradient at every chunk end, 4 (G ceil(L / 8) + nc) dk dv
+ *               bytes per (batch, head) in place of 4 ceil(L / 8) dk dv (the
+ *               row-lane schedules keep the state at every 8-token sub-block
+ *               start rather than at every token; 4 L dk dv at dk = 128 with
+ *               a projection)
  * No output may overlap an input, another output or the workspace, except
  * for the two aliases above. Results are deterministic (no atomics).
  * Returns the status codes of carve_chunk_fwd. */

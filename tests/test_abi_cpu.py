@@ -187,14 +187,16 @@ def call_bwd(L, c, ws_bytes=None, **ptrs):
 
 def test_bwd_workspace_size():
     """The backward workspace holds, per (batch, head), the fp32 state at every
-    chunk start and one chunk's per-token states, small per-chunk vectors, and
+    chunk start and one chunk's recomputed states (every token's for the
+    one-workgroup-per-head kernel at d = 128 with a projection, every 8-token
+    sub-block start for the row-lane kernel), small per-chunk vectors, and
     every token's column sums per row slice (one slice of all rows with a
     projection at d = 64, d / 16 slices without one, none at d = 128 with one);
     in bf16 without a projection and with L a multiple of 64, also the
     forward pair's block images and output."""
     sh = _lib.ref_shapes(cfg())                      # B2 H3 T100 d64 L64 rank 4: two chunks
     vecs = 2 * 2 * 64 + 2 * 4 + 2 * 4 * 64           # z and m per chunk, U_down m per chunk, dU partials
-    per_bh = 2 * 64 * 64 + 64 * 64 * 64 + vecs
+    per_bh = 2 * 64 * 64 + 8 * 64 * 64 + vecs
     per_bh = (per_bh + 3) // 4 * 4 + 100 * 1 * (4 * 64 + 1)
     assert sh.bwd_workspace_bytes == 6 * 4 * ((per_bh + 3) // 4 * 4)
     sh128 = _lib.ref_shapes(cfg(dk=128, dv=128))
@@ -203,10 +205,10 @@ def test_bwd_workspace_size():
     assert _lib.ref_shapes(cfg(B=0)).bwd_workspace_bytes == 0
     # without a projection the rows of a head are split into d / 16 slices, and
     # each token keeps every slice's four column sums and its dw share
-    per_bh0 = 2 * 64 * 64 + 64 * 64 * 64 + 2 * 2 * 64 + 100 * 4 * (4 * 64 + 1)
+    per_bh0 = 2 * 64 * 64 + 8 * 64 * 64 + 2 * 2 * 64 + 100 * 4 * (4 * 64 + 1)
     own0 = 6 * 4 * ((per_bh0 + 3) // 4 * 4)
     assert _lib.ref_shapes(cfg(rank=0, dtype=_lib.CARVE_F32)).bwd_workspace_bytes == own0
-    per_bh32 = 4 * 64 * 64 + 32 * 64 * 64 + 4 * 2 * 64 + 100 * 4 * (4 * 64 + 1)   # L = 32: four chunks
+    per_bh32 = 4 * 64 * 64 + 4 * 64 * 64 + 4 * 2 * 64 + 100 * 4 * (4 * 64 + 1)   # L = 32: four chunks
     assert _lib.ref_shapes(cfg(rank=0, L=32)).bwd_workspace_bytes == 6 * 4 * per_bh32
     # in bf16 with L a multiple of 64 the forward pair supplies the chunk-start
     # states, and the chunks are walked in groups (here both chunks at once):
@@ -215,12 +217,12 @@ def test_bwd_workspace_size():
     sh0 = _lib.ref_shapes(cfg(rank=0))
     fwd = sh0.workspace_bytes
     assert fwd > 0
-    per_bh_pre = 2 * 64 * 64 + 2 * 64 * 64 * 64 + 2 * 64 * 64 + 2 * 2 * 64 + 100 * 4 * (4 * 64 + 1)
+    per_bh_pre = 2 * 64 * 64 + 2 * 8 * 64 * 64 + 2 * 64 * 64 + 2 * 2 * 64 + 100 * 4 * (4 * 64 + 1)
     own_pre = 6 * 4 * ((per_bh_pre + 3) // 4 * 4)
     assert sh0.bwd_workspace_bytes == (own_pre + 255) // 256 * 256 + fwd + 2 * 100 * 3 * 64 * 2
     # at most eight groups: 40 chunks of 64 tokens
     long_pre = _lib.ref_shapes(cfg(rank=0, T=2560))
-    per_bh_long = 40 * 64 * 64 + 8 * 64 * 64 * 64 + 40 * 64 * 64 + 40 * 2 * 64 + 2560 * 4 * (4 * 64 + 1)
+    per_bh_long = 40 * 64 * 64 + 8 * 8 * 64 * 64 + 40 * 64 * 64 + 40 * 2 * 64 + 2560 * 4 * (4 * 64 + 1)
     own_long = 6 * 4 * ((per_bh_long + 3) // 4 * 4)
     assert long_pre.bwd_workspace_bytes == ((own_long + 255) // 256 * 256 + long_pre.workspace_bytes
                                             + 2 * 2560 * 3 * 64 * 2)
