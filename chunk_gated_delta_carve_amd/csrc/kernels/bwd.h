@@ -64,8 +64,8 @@ struct BwdArgs {
 // gradient at every chunk end is first carried back over all tokens alone
 // (the dS sweep: its recurrence needs the inputs, not the forward states),
 // and then up to kBwdGroups workgroups per row slice walk disjoint runs of
-// chunks at once. Otherwise one workgroup walks all chunks.
-constexpr int kBwdGroups = 8;
+// chunks at once (16: measured 2% faster than 8, no slower than 32). Otherwise one workgroup walks all chunks.
+constexpr int kBwdGroups = 16;
 // Tokens per sub-block of the row-lane reverse walk: the walk keeps a
 // sub-block's recomputed states in registers and stores only the state at
 // each sub-block start.

@@ -189,7 +189,7 @@ int carve_chunk_fwd_noalloc(const carve_config* cfg,
  *               with rank == 0 and L a multiple of 64, also the forward
  *               pair's block images and an output, since the chunk-start
  *               states then come from the forward's chunk-parallel state pass;
- *               the chunks are then walked in up to 8 groups at once, which
+ *               the chunks are then walked in up to 16 groups at once, which
  *               takes one chunk's recomputed states per group and the state
  *               gradient at every chunk end, 4 (G ceil(L / 8) + nc) dk dv
  *               bytes per (batch, head) in place of 4 ceil(L / 8) dk dv (the

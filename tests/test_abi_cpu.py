@@ -220,9 +220,9 @@ def test_bwd_workspace_size():
     per_bh_pre = 2 * 64 * 64 + 2 * 8 * 64 * 64 + 2 * 64 * 64 + 2 * 2 * 64 + 100 * 4 * (4 * 64 + 1)
     own_pre = 6 * 4 * ((per_bh_pre + 3) // 4 * 4)
     assert sh0.bwd_workspace_bytes == (own_pre + 255) // 256 * 256 + fwd + 2 * 100 * 3 * 64 * 2
-    # at most eight groups: 40 chunks of 64 tokens
+    # at most sixteen groups: 40 chunks of 64 tokens
     long_pre = _lib.ref_shapes(cfg(rank=0, T=2560))
-    per_bh_long = 40 * 64 * 64 + 8 * 8 * 64 * 64 + 40 * 64 * 64 + 40 * 2 * 64 + 2560 * 4 * (4 * 64 + 1)
+    per_bh_long = 40 * 64 * 64 + 16 * 8 * 64 * 64 + 40 * 64 * 64 + 40 * 2 * 64 + 2560 * 4 * (4 * 64 + 1)
     own_long = 6 * 4 * ((per_bh_long + 3) // 4 * 4)
     assert long_pre.bwd_workspace_bytes == ((own_long + 255) // 256 * 256 + long_pre.workspace_bytes
                                             + 2 * 2560 * 3 * 64 * 2)
