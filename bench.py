@@ -454,6 +454,8 @@ def backward_kernels(wl, rank):
     if rank == 0:
         pre = ("carve_intra_kernel + carve_state_kernel (chunk-start states) + "
                if wl.dtype == "bf16" and wl.L % 64 == 0 else "")
+        if pre and wl.L == 64 and wl.dk == 64:
+            return pre + "carve_bwd_split_kernel (dS sweep) + carve_bwd_chunk_kernel (one call)"
         return pre + "carve_bwd_split_kernel + carve_bwd_finish_kernel (one call)"
     if wl.dk == 64:
         return "carve_bwd_split_kernel + carve_bwd_finish_kernel + carve_bwd_ub_kernel (one call)"

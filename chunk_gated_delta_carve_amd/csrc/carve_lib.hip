@@ -10,6 +10,7 @@
 #include "carve.h"
 #include "kernels/kernels.h"
 #include "kernels/bwd.h"
+#include "kernels/bwd_chunk.h"
 #include "kernels/step.h"
 
 namespace {
@@ -76,13 +77,21 @@ int64_t parallel_workspace_bytes(const carve_config* c) {
 // backward's own workspace.
 bool bwd_from_forward(const carve_config* c) { return chunk_parallel(c) && c->L % kParallelBlock == 0; }
 
+// The chunk-parallel backward (one workgroup per (batch, head, chunk), dense
+// products on the matrix cores) covers d = 64 with 64-token chunks and the
+// decay and keys as given; every other shape walks the tokens.
+bool bwd_chunked(const carve_config* c) {
+  return bwd_from_forward(c) && c->L == kParallelBlock && c->dk == 64 && c->T > 0 &&
+         !(c->flags & (CARVE_DECAY_LOGITS | CARVE_QK_L2NORM));
+}
+
 struct BwdBytes {
   int64_t img, o, total;   // byte offsets of the forward's images and output, and the size
 };
 BwdBytes bwd_bytes(const carve_config* c) {
   const int64_t B = c->B, H = c->H, T = c->T;
   const int64_t own = B * H * 4 * (int64_t)carve::BwdWs(c->dk, c->T, c->L, c->rank, (c->flags & CARVE_QK_L2NORM) != 0,
-                                                       bwd_from_forward(c) && c->T > 0).total;
+                                                       bwd_from_forward(c) && c->T > 0, bwd_chunked(c)).total;
   if (!bwd_from_forward(c)) return {0, 0, own};
   const int64_t img = (own + 255) & ~(int64_t)255;
   const int64_t o = img + parallel_workspace_bytes(c);
@@ -218,6 +227,25 @@ hipError_t launch_row_lane(const carve::BwdArgs& a, hipStream_t s) {
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL((carve::carve_bwd_finish_kernel<E, D, LG, CONTENT, NRM>), dim3((unsigned)((n + 255) / 256)),
                      dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// Chunk-parallel schedule: the dS sweep stores the state gradient at every
+// chunk end, then one workgroup per (batch, head, chunk) forms the gradients.
+hipError_t launch_chunked(const carve::BwdArgs& a, hipStream_t s) {
+  using SL = carve::SplitLayout<64, false>;
+  using CL = carve::ChunkBwdLayout<64>;
+  constexpr auto sweep = carve::carve_bwd_split_kernel<carve::bf16, 64, false, false, false, true>;
+  constexpr auto chunk = carve::carve_bwd_chunk_kernel<64>;
+  hipError_t e = set_lds<sweep>(SL::bytes);
+  if (e != hipSuccess) return e;
+  e = set_lds<chunk>(CL::bytes);
+  if (e != hipSuccess) return e;
+  const int nc = (a.T + a.L - 1) / a.L;
+  hipLaunchKernelGGL(sweep, dim3(a.B * a.H * SL::S), dim3(SL::NT), SL::bytes, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(chunk, dim3((unsigned)((int64_t)a.B * a.H * nc)), dim3(CL::NT), CL::bytes, s, a);
   return hipGetLastError();
 }
 
@@ -507,7 +535,7 @@ extern "C" int carve_chunk_bwd(const carve_config* cfg,
   a.B = cfg->B; a.H = cfg->H; a.T = cfg->T; a.L = cfg->L; a.rank = cfg->rank;
   a.norm = (cfg->flags & CARVE_QK_L2NORM) != 0;
   a.detach = (cfg->flags & CARVE_DETACH_MEAN) != 0;
-  a.pre_ckpt = bwd_from_forward(cfg) && cfg->T > 0;
+  a.pre_ckpt = bwd_chunked(cfg) ? 2 : bwd_from_forward(cfg) && cfg->T > 0;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool lg = (cfg->flags & CARVE_DECAY_LOGITS) != 0;
   hipError_t e = hipSuccess;
@@ -524,11 +552,13 @@ extern "C" int carve_chunk_bwd(const carve_config* cfg,
     f.ws = wsb + bb.img;
     f.B = cfg->B; f.H = cfg->H; f.T = cfg->T; f.L = cfg->L; f.rank = 0;
     f.ckpt = static_cast<float*>(workspace);
-    f.ckpt_bh = carve::BwdWs(cfg->dk, cfg->T, cfg->L, 0, a.norm != 0, true).total;
+    f.ckpt_bh = carve::BwdWs(cfg->dk, cfg->T, cfg->L, 0, a.norm != 0, true, a.pre_ckpt == 2).total;
     f.ckpt_shift = cfg->L == 2 * kParallelBlock ? 1 : 0;
     e = dispatch_fwd_ckpt_flags(cfg, f, s);
   }
-  if (e == hipSuccess)
+  if (e == hipSuccess && a.pre_ckpt == 2)
+    e = launch_chunked(a, s);
+  else if (e == hipSuccess)
     e = cfg->dtype == CARVE_BF16
             ? (lg ? dispatch_bwd_width<carve::bf16, true>(cfg, a, s) : dispatch_bwd_width<carve::bf16, false>(cfg, a, s))
             : (lg ? dispatch_bwd_width<float, true>(cfg, a, s) : dispatch_bwd_width<float, false>(cfg, a, s));

@@ -56,7 +56,8 @@ struct BwdArgs {
   int B, H, T, L, rank;
   int norm;   // nonzero: q, k are used over their L2 norms (inverse norms in the workspace)
   int detach; // nonzero: the gate's chunk means are constants (no dm from the gate)
-  int pre_ckpt; // nonzero: the chunk-start states are already in the workspace (no forward sweep)
+  int pre_ckpt; // nonzero: the chunk-start states are already in the workspace (no forward sweep);
+                // 2: in the chunk-parallel schedule's layout (the dS sweep then feeds carve_bwd_chunk_kernel)
 };
 
 // Chunk groups of the row-lane schedule without a projection when the
@@ -90,11 +91,25 @@ __host__ __device__ constexpr int bwd_slices(int D, int rank) { return rank == 0
 // With q, k normalisation it also keeps every token's inverse norms of q
 // and k and the fp32 gradients of the normalised q and k, which a last
 // kernel takes through the normalisation.
+//
+// The chunk-parallel schedule (carve_bwd_chunk_kernel, `chunked`) keeps only
+// the chunk-start states, the state gradient at every chunk end and each
+// row's share of d_mean_out over the last chunk's tokens.
 struct BwdWs {
-  size_t ckpt, sbuf, sbuf_group, dsck, z, m, y, dud, duu, part, wpart, nrm, dqh, dkh, total;
+  size_t ckpt, sbuf, sbuf_group, dsck, dmo, z, m, y, dud, duu, part, wpart, nrm, dqh, dkh, total;
   int groups;
-  __host__ __device__ BwdWs(int D, int T, int L, int rank, bool norm, bool pre_ckpt) {
+  __host__ __device__ BwdWs(int D, int T, int L, int rank, bool norm, bool pre_ckpt, bool chunked = false) {
     const size_t nc = (size_t)(T + L - 1) / L, DD = (size_t)D * D;
+    if (chunked) {
+      groups = 1;
+      ckpt = 0;
+      sbuf = sbuf_group = 0;
+      dsck = nc * DD;
+      dmo = 2 * nc * DD;
+      z = m = y = dud = duu = part = wpart = nrm = dqh = dkh = dmo + D;
+      total = (dmo + D + 3) & ~(size_t)3;
+      return;
+    }
     groups = bwd_groups(T, L, rank, pre_ckpt);
     ckpt = 0;
     sbuf = ckpt + nc * DD;
@@ -103,7 +118,7 @@ struct BwdWs {
     // sub-block start for the row-lane kernel
     sbuf_group = (rank > 0 && D == 128 ? (size_t)L : (size_t)(L + kBwdSub - 1) / kBwdSub) * DD;
     dsck = sbuf + (size_t)groups * sbuf_group;
-    z = dsck + (groups > 1 ? nc * DD : 0);
+    dmo = z = dsck + (groups > 1 ? nc * DD : 0);
     m = z + nc * D;
     y = m + nc * D;
     dud = y + nc * rank;
@@ -652,7 +667,7 @@ carve_bwd_split_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, L = a.L, H = a.H, rank = kContent ? a.rank : 0;
   const int nc = (T + L - 1) / L;
-  const BwdWs lay(D, T, L, rank, kNorm, a.pre_ckpt != 0);
+  const BwdWs lay(D, T, L, rank, kNorm, a.pre_ckpt != 0, a.pre_ckpt == 2);
   // workgroup: (batch, head), chunk group (the dS sweep has one), row slice
   const int NG = kDsSweep ? 1 : lay.groups;
   const int slice = blockIdx.x % S, grp = (blockIdx.x / S) % NG, bh = blockIdx.x / S / NG;
@@ -859,6 +874,13 @@ carve_bwd_split_kernel(BwdArgs a) {
     const int tl0 = (nc - 1) * L;                        // first token of the last chunk
     // this row's share of d_mean_out, added to each output gradient of the last chunk
     const float dml = a.d_mean_out ? a.d_mean_out[(size_t)bh * D + e] / (float)(T - tl0) : 0.f;
+    if (a.pre_ckpt == 2 && cl == 0) {
+      // for the chunk-parallel kernel, which must not read d_mean_out (it may
+      // be the buffer that receives d_mean_in, zero here: without a
+      // projection no gradient reaches the incoming mean)
+      ws[lay.dmo + e] = dml;
+      if (a.d_mean_in) a.d_mean_in[(size_t)bh * D + e] = 0.f;
+    }
     const int nbt = (T + NB - 1) / NB, nwalk = nbt - L / NB;   // blocks of chunks nc - 1 .. 1
     auto tb0_of = [&](int kb) { return (nbt - 1 - kb) * NB; };
     auto nb_of = [&](int kb) { return min(NB, T - tb0_of(kb)); };

@@ -1,0 +1,647 @@
+// Chunk-parallel backward pass without a content projection (bf16 inputs,
+// d_k = d_v = 64, 64-token chunks): one workgroup per (batch, head, chunk)
+// forms every gradient of the chunk's tokens at once, from the state S at the
+// chunk start (written by the forward pair), the state gradient dS_L at the
+// chunk end (written by the dS sweep of carve_bwd_split_kernel) and the
+// chunk's inputs, as 16x16 products on the matrix cores.
+//
+// The pages train the layer but give no backward pass (gist.science technical
+// summaries, §2 and §3); the forward these derivatives belong to is the WY
+// block form of the key-axis recurrence (§2.1 erase gate, §2.2 write gate,
+// §2.3 key-axis decay). Inside a chunk, with G_i the inclusive cumulative
+// log-decay (G_{-1} = 0), E(a, b) = e^{a - b} per key channel, and
+// u_i = w_i v_i - S_{i-1} D_i (b_i k_i) (the rows of Delta):
+//   A_ij = sum_c b_i k_i k_j E(G_i, G_j),  P_ij = sum_c q_i k_j E(G_{i-1}, G_j)   (j < i)
+//   Delta = (I + A)^{-1} (W V - Kb S^T),   Kb_i = b_i k_i e^{G_i}
+// The gradient du_i = dS_i k_i of every u_i solves the transposed system
+//   dU = (I + A)^{-T} (P^T dO + Kdec dS_L^T),   Kdec_i = k_i e^{G_L - G_i},
+// and with Z_ij = do_i . u_j and N_ij = du_i . u_j:
+//   dq_i = e^{G_{i-1}} (dO S)_i + sum_{j<i} Z_ij k_j E(G_{i-1}, G_j)
+//   x_i  = e^{G_i} (dU S)_i + sum_{j<i} N_ij k_j E(G_i, G_j)          (x_i = X_i^T du_i, X_i = S_{i-1} D_i)
+//   dk_i = e^{G_L - G_i} (Delta dS_L)_i + sum_{j>i} Z_ji q_j E(G_{j-1}, G_i)
+//          - sum_{j>i} N_ji b_j k_j E(G_j, G_i) - b_i x_i
+//   db_i = -k_i x_i,  dv_i = w_i du_i,  dw_i = v_i . du_i.
+// The decay gradient needs no per-token state: H_i = diag(S_i^T dS_i) obeys
+// H_{i-1} = H_i + phi_i with phi_i = q_i dq_i - k_i dk_i + 2 b_i db_i, and
+// dg_i = H_{i-1} - q_i dq_i, so
+//   dg_i = H_L + sum_{j>=i} phi_j - q_i dq_i,
+//   H_L  = e^{G_L} diag(S^T dS_L) + sum_i Kdec_i (Delta dS_L)_i.
+// Chunk 0 also returns d_state_in = dS_L diag(e^{G_L}) + dO^T Qd - dU^T Kb,
+// Qd_i = q_i e^{G_{i-1}}.
+//
+// Decay factors use the 16-row sub-blocks of the forward (Gs_I: G before
+// sub-block I, Ge_I: G at its end): for sub-blocks I > J,
+// E(G_a, G_j) = E(G_a, Gs_I) E(Gs_I, Ge_J) E(Ge_J, G_j), every factor <= 1;
+// the middle factor scales a reduction index (Grams) or an output column
+// (token sums). Diagonal sub-blocks use E(Gs_I, Ge_I) <= 2^kSpanLimit2 on
+// top; a sub-block whose decay is steeper takes its diagonal terms pairwise,
+// from the raw inputs (slow, exact).
+//
+// Work split: four waves, wave I owning token rows 16I..16I+15 of every L x d
+// result and the 16x16 tiles that feed them. LDS holds the bf16 operands
+// (BKl_i = b_i k_i E(G_i, Gs_I), Ql_i = q_i E(G_{i-1}, Gs_I),
+// Kr_j = k_j E(Ge_J, G_j), W V, dO, S, dS_L, Delta and dU), G in fp32 and
+// the factor tables.
+#pragma once
+
+#include "bwd.h"
+
+namespace carve {
+
+template <int D>
+struct ChunkBwdLayout {
+  static_assert(D == 64, "the chunk-parallel backward is built for d = 64");
+  static constexpr int L = 64, LD = 72, GLD = 68;                // bf16 / fp32 row strides
+  static constexpr int MB = L * LD * 2;                           // one bf16 [64][LD] matrix
+  static constexpr int oBKl = 0, oQl = MB, oKr = 2 * MB, oWV = 3 * MB, odO = 4 * MB, oS = 5 * MB,
+                       odS = 6 * MB, oDel = 7 * MB;
+  static constexpr int oG = 8 * MB;                               // fp32 [L][GLD]: G in log2 units
+  static constexpr int oGs = oG + L * GLD * 4;                    // fp32 [4][D]
+  static constexpr int oGe = oGs + 4 * D * 4;                     // fp32 [4][D]
+  static constexpr int oMid = oGe + 4 * D * 4;                    // fp32 [4][4][D]
+  static constexpr int oDec = oMid + 16 * D * 4;                  // fp32 [4][D]: 2^{G_L - Ge_I}
+  static constexpr int oEg = oDec + 4 * D * 4;                    // fp32 [4][D]: 2^{Gs_I}
+  static constexpr int oAd = oEg + 4 * D * 4;                     // fp32 [4][16][16]: diagonal tiles of A
+  static constexpr int oTd = oAd + 4 * 256 * 4;                   // fp32 [4][16][16]: their inverses
+  static constexpr int oRed = oTd + 4 * 256 * 4;                  // fp32 [3][4][D]: column partial sums
+  static constexpr int oScr = oRed + 3 * 4 * D * 4;               // fp32 [4 waves][4][16][16]
+  static constexpr int oFlag = oScr + 4 * 4 * 256 * 4;            // int [4]: steep sub-blocks
+  static constexpr int bytes = oFlag + 16;
+  static constexpr int NT = 256;
+};
+
+template <int D>
+__global__ void __launch_bounds__(256) carve_bwd_chunk_kernel(BwdArgs a) {
+  using LY = ChunkBwdLayout<D>;
+  constexpr int L = LY::L, LD = LY::LD, GLD = LY::GLD;
+  constexpr size_t DD = (size_t)D * D;
+  typedef bf16x4 b4;
+  typedef Mma16<bf16> MB;
+  typedef Mma16<float> MF;
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16* BKl = reinterpret_cast<bf16*>(smem + LY::oBKl);
+  bf16* Ql = reinterpret_cast<bf16*>(smem + LY::oQl);
+  bf16* Kr = reinterpret_cast<bf16*>(smem + LY::oKr);
+  bf16* WV = reinterpret_cast<bf16*>(smem + LY::oWV);
+  bf16* dU = WV;                                                  // W V is dead once R is formed
+  bf16* dO = reinterpret_cast<bf16*>(smem + LY::odO);
+  bf16* Sm = reinterpret_cast<bf16*>(smem + LY::oS);
+  bf16* dSm = reinterpret_cast<bf16*>(smem + LY::odS);
+  bf16* Del = reinterpret_cast<bf16*>(smem + LY::oDel);
+  float* Gf = reinterpret_cast<float*>(smem + LY::oG);
+  float* Gs = reinterpret_cast<float*>(smem + LY::oGs);
+  float* Ge = reinterpret_cast<float*>(smem + LY::oGe);
+  float* Mid = reinterpret_cast<float*>(smem + LY::oMid);
+  float* Dec = reinterpret_cast<float*>(smem + LY::oDec);
+  float* Eg = reinterpret_cast<float*>(smem + LY::oEg);
+  float* Ad = reinterpret_cast<float*>(smem + LY::oAd);
+  float* Td = reinterpret_cast<float*>(smem + LY::oTd);
+  float* Red = reinterpret_cast<float*>(smem + LY::oRed);
+  float* Scr = reinterpret_cast<float*>(smem + LY::oScr);
+  int* Flag = reinterpret_cast<int*>(smem + LY::oFlag);
+
+  const int tid = threadIdx.x, lane = tid & 63, I = wave_id(), c16 = lane & 15, g4 = lane >> 4;
+  const int T = a.T, H = a.H, nc = (T + L - 1) / L;
+  const int ch = blockIdx.x % nc, bh = blockIdx.x / nc, bi = bh / H, h = bh % H;
+  const int t0 = ch * L, n = min(L, T - t0);
+  const BwdWs lay(D, T, L, 0, false, true, true);
+  const float* wsb = a.ws + (size_t)bh * lay.total;
+  const float* Sg = wsb + lay.ckpt + (size_t)ch * DD;
+  const float* dSg = wsb + lay.dsck + (size_t)ch * DD;
+  const bf16* Q = static_cast<const bf16*>(a.q);
+  const bf16* K = static_cast<const bf16*>(a.k);
+  const bf16* V = static_cast<const bf16*>(a.v);
+  const bf16* Gin = static_cast<const bf16*>(a.g);
+  const bf16* BX = static_cast<const bf16*>(a.bx);
+  const bf16* W = static_cast<const bf16*>(a.w);
+  const bf16* DOg = static_cast<const bf16*>(a.d_o);
+  auto tok = [&](int t) { return ((size_t)bi * T + t) * H + h; };
+
+  // ------------------------------------------------------------------ staging
+  // thread (row r, channels cs .. cs + 15) for the token inputs; rows past
+  // the chunk's tokens stay zero (they add nothing to any sum)
+  const int r = tid >> 2, cs = (tid & 3) * 16;
+  const bool rv = r < n;
+  bf16x8 xq[2], xk[2], xbx[2];
+  {
+    bf16x8 xv[2], xg[2], xdo[2];
+    float wr = 0.f;
+    if (rv) {
+      const size_t o = tok(t0 + r) * D + cs;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        xq[j] = *reinterpret_cast<const bf16x8*>(Q + o + 8 * j);
+        xk[j] = *reinterpret_cast<const bf16x8*>(K + o + 8 * j);
+        xv[j] = *reinterpret_cast<const bf16x8*>(V + o + 8 * j);
+        xg[j] = *reinterpret_cast<const bf16x8*>(Gin + o + 8 * j);
+        xbx[j] = *reinterpret_cast<const bf16x8*>(BX + o + 8 * j);
+        xdo[j] = *reinterpret_cast<const bf16x8*>(DOg + o + 8 * j);
+      }
+      wr = to_f32(W[tok(t0 + r)]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xq[j][i] = xk[j][i] = xv[j][i] = xg[j][i] = xbx[j][i] = xdo[j][i] = (bf16)0.f;
+    }
+    // the last chunk's outputs also carry d_mean_out / n (the dS sweep left
+    // each row's share in the workspace)
+    const bool lastc = ch == nc - 1;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      bf16x8 pwv, pdo;
+      f32x4 gg[2];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int cc = cs + 8 * j + i;
+        pwv[i] = (bf16)(wr * to_f32(xv[j][i]));
+        const float dml = lastc && rv ? wsb[lay.dmo + cc] : 0.f;
+        pdo[i] = (bf16)(to_f32(xdo[j][i]) + dml);
+        gg[i >> 2][i & 3] = to_f32(xg[j][i]) * kLog2e;
+      }
+      *reinterpret_cast<bf16x8*>(WV + r * LD + cs + 8 * j) = pwv;
+      *reinterpret_cast<bf16x8*>(dO + r * LD + cs + 8 * j) = pdo;
+      *reinterpret_cast<f32x4*>(Gf + r * GLD + cs + 8 * j) = gg[0];
+      *reinterpret_cast<f32x4*>(Gf + r * GLD + cs + 8 * j + 4) = gg[1];
+    }
+  }
+  {
+    // S and dS_L: thread (channel cc, rows 16 s .. 16 s + 15), the partial
+    // column sums of S .* dS_L on the side
+    const int cc = tid & 63, s = tid >> 6;
+    float hs = 0.f;
+#pragma unroll 4
+    for (int e = 16 * s; e < 16 * s + 16; ++e) {
+      const float sv = Sg[(size_t)e * D + cc], dv = dSg[(size_t)e * D + cc];
+      hs += sv * dv;
+      Sm[e * LD + cc] = (bf16)sv;
+      dSm[e * LD + cc] = (bf16)dv;
+    }
+    Red[s * D + cc] = hs;
+  }
+  lds_barrier();
+  {
+    // G: inclusive prefix over the chunk's rows, by (channel, 16-row segment)
+    const int cc = tid & 63, s = tid >> 6;
+    float gv[16], run = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      run += Gf[(16 * s + j) * GLD + cc];
+      gv[j] = run;
+    }
+    Red[4 * D + s * D + cc] = run;
+    lds_barrier();
+    float off = 0.f;
+    for (int s2 = 0; s2 < s; ++s2) off += Red[4 * D + s2 * D + cc];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) Gf[(16 * s + j) * GLD + cc] = gv[j] + off;
+    Gs[s * D + cc] = off;
+    Ge[s * D + cc] = off + run;
+    const bool steep = -run > kSpanLimit2;
+    const bool any = __builtin_amdgcn_ballot_w64(steep) != 0;
+    if (lane == 0) Flag[s] = any ? 1 : 0;
+  }
+  lds_barrier();
+  // factor tables: Mid[I][J] = 2^{Gs_I - Ge_J} (J < I), Mid[I][I] = 2^{Gs_I - Ge_I},
+  // Dec[I] = 2^{G_L - Ge_I}, Eg[I] = 2^{Gs_I}
+  for (int idx = tid; idx < 16 * D; idx += LY::NT) {
+    const int i1 = idx / (4 * D), j1 = (idx / D) & 3, cc = idx % D;
+    if (j1 <= i1) Mid[idx] = fast_exp2(Gs[i1 * D + cc] - Ge[j1 * D + cc]);
+  }
+  {
+    const int i1 = tid / D, cc = tid % D;
+    Dec[tid] = fast_exp2(Ge[3 * D + cc] - Ge[i1 * D + cc]);
+    Eg[tid] = fast_exp2(Gs[i1 * D + cc]);
+  }
+  {
+    // decayed operands of the thread's row
+    const int I0 = r >> 4;
+    const float* gr = Gf + r * GLD;
+    const float* grm = (r & 15) ? Gf + (r - 1) * GLD : Gs + I0 * D;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      bf16x8 pb, pq, pk;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int cc = cs + 8 * j + i;
+        const float G0 = gr[cc], gs = Gs[I0 * D + cc], ge = Ge[I0 * D + cc];
+        const float kv = to_f32(xk[j][i]);
+        pb[i] = (bf16)(sigmoid_f(to_f32(xbx[j][i])) * kv * fast_exp2(G0 - gs));
+        pq[i] = (bf16)(to_f32(xq[j][i]) * fast_exp2(grm[cc] - gs));
+        pk[i] = (bf16)(kv * fast_exp2(ge - G0));
+      }
+      *reinterpret_cast<bf16x8*>(BKl + r * LD + cs + 8 * j) = pb;
+      *reinterpret_cast<bf16x8*>(Ql + r * LD + cs + 8 * j) = pq;
+      *reinterpret_cast<bf16x8*>(Kr + r * LD + cs + 8 * j) = pk;
+    }
+  }
+  lds_barrier();
+
+  // ------------------------------------------------------------- fragments
+  // A operand: row r0 + c16, reduction indices k0 + 4 g4 .. + 3 of a
+  // row-major [row][k] matrix (also the B operand of a product against the
+  // rows of a second matrix, B[k][n] = Y[n][k]).
+  auto ldA = [&](const bf16* m, int r0, int k0) -> b4 {
+    return *reinterpret_cast<const b4*>(m + (r0 + c16) * LD + k0 + 4 * g4);
+  };
+  auto ldAs = [&](const bf16* m, int r0, int k0, const float* sc, float sign) -> b4 {
+    const b4 x = ldA(m, r0, k0);
+    const f32x4 f = *reinterpret_cast<const f32x4*>(sc + k0 + 4 * g4);
+    return b4{(bf16)(sign * to_f32(x[0]) * f[0]), (bf16)(sign * to_f32(x[1]) * f[1]),
+              (bf16)(sign * to_f32(x[2]) * f[2]), (bf16)(sign * to_f32(x[3]) * f[3])};
+  };
+  // B operand from a row-major [k][n] matrix: B[k0 + 4 g4 + p][n0 + c16]
+  auto ldBc = [&](const bf16* m, int k0, int n0) -> b4 {
+    const bf16* p = m + (k0 + 4 * g4) * LD + n0 + c16;
+    return b4{p[0], p[LD], p[2 * LD], p[3 * LD]};
+  };
+  auto scl = [](b4 x, float f) -> b4 {
+    return b4{(bf16)(to_f32(x[0]) * f), (bf16)(to_f32(x[1]) * f), (bf16)(to_f32(x[2]) * f), (bf16)(to_f32(x[3]) * f)};
+  };
+  // 16x16 tile C[row][col] = sum over the 64 columns of X[rx + row] . Y[ry + col]
+  auto gram = [&](const bf16* X, int rx, const bf16* Y, int ry) -> f32x4 {
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) acc = MB::mma(ldA(X, rx, 16 * ks), ldA(Y, ry, 16 * ks), acc);
+    return acc;
+  };
+  auto grams = [&](const bf16* X, int rx, const float* sx, const bf16* Y, int ry) -> f32x4 {
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) acc = MB::mma(ldAs(X, rx, 16 * ks, sx, 1.f), ldA(Y, ry, 16 * ks), acc);
+    return acc;
+  };
+  auto rnd = [](f32x4 x) { return MB::round(x); };
+  const bool steep = Flag[I] != 0;
+  // raw inputs of the pairwise path (steep sub-blocks only)
+  auto raw = [&](const bf16* X, int row, int cc) { return row < n ? to_f32(X[tok(t0 + row) * D + cc]) : 0.f; };
+  auto raw_bk = [&](int row, int cc) {
+    return row < n ? sigmoid_f(to_f32(BX[tok(t0 + row) * D + cc])) * to_f32(K[tok(t0 + row) * D + cc]) : 0.f;
+  };
+  auto gprev = [&](int row, int cc) { return (row & 15) ? Gf[(row - 1) * GLD + cc] : Gs[(row >> 4) * D + cc]; };
+
+  // ------------------------------------------------- Grams, R and the right side
+  const int r0 = 16 * I;
+  // aF[J] (J < I): C[j][i] = A[i][j]; aB[J] (J > I): C[j][i] = A[j][i]
+  f32x4 aF[4], aB[4];
+#pragma unroll
+  for (int J = 0; J < 4; ++J) {
+    aF[J] = aB[J] = zero4();
+    if (J < I) aF[J] = grams(Kr, 16 * J, Mid + (I * 4 + J) * D, BKl, r0);
+    if (J > I) aB[J] = grams(BKl, 16 * J, Mid + (J * 4 + I) * D, Kr, r0);
+  }
+  {
+    // diagonal tile of A: C[i][j], j < i
+    f32x4 ad;
+    if (!steep) {
+      ad = grams(BKl, r0, Mid + I * 5 * D, Kr, r0);
+    } else {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int i = r0 + 4 * g4 + ii, j = r0 + c16;
+        float acc = 0.f;
+        if (j < i)
+          for (int cc = 0; cc < D; ++cc)
+            acc += raw_bk(i, cc) * raw(K, j, cc) * fast_exp2(Gf[i * GLD + cc] - Gf[j * GLD + cc]);
+        ad[ii] = acc;
+      }
+    }
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) Ad[I * 256 + (4 * g4 + ii) * 16 + c16] = c16 < 4 * g4 + ii ? ad[ii] : 0.f;
+  }
+  // Y = P^T dO + Kdec dS_L^T  (rows i of block I, columns e)
+  f32x4 y[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) y[nt] = zero4();
+#pragma unroll
+  for (int J = 0; J < 4; ++J) {
+    if (J < I) continue;
+    f32x4 p;                                                      // C[j][i] = P[j][i]
+    if (J > I) {
+      p = grams(Ql, 16 * J, Mid + (J * 4 + I) * D, Kr, r0);
+    } else {
+      if (!steep) {
+        p = grams(Ql, r0, Mid + I * 5 * D, Kr, r0);
+      } else {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int j = r0 + 4 * g4 + ii, i = r0 + c16;
+          float acc = 0.f;
+          if (j > i)
+            for (int cc = 0; cc < D; ++cc)
+              acc += raw(Q, j, cc) * raw(K, i, cc) * fast_exp2(gprev(j, cc) - Gf[i * GLD + cc]);
+          p[ii] = acc;
+        }
+      }
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+        if (!(4 * g4 + ii > c16)) p[ii] = 0.f;
+    }
+    const b4 pa = rnd(p);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) y[nt] = MB::mma(pa, ldBc(dO, 16 * J, 16 * nt), y[nt]);
+  }
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      y[nt] = MB::mma(ldAs(Kr, r0, 16 * ks, Dec + I * D, 1.f), ldA(dSm, 16 * nt, 16 * ks), y[nt]);
+  // R = W V - Kb S^T
+  f32x4 R[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) R[nt][ii] = to_f32(WV[(r0 + 4 * g4 + ii) * LD + 16 * nt + c16]);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      R[nt] = MB::mma(ldAs(BKl, r0, 16 * ks, Eg + I * D, -1.f), ldA(Sm, 16 * nt, 16 * ks), R[nt]);
+  }
+  lds_barrier();
+  {
+    // Td_I = (I + A_II)^{-1}: lane c16 walks column c16 down the rows
+    const float* A_ = Ad + I * 256;
+    float t[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float v = i == c16 ? 1.f : 0.f;
+#pragma unroll
+      for (int k = 0; k < i; ++k) v -= A_[i * 16 + k] * t[k];
+      t[i] = v;
+    }
+    if (lane < 16)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) Td[I * 256 + i * 16 + c16] = t[i];
+  }
+  lds_barrier();
+
+  // ------------------------------------------ Delta = (I + A)^{-1} R, by blocks
+  f32x4 acc[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) acc[nt] = zero4();
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    if (I == rr) {
+      const f32x4 ta = *reinterpret_cast<const f32x4*>(Td + rr * 256 + c16 * 16 + 4 * g4);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const f32x4 dl = MF::mma(ta, R[nt] - acc[nt], zero4());
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) Del[(16 * rr + 4 * g4 + ii) * LD + 16 * nt + c16] = (bf16)dl[ii];
+      }
+    }
+    lds_barrier();
+    if (I > rr) {
+      const b4 af = rnd(aF[rr]);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) acc[nt] = MB::mma(af, ldBc(Del, 16 * rr, 16 * nt), acc[nt]);
+    }
+  }
+
+  // ------------------------------------------ dU = (I + A)^{-T} Y, by blocks
+  f32x4 du[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    acc[nt] = zero4();
+    du[nt] = zero4();
+  }
+#pragma unroll
+  for (int rr = 3; rr >= 0; --rr) {
+    if (I == rr) {
+      const float* tdb = Td + rr * 256 + 4 * g4 * 16 + c16;
+      const f32x4 ta = {tdb[0], tdb[16], tdb[32], tdb[48]};     // (Td^T)[c16][4 g4 + p]
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        du[nt] = MF::mma(ta, y[nt] - acc[nt], zero4());
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) dU[(16 * rr + 4 * g4 + ii) * LD + 16 * nt + c16] = (bf16)du[nt][ii];
+      }
+    }
+    lds_barrier();
+    if (I < rr) {
+      const b4 ab = rnd(aB[rr]);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) acc[nt] = MB::mma(ab, ldBc(dU, 16 * rr, 16 * nt), acc[nt]);
+    }
+  }
+
+  // ------------------------------------------------------------ token sums
+  // raw inputs of the lane's output elements (rows 16 I + 4 g4 + ii,
+  // columns 16 nt + c16), loaded now so they land during the products
+  bf16 pq[4][4], pk[4][4], pbx[4][4], pv[4][4];
+  float pw[4];
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) {
+    const int i = r0 + 4 * g4 + ii;
+    const bool ok = i < n;
+    const size_t ro = tok(t0 + min(i, n - 1)) * D;
+    pw[ii] = ok ? to_f32(W[tok(t0 + min(i, n - 1))]) : 0.f;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const size_t o = ro + 16 * nt + c16;
+      pq[nt][ii] = ok ? Q[o] : (bf16)0.f;
+      pk[nt][ii] = ok ? K[o] : (bf16)0.f;
+      pbx[nt][ii] = ok ? BX[o] : (bf16)0.f;
+      pv[nt][ii] = ok ? V[o] : (bf16)0.f;
+    }
+  }
+  // qa, xa: sums over j < i (left factor applied at the end); ka: sums over
+  // j > i; qx, xx, kx: exact diagonal terms of steep sub-blocks
+  f32x4 qa[4], xa[4], ka[4], qx[4], xx[4], kx[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) qa[nt] = xa[nt] = ka[nt] = qx[nt] = xx[nt] = kx[nt] = zero4();
+#pragma unroll
+  for (int J = 0; J < 4; ++J) {
+    if (J < I) {
+      const b4 zt = rnd(gram(Del, 16 * J, dO, r0));              // C[j][i] = Z[i][j]
+      const b4 nt_ = rnd(gram(Del, 16 * J, dU, r0));             // C[j][i] = N[i][j]
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const b4 kb = ldBc(Kr, 16 * J, 16 * nt);
+        const float m = Mid[(I * 4 + J) * D + 16 * nt + c16];
+        qa[nt] += m * MB::mma(zt, kb, zero4());
+        xa[nt] += m * MB::mma(nt_, kb, zero4());
+      }
+    } else if (J > I) {
+      const b4 z = rnd(gram(dO, 16 * J, Del, r0));               // C[j][i] = Z[j][i]
+      const b4 nn = rnd(-gram(dU, 16 * J, Del, r0));             // C[j][i] = -N[j][i]
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const float m = Mid[(J * 4 + I) * D + 16 * nt + c16];
+        ka[nt] += m * MB::mma(z, ldBc(Ql, 16 * J, 16 * nt), MB::mma(nn, ldBc(BKl, 16 * J, 16 * nt), zero4()));
+      }
+    } else {
+      f32x4 zt = gram(Del, r0, dO, r0), nt_ = gram(Del, r0, dU, r0);
+      f32x4 z = gram(dO, r0, Del, r0), nn = gram(dU, r0, Del, r0);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int jr = 4 * g4 + ii;                              // C row: j; column: i = c16
+        if (!(jr < c16)) zt[ii] = nt_[ii] = 0.f;
+        if (!(jr > c16)) z[ii] = nn[ii] = 0.f;
+      }
+      if (!steep) {
+        const b4 zb = rnd(zt), nb = rnd(nt_), z2 = rnd(z), n2 = rnd(-nn);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const b4 kb = ldBc(Kr, r0, 16 * nt);
+          const float m = Mid[I * 5 * D + 16 * nt + c16];
+          qa[nt] += m * MB::mma(zb, kb, zero4());
+          xa[nt] += m * MB::mma(nb, kb, zero4());
+          ka[nt] += m * MB::mma(z2, ldBc(Ql, r0, 16 * nt), MB::mma(n2, ldBc(BKl, r0, 16 * nt), zero4()));
+        }
+      } else {
+        // the four diagonal tiles to LDS, then each output element's terms pairwise
+        float* sc = Scr + I * 1024;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int o = (4 * g4 + ii) * 16 + c16;
+          sc[o] = zt[ii];
+          sc[256 + o] = nt_[ii];
+          sc[512 + o] = z[ii];
+          sc[768 + o] = nn[ii];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const int cc = 16 * nt + c16;
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int il = 4 * g4 + ii, i = r0 + il;
+            const float gi = Gf[i * GLD + cc], gim = gprev(i, cc);
+            float sq = 0.f, sx = 0.f, sk = 0.f;
+            for (int jl = 0; jl < 16; ++jl) {
+              const int j = r0 + jl;
+              if (jl < il) {
+                const float kj = raw(K, j, cc), gj = Gf[j * GLD + cc];
+                sq += sc[jl * 16 + il] * kj * fast_exp2(gim - gj);
+                sx += sc[256 + jl * 16 + il] * kj * fast_exp2(gi - gj);
+              } else if (jl > il) {
+                sk += sc[512 + jl * 16 + il] * raw(Q, j, cc) * fast_exp2(gprev(j, cc) - gi) -
+                      sc[768 + jl * 16 + il] * raw_bk(j, cc) * fast_exp2(Gf[j * GLD + cc] - gi);
+              }
+            }
+            qx[nt][ii] = sq;
+            xx[nt][ii] = sx;
+            kx[nt][ii] = sk;
+          }
+        }
+      }
+    }
+  }
+
+  // -------------------------------------------------------- assembly
+  bf16* dq_o = static_cast<bf16*>(a.dq);
+  bf16* dk_o = static_cast<bf16*>(a.dk);
+  bf16* dv_o = static_cast<bf16*>(a.dv);
+  bf16* dg_o = static_cast<bf16*>(a.dg);
+  bf16* dbx_o = static_cast<bf16*>(a.dbx);
+  bf16* dw_o = static_cast<bf16*>(a.dw);
+  f32x4 sfx[4];                                  // within-lane suffix of phi minus q dq
+  float tot[4], hlc[4], dwp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    f32x4 dOS = zero4(), dUS = zero4(), DdS = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const b4 sb = ldBc(Sm, 16 * ks, 16 * nt);
+      dOS = MB::mma(ldA(dO, r0, 16 * ks), sb, dOS);
+      dUS = MB::mma(ldA(dU, r0, 16 * ks), sb, dUS);
+      DdS = MB::mma(ldA(Del, r0, 16 * ks), ldBc(dSm, 16 * ks, 16 * nt), DdS);
+    }
+    const int cc = 16 * nt + c16;
+    const float gs = Gs[I * D + cc], ge = Ge[I * D + cc], gl = Ge[3 * D + cc];
+    f32x4 phi, qdq;
+    float hl = 0.f;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int i = r0 + 4 * g4 + ii;
+      const float gi = Gf[i * GLD + cc], gim = gprev(i, cc);
+      const float qv = to_f32(pq[nt][ii]), kv = to_f32(pk[nt][ii]), bv = sigmoid_f(to_f32(pbx[nt][ii]));
+      const float ed = fast_exp2(gl - gi);
+      const float dq = fast_exp2(gim - gs) * qa[nt][ii] + qx[nt][ii] + fast_exp2(gim) * dOS[ii];
+      const float xd = fast_exp2(gi - gs) * xa[nt][ii] + xx[nt][ii] + fast_exp2(gi) * dUS[ii];
+      const float dk = ed * DdS[ii] + fast_exp2(ge - gi) * ka[nt][ii] + kx[nt][ii] - bv * xd;
+      const float db = -kv * xd;
+      phi[ii] = qv * dq - kv * dk + 2.f * bv * db;
+      qdq[ii] = qv * dq;
+      hl += kv * ed * DdS[ii];
+      const float dvv = pw[ii] * du[nt][ii];
+      dwp[ii] += to_f32(pv[nt][ii]) * du[nt][ii];
+      if (i < n) {
+        const size_t o = tok(t0 + i) * D + cc;
+        dq_o[o] = (bf16)dq;
+        dk_o[o] = (bf16)dk;
+        dbx_o[o] = (bf16)(db * bv * (1.f - bv));
+        dv_o[o] = (bf16)dvv;
+      }
+    }
+    // suffix sums of phi over the lane's rows, minus q dq
+    const float s3 = phi[3], s2 = phi[2] + s3, s1 = phi[1] + s2, s0 = phi[0] + s1;
+    sfx[nt] = f32x4{s0 - qdq[0], s1 - qdq[1], s2 - qdq[2], s3 - qdq[3]};
+    tot[nt] = s0;
+    hlc[nt] = hl;
+  }
+  // dw: row sums over the 64 value columns
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) {
+    const float s = sum_row16(dwp[ii]);
+    const int i = r0 + 4 * g4 + ii;
+    if (c16 == ii && i < n) dw_o[tok(t0 + i)] = (bf16)s;
+  }
+  // phi suffixes over the lane groups of the wave, and wave totals
+  float sg[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const float t1 = __shfl(tot[nt], c16 + 16), t2 = __shfl(tot[nt], c16 + 32), t3 = __shfl(tot[nt], c16 + 48);
+    const float t0v = __shfl(tot[nt], c16);
+    sg[nt] = (g4 < 1 ? t1 : 0.f) + (g4 < 2 ? t2 : 0.f) + (g4 < 3 ? t3 : 0.f);
+    const float hw = sum_groups(hlc[nt]);
+    if (g4 == 0) {
+      Red[4 * D + I * D + 16 * nt + c16] = t0v + t1 + t2 + t3;
+      Red[8 * D + I * D + 16 * nt + c16] = hw;
+    }
+  }
+  lds_barrier();
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int cc = 16 * nt + c16;
+    float hsum = 0.f, hl = 0.f, sw = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      hsum += Red[w * D + cc];
+      hl += Red[8 * D + w * D + cc];
+      if (w > I) sw += Red[4 * D + w * D + cc];
+    }
+    const float HL = fast_exp2(Ge[3 * D + cc]) * hsum + hl;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int i = r0 + 4 * g4 + ii;
+      if (i < n) dg_o[tok(t0 + i) * D + cc] = (bf16)(HL + sw + sg[nt] + sfx[nt][ii]);
+    }
+  }
+
+  // ------------------------------------------- gradient of the incoming state
+  if (ch == 0 && a.d_state_in) {
+    // rows e = 16 I + 4 g4 + ii, columns c = 16 nt + c16
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      f32x4 s1 = zero4(), s2 = zero4();
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const float eg = Eg[ks * D + 16 * nt + c16];
+        s1 = MB::mma(ldBc(dO, 16 * ks, r0), scl(ldBc(Ql, 16 * ks, 16 * nt), eg), s1);
+        s2 = MB::mma(ldBc(dU, 16 * ks, r0), scl(ldBc(BKl, 16 * ks, 16 * nt), eg), s2);
+      }
+      const int cc = 16 * nt + c16;
+      const float el = fast_exp2(Ge[3 * D + cc]);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int e = r0 + 4 * g4 + ii;
+        a.d_state_in[(size_t)bh * DD + (size_t)e * D + cc] = dSg[(size_t)e * D + cc] * el + s1[ii] - s2[ii];
+      }
+    }
+  }
+}
+
+}  // namespace carve

@@ -138,6 +138,54 @@ def test_backward_without_state_gradients(torch_cuda):
     assert_grads(got, bwd_oracle(inp, "bf16", 64, do, None, None, None, None), TOL["bf16"], "no state")
 
 
+CHUNK_CASES = [
+    # bf16, d 64, L 64, no projection: the chunk-parallel schedule (one
+    # workgroup per (batch, head, 64-token chunk) on the matrix cores)
+    ("one-short-chunk-40", 2, 2, 40, True),
+    ("whole-chunks-256", 1, 3, 256, True),
+    ("ragged-150", 2, 1, 150, True),
+    ("no-state-gradients-200", 2, 2, 200, False),
+]
+
+
+@pytest.mark.parametrize("name,B,H,T,with_state", CHUNK_CASES, ids=[c[0] for c in CHUNK_CASES])
+def test_backward_chunk_parallel(torch_cuda, name, B, H, T, with_state):
+    wl = workload("chunk-" + name, "bf16", B, H, T, 64, 64, 0, 6900 + T)
+    say("case chunk", wl)
+    inp = make_inputs(wl)
+    do, dSo, dmo, S_in, m_in = cotangents(B, H, T, 64, "bf16", 6950 + T, with_state=with_state)
+    got = bwd_gpu(torch_cuda, inp, "bf16", 64, do, dSo, dmo, S_in, m_in)
+    assert_grads(got, bwd_oracle(inp, "bf16", 64, do, dSo, dmo, S_in, m_in), TOL["bf16"], "chunk " + name)
+
+
+def test_backward_chunk_parallel_steep_decay(torch_cuda):
+    """Sub-blocks whose decay falls by more than 2^96 over 16 tokens in some
+    channel (log-decays of about -6 and -30 per token) take their diagonal
+    terms pairwise from the raw inputs; the rest of the chunk is factorised."""
+    from chunk_gated_delta_carve_amd.workloads import bf16_bits_from_f32
+    wl = workload("chunk-steep", "bf16", 1, 2, 150, 64, 64, 0, 7000)
+    inp = make_inputs(wl)
+    g = to_f64(inp["g"], "bf16")
+    g[:, :, 0, :8] *= 10.0                       # head 0: eight steep channels
+    g[:, 40:90, 1, 8:12] = -30.0                 # head 1: near-total forgetting in the middle
+    inp["g"] = bf16_bits_from_f32(g.astype(np.float32))
+    do, dSo, dmo, S_in, m_in = cotangents(1, 2, 150, 64, "bf16", 7001)
+    got = bwd_gpu(torch_cuda, inp, "bf16", 64, do, dSo, dmo, S_in, m_in)
+    assert_grads(got, bwd_oracle(inp, "bf16", 64, do, dSo, dmo, S_in, m_in), TOL["bf16"], "chunk steep")
+
+
+def test_backward_chunk_parallel_in_place(torch_cuda):
+    """The chunk-parallel schedule with d_state_in and d_mean_in written over
+    d_state_out and d_mean_out (several chunks, so other workgroups still
+    need the last chunk's mean gradient when chunk 0's is written)."""
+    wl = workload("chunk-alias", "bf16", 2, 2, 200, 64, 64, 0, 7100)
+    inp = make_inputs(wl)
+    do, dSo, dmo, S_in, m_in = cotangents(2, 2, 200, 64, "bf16", 7101)
+    ref = bwd_oracle(inp, "bf16", 64, do, dSo, dmo, S_in, m_in)
+    got = bwd_gpu(torch_cuda, inp, "bf16", 64, do, dSo.copy(), dmo.copy(), S_in, m_in, alias=True)
+    assert_grads(got, ref, TOL["bf16"], "chunk in place")
+
+
 @pytest.mark.parametrize("dtype,L,rank", [("f32", 32, 0), ("f32", 32, 8), ("bf16", 64, 0)],
                          ids=["f32-r0", "f32-r8", "bf16-r0-forward-checkpoints"])
 def test_backward_with_decay_logits(torch_cuda, dtype, L, rank):
