@@ -230,22 +230,36 @@ hipError_t launch_row_lane(const carve::BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Chunk-parallel schedule: the dS sweep stores the state gradient at every
-// chunk end, then one workgroup per (batch, head, chunk) forms the gradients.
-hipError_t launch_chunked(const carve::BwdArgs& a, hipStream_t s) {
-  using SL = carve::SplitLayout<64, false>;
+// Chunk-parallel schedule (after the forward pair has written the chunk-start
+// states and its block images): the images become the backward chain's, the
+// checkpointing state pass walks that chain from the last chunk and stores
+// the state gradient at every chunk end, then one workgroup per (batch,
+// head, chunk) forms the gradients.
+hipError_t launch_chunked(const carve::BwdArgs& a, unsigned char* imgs, void* o_scratch, hipStream_t s) {
   using CL = carve::ChunkBwdLayout<64>;
-  constexpr auto sweep = carve::carve_bwd_split_kernel<carve::bf16, 64, false, false, false, true>;
+  using LY = carve::BlockLayout<carve::bf16, 64, 64, kParallelBlock>;
+  constexpr auto image = carve::carve_bwd_image_kernel<64>;
+  constexpr auto chain = carve::carve_state_kernel<carve::bf16, 64, 64, kParallelBlock, true>;
   constexpr auto chunk = carve::carve_bwd_chunk_kernel<64>;
-  hipError_t e = set_lds<sweep>(SL::bytes);
+  hipError_t e = set_lds<chunk>(CL::bytes);
   if (e != hipSuccess) return e;
-  e = set_lds<chunk>(CL::bytes);
-  if (e != hipSuccess) return e;
-  const int nc = (a.T + a.L - 1) / a.L;
-  hipLaunchKernelGGL(sweep, dim3(a.B * a.H * SL::S), dim3(SL::NT), SL::bytes, s, a);
+  const int64_t nc = (a.T + kParallelBlock - 1) / kParallelBlock, BH = (int64_t)a.B * a.H;
+  hipLaunchKernelGGL(image, dim3((unsigned)(BH * ((nc + 1) / 2))), dim3(256), 0, s, a, imgs);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(chunk, dim3((unsigned)((int64_t)a.B * a.H * nc)), dim3(CL::NT), CL::bytes, s, a);
+  const carve::BwdWs lay(64, a.T, kParallelBlock, 0, false, true, true);
+  carve::FwdArgs f{};
+  f.ws = imgs;
+  f.state_in = a.d_state_out;
+  f.o = o_scratch;
+  f.ckpt = a.ws + lay.dsck;
+  f.ckpt_bh = lay.total;
+  f.ckpt_shift = 0;
+  f.B = a.B; f.H = a.H; f.T = a.T; f.L = kParallelBlock; f.rank = 0;
+  hipLaunchKernelGGL(chain, dim3(carve::state_grid(a.B * a.H, LY::NW)), dim3(carve::kStateThreads), 0, s, f);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(chunk, dim3((unsigned)(BH * nc)), dim3(CL::NT), CL::bytes, s, a);
   return hipGetLastError();
 }
 
@@ -556,8 +570,11 @@ extern "C" int carve_chunk_bwd(const carve_config* cfg,
     f.ckpt_shift = cfg->L == 2 * kParallelBlock ? 1 : 0;
     e = dispatch_fwd_ckpt_flags(cfg, f, s);
   }
-  if (e == hipSuccess && a.pre_ckpt == 2)
-    e = launch_chunked(a, s);
+  if (e == hipSuccess && a.pre_ckpt == 2) {
+    const BwdBytes bb = bwd_bytes(cfg);
+    unsigned char* wsb = static_cast<unsigned char*>(workspace);
+    e = launch_chunked(a, wsb + bb.img, wsb + bb.o, s);
+  }
   else if (e == hipSuccess)
     e = cfg->dtype == CARVE_BF16
             ? (lg ? dispatch_bwd_width<carve::bf16, true>(cfg, a, s) : dispatch_bwd_width<carve::bf16, false>(cfg, a, s))

@@ -57,7 +57,7 @@ struct BwdArgs {
   int norm;   // nonzero: q, k are used over their L2 norms (inverse norms in the workspace)
   int detach; // nonzero: the gate's chunk means are constants (no dm from the gate)
   int pre_ckpt; // nonzero: the chunk-start states are already in the workspace (no forward sweep);
-                // 2: in the chunk-parallel schedule's layout (the dS sweep then feeds carve_bwd_chunk_kernel)
+                // 2: in the layout of the chunk-parallel schedule (carve_bwd_chunk_kernel)
 };
 
 // Chunk groups of the row-lane schedule without a projection when the
@@ -667,7 +667,7 @@ carve_bwd_split_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, L = a.L, H = a.H, rank = kContent ? a.rank : 0;
   const int nc = (T + L - 1) / L;
-  const BwdWs lay(D, T, L, rank, kNorm, a.pre_ckpt != 0, a.pre_ckpt == 2);
+  const BwdWs lay(D, T, L, rank, kNorm, a.pre_ckpt != 0);
   // workgroup: (batch, head), chunk group (the dS sweep has one), row slice
   const int NG = kDsSweep ? 1 : lay.groups;
   const int slice = blockIdx.x % S, grp = (blockIdx.x / S) % NG, bh = blockIdx.x / S / NG;
@@ -874,13 +874,6 @@ carve_bwd_split_kernel(BwdArgs a) {
     const int tl0 = (nc - 1) * L;                        // first token of the last chunk
     // this row's share of d_mean_out, added to each output gradient of the last chunk
     const float dml = a.d_mean_out ? a.d_mean_out[(size_t)bh * D + e] / (float)(T - tl0) : 0.f;
-    if (a.pre_ckpt == 2 && cl == 0) {
-      // for the chunk-parallel kernel, which must not read d_mean_out (it may
-      // be the buffer that receives d_mean_in, zero here: without a
-      // projection no gradient reaches the incoming mean)
-      ws[lay.dmo + e] = dml;
-      if (a.d_mean_in) a.d_mean_in[(size_t)bh * D + e] = 0.f;
-    }
     const int nbt = (T + NB - 1) / NB, nwalk = nbt - L / NB;   // blocks of chunks nc - 1 .. 1
     auto tb0_of = [&](int kb) { return (nbt - 1 - kb) * NB; };
     auto nb_of = [&](int kb) { return min(NB, T - tb0_of(kb)); };

@@ -2,8 +2,14 @@
 // d_k = d_v = 64, 64-token chunks): one workgroup per (batch, head, chunk)
 // forms every gradient of the chunk's tokens at once, from the state S at the
 // chunk start (written by the forward pair), the state gradient dS_L at the
-// chunk end (written by the dS sweep of carve_bwd_split_kernel) and the
-// chunk's inputs, as 16x16 products on the matrix cores.
+// chunk end and the chunk's inputs, as 16x16 products on the matrix cores.
+// The state gradients come from a chain over chunks run by the forward's own
+// state pass (carve_state_kernel with checkpoints) on images that
+// carve_bwd_image_kernel derives from the forward pair's: the adjoint of
+// S <- S M + C, O = Q_eff S^T + O_loc is
+//   dS_start = dS_end M^T + dO^T Q_eff,
+// which is the state pass's S^T <- M^T S^T + C^T with M^T replaced by M and
+// C^T by (dO^T Q_eff)^T, walked from the last chunk to the first.
 //
 // The pages train the layer but give no backward pass (gist.science technical
 // summaries, §2 and §3); the forward these derivatives belong to is the WY
@@ -44,6 +50,7 @@
 // the factor tables.
 #pragma once
 
+#include "block.h"
 #include "bwd.h"
 
 namespace carve {
@@ -107,7 +114,7 @@ __global__ void __launch_bounds__(256) carve_bwd_chunk_kernel(BwdArgs a) {
   const BwdWs lay(D, T, L, 0, false, true, true);
   const float* wsb = a.ws + (size_t)bh * lay.total;
   const float* Sg = wsb + lay.ckpt + (size_t)ch * DD;
-  const float* dSg = wsb + lay.dsck + (size_t)ch * DD;
+  const float* dSg = wsb + lay.dsck + (size_t)(nc - 1 - ch) * DD;   // the chain runs from the last chunk
   const bf16* Q = static_cast<const bf16*>(a.q);
   const bf16* K = static_cast<const bf16*>(a.k);
   const bf16* V = static_cast<const bf16*>(a.v);
@@ -144,8 +151,8 @@ __global__ void __launch_bounds__(256) carve_bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) xq[j][i] = xk[j][i] = xv[j][i] = xg[j][i] = xbx[j][i] = xdo[j][i] = (bf16)0.f;
     }
-    // the last chunk's outputs also carry d_mean_out / n (the dS sweep left
-    // each row's share in the workspace)
+    // the last chunk's outputs also carry d_mean_out / n (carve_bwd_image_kernel
+    // left each row's share in the workspace)
     const bool lastc = ch == nc - 1;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -621,7 +628,9 @@ __global__ void __launch_bounds__(256) carve_bwd_chunk_kernel(BwdArgs a) {
     }
   }
 
-  // ------------------------------------------- gradient of the incoming state
+  // ------------------------------------------- gradients of the incoming state and mean
+  // (no gradient reaches the incoming mean without a projection)
+  if (ch == 0 && a.d_mean_in && tid < D) a.d_mean_in[(size_t)bh * D + tid] = 0.f;
   if (ch == 0 && a.d_state_in) {
     // rows e = 16 I + 4 g4 + ii, columns c = 16 nt + c16
 #pragma unroll
@@ -640,6 +649,127 @@ __global__ void __launch_bounds__(256) carve_bwd_chunk_kernel(BwdArgs a) {
         const int e = r0 + 4 * g4 + ii;
         a.d_state_in[(size_t)bh * DD + (size_t)e * D + cc] = dSg[(size_t)e * D + cc] * el + s1[ii] - s2[ii];
       }
+    }
+  }
+}
+
+// Backward images of the chunk-parallel schedule, in place of the forward
+// pair's: chunk c's goes to image slot nc - 1 - c (one workgroup per pair of
+// chunks c, nc - 1 - c, which swap slots), so that the checkpointing state
+// pass, reading the slots in order, walks the chunks from the last:
+//   Mt slot: A operands of M (rows d, k = d'), i.e. the forward's M^T units
+//            transposed (gathered element by element through LDS);
+//   Ct slot: C tiles of F^T = (dO^T Q_eff)^T (rows d, columns e), per value
+//            slice and paired as the forward's C^T tiles, with the last
+//            chunk's dO carrying d_mean_out / n.
+// The Q_eff and O_loc slots keep the forward's contents (the state pass
+// forms an output from them into a scratch buffer, unused). The workgroup
+// that holds the last chunk also leaves each row's share of d_mean_out in the
+// workspace for carve_bwd_chunk_kernel.
+template <int D>
+__global__ void __launch_bounds__(256) carve_bwd_image_kernel(BwdArgs a, unsigned char* imgs) {
+  using LY = BlockLayout<bf16, D, D, 64>;
+  static_assert(D == 64 && LY::NU == 2 && LY::TD == 4 && LY::NB == 4, "d = 64 images of 64-token blocks");
+  constexpr int NU = LY::NU, TD = LY::TD, LDO = 72;
+  constexpr int MTB = D * D * 2;                                  // bytes of the Mt units (Q_eff follows)
+  static_assert(LY::wMt == 0 && LY::wQe == MTB, "Mt and Q_eff units are contiguous");
+  typedef bf16x4 b4;
+  typedef bf16x8 b8;
+  __shared__ __align__(16) unsigned char sm[2][2 * MTB];          // Mt and Q_eff units of each chunk
+  __shared__ __align__(16) bf16 sdo[2][64 * LDO];                 // dO of each chunk [t][e]
+  const int T = a.T, H = a.H, nc = (T + 63) / 64, np = (nc + 1) / 2;
+  const int pr = blockIdx.x % np, bh = blockIdx.x / np, bi = bh / H, h = bh % H;
+  const int cA = pr, cB = nc - 1 - pr, nch = cA == cB ? 1 : 2;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), c16 = lane & 15, g4 = lane >> 4;
+  unsigned char* base = imgs + (size_t)bh * nc * LY::wBytes;
+  const BwdWs lay(D, T, 64, 0, false, true, true);
+  float* wsb = a.ws + (size_t)bh * lay.total;
+  const bf16* DOg = static_cast<const bf16*>(a.d_o);
+  const int tl0 = (nc - 1) * 64;
+  for (int x = 0; x < nch; ++x) {
+    const int c = x ? cB : cA, t0 = 64 * c, n = min(64, T - t0);
+    const uint4* src = reinterpret_cast<const uint4*>(base + (size_t)c * LY::wBytes);
+#pragma unroll
+    for (int i = 0; i < 2 * MTB / 16 / 256; ++i) reinterpret_cast<uint4*>(sm[x])[tid + 256 * i] = src[tid + 256 * i];
+    const int r = tid >> 2, cs = (tid & 3) * 16;
+    b8 v[2];
+    if (r < n) {
+      const size_t o = (((size_t)bi * T + t0 + r) * H + h) * D + cs;
+      v[0] = *reinterpret_cast<const b8*>(DOg + o);
+      v[1] = *reinterpret_cast<const b8*>(DOg + o + 8);
+      if (c == nc - 1 && a.d_mean_out) {
+        const float inv = 1.f / (float)(T - tl0);
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          v[j >> 3][j & 7] = (bf16)(to_f32(v[j >> 3][j & 7]) + a.d_mean_out[(size_t)bh * D + cs + j] * inv);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j >> 3][j & 7] = (bf16)0.f;
+    }
+    *reinterpret_cast<b8*>(&sdo[x][r * LDO + cs]) = v[0];
+    *reinterpret_cast<b8*>(&sdo[x][r * LDO + cs + 8]) = v[1];
+    if (c == nc - 1 && tid < D)
+      wsb[lay.dmo + tid] = a.d_mean_out ? a.d_mean_out[(size_t)bh * D + tid] / (float)(T - tl0) : 0.f;
+  }
+  lds_barrier();
+  // element (row r, column col) of a forward unit block (Mt or Q_eff):
+  // unit (r / 16, col / 32), lane 16 ((col % 16) / 4) + r % 16, half (col / 16) % 2, element col % 4
+  auto at = [](const unsigned char* units, int r, int col) {
+    const int off = (((r >> 4) * NU + (col >> 5)) * 64 + 16 * ((col & 15) >> 2) + (r & 15)) * 16 +
+                    ((col >> 4) & 1) * 8 + (col & 3) * 2;
+    return *reinterpret_cast<const bf16*>(units + off);
+  };
+  for (int x = 0; x < nch; ++x) {
+    const int c = x ? cB : cA;
+    unsigned char* dst = base + (size_t)(nc - 1 - c) * LY::wBytes;
+    // Mb units (D = w, u): lane (g4, c16) holds M[d = 16 D + c16][k], k = 32 u + 4 g4 + i and
+    // 32 u + 16 + 4 g4 + i, with M[d][k] = Mt[k][d]
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      b8 m;
+      const int d = 16 * w + c16;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m[j] = at(sm[x], 32 * u + 16 * (j >> 2) + 4 * g4 + (j & 3), d);
+      *reinterpret_cast<b8*>(dst + LY::wMt + ((w * NU + u) * 64 + lane) * 16) = m;
+    }
+    // F^T tiles (rows d, columns e) = sum_t Q_eff[t][d] dO[t][e]: this wave
+    // takes the row tiles 2 a, 2 a + 1 of value slices 2 b, 2 b + 1
+    const int ta = w & 1, sb = w >> 1;
+    f32x4 f[2][2];
+#pragma unroll
+    for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+      for (int ss = 0; ss < 2; ++ss) f[dd][ss] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      b4 qa[2], db[2];
+#pragma unroll
+      for (int dd = 0; dd < 2; ++dd) {
+        const int d = 16 * (2 * ta + dd) + c16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qa[dd][i] = at(sm[x] + MTB, 16 * ks + 4 * g4 + i, d);
+      }
+#pragma unroll
+      for (int ss = 0; ss < 2; ++ss) {
+        const bf16* p = &sdo[x][(16 * ks + 4 * g4) * LDO + 16 * (2 * sb + ss) + c16];
+        db[ss] = b4{p[0], p[LDO], p[2 * LDO], p[3 * LDO]};
+      }
+#pragma unroll
+      for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+        for (int ss = 0; ss < 2; ++ss) f[dd][ss] = Mma16<bf16>::mma(qa[dd], db[ss], f[dd][ss]);
+    }
+#pragma unroll
+    for (int ss = 0; ss < 2; ++ss) {
+      const int slice = 2 * sb + ss;
+      b8 pv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pv[i] = (bf16)f[0][ss][i];
+        pv[4 + i] = (bf16)f[1][ss][i];
+      }
+      *reinterpret_cast<b8*>(dst + LY::wCt + ((slice * (TD / 2) + ta) * 64 + lane) * 16) = pv;
     }
   }
 }
