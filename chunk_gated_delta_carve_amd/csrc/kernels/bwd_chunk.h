@@ -43,9 +43,9 @@
 // top; a sub-block whose decay is steeper takes its diagonal terms pairwise,
 // from the raw inputs (slow, exact).
 //
-// Work split: four waves, wave I owning token rows 16I..16I+15 of every L x d
-// result and the 16x16 tiles that feed them. LDS holds the bf16 operands
-// (BKl_i = b_i k_i E(G_i, Gs_I), Ql_i = q_i E(G_{i-1}, Gs_I),
+// Work split: eight waves, two per 16-row block I: both form the 16x16 tiles
+// that feed rows 16I..16I+15, and each takes half of the d output columns.
+// LDS holds the bf16 operands (BKl_i = b_i k_i E(G_i, Gs_I), Ql_i = q_i E(G_{i-1}, Gs_I),
 // Kr_j = k_j E(Ge_J, G_j), W V, dO, S, dS_L, Delta and dU), G in fp32 and
 // the factor tables.
 #pragma once
@@ -59,6 +59,7 @@ template <int D>
 struct ChunkBwdLayout {
   static_assert(D == 64, "the chunk-parallel backward is built for d = 64");
   static constexpr int L = 64, LD = 72, GLD = 68;                // bf16 / fp32 row strides
+  static constexpr int NWV = 8, NT = 64 * NWV;                    // two waves per 16-row block
   static constexpr int MB = L * LD * 2;                           // one bf16 [64][LD] matrix
   static constexpr int oBKl = 0, oQl = MB, oKr = 2 * MB, oWV = 3 * MB, odO = 4 * MB, oS = 5 * MB,
                        odS = 6 * MB, oDel = 7 * MB;
@@ -70,17 +71,18 @@ struct ChunkBwdLayout {
   static constexpr int oEg = oDec + 4 * D * 4;                    // fp32 [4][D]: 2^{Gs_I}
   static constexpr int oAd = oEg + 4 * D * 4;                     // fp32 [4][16][16]: diagonal tiles of A
   static constexpr int oTd = oAd + 4 * 256 * 4;                   // fp32 [4][16][16]: their inverses
-  static constexpr int oRed = oTd + 4 * 256 * 4;                  // fp32 [3][4][D]: column partial sums
-  static constexpr int oScr = oRed + 3 * 4 * D * 4;               // fp32 [4 waves][4][16][16]
-  static constexpr int oFlag = oScr + 4 * 4 * 256 * 4;            // int [4]: steep sub-blocks
+  static constexpr int oRed = oTd + 4 * 256 * 4;                  // fp32 [16][D]: column partial sums
+  static constexpr int oScr = oRed + 16 * D * 4;                  // bf16 [NWV][4][16][16]
+  static constexpr int oDw = oScr + NWV * 4 * 256 * 2;            // fp32 [NWV][16]: dw partials
+  static constexpr int oFlag = oDw + NWV * 16 * 4;                // int [4]: steep sub-blocks
   static constexpr int bytes = oFlag + 16;
-  static constexpr int NT = 256;
 };
 
 template <int D>
-__global__ void __launch_bounds__(256) carve_bwd_chunk_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(512) carve_bwd_chunk_kernel(BwdArgs a) {
   using LY = ChunkBwdLayout<D>;
-  constexpr int L = LY::L, LD = LY::LD, GLD = LY::GLD;
+  constexpr int L = LY::L, LD = LY::LD, GLD = LY::GLD, NT = LY::NT;
+  static_assert(NT == 512, "eight waves: two per 16-row block, two column tiles each");
   constexpr size_t DD = (size_t)D * D;
   typedef bf16x4 b4;
   typedef Mma16<bf16> MB;
@@ -104,10 +106,14 @@ __global__ void __launch_bounds__(256) carve_bwd_chunk_kernel(BwdArgs a) {
   float* Ad = reinterpret_cast<float*>(smem + LY::oAd);
   float* Td = reinterpret_cast<float*>(smem + LY::oTd);
   float* Red = reinterpret_cast<float*>(smem + LY::oRed);
-  float* Scr = reinterpret_cast<float*>(smem + LY::oScr);
+  bf16* Scr = reinterpret_cast<bf16*>(smem + LY::oScr);
+  float* Dwp = reinterpret_cast<float*>(smem + LY::oDw);
   int* Flag = reinterpret_cast<int*>(smem + LY::oFlag);
 
-  const int tid = threadIdx.x, lane = tid & 63, I = wave_id(), c16 = lane & 15, g4 = lane >> 4;
+  // wave w: rows 16 I .. 16 I + 15 (I = w / 2) of every L x d result, column
+  // tiles 2 hc and 2 hc + 1 (hc = w % 2)
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), I = w >> 1, hc = w & 1;
+  const int c16 = lane & 15, g4 = lane >> 4;
   const int T = a.T, H = a.H, nc = (T + L - 1) / L;
   const int ch = blockIdx.x % nc, bh = blockIdx.x / nc, bi = bh / H, h = bh % H;
   const int t0 = ch * L, n = min(L, T - t0);
@@ -125,97 +131,96 @@ __global__ void __launch_bounds__(256) carve_bwd_chunk_kernel(BwdArgs a) {
   auto tok = [&](int t) { return ((size_t)bi * T + t) * H + h; };
 
   // ------------------------------------------------------------------ staging
-  // thread (row r, channels cs .. cs + 15) for the token inputs; rows past
+  // thread (row r, channels cs .. cs + 7) for the token inputs; rows past
   // the chunk's tokens stay zero (they add nothing to any sum)
-  const int r = tid >> 2, cs = (tid & 3) * 16;
+  const int r = tid >> 3, cs = (tid & 7) * 8;
   const bool rv = r < n;
-  bf16x8 xq[2], xk[2], xbx[2];
+  bf16x8 xq, xk, xbx;
   {
-    bf16x8 xv[2], xg[2], xdo[2];
+    bf16x8 xv, xg, xdo;
     float wr = 0.f;
     if (rv) {
       const size_t o = tok(t0 + r) * D + cs;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        xq[j] = *reinterpret_cast<const bf16x8*>(Q + o + 8 * j);
-        xk[j] = *reinterpret_cast<const bf16x8*>(K + o + 8 * j);
-        xv[j] = *reinterpret_cast<const bf16x8*>(V + o + 8 * j);
-        xg[j] = *reinterpret_cast<const bf16x8*>(Gin + o + 8 * j);
-        xbx[j] = *reinterpret_cast<const bf16x8*>(BX + o + 8 * j);
-        xdo[j] = *reinterpret_cast<const bf16x8*>(DOg + o + 8 * j);
-      }
+      xq = *reinterpret_cast<const bf16x8*>(Q + o);
+      xk = *reinterpret_cast<const bf16x8*>(K + o);
+      xv = *reinterpret_cast<const bf16x8*>(V + o);
+      xg = *reinterpret_cast<const bf16x8*>(Gin + o);
+      xbx = *reinterpret_cast<const bf16x8*>(BX + o);
+      xdo = *reinterpret_cast<const bf16x8*>(DOg + o);
       wr = to_f32(W[tok(t0 + r)]);
     } else {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int i = 0; i < 8; ++i) xq[i] = xk[i] = xv[i] = xg[i] = xbx[i] = xdo[i] = (bf16)0.f;
+    }
+    // S and dS_L: thread (channel cc, rows 8 s .. 8 s + 7), every load issued
+    // before any store; the partial column sums of S .* dS_L on the side
+    const int cc = tid & 63, s = tid >> 6;
+    float sv[8], dv[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) xq[j][i] = xk[j][i] = xv[j][i] = xg[j][i] = xbx[j][i] = xdo[j][i] = (bf16)0.f;
+    for (int j = 0; j < 8; ++j) {
+      sv[j] = Sg[(size_t)(8 * s + j) * D + cc];
+      dv[j] = dSg[(size_t)(8 * s + j) * D + cc];
     }
     // the last chunk's outputs also carry d_mean_out / n (carve_bwd_image_kernel
     // left each row's share in the workspace)
     const bool lastc = ch == nc - 1;
+    bf16x8 pwv, pdo;
+    f32x4 gg[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      bf16x8 pwv, pdo;
-      f32x4 gg[2];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int cc = cs + 8 * j + i;
-        pwv[i] = (bf16)(wr * to_f32(xv[j][i]));
-        const float dml = lastc && rv ? wsb[lay.dmo + cc] : 0.f;
-        pdo[i] = (bf16)(to_f32(xdo[j][i]) + dml);
-        gg[i >> 2][i & 3] = to_f32(xg[j][i]) * kLog2e;
-      }
-      *reinterpret_cast<bf16x8*>(WV + r * LD + cs + 8 * j) = pwv;
-      *reinterpret_cast<bf16x8*>(dO + r * LD + cs + 8 * j) = pdo;
-      *reinterpret_cast<f32x4*>(Gf + r * GLD + cs + 8 * j) = gg[0];
-      *reinterpret_cast<f32x4*>(Gf + r * GLD + cs + 8 * j + 4) = gg[1];
+    for (int i = 0; i < 8; ++i) {
+      pwv[i] = (bf16)(wr * to_f32(xv[i]));
+      const float dml = lastc && rv ? wsb[lay.dmo + cs + i] : 0.f;
+      pdo[i] = (bf16)(to_f32(xdo[i]) + dml);
+      gg[i >> 2][i & 3] = to_f32(xg[i]) * kLog2e;
     }
-  }
-  {
-    // S and dS_L: thread (channel cc, rows 16 s .. 16 s + 15), the partial
-    // column sums of S .* dS_L on the side
-    const int cc = tid & 63, s = tid >> 6;
+    *reinterpret_cast<bf16x8*>(WV + r * LD + cs) = pwv;
+    *reinterpret_cast<bf16x8*>(dO + r * LD + cs) = pdo;
+    *reinterpret_cast<f32x4*>(Gf + r * GLD + cs) = gg[0];
+    *reinterpret_cast<f32x4*>(Gf + r * GLD + cs + 4) = gg[1];
     float hs = 0.f;
-#pragma unroll 4
-    for (int e = 16 * s; e < 16 * s + 16; ++e) {
-      const float sv = Sg[(size_t)e * D + cc], dv = dSg[(size_t)e * D + cc];
-      hs += sv * dv;
-      Sm[e * LD + cc] = (bf16)sv;
-      dSm[e * LD + cc] = (bf16)dv;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      hs += sv[j] * dv[j];
+      Sm[(8 * s + j) * LD + cc] = (bf16)sv[j];
+      dSm[(8 * s + j) * LD + cc] = (bf16)dv[j];
     }
-    Red[s * D + cc] = hs;
+    Red[s * D + cc] = hs;                                         // rows 0 .. 7: S .* dS_L partials
   }
   lds_barrier();
   {
-    // G: inclusive prefix over the chunk's rows, by (channel, 16-row segment)
+    // G: inclusive prefix over the chunk's rows, by (channel, 16-row
+    // segment) in the first four waves
     const int cc = tid & 63, s = tid >> 6;
     float gv[16], run = 0.f;
+    if (s < 4) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      run += Gf[(16 * s + j) * GLD + cc];
-      gv[j] = run;
+      for (int j = 0; j < 16; ++j) {
+        run += Gf[(16 * s + j) * GLD + cc];
+        gv[j] = run;
+      }
+      Red[(8 + s) * D + cc] = run;
     }
-    Red[4 * D + s * D + cc] = run;
     lds_barrier();
-    float off = 0.f;
-    for (int s2 = 0; s2 < s; ++s2) off += Red[4 * D + s2 * D + cc];
+    if (s < 4) {
+      float off = 0.f;
+      for (int s2 = 0; s2 < s; ++s2) off += Red[(8 + s2) * D + cc];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) Gf[(16 * s + j) * GLD + cc] = gv[j] + off;
-    Gs[s * D + cc] = off;
-    Ge[s * D + cc] = off + run;
-    const bool steep = -run > kSpanLimit2;
-    const bool any = __builtin_amdgcn_ballot_w64(steep) != 0;
-    if (lane == 0) Flag[s] = any ? 1 : 0;
+      for (int j = 0; j < 16; ++j) Gf[(16 * s + j) * GLD + cc] = gv[j] + off;
+      Gs[s * D + cc] = off;
+      Ge[s * D + cc] = off + run;
+      const bool steep = -run > kSpanLimit2;
+      const bool any = __builtin_amdgcn_ballot_w64(steep) != 0;
+      if (lane == 0) Flag[s] = any ? 1 : 0;
+    }
   }
   lds_barrier();
   // factor tables: Mid[I][J] = 2^{Gs_I - Ge_J} (J < I), Mid[I][I] = 2^{Gs_I - Ge_I},
   // Dec[I] = 2^{G_L - Ge_I}, Eg[I] = 2^{Gs_I}
-  for (int idx = tid; idx < 16 * D; idx += LY::NT) {
+  for (int idx = tid; idx < 16 * D; idx += NT) {
     const int i1 = idx / (4 * D), j1 = (idx / D) & 3, cc = idx % D;
     if (j1 <= i1) Mid[idx] = fast_exp2(Gs[i1 * D + cc] - Ge[j1 * D + cc]);
   }
-  {
+  if (tid < 4 * D) {
     const int i1 = tid / D, cc = tid % D;
     Dec[tid] = fast_exp2(Ge[3 * D + cc] - Ge[i1 * D + cc]);
     Eg[tid] = fast_exp2(Gs[i1 * D + cc]);
@@ -225,22 +230,19 @@ __global__ void __launch_bounds__(256) carve_bwd_chunk_kernel(BwdArgs a) {
     const int I0 = r >> 4;
     const float* gr = Gf + r * GLD;
     const float* grm = (r & 15) ? Gf + (r - 1) * GLD : Gs + I0 * D;
+    bf16x8 pb, pq, pk;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      bf16x8 pb, pq, pk;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int cc = cs + 8 * j + i;
-        const float G0 = gr[cc], gs = Gs[I0 * D + cc], ge = Ge[I0 * D + cc];
-        const float kv = to_f32(xk[j][i]);
-        pb[i] = (bf16)(sigmoid_f(to_f32(xbx[j][i])) * kv * fast_exp2(G0 - gs));
-        pq[i] = (bf16)(to_f32(xq[j][i]) * fast_exp2(grm[cc] - gs));
-        pk[i] = (bf16)(kv * fast_exp2(ge - G0));
-      }
-      *reinterpret_cast<bf16x8*>(BKl + r * LD + cs + 8 * j) = pb;
-      *reinterpret_cast<bf16x8*>(Ql + r * LD + cs + 8 * j) = pq;
-      *reinterpret_cast<bf16x8*>(Kr + r * LD + cs + 8 * j) = pk;
+    for (int i = 0; i < 8; ++i) {
+      const int cc = cs + i;
+      const float G0 = gr[cc], gs = Gs[I0 * D + cc], ge = Ge[I0 * D + cc];
+      const float kv = to_f32(xk[i]);
+      pb[i] = (bf16)(sigmoid_f(to_f32(xbx[i])) * kv * fast_exp2(G0 - gs));
+      pq[i] = (bf16)(to_f32(xq[i]) * fast_exp2(grm[cc] - gs));
+      pk[i] = (bf16)(kv * fast_exp2(ge - G0));
     }
+    *reinterpret_cast<bf16x8*>(BKl + r * LD + cs) = pb;
+    *reinterpret_cast<bf16x8*>(Ql + r * LD + cs) = pq;
+    *reinterpret_cast<bf16x8*>(Kr + r * LD + cs) = pk;
   }
   lds_barrier();
 
@@ -290,6 +292,7 @@ __global__ void __launch_bounds__(256) carve_bwd_chunk_kernel(BwdArgs a) {
   // ------------------------------------------------- Grams, R and the right side
   const int r0 = 16 * I;
   // aF[J] (J < I): C[j][i] = A[i][j]; aB[J] (J > I): C[j][i] = A[j][i]
+  // (both waves of a block form them)
   f32x4 aF[4], aB[4];
 #pragma unroll
   for (int J = 0; J < 4; ++J) {
@@ -297,7 +300,7 @@ __global__ void __launch_bounds__(256) carve_bwd_chunk_kernel(BwdArgs a) {
     if (J < I) aF[J] = grams(Kr, 16 * J, Mid + (I * 4 + J) * D, BKl, r0);
     if (J > I) aB[J] = grams(BKl, 16 * J, Mid + (J * 4 + I) * D, Kr, r0);
   }
-  {
+  if (hc == 0) {
     // diagonal tile of A: C[i][j], j < i
     f32x4 ad;
     if (!steep) {
@@ -316,10 +319,10 @@ __global__ void __launch_bounds__(256) carve_bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) Ad[I * 256 + (4 * g4 + ii) * 16 + c16] = c16 < 4 * g4 + ii ? ad[ii] : 0.f;
   }
-  // Y = P^T dO + Kdec dS_L^T  (rows i of block I, columns e)
-  f32x4 y[4];
+  // Y = P^T dO + Kdec dS_L^T  (rows i of block I, this wave's columns e)
+  f32x4 y[2];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) y[nt] = zero4();
+  for (int q = 0; q < 2; ++q) y[q] = zero4();
 #pragma unroll
   for (int J = 0; J < 4; ++J) {
     if (J < I) continue;
@@ -346,25 +349,26 @@ __global__ void __launch_bounds__(256) carve_bwd_chunk_kernel(BwdArgs a) {
     }
     const b4 pa = rnd(p);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) y[nt] = MB::mma(pa, ldBc(dO, 16 * J, 16 * nt), y[nt]);
+    for (int q = 0; q < 2; ++q) y[q] = MB::mma(pa, ldBc(dO, 16 * J, 16 * (2 * hc + q)), y[q]);
   }
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
+  for (int q = 0; q < 2; ++q)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      y[nt] = MB::mma(ldAs(Kr, r0, 16 * ks, Dec + I * D, 1.f), ldA(dSm, 16 * nt, 16 * ks), y[nt]);
+      y[q] = MB::mma(ldAs(Kr, r0, 16 * ks, Dec + I * D, 1.f), ldA(dSm, 16 * (2 * hc + q), 16 * ks), y[q]);
   // R = W V - Kb S^T
-  f32x4 R[4];
+  f32x4 R[2];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
+  for (int q = 0; q < 2; ++q) {
+    const int nt = 2 * hc + q;
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) R[nt][ii] = to_f32(WV[(r0 + 4 * g4 + ii) * LD + 16 * nt + c16]);
+    for (int ii = 0; ii < 4; ++ii) R[q][ii] = to_f32(WV[(r0 + 4 * g4 + ii) * LD + 16 * nt + c16]);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      R[nt] = MB::mma(ldAs(BKl, r0, 16 * ks, Eg + I * D, -1.f), ldA(Sm, 16 * nt, 16 * ks), R[nt]);
+      R[q] = MB::mma(ldAs(BKl, r0, 16 * ks, Eg + I * D, -1.f), ldA(Sm, 16 * nt, 16 * ks), R[q]);
   }
   lds_barrier();
-  {
+  if (hc == 0) {
     // Td_I = (I + A_II)^{-1}: lane c16 walks column c16 down the rows
     const float* A_ = Ad + I * 256;
     float t[16];
@@ -382,34 +386,34 @@ __global__ void __launch_bounds__(256) carve_bwd_chunk_kernel(BwdArgs a) {
   lds_barrier();
 
   // ------------------------------------------ Delta = (I + A)^{-1} R, by blocks
-  f32x4 acc[4];
+  f32x4 acc[2];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) acc[nt] = zero4();
+  for (int q = 0; q < 2; ++q) acc[q] = zero4();
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     if (I == rr) {
       const f32x4 ta = *reinterpret_cast<const f32x4*>(Td + rr * 256 + c16 * 16 + 4 * g4);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const f32x4 dl = MF::mma(ta, R[nt] - acc[nt], zero4());
+      for (int q = 0; q < 2; ++q) {
+        const f32x4 dl = MF::mma(ta, R[q] - acc[q], zero4());
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) Del[(16 * rr + 4 * g4 + ii) * LD + 16 * nt + c16] = (bf16)dl[ii];
+        for (int ii = 0; ii < 4; ++ii) Del[(16 * rr + 4 * g4 + ii) * LD + 16 * (2 * hc + q) + c16] = (bf16)dl[ii];
       }
     }
     lds_barrier();
     if (I > rr) {
       const b4 af = rnd(aF[rr]);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[nt] = MB::mma(af, ldBc(Del, 16 * rr, 16 * nt), acc[nt]);
+      for (int q = 0; q < 2; ++q) acc[q] = MB::mma(af, ldBc(Del, 16 * rr, 16 * (2 * hc + q)), acc[q]);
     }
   }
 
   // ------------------------------------------ dU = (I + A)^{-T} Y, by blocks
-  f32x4 du[4];
+  f32x4 du[2];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    acc[nt] = zero4();
-    du[nt] = zero4();
+  for (int q = 0; q < 2; ++q) {
+    acc[q] = zero4();
+    du[q] = zero4();
   }
 #pragma unroll
   for (int rr = 3; rr >= 0; --rr) {
@@ -417,24 +421,24 @@ __global__ void __launch_bounds__(256) carve_bwd_chunk_kernel(BwdArgs a) {
       const float* tdb = Td + rr * 256 + 4 * g4 * 16 + c16;
       const f32x4 ta = {tdb[0], tdb[16], tdb[32], tdb[48]};     // (Td^T)[c16][4 g4 + p]
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        du[nt] = MF::mma(ta, y[nt] - acc[nt], zero4());
+      for (int q = 0; q < 2; ++q) {
+        du[q] = MF::mma(ta, y[q] - acc[q], zero4());
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) dU[(16 * rr + 4 * g4 + ii) * LD + 16 * nt + c16] = (bf16)du[nt][ii];
+        for (int ii = 0; ii < 4; ++ii) dU[(16 * rr + 4 * g4 + ii) * LD + 16 * (2 * hc + q) + c16] = (bf16)du[q][ii];
       }
     }
     lds_barrier();
     if (I < rr) {
       const b4 ab = rnd(aB[rr]);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[nt] = MB::mma(ab, ldBc(dU, 16 * rr, 16 * nt), acc[nt]);
+      for (int q = 0; q < 2; ++q) acc[q] = MB::mma(ab, ldBc(dU, 16 * rr, 16 * (2 * hc + q)), acc[q]);
     }
   }
 
   // ------------------------------------------------------------ token sums
   // raw inputs of the lane's output elements (rows 16 I + 4 g4 + ii,
   // columns 16 nt + c16), loaded now so they land during the products
-  bf16 pq[4][4], pk[4][4], pbx[4][4], pv[4][4];
+  bf16 pq[2][4], pk[2][4], pbx[2][4], pv[2][4];
   float pw[4];
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii) {
@@ -443,38 +447,40 @@ __global__ void __launch_bounds__(256) carve_bwd_chunk_kernel(BwdArgs a) {
     const size_t ro = tok(t0 + min(i, n - 1)) * D;
     pw[ii] = ok ? to_f32(W[tok(t0 + min(i, n - 1))]) : 0.f;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const size_t o = ro + 16 * nt + c16;
-      pq[nt][ii] = ok ? Q[o] : (bf16)0.f;
-      pk[nt][ii] = ok ? K[o] : (bf16)0.f;
-      pbx[nt][ii] = ok ? BX[o] : (bf16)0.f;
-      pv[nt][ii] = ok ? V[o] : (bf16)0.f;
+    for (int q = 0; q < 2; ++q) {
+      const size_t o = ro + 16 * (2 * hc + q) + c16;
+      pq[q][ii] = ok ? Q[o] : (bf16)0.f;
+      pk[q][ii] = ok ? K[o] : (bf16)0.f;
+      pbx[q][ii] = ok ? BX[o] : (bf16)0.f;
+      pv[q][ii] = ok ? V[o] : (bf16)0.f;
     }
   }
   // qa, xa: sums over j < i (left factor applied at the end); ka: sums over
   // j > i; qx, xx, kx: exact diagonal terms of steep sub-blocks
-  f32x4 qa[4], xa[4], ka[4], qx[4], xx[4], kx[4];
+  f32x4 qa[2], xa[2], ka[2], qx[2], xx[2], kx[2];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) qa[nt] = xa[nt] = ka[nt] = qx[nt] = xx[nt] = kx[nt] = zero4();
+  for (int q = 0; q < 2; ++q) qa[q] = xa[q] = ka[q] = qx[q] = xx[q] = kx[q] = zero4();
 #pragma unroll
   for (int J = 0; J < 4; ++J) {
     if (J < I) {
       const b4 zt = rnd(gram(Del, 16 * J, dO, r0));              // C[j][i] = Z[i][j]
       const b4 nt_ = rnd(gram(Del, 16 * J, dU, r0));             // C[j][i] = N[i][j]
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int q = 0; q < 2; ++q) {
+        const int nt = 2 * hc + q;
         const b4 kb = ldBc(Kr, 16 * J, 16 * nt);
         const float m = Mid[(I * 4 + J) * D + 16 * nt + c16];
-        qa[nt] += m * MB::mma(zt, kb, zero4());
-        xa[nt] += m * MB::mma(nt_, kb, zero4());
+        qa[q] += m * MB::mma(zt, kb, zero4());
+        xa[q] += m * MB::mma(nt_, kb, zero4());
       }
     } else if (J > I) {
       const b4 z = rnd(gram(dO, 16 * J, Del, r0));               // C[j][i] = Z[j][i]
       const b4 nn = rnd(-gram(dU, 16 * J, Del, r0));             // C[j][i] = -N[j][i]
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int q = 0; q < 2; ++q) {
+        const int nt = 2 * hc + q;
         const float m = Mid[(J * 4 + I) * D + 16 * nt + c16];
-        ka[nt] += m * MB::mma(z, ldBc(Ql, 16 * J, 16 * nt), MB::mma(nn, ldBc(BKl, 16 * J, 16 * nt), zero4()));
+        ka[q] += m * MB::mma(z, ldBc(Ql, 16 * J, 16 * nt), MB::mma(nn, ldBc(BKl, 16 * J, 16 * nt), zero4()));
       }
     } else {
       f32x4 zt = gram(Del, r0, dO, r0), nt_ = gram(Del, r0, dU, r0);
@@ -488,30 +494,32 @@ __global__ void __launch_bounds__(256) carve_bwd_chunk_kernel(BwdArgs a) {
       if (!steep) {
         const b4 zb = rnd(zt), nb = rnd(nt_), z2 = rnd(z), n2 = rnd(-nn);
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
+        for (int q = 0; q < 2; ++q) {
+          const int nt = 2 * hc + q;
           const b4 kb = ldBc(Kr, r0, 16 * nt);
           const float m = Mid[I * 5 * D + 16 * nt + c16];
-          qa[nt] += m * MB::mma(zb, kb, zero4());
-          xa[nt] += m * MB::mma(nb, kb, zero4());
-          ka[nt] += m * MB::mma(z2, ldBc(Ql, r0, 16 * nt), MB::mma(n2, ldBc(BKl, r0, 16 * nt), zero4()));
+          qa[q] += m * MB::mma(zb, kb, zero4());
+          xa[q] += m * MB::mma(nb, kb, zero4());
+          ka[q] += m * MB::mma(z2, ldBc(Ql, r0, 16 * nt), MB::mma(n2, ldBc(BKl, r0, 16 * nt), zero4()));
         }
       } else {
-        // the four diagonal tiles to LDS, then each output element's terms pairwise
-        float* sc = Scr + I * 1024;
+        // the four diagonal tiles (bf16, as the factorised path rounds them)
+        // to this wave's scratch, then each output element's terms pairwise
+        bf16* sc = Scr + w * 1024;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int o = (4 * g4 + ii) * 16 + c16;
-          sc[o] = zt[ii];
-          sc[256 + o] = nt_[ii];
-          sc[512 + o] = z[ii];
-          sc[768 + o] = nn[ii];
+          sc[o] = (bf16)zt[ii];
+          sc[256 + o] = (bf16)nt_[ii];
+          sc[512 + o] = (bf16)z[ii];
+          sc[768 + o] = (bf16)nn[ii];
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const int cc = 16 * nt + c16;
+        for (int q = 0; q < 2; ++q) {
+          const int cc = 16 * (2 * hc + q) + c16;
 #pragma unroll
           for (int ii = 0; ii < 4; ++ii) {
             const int il = 4 * g4 + ii, i = r0 + il;
@@ -521,16 +529,16 @@ __global__ void __launch_bounds__(256) carve_bwd_chunk_kernel(BwdArgs a) {
               const int j = r0 + jl;
               if (jl < il) {
                 const float kj = raw(K, j, cc), gj = Gf[j * GLD + cc];
-                sq += sc[jl * 16 + il] * kj * fast_exp2(gim - gj);
-                sx += sc[256 + jl * 16 + il] * kj * fast_exp2(gi - gj);
+                sq += to_f32(sc[jl * 16 + il]) * kj * fast_exp2(gim - gj);
+                sx += to_f32(sc[256 + jl * 16 + il]) * kj * fast_exp2(gi - gj);
               } else if (jl > il) {
-                sk += sc[512 + jl * 16 + il] * raw(Q, j, cc) * fast_exp2(gprev(j, cc) - gi) -
-                      sc[768 + jl * 16 + il] * raw_bk(j, cc) * fast_exp2(Gf[j * GLD + cc] - gi);
+                sk += to_f32(sc[512 + jl * 16 + il]) * raw(Q, j, cc) * fast_exp2(gprev(j, cc) - gi) -
+                      to_f32(sc[768 + jl * 16 + il]) * raw_bk(j, cc) * fast_exp2(Gf[j * GLD + cc] - gi);
               }
             }
-            qx[nt][ii] = sq;
-            xx[nt][ii] = sx;
-            kx[nt][ii] = sk;
+            qx[q][ii] = sq;
+            xx[q][ii] = sx;
+            kx[q][ii] = sk;
           }
         }
       }
@@ -544,10 +552,11 @@ __global__ void __launch_bounds__(256) carve_bwd_chunk_kernel(BwdArgs a) {
   bf16* dg_o = static_cast<bf16*>(a.dg);
   bf16* dbx_o = static_cast<bf16*>(a.dbx);
   bf16* dw_o = static_cast<bf16*>(a.dw);
-  f32x4 sfx[4];                                  // within-lane suffix of phi minus q dq
-  float tot[4], hlc[4], dwp[4] = {0.f, 0.f, 0.f, 0.f};
+  f32x4 sfx[2];                                  // within-lane suffix of phi minus q dq
+  float tot[2], hlc[2], dwp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
+  for (int q = 0; q < 2; ++q) {
+    const int nt = 2 * hc + q;
     f32x4 dOS = zero4(), dUS = zero4(), DdS = zero4();
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -564,17 +573,17 @@ __global__ void __launch_bounds__(256) carve_bwd_chunk_kernel(BwdArgs a) {
     for (int ii = 0; ii < 4; ++ii) {
       const int i = r0 + 4 * g4 + ii;
       const float gi = Gf[i * GLD + cc], gim = gprev(i, cc);
-      const float qv = to_f32(pq[nt][ii]), kv = to_f32(pk[nt][ii]), bv = sigmoid_f(to_f32(pbx[nt][ii]));
+      const float qv = to_f32(pq[q][ii]), kv = to_f32(pk[q][ii]), bv = sigmoid_f(to_f32(pbx[q][ii]));
       const float ed = fast_exp2(gl - gi);
-      const float dq = fast_exp2(gim - gs) * qa[nt][ii] + qx[nt][ii] + fast_exp2(gim) * dOS[ii];
-      const float xd = fast_exp2(gi - gs) * xa[nt][ii] + xx[nt][ii] + fast_exp2(gi) * dUS[ii];
-      const float dk = ed * DdS[ii] + fast_exp2(ge - gi) * ka[nt][ii] + kx[nt][ii] - bv * xd;
+      const float dq = fast_exp2(gim - gs) * qa[q][ii] + qx[q][ii] + fast_exp2(gim) * dOS[ii];
+      const float xd = fast_exp2(gi - gs) * xa[q][ii] + xx[q][ii] + fast_exp2(gi) * dUS[ii];
+      const float dk = ed * DdS[ii] + fast_exp2(ge - gi) * ka[q][ii] + kx[q][ii] - bv * xd;
       const float db = -kv * xd;
       phi[ii] = qv * dq - kv * dk + 2.f * bv * db;
       qdq[ii] = qv * dq;
       hl += kv * ed * DdS[ii];
-      const float dvv = pw[ii] * du[nt][ii];
-      dwp[ii] += to_f32(pv[nt][ii]) * du[nt][ii];
+      const float dvv = pw[ii] * du[q][ii];
+      dwp[ii] += to_f32(pv[q][ii]) * du[q][ii];
       if (i < n) {
         const size_t o = tok(t0 + i) * D + cc;
         dq_o[o] = (bf16)dq;
@@ -585,46 +594,51 @@ __global__ void __launch_bounds__(256) carve_bwd_chunk_kernel(BwdArgs a) {
     }
     // suffix sums of phi over the lane's rows, minus q dq
     const float s3 = phi[3], s2 = phi[2] + s3, s1 = phi[1] + s2, s0 = phi[0] + s1;
-    sfx[nt] = f32x4{s0 - qdq[0], s1 - qdq[1], s2 - qdq[2], s3 - qdq[3]};
-    tot[nt] = s0;
-    hlc[nt] = hl;
+    sfx[q] = f32x4{s0 - qdq[0], s1 - qdq[1], s2 - qdq[2], s3 - qdq[3]};
+    tot[q] = s0;
+    hlc[q] = hl;
   }
-  // dw: row sums over the 64 value columns
+  // dw: this wave's half of each row's sum over the 64 value columns
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii) {
-    const float s = sum_row16(dwp[ii]);
-    const int i = r0 + 4 * g4 + ii;
-    if (c16 == ii && i < n) dw_o[tok(t0 + i)] = (bf16)s;
+    const float sm = sum_row16(dwp[ii]);
+    if (c16 == ii) Dwp[w * 16 + 4 * g4 + ii] = sm;
   }
   // phi suffixes over the lane groups of the wave, and wave totals
-  float sg[4];
+  float sg[2];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const float t1 = __shfl(tot[nt], c16 + 16), t2 = __shfl(tot[nt], c16 + 32), t3 = __shfl(tot[nt], c16 + 48);
-    const float t0v = __shfl(tot[nt], c16);
-    sg[nt] = (g4 < 1 ? t1 : 0.f) + (g4 < 2 ? t2 : 0.f) + (g4 < 3 ? t3 : 0.f);
-    const float hw = sum_groups(hlc[nt]);
+  for (int q = 0; q < 2; ++q) {
+    const int nt = 2 * hc + q;
+    const float t1 = __shfl(tot[q], c16 + 16), t2 = __shfl(tot[q], c16 + 32), t3 = __shfl(tot[q], c16 + 48);
+    const float t0v = __shfl(tot[q], c16);
+    sg[q] = (g4 < 1 ? t1 : 0.f) + (g4 < 2 ? t2 : 0.f) + (g4 < 3 ? t3 : 0.f);
+    const float hw = sum_groups(hlc[q]);
     if (g4 == 0) {
-      Red[4 * D + I * D + 16 * nt + c16] = t0v + t1 + t2 + t3;
-      Red[8 * D + I * D + 16 * nt + c16] = hw;
+      Red[(8 + I) * D + 16 * nt + c16] = t0v + t1 + t2 + t3;
+      Red[(12 + I) * D + 16 * nt + c16] = hw;
     }
   }
   lds_barrier();
+  if (hc == 0 && lane < 16) {
+    const int i = r0 + lane;
+    if (i < n) dw_o[tok(t0 + i)] = (bf16)(Dwp[w * 16 + lane] + Dwp[(w + 1) * 16 + lane]);
+  }
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int cc = 16 * nt + c16;
+  for (int q = 0; q < 2; ++q) {
+    const int cc = 16 * (2 * hc + q) + c16;
     float hsum = 0.f, hl = 0.f, sw = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      hsum += Red[w * D + cc];
-      hl += Red[8 * D + w * D + cc];
-      if (w > I) sw += Red[4 * D + w * D + cc];
+    for (int s8 = 0; s8 < 8; ++s8) hsum += Red[s8 * D + cc];
+#pragma unroll
+    for (int w4 = 0; w4 < 4; ++w4) {
+      hl += Red[(12 + w4) * D + cc];
+      if (w4 > I) sw += Red[(8 + w4) * D + cc];
     }
     const float HL = fast_exp2(Ge[3 * D + cc]) * hsum + hl;
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int i = r0 + 4 * g4 + ii;
-      if (i < n) dg_o[tok(t0 + i) * D + cc] = (bf16)(HL + sw + sg[nt] + sfx[nt][ii]);
+      if (i < n) dg_o[tok(t0 + i) * D + cc] = (bf16)(HL + sw + sg[q] + sfx[q][ii]);
     }
   }
 
@@ -634,7 +648,8 @@ __global__ void __launch_bounds__(256) carve_bwd_chunk_kernel(BwdArgs a) {
   if (ch == 0 && a.d_state_in) {
     // rows e = 16 I + 4 g4 + ii, columns c = 16 nt + c16
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int q = 0; q < 2; ++q) {
+      const int nt = 2 * hc + q;
       f32x4 s1 = zero4(), s2 = zero4();
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
