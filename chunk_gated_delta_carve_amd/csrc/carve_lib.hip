@@ -78,11 +78,10 @@ int64_t parallel_workspace_bytes(const carve_config* c) {
 bool bwd_from_forward(const carve_config* c) { return chunk_parallel(c) && c->L % kParallelBlock == 0; }
 
 // The chunk-parallel backward (one workgroup per (batch, head, chunk), dense
-// products on the matrix cores) covers d = 64 with 64-token chunks and the
-// decay and keys as given; every other shape walks the tokens.
+// products on the matrix cores) covers d = 64 with 64-token chunks and keys
+// as given (not normalised in the kernel); every other shape walks the tokens.
 bool bwd_chunked(const carve_config* c) {
-  return bwd_from_forward(c) && c->L == kParallelBlock && c->dk == 64 && c->T > 0 &&
-         !(c->flags & (CARVE_DECAY_LOGITS | CARVE_QK_L2NORM));
+  return bwd_from_forward(c) && c->L == kParallelBlock && c->dk == 64 && c->T > 0 && !(c->flags & CARVE_QK_L2NORM);
 }
 
 struct BwdBytes {
@@ -235,12 +234,13 @@ hipError_t launch_row_lane(const carve::BwdArgs& a, hipStream_t s) {
 // checkpointing state pass walks that chain from the last chunk and stores
 // the state gradient at every chunk end, then one workgroup per (batch,
 // head, chunk) forms the gradients.
+template <bool LG>
 hipError_t launch_chunked(const carve::BwdArgs& a, unsigned char* imgs, void* o_scratch, hipStream_t s) {
   using CL = carve::ChunkBwdLayout<64>;
   using LY = carve::BlockLayout<carve::bf16, 64, 64, kParallelBlock>;
   constexpr auto image = carve::carve_bwd_image_kernel<64>;
   constexpr auto chain = carve::carve_state_kernel<carve::bf16, 64, 64, kParallelBlock, true>;
-  constexpr auto chunk = carve::carve_bwd_chunk_kernel<64>;
+  constexpr auto chunk = carve::carve_bwd_chunk_kernel<64, LG>;
   hipError_t e = set_lds<chunk>(CL::bytes);
   if (e != hipSuccess) return e;
   const int64_t nc = (a.T + kParallelBlock - 1) / kParallelBlock, BH = (int64_t)a.B * a.H;
@@ -573,7 +573,7 @@ extern "C" int carve_chunk_bwd(const carve_config* cfg,
   if (e == hipSuccess && a.pre_ckpt == 2) {
     const BwdBytes bb = bwd_bytes(cfg);
     unsigned char* wsb = static_cast<unsigned char*>(workspace);
-    e = launch_chunked(a, wsb + bb.img, wsb + bb.o, s);
+    e = lg ? launch_chunked<true>(a, wsb + bb.img, wsb + bb.o, s) : launch_chunked<false>(a, wsb + bb.img, wsb + bb.o, s);
   }
   else if (e == hipSuccess)
     e = cfg->dtype == CARVE_BF16

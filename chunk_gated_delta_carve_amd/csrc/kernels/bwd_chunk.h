@@ -78,7 +78,9 @@ struct ChunkBwdLayout {
   static constexpr int bytes = oFlag + 16;
 };
 
-template <int D>
+// kLogits: g holds raw decay logits a (g = -softplus(a)); dg is then the
+// gradient of a, dg_g (-sigmoid(a)).
+template <int D, bool kLogits>
 __global__ void __launch_bounds__(512) carve_bwd_chunk_kernel(BwdArgs a) {
   using LY = ChunkBwdLayout<D>;
   constexpr int L = LY::L, LD = LY::LD, GLD = LY::GLD, NT = LY::NT;
@@ -171,7 +173,7 @@ __global__ void __launch_bounds__(512) carve_bwd_chunk_kernel(BwdArgs a) {
       pwv[i] = (bf16)(wr * to_f32(xv[i]));
       const float dml = lastc && rv ? wsb[lay.dmo + cs + i] : 0.f;
       pdo[i] = (bf16)(to_f32(xdo[i]) + dml);
-      gg[i >> 2][i & 3] = to_f32(xg[i]) * kLog2e;
+      gg[i >> 2][i & 3] = rv ? decay_log2<kLogits>(to_f32(xg[i])) : 0.f;   // padding rows do not decay
     }
     *reinterpret_cast<bf16x8*>(WV + r * LD + cs) = pwv;
     *reinterpret_cast<bf16x8*>(dO + r * LD + cs) = pdo;
@@ -438,7 +440,7 @@ __global__ void __launch_bounds__(512) carve_bwd_chunk_kernel(BwdArgs a) {
   // ------------------------------------------------------------ token sums
   // raw inputs of the lane's output elements (rows 16 I + 4 g4 + ii,
   // columns 16 nt + c16), loaded now so they land during the products
-  bf16 pq[2][4], pk[2][4], pbx[2][4], pv[2][4];
+  bf16 pq[2][4], pk[2][4], pbx[2][4], pv[2][4], pg[2][4];
   float pw[4];
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii) {
@@ -453,6 +455,7 @@ __global__ void __launch_bounds__(512) carve_bwd_chunk_kernel(BwdArgs a) {
       pk[q][ii] = ok ? K[o] : (bf16)0.f;
       pbx[q][ii] = ok ? BX[o] : (bf16)0.f;
       pv[q][ii] = ok ? V[o] : (bf16)0.f;
+      pg[q][ii] = kLogits && ok ? Gin[o] : (bf16)0.f;
     }
   }
   // qa, xa: sums over j < i (left factor applied at the end); ka: sums over
@@ -638,7 +641,9 @@ __global__ void __launch_bounds__(512) carve_bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int i = r0 + 4 * g4 + ii;
-      if (i < n) dg_o[tok(t0 + i) * D + cc] = (bf16)(HL + sw + sg[q] + sfx[q][ii]);
+      float dgv = HL + sw + sg[q] + sfx[q][ii];
+      if (kLogits) dgv *= -sigmoid_f(to_f32(pg[q][ii]));
+      if (i < n) dg_o[tok(t0 + i) * D + cc] = (bf16)dgv;
     }
   }
 

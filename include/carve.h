@@ -196,7 +196,7 @@ int carve_chunk_fwd_noalloc(const carve_config* cfg,
  *               row-lane schedules keep the state at every 8-token sub-block
  *               start rather than at every token; 4 L dk dv at dk = 128 with
  *               a projection). In bf16 with rank == 0, dk = 64, L = 64 and
- *               neither CARVE_DECAY_LOGITS nor CARVE_QK_L2NORM, every chunk
+ *               without CARVE_QK_L2NORM, every chunk
  *               is differentiated at once from its start state and its
  *               end-of-chunk state gradient (dense products per chunk); the
  *               workspace then holds only those two per chunk and a row share
