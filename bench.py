@@ -374,7 +374,9 @@ def write_trace_summary(wl, stats_csv, bench_log, commands, backward=False):
             f.write(f"    {c}\n")
         if backward:
             f.write("\nPer-kernel statistics of the profiled run (`run_kernel_stats.csv`). Every call of "
-                    "carve_chunk_bwd launches its kernels once (warm-up and timed calls):\n\n")
+                    "carve_chunk_bwd launches each of its kernels once, the state pass twice when it both "
+                    "forms the chunk-start states and runs the state-gradient chain (warm-up and timed "
+                    "calls):\n\n")
         else:
             f.write("\nPer-kernel statistics of the profiled run (`run_kernel_stats.csv`). Every call of "
                     "carve_chunk_fwd launches its kernels once; bench.py makes warm-up, back-to-back, "
@@ -386,8 +388,14 @@ def write_trace_summary(wl, stats_csv, bench_log, commands, backward=False):
             f.write(f"| `{n}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                     f"{float(r['MaxNs']) / 1e3:.2f} | {100 * float(r['TotalDurationNs']) / total:.1f}% |\n")
         carve = [(r, n) for r, n in zip(rows, names) if "carve_" in r["Name"]]
-        f.write(f"\n- sum of the CARVE kernels' averages per call: "
-                f"{sum(float(r['AverageNs']) for r, _ in carve) / 1e3:.2f} us\n")
+        if backward and carve:
+            # calls of carve_chunk_bwd: the fewest launches of any of its kernels
+            ncall = min(int(r["Calls"]) for r, _ in carve)
+            f.write(f"\n- CARVE kernel time per carve_chunk_bwd call ({ncall} calls): "
+                    f"{sum(float(r['TotalDurationNs']) for r, _ in carve) / ncall / 1e3:.2f} us\n")
+        else:
+            f.write(f"\n- sum of the CARVE kernels' averages per call: "
+                    f"{sum(float(r['AverageNs']) for r, _ in carve) / 1e3:.2f} us\n")
         if line:
             rf = line["roofline"]
             timing = rf.get("timing", "HIP events around the timed calls").split(",")[0]
@@ -455,7 +463,8 @@ def backward_kernels(wl, rank):
         pre = ("carve_intra_kernel + carve_state_kernel (chunk-start states) + "
                if wl.dtype == "bf16" and wl.L % 64 == 0 else "")
         if pre and wl.L == 64 and wl.dk == 64:
-            return pre + "carve_bwd_split_kernel (dS sweep) + carve_bwd_chunk_kernel (one call)"
+            return (pre + "carve_bwd_image_kernel + carve_state_kernel (state-gradient chain) + "
+                    "carve_bwd_chunk_kernel (one call)")
         return pre + "carve_bwd_split_kernel + carve_bwd_finish_kernel (one call)"
     if wl.dk == 64:
         return "carve_bwd_split_kernel + carve_bwd_finish_kernel + carve_bwd_ub_kernel (one call)"
