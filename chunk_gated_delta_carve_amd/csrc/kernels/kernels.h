@@ -338,7 +338,9 @@ carve_state_kernel(FwdArgs a) {
   using e8 = typename B::e8;
   constexpr int NB = LY::NB, TD = LY::TD, NU = LY::NU, NW = LY::NW, NF = DK / Mma<E>::KS;
   constexpr int K = kOutWaves;
-  constexpr int NSC = DK == 64 ? 8 : 2;                // register sets of the chain wave
+  // register sets of the chain wave (six with the checkpoint stores: eight
+  // spilled there, 636 bytes per lane)
+  constexpr int NSC = DK == 64 ? (kCkpt ? 6 : 8) : 2;
   constexpr int NSO = DK == 64 ? 4 : 2;                // register sets of an output wave
   constexpr int R = 8;                                 // ring slots
   __shared__ Frag ring[R][NF][64];
