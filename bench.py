@@ -459,12 +459,12 @@ def backward_cpu_baseline(wl, inp, do, budget_s):
 
 def backward_kernels(wl, rank):
     """The kernels one carve_chunk_bwd call launches on this workload."""
+    if rank == 0 and wl.dtype == "bf16" and wl.dk == 64:
+        return ("carve_intra_kernel + carve_state_kernel (64-token block start states) + carve_bwd_image_kernel + "
+                "carve_state_kernel (state-gradient chain) + carve_bwd_chunk_kernel (one call)")
     if rank == 0:
         pre = ("carve_intra_kernel + carve_state_kernel (chunk-start states) + "
                if wl.dtype == "bf16" and wl.L % 64 == 0 else "")
-        if pre and wl.L == 64 and wl.dk == 64:
-            return (pre + "carve_bwd_image_kernel + carve_state_kernel (state-gradient chain) + "
-                    "carve_bwd_chunk_kernel (one call)")
         return pre + "carve_bwd_split_kernel + carve_bwd_finish_kernel (one call)"
     if wl.dk == 64:
         return "carve_bwd_split_kernel + carve_bwd_finish_kernel + carve_bwd_ub_kernel (one call)"

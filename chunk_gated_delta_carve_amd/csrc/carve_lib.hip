@@ -77,11 +77,12 @@ int64_t parallel_workspace_bytes(const carve_config* c) {
 // backward's own workspace.
 bool bwd_from_forward(const carve_config* c) { return chunk_parallel(c) && c->L % kParallelBlock == 0; }
 
-// The chunk-parallel backward (one workgroup per (batch, head, chunk), dense
-// products on the matrix cores) covers d = 64 with 64-token chunks and keys
-// as given (not normalised in the kernel); every other shape walks the tokens.
+// The chunk-parallel backward (one workgroup per (batch, head, 64-token
+// block), dense products on the matrix cores) covers bf16 without a
+// projection at d = 64, any L, with keys as given (not normalised in the
+// kernel); every other shape walks the tokens.
 bool bwd_chunked(const carve_config* c) {
-  return bwd_from_forward(c) && c->L == kParallelBlock && c->dk == 64 && c->T > 0 && !(c->flags & CARVE_QK_L2NORM);
+  return chunk_parallel(c) && c->dk == 64 && c->T > 0 && !(c->flags & CARVE_QK_L2NORM);
 }
 
 struct BwdBytes {
@@ -91,7 +92,7 @@ BwdBytes bwd_bytes(const carve_config* c) {
   const int64_t B = c->B, H = c->H, T = c->T;
   const int64_t own = B * H * 4 * (int64_t)carve::BwdWs(c->dk, c->T, c->L, c->rank, (c->flags & CARVE_QK_L2NORM) != 0,
                                                        bwd_from_forward(c) && c->T > 0, bwd_chunked(c)).total;
-  if (!bwd_from_forward(c)) return {0, 0, own};
+  if (!bwd_from_forward(c) && !bwd_chunked(c)) return {0, 0, own};
   const int64_t img = (own + 255) & ~(int64_t)255;
   const int64_t o = img + parallel_workspace_bytes(c);
   return {img, o, o + B * T * H * c->dv * (int64_t)sizeof(carve::bf16)};
@@ -567,7 +568,7 @@ extern "C" int carve_chunk_bwd(const carve_config* cfg,
     f.B = cfg->B; f.H = cfg->H; f.T = cfg->T; f.L = cfg->L; f.rank = 0;
     f.ckpt = static_cast<float*>(workspace);
     f.ckpt_bh = carve::BwdWs(cfg->dk, cfg->T, cfg->L, 0, a.norm != 0, true, a.pre_ckpt == 2).total;
-    f.ckpt_shift = cfg->L == 2 * kParallelBlock ? 1 : 0;
+    f.ckpt_shift = a.pre_ckpt != 2 && cfg->L == 2 * kParallelBlock ? 1 : 0;
     e = dispatch_fwd_ckpt_flags(cfg, f, s);
   }
   if (e == hipSuccess && a.pre_ckpt == 2) {

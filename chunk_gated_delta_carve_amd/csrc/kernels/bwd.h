@@ -93,19 +93,20 @@ __host__ __device__ constexpr int bwd_slices(int D, int rank) { return rank == 0
 // kernel takes through the normalisation.
 //
 // The chunk-parallel schedule (carve_bwd_chunk_kernel, `chunked`) keeps only
-// the chunk-start states, the state gradient at every chunk end and each
-// row's share of d_mean_out over the last chunk's tokens.
+// the state at every 64-token block start, the state gradient at every block
+// end and each row's share of d_mean_out over the last chunk's tokens.
 struct BwdWs {
   size_t ckpt, sbuf, sbuf_group, dsck, dmo, z, m, y, dud, duu, part, wpart, nrm, dqh, dkh, total;
   int groups;
   __host__ __device__ BwdWs(int D, int T, int L, int rank, bool norm, bool pre_ckpt, bool chunked = false) {
     const size_t nc = (size_t)(T + L - 1) / L, DD = (size_t)D * D;
-    if (chunked) {
+    if (chunked) {                                     // per 64-token block, whatever L is
+      const size_t nb = (size_t)(T + 63) / 64;
       groups = 1;
       ckpt = 0;
       sbuf = sbuf_group = 0;
-      dsck = nc * DD;
-      dmo = 2 * nc * DD;
+      dsck = nb * DD;
+      dmo = 2 * nb * DD;
       z = m = y = dud = duu = part = wpart = nrm = dqh = dkh = dmo + D;
       total = (dmo + D + 3) & ~(size_t)3;
       return;

@@ -1,8 +1,11 @@
 // Chunk-parallel backward pass without a content projection (bf16 inputs,
-// d_k = d_v = 64, 64-token chunks): one workgroup per (batch, head, chunk)
-// forms every gradient of the chunk's tokens at once, from the state S at the
-// chunk start (written by the forward pair), the state gradient dS_L at the
-// chunk end and the chunk's inputs, as 16x16 products on the matrix cores.
+// d_k = d_v = 64). Without a projection the chunk length L only decides which
+// tokens d_mean_out reaches, so the work is cut into 64-token blocks whatever
+// L is; "chunk" below means such a block. One workgroup per (batch, head,
+// chunk) forms every gradient of the chunk's tokens at once, from the state S
+// at the chunk start (written by the forward pair), the state gradient dS_L
+// at the chunk end and the chunk's inputs, as 16x16 products on the matrix
+// cores.
 // The state gradients come from a chain over chunks run by the forward's own
 // state pass (carve_state_kernel with checkpoints) on images that
 // carve_bwd_image_kernel derives from the forward pair's: the adjoint of
@@ -163,9 +166,9 @@ __global__ void __launch_bounds__(512) carve_bwd_chunk_kernel(BwdArgs a) {
       sv[j] = Sg[(size_t)(8 * s + j) * D + cc];
       dv[j] = dSg[(size_t)(8 * s + j) * D + cc];
     }
-    // the last chunk's outputs also carry d_mean_out / n (carve_bwd_image_kernel
-    // left each row's share in the workspace)
-    const bool lastc = ch == nc - 1;
+    // the outputs of the last L-token chunk also carry d_mean_out / n
+    // (carve_bwd_image_kernel left each row's share in the workspace)
+    const bool lastc = t0 + r >= (T - 1) / a.L * a.L;
     bf16x8 pwv, pdo;
     f32x4 gg[2];
 #pragma unroll
@@ -680,12 +683,12 @@ __global__ void __launch_bounds__(512) carve_bwd_chunk_kernel(BwdArgs a) {
 //   Mt slot: A operands of M (rows d, k = d'), i.e. the forward's M^T units
 //            transposed (gathered element by element through LDS);
 //   Ct slot: C tiles of F^T = (dO^T Q_eff)^T (rows d, columns e), per value
-//            slice and paired as the forward's C^T tiles, with the last
-//            chunk's dO carrying d_mean_out / n.
+//            slice and paired as the forward's C^T tiles, with the dO of the
+//            last L-token chunk's tokens carrying d_mean_out / n.
 // The Q_eff and O_loc slots keep the forward's contents (the state pass
 // forms an output from them into a scratch buffer, unused). The workgroup
-// that holds the last chunk also leaves each row's share of d_mean_out in the
-// workspace for carve_bwd_chunk_kernel.
+// that holds the last 64-token chunk also leaves each row's share of
+// d_mean_out in the workspace for carve_bwd_chunk_kernel.
 template <int D>
 __global__ void __launch_bounds__(256) carve_bwd_image_kernel(BwdArgs a, unsigned char* imgs) {
   using LY = BlockLayout<bf16, D, D, 64>;
@@ -705,7 +708,7 @@ __global__ void __launch_bounds__(256) carve_bwd_image_kernel(BwdArgs a, unsigne
   const BwdWs lay(D, T, 64, 0, false, true, true);
   float* wsb = a.ws + (size_t)bh * lay.total;
   const bf16* DOg = static_cast<const bf16*>(a.d_o);
-  const int tl0 = (nc - 1) * 64;
+  const int tl0 = (T - 1) / a.L * a.L;                           // first token of the last L-token chunk
   for (int x = 0; x < nch; ++x) {
     const int c = x ? cB : cA, t0 = 64 * c, n = min(64, T - t0);
     const uint4* src = reinterpret_cast<const uint4*>(base + (size_t)c * LY::wBytes);
@@ -717,7 +720,7 @@ __global__ void __launch_bounds__(256) carve_bwd_image_kernel(BwdArgs a, unsigne
       const size_t o = (((size_t)bi * T + t0 + r) * H + h) * D + cs;
       v[0] = *reinterpret_cast<const b8*>(DOg + o);
       v[1] = *reinterpret_cast<const b8*>(DOg + o + 8);
-      if (c == nc - 1 && a.d_mean_out) {
+      if (t0 + r >= tl0 && a.d_mean_out) {
         const float inv = 1.f / (float)(T - tl0);
 #pragma unroll
         for (int j = 0; j < 16; ++j)

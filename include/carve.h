@@ -195,13 +195,14 @@ int carve_chunk_fwd_noalloc(const carve_config* cfg,
  *               bytes per (batch, head) in place of 4 ceil(L / 8) dk dv (the
  *               row-lane schedules keep the state at every 8-token sub-block
  *               start rather than at every token; 4 L dk dv at dk = 128 with
- *               a projection). In bf16 with rank == 0, dk = 64, L = 64 and
- *               without CARVE_QK_L2NORM, every chunk
- *               is differentiated at once from its start state and its
- *               end-of-chunk state gradient (dense products per chunk); the
- *               workspace then holds only those two per chunk and a row share
- *               of d_mean_out, 4 (2 nc dk dv + dv) bytes per (batch, head),
- *               besides the forward pair's images and output
+ *               a projection). In bf16 with rank == 0, dk = 64 and without
+ *               CARVE_QK_L2NORM (any L), every 64-token block is
+ *               differentiated at once from its start state and its
+ *               end-of-block state gradient (dense products per block); the
+ *               workspace then holds only those two per block and a row share
+ *               of d_mean_out, 4 (2 nb dk dv + dv) bytes per (batch, head)
+ *               with nb = ceil(T / 64), besides the forward pair's images and
+ *               output
  * No output may overlap an input, another output or the workspace, except
  * for the two aliases above. Results are deterministic (no atomics).
  * Returns the status codes of carve_chunk_fwd. */

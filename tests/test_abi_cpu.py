@@ -209,7 +209,7 @@ def test_bwd_workspace_size():
     own0 = 6 * 4 * ((per_bh0 + 3) // 4 * 4)
     assert _lib.ref_shapes(cfg(rank=0, dtype=_lib.CARVE_F32)).bwd_workspace_bytes == own0
     per_bh32 = 4 * 64 * 64 + 4 * 64 * 64 + 4 * 2 * 64 + 100 * 4 * (4 * 64 + 1)   # L = 32: four chunks
-    assert _lib.ref_shapes(cfg(rank=0, L=32)).bwd_workspace_bytes == 6 * 4 * per_bh32
+    assert _lib.ref_shapes(cfg(rank=0, L=32, dtype=_lib.CARVE_F32)).bwd_workspace_bytes == 6 * 4 * per_bh32
     # in bf16 at d 64 with 64-token chunks the chunk-parallel schedule keeps
     # the state at every chunk start (written by the forward pair), the state
     # gradient at every chunk end and each row's share of d_mean_out; the
@@ -223,15 +223,21 @@ def test_bwd_workspace_size():
     own_long_ch = 6 * 4 * (2 * 40 * 64 * 64 + 64)
     assert long_ch.bwd_workspace_bytes == ((own_long_ch + 255) // 256 * 256 + long_ch.workspace_bytes
                                            + 2 * 2560 * 3 * 64 * 2)
-    # with 128-token chunks (a multiple of the pair's 64-token blocks) the
-    # row-lane walk runs in chunk groups: one chunk's sub-block start states
-    # per group and the state gradient at every chunk end; at most sixteen
-    # groups (20 chunks here)
-    long_pre = _lib.ref_shapes(cfg(rank=0, T=2560, L=128))
-    per_bh_long = 20 * 64 * 64 + 16 * 16 * 64 * 64 + 20 * 64 * 64 + 20 * 2 * 64 + 2560 * 4 * (4 * 64 + 1)
+    # the schedule works on 64-token blocks whatever L is (L only decides
+    # which tokens d_mean_out reaches)
+    for L in (16, 32, 128):
+        assert _lib.ref_shapes(cfg(rank=0, L=L)).bwd_workspace_bytes == sh0.bwd_workspace_bytes
+        assert _lib.ref_shapes(cfg(rank=0, T=2560, L=L)).bwd_workspace_bytes == long_ch.bwd_workspace_bytes
+    # at d = 128 with 128-token chunks (a multiple of the pair's 64-token
+    # blocks) the row-lane walk runs in chunk groups: one chunk's sub-block
+    # start states per group and the state gradient at every chunk end; at
+    # most sixteen groups (20 chunks here)
+    long_pre = _lib.ref_shapes(cfg(rank=0, T=2560, L=128, dk=128, dv=128))
+    DD = 128 * 128
+    per_bh_long = 20 * DD + 16 * 16 * DD + 20 * DD + 20 * 2 * 128 + 2560 * 8 * (4 * 128 + 1)
     own_long = 6 * 4 * ((per_bh_long + 3) // 4 * 4)
     assert long_pre.bwd_workspace_bytes == ((own_long + 255) // 256 * 256 + long_pre.workspace_bytes
-                                            + 2 * 2560 * 3 * 64 * 2)
+                                            + 2 * 2560 * 3 * 128 * 2)
     # d = 128 in bf16 keeps the grouped row-lane walk (two chunks, two groups)
     sh128_0 = _lib.ref_shapes(cfg(rank=0, dk=128, dv=128))
     per_bh128_0 = 2 * 128 * 128 + 2 * 8 * 128 * 128 + 2 * 128 * 128 + 2 * 2 * 128 + 100 * 8 * (4 * 128 + 1)

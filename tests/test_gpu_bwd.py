@@ -139,23 +139,28 @@ def test_backward_without_state_gradients(torch_cuda):
 
 
 CHUNK_CASES = [
-    # bf16, d 64, L 64, no projection: the chunk-parallel schedule (one
-    # workgroup per (batch, head, 64-token chunk) on the matrix cores)
-    ("one-short-chunk-40", 2, 2, 40, True),
-    ("whole-chunks-256", 1, 3, 256, True),
-    ("ragged-150", 2, 1, 150, True),
-    ("no-state-gradients-200", 2, 2, 200, False),
+    # bf16, d 64, no projection: the chunk-parallel schedule (one workgroup per
+    # (batch, head, 64-token block) on the matrix cores, whatever L is; L
+    # only decides which tokens d_mean_out reaches)
+    ("one-short-chunk-40", 2, 2, 40, 64, True),
+    ("whole-chunks-256", 1, 3, 256, 64, True),
+    ("ragged-150", 2, 1, 150, 64, True),
+    ("no-state-gradients-200", 2, 2, 200, 64, False),
+    ("L16-ragged-90", 1, 2, 90, 16, True),
+    ("L32-ragged-170", 2, 1, 170, 32, True),
+    ("L128-ragged-200", 1, 2, 200, 128, True),
+    ("L128-one-chunk-100", 2, 1, 100, 128, True),
 ]
 
 
-@pytest.mark.parametrize("name,B,H,T,with_state", CHUNK_CASES, ids=[c[0] for c in CHUNK_CASES])
-def test_backward_chunk_parallel(torch_cuda, name, B, H, T, with_state):
-    wl = workload("chunk-" + name, "bf16", B, H, T, 64, 64, 0, 6900 + T)
+@pytest.mark.parametrize("name,B,H,T,L,with_state", CHUNK_CASES, ids=[c[0] for c in CHUNK_CASES])
+def test_backward_chunk_parallel(torch_cuda, name, B, H, T, L, with_state):
+    wl = workload("chunk-" + name, "bf16", B, H, T, 64, L, 0, 6900 + T)
     say("case chunk", wl)
     inp = make_inputs(wl)
     do, dSo, dmo, S_in, m_in = cotangents(B, H, T, 64, "bf16", 6950 + T, with_state=with_state)
-    got = bwd_gpu(torch_cuda, inp, "bf16", 64, do, dSo, dmo, S_in, m_in)
-    assert_grads(got, bwd_oracle(inp, "bf16", 64, do, dSo, dmo, S_in, m_in), TOL["bf16"], "chunk " + name)
+    got = bwd_gpu(torch_cuda, inp, "bf16", L, do, dSo, dmo, S_in, m_in)
+    assert_grads(got, bwd_oracle(inp, "bf16", L, do, dSo, dmo, S_in, m_in), TOL["bf16"], "chunk " + name)
 
 
 def test_backward_chunk_parallel_steep_decay(torch_cuda):
