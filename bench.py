@@ -466,6 +466,9 @@ def backward_kernels(wl, rank):
         pre = ("carve_intra_kernel + carve_state_kernel (chunk-start states) + "
                if wl.dtype == "bf16" and wl.L % 64 == 0 else "")
         return pre + "carve_bwd_split_kernel + carve_bwd_finish_kernel (one call)"
+    if wl.dk == 64 and wl.dtype == "bf16" and wl.L == 64:
+        return ("carve_chunk_serial_kernel (chunk-start states, gate biases and means) + "
+                "carve_bwd_chunk_serial_kernel + carve_bwd_ub_kernel (one call)")
     if wl.dk == 64:
         return "carve_bwd_split_kernel + carve_bwd_finish_kernel + carve_bwd_ub_kernel (one call)"
     return "carve_bwd_kernel + carve_bwd_ub_kernel (one call)"

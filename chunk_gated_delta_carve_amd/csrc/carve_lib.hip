@@ -84,6 +84,13 @@ bool bwd_from_forward(const carve_config* c) { return chunk_parallel(c) && c->L 
 bool bwd_chunked(const carve_config* c) {
   return chunk_parallel(c) && c->dk == 64 && c->T > 0 && !(c->flags & CARVE_QK_L2NORM);
 }
+// With a projection in bf16 at d = 64 and 64-token chunks the chunks are
+// differentiated one after another by one workgroup per head with the same
+// dense per-chunk products, after a checkpointing chunk-serial forward.
+bool bwd_content_chunked(const carve_config* c) {
+  return c->rank > 0 && c->dtype == CARVE_BF16 && c->dk == 64 && c->L == kParallelBlock && c->T > 0 &&
+         !(c->flags & CARVE_QK_L2NORM);
+}
 
 struct BwdBytes {
   int64_t img, o, total;   // byte offsets of the forward's images and output, and the size
@@ -91,7 +98,12 @@ struct BwdBytes {
 BwdBytes bwd_bytes(const carve_config* c) {
   const int64_t B = c->B, H = c->H, T = c->T;
   const int64_t own = B * H * 4 * (int64_t)carve::BwdWs(c->dk, c->T, c->L, c->rank, (c->flags & CARVE_QK_L2NORM) != 0,
-                                                       bwd_from_forward(c) && c->T > 0, bwd_chunked(c)).total;
+                                                       bwd_from_forward(c) && c->T > 0,
+                                                       bwd_chunked(c) || bwd_content_chunked(c)).total;
+  if (bwd_content_chunked(c)) {                      // the forward's output goes to a scratch buffer
+    const int64_t o = (own + 255) & ~(int64_t)255;
+    return {o, o, o + B * T * H * c->dv * (int64_t)sizeof(carve::bf16)};
+  }
   if (!bwd_from_forward(c) && !bwd_chunked(c)) return {0, 0, own};
   const int64_t img = (own + 255) & ~(int64_t)255;
   const int64_t o = img + parallel_workspace_bytes(c);
@@ -268,7 +280,7 @@ hipError_t launch_chunked(const carve::BwdArgs& a, unsigned char* imgs, void* o_
 template <int D>
 hipError_t launch_ub_sum(const carve::BwdArgs& a, hipStream_t s) {
   if (a.H == 0) return hipSuccess;
-  const carve::BwdWs lay(D, a.T, a.L, a.rank, a.norm != 0, a.pre_ckpt != 0);
+  const carve::BwdWs lay(D, a.T, a.L, a.rank, a.norm != 0, a.pre_ckpt != 0, a.pre_ckpt == 3);
   const size_t n = 2 * (size_t)a.rank * D * a.H;
   hipLaunchKernelGGL(carve::carve_bwd_ub_kernel<D>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                      a.ws, lay.total, lay.dud, a.B, a.H, a.rank, a.d_ub_down, a.d_ub_up);
@@ -320,6 +332,34 @@ hipError_t launch_bwd(const carve::BwdArgs& a, hipStream_t s) {
 template <typename E, bool LG>
 hipError_t dispatch_bwd_width(const carve_config* cfg, const carve::BwdArgs& a, hipStream_t s) {
   return cfg->dk == 64 ? launch_bwd<E, 64, LG>(a, s) : launch_bwd<E, 128, LG>(a, s);
+}
+
+// Content schedule at d = 64 (after the checkpointing chunk-serial forward):
+// the per-head chunk walk, then the factor gradients summed over the batch.
+template <bool LG>
+hipError_t launch_content_chunked(const carve::BwdArgs& a, hipStream_t s) {
+  using CL = carve::ChunkBwdLayout<64>;
+  constexpr auto kern = carve::carve_bwd_chunk_serial_kernel<64, LG>;
+  hipError_t e = set_lds<kern>(CL::bytes);
+  if (e != hipSuccess) return e;
+  if ((int64_t)a.B * a.H > 0) {
+    hipLaunchKernelGGL(kern, dim3(a.B * a.H), dim3(CL::NT), CL::bytes, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_ub_sum<64>(a, s);
+}
+
+// the checkpointing chunk-serial forward of the content schedule
+template <bool LG>
+hipError_t launch_serial_ckpt(const carve::FwdArgs& a, hipStream_t s) {
+  using E = carve::bf16;
+  using LY = carve::BlockLayout<E, 64, 64, kParallelBlock, carve::serial_waves<64, kParallelBlock>()>;
+  constexpr auto kern = carve::carve_chunk_serial_kernel<E, 64, 64, kParallelBlock, LG, false, true>;
+  hipError_t e = set_lds<kern>(LY::serial_bytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(a.B * a.H), dim3(LY::NT), LY::serial_bytes, s, a);
+  return hipGetLastError();
 }
 
 template <typename E, int D>
@@ -550,11 +590,30 @@ extern "C" int carve_chunk_bwd(const carve_config* cfg,
   a.B = cfg->B; a.H = cfg->H; a.T = cfg->T; a.L = cfg->L; a.rank = cfg->rank;
   a.norm = (cfg->flags & CARVE_QK_L2NORM) != 0;
   a.detach = (cfg->flags & CARVE_DETACH_MEAN) != 0;
-  a.pre_ckpt = bwd_chunked(cfg) ? 2 : bwd_from_forward(cfg) && cfg->T > 0;
+  a.pre_ckpt = bwd_content_chunked(cfg) ? 3 : bwd_chunked(cfg) ? 2 : bwd_from_forward(cfg) && cfg->T > 0;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool lg = (cfg->flags & CARVE_DECAY_LOGITS) != 0;
   hipError_t e = hipSuccess;
-  if (a.pre_ckpt) {
+  if (a.pre_ckpt == 3 && (int64_t)cfg->B * cfg->H > 0) {
+    // the chunk-serial forward stores the state, gate bias and gate mean at
+    // every chunk start; its output goes to a scratch buffer
+    const BwdBytes bb = bwd_bytes(cfg);
+    const carve::BwdWs lay(64, cfg->T, cfg->L, cfg->rank, false, true, true);
+    carve::FwdArgs f{};
+    f.q = q; f.k = k; f.v = v; f.g = g; f.bx = bx; f.w = w;
+    f.ub_down = ub_down; f.ub_up = ub_up;
+    f.state_in = state_in; f.mean_in = mean_in;
+    f.o = static_cast<unsigned char*>(workspace) + bb.o;
+    f.B = cfg->B; f.H = cfg->H; f.T = cfg->T; f.L = cfg->L; f.rank = cfg->rank;
+    f.ckpt = static_cast<float*>(workspace);
+    f.ckpt_bh = lay.total;
+    f.ckpt_z = lay.z;
+    f.ckpt_m = lay.m;
+    e = lg ? launch_serial_ckpt<true>(f, s) : launch_serial_ckpt<false>(f, s);
+    if (e == hipSuccess) e = lg ? launch_content_chunked<true>(a, s) : launch_content_chunked<false>(a, s);
+  } else if (a.pre_ckpt == 3) {
+    e = launch_ub_sum<64>(a, s);                      // no (batch, head): zero factor gradients
+  } else if (a.pre_ckpt) {
     // the forward pair writes the state at every chunk start into the
     // backward's checkpoints (chunk c starts at block c L / 64)
     const BwdBytes bb = bwd_bytes(cfg);
@@ -576,7 +635,7 @@ extern "C" int carve_chunk_bwd(const carve_config* cfg,
     unsigned char* wsb = static_cast<unsigned char*>(workspace);
     e = lg ? launch_chunked<true>(a, wsb + bb.img, wsb + bb.o, s) : launch_chunked<false>(a, wsb + bb.img, wsb + bb.o, s);
   }
-  else if (e == hipSuccess)
+  else if (e == hipSuccess && a.pre_ckpt != 3)
     e = cfg->dtype == CARVE_BF16
             ? (lg ? dispatch_bwd_width<carve::bf16, true>(cfg, a, s) : dispatch_bwd_width<carve::bf16, false>(cfg, a, s))
             : (lg ? dispatch_bwd_width<float, true>(cfg, a, s) : dispatch_bwd_width<float, false>(cfg, a, s));

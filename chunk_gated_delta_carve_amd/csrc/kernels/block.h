@@ -49,6 +49,10 @@ struct FwdArgs {
   // start of every (1 << ckpt_shift)-th block, the k-th at
   // ckpt + bh ckpt_bh + k dv dk
   float* ckpt; size_t ckpt_bh; int ckpt_shift;
+  // the chunk-serial kernel's checkpointing variant: at every chunk start c
+  // also the gate's bias z [dk] at ckpt + bh ckpt_bh + ckpt_z + c dk and the
+  // mean it was formed from, m_{c-1} [dv], at ... + ckpt_m + c dv
+  size_t ckpt_z, ckpt_m;
 };
 
 constexpr float kSpanLimit2 = 96.0f;   // max decay (log2 units) inside a 16-row sub-block

@@ -94,7 +94,10 @@ __host__ __device__ constexpr int bwd_slices(int D, int rank) { return rank == 0
 //
 // The chunk-parallel schedule (carve_bwd_chunk_kernel, `chunked`) keeps only
 // the state at every 64-token block start, the state gradient at every block
-// end and each row's share of d_mean_out over the last chunk's tokens.
+// end and each row's share of d_mean_out over the last chunk's tokens; with a
+// projection (carve_bwd_chunk_serial_kernel) the states, gate biases and
+// gate means of every chunk, one carried state gradient and the factor
+// gradients' partial sums.
 struct BwdWs {
   size_t ckpt, sbuf, sbuf_group, dsck, dmo, z, m, y, dud, duu, part, wpart, nrm, dqh, dkh, total;
   int groups;
@@ -105,9 +108,22 @@ struct BwdWs {
       groups = 1;
       ckpt = 0;
       sbuf = sbuf_group = 0;
-      dsck = nb * DD;
-      dmo = 2 * nb * DD;
-      z = m = y = dud = duu = part = wpart = nrm = dqh = dkh = dmo + D;
+      if (rank > 0) {
+        // the per-head chunk walk of the content schedule (L = 64): the
+        // carried state gradient, each chunk's gate bias and gate mean, and
+        // the factor gradients' partial sums
+        dsck = nb * DD;
+        z = dsck + DD;
+        m = z + nb * D;
+        y = dud = m + nb * D;
+        duu = dud + (size_t)rank * D;
+        dmo = duu + (size_t)D * rank;
+      } else {
+        dsck = nb * DD;
+        dmo = 2 * nb * DD;
+        z = m = y = dud = duu = dmo + D;
+      }
+      part = wpart = nrm = dqh = dkh = dmo + D;
       total = (dmo + D + 3) & ~(size_t)3;
       return;
     }

@@ -74,17 +74,33 @@ struct ChunkBwdLayout {
   static constexpr int oEg = oDec + 4 * D * 4;                    // fp32 [4][D]: 2^{Gs_I}
   static constexpr int oAd = oEg + 4 * D * 4;                     // fp32 [4][16][16]: diagonal tiles of A
   static constexpr int oTd = oAd + 4 * 256 * 4;                   // fp32 [4][16][16]: their inverses
-  static constexpr int oRed = oTd + 4 * 256 * 4;                  // fp32 [16][D]: column partial sums
-  static constexpr int oScr = oRed + 16 * D * 4;                  // bf16 [NWV][4][16][16]
+  static constexpr int oRed = oTd + 4 * 256 * 4;                  // fp32 [20][D]: column partial sums
+  static constexpr int oScr = oRed + 20 * D * 4;                  // bf16 [NWV][4][16][16]
   static constexpr int oDw = oScr + NWV * 4 * 256 * 2;            // fp32 [NWV][16]: dw partials
   static constexpr int oFlag = oDw + NWV * 16 * 4;                // int [4]: steep sub-blocks
-  static constexpr int bytes = oFlag + 16;
+  static constexpr int oVec = oFlag + 16;                         // fp32 [5][64]: the content schedule's vectors
+  static constexpr int oU = oVec + 5 * 64 * 4;                    // bf16 U_down [r][D], U_up [D][r] (r <= 64)
+  static constexpr int bytes = oU + 2 * 64 * D * 2;
+  static_assert(bytes <= 160 * 1024, "LDS budget");
+};
+
+// What one chunk's gradients are formed from, and what else they return.
+struct ChunkIO {
+  const float* S0;    // fp32 [dv][dk] state at the chunk start
+  const float* dSL;   // fp32 [dv][dk] state gradient at the chunk end (nullptr: zeros)
+  const float* z;     // content bias of the chunk's erase gate [dk] (nullptr: none)
+  const float* dml;   // per value channel, added to the output gradients of tokens >= dml_from (nullptr: none)
+  int dml_from;
+  float* dS0;         // the state gradient at the chunk start [dv][dk] (nullptr: not formed)
+  float* dz;          // LDS [dk]: the chunk's sum of dbx over its tokens (nullptr: not formed)
 };
 
 // kLogits: g holds raw decay logits a (g = -softplus(a)); dg is then the
-// gradient of a, dg_g (-sigmoid(a)).
+// gradient of a, dg_g (-sigmoid(a)). Called by all threads of a
+// 512-thread workgroup; ends with the gradient stores (no barrier after).
 template <int D, bool kLogits>
-__global__ void __launch_bounds__(512) carve_bwd_chunk_kernel(BwdArgs a) {
+__device__ __forceinline__ void chunk_body(const BwdArgs& a, unsigned char* smem, const int bh, const int ch,
+                                           const ChunkIO& io) {
   using LY = ChunkBwdLayout<D>;
   constexpr int L = LY::L, LD = LY::LD, GLD = LY::GLD, NT = LY::NT;
   static_assert(NT == 512, "eight waves: two per 16-row block, two column tiles each");
@@ -92,7 +108,6 @@ __global__ void __launch_bounds__(512) carve_bwd_chunk_kernel(BwdArgs a) {
   typedef bf16x4 b4;
   typedef Mma16<bf16> MB;
   typedef Mma16<float> MF;
-  extern __shared__ __align__(16) unsigned char smem[];
   bf16* BKl = reinterpret_cast<bf16*>(smem + LY::oBKl);
   bf16* Ql = reinterpret_cast<bf16*>(smem + LY::oQl);
   bf16* Kr = reinterpret_cast<bf16*>(smem + LY::oKr);
@@ -116,16 +131,19 @@ __global__ void __launch_bounds__(512) carve_bwd_chunk_kernel(BwdArgs a) {
   int* Flag = reinterpret_cast<int*>(smem + LY::oFlag);
 
   // wave w: rows 16 I .. 16 I + 15 (I = w / 2) of every L x d result, column
-  // tiles 2 hc and 2 hc + 1 (hc = w % 2)
-  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), I = w >> 1, hc = w & 1;
+  // tiles 2 hc and 2 hc + 1 (hc = w % 2). The thread index is read through an
+  // empty asm statement so that a caller's chunk loop cannot hoist the
+  // per-lane addresses derived from it (they would hold registers across
+  // the whole loop).
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, w = wave_id(), I = w >> 1, hc = w & 1;
   const int c16 = lane & 15, g4 = lane >> 4;
-  const int T = a.T, H = a.H, nc = (T + L - 1) / L;
-  const int ch = blockIdx.x % nc, bh = blockIdx.x / nc, bi = bh / H, h = bh % H;
+  const int T = a.T, H = a.H, bi = bh / H, h = bh % H;
   const int t0 = ch * L, n = min(L, T - t0);
-  const BwdWs lay(D, T, L, 0, false, true, true);
-  const float* wsb = a.ws + (size_t)bh * lay.total;
-  const float* Sg = wsb + lay.ckpt + (size_t)ch * DD;
-  const float* dSg = wsb + lay.dsck + (size_t)(nc - 1 - ch) * DD;   // the chain runs from the last chunk
+  const float* Sg = io.S0;
+  const float* dSg = io.dSL;
+  auto zb = [&](int cc) { return io.z ? io.z[cc] : 0.f; };     // content bias of key channel cc
   const bf16* Q = static_cast<const bf16*>(a.q);
   const bf16* K = static_cast<const bf16*>(a.k);
   const bf16* V = static_cast<const bf16*>(a.v);
@@ -164,17 +182,17 @@ __global__ void __launch_bounds__(512) carve_bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       sv[j] = Sg[(size_t)(8 * s + j) * D + cc];
-      dv[j] = dSg[(size_t)(8 * s + j) * D + cc];
+      dv[j] = dSg ? dSg[(size_t)(8 * s + j) * D + cc] : 0.f;
     }
-    // the outputs of the last L-token chunk also carry d_mean_out / n
-    // (carve_bwd_image_kernel left each row's share in the workspace)
-    const bool lastc = t0 + r >= (T - 1) / a.L * a.L;
+    // output gradients from the chunk mean (d_mean_out / n on the last
+    // L-token chunk's tokens; with a projection, the next chunk's gate too)
+    const bool lastc = io.dml && t0 + r >= io.dml_from;
     bf16x8 pwv, pdo;
     f32x4 gg[2];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       pwv[i] = (bf16)(wr * to_f32(xv[i]));
-      const float dml = lastc && rv ? wsb[lay.dmo + cs + i] : 0.f;
+      const float dml = lastc && rv ? io.dml[cs + i] : 0.f;
       pdo[i] = (bf16)(to_f32(xdo[i]) + dml);
       gg[i >> 2][i & 3] = rv ? decay_log2<kLogits>(to_f32(xg[i])) : 0.f;   // padding rows do not decay
     }
@@ -241,7 +259,7 @@ __global__ void __launch_bounds__(512) carve_bwd_chunk_kernel(BwdArgs a) {
       const int cc = cs + i;
       const float G0 = gr[cc], gs = Gs[I0 * D + cc], ge = Ge[I0 * D + cc];
       const float kv = to_f32(xk[i]);
-      pb[i] = (bf16)(sigmoid_f(to_f32(xbx[i])) * kv * fast_exp2(G0 - gs));
+      pb[i] = (bf16)(sigmoid_f(to_f32(xbx[i]) + zb(cc)) * kv * fast_exp2(G0 - gs));
       pq[i] = (bf16)(to_f32(xq[i]) * fast_exp2(grm[cc] - gs));
       pk[i] = (bf16)(kv * fast_exp2(ge - G0));
     }
@@ -290,7 +308,7 @@ __global__ void __launch_bounds__(512) carve_bwd_chunk_kernel(BwdArgs a) {
   // raw inputs of the pairwise path (steep sub-blocks only)
   auto raw = [&](const bf16* X, int row, int cc) { return row < n ? to_f32(X[tok(t0 + row) * D + cc]) : 0.f; };
   auto raw_bk = [&](int row, int cc) {
-    return row < n ? sigmoid_f(to_f32(BX[tok(t0 + row) * D + cc])) * to_f32(K[tok(t0 + row) * D + cc]) : 0.f;
+    return row < n ? sigmoid_f(to_f32(BX[tok(t0 + row) * D + cc]) + zb(cc)) * to_f32(K[tok(t0 + row) * D + cc]) : 0.f;
   };
   auto gprev = [&](int row, int cc) { return (row & 15) ? Gf[(row - 1) * GLD + cc] : Gs[(row >> 4) * D + cc]; };
 
@@ -559,7 +577,7 @@ __global__ void __launch_bounds__(512) carve_bwd_chunk_kernel(BwdArgs a) {
   bf16* dbx_o = static_cast<bf16*>(a.dbx);
   bf16* dw_o = static_cast<bf16*>(a.dw);
   f32x4 sfx[2];                                  // within-lane suffix of phi minus q dq
-  float tot[2], hlc[2], dwp[4] = {0.f, 0.f, 0.f, 0.f};
+  float tot[2], hlc[2], dzc[2], dwp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int nt = 2 * hc + q;
@@ -572,14 +590,14 @@ __global__ void __launch_bounds__(512) carve_bwd_chunk_kernel(BwdArgs a) {
       DdS = MB::mma(ldA(Del, r0, 16 * ks), ldBc(dSm, 16 * ks, 16 * nt), DdS);
     }
     const int cc = 16 * nt + c16;
-    const float gs = Gs[I * D + cc], ge = Ge[I * D + cc], gl = Ge[3 * D + cc];
+    const float gs = Gs[I * D + cc], ge = Ge[I * D + cc], gl = Ge[3 * D + cc], zc = zb(cc);
     f32x4 phi, qdq;
-    float hl = 0.f;
+    float hl = 0.f, dzs = 0.f;
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int i = r0 + 4 * g4 + ii;
       const float gi = Gf[i * GLD + cc], gim = gprev(i, cc);
-      const float qv = to_f32(pq[q][ii]), kv = to_f32(pk[q][ii]), bv = sigmoid_f(to_f32(pbx[q][ii]));
+      const float qv = to_f32(pq[q][ii]), kv = to_f32(pk[q][ii]), bv = sigmoid_f(to_f32(pbx[q][ii]) + zc);
       const float ed = fast_exp2(gl - gi);
       const float dq = fast_exp2(gim - gs) * qa[q][ii] + qx[q][ii] + fast_exp2(gim) * dOS[ii];
       const float xd = fast_exp2(gi - gs) * xa[q][ii] + xx[q][ii] + fast_exp2(gi) * dUS[ii];
@@ -590,12 +608,14 @@ __global__ void __launch_bounds__(512) carve_bwd_chunk_kernel(BwdArgs a) {
       hl += kv * ed * DdS[ii];
       const float dvv = pw[ii] * du[q][ii];
       dwp[ii] += to_f32(pv[q][ii]) * du[q][ii];
+      const float dbxv = db * bv * (1.f - bv);
       if (i < n) {
         const size_t o = tok(t0 + i) * D + cc;
         dq_o[o] = (bf16)dq;
         dk_o[o] = (bf16)dk;
-        dbx_o[o] = (bf16)(db * bv * (1.f - bv));
+        dbx_o[o] = (bf16)dbxv;
         dv_o[o] = (bf16)dvv;
+        dzs += dbxv;
       }
     }
     // suffix sums of phi over the lane's rows, minus q dq
@@ -603,6 +623,7 @@ __global__ void __launch_bounds__(512) carve_bwd_chunk_kernel(BwdArgs a) {
     sfx[q] = f32x4{s0 - qdq[0], s1 - qdq[1], s2 - qdq[2], s3 - qdq[3]};
     tot[q] = s0;
     hlc[q] = hl;
+    dzc[q] = dzs;
   }
   // dw: this wave's half of each row's sum over the 64 value columns
 #pragma unroll
@@ -619,12 +640,16 @@ __global__ void __launch_bounds__(512) carve_bwd_chunk_kernel(BwdArgs a) {
     const float t0v = __shfl(tot[q], c16);
     sg[q] = (g4 < 1 ? t1 : 0.f) + (g4 < 2 ? t2 : 0.f) + (g4 < 3 ? t3 : 0.f);
     const float hw = sum_groups(hlc[q]);
+    const float zw = io.dz ? sum_groups(dzc[q]) : 0.f;
     if (g4 == 0) {
       Red[(8 + I) * D + 16 * nt + c16] = t0v + t1 + t2 + t3;
       Red[(12 + I) * D + 16 * nt + c16] = hw;
+      Red[(16 + I) * D + 16 * nt + c16] = zw;
     }
   }
   lds_barrier();
+  if (io.dz && tid < D)
+    io.dz[tid] = Red[16 * D + tid] + Red[17 * D + tid] + Red[18 * D + tid] + Red[19 * D + tid];
   if (hc == 0 && lane < 16) {
     const int i = r0 + lane;
     if (i < n) dw_o[tok(t0 + i)] = (bf16)(Dwp[w * 16 + lane] + Dwp[(w + 1) * 16 + lane]);
@@ -650,10 +675,8 @@ __global__ void __launch_bounds__(512) carve_bwd_chunk_kernel(BwdArgs a) {
     }
   }
 
-  // ------------------------------------------- gradients of the incoming state and mean
-  // (no gradient reaches the incoming mean without a projection)
-  if (ch == 0 && a.d_mean_in && tid < D) a.d_mean_in[(size_t)bh * D + tid] = 0.f;
-  if (ch == 0 && a.d_state_in) {
+  // ------------------------------------------- the state gradient at the chunk start
+  if (io.dS0) {
     // rows e = 16 I + 4 g4 + ii, columns c = 16 nt + c16
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -670,9 +693,110 @@ __global__ void __launch_bounds__(512) carve_bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int e = r0 + 4 * g4 + ii;
-        a.d_state_in[(size_t)bh * DD + (size_t)e * D + cc] = dSg[(size_t)e * D + cc] * el + s1[ii] - s2[ii];
+        const float dsl = dSg ? dSg[(size_t)e * D + cc] : 0.f;
+        io.dS0[(size_t)e * D + cc] = dsl * el + s1[ii] - s2[ii];
       }
     }
+  }
+}
+
+// Without a projection: one workgroup per (batch, head, chunk), all at once.
+template <int D, bool kLogits>
+__global__ void __launch_bounds__(512) carve_bwd_chunk_kernel(BwdArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int nc = (a.T + 63) / 64;
+  const int ch = blockIdx.x % nc, bh = blockIdx.x / nc;
+  const BwdWs lay(D, a.T, 64, 0, false, true, true);
+  float* wsb = a.ws + (size_t)bh * lay.total;
+  ChunkIO io;
+  io.S0 = wsb + lay.ckpt + (size_t)ch * D * D;
+  io.dSL = wsb + lay.dsck + (size_t)(nc - 1 - ch) * D * D;      // the chain runs from the last chunk
+  io.z = nullptr;
+  io.dml = wsb + lay.dmo;                                       // d_mean_out / n, left by the image kernel
+  io.dml_from = (a.T - 1) / a.L * a.L;                          // first token of the last L-token chunk
+  io.dS0 = ch == 0 && a.d_state_in ? a.d_state_in + (size_t)bh * D * D : nullptr;
+  io.dz = nullptr;
+  // no gradient reaches the incoming mean without a projection
+  if (ch == 0 && a.d_mean_in && threadIdx.x < D) a.d_mean_in[(size_t)bh * D + threadIdx.x] = 0.f;
+  chunk_body<D, kLogits>(a, smem, bh, ch, io);
+}
+
+// With a content projection (d = 64, 64-token chunks): chunk c's erase gate
+// reads the mean of chunk c - 1's outputs, so the chunks are walked from the
+// last, one workgroup per (batch, head). chunk_body forms each chunk's
+// gradients and the state gradient at its start (carried to the previous
+// chunk in fp32 through the workspace); then the gate's gradient
+//   dz = sum over the chunk of dbx,  y = U_down m_{c-1},  dy = U_up^T dz,
+//   dU_up += dz y^T,  dU_down += dy m_{c-1}^T,  dm_{c-1} = U_down^T dy
+// adds dm_{c-1} / 64 to every output gradient of chunk c - 1 (nothing with
+// detached means) and leaves the factor gradients of this (batch, head) in
+// the workspace for carve_bwd_ub_kernel. The chunk-start states, gate biases
+// and gate means come from the checkpointing chunk-serial forward.
+template <int D, bool kLogits>
+__global__ void __launch_bounds__(512) carve_bwd_chunk_serial_kernel(BwdArgs a) {
+  using LY = ChunkBwdLayout<D>;
+  constexpr size_t DD = (size_t)D * D;
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* vec = reinterpret_cast<float*>(smem + LY::oVec);
+  float* dzs = vec;                      // the chunk's dz
+  float* dml = vec + 64;                 // per value channel, added to the chunk's output gradients
+  float* ms = vec + 128;                 // m_{c-1}
+  float* ys = vec + 192;                 // U_down m_{c-1}
+  float* dys = vec + 256;                // U_up^T dz
+  bf16* Uds = reinterpret_cast<bf16*>(smem + LY::oU);
+  bf16* Uus = Uds + 64 * D;
+  const int tid = threadIdx.x, bh = blockIdx.x, h = bh % a.H, T = a.T, rank = a.rank;
+  const int nc = (T + 63) / 64;
+  const BwdWs lay(D, T, 64, rank, false, true, true);
+  float* wsb = a.ws + (size_t)bh * lay.total;
+  float* carry = wsb + lay.dsck;
+  const bf16* Ud = static_cast<const bf16*>(a.ub_down) + (size_t)h * rank * D;   // [rank][D]
+  const bf16* Uu = static_cast<const bf16*>(a.ub_up) + (size_t)h * D * rank;     // [D][rank]
+  for (int i = tid; i < rank * D; i += LY::NT) {
+    Uds[i] = Ud[i];
+    Uus[i] = Uu[i];
+    wsb[lay.dud + i] = 0.f;              // this (batch, head)'s factor gradients, each element
+    wsb[lay.duu + i] = 0.f;              // cleared and later updated by the same thread
+  }
+  const int tl0 = (nc - 1) * 64;
+  if (tid < D) dml[tid] = a.d_mean_out ? a.d_mean_out[(size_t)bh * D + tid] / (float)(T - tl0) : 0.f;
+  __syncthreads();
+  for (int ch = nc - 1; ch >= 0; --ch) {
+    ChunkIO io;
+    io.S0 = wsb + lay.ckpt + (size_t)ch * DD;
+    io.dSL = ch == nc - 1 ? (a.d_state_out ? a.d_state_out + (size_t)bh * DD : nullptr) : carry;
+    io.z = wsb + lay.z + (size_t)ch * D;
+    io.dml = dml;
+    io.dml_from = 64 * ch;
+    io.dS0 = ch > 0 ? carry : (a.d_state_in ? a.d_state_in + (size_t)bh * DD : nullptr);
+    io.dz = dzs;
+    chunk_body<D, kLogits>(a, smem, bh, ch, io);
+    __syncthreads();                     // the carried gradient and dz are complete
+    if (tid < D) ms[tid] = wsb[lay.m + (size_t)ch * D + tid];
+    __syncthreads();
+    if (tid < rank) {
+      float y = 0.f, dy = 0.f;
+#pragma unroll 8
+      for (int e = 0; e < D; ++e) {
+        y += to_f32(Uds[tid * D + e]) * ms[e];
+        dy += to_f32(Uus[e * rank + tid]) * dzs[e];
+      }
+      ys[tid] = y;
+      dys[tid] = dy;
+    }
+    __syncthreads();
+    for (int i = tid; i < rank * D; i += LY::NT) {
+      wsb[lay.dud + i] += dys[i / D] * ms[i % D];          // dU_down[r][e]
+      wsb[lay.duu + i] += dzs[i / rank] * ys[i % rank];    // dU_up[d][r]
+    }
+    if (tid < D) {
+      float dm = 0.f;
+      for (int r = 0; r < rank; ++r) dm += to_f32(Uds[r * D + tid]) * dys[r];
+      if (a.detach) dm = 0.f;
+      if (ch > 0) dml[tid] = dm * (1.f / 64.f);
+      else if (a.d_mean_in) a.d_mean_in[(size_t)bh * D + tid] = dm;
+    }
+    __syncthreads();
   }
 }
 

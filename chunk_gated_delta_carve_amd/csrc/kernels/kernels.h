@@ -32,8 +32,10 @@ constexpr int serial_waves() { return DK == 64 && BL >= 32 ? 8 : DK / 16; }
 
 // kLogits: the decay input g holds raw decay logits a, and the log-decay is
 // -softplus(a), formed where g is read. kNorm: q and k are divided per token
-// by their L2 norms over d_k where they are read.
-template <typename E, int DK, int DV, int BL, bool kLogits, bool kNorm>
+// by their L2 norms over d_k where they are read. kCkpt: at every chunk start
+// the state, the gate's bias z and the mean m_{c-1} behind it are stored for
+// the backward pass (a.ckpt, a.ckpt_z, a.ckpt_m).
+template <typename E, int DK, int DV, int BL, bool kLogits, bool kNorm, bool kCkpt = false>
 __global__ void __launch_bounds__((BlockLayout<E, DK, DV, BL, serial_waves<DK, BL>()>::NT))
 carve_chunk_serial_kernel(FwdArgs a) {
   using B = Block<E, DK, DV, BL, serial_waves<DK, BL>()>;
@@ -174,6 +176,17 @@ carve_chunk_serial_kernel(FwdArgs a) {
     const int nvalid = min(BL, T - t0);
     E qd[16];
     f32x4 Pt[B::TPW];
+    if constexpr (kCkpt) {
+      if (t0 % L == 0) {
+        const int c = t0 / L;
+        float* base = a.ckpt + (size_t)bh * a.ckpt_bh;
+        float* S = base + (size_t)c * DV * DK + (size_t)(e0 + cc) * DK + 4 * gq;
+#pragma unroll
+        for (int t = 0; t < TDP; ++t) *reinterpret_cast<f32x4*>(S + 16 * (TDP * part + t)) = St[t];
+        for (int e = tid; e < DK; e += NT) base[a.ckpt_z + (size_t)c * DK + e] = s.Z[e];
+        for (int e = tid; e < DV; e += NT) base[a.ckpt_m + (size_t)c * DV + e] = s.M[e];
+      }
+    }
     if (kFetch == 2) raw.template load<kNorm>(src, t0, nvalid);
     const bool fallback = B::template gate_pass<true, kLogits, kNorm>(s, raw, nvalid, qd);
     if (kFetch == 0) fetch_next(blk);

@@ -194,11 +194,19 @@ def test_bwd_workspace_size():
     projection at d = 64, d / 16 slices without one, none at d = 128 with one);
     in bf16 without a projection and with L a multiple of 64, also the
     forward pair's block images and output."""
-    sh = _lib.ref_shapes(cfg())                      # B2 H3 T100 d64 L64 rank 4: two chunks
+    sh = _lib.ref_shapes(cfg(dtype=_lib.CARVE_F32))  # B2 H3 T100 d64 L64 rank 4: two chunks
     vecs = 2 * 2 * 64 + 2 * 4 + 2 * 4 * 64           # z and m per chunk, U_down m per chunk, dU partials
     per_bh = 2 * 64 * 64 + 8 * 64 * 64 + vecs
     per_bh = (per_bh + 3) // 4 * 4 + 100 * 1 * (4 * 64 + 1)
     assert sh.bwd_workspace_bytes == 6 * 4 * ((per_bh + 3) // 4 * 4)
+    # in bf16 at d 64 with 64-token chunks, the per-head chunk walk: the state,
+    # gate bias and gate mean of every chunk, one carried state gradient, the
+    # factor gradients' partial sums and a d_mean_out share; then a scratch
+    # output for the checkpointing forward
+    shc = _lib.ref_shapes(cfg())
+    per_bh_c = 2 * 64 * 64 + 64 * 64 + 2 * 2 * 64 + 2 * 4 * 64 + 64
+    own_c = 6 * 4 * ((per_bh_c + 3) // 4 * 4)
+    assert shc.bwd_workspace_bytes == (own_c + 255) // 256 * 256 + 2 * 100 * 3 * 64 * 2
     sh128 = _lib.ref_shapes(cfg(dk=128, dv=128))
     per_bh128 = 2 * 128 * 128 + 64 * 128 * 128 + 2 * 2 * 128 + 2 * 4 + 2 * 4 * 128
     assert sh128.bwd_workspace_bytes == 6 * 4 * ((per_bh128 + 3) // 4 * 4)

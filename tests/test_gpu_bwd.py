@@ -191,6 +191,49 @@ def test_backward_chunk_parallel_in_place(torch_cuda):
     assert_grads(got, ref, TOL["bf16"], "chunk in place")
 
 
+CONTENT_CHUNK_CASES = [
+    # bf16, d 64, 64-token chunks, with a projection: one workgroup per head
+    # walks the chunks from the last with the chunk-parallel products
+    # name, B, H, T, rank, with_state, detach, alias
+    ("r16-ragged-150", 2, 2, 150, 16, True, False, False),
+    ("r64-one-chunk-64", 1, 3, 64, 64, True, False, False),
+    ("r4-short-40", 2, 1, 40, 4, True, False, False),
+    ("r8-no-state-gradients-256", 2, 2, 256, 8, False, False, False),
+    ("r8-detached-200", 1, 2, 200, 8, True, True, False),
+    ("r16-in-place-190", 2, 2, 190, 16, True, False, True),
+]
+
+
+@pytest.mark.parametrize("name,B,H,T,rank,with_state,detach,alias", CONTENT_CHUNK_CASES,
+                         ids=[c[0] for c in CONTENT_CHUNK_CASES])
+def test_backward_content_chunk_walk(torch_cuda, name, B, H, T, rank, with_state, detach, alias):
+    wl = workload("content-chunk-" + name, "bf16", B, H, T, 64, 64, rank, 7200 + T)
+    say("case content chunk", wl)
+    inp = make_inputs(wl)
+    do, dSo, dmo, S_in, m_in = cotangents(B, H, T, 64, "bf16", 7250 + T, with_state=with_state)
+    ref = bwd_oracle(inp, "bf16", 64, do, dSo, dmo, S_in, m_in, detach=detach)
+    if alias:
+        got = bwd_gpu(torch_cuda, inp, "bf16", 64, do, dSo.copy(), dmo.copy(), S_in, m_in, alias=True)
+    else:
+        got = bwd_gpu(torch_cuda, inp, "bf16", 64, do, dSo, dmo, S_in, m_in, detach=detach)
+    assert_grads(got, ref, TOL["bf16"], "content chunk " + name)
+
+
+def test_backward_content_chunk_walk_steep_decay(torch_cuda):
+    """The content walk through sub-blocks whose decay is too steep for the
+    factorised diagonal products (pairwise path, with the gate bias)."""
+    from chunk_gated_delta_carve_amd.workloads import bf16_bits_from_f32
+    wl = workload("content-chunk-steep", "bf16", 1, 2, 150, 64, 64, 16, 7300)
+    inp = make_inputs(wl)
+    g = to_f64(inp["g"], "bf16")
+    g[:, :, 0, :8] *= 10.0
+    g[:, 40:90, 1, 8:12] = -30.0
+    inp["g"] = bf16_bits_from_f32(g.astype(np.float32))
+    do, dSo, dmo, S_in, m_in = cotangents(1, 2, 150, 64, "bf16", 7301)
+    got = bwd_gpu(torch_cuda, inp, "bf16", 64, do, dSo, dmo, S_in, m_in)
+    assert_grads(got, bwd_oracle(inp, "bf16", 64, do, dSo, dmo, S_in, m_in), TOL["bf16"], "content chunk steep")
+
+
 @pytest.mark.parametrize("dtype,L,rank", [("f32", 32, 0), ("f32", 32, 8), ("bf16", 64, 0)],
                          ids=["f32-r0", "f32-r8", "bf16-r0-forward-checkpoints"])
 def test_backward_with_decay_logits(torch_cuda, dtype, L, rank):
