@@ -493,15 +493,15 @@ def bench_backward(args, wl):
     ub = (t["U_down"], t["U_up"]) if rank else (None, None)
     from chunk_gated_delta_carve_amd import recurrent_ref_shapes
     tdtype = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
-    ws = torch.empty(int(recurrent_ref_shapes(B, H, T, dk, dv, L, rank, tdtype).bwd_workspace_bytes),
-                     dtype=torch.uint8, device="cuda")
+    ws = torch.empty(int(recurrent_ref_shapes(B, H, T, dk, dv, L, rank, tdtype, qk_l2norm=args.qk_l2norm)
+                         .bwd_workspace_bytes), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     out = None
 
     def step():
         nonlocal out
         out = chunk_bwd(*(t[k] for k in ("q", "k", "v", "g", "bx", "w")), d_o, L=L, ub_down=ub[0], ub_up=ub[1],
-                        decay_logits=args.decay_logits, workspace=ws, out=out)
+                        decay_logits=args.decay_logits, qk_l2norm=args.qk_l2norm, workspace=ws, out=out)
 
     for _ in range(max(1, args.warmup)):
         step()
@@ -534,13 +534,14 @@ def bench_backward(args, wl):
         "config": {"workload": f"carve_chunk_bwd B{B} H{H} T{T} dk{dk} dv{dv} L{L} {wl.dtype}, "
                                + (f"content projection rank {rank}" if rank else "no content projection"),
                    "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "L": L, "rank": rank,
-                   "decay_input": "raw logits, -softplus in-kernel" if args.decay_logits else "log-decay g"},
+                   "decay_input": "raw logits, -softplus in-kernel" if args.decay_logits else "log-decay g",
+                   "qk": "L2-normalised in-kernel" if args.qk_l2norm else "as given"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "kernel": backward_kernels(wl, rank),
                      "kernel_ms": kernel_ms, "algorithmic_bytes_per_launch": alg},
     }
-    if not args.no_cpu_baseline and not args.decay_logits:
+    if not args.no_cpu_baseline and not args.decay_logits and not args.qk_l2norm:
         line["cpu_baseline"] = backward_cpu_baseline(wl, inp, do, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 

@@ -24,8 +24,9 @@ def make_config(B, H, T, dk, dv, L, rank, dtype, decay_logits=False, qk_l2norm=F
                             flags)
 
 
-def recurrent_ref_shapes(B, H, T, dk, dv, L, rank=0, dtype=torch.bfloat16) -> _lib.CarveShapes:
-    return _lib.ref_shapes(make_config(B, H, T, dk, dv, L, rank, dtype))
+def recurrent_ref_shapes(B, H, T, dk, dv, L, rank=0, dtype=torch.bfloat16, decay_logits=False, qk_l2norm=False,
+                         detach_mean=False) -> _lib.CarveShapes:
+    return _lib.ref_shapes(make_config(B, H, T, dk, dv, L, rank, dtype, decay_logits, qk_l2norm, detach_mean))
 
 
 def _ptr(t):

@@ -79,11 +79,8 @@ bool bwd_from_forward(const carve_config* c) { return chunk_parallel(c) && c->L 
 
 // The chunk-parallel backward (one workgroup per (batch, head, 64-token
 // block), dense products on the matrix cores) covers bf16 without a
-// projection at d = 64, any L, with keys as given (not normalised in the
-// kernel); every other shape walks the tokens.
-bool bwd_chunked(const carve_config* c) {
-  return chunk_parallel(c) && c->dk == 64 && c->T > 0 && !(c->flags & CARVE_QK_L2NORM);
-}
+// projection at d = 64, any L; every other shape walks the tokens.
+bool bwd_chunked(const carve_config* c) { return chunk_parallel(c) && c->dk == 64 && c->T > 0; }
 // With a projection in bf16 at d = 64 and 64-token chunks the chunks are
 // differentiated one after another by one workgroup per head with the same
 // dense per-chunk products, after a checkpointing chunk-serial forward.
@@ -242,40 +239,6 @@ hipError_t launch_row_lane(const carve::BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Chunk-parallel schedule (after the forward pair has written the chunk-start
-// states and its block images): the images become the backward chain's, the
-// checkpointing state pass walks that chain from the last chunk and stores
-// the state gradient at every chunk end, then one workgroup per (batch,
-// head, chunk) forms the gradients.
-template <bool LG>
-hipError_t launch_chunked(const carve::BwdArgs& a, unsigned char* imgs, void* o_scratch, hipStream_t s) {
-  using CL = carve::ChunkBwdLayout<64>;
-  using LY = carve::BlockLayout<carve::bf16, 64, 64, kParallelBlock>;
-  constexpr auto image = carve::carve_bwd_image_kernel<64>;
-  constexpr auto chain = carve::carve_state_kernel<carve::bf16, 64, 64, kParallelBlock, true>;
-  constexpr auto chunk = carve::carve_bwd_chunk_kernel<64, LG>;
-  hipError_t e = set_lds<chunk>(CL::bytes);
-  if (e != hipSuccess) return e;
-  const int64_t nc = (a.T + kParallelBlock - 1) / kParallelBlock, BH = (int64_t)a.B * a.H;
-  hipLaunchKernelGGL(image, dim3((unsigned)(BH * ((nc + 1) / 2))), dim3(256), 0, s, a, imgs);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const carve::BwdWs lay(64, a.T, kParallelBlock, 0, false, true, true);
-  carve::FwdArgs f{};
-  f.ws = imgs;
-  f.state_in = a.d_state_out;
-  f.o = o_scratch;
-  f.ckpt = a.ws + lay.dsck;
-  f.ckpt_bh = lay.total;
-  f.ckpt_shift = 0;
-  f.B = a.B; f.H = a.H; f.T = a.T; f.L = kParallelBlock; f.rank = 0;
-  hipLaunchKernelGGL(chain, dim3(carve::state_grid(a.B * a.H, LY::NW)), dim3(carve::kStateThreads), 0, s, f);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(chunk, dim3((unsigned)(BH * nc)), dim3(CL::NT), CL::bytes, s, a);
-  return hipGetLastError();
-}
-
 // the projection factors' gradients, summed over the batch (zeros for B = 0)
 template <int D>
 hipError_t launch_ub_sum(const carve::BwdArgs& a, hipStream_t s) {
@@ -296,6 +259,47 @@ hipError_t launch_norm(const carve::BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((carve::carve_bwd_norm_kernel<E, D, NORMS>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
                      a);
   return hipGetLastError();
+}
+
+// Chunk-parallel schedule (after the forward pair has written the chunk-start
+// states and its block images): the images become the backward chain's, the
+// checkpointing state pass walks that chain from the last chunk and stores
+// the state gradient at every chunk end, then one workgroup per (batch,
+// head, chunk) forms the gradients.
+template <bool LG, bool NRM>
+hipError_t launch_chunked(const carve::BwdArgs& a, unsigned char* imgs, void* o_scratch, hipStream_t s) {
+  using CL = carve::ChunkBwdLayout<64>;
+  using LY = carve::BlockLayout<carve::bf16, 64, 64, kParallelBlock>;
+  constexpr auto image = carve::carve_bwd_image_kernel<64>;
+  constexpr auto chain = carve::carve_state_kernel<carve::bf16, 64, 64, kParallelBlock, true>;
+  constexpr auto chunk = carve::carve_bwd_chunk_kernel<64, LG, NRM>;
+  hipError_t e = set_lds<chunk>(CL::bytes);
+  if (e != hipSuccess) return e;
+  const int64_t nc = (a.T + kParallelBlock - 1) / kParallelBlock, BH = (int64_t)a.B * a.H;
+  hipLaunchKernelGGL(image, dim3((unsigned)(BH * ((nc + 1) / 2))), dim3(256), 0, s, a, imgs);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const carve::BwdWs lay(64, a.T, kParallelBlock, 0, NRM, true, true);
+  carve::FwdArgs f{};
+  f.ws = imgs;
+  f.state_in = a.d_state_out;
+  f.o = o_scratch;
+  f.ckpt = a.ws + lay.dsck;
+  f.ckpt_bh = lay.total;
+  f.ckpt_shift = 0;
+  f.B = a.B; f.H = a.H; f.T = a.T; f.L = kParallelBlock; f.rank = 0;
+  hipLaunchKernelGGL(chain, dim3(carve::state_grid(a.B * a.H, LY::NW)), dim3(carve::kStateThreads), 0, s, f);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if constexpr (NRM) {                               // every token's inverse norms of q and k
+    e = launch_norm<carve::bf16, 64, true>(a, s);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(chunk, dim3((unsigned)(BH * nc)), dim3(CL::NT), CL::bytes, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if constexpr (NRM) return launch_norm<carve::bf16, 64, false>(a, s);   // through the normalisation
+  return hipSuccess;
 }
 
 template <typename E, int D, bool LG, bool NRM>
@@ -633,7 +637,10 @@ extern "C" int carve_chunk_bwd(const carve_config* cfg,
   if (e == hipSuccess && a.pre_ckpt == 2) {
     const BwdBytes bb = bwd_bytes(cfg);
     unsigned char* wsb = static_cast<unsigned char*>(workspace);
-    e = lg ? launch_chunked<true>(a, wsb + bb.img, wsb + bb.o, s) : launch_chunked<false>(a, wsb + bb.img, wsb + bb.o, s);
+    unsigned char* img = wsb + bb.img;
+    void* o = wsb + bb.o;
+    e = a.norm ? (lg ? launch_chunked<true, true>(a, img, o, s) : launch_chunked<false, true>(a, img, o, s))
+               : (lg ? launch_chunked<true, false>(a, img, o, s) : launch_chunked<false, false>(a, img, o, s));
   }
   else if (e == hipSuccess && a.pre_ckpt != 3)
     e = cfg->dtype == CARVE_BF16

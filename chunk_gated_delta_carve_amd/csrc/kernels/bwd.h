@@ -123,8 +123,14 @@ struct BwdWs {
         dmo = 2 * nb * DD;
         z = m = y = dud = duu = dmo + D;
       }
-      part = wpart = nrm = dqh = dkh = dmo + D;
-      total = (dmo + D + 3) & ~(size_t)3;
+      // with q, k normalisation: every token's inverse norms and the fp32
+      // gradients of the normalised q and k
+      part = wpart = dmo + D;
+      nrm = (dmo + D + 3) & ~(size_t)3;
+      const size_t tn = norm ? (size_t)T : 0;
+      dqh = nrm + 2 * tn;
+      dkh = dqh + tn * D;
+      total = (dkh + tn * D + 3) & ~(size_t)3;
       return;
     }
     groups = bwd_groups(T, L, rank, pre_ckpt);
@@ -1181,7 +1187,7 @@ carve_bwd_norm_kernel(BwdArgs a) {
   const int h = (int)(row % a.H);
   const size_t bt = row / a.H;
   const int t = (int)(bt % a.T), bi = (int)(bt / a.T);
-  const BwdWs lay(D, a.T, a.L, a.rank, true, a.pre_ckpt != 0);
+  const BwdWs lay(D, a.T, a.L, a.rank, true, a.pre_ckpt != 0, a.pre_ckpt >= 2);
   float* ws = a.ws + ((size_t)bi * a.H + h) * lay.total;
   const E* Q = static_cast<const E*>(a.q) + row * D;
   const E* K = static_cast<const E*>(a.k) + row * D;

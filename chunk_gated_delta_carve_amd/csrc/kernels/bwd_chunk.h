@@ -93,12 +93,20 @@ struct ChunkIO {
   int dml_from;
   float* dS0;         // the state gradient at the chunk start [dv][dk] (nullptr: not formed)
   float* dz;          // LDS [dk]: the chunk's sum of dbx over its tokens (nullptr: not formed)
+  // with q, k normalisation (kNorm): every token's inverse norms of q and k
+  // (2 t, 2 t + 1), and where the fp32 gradients of the normalised q and k
+  // go ([t][dk]) for carve_bwd_norm_kernel
+  const float* nrm;
+  float* dqh;
+  float* dkh;
 };
 
 // kLogits: g holds raw decay logits a (g = -softplus(a)); dg is then the
-// gradient of a, dg_g (-sigmoid(a)). Called by all threads of a
-// 512-thread workgroup; ends with the gradient stores (no barrier after).
-template <int D, bool kLogits>
+// gradient of a, dg_g (-sigmoid(a)). kNorm: q and k are used over their L2
+// norms, and dq, dk are left as gradients of the normalised q and k. Called
+// by all threads of a 512-thread workgroup; ends with the gradient stores
+// (no barrier after).
+template <int D, bool kLogits, bool kNorm>
 __device__ __forceinline__ void chunk_body(const BwdArgs& a, unsigned char* smem, const int bh, const int ch,
                                            const ChunkIO& io) {
   using LY = ChunkBwdLayout<D>;
@@ -144,6 +152,8 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, unsigned char* smem
   const float* Sg = io.S0;
   const float* dSg = io.dSL;
   auto zb = [&](int cc) { return io.z ? io.z[cc] : 0.f; };     // content bias of key channel cc
+  // inverse norms of q (0) and k (1) of chunk row `row` (1 without kNorm)
+  auto nrm = [&](int row, int which) { return kNorm ? io.nrm[2 * (size_t)(t0 + row) + which] : 1.f; };
   const bf16* Q = static_cast<const bf16*>(a.q);
   const bf16* K = static_cast<const bf16*>(a.k);
   const bf16* V = static_cast<const bf16*>(a.v);
@@ -254,13 +264,14 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, unsigned char* smem
     const float* gr = Gf + r * GLD;
     const float* grm = (r & 15) ? Gf + (r - 1) * GLD : Gs + I0 * D;
     bf16x8 pb, pq, pk;
+    const float nq = rv ? nrm(r, 0) : 0.f, nk = rv ? nrm(r, 1) : 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int cc = cs + i;
       const float G0 = gr[cc], gs = Gs[I0 * D + cc], ge = Ge[I0 * D + cc];
-      const float kv = to_f32(xk[i]);
+      const float kv = to_f32(xk[i]) * nk;
       pb[i] = (bf16)(sigmoid_f(to_f32(xbx[i]) + zb(cc)) * kv * fast_exp2(G0 - gs));
-      pq[i] = (bf16)(to_f32(xq[i]) * fast_exp2(grm[cc] - gs));
+      pq[i] = (bf16)(to_f32(xq[i]) * nq * fast_exp2(grm[cc] - gs));
       pk[i] = (bf16)(kv * fast_exp2(ge - G0));
     }
     *reinterpret_cast<bf16x8*>(BKl + r * LD + cs) = pb;
@@ -306,9 +317,14 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, unsigned char* smem
   auto rnd = [](f32x4 x) { return MB::round(x); };
   const bool steep = Flag[I] != 0;
   // raw inputs of the pairwise path (steep sub-blocks only)
-  auto raw = [&](const bf16* X, int row, int cc) { return row < n ? to_f32(X[tok(t0 + row) * D + cc]) : 0.f; };
+  // q (X = Q) or k (X = K) of a chunk row, over its norm with kNorm
+  auto raw = [&](const bf16* X, int row, int cc) {
+    return row < n ? to_f32(X[tok(t0 + row) * D + cc]) * nrm(row, X == K ? 1 : 0) : 0.f;
+  };
   auto raw_bk = [&](int row, int cc) {
-    return row < n ? sigmoid_f(to_f32(BX[tok(t0 + row) * D + cc]) + zb(cc)) * to_f32(K[tok(t0 + row) * D + cc]) : 0.f;
+    return row < n ? sigmoid_f(to_f32(BX[tok(t0 + row) * D + cc]) + zb(cc)) * to_f32(K[tok(t0 + row) * D + cc]) *
+                         nrm(row, 1)
+                   : 0.f;
   };
   auto gprev = [&](int row, int cc) { return (row & 15) ? Gf[(row - 1) * GLD + cc] : Gs[(row >> 4) * D + cc]; };
 
@@ -462,13 +478,15 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, unsigned char* smem
   // raw inputs of the lane's output elements (rows 16 I + 4 g4 + ii,
   // columns 16 nt + c16), loaded now so they land during the products
   bf16 pq[2][4], pk[2][4], pbx[2][4], pv[2][4], pg[2][4];
-  float pw[4];
+  float pw[4], pnq[4], pnk[4];
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii) {
     const int i = r0 + 4 * g4 + ii;
     const bool ok = i < n;
     const size_t ro = tok(t0 + min(i, n - 1)) * D;
     pw[ii] = ok ? to_f32(W[tok(t0 + min(i, n - 1))]) : 0.f;
+    pnq[ii] = ok ? nrm(i, 0) : 0.f;
+    pnk[ii] = ok ? nrm(i, 1) : 0.f;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const size_t o = ro + 16 * (2 * hc + q) + c16;
@@ -597,7 +615,8 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, unsigned char* smem
     for (int ii = 0; ii < 4; ++ii) {
       const int i = r0 + 4 * g4 + ii;
       const float gi = Gf[i * GLD + cc], gim = gprev(i, cc);
-      const float qv = to_f32(pq[q][ii]), kv = to_f32(pk[q][ii]), bv = sigmoid_f(to_f32(pbx[q][ii]) + zc);
+      const float qv = to_f32(pq[q][ii]) * pnq[ii], kv = to_f32(pk[q][ii]) * pnk[ii];
+      const float bv = sigmoid_f(to_f32(pbx[q][ii]) + zc);
       const float ed = fast_exp2(gl - gi);
       const float dq = fast_exp2(gim - gs) * qa[q][ii] + qx[q][ii] + fast_exp2(gim) * dOS[ii];
       const float xd = fast_exp2(gi - gs) * xa[q][ii] + xx[q][ii] + fast_exp2(gi) * dUS[ii];
@@ -611,8 +630,13 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, unsigned char* smem
       const float dbxv = db * bv * (1.f - bv);
       if (i < n) {
         const size_t o = tok(t0 + i) * D + cc;
-        dq_o[o] = (bf16)dq;
-        dk_o[o] = (bf16)dk;
+        if constexpr (kNorm) {
+          io.dqh[(size_t)(t0 + i) * D + cc] = dq;
+          io.dkh[(size_t)(t0 + i) * D + cc] = dk;
+        } else {
+          dq_o[o] = (bf16)dq;
+          dk_o[o] = (bf16)dk;
+        }
         dbx_o[o] = (bf16)dbxv;
         dv_o[o] = (bf16)dvv;
         dzs += dbxv;
@@ -701,12 +725,12 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, unsigned char* smem
 }
 
 // Without a projection: one workgroup per (batch, head, chunk), all at once.
-template <int D, bool kLogits>
+template <int D, bool kLogits, bool kNorm>
 __global__ void __launch_bounds__(512) carve_bwd_chunk_kernel(BwdArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int nc = (a.T + 63) / 64;
   const int ch = blockIdx.x % nc, bh = blockIdx.x / nc;
-  const BwdWs lay(D, a.T, 64, 0, false, true, true);
+  const BwdWs lay(D, a.T, 64, 0, kNorm, true, true);
   float* wsb = a.ws + (size_t)bh * lay.total;
   ChunkIO io;
   io.S0 = wsb + lay.ckpt + (size_t)ch * D * D;
@@ -716,9 +740,12 @@ __global__ void __launch_bounds__(512) carve_bwd_chunk_kernel(BwdArgs a) {
   io.dml_from = (a.T - 1) / a.L * a.L;                          // first token of the last L-token chunk
   io.dS0 = ch == 0 && a.d_state_in ? a.d_state_in + (size_t)bh * D * D : nullptr;
   io.dz = nullptr;
+  io.nrm = wsb + lay.nrm;
+  io.dqh = wsb + lay.dqh;
+  io.dkh = wsb + lay.dkh;
   // no gradient reaches the incoming mean without a projection
   if (ch == 0 && a.d_mean_in && threadIdx.x < D) a.d_mean_in[(size_t)bh * D + threadIdx.x] = 0.f;
-  chunk_body<D, kLogits>(a, smem, bh, ch, io);
+  chunk_body<D, kLogits, kNorm>(a, smem, bh, ch, io);
 }
 
 // With a content projection (d = 64, 64-token chunks): chunk c's erase gate
@@ -770,7 +797,9 @@ __global__ void __launch_bounds__(512) carve_bwd_chunk_serial_kernel(BwdArgs a) 
     io.dml_from = 64 * ch;
     io.dS0 = ch > 0 ? carry : (a.d_state_in ? a.d_state_in + (size_t)bh * DD : nullptr);
     io.dz = dzs;
-    chunk_body<D, kLogits>(a, smem, bh, ch, io);
+    io.nrm = nullptr;
+    io.dqh = io.dkh = nullptr;
+    chunk_body<D, kLogits, false>(a, smem, bh, ch, io);
     __syncthreads();                     // the carried gradient and dz are complete
     if (tid < D) ms[tid] = wsb[lay.m + (size_t)ch * D + tid];
     __syncthreads();
@@ -829,7 +858,7 @@ __global__ void __launch_bounds__(256) carve_bwd_image_kernel(BwdArgs a, unsigne
   const int cA = pr, cB = nc - 1 - pr, nch = cA == cB ? 1 : 2;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), c16 = lane & 15, g4 = lane >> 4;
   unsigned char* base = imgs + (size_t)bh * nc * LY::wBytes;
-  const BwdWs lay(D, T, 64, 0, false, true, true);
+  const BwdWs lay(D, T, 64, 0, a.norm != 0, true, true);
   float* wsb = a.ws + (size_t)bh * lay.total;
   const bf16* DOg = static_cast<const bf16*>(a.d_o);
   const int tl0 = (T - 1) / a.L * a.L;                           // first token of the last L-token chunk

@@ -167,9 +167,11 @@ def test_step_normalises_q_and_k(torch_cuda, dtype, d, L, rank):
 
 
 BWD_CASES = [
-    # name, dtype, B, H, T, d, L, rank: the row-lane kernels (rank 0; d = 64 with
-    # a projection) and the per-head kernel (d = 128 with a projection)
+    # name, dtype, B, H, T, d, L, rank: the chunk-parallel kernel (bf16, d = 64,
+    # rank 0), the row-lane kernels (rank 0; d = 64 with a projection) and the
+    # per-head kernel (d = 128 with a projection)
     ("bwd-bf16-d64-r0-ragged-150", "bf16", 2, 2, 150, 64, 64, 0),
+    ("bwd-bf16-d64-r0-L128-ragged-200", "bf16", 1, 3, 200, 64, 128, 0),
     ("bwd-f32-d128-r0", "f32", 1, 2, 96, 128, 32, 0),
     ("bwd-f32-d64-r8-ragged-75", "f32", 1, 2, 75, 64, 16, 8),
     ("bwd-f32-d128-r4", "f32", 1, 2, 64, 128, 32, 4),
