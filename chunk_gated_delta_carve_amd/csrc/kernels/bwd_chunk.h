@@ -287,12 +287,6 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, unsigned char* smem
   auto ldA = [&](const bf16* m, int r0, int k0) -> b4 {
     return *reinterpret_cast<const b4*>(m + (r0 + c16) * LD + k0 + 4 * g4);
   };
-  auto ldAs = [&](const bf16* m, int r0, int k0, const float* sc, float sign) -> b4 {
-    const b4 x = ldA(m, r0, k0);
-    const f32x4 f = *reinterpret_cast<const f32x4*>(sc + k0 + 4 * g4);
-    return b4{(bf16)(sign * to_f32(x[0]) * f[0]), (bf16)(sign * to_f32(x[1]) * f[1]),
-              (bf16)(sign * to_f32(x[2]) * f[2]), (bf16)(sign * to_f32(x[3]) * f[3])};
-  };
   // B operand from a row-major [k][n] matrix: B[k0 + 4 g4 + p][n0 + c16]
   auto ldBc = [&](const bf16* m, int k0, int n0) -> b4 {
     const bf16* p = m + (k0 + 4 * g4) * LD + n0 + c16;
@@ -301,17 +295,35 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, unsigned char* smem
   auto scl = [](b4 x, float f) -> b4 {
     return b4{(bf16)(to_f32(x[0]) * f), (bf16)(to_f32(x[1]) * f), (bf16)(to_f32(x[2]) * f), (bf16)(to_f32(x[3]) * f)};
   };
+  // 16x32 operand of a 16x16x32 product: row r0 + c16, reduction indices
+  // k0 + 8 g4 .. + 7 (one 16-byte read), optionally times sc[k] and a sign
+  typedef Mma<bf16> M32;
+  auto ld8 = [&](const bf16* m, int r0, int k0) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(m + (r0 + c16) * LD + k0 + 8 * g4);
+  };
+  auto ld8s = [&](const bf16* m, int r0, int k0, const float* sc, float sign) -> bf16x8 {
+    const bf16x8 x = ld8(m, r0, k0);
+    const f32x4 f0 = *reinterpret_cast<const f32x4*>(sc + k0 + 8 * g4);
+    const f32x4 f1 = *reinterpret_cast<const f32x4*>(sc + k0 + 8 * g4 + 4);
+    bf16x8 y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      y[i] = (bf16)(sign * to_f32(x[i]) * f0[i]);
+      y[4 + i] = (bf16)(sign * to_f32(x[4 + i]) * f1[i]);
+    }
+    return y;
+  };
   // 16x16 tile C[row][col] = sum over the 64 columns of X[rx + row] . Y[ry + col]
   auto gram = [&](const bf16* X, int rx, const bf16* Y, int ry) -> f32x4 {
     f32x4 acc = zero4();
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) acc = MB::mma(ldA(X, rx, 16 * ks), ldA(Y, ry, 16 * ks), acc);
+    for (int k0 = 0; k0 < 64; k0 += 32) acc = M32::mma(ld8(X, rx, k0), ld8(Y, ry, k0), acc);
     return acc;
   };
   auto grams = [&](const bf16* X, int rx, const float* sx, const bf16* Y, int ry) -> f32x4 {
     f32x4 acc = zero4();
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) acc = MB::mma(ldAs(X, rx, 16 * ks, sx, 1.f), ldA(Y, ry, 16 * ks), acc);
+    for (int k0 = 0; k0 < 64; k0 += 32) acc = M32::mma(ld8s(X, rx, k0, sx, 1.f), ld8(Y, ry, k0), acc);
     return acc;
   };
   auto rnd = [](f32x4 x) { return MB::round(x); };
@@ -393,8 +405,8 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, unsigned char* smem
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      y[q] = MB::mma(ldAs(Kr, r0, 16 * ks, Dec + I * D, 1.f), ldA(dSm, 16 * (2 * hc + q), 16 * ks), y[q]);
+    for (int k0 = 0; k0 < 64; k0 += 32)
+      y[q] = M32::mma(ld8s(Kr, r0, k0, Dec + I * D, 1.f), ld8(dSm, 16 * (2 * hc + q), k0), y[q]);
   // R = W V - Kb S^T
   f32x4 R[2];
 #pragma unroll
@@ -403,8 +415,8 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, unsigned char* smem
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) R[q][ii] = to_f32(WV[(r0 + 4 * g4 + ii) * LD + 16 * nt + c16]);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      R[q] = MB::mma(ldAs(BKl, r0, 16 * ks, Eg + I * D, -1.f), ldA(Sm, 16 * nt, 16 * ks), R[q]);
+    for (int k0 = 0; k0 < 64; k0 += 32)
+      R[q] = M32::mma(ld8s(BKl, r0, k0, Eg + I * D, -1.f), ld8(Sm, 16 * nt, k0), R[q]);
   }
   lds_barrier();
   if (hc == 0) {
