@@ -141,7 +141,8 @@ struct BlockLayout {
   static constexpr int oXc = oQe + BL * DK * ES;             // [2][NW][NFR][64] fragments
   static constexpr int szXc = PARTS > 1 ? 2 * NW * NFR * 64 * FRB : 0;
   static constexpr int oMp = oXc + szXc;                     // [PARTS][DV] f32
-  static constexpr int serial_bytes = oMp + (PARTS > 1 ? PARTS * DV * 4 : 0);
+  static constexpr int oYp = oMp + (PARTS > 1 ? PARTS * DV * 4 : 0);   // [64][NWV] f32 partial sums of U_down m
+  static constexpr int serial_bytes = oYp + 64 * NWV * 4;
   static_assert(serial_bytes <= 160 * 1024, "LDS budget");
   static_assert(oR1 % 16 == 0 && oR2 % 16 == 0 && oR3 % 16 == 0 && oR4 % 16 == 0 && oMt % 16 == 0, "alignment");
   static_assert(NB * 256 * 4 <= DK * LK * ES, "pairwise scratch fits in R4");

@@ -90,66 +90,91 @@ carve_chunk_serial_kernel(FwdArgs a) {
 
   // The content projection of this head stays in registers for the whole
   // sequence (the bias is recomputed at every chunk boundary, on the serial
-  // chain, so it must not wait for memory):
-  //   y_r = sum_e U_down[h][r][e] m[e]: eight lanes per row r (lane group
-  //       gi = lane / 8 of wave w takes r = 8 (w + NWV k) + gi), lane
-  //       c = lane % 8 holds e in [c DV/8, (c + 1) DV/8): ud(k, i);
+  // chain, so it must not wait for memory). The chunk mean reaches it as the
+  // column sums of each wave's own output tiles, so no wave waits for the
+  // whole mean before it forms its share of y = U_down m:
+  //   y_r: lane (g, c) holds U_down[h][r][e0 + 4g + i] (i < 4) for the rows
+  //       r = c + 16 k of its value slice's channels (ud(k)); it multiplies
+  //       them with its row group's channel sums, the four row groups are
+  //       added with lane swaps, and the wave's partial sum of y_r goes to
+  //       Yp[r][wave]; whoever forms z adds the partials of every wave;
   //   z_d = sum_r U_up[h][d][r] y_r: TPD = NT / DK lanes per key channel
   //       (d = tid / TPD), lane q = tid % TPD holds r = q + TPD i: uu(i).
-  // Values stay in the input type, two per register; the partial sums are
-  // combined with DPP lane moves inside quads and rows.
-  constexpr int NWV = NT / 64, RK = (kMaxRank + 8 * NWV - 1) / (8 * NWV), EPR = DV / 8;
+  // Values stay in the input type, two per register for U_up; the sums over
+  // a key channel's lanes are DPP moves inside quads and rows.
+  constexpr int NWV = NT / 64, RKG = kMaxRank / 16;
   constexpr int TPD = NT / DK, RPT = kMaxRank / TPD;
-  static_assert((TPD == 4 || TPD == 8) && EPR % 4 == 0 && RPT % 2 == 0, "lanes per key channel");
+  static_assert((TPD == 4 || TPD == 8) && RPT % 2 == 0 && NWV % 4 == 0, "lanes per key channel");
   typedef E e2 __attribute__((ext_vector_type(2)));
-  const int zd = tid / TPD, zq = tid % TPD, gi = lane >> 3, gc = lane & 7;
-  e2 ud[RK][EPR / 2], uu[RPT / 2];
+  const int zd = tid / TPD, zq = tid % TPD;
+  float* Yp = reinterpret_cast<float*>(smem + LY::oYp);     // [kMaxRank][NWV]
+  typename B::e4 ud[RKG];
+  e2 uu[RPT / 2];
 #pragma unroll
-  for (int k = 0; k < RK; ++k) {
-    const int r = 8 * (wave + NWV * k) + gi;
-#pragma unroll
-    for (int i = 0; i < EPR; ++i)
-      ud[k][i / 2][i % 2] = r < rank ? Ud[((size_t)h * rank + r) * DV + gc * EPR + i] : from_f32<E>(0.f);
+  for (int k = 0; k < RKG; ++k) {
+    const int r = cc + 16 * k;
+    ud[k] = r < rank ? *reinterpret_cast<const typename B::e4*>(Ud + ((size_t)h * rank + r) * DV + e0 + 4 * gq)
+                     : typename B::e4{};
   }
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int r = zq + TPD * i;
     uu[i / 2][i % 2] = r < rank ? Uu[((size_t)h * DK + zd) * rank + r] : from_f32<E>(0.f);
   }
-  // z = U_up (U_down m) into s.Z (all threads call; ends with a barrier)
-  auto content_bias = [&]() {
-    if (rank > 0) {
-      float me[EPR];
+  // z = U_up (U_down m) into s.Z with m = scale * (the sum over waves of tot),
+  // tot: this wave's sums for channels e0 + 4g + i. With `mean` and several
+  // waves per value slice, s.M = scale * (the parts' sums in Mp) as well.
+  // All threads call; two barriers.
+  auto content_bias = [&](const f32x4& tot, float scale, bool bias, bool mean) {
+    if (bias && rank > 0) {
 #pragma unroll
-      for (int i = 0; i < EPR; i += 4) {
-        const f32x4 m4 = *reinterpret_cast<const f32x4*>(s.M + gc * EPR + i);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) me[i + t] = m4[t];
-      }
-#pragma unroll
-      for (int k = 0; k < RK; ++k) {
-        if (8 * (wave + NWV * k) < rank) {           // wave-uniform
+      for (int k = 0; k < RKG; ++k) {
+        if (16 * k < rank) {                         // uniform
           float p = 0.f;
 #pragma unroll
-          for (int i = 0; i < EPR; ++i) p += to_f32(ud[k][i / 2][i % 2]) * me[i];
-          p = quad_sum(p);
-          p += dpp_mov<0x114>(p);                    // lanes 4..7 of a group: the group's sum
-          const int r = 8 * (wave + NWV * k) + gi;
-          if (gc == 7 && r < rank) s.Y[r] = p;
+          for (int i = 0; i < 4; ++i) p += to_f32(ud[k][i]) * tot[i];
+          p = sum_halves(sum_row_pairs(p));          // the four row groups: all 16 channels of the slice
+          if (gq == 0) Yp[(16 * k + cc) * NWV + wave] = p;
         }
       }
-      __syncthreads();
+    }
+    __syncthreads();
+    if (bias && rank > 0) {
       float z = 0.f;
 #pragma unroll
-      for (int i = 0; i < RPT; ++i)
-        if (zq + TPD * i < rank) z += to_f32(uu[i / 2][i % 2]) * s.Y[zq + TPD * i];
+      for (int i = 0; i < RPT; ++i) {
+        const int r = zq + TPD * i;
+        if (r < rank) {
+          float y = 0.f;
+#pragma unroll
+          for (int w = 0; w < NWV; w += 4) {
+            const f32x4 yv = *reinterpret_cast<const f32x4*>(Yp + r * NWV + w);
+            y += (yv[0] + yv[1]) + (yv[2] + yv[3]);
+          }
+          z += to_f32(uu[i / 2][i % 2]) * y;
+        }
+      }
       z = quad_sum(z);
       if constexpr (TPD == 8) z += dpp_mov<0x114>(z);  // lanes 4..7 of an eight: the total
-      if (zq == TPD - 1) s.Z[zd] = z;
+      if (zq == TPD - 1) s.Z[zd] = z * scale;
+    }
+    if constexpr (PARTS > 1) {
+      if (mean)
+        for (int e = tid; e < DV; e += NT) {
+          float m = 0.f;
+#pragma unroll
+          for (int p = 0; p < PARTS; ++p) m += Mp[p * DV + e];
+          s.M[e] = m * scale;
+        }
     }
     __syncthreads();
   };
-  content_bias();
+  {
+    // the bias of the first chunk, from mean_in (part 0 of each slice holds it)
+    f32x4 m0 = zero4();
+    if (a.mean_in && part == 0) m0 = *reinterpret_cast<const f32x4*>(a.mean_in + (size_t)bh * DV + e0 + 4 * gq);
+    content_bias(m0, 1.0f, true, false);
+  }
 
   f32x4 m_part = zero4();               // running sums of O over tokens, channels e0 + 4g + i
   const int nblk = (T + BL - 1) / BL;
@@ -233,27 +258,26 @@ carve_chunk_serial_kernel(FwdArgs a) {
         *reinterpret_cast<typename B::e4*>(O + src.row(t0 + r) * DV + e0 + 4 * gq) =
             typename B::e4{from_f32<E>(Ot[j][0]), from_f32<E>(Ot[j][1]), from_f32<E>(Ot[j][2]), from_f32<E>(Ot[j][3])};
     }
-    __syncthreads();
+    // No barrier here: the next block's gate pass writes only LDS that this
+    // block's output stage does not read (the S fragments and the Mt/Qe
+    // units have their own areas), and at a chunk end the bias below holds
+    // two barriers of its own.
     const bool chunk_end = ((t0 + BL) % L == 0) || (t0 + BL >= T);
     if (chunk_end) {
       const int chunk = t0 / L;
       const int count = min(L, T - chunk * L);
-      const f32x4 tot = sum_cols(m_part);
+      // this wave's output sums over its tokens of the chunk, channels e0 + 4g + i
+      f32x4 tot;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tot[i] = sum_row16(m_part[i]);
+      const float scale = 1.0f / (float)count;
       if constexpr (PARTS == 1) {
-        if (cc == 0) *reinterpret_cast<f32x4*>(s.M + e0 + 4 * gq) = tot * (1.0f / (float)count);
+        if (cc == 0) *reinterpret_cast<f32x4*>(s.M + e0 + 4 * gq) = tot * scale;
       } else {
         if (cc == 0) *reinterpret_cast<f32x4*>(Mp + part * DV + e0 + 4 * gq) = tot;
-        __syncthreads();
-        for (int e = tid; e < DV; e += NT) {
-          float m = 0.f;
-#pragma unroll
-          for (int p = 0; p < PARTS; ++p) m += Mp[p * DV + e];
-          s.M[e] = m * (1.0f / (float)count);
-        }
       }
       m_part = zero4();
-      __syncthreads();
-      if (t0 + BL < T) content_bias();
+      content_bias(tot, scale, t0 + BL < T, true);
     }
   }
   if (a.state_out) {
