@@ -142,9 +142,21 @@ struct BlockLayout {
   static constexpr int szXc = PARTS > 1 ? 2 * NW * NFR * 64 * FRB : 0;
   static constexpr int oMp = oXc + szXc;                     // [PARTS][DV] f32
   static constexpr int oYp = oMp + (PARTS > 1 ? PARTS * DV * 4 : 0);   // [64][NWV] f32 partial sums of U_down m
-  static constexpr int serial_bytes = oYp + 64 * NWV * 4;
+  // Lean chunk-serial blocks (bf16, d = 64, 64-token blocks, eight waves):
+  // the triangular system's operands in areas of their own
+  static constexpr bool kLean = ES == 2 && DK == 64 && DV == 64 && BL == 64 && NWV == 8;
+  static constexpr int oLP = oYp + 64 * NWV * 4;             // [BL][LK] E: P
+  static constexpr int oLQd = oLP + BL * LK * ES;            // [BL][LD] E: Q_dec
+  static constexpr int oLAn = oLQd + BL * LD * ES;           // [BL][LK] E: -A_IJ, J < I
+  static constexpr int oLTd = oLAn + BL * LK * ES;           // [NB][16][LTD] E: T_II
+  static constexpr int oLCx = oLTd + NB * 16 * LTD * ES;     // [NW][TD/2 + NB/2][64] 8-byte C tiles
+  static constexpr int oLXm = oLCx + NW * (TD / 2 + NB / 2) * 64 * 8;   // [NW][64] f32x4 mean partials
+  static constexpr int lean_bytes = oLXm + NW * 64 * 16;
+  static constexpr int serial_bytes = kLean ? lean_bytes : oYp + 64 * NWV * 4;
   static_assert(serial_bytes <= 160 * 1024, "LDS budget");
   static_assert(oR1 % 16 == 0 && oR2 % 16 == 0 && oR3 % 16 == 0 && oR4 % 16 == 0 && oMt % 16 == 0, "alignment");
+  static_assert(oLP % 16 == 0 && oLQd % 16 == 0 && oLAn % 16 == 0 && oLTd % 16 == 0 && oLCx % 16 == 0 &&
+                oLXm % 16 == 0, "alignment");
   static_assert(NB * 256 * 4 <= DK * LK * ES, "pairwise scratch fits in R4");
 
   // ---- image of one block's state-pass operands (workspace), every part in
@@ -1012,6 +1024,208 @@ struct Block {
       OltR[j] = acc;
     }
     __syncthreads();
+  }
+
+  // -------------------------------------------------------------- lean blocks
+  // The chunk-serial kernel at d = 64 with 64-token bf16 blocks has LDS to
+  // spare, so the operands of the triangular system get areas of their own
+  // and the stage sequence loses three barriers and a round trip:
+  //   - P, -A_IJ and Q_dec do not wait for the gate operands to die;
+  //   - the wave that computes a diagonal Gram tile forms its inverse
+  //     T_II = (I + A_II)^{-1} at once from its registers (the transposed
+  //     copy of -A_II comes from a product with the identity, which is
+  //     exact), as inverse_diag does from LDS;
+  //   - the affine maps come from the solve's registers as in the
+  //     chunk-parallel intra kernel (image_from_x): M^T and Qe units go to
+  //     the kernel's LDS sink, and the U waves keep the C^T and Ol^T tiles of
+  //     their value slice, handing half of them to the other wave of the
+  //     slice through Cx.
+  // Blocks whose decay is too steep for the factorised Grams take the
+  // general stages instead.
+  struct Lean {
+    E* P; E* Qd; E* An; E* Td; e4* Cx;
+  };
+  __device__ static Lean lean(unsigned char* smem) {
+    return Lean{reinterpret_cast<E*>(smem + LY::oLP), reinterpret_cast<E*>(smem + LY::oLQd),
+                reinterpret_cast<E*>(smem + LY::oLAn), reinterpret_cast<E*>(smem + LY::oLTd),
+                reinterpret_cast<e4*>(smem + LY::oLCx)};
+  }
+  // Q_dec rows of this thread from the gate-pass registers
+  __device__ static void lean_qd(const Lean& ln, const E (&qd)[16]) {
+    const GateCoord gc;
+    if (gc.active())
+#pragma unroll
+      for (int i = 0; i < RPL; ++i)
+        *reinterpret_cast<e4*>(ln.Qd + (gc.r0 + i) * LD + gc.d0) = e4{qd[4 * i], qd[4 * i + 1], qd[4 * i + 2], qd[4 * i + 3]};
+  }
+  // Grams A and P (factorised form only) and the diagonal inverses. Ends
+  // with a barrier.
+  __device__ static void grams_lean(const Smem& s, const Lean& ln) {
+    static_assert(LY::kLean, "lean blocks only");
+    const int wave = wave_id(), lane = threadIdx.x & 63;
+    const int gq = lane >> 4, cc = lane & 15;
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      int I, J;
+      if (!gram_tile(wave, k, I, J)) continue;
+      const bool diag = (I == J), far = (J < I - 1);
+      Frag ka[DK / KS], qa[DK / KS], kb[DK / KS];
+#pragma unroll
+      for (int p = 0; p < DK / KS; ++p) {
+        ka[p] = MM::ld_nat(s.Kx, LD, 16 * I + cc, p * KS);
+        qa[p] = MM::ld_nat(s.Qx, LD, 16 * I + cc, p * KS);
+        kb[p] = MM::ld_nat(s.Ky, LD, 16 * J + cc, p * KS);
+      }
+      if (far || diag) {
+        const float* fr = far ? s.Ff + ((I - 2) * (I - 1) / 2 + J) * DK : s.Fd + J * DK;
+#pragma unroll
+        for (int p = 0; p < DK / KS; ++p) kb[p] = FragScale<E>::apply(kb[p], fr, p * KS);
+      }
+      f32x4 accA = zero4(), acP = zero4();
+#pragma unroll
+      for (int p = 0; p < DK / KS; ++p) {
+        accA = MM::mma(ka[p], kb[p], accA);
+        acP = MM::mma(qa[p], kb[p], acP);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * I + 4 * gq + i, j = 16 * J + cc;
+        const bool keep = !diag || (j < r);
+        accA[i] = keep ? accA[i] : 0.f;
+        ln.P[r * LK + j] = from_f32<E>(keep ? acP[i] : 0.f);
+      }
+      if (diag) {
+        // (I + P)(I + P^2)(I + P^4)(I + P^8) with P = -A_II, as in inverse_diag
+        using M16 = Mma16<float>;
+        f32x4 Pc, Id;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          Pc[i] = -accA[i];
+          Id[i] = 4 * gq + i == cc ? 1.f : 0.f;
+        }
+        const f32x4 Pt = M16::mma(Pc, Id, zero4());   // (P^T I)_C: P in the transposed layout
+        f32x4 Rt = Pt;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * gq + i == cc) Rt[i] += 1.f;
+        const f32x4 P2c = M16::mma(Pt, Pc, zero4()), P2t = M16::mma(Pc, Pt, zero4());
+        Rt += M16::mma(P2c, Rt, zero4());
+        const f32x4 P4c = M16::mma(P2t, P2c, zero4()), P4t = M16::mma(P2c, P2t, zero4());
+        Rt += M16::mma(P4c, Rt, zero4());
+        const f32x4 P8c = M16::mma(P4t, P4c, zero4());
+        Rt += M16::mma(P8c, Rt, zero4());
+        *reinterpret_cast<e4*>(ln.Td + I * 16 * LTD + cc * LTD + 4 * gq) =
+            e4{from_f32<E>(Rt[0]), from_f32<E>(Rt[1]), from_f32<E>(Rt[2]), from_f32<E>(Rt[3])};
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ln.An[(16 * I + 4 * gq + i) * LK + 16 * J + cc] = from_f32<E>(-accA[i]);
+      }
+    }
+    __syncthreads();
+  }
+  // [W | U] by blocked forward substitution (as in solve) into registers, then
+  // the affine maps from them. W waves write M^T and Qe units to the sink;
+  // U waves return the C^T and Ol^T tiles of this wave's part of its value
+  // slice (rounded to E) in CtR, OltR and hand the other part's to Cx. Ends
+  // with a barrier, after which the waves of part 0 read theirs from Cx.
+  __device__ static void solve_affine_lean(const Smem& s, const Lean& ln, f32x4 (&CtR)[CTP], f32x4 (&OltR)[OLP]) {
+    static_assert(LY::kLean && CTW == 1 && PARTS == 2 && CTP * 2 == TD && OLP * 2 == NB, "lean blocks only");
+    using M16 = Mma16<E>;
+    const int wave = wave_id(), lane = threadIdx.x & 63;
+    const int gq = lane >> 4, cc = lane & 15;
+    const bool isW = wave < DK / 16;
+    const int col0 = 16 * wave - (isW ? 0 : DK) + cc;
+    f32x4 R[NB];
+#pragma unroll
+    for (int I = 0; I < NB; ++I)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * I + 4 * gq + i;
+        R[I][i] = isW ? to_f32(s.Kx[r * LD + col0]) * s.EGs[I * DK + col0]     // b k e^{G_r}
+                      : s.Wg[r] * to_f32(s.V[r * LV + col0]);                  // w v
+      }
+    e4 X[NB];
+#pragma unroll
+    for (int I = 0; I < NB; ++I) {
+      f32x4 acc = R[I];
+#pragma unroll
+      for (int J = 0; J < I; ++J)
+        acc = M16::mma(*reinterpret_cast<const e4*>(ln.An + (16 * I + cc) * LK + 16 * J + 4 * gq), X[J], acc);
+      const e4 T = *reinterpret_cast<const e4*>(ln.Td + I * 16 * LTD + cc * LTD + 4 * gq);
+      X[I] = M16::round(M16::mma(T, M16::round(acc), zero4()));
+    }
+    auto rd = [&](const E* base, int pitch, int row, int I) {
+      return *reinterpret_cast<const e4*>(base + row * pitch + 16 * I + 4 * gq);
+    };
+    if (isW) {
+      // M^T (rows d = 16 D + c) and Qe (rows r = 16 R + c) against k = 16 kt + 4g + i:
+      // one half of a sink unit each
+      unsigned char* sink = reinterpret_cast<unsigned char*>(s.Mt);
+      const int kt = wave, u = kt / 2, half = kt % 2;
+#pragma unroll
+      for (int D = 0; D < TD; ++D) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int I = 0; I < NB; ++I) acc = M16::mma(X[I], rd(s.KdT, LK, 16 * D + cc, I), acc);
+        const float eg = s.Egl[16 * D + cc];
+        e4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = from_f32<E>((16 * kt + 4 * gq + i == 16 * D + cc ? eg : 0.f) - acc[i]);
+        *reinterpret_cast<e4*>(sink + LY::wMt + ((D * NU + u) * 64 + lane) * 16 + half * 8) = v;
+      }
+#pragma unroll
+      for (int Rb = 0; Rb < NB; ++Rb) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int I = 0; I <= Rb; ++I) acc = M16::mma(X[I], rd(ln.P, LK, 16 * Rb + cc, I), acc);
+        const e4 q = *reinterpret_cast<const e4*>(ln.Qd + (16 * Rb + cc) * LD + 16 * kt + 4 * gq);
+        e4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = from_f32<E>(to_f32(q[i]) - acc[i]);
+        *reinterpret_cast<e4*>(sink + LY::wQe + ((Rb * NU + u) * 64 + lane) * 16 + half * 8) = v;
+      }
+    } else {
+      const int slice = wave - DK / 16;               // = wave % NW: this wave is part 1 of its slice
+      e4* cx = ln.Cx + slice * (CTP + OLP) * 64 + lane;
+#pragma unroll
+      for (int D = 0; D < TD; ++D) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int I = 0; I < NB; ++I) acc = M16::mma(rd(s.KdT, LK, 16 * D + cc, I), X[I], acc);
+        const e4 v = M16::round(acc);
+        if (D < CTP) cx[D * 64] = v;
+        else
+#pragma unroll
+          for (int i = 0; i < 4; ++i) CtR[D - CTP][i] = to_f32(v[i]);
+      }
+#pragma unroll
+      for (int Rb = 0; Rb < NB; ++Rb) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int I = 0; I <= Rb; ++I) acc = M16::mma(X[I], rd(ln.P, LK, 16 * Rb + cc, I), acc);
+        const e4 v = M16::round(acc);
+        if (Rb < OLP) cx[(CTP + Rb) * 64] = v;
+        else
+#pragma unroll
+          for (int i = 0; i < 4; ++i) OltR[Rb - OLP][i] = to_f32(v[i]);
+      }
+    }
+    __syncthreads();
+    if (isW) {
+      const e4* cx = ln.Cx + wave * (CTP + OLP) * 64 + lane;   // part 0 of slice `wave`
+#pragma unroll
+      for (int t = 0; t < CTP; ++t) {
+        const e4 v = cx[t * 64];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) CtR[t][i] = to_f32(v[i]);
+      }
+#pragma unroll
+      for (int j = 0; j < OLP; ++j) {
+        const e4 v = cx[(CTP + j) * 64];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) OltR[j][i] = to_f32(v[i]);
+      }
+    }
   }
 
   // -------------------------------------------------------------- state and output

@@ -196,6 +196,8 @@ carve_chunk_serial_kernel(FwdArgs a) {
     const int nb = min(blk + 1, nblk - 1);           // unconditional: keeps the load waits simple
     raw.template load<kNorm>(src, nb * BL, min(BL, T - nb * BL));
   };
+  // the final mean in the order of the chunk-parallel state pass (see below)
+  const bool lean_mean_out = LY::kLean && L == BL && a.mean_out != nullptr;
   for (int blk = 0; blk < nblk; ++blk) {
     const int t0 = blk * BL;
     const int nvalid = min(BL, T - t0);
@@ -215,11 +217,21 @@ carve_chunk_serial_kernel(FwdArgs a) {
     if (kFetch == 2) raw.template load<kNorm>(src, t0, nvalid);
     const bool fallback = B::template gate_pass<true, kLogits, kNorm>(s, raw, nvalid, qd);
     if (kFetch == 0) fetch_next(blk);
-    B::template grams<kLogits, kNorm>(s, src, t0, nvalid, fallback, Pt);
-    B::inverse_diag(s);
-    B::solve(s, qd, Pt);
     f32x4 CtR[TDP], OltR[NBP], Ot[NBP];
-    B::affine(s, sink, CtR, OltR);                   // ends with a barrier
+    // lean blocks (uniform: the flag is read after the gate pass's barrier)
+    if (LY::kLean && !fallback) {
+      if constexpr (LY::kLean) {
+        const auto ln = B::lean(smem);
+        B::lean_qd(ln, qd);
+        B::grams_lean(s, ln);                        // ends with a barrier
+        B::solve_affine_lean(s, ln, CtR, OltR);      // ends with a barrier (then part 0 reads Cx)
+      }
+    } else {
+      B::template grams<kLogits, kNorm>(s, src, t0, nvalid, fallback, Pt);
+      B::inverse_diag(s);
+      B::solve(s, qd, Pt);
+      B::affine(s, sink, CtR, OltR);                 // ends with a barrier
+    }
     if (kFetch == 1) fetch_next(blk);
     // S operand fragments of the state at the block start: this wave's from
     // its registers, the other parts' from the exchange buffer
@@ -276,8 +288,29 @@ carve_chunk_serial_kernel(FwdArgs a) {
       } else {
         if (cc == 0) *reinterpret_cast<f32x4*>(Mp + part * DV + e0 + 4 * gq) = tot;
       }
+      // Lean blocks with one block per chunk: the final mean is summed in
+      // the order of the chunk-parallel state pass (the four token tiles of
+      // the last block in turn, then the columns by xor swaps), so that with
+      // a zero projection this kernel's mean_out equals that of the pair
+      // without one bit for bit, as its o and state do: part 0 hands its
+      // running tile sum to part 1, which adds its own tiles after the
+      // bias's first barrier.
+      const bool lean_mean = lean_mean_out && t0 + BL >= T;   // uniform
+      f32x4* xm = reinterpret_cast<f32x4*>(smem + LY::oLXm) + slice * 64 + lane;
+      if (lean_mean && part == 0) *xm = m_part;
       m_part = zero4();
       content_bias(tot, scale, t0 + BL < T, true);
+      if (lean_mean && part == 1) {
+        f32x4 fin = *xm;
+#pragma unroll
+        for (int j = 0; j < NBP; ++j) fin += Ot[j];
+        fin = sum_cols(fin);
+        if (cc == 0) {
+          float* mo = a.mean_out + (size_t)bh * DV + e0 + 4 * gq;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mo[i] = fin[i] * scale;
+        }
+      }
     }
   }
   if (a.state_out) {

@@ -125,21 +125,25 @@ def test_zero_projection_is_bitwise_absent_projection(torch_cuda):
         assert np.array_equal(x, y)
 
 
-def test_zero_projection_matches_parallel_schedule(torch_cuda):
-    """bf16: a zero-filled projection runs the chunk-serial kernel, an absent
-    one the chunk-parallel pair. They evaluate the same expressions with
-    differently ordered fp32 sums inside the gate pass, so they agree to
-    rounding (a few bf16 roundings of intermediates), far inside the
-    tolerance against the oracle that each meets on its own."""
-    wl = WORKLOADS["init_equiv"].with_(B=2, T=512, rank=16, ub_std=0.05)
+@pytest.mark.parametrize("T", [2048, 2000])
+def test_zero_projection_is_bitwise_parallel_schedule(torch_cuda, T):
+    """bf16 at the B4 H12 d64 L64 shape: a zero-filled rank-16 projection runs
+    the chunk-serial kernel, an absent one the chunk-parallel pair. The serial
+    kernel's 64-token blocks form the affine maps from the solve's registers
+    with the pair's products, apply them in the pair's order and sum the final
+    mean in the state pass's order, and a zero projection adds a content bias
+    of exactly zero, so o, the final state and the final mean are equal bit
+    for bit (the layer at initialisation is the memory-blind rule exactly;
+    shd-paper.top English abstract, and gist.science technical summary §2.1).
+    T = 2000 ends in a ragged block."""
+    wl = WORKLOADS["init_equiv"].with_(T=T, rank=16, ub_std=0.05)
     say("case zero U_b (serial) vs absent U_b (parallel)", wl)
     inp = make_inputs(wl)
     a = run_gpu(torch_cuda, inp, wl.dtype, wl.L, use_ub=False)
     b = run_gpu(torch_cuda, inp, wl.dtype, wl.L, zero_ub=True)
-    errs = [rel_err(x, y) for x, y in zip(a, b)]
-    say("schedules differ by " + ", ".join(f"{e:.2e}" for e in errs))
-    for e in errs:
-        assert e <= TOL["bf16"] / 4
+    for name, x, y in zip(("o", "state", "mean"), a, b):
+        say(name, "differing elements:", int(np.count_nonzero(x != y)))
+        assert np.array_equal(x, y), name
 
 
 def test_content_bf16_sampled(torch_cuda):
