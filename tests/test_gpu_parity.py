@@ -187,6 +187,8 @@ EDGE = [
     ("f32-d128-L128", "f32", 1, 2, 384, 128, 128, 8),
     ("bf16-d64-L32", "bf16", 2, 2, 320, 64, 32, 8),
     ("bf16-d128-L16", "bf16", 1, 2, 160, 128, 16, 8),
+    # the lean 64-token blocks of the chunk-serial kernel, ending in a ragged block
+    ("lean-ragged-200", "bf16", 2, 2, 200, 64, 64, 8),
     ("no-ub-L16", "f32", 1, 2, 192, 64, 16, 0),
     # no content projection in bf16: the chunk-parallel schedule
     ("par-T1", "bf16", 1, 2, 1, 64, 32, 0),
@@ -363,3 +365,24 @@ def test_forward_graph_replays_match_eager(torch_cuda, rank):
         torch.cuda.synchronize()
         assert torch.equal(o, ref[0]), f"replay {i}"
         assert float(scratch) == float(1 << 20)
+
+
+def test_steep_blocks_between_lean_blocks(torch_cuda):
+    """bf16 with a projection at d = 64, L = 64 (the chunk-serial kernel's
+    lean blocks): in blocks 1 and 3 half the key channels decay by e^-10 per
+    token, too steep for the factorised Grams, so those blocks take the
+    general stages with the pairwise rebuild while blocks 0, 2 and 4 stay
+    lean; the state, the content bias and the chunk means pass between the
+    two kinds of block."""
+    wl = WORKLOADS["init_equiv"].with_(B=1, H=3, T=320, rank=16, ub_std=0.5, seed=3005)
+    inp = make_inputs(wl)
+    g = np.full(inp["g"].shape, -0.02, np.float32)
+    for blk in (1, 3):
+        g[:, 64 * blk: 64 * (blk + 1), :, : wl.dk // 2] = -10.0
+    inp["g"] = bf16_bits_from_f32(g)
+    say("case steep blocks between lean blocks", wl)
+    rng = np.random.default_rng(11)
+    m_in = (0.3 * rng.standard_normal((wl.B, wl.H, wl.dv))).astype(np.float32)
+    got = run_gpu(torch_cuda, inp, wl.dtype, wl.L, mean_in=m_in)
+    ref = run_oracle(inp, wl.dtype, wl.L, mean_in=m_in.astype(np.float64))
+    assert_parity(got, ref, TOL["bf16"], "steep blocks between lean blocks")
