@@ -318,7 +318,8 @@ carve_chunk_serial_kernel(FwdArgs a) {
 #pragma unroll
     for (int t = 0; t < TDP; ++t) *reinterpret_cast<f32x4*>(So + 16 * (TDP * part + t)) = St[t];
   }
-  if (a.mean_out)
+  // (the lean blocks' part-1 waves have written mean_out already)
+  if (a.mean_out && !(lean_mean_out && T > 0))
     for (int e = tid; e < DV; e += NT) a.mean_out[(size_t)bh * DV + e] = s.M[e];
 }
 

@@ -325,12 +325,16 @@ def test_delta_rule_special_case(torch_cuda):
 
 
 def test_deterministic(torch_cuda):
-    wl = WORKLOADS["content"].with_(B=2, T=1024)
+    """Repeated chunk-serial calls agree bit for bit in o, the state and the
+    mean (48 heads, four calls: a race between two writers of the final mean
+    once showed here as last-bit differences in a few heads per call)."""
+    wl = WORKLOADS["content"].with_(B=4, T=2048)
     inp = make_inputs(wl)
     a = run_gpu(torch_cuda, inp, wl.dtype, wl.L)
-    b = run_gpu(torch_cuda, inp, wl.dtype, wl.L)
-    for x, y in zip(a, b):
-        assert np.array_equal(x, y)
+    for _ in range(3):
+        b = run_gpu(torch_cuda, inp, wl.dtype, wl.L)
+        for name, x, y in zip(("o", "state", "mean"), a, b):
+            assert np.array_equal(x, y), name
 
 
 @pytest.mark.parametrize("rank", [0, 8], ids=["chunk-parallel", "chunk-serial"])
