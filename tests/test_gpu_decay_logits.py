@@ -83,6 +83,8 @@ FWD_CASES = [
     ("ser-bf16-d64-L32-r16-ragged-300", "bf16", 2, 2, 300, 64, 32, 16),
     ("ser-f32-d128-L16-r4-ragged-150", "f32", 1, 2, 150, 128, 16, 4),
     ("ser-bf16-d128-L64-r8", "bf16", 1, 2, 256, 128, 64, 8),
+    # the chunk-serial kernel's lean 64-token blocks (bf16, d = 64), ragged tail
+    ("lean-bf16-d64-L64-r16-ragged-200", "bf16", 2, 2, 200, 64, 64, 16),
 ]
 
 

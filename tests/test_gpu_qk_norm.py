@@ -78,6 +78,8 @@ FWD_CASES = [
     ("ser-f32-d64-L64-r8", "f32", 1, 2, 256, 64, 64, 8),
     ("ser-bf16-d128-L32-r8-ragged-150", "bf16", 1, 2, 150, 128, 32, 8),
     ("ser-f32-d128-L16-r4", "f32", 1, 2, 96, 128, 16, 4),
+    # the chunk-serial kernel's lean 64-token blocks (bf16, d = 64), ragged tail
+    ("lean-bf16-d64-L64-r16-ragged-200", "bf16", 2, 2, 200, 64, 64, 16),
 ]
 
 
